@@ -1,0 +1,131 @@
+/*
+ * w4a16.h — C ABI of the W4A16 linear layer for AMD Instinct MI355X (gfx950).
+ *
+ * Weight-only INT4: fp16 weights W[N,K] (N = out_features, K = in_features)
+ * are quantized round-to-nearest, symmetric, one fp16 scale per group of 128
+ * consecutive elements along K; activations stay fp16 and the weights are
+ * dequantized in registers inside the GEMV/GEMM kernels.
+ *
+ * Sources (web pages; cited by key in every comment of this library):
+ *   [BENCH] "W4A16 量化算子解码性能基准跑分与端侧大模型推理显存实测报告"
+ *           (W4A16 operator decode benchmark report), mhpq.cn/news/1206820.
+ *           §一 test setup (group 128, symmetric INT4, fp16 scales),
+ *           §二 results (decode is memory-bound, every token sweeps all
+ *           weights), §五 lessons (dequantize on the fly in registers).
+ *   [QUANT] qaqbuyan.com article 126 on LLM quantization, section
+ *           "量化的数学基石——从 IEEE 754 到量化误差":
+ *           sub-section 1 (FP16 bit layout, INT4 range [-8,7]),
+ *           sub-section 2 (symmetric quantization equations; rounding error
+ *           uniform in [-s/2, s/2]),
+ *           sub-section 3 (granularity table; per-group quantizer listing
+ *           with group 128 along in_features, two nibbles per byte, offset
+ *           binary q+8, even index in the low nibble; 3.1% scale overhead).
+ *   [INT4]  guijiagi.com tag page "量化", entry on INT8 / INT4 / FP8
+ *           schemes, "INT4量化" paragraph and its group-quantization example.
+ *
+ * Packed layout (one row n of W; word j of the row holds elements 8j..8j+7):
+ *     packed[n*(K/8) + j] = sum_{i=0..7} ((q[n][8j+i] + 8) & 0xF) << (4*i)
+ *     scales[n*(K/128) + g] = fp16 bits of s[n][g]
+ * Read as little-endian bytes this is exactly the two-nibbles-per-byte,
+ * even-index-low layout of [QUANT] sub-section 3's listing, widened to
+ * eight nibbles per uint32.  Packed bytes: N*K/2; scale bytes: N*K/64.
+ *
+ * Quantizer, per row n and group g (k in [128g, 128g+128)):
+ *     a = max_k |W[n,k]|
+ *     s = round-to-nearest-even fp16 of a/7              ([QUANT] sub-sec. 2)
+ *     q = clamp(round_half_even(W[n,k] / s), -8, 7)      ([QUANT] sub-sec. 2)
+ *     q = 0 for every element when s == 0 (all-zero or underflowing group)
+ * The quotient W/s is decided exactly (as with real numbers) and q is taken
+ * against the stored fp16 scale, the only scale the dequantizer sees.
+ *
+ * Linear layer: Y[m,n] = sum_k X[m,k] * s[n,k/128] * q[n,k]  (Y = X·Ŵᵀ),
+ * accumulated in fp32, written as fp16 (round to nearest even).
+ *
+ * Conventions shared by every entry point:
+ *   - Every tensor pointer is a DEVICE pointer into memory the caller owns;
+ *     the library allocates nothing and keeps no per-call state.
+ *   - fp16 values are passed as their IEEE binary16 bit patterns (uint16_t).
+ *   - All tensors are dense row-major with no padding between rows.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
+ *     asynchronously; nothing synchronizes.  Faults surface at the caller's
+ *     next synchronization, as for any HIP launch.
+ *   - Arguments are validated on the host before anything is enqueued; a
+ *     non-zero status means nothing was enqueued.
+ *   - Sizes: M, N, K >= 0 and K % 128 == 0.  M == 0 or N == 0 enqueues
+ *     nothing (pointers may then be NULL).  K == 0 makes every output 0.
+ *   - Alignment: W, X, x and packed must be 16-byte aligned; scales, Y and
+ *     y 2-byte aligned.
+ *   - Outputs must not overlap any input.
+ *   - Inputs must be finite (a precondition, not checked).
+ *   - The current HIP device must be gfx950.
+ */
+#ifndef W4A16_H
+#define W4A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define W4A16_GROUP 128
+
+typedef enum {
+    W4A16_OK = 0,
+    W4A16_ERR_INVALID_ARG = 1, /* NULL pointer, negative size, size overflow, overlapping output */
+    W4A16_ERR_SHAPE = 2,       /* K % 128 != 0 */
+    W4A16_ERR_MISALIGNED = 3,  /* alignment rule above violated */
+    W4A16_ERR_DEVICE = 4,      /* no HIP device, or the current device is not gfx950 */
+    W4A16_ERR_LAUNCH = 5       /* the HIP runtime rejected a launch */
+} w4a16_status;
+
+enum {
+    W4A16_ALGO_AUTO = 0, /* pick by M: VALU GEMV for small M, MFMA GEMM above the crossover */
+    W4A16_ALGO_VALU = 1, /* force the VALU (dot-product) path, any M */
+    W4A16_ALGO_MFMA = 2  /* force the MFMA path, any M */
+};
+
+/* Byte sizes of the packed weights (N*K/2) and the scales (N*(K/128)*2).
+ * Return 0 for negative sizes, K % 128 != 0 or overflow. */
+size_t w4a16_packed_bytes(int64_t N, int64_t K);
+size_t w4a16_scales_bytes(int64_t N, int64_t K);
+
+/* Quantize and pack W ([QUANT] sub-sections 2-3; [INT4]).
+ *   W       in : fp16 [N, K]
+ *   packed  out: uint32 [N, K/8]   (layout above)
+ *   scales  out: fp16 [N, K/128]
+ * Bit-exact: exactly one correct output exists for every finite W. */
+int w4a16_quantize(const uint16_t* W, int64_t N, int64_t K,
+                   uint32_t* packed, uint16_t* scales, void* stream);
+
+/* Decode GEMV, M = 1 ([BENCH] §二, §五):  y[n] = sum_k x[k] * ŵ[n,k].
+ *   x       in : fp16 [K]
+ *   packed  in : uint32 [N, K/8];  scales in : fp16 [N, K/128]
+ *   y       out: fp16 [N] */
+int w4a16_gemv(const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
+               int64_t N, int64_t K, uint16_t* y, void* stream);
+
+/* Batched decode / prefill ([BENCH] §一 prompt of 512 tokens, §二 prefill):
+ *   X in : fp16 [M, K];  Y out: fp16 [M, N];  Y = X·Ŵᵀ.
+ * Picks the kernel by M (W4A16_ALGO_AUTO). */
+int w4a16_gemm(const uint16_t* X, int64_t M, const uint32_t* packed, const uint16_t* scales,
+               int64_t N, int64_t K, uint16_t* Y, void* stream);
+
+/* w4a16_gemm with the kernel family forced by `algo` (W4A16_ALGO_*); an
+ * unknown algo is W4A16_ERR_INVALID_ARG.  Results of every algo meet the same
+ * tolerance; used to measure the VALU/MFMA crossover. */
+int w4a16_gemm_ex(const uint16_t* X, int64_t M, const uint32_t* packed, const uint16_t* scales,
+                  int64_t N, int64_t K, uint16_t* Y, int algo, void* stream);
+
+/* Largest M that W4A16_ALGO_AUTO sends to the VALU path. */
+int64_t w4a16_valu_max_m(void);
+
+/* Static description of a status code (never NULL). */
+const char* w4a16_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A16_H */

@@ -1,0 +1,319 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle.
+
+Each pin takes an ``oracle.Oracle`` and returns a list of failure messages
+(empty = pinned).  ``test_oracle_pins.py`` runs them on the real oracle;
+``test_oracle_mutants.py`` runs them on copies of the oracle with a mistake
+planted, to show that a plausible mistake anywhere in it fails at least one.
+
+What each pin compares against:
+  * fp16 codec            numpy's binary16 conversions (library routine)
+  * scale, every fp16     exact rational RNE of a/7 by nearest-value search
+  * hand-worked groups    tests/golden/hand_worked_groups.json (by hand)
+  * codes                 brute-force nearest code among the 16 INT4 values,
+                          ties to the even code, in exact integer arithmetic
+  * invariants            |w - s q| <= s/2 when unclipped, q in [-8, 7],
+                          absmax -> +-7 ([QUANT] sub-section 2)
+  * byte layout           two nibbles per byte, even index low ([QUANT]
+                          sub-section 3 listing), built from the codes
+  * statistics            rounding error uniform on [-s/2, s/2]: mean |e| =
+                          s/4, mean e^2 = s^2/12 ([QUANT] sub-section 2)
+  * matmul                exact rational dot products (fractions) within the
+                          binary64 summation bound; one-hot activations
+"""
+from __future__ import annotations
+
+import bisect
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+
+from weight_only_int4_gemv_amd import inputs  # seeded draws only
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                      "hand_worked_groups.json")
+
+# All finite non-negative fp16 values, decoded by numpy, as exact fractions.
+_POS_BITS = np.arange(0x7C00, dtype=np.uint16)
+_POS_VALUES = _POS_BITS.view(np.float16).astype(np.float64)
+_POS_FRACS = [Fraction(float(v)) for v in _POS_VALUES]
+
+
+def exact_rne_f16(value: Fraction) -> int:
+    """binary16 bits nearest to a non-negative rational (ties: even mantissa),
+    found by searching the table of all fp16 values."""
+    if value >= Fraction(65520):
+        return 0x7C00
+    i = bisect.bisect_left(_POS_FRACS, value)
+    if i < len(_POS_FRACS) and _POS_FRACS[i] == value:
+        return i
+    lo, hi = i - 1, i
+    if hi >= len(_POS_FRACS):
+        return lo
+    dlo, dhi = value - _POS_FRACS[lo], _POS_FRACS[hi] - value
+    if dlo < dhi:
+        return lo
+    if dhi < dlo:
+        return hi
+    return lo if lo % 2 == 0 else hi
+
+
+def codes_from_bytes(packed: np.ndarray) -> np.ndarray:
+    """INT4 codes read through the byte layout: byte b of a row holds element
+    2b in its low nibble and 2b+1 in its high nibble, offset by 8."""
+    b = np.ascontiguousarray(packed).view(np.uint8).astype(np.int16)
+    lo = (b & 0xF) - 8
+    hi = (b >> 4) - 8
+    out = np.empty((b.shape[0], b.shape[1] * 2), dtype=np.int16)
+    out[:, 0::2] = lo
+    out[:, 1::2] = hi
+    return out
+
+
+def _fixed24(a16: np.ndarray) -> np.ndarray:
+    """fp16 values as exact int64 multiples of 2^-24."""
+    return np.round(a16.astype(np.float64) * 2.0 ** 24).astype(np.int64)
+
+
+def brute_force_codes(W: np.ndarray, scale_bits: np.ndarray, group: int = 128) -> np.ndarray:
+    """Nearest of the 16 codes c in [-8, 7] to w/s (|w - c s| minimal, ties to
+    the even c), in exact integer arithmetic; 0 where s == 0."""
+    W24 = _fixed24(W)
+    S24 = np.repeat(_fixed24(scale_bits.view(np.float16)), group, axis=1)
+    best = np.zeros(W.shape, dtype=np.int64)
+    best_d = None
+    for c in range(-8, 8):
+        d = np.abs(W24 - c * S24)
+        if best_d is None:
+            best, best_d = np.full(W.shape, c, dtype=np.int64), d
+            continue
+        better = (d < best_d) | ((d == best_d) & (c % 2 == 0))
+        best = np.where(better, c, best)
+        best_d = np.where(better, d, best_d)
+    return np.where(S24 == 0, 0, best)
+
+
+# --------------------------------------------------------------------- pins
+
+def pin_f16_codec(o) -> list:
+    fails = []
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = np.array([o.f64_from_f16(int(b)) for b in bits])
+    same = (got == ref) | (np.isnan(got) & np.isnan(ref))
+    if not same.all():
+        fails.append("f16 decode differs from numpy at %d patterns" % (~same).sum())
+    rng = np.random.default_rng(1234)
+    finite = ref[np.isfinite(ref)]
+    fin_sorted = np.unique(finite)
+    mids = (fin_sorted[:-1] + fin_sorted[1:]) / 2.0          # exact ties
+    vals = np.concatenate([
+        mids,
+        np.nextafter(mids, np.inf), np.nextafter(mids, -np.inf),
+        rng.standard_normal(20000) * 10.0 ** rng.uniform(-9, 5, 20000),
+        np.array([65504.0, 65519.99, 65520.0, 1e6, -65520.0, 2.0 ** -25, 2.0 ** -24,
+                  3 * 2.0 ** -26, 2.0 ** -14 - 2.0 ** -26, 0.0, -0.0]),
+    ])
+    with np.errstate(over="ignore"):
+        ref_bits = vals.astype(np.float16).view(np.uint16)
+    got_bits = np.array([o.f16_from_f64(float(v)) for v in vals], dtype=np.uint16)
+    bad = got_bits != ref_bits
+    if bad.any():
+        i = int(np.argmax(bad))
+        fails.append("f16 encode differs from numpy at %d values (first %r: %#06x vs %#06x)"
+                     % (bad.sum(), vals[i], got_bits[i], ref_bits[i]))
+    return fails
+
+
+def pin_scale_every_fp16(o) -> list:
+    """For every positive finite fp16 a, a group with absmax a stores RNE(a/7)
+    and maps a to 7 (clamped from 8 only for a few subnormal scales)."""
+    fails = []
+    a_bits = np.arange(1, 0x7C00, dtype=np.uint16)
+    W = np.zeros((a_bits.size, 128), dtype=np.uint16)
+    W[:, 5] = a_bits
+    packed, scales = o.quantize(W)
+    want = np.array([exact_rne_f16(_POS_FRACS[int(b)] / 7) for b in a_bits], dtype=np.uint16)
+    bad = scales[:, 0] != want
+    if bad.any():
+        i = int(np.argmax(bad))
+        fails.append("scale differs from exact RNE(a/7) for %d values (first a bits %#06x)"
+                     % (bad.sum(), a_bits[i]))
+        return fails
+    codes = codes_from_bytes(packed)
+    q5 = codes[:, 5]
+    normal = want >= 0x0400
+    if not (q5[normal] == 7).all():
+        fails.append("absmax does not map to 7 for a normal scale")
+    zero = want == 0
+    if not (q5[zero] == 0).all():
+        fails.append("zero scale does not give q = 0")
+    want_q = brute_force_codes(W[:, :8].view(np.float16), scales[:, :1], group=8)[:, 5]
+    if not (q5 == want_q).all():
+        fails.append("absmax code differs from the nearest code")
+    others = np.delete(codes, 5, axis=1)
+    if not (others == 0).all():
+        fails.append("zeros do not map to code 0")
+    return fails
+
+
+def pin_hand_worked(o) -> list:
+    fails = []
+    with open(GOLDEN) as f:
+        spec = json.load(f)
+    groups = spec["groups"]
+    W = np.zeros((len(groups), 128), dtype=np.float16)
+    for r, g in enumerate(groups):
+        for k, v in g["nonzero"].items():
+            W[r, int(k)] = np.float16(v)
+            if float(W[r, int(k)]) != v:
+                fails.append("%s: fixture value %r is not an fp16 number" % (g["name"], v))
+    packed, scales = o.quantize(W)
+    codes = codes_from_bytes(packed)
+    for r, g in enumerate(groups):
+        if scales[r, 0] != int(g["scale_bits"], 16):
+            fails.append("%s: scale %#06x, want %s" % (g["name"], scales[r, 0], g["scale_bits"]))
+        if list(codes[r, :8]) != g["q_first8"]:
+            fails.append("%s: q %s, want %s" % (g["name"], list(codes[r, :8]), g["q_first8"]))
+        for k, q in g.get("q_at", {}).items():
+            if codes[r, int(k)] != q:
+                fails.append("%s: q[%s] = %d, want %d" % (g["name"], k, codes[r, int(k)], q))
+        for j in range(16):
+            want = int(g["words"].get(str(j), g["words"]["rest"]), 16)
+            if int(packed[r, j]) != want:
+                fails.append("%s: word %d = %#010x, want %#010x" % (g["name"], j,
+                                                                   int(packed[r, j]), want))
+    # Two groups in one row: scale index follows the group.
+    row = np.concatenate([W[0], W[2]]).reshape(1, 256)
+    p2, s2 = o.quantize(row)
+    if list(s2[0]) != [0x2400, 0x2C92]:
+        fails.append("two-group row: scales %s" % [hex(v) for v in s2[0]])
+    if not (p2[0, :16] == packed[0]).all() or not (p2[0, 16:] == packed[2]).all():
+        fails.append("two-group row: words do not follow the groups")
+    return fails
+
+
+def pin_codes_nearest(o) -> list:
+    """Random layer-like weights: every code is the nearest INT4 code to w/s
+    against the stored scale; byte layout; dequantizer = s * code."""
+    fails = []
+    W = inputs.weight(96, 1024, seed=[99, 0, 0])
+    # a few groups with extreme ranges
+    W[0, :128] = np.float16(0)
+    W[1, 128:256] *= np.float16(1e-4)
+    W[2, 256:384] = np.float16(60000.0) * np.sign(W[2, 256:384].astype(np.float32))
+    packed, scales = o.quantize(W)
+    codes = codes_from_bytes(packed)
+    want = brute_force_codes(W, scales)
+    if not (codes == want).all():
+        fails.append("%d codes differ from the brute-force nearest code" % (codes != want).sum())
+    a = np.abs(W.astype(np.float64)).reshape(96, 8, 128).max(axis=2)
+    want_s = np.array([[exact_rne_f16(Fraction(float(v)) / 7) for v in row] for row in a],
+                      dtype=np.uint16)
+    if not (scales == want_s).all():
+        fails.append("scales differ from exact RNE(absmax/7)")
+    deq = o.dequantize(packed, scales)
+    s64 = np.repeat(scales.view(np.float16).astype(np.float64), 128, axis=1)
+    if not (deq == s64 * codes).all():
+        fails.append("dequantize differs from s * code")
+    return fails
+
+
+def pin_invariants(o) -> list:
+    fails = []
+    W = inputs.weight(256, 2048, seed=[99, 1, 0])
+    packed, scales = o.quantize(W)
+    codes = codes_from_bytes(packed)
+    if codes.min() < -8 or codes.max() > 7:
+        fails.append("code outside [-8, 7]")
+    W24 = _fixed24(W)
+    S24 = np.repeat(_fixed24(scales.view(np.float16)), 128, axis=1)
+    err2 = np.abs(2 * (W24 - codes * S24))              # 2|w - s q| in units of 2^-24
+    unclipped = np.abs(2 * W24) <= 15 * S24            # |w/s| <= 7.5
+    if (err2[unclipped] > S24[unclipped]).any():
+        fails.append("|w - s q| > s/2 for an unclipped element")
+    normal = scales.view(np.float16).astype(np.float64) >= 2.0 ** -14
+    if (codes[np.repeat(normal, 128, axis=1)] == -8).any():
+        fails.append("q = -8 produced with a normal scale")
+    amax_pos = np.abs(W.astype(np.float64)).reshape(256, 16, 128).argmax(axis=2)
+    qa = np.take_along_axis(codes.reshape(256, 16, 128), amax_pos[..., None], axis=2)[..., 0]
+    if not (np.abs(qa[normal]) == 7).all():
+        fails.append("absmax element not mapped to +-7")
+    # rounding error statistics ([QUANT] sub-section 2: uniform on [-s/2, s/2]),
+    # on Gaussian weights without outliers (an outlier makes the step coarse
+    # against the rest of its group, and the error then follows the weights)
+    rng = np.random.default_rng(4321)
+    G = (rng.standard_normal((256, 2048)) * 0.02).astype(np.float16)
+    gp, gs = o.quantize(G)
+    gc = codes_from_bytes(gp)
+    G24 = _fixed24(G)
+    GS24 = np.repeat(_fixed24(gs.view(np.float16)), 128, axis=1)
+    e = (G24 - gc * GS24) / GS24
+    mean_abs, mean_sq = float(np.mean(np.abs(e))), float(np.mean(e * e))
+    if abs(mean_abs - 0.25) > 0.01 or abs(mean_sq - 1 / 12) > 0.004:
+        fails.append("rounding error not uniform: E|e|/s=%.4f E e^2/s^2=%.4f"
+                     % (mean_abs, mean_sq))
+    # sizes: 2 bytes of scale per 128 INT4 elements = 3.125 % of the packed bytes
+    if (scales.nbytes * 32) != packed.nbytes:
+        fails.append("scale storage is not 1/32 of the packed storage")
+    return fails
+
+
+def pin_matmul_exact(o) -> list:
+    """Tiny shapes against exact rational sums."""
+    fails = []
+    for (M, N, K, seed) in [(1, 3, 128, 5), (3, 4, 256, 6), (2, 2, 384, 7)]:
+        W, X = inputs.weight_and_activation(N, K, M, seed=[98, seed, 0])
+        packed, scales = o.quantize(W)
+        Y, Yabs = o.matmul(X, packed, scales)
+        codes = codes_from_bytes(packed)
+        s = scales.view(np.float16).astype(np.float64)
+        xf = [[Fraction(float(v)) for v in X[m].astype(np.float64)] for m in range(M)]
+        for n in range(N):
+            wf = [Fraction(float(s[n, k // 128])) * int(codes[n, k]) for k in range(K)]
+            for m in range(M):
+                terms = [a * b for a, b in zip(xf[m], wf)]
+                exact = sum(terms, Fraction(0))
+                exact_abs = sum((abs(t) for t in terms), Fraction(0))
+                bound = K * 2.0 ** -53 * float(exact_abs)
+                if abs(Fraction(Y[m, n]) - exact) > Fraction(bound):
+                    fails.append("matmul (%d,%d) of %dx%dx%d off the exact sum"
+                                 % (m, n, M, N, K))
+                if abs(Fraction(Yabs[m, n]) - exact_abs) > Fraction(bound):
+                    fails.append("sum |x w| (%d,%d) off the exact sum" % (m, n))
+    # one-hot activations pick one dequantized weight exactly
+    W = inputs.weight(8, 256, seed=[98, 9, 0])
+    packed, scales = o.quantize(W)
+    codes = codes_from_bytes(packed)
+    s = np.repeat(scales.view(np.float16).astype(np.float64), 128, axis=1)
+    X = np.zeros((256, 256), dtype=np.float16)
+    X[np.arange(256), np.arange(256)] = np.float16(1.0)
+    Y, _ = o.matmul(X, packed, scales)
+    if not (Y == (s * codes).T).all():
+        fails.append("one-hot activations do not select s*q")
+    # sampled outputs equal the full product
+    W, X = inputs.weight_and_activation(16, 512, 4, seed=[98, 10, 0])
+    packed, scales = o.quantize(W)
+    Y, Yabs = o.matmul(X, packed, scales)
+    rows = np.array([0, 3, 2, 1, 3])
+    cols = np.array([15, 0, 7, 7, 9])
+    Ys, Yas = o.matmul_sampled(X, packed, scales, rows, cols)
+    if not ((Ys == Y[rows, cols]).all() and (Yas == Yabs[rows, cols]).all()):
+        fails.append("sampled outputs differ from the full product")
+    return fails
+
+
+ALL_PINS = [pin_f16_codec, pin_scale_every_fp16, pin_hand_worked, pin_codes_nearest,
+            pin_invariants, pin_matmul_exact]
+
+
+def run_all(o) -> dict:
+    """{pin name: [failures]} for every pin (exceptions count as failures)."""
+    out = {}
+    for pin in ALL_PINS:
+        try:
+            out[pin.__name__] = pin(o)
+        except Exception as exc:  # a broken oracle may raise instead of differ
+            out[pin.__name__] = ["raised %s: %s" % (type(exc).__name__, exc)]
+    return out
