@@ -51,8 +51,9 @@
  *     next synchronization, as for any HIP launch.
  *   - Arguments are validated on the host before anything is enqueued; a
  *     non-zero status means nothing was enqueued.
- *   - Sizes: M, N, K >= 0 and K % 128 == 0.  M == 0 or N == 0 enqueues
- *     nothing (pointers may then be NULL).  K == 0 makes every output 0.
+ *   - Sizes: 0 <= M, N <= 2^24, 0 <= K < 2^31, K % 128 == 0.  M == 0 or
+ *     N == 0 enqueues nothing (pointers may then be NULL).  K == 0 makes
+ *     every output 0 (the inputs, which then hold no bytes, may be NULL).
  *   - Alignment: W, X, x and packed must be 16-byte aligned; scales, Y and
  *     y 2-byte aligned.
  *   - Outputs must not overlap any input.

@@ -1,0 +1,139 @@
+"""C ABI on the host: the library loads, exports every declared symbol, and
+validates arguments before touching a device (no kernel is launched here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from weight_only_int4_gemv_amd import w4a16
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4a16.h")
+
+OK, INVALID, SHAPE, MISALIGNED, DEVICE = 0, 1, 2, 3, 4
+FAKE = 0x10000  # 64 KiB-aligned host address; only ever rejected before use
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*[\w\s\*]+?\b(w4a16_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(w4a16.LIBRARY):
+        from weight_only_int4_gemv_amd import build
+        build.build()
+    return w4a16.library()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for fn in ["w4a16_quantize", "w4a16_gemv", "w4a16_gemm", "w4a16_gemm_ex",
+               "w4a16_packed_bytes", "w4a16_scales_bytes", "w4a16_status_string",
+               "w4a16_valu_max_m"]:
+        assert fn in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", w4a16.LIBRARY], check=True,
+                         capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (w4a16_\w+)$", out, re.M))
+    for fn in declared_functions():
+        assert fn in exported, fn
+        assert hasattr(lib, fn)
+
+
+def test_no_torch_types_in_header():
+    text = open(HEADER).read()
+    assert "torch" not in text and "at::" not in text and "hip_runtime" not in text
+
+
+def test_size_helpers(lib):
+    assert lib.w4a16_packed_bytes(4096, 4096) == 4096 * 4096 // 2
+    assert lib.w4a16_scales_bytes(4096, 4096) == 4096 * 32 * 2
+    assert lib.w4a16_packed_bytes(14336, 4096) * 2 == 4096 * 14336
+    # 2 bytes of scale per 64 bytes of codes: 3.125 %
+    assert lib.w4a16_scales_bytes(512, 1024) * 32 == lib.w4a16_packed_bytes(512, 1024)
+    assert lib.w4a16_packed_bytes(4, 100) == 0       # K % 128 != 0
+    assert lib.w4a16_packed_bytes(-1, 128) == 0
+    assert lib.w4a16_scales_bytes(4, -128) == 0
+
+
+def test_status_strings(lib):
+    for st in range(6):
+        assert len(w4a16.status_string(st)) >= 2
+    assert w4a16.status_string(99) == "unknown status"
+
+
+def test_quantize_validation(lib):
+    q = lib.w4a16_quantize
+    assert q(FAKE, 4, 100, FAKE, FAKE, None) == SHAPE
+    assert q(FAKE, -4, 128, FAKE, FAKE, None) == INVALID
+    assert q(FAKE, 4, 1 << 31, FAKE, FAKE, None) == INVALID
+    assert q(FAKE, (1 << 24) + 1, 128, FAKE, FAKE, None) == INVALID
+    assert q(None, 4, 128, FAKE, FAKE, None) == INVALID
+    assert q(FAKE, 4, 128, None, FAKE, None) == INVALID
+    assert q(FAKE, 4, 128, FAKE, None, None) == INVALID
+    assert q(FAKE + 8, 4, 128, FAKE * 2, FAKE * 3, None) == MISALIGNED
+    assert q(FAKE, 4, 128, FAKE * 2 + 4, FAKE * 3, None) == MISALIGNED
+    assert q(FAKE, 4, 128, FAKE * 2, FAKE * 3 + 1, None) == MISALIGNED
+    # outputs overlapping the input or each other
+    assert q(FAKE, 4, 128, FAKE + 256, FAKE * 3, None) == INVALID
+    assert q(FAKE, 4, 128, FAKE * 2, FAKE * 2 + 32, None) == INVALID
+    # empty problems enqueue nothing and accept NULL
+    assert q(None, 0, 128, None, None, None) == OK
+    assert q(None, 5, 0, None, None, None) == OK
+
+
+def test_linear_validation(lib):
+    g = lib.w4a16_gemm_ex
+    A, B, C, D = FAKE, FAKE * 4, FAKE * 8, FAKE * 12
+    assert g(A, 2, B, C, 16, 100, D, 0, None) == SHAPE
+    assert g(A, -2, B, C, 16, 128, D, 0, None) == INVALID
+    assert g(A, 2, B, C, -16, 128, D, 0, None) == INVALID
+    assert g(A, 2, B, C, 16, 128, D, 7, None) == INVALID        # unknown algo
+    assert g(A, (1 << 24) + 1, B, C, 16, 128, D, 0, None) == INVALID
+    assert g(A, 2, B, C, (1 << 24) + 1, 128, D, 0, None) == INVALID
+    assert g(None, 2, B, C, 16, 128, D, 0, None) == INVALID
+    assert g(A, 2, None, C, 16, 128, D, 0, None) == INVALID
+    assert g(A, 2, B, None, 16, 128, D, 0, None) == INVALID
+    assert g(A, 2, B, C, 16, 128, None, 0, None) == INVALID
+    assert g(A + 2, 2, B, C, 16, 128, D, 0, None) == MISALIGNED
+    assert g(A, 2, B + 4, C, 16, 128, D, 0, None) == MISALIGNED
+    assert g(A, 2, B, C + 1, 16, 128, D, 0, None) == MISALIGNED
+    assert g(A, 2, B, C, 16, 128, D + 1, 0, None) == MISALIGNED
+    assert g(A, 2, B, C, 16, 128, A + 16, 0, None) == INVALID   # Y overlaps X
+    assert g(A, 2, B, C, 16, 128, B, 0, None) == INVALID        # Y overlaps packed
+    assert g(A, 2, B, C, 16, 128, C + 2, 0, None) == INVALID    # Y overlaps scales
+    assert g(None, 0, None, None, 16, 128, None, 0, None) == OK
+    assert g(None, 3, None, None, 0, 128, None, 0, None) == OK
+    gv = lib.w4a16_gemv
+    assert gv(A, B, C, 16, 130, D, None) == SHAPE
+    assert gv(A + 8, B, C, 16, 128, D, None) == MISALIGNED
+    assert gv(A, B, C, 0, 128, None, None) == OK
+
+
+@pytest.mark.skipif(__import__("torch").cuda.device_count() > 0,
+                    reason="with a GPU present valid arguments would launch")
+def test_valid_arguments_without_device_report_device_error(lib):
+    A, B, C, D = FAKE, FAKE * 4, FAKE * 8, FAKE * 12
+    assert lib.w4a16_gemm(A, 2, B, C, 16, 128, D, None) == DEVICE
+    assert lib.w4a16_quantize(A, 4, 128, B, C, None) == DEVICE
+
+
+def test_binding_rejects_bad_tensors():
+    import torch
+    W = torch.zeros(4, 128, dtype=torch.float16)          # on the CPU
+    with pytest.raises(ValueError):
+        w4a16.quantize(W)
+    with pytest.raises(ValueError):
+        w4a16.gemv(torch.zeros(128, dtype=torch.float16),
+                   torch.zeros(4, 16, dtype=torch.int32),
+                   torch.zeros(4, 1, dtype=torch.float16))
+    with pytest.raises(ValueError):
+        w4a16.gemm(torch.zeros(2, 128, dtype=torch.float32),
+                   torch.zeros(4, 16, dtype=torch.int32),
+                   torch.zeros(4, 1, dtype=torch.float16))

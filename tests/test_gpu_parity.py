@@ -1,0 +1,343 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Bar:
+  * packed codes and scales: bit-exact;
+  * outputs: |y - y_ref| <= 1e-3 * sum_k |x_k w_k| + 2^-10 |y_ref| per element;
+  * one-hot activations: bit-exact fp16(s*q).
+Inputs: seeded draws of weight_only_int4_gemv_amd.inputs (layer-like weights
+with 0.1 % outliers, N(0,1) activations).  Weights given to the linear
+kernels are the oracle's own packed codes and scales.
+"""
+import functools
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from weight_only_int4_gemv_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def say(msg):
+    print("[case] " + msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def w4():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    from weight_only_int4_gemv_amd import w4a16
+    w4a16.library()                       # must be built; no fallback
+    return w4a16
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.get()
+
+
+def dev(a: np.ndarray):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    return t.to("cuda")
+
+
+def packed_to_dev(p: np.ndarray):
+    return dev(p.view(np.int32))
+
+
+def scales_to_dev(s: np.ndarray):
+    return dev(s.view(np.float16))
+
+
+# ------------------------------------------------------------------ quantize
+
+def check_quantize(w4, orc, W: np.ndarray, name: str):
+    N, K = W.shape
+    say("quantize %s N=%d K=%d" % (name, N, K))
+    pg, sg = w4.quantize(dev(W))
+    torch.cuda.synchronize()
+    po, so = orc.quantize(W)
+    got_p = pg.cpu().numpy().view(np.uint32)
+    got_s = sg.cpu().numpy().view(np.uint16)
+    bad_s = np.argwhere(got_s != so)
+    assert bad_s.size == 0, "%s: %d scales differ, first at %s" % (name, len(bad_s), bad_s[0])
+    bad_p = np.argwhere(got_p != po)
+    assert bad_p.size == 0, "%s: %d words differ, first at %s (%#x vs %#x)" % (
+        name, len(bad_p), bad_p[0], got_p[tuple(bad_p[0])], po[tuple(bad_p[0])])
+
+
+@pytest.mark.parametrize("N,K,seed", [(1, 128, 1), (3, 256, 2), (37, 384, 3), (129, 1152, 4),
+                                      (4096, 4096, 0)])
+def test_quantize_bit_exact(w4, orc, N, K, seed):
+    W = inputs.weight(N, K, seed=seed)
+    check_quantize(w4, orc, W, "seed %d" % seed)
+
+
+@pytest.mark.parametrize("name,K,N", inputs.LLAMA3_8B[::3] + inputs.QWEN25_7B[4:]
+                         + inputs.FFN_70B)
+def test_quantize_bit_exact_layer_shapes(w4, orc, name, K, N):
+    W = inputs.weight(N, K, seed=inputs.matrix_seed(2, 0, K * 7 + N))
+    check_quantize(w4, orc, W, name)
+
+
+def test_quantize_every_fp16_absmax(w4, orc):
+    """One group per positive finite fp16 value a (absmax a, sign alternating,
+    the rest of the group a ramp below a): scale rounding, subnormal scales,
+    clamping and ties over the whole fp16 range."""
+    a_bits = np.arange(1, 0x7C00, dtype=np.uint16)
+    a = a_bits.view(np.float16).astype(np.float32)
+    ramp = np.linspace(-1.0, 1.0, 127, dtype=np.float32)
+    W = np.empty((a_bits.size, 128), dtype=np.float16)
+    W[:, 1:] = (a[:, None] * ramp[None, :]).astype(np.float16)
+    W[:, 0] = np.where(np.arange(a_bits.size) % 2 == 0, 1, -1) * a.astype(np.float16)
+    check_quantize(w4, orc, W, "every fp16 absmax")
+
+
+def test_quantize_hand_worked_groups(w4, orc):
+    import json
+    import oracle_pins
+    spec = json.load(open(oracle_pins.GOLDEN))
+    W = np.zeros((len(spec["groups"]), 128), dtype=np.float16)
+    for r, g in enumerate(spec["groups"]):
+        for k, v in g["nonzero"].items():
+            W[r, int(k)] = np.float16(v)
+    say("quantize hand-worked groups")
+    pg, sg = w4.quantize(dev(W))
+    got_p = pg.cpu().numpy().view(np.uint32)
+    got_s = sg.cpu().numpy().view(np.uint16)
+    for r, g in enumerate(spec["groups"]):
+        assert got_s[r, 0] == int(g["scale_bits"], 16), g["name"]
+        for j in range(16):
+            want = int(g["words"].get(str(j), g["words"]["rest"]), 16)
+            assert got_p[r, j] == want, (g["name"], j, hex(got_p[r, j]), hex(want))
+
+
+def test_quantize_edge_values(w4, orc):
+    rng = np.random.default_rng(77)
+    W = (rng.standard_normal((64, 512)) * 0.02).astype(np.float16)
+    W[0] = 0                                                  # all zero
+    W[1] = np.float16(-0.0)                                   # negative zeros
+    W[2, :128] = np.float16(65504.0)                          # largest fp16
+    W[2, 128:256] = np.float16(-65504.0)
+    W[3] = (rng.standard_normal(512) * 1e-6).astype(np.float16)   # subnormal scales
+    W[4, :128] = np.uint16(1).view(np.float16)               # smallest subnormal
+    W[5, :128] = np.uint16(3).view(np.float16)               # scale rounds to 0
+    W[5, 128:256] = np.uint16(4).view(np.float16)            # smallest non-zero scale
+    check_quantize(w4, orc, W, "edge values")
+
+
+def test_quantize_empty_and_deterministic(w4, orc):
+    say("quantize empty")
+    p, s = w4.quantize(torch.empty((0, 256), dtype=torch.float16, device="cuda"))
+    assert p.shape == (0, 32) and s.shape == (0, 2)
+    W = inputs.weight(300, 640, seed=12)
+    p1, s1 = w4.quantize(dev(W))
+    p2, s2 = w4.quantize(dev(W))
+    assert torch.equal(p1, p2) and torch.equal(s1, s2)
+
+
+# -------------------------------------------------------------------- linear
+
+def run_linear(w4, X16: np.ndarray, packed: np.ndarray, scales: np.ndarray, algo):
+    Xd = dev(X16)
+    if algo == "gemv":
+        return w4.gemv(Xd[0], packed_to_dev(packed), scales_to_dev(scales)).cpu().numpy()[None]
+    return w4.gemm(Xd, packed_to_dev(packed), scales_to_dev(scales), algo=algo).cpu().numpy()
+
+
+@functools.lru_cache(maxsize=3)
+def layer(N, K, wseed):
+    """(W, packed, scales) of one seeded layer, quantized by the oracle."""
+    W = inputs.weight(N, K, seed=list(wseed) if isinstance(wseed, tuple) else wseed)
+    packed, scales = oracle.get().quantize(W)
+    return W, packed, scales
+
+
+def check_linear(w4, orc, M, N, K, seed, algo, name="", full_limit=6e8):
+    """seed: (weight seed, activation seed) or one seed for both."""
+    say("linear %s M=%d N=%d K=%d algo=%s" % (name, M, N, K, algo))
+    wseed, xseed = seed if isinstance(seed, tuple) else (seed, [1000, seed] if isinstance(
+        seed, int) else [1000] + list(seed))
+    _, packed, scales = layer(N, K, tuple(wseed) if isinstance(wseed, list) else wseed)
+    X = inputs.activation(M, K, seed=xseed)
+    Y = run_linear(w4, X, packed, scales, algo)
+    torch.cuda.synchronize()
+    assert Y.shape == (M, N)
+    if M * N * K <= full_limit:
+        Yref, Yabs = orc.matmul(X, packed, scales)
+        got = Y.astype(np.float64)
+    else:
+        rng = np.random.default_rng(M * 1000003 + N * 7 + K)
+        cols = np.unique(np.concatenate([[0, N - 1], rng.integers(0, N, 96)]))
+        rows = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, 8)]))
+        rr, cc = np.meshgrid(rows, cols, indexing="ij")
+        ys, ya = orc.matmul_sampled(X, packed, scales, rr.ravel(), cc.ravel())
+        Yref, Yabs = ys.reshape(rr.shape), ya.reshape(rr.shape)
+        got = Y[rr, cc].astype(np.float64)
+    tol = oracle.tolerance(Yref, Yabs)
+    err = np.abs(got - Yref)
+    bad = np.argwhere(~(err <= tol))
+    assert bad.size == 0, "%s: %d outputs out of tolerance, first %s: got %r want %r tol %r" % (
+        name, len(bad), bad[0], got[tuple(bad[0])], Yref[tuple(bad[0])], tol[tuple(bad[0])])
+    return float((err / np.maximum(tol, 1e-30)).max())
+
+
+@pytest.mark.parametrize("N,K", [(1, 128), (7, 256), (37, 384), (300, 1152), (1000, 2048),
+                                 (2053, 4224)])
+@pytest.mark.parametrize("algo", ["gemv", "valu", "mfma"])
+def test_linear_m1_small_and_ragged(w4, orc, N, K, algo):
+    check_linear(w4, orc, 1, N, K, seed=[5, N, K], algo=algo)
+
+
+def test_gemv_config1_single_layer(w4, orc):
+    """4096 x 4096, M = 1, seed 0 (the single-layer case)."""
+    check_linear(w4, orc, 1, 4096, 4096, seed=0, algo="gemv", name="4096x4096")
+
+
+LAYER_SHAPES = [("llama " + n, K, N) for n, K, N in inputs.LLAMA3_8B] + \
+               [("llama qkv", 4096, 6144), ("llama gate_up", 4096, 28672)] + \
+               [("qwen " + n, K, N) for n, K, N in inputs.QWEN25_7B] + \
+               [("qwen qkv", 3584, 4608), ("qwen gate_up", 3584, 37888)] + \
+               [("70b gate_up", 8192, 28672)]
+
+
+@pytest.mark.parametrize("name,K,N", LAYER_SHAPES, ids=[s[0] for s in LAYER_SHAPES])
+def test_gemv_decode_layer_shapes(w4, orc, name, K, N):
+    check_linear(w4, orc, 1, N, K, seed=[2, 0, N * 7 + K], algo="gemv", name=name)
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 16, 32])
+@pytest.mark.parametrize("K,N", [(4096, 14336), (14336, 4096)])
+@pytest.mark.parametrize("algo", ["valu", "mfma", "auto"])
+def test_batched_decode_ffn(w4, orc, M, K, N, algo):
+    check_linear(w4, orc, M, N, K, seed=([4, K], [4, K, M]), algo=algo, name="ffn")
+
+
+@pytest.mark.parametrize("M", [2, 3, 9, 15, 16, 17, 31, 33, 48, 64, 65, 127, 129, 200])
+@pytest.mark.parametrize("algo", ["valu", "mfma"])
+def test_gemm_ragged_m(w4, orc, M, algo):
+    check_linear(w4, orc, M, 300, 640, seed=([6], [6, M]), algo=algo, name="ragged")
+
+
+@pytest.mark.parametrize("K,N", [(4096, 14336), (14336, 4096), (8192, 28672)])
+def test_prefill_512(w4, orc, K, N):
+    check_linear(w4, orc, 512, N, K, seed=[5, K, N], algo="auto", name="prefill")
+
+
+def test_70b_ffn_decode(w4, orc):
+    check_linear(w4, orc, 1, 28672, 8192, seed=[5, 1, 8192], algo="auto", name="70b m1")
+
+
+# -------------------------------------------------------------- exact cases
+
+@pytest.mark.parametrize("algo", ["gemv", "valu", "mfma"])
+def test_one_hot_activations_are_exact(w4, orc, algo):
+    """x = e_k reproduces fp16(s*q) of column k exactly, for every k of two
+    groups: checks nibble order, word order and scale indexing."""
+    N, K = 96, 256
+    W = inputs.weight(N, K, seed=21)
+    packed, scales = orc.quantize(W)
+    What = orc.dequantize(packed, scales)
+    want = What.astype(np.float16)                     # RNE of the exact s*q
+    for k0 in range(0, K, 64):
+        ks = list(range(k0, k0 + 64))
+        say("one-hot %s k=%d..%d" % (algo, ks[0], ks[-1]))
+        if algo == "gemv":
+            rows = []
+            for k in ks:
+                x = np.zeros((1, K), dtype=np.float16)
+                x[0, k] = 1
+                rows.append(run_linear(w4, x, packed, scales, "gemv")[0])
+            Y = np.stack(rows)
+        else:
+            X = np.zeros((len(ks), K), dtype=np.float16)
+            X[np.arange(len(ks)), ks] = 1
+            Y = run_linear(w4, X, packed, scales, algo)
+        np.testing.assert_array_equal(Y.view(np.uint16), want[:, ks].T.view(np.uint16))
+
+
+@pytest.mark.parametrize("algo", ["gemv", "valu", "mfma"])
+def test_scaled_identity(w4, orc, algo):
+    """W = c I with c = 7 * 2^-6: s = 2^-6, q = 7 on the diagonal, so
+    y = c x within tolerance."""
+    K = 512
+    W = np.zeros((K, K), dtype=np.float16)
+    W[np.arange(K), np.arange(K)] = np.float16(0.109375)
+    packed, scales = orc.quantize(W)
+    X = inputs.activation(3 if algo != "gemv" else 1, K, seed=22)
+    say("scaled identity %s" % algo)
+    Y = run_linear(w4, X, packed, scales, algo).astype(np.float64)
+    want = 0.109375 * X.astype(np.float64)
+    tol = 1e-3 * np.abs(want) + 2.0 ** -10 * np.abs(want)
+    assert (np.abs(Y - want) <= tol).all()
+
+
+@pytest.mark.parametrize("algo", ["gemv", "valu", "mfma"])
+def test_k_zero_gives_zeros(w4, algo):
+    say("K=0 %s" % algo)
+    packed = torch.empty((5, 0), dtype=torch.int32, device="cuda")
+    scales = torch.empty((5, 0), dtype=torch.float16, device="cuda")
+    if algo == "gemv":
+        y = w4.gemv(torch.empty((0,), dtype=torch.float16, device="cuda"), packed, scales)
+    else:
+        y = w4.gemm(torch.empty((2, 0), dtype=torch.float16, device="cuda"), packed, scales,
+                    algo=algo)
+    assert torch.count_nonzero(y).item() == 0
+
+
+def test_empty_m_and_n(w4):
+    say("empty M / N")
+    packed = torch.zeros((4, 16), dtype=torch.int32, device="cuda")
+    scales = torch.zeros((4, 1), dtype=torch.float16, device="cuda")
+    Y = w4.gemm(torch.empty((0, 128), dtype=torch.float16, device="cuda"), packed, scales)
+    assert Y.shape == (0, 4)
+    Y = w4.gemm(torch.zeros((3, 128), dtype=torch.float16, device="cuda"),
+                torch.zeros((0, 16), dtype=torch.int32, device="cuda"),
+                torch.zeros((0, 1), dtype=torch.float16, device="cuda"))
+    assert Y.shape == (3, 0)
+
+
+@pytest.mark.parametrize("M,algo", [(1, "gemv"), (3, "valu"), (20, "mfma"), (130, "mfma")])
+def test_outputs_stay_inside_their_buffer(w4, orc, M, algo):
+    """Canary words around Y must survive (no out-of-bounds stores)."""
+    N, K = 333, 768
+    W, X = inputs.weight_and_activation(N, K, M, seed=[23, M])
+    packed, scales = orc.quantize(W)
+    pad = 4096
+    buf = torch.full((pad + M * N + pad,), float("nan"), dtype=torch.float16, device="cuda")
+    Y = buf[pad:pad + M * N].view(M, N)
+    say("canary %s M=%d" % (algo, M))
+    if algo == "gemv":
+        w4.gemv(dev(X)[0], packed_to_dev(packed), scales_to_dev(scales), y=Y[0])
+    else:
+        w4.gemm(dev(X), packed_to_dev(packed), scales_to_dev(scales), algo=algo, Y=Y)
+    b = buf.cpu().numpy().view(np.uint16)
+    nan_bits = np.float16("nan").view(np.uint16)
+    assert (b[:pad] == nan_bits).all() and (b[pad + M * N:] == nan_bits).all()
+    assert not np.isnan(buf[pad:pad + M * N].cpu().numpy()).any()
+
+
+@pytest.mark.parametrize("M,algo", [(1, "gemv"), (8, "valu"), (32, "mfma"), (512, "mfma")])
+def test_deterministic_and_stream_ordered(w4, orc, M, algo):
+    N, K = 2048, 2048
+    W, X = inputs.weight_and_activation(N, K, M, seed=[24, M])
+    packed, scales = orc.quantize(W)
+    pd, sd, Xd = packed_to_dev(packed), scales_to_dev(scales), dev(X)
+    say("determinism %s M=%d" % (algo, M))
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for s in (torch.cuda.current_stream(), side, side):
+        with torch.cuda.stream(s):
+            if algo == "gemv":
+                outs.append(w4.gemv(Xd[0], pd, sd)[None])
+            else:
+                outs.append(w4.gemm(Xd, pd, sd, algo=algo))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[1], outs[2])

@@ -1,0 +1,157 @@
+// api.hip — the C ABI of include/w4a16.h: host-side validation, device
+// checks and dispatch to the kernels.  Nothing here allocates device memory.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <string.h>
+
+#include "w4a16.h"
+#include "w4a16_launch.h"
+
+namespace {
+
+// Launch grids stay within the dispatch limits for M, N <= 2^24; kernels
+// index K with int.
+constexpr int64_t kMaxRows = (int64_t)1 << 24;
+constexpr int64_t kMaxK = ((int64_t)1 << 31) - 128;
+
+// Largest M sent to the VALU path by W4A16_ALGO_AUTO.
+constexpr int64_t kValuMaxM = 8;
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+// [p, p + bytes) and [q, q + qbytes) intersect (both non-empty).
+bool overlap(const void* p, size_t bytes, const void* q, size_t qbytes) {
+    if (bytes == 0 || qbytes == 0) return false;
+    const uintptr_t a = (uintptr_t)p, b = (uintptr_t)q;
+    return a < b + qbytes && b < a + bytes;
+}
+
+// Per-device facts, filled on first use of each device.
+struct DeviceInfo {
+    bool probed = false;
+    bool ok = false;
+    int num_cu = 0;
+};
+constexpr int kMaxDevices = 64;
+DeviceInfo g_devices[kMaxDevices];
+std::mutex g_mutex;
+
+int current_device(int* num_cu) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return W4A16_ERR_DEVICE;
+    std::lock_guard<std::mutex> lock(g_mutex);
+    DeviceInfo& d = g_devices[dev];
+    if (!d.probed) {
+        hipDeviceProp_t prop;
+        d.probed = true;
+        if (hipGetDeviceProperties(&prop, dev) == hipSuccess) {
+            d.ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+            d.num_cu = prop.multiProcessorCount;
+        }
+    }
+    if (!d.ok) return W4A16_ERR_DEVICE;
+    *num_cu = d.num_cu;
+    return W4A16_OK;
+}
+
+int check_sizes(int64_t M, int64_t N, int64_t K) {
+    if (M < 0 || N < 0 || K < 0) return W4A16_ERR_INVALID_ARG;
+    if (M > kMaxRows || N > kMaxRows || K > kMaxK) return W4A16_ERR_INVALID_ARG;
+    if (K % W4A16_GROUP != 0) return W4A16_ERR_SHAPE;
+    return W4A16_OK;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH; }
+
+int linear(const uint16_t* X, int64_t M, const uint32_t* packed, const uint16_t* scales,
+           int64_t N, int64_t K, uint16_t* Y, int algo, void* stream) {
+    int st = check_sizes(M, N, K);
+    if (st != W4A16_OK) return st;
+    if (algo != W4A16_ALGO_AUTO && algo != W4A16_ALGO_VALU && algo != W4A16_ALGO_MFMA)
+        return W4A16_ERR_INVALID_ARG;
+    if (M == 0 || N == 0) return W4A16_OK;
+    // With K == 0 the inputs hold no bytes and may be NULL; they are never read.
+    if (!Y || (K > 0 && (!X || !packed || !scales))) return W4A16_ERR_INVALID_ARG;
+    if (!aligned(X, 16) || !aligned(packed, 16) || !aligned(scales, 2) || !aligned(Y, 2))
+        return W4A16_ERR_MISALIGNED;
+    const size_t y_bytes = (size_t)M * N * 2;
+    if (overlap(Y, y_bytes, X, (size_t)M * K * 2) ||
+        overlap(Y, y_bytes, packed, (size_t)N * K / 2) ||
+        overlap(Y, y_bytes, scales, (size_t)N * (K / W4A16_GROUP) * 2))
+        return W4A16_ERR_INVALID_ARG;
+    int num_cu = 0;
+    st = current_device(&num_cu);
+    if (st != W4A16_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool valu = algo == W4A16_ALGO_VALU || (algo == W4A16_ALGO_AUTO && M <= kValuMaxM);
+    if (valu) return status_of(w4a16::launch_gemv_valu(X, M, packed, scales, N, K, Y, s, num_cu));
+    return status_of(w4a16::launch_gemm_mfma(X, M, packed, scales, N, K, Y, s, num_cu));
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t w4a16_packed_bytes(int64_t N, int64_t K) {
+    if (check_sizes(0, N, K) != W4A16_OK) return 0;
+    return (size_t)N * (size_t)K / 2;
+}
+
+size_t w4a16_scales_bytes(int64_t N, int64_t K) {
+    if (check_sizes(0, N, K) != W4A16_OK) return 0;
+    return (size_t)N * (size_t)(K / W4A16_GROUP) * 2;
+}
+
+int w4a16_quantize(const uint16_t* W, int64_t N, int64_t K, uint32_t* packed, uint16_t* scales,
+                   void* stream) {
+    int st = check_sizes(0, N, K);
+    if (st != W4A16_OK) return st;
+    if (N == 0 || K == 0) return W4A16_OK;
+    if (!W || !packed || !scales) return W4A16_ERR_INVALID_ARG;
+    if (!aligned(W, 16) || !aligned(packed, 16) || !aligned(scales, 2))
+        return W4A16_ERR_MISALIGNED;
+    const size_t w_bytes = (size_t)N * K * 2;
+    const size_t p_bytes = (size_t)N * K / 2;
+    const size_t s_bytes = (size_t)N * (K / W4A16_GROUP) * 2;
+    if (overlap(packed, p_bytes, W, w_bytes) || overlap(scales, s_bytes, W, w_bytes) ||
+        overlap(packed, p_bytes, scales, s_bytes))
+        return W4A16_ERR_INVALID_ARG;
+    int num_cu = 0;
+    st = current_device(&num_cu);
+    if (st != W4A16_OK) return st;
+    return status_of(w4a16::launch_quantize(W, N, K, packed, scales,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+int w4a16_gemv(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, int64_t N,
+               int64_t K, uint16_t* y, void* stream) {
+    return linear(x, 1, packed, scales, N, K, y, W4A16_ALGO_VALU, stream);
+}
+
+int w4a16_gemm(const uint16_t* X, int64_t M, const uint32_t* packed, const uint16_t* scales,
+               int64_t N, int64_t K, uint16_t* Y, void* stream) {
+    return linear(X, M, packed, scales, N, K, Y, W4A16_ALGO_AUTO, stream);
+}
+
+int w4a16_gemm_ex(const uint16_t* X, int64_t M, const uint32_t* packed, const uint16_t* scales,
+                  int64_t N, int64_t K, uint16_t* Y, int algo, void* stream) {
+    return linear(X, M, packed, scales, N, K, Y, algo, stream);
+}
+
+int64_t w4a16_valu_max_m(void) { return kValuMaxM; }
+
+const char* w4a16_status_string(int status) {
+    switch (status) {
+        case W4A16_OK: return "ok";
+        case W4A16_ERR_INVALID_ARG: return "invalid argument (null pointer, negative or too large size, overlapping output, unknown algo)";
+        case W4A16_ERR_SHAPE: return "K must be a multiple of 128";
+        case W4A16_ERR_MISALIGNED: return "misaligned pointer (W, X, x, packed need 16 bytes; scales, Y, y need 2)";
+        case W4A16_ERR_DEVICE: return "no HIP device, or the current device is not gfx950";
+        case W4A16_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,243 @@
+// gemm_mfma.hip — W4A16 GEMM on the gfx950 matrix cores (batched decode,
+// M >= 16, and prefill, [BENCH] §一 512-token prompt, §二 prefill latency).
+//
+// Y[m,n] = sum_k X[m,k] * fp16(s[n,k/128] * q[n,k]), fp32 accumulation in
+// v_mfma_f32_16x16x32_f16, fp16 output.
+//
+// Operand mapping of v_mfma_f32_16x16x32_f16 (lane l, j = l/16):
+//   A (16 x 32): row l%16, eight k values of slot j
+//   B (32 x 16): column l%16, eight k values of slot j
+//   D (16 x 16): rows 4j..4j+3 of column l%16
+// The contraction does not depend on which k a slot holds as long as A and
+// B agree, so a lane's B operand for the four k-steps of a 128-wide group is
+// one 16-byte load of its row: words 4j..4j+3 (elements 32j .. 32j+31), word
+// 4j+kk feeding k-step kk.  The word is dequantized in registers to
+// fp16(s*q) in the paired order of dequant_word(), and A is staged in LDS in
+// the same paired order (pair_block), so no B tile passes through LDS.
+//
+// Block: 4 waves as WM x WN x WK.  A wave computes a (16 TM) x (16 TN) tile;
+// WK > 1 splits the groups of K over waves (for few output tiles) and the
+// partial tiles are summed through LDS at the end.  The next group's A
+// slices and B words are loaded into registers while the current one is
+// multiplied.
+// Precision: fp16(s*q) has relative error <= 2^-11, so |y - y_exact| <=
+// 2^-11 sum |x w| plus fp32 accumulation error, inside the 1e-3 sum |x w|
+// allowance for every K.
+#include "w4a16_device.h"
+#include "w4a16_launch.h"
+
+namespace w4a16 {
+
+namespace {
+constexpr int kLdaHalfs = 136;             // staged A row: 128 halves + 8 pad (bank spread)
+constexpr int kLdaVec = kLdaHalfs / 8;     // in uint4
+}  // namespace
+
+template <int TM, int TN, int WM, int WN, int WK>
+__global__ __launch_bounds__(256) void gemm_mfma_kernel(
+    const uint16_t* __restrict__ X, int M, const uint4* __restrict__ packed,
+    const uint16_t* __restrict__ scales, uint16_t* __restrict__ Y, int N, int K) {
+    static_assert(WM * WN * WK == 4, "four waves per block");
+    constexpr int BM = 16 * TM * WM;
+    constexpr int BN = 16 * TN * WN;
+    constexpr int A_VECS = WK * BM * 16;              // uint4 of A per stage (WK groups)
+    constexpr int A_PER_THREAD = (A_VECS + 255) / 256;
+    extern __shared__ uint4 lds[];                    // [WK][BM][kLdaVec]
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int wk = wave % WK;
+    const int wn = (wave / WK) % WN;
+    const int wm = wave / (WK * WN);
+    const int l16 = lane & 15;
+    const int j = lane >> 4;
+    const int m_blk = blockIdx.y * BM;
+    const int n_blk = blockIdx.x * BN;
+    const int ngroups = K >> 7;
+    const int nchunks = K >> 5;
+    const int nsteps = (ngroups + WK - 1) / WK;
+
+    int brow[TN];
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) brow[tn] = min(n_blk + (wn * TN + tn) * 16 + l16, N - 1);
+
+    // A staging: element e of the stage is (group slot, row, 8-block)
+    auto load_a = [&](int step, uint4 (&regs)[A_PER_THREAD]) {
+#pragma unroll
+        for (int i = 0; i < A_PER_THREAD; ++i) {
+            const int e = threadIdx.x + i * 256;
+            regs[i] = make_uint4(0, 0, 0, 0);
+            if (e < A_VECS) {
+                const int slot = e / (BM * 16);
+                const int rem = e - slot * BM * 16;
+                const int row = rem >> 4;
+                const int blk = rem & 15;
+                const int g = step * WK + slot;
+                const int m = m_blk + row;
+                if (g < ngroups && m < M)
+                    regs[i] = reinterpret_cast<const uint4*>(X + (size_t)m * K)[g * 16 + blk];
+            }
+        }
+    };
+    auto store_a = [&](const uint4 (&regs)[A_PER_THREAD]) {
+#pragma unroll
+        for (int i = 0; i < A_PER_THREAD; ++i) {
+            const int e = threadIdx.x + i * 256;
+            if (e < A_VECS) {
+                const int slot = e / (BM * 16);
+                const int rem = e - slot * BM * 16;
+                const int row = rem >> 4;
+                const int blk = rem & 15;
+                const uint4 v = regs[i];
+                lds[(slot * BM + row) * kLdaVec + blk] = pair_block(v.x, v.y, v.z, v.w);
+            }
+        }
+    };
+    auto load_b = [&](int step, uint4 (&bw)[TN], uint32_t (&bs)[TN]) {
+        const int g = step * WK + wk;
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+            if (g < ngroups) {
+                bw[tn] = packed[(size_t)brow[tn] * nchunks + g * 4 + j];
+                bs[tn] = scales[(size_t)brow[tn] * ngroups + g];
+            } else {
+                bw[tn] = make_uint4(0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u);
+                bs[tn] = 0;
+            }
+        }
+    };
+
+    float4_t acc[TM][TN];
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = (float4_t){0.f, 0.f, 0.f, 0.f};
+
+    uint4 a_regs[A_PER_THREAD];
+    uint4 bw[TN], bw_next[TN];
+    uint32_t bs[TN], bs_next[TN];
+    load_a(0, a_regs);
+    load_b(0, bw, bs);
+
+    for (int step = 0; step < nsteps; ++step) {
+        store_a(a_regs);
+        __syncthreads();
+        if (step + 1 < nsteps) {
+            load_a(step + 1, a_regs);
+            load_b(step + 1, bw_next, bs_next);
+        }
+        // B fragments of this wave's group: [tn][kk]
+        half8_t bf[TN][4];
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+            const _Float16 sh = __builtin_bit_cast(_Float16, (uint16_t)bs[tn]);
+            const half2_t s2 = {sh, sh};
+            const uint32_t words[4] = {bw[tn].x, bw[tn].y, bw[tn].z, bw[tn].w};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                half2_t h[4];
+                dequant_word(words[kk], s2, h);
+                bf[tn][kk] = (half8_t){h[0].x, h[0].y, h[1].x, h[1].y,
+                                       h[2].x, h[2].y, h[3].x, h[3].y};
+            }
+        }
+        const uint4* abase = lds + (wk * BM + wm * TM * 16 + l16) * kLdaVec + 4 * j;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+            for (int tm = 0; tm < TM; ++tm) {
+                const uint4 av = abase[tm * 16 * kLdaVec + kk];
+                const half8_t af = __builtin_bit_cast(half8_t, av);
+#pragma unroll
+                for (int tn = 0; tn < TN; ++tn)
+                    acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[tn][kk],
+                                                                         acc[tm][tn], 0, 0, 0);
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+            bw[tn] = bw_next[tn];
+            bs[tn] = bs_next[tn];
+        }
+    }
+
+    if constexpr (WK > 1) {
+        // Sum the WK partial tiles: waves wk > 0 publish, wave wk == 0 adds.
+        float4_t* red = reinterpret_cast<float4_t*>(lds);
+        const int tile = wm * WN + wn;
+        if (wk > 0) {
+#pragma unroll
+            for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+                for (int tn = 0; tn < TN; ++tn)
+                    red[(((wk - 1) * WM * WN + tile) * TM * TN + tm * TN + tn) * 64 + lane] =
+                        acc[tm][tn];
+        }
+        __syncthreads();
+        if (wk > 0) return;
+#pragma unroll
+        for (int w = 1; w < WK; ++w)
+#pragma unroll
+            for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+                for (int tn = 0; tn < TN; ++tn)
+                    acc[tm][tn] += red[(((w - 1) * WM * WN + tile) * TM * TN + tm * TN + tn) * 64 +
+                                       lane];
+    }
+
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+            const int n = n_blk + (wn * TN + tn) * 16 + l16;
+            if (n >= N) continue;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = m_blk + (wm * TM + tm) * 16 + 4 * j + r;
+                if (m < M) Y[(size_t)m * N + n] = f32_to_f16_bits(acc[tm][tn][r]);
+            }
+        }
+    }
+}
+
+namespace {
+
+template <int TM, int TN, int WM, int WN, int WK>
+hipError_t launch_mfma_t(const uint16_t* X, int64_t M, const uint32_t* packed,
+                         const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y,
+                         hipStream_t stream) {
+    constexpr int BM = 16 * TM * WM;
+    constexpr int BN = 16 * TN * WN;
+    const size_t a_bytes = (size_t)WK * BM * kLdaVec * sizeof(uint4);
+    const size_t red_bytes = (size_t)(WK - 1) * WM * WN * TM * TN * 64 * sizeof(float4_t);
+    const size_t lds = a_bytes > red_bytes ? a_bytes : red_bytes;
+    const dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM));
+    hipLaunchKernelGGL((gemm_mfma_kernel<TM, TN, WM, WN, WK>), grid, dim3(256), lds, stream, X,
+                       (int)M, reinterpret_cast<const uint4*>(packed), scales, Y, (int)N,
+                       (int)K);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm_mfma(const uint16_t* X, int64_t M, const uint32_t* packed,
+                            const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y,
+                            hipStream_t stream, int num_cu) {
+    // Few rows: one 16- or 32-row tile, waves split K; enough column tiles
+    // to give every compute unit work.
+    if (M <= 16) {
+        if (N >= (int64_t)64 * num_cu)
+            return launch_mfma_t<1, 2, 1, 1, 4>(X, M, packed, scales, N, K, Y, stream);
+        return launch_mfma_t<1, 1, 1, 1, 4>(X, M, packed, scales, N, K, Y, stream);
+    }
+    if (M <= 32) {
+        if (N >= (int64_t)64 * num_cu)
+            return launch_mfma_t<2, 2, 1, 1, 4>(X, M, packed, scales, N, K, Y, stream);
+        return launch_mfma_t<2, 1, 1, 1, 4>(X, M, packed, scales, N, K, Y, stream);
+    }
+    if (M <= 64) return launch_mfma_t<2, 2, 2, 2, 1>(X, M, packed, scales, N, K, Y, stream);
+    return launch_mfma_t<4, 4, 2, 2, 1>(X, M, packed, scales, N, K, Y, stream);
+}
+
+}  // namespace w4a16

@@ -1,0 +1,167 @@
+"""Python binding of ``libw4a16.so`` (the C ABI in include/w4a16.h).
+
+Argument marshalling only: torch supplies device memory and the current
+stream; every step of the computation runs in the library's HIP kernels.
+There is no fallback: a missing library or a non-gfx950 device is an error.
+
+    packed, scales = quantize(W)            # W: fp16 [N, K] on the GPU
+    y = gemv(x, packed, scales)             # x: fp16 [K]      -> [N]
+    Y = gemm(X, packed, scales)             # X: fp16 [M, K]   -> [M, N]
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LIBRARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw4a16.so")
+
+W4A16_GROUP = 128
+ALGO_AUTO, ALGO_VALU, ALGO_MFMA = 0, 1, 2
+_ALGOS = {None: ALGO_AUTO, "auto": ALGO_AUTO, "valu": ALGO_VALU, "mfma": ALGO_MFMA}
+
+_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_lib = None
+
+
+class W4A16Error(RuntimeError):
+    """A non-zero status from the library."""
+
+    def __init__(self, fn: str, status: int):
+        super().__init__("%s failed: status %d (%s)" % (fn, status, status_string(status)))
+        self.status = status
+
+
+def library() -> ctypes.CDLL:
+    """The loaded library (loaded on first use; raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIBRARY):
+            raise ImportError("%s is not built: run python -m weight_only_int4_gemv_amd.build"
+                              % LIBRARY)
+        lib = ctypes.CDLL(LIBRARY)
+        lib.w4a16_packed_bytes.argtypes = [_i64, _i64]
+        lib.w4a16_packed_bytes.restype = ctypes.c_size_t
+        lib.w4a16_scales_bytes.argtypes = [_i64, _i64]
+        lib.w4a16_scales_bytes.restype = ctypes.c_size_t
+        lib.w4a16_quantize.argtypes = [_p, _i64, _i64, _p, _p, _p]
+        lib.w4a16_gemv.argtypes = [_p, _p, _p, _i64, _i64, _p, _p]
+        lib.w4a16_gemm.argtypes = [_p, _i64, _p, _p, _i64, _i64, _p, _p]
+        lib.w4a16_gemm_ex.argtypes = [_p, _i64, _p, _p, _i64, _i64, _p, ctypes.c_int, _p]
+        for f in (lib.w4a16_quantize, lib.w4a16_gemv, lib.w4a16_gemm, lib.w4a16_gemm_ex):
+            f.restype = ctypes.c_int
+        lib.w4a16_valu_max_m.restype = ctypes.c_int64
+        lib.w4a16_status_string.argtypes = [ctypes.c_int]
+        lib.w4a16_status_string.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return library().w4a16_status_string(int(status)).decode()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise W4A16Error(fn, status)
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise ValueError("%s must be a torch.Tensor" % name)
+    if t.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on the GPU, got %s" % (name, t.device))
+    if t.dim() != ndim:
+        raise ValueError("%s must have %d dims, got shape %s" % (name, ndim, tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def packed_bytes(N: int, K: int) -> int:
+    return library().w4a16_packed_bytes(N, K)
+
+
+def scales_bytes(N: int, K: int) -> int:
+    return library().w4a16_scales_bytes(N, K)
+
+
+def quantize(W: torch.Tensor, packed: torch.Tensor = None, scales: torch.Tensor = None):
+    """W fp16 [N, K] -> (packed int32 [N, K/8] holding uint32 words, scales fp16 [N, K/128])."""
+    lib = library()
+    _need(W, "W", torch.float16, 2)
+    N, K = W.shape
+    if K % W4A16_GROUP:
+        raise ValueError("K = %d is not a multiple of %d" % (K, W4A16_GROUP))
+    if packed is None:
+        packed = torch.empty((N, K // 8), dtype=torch.int32, device=W.device)
+    if scales is None:
+        scales = torch.empty((N, K // W4A16_GROUP), dtype=torch.float16, device=W.device)
+    _need(packed, "packed", torch.int32, 2)
+    _need(scales, "scales", torch.float16, 2)
+    if tuple(packed.shape) != (N, K // 8) or tuple(scales.shape) != (N, K // W4A16_GROUP):
+        raise ValueError("output shapes do not match W")
+    _check("w4a16_quantize", lib.w4a16_quantize(W.data_ptr(), N, K, packed.data_ptr(),
+                                                scales.data_ptr(), _stream()))
+    return packed, scales
+
+
+def _weights(packed: torch.Tensor, scales: torch.Tensor):
+    _need(packed, "packed", torch.int32, 2)
+    _need(scales, "scales", torch.float16, 2)
+    N, K = packed.shape[0], packed.shape[1] * 8
+    if tuple(scales.shape) != (N, K // W4A16_GROUP):
+        raise ValueError("scales shape %s does not match packed %s"
+                         % (tuple(scales.shape), tuple(packed.shape)))
+    return N, K
+
+
+def gemv(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,
+         y: torch.Tensor = None) -> torch.Tensor:
+    """x fp16 [K] -> y fp16 [N] (decode GEMV, M = 1)."""
+    lib = library()
+    N, K = _weights(packed, scales)
+    _need(x, "x", torch.float16, 1)
+    if x.shape[0] != K:
+        raise ValueError("x has %d elements, K = %d" % (x.shape[0], K))
+    if y is None:
+        y = torch.empty((N,), dtype=torch.float16, device=x.device)
+    _need(y, "y", torch.float16, 1)
+    if y.shape[0] != N:
+        raise ValueError("y has %d elements, N = %d" % (y.shape[0], N))
+    _check("w4a16_gemv", lib.w4a16_gemv(x.data_ptr(), packed.data_ptr(), scales.data_ptr(), N, K,
+                                        y.data_ptr(), _stream()))
+    return y
+
+
+def gemm(X: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, algo=None,
+         Y: torch.Tensor = None) -> torch.Tensor:
+    """X fp16 [M, K] -> Y fp16 [M, N].  algo: None/'auto', 'valu' or 'mfma'."""
+    lib = library()
+    N, K = _weights(packed, scales)
+    _need(X, "X", torch.float16, 2)
+    M = X.shape[0]
+    if X.shape[1] != K:
+        raise ValueError("X has %d columns, K = %d" % (X.shape[1], K))
+    if algo not in _ALGOS:
+        raise ValueError("algo must be one of %s" % sorted(k for k in _ALGOS if k))
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float16, device=X.device)
+    _need(Y, "Y", torch.float16, 2)
+    if tuple(Y.shape) != (M, N):
+        raise ValueError("Y shape %s, want %s" % (tuple(Y.shape), (M, N)))
+    _check("w4a16_gemm_ex", lib.w4a16_gemm_ex(X.data_ptr(), M, packed.data_ptr(),
+                                              scales.data_ptr(), N, K, Y.data_ptr(),
+                                              _ALGOS[algo], _stream()))
+    return Y
+
+
+def valu_max_m() -> int:
+    return library().w4a16_valu_max_m()
