@@ -4,25 +4,23 @@
 // fp16 output ([BENCH] §二: decode streams every weight once and is
 // memory-bound; §五: dequantize on the fly in registers, never in memory).
 //
-// Design for gfx950 (HBM3E-bound streaming, VALU kept well below its limit):
+// Design for gfx950 (HBM3E-bound streaming, VALU kept below its limit):
 //   - Activations are staged once per block into LDS, in the paired order of
-//     pair_block(), with two per-chunk offsets that remove the +8 of the
-//     codes (see dot_word_nibbles).  Slices of K are staged in turn when
-//     M * K does not fit the LDS budget.
+//     pair_block().  Slices of K are staged in turn when M * K does not fit
+//     the LDS budget.
 //   - Each wave owns R consecutive rows.  Its 64 lanes walk K in 16-byte
 //     chunks (32 codes), lane l taking chunks l, l+64, ...: every load
 //     instruction of the wave reads R fully used, contiguous 1 KiB spans.
 //     U chunk steps of all R rows are loaded before any is consumed.
-//   - A chunk costs 4 shifts, 16 ANDs and 16 v_dot2_f32_f16 per row and per
-//     activation row: the nibble read as an fp16 subnormal is n * 2^-24 (or
-//     n * 2^-20 for the nibbles at bits 4-7), so no conversion instruction
-//     is needed.  Per chunk, one fma folds the two accumulators and one fma
-//     applies the group scale.
-//   - Partial sums are reduced across the wave with butterfly shuffles; the
-//     result (scaled back by 2^24) is rounded once to fp16.
-// Precision: the offsets are removed per 32-element chunk, so accumulated
-// magnitudes stay those of sum |q x| (codes <= 15 in magnitude, never the
-// 1032 of magic-number unpacking); a one-hot x is reproduced exactly.
+//   - A word of 8 codes costs one shift, four v_and_or_b32 and four packed
+//     fp16 add/fma to form the codes exactly in fp16 (codes_word), then four
+//     v_dot2_f32_f16 per activation row; per chunk one fma applies the group
+//     scale to the chunk's partial sum.
+//   - Partial sums are reduced across the wave with butterfly shuffles and
+//     the result is rounded once to fp16.
+// Precision: every product q*x is exact in fp32, so accumulation error is
+// relative to sum |q x| (within the 1e-3 sum |x w| allowance for every K);
+// a one-hot x reproduces fp16(s*q) exactly.
 #include "w4a16_device.h"
 #include "w4a16_launch.h"
 
@@ -36,25 +34,16 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
-// Stage activation rows [0, M) x elements [k0, k0 + ks) into LDS.
-//   xs[m * (ks/8) + b]   paired 8-element block b of the slice
-//   xb[m * (ks/32) + c]  (-8 * 2^-24 * lo-sum, -8 * 2^-20 * hi-sum) of chunk c
+// Stage activation rows [0, M) x elements [k0, k0 + ks) into LDS:
+//   xs[m * (ks/8) + b] = paired 8-element block b of the slice.
 __device__ __forceinline__ void stage_activations(const uint16_t* __restrict__ X, int M, int K,
-                                                  int k0, int ks, uint4* xs, float2* xb) {
-    const int nch = ks >> 5;
-    for (int i = threadIdx.x; i < M * nch; i += blockDim.x) {
-        const int m = i / nch;
-        const int c = i - m * nch;
-        const uint4* src = reinterpret_cast<const uint4*>(X + (size_t)m * K + k0) + c * 4;
-        uint4 p[4];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const uint4 v = src[b];
-            p[b] = pair_block(v.x, v.y, v.z, v.w);
-            xs[m * (ks >> 3) + c * 4 + b] = p[b];
-        }
-        const float2 sums = chunk_sums(p);
-        xb[m * nch + c] = make_float2(-8.0f * 0x1p-24f * sums.x, -8.0f * 0x1p-20f * sums.y);
+                                                  int k0, int ks, uint4* xs) {
+    const int nblk = ks >> 3;
+    for (int i = threadIdx.x; i < M * nblk; i += blockDim.x) {
+        const int m = i / nblk;
+        const int b = i - m * nblk;
+        const uint4 v = reinterpret_cast<const uint4*>(X + (size_t)m * K + k0)[b];
+        xs[m * nblk + b] = pair_block(v.x, v.y, v.z, v.w);
     }
 }
 
@@ -88,9 +77,8 @@ __global__ __launch_bounds__(WAVES * kWave) void gemv_kernel(
         const int c0 = k0 >> 5;          // first chunk of the slice
         const int nch = ks >> 5;
         uint4* xs = lds;
-        float2* xb = reinterpret_cast<float2*>(lds + MMAX * (kslice >> 3));
         if (k0 > 0) __syncthreads();     // previous slice fully consumed
-        stage_activations(X, M, K, k0, ks, xs, xb);
+        stage_activations(X, M, K, k0, ks, xs);
         __syncthreads();
 
         for (int cbase = lane; cbase < nch; cbase += U * kWave) {
@@ -116,16 +104,13 @@ __global__ __launch_bounds__(WAVES * kWave) void gemv_kernel(
                     if (m >= M) break;
                     const uint4* xp = xs + m * (ks >> 3) + c * 4;
                     const uint4 x0 = xp[0], x1 = xp[1], x2 = xp[2], x3 = xp[3];
-                    const float2 bias = xb[m * nch + c];
 #pragma unroll
                     for (int r = 0; r < R; ++r) {
-                        float lo = bias.x, hi = bias.y;
-                        dot_word_nibbles(w[u][r].x, x0, lo, hi);
-                        dot_word_nibbles(w[u][r].y, x1, lo, hi);
-                        dot_word_nibbles(w[u][r].z, x2, lo, hi);
-                        dot_word_nibbles(w[u][r].w, x3, lo, hi);
-                        // lo + 16 hi = 2^-24 * sum_k q_k x_k over the chunk
-                        acc[m][r] = fmaf(f16_bits_to_f32(sb[u][r]), fmaf(hi, 16.0f, lo), acc[m][r]);
+                        float part = dot_word(w[u][r].x, x0, 0.0f);
+                        part = dot_word(w[u][r].y, x1, part);
+                        part = dot_word(w[u][r].z, x2, part);
+                        part = dot_word(w[u][r].w, x3, part);
+                        acc[m][r] = fmaf(f16_bits_to_f32(sb[u][r]), part, acc[m][r]);
                     }
                 }
             }
@@ -138,7 +123,7 @@ __global__ __launch_bounds__(WAVES * kWave) void gemv_kernel(
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const float v = wave_sum(acc[m][r]);
-            if (lane == 0 && row0 + r < N) Y[(size_t)m * N + row0 + r] = f32_to_f16_bits(v * 0x1p24f);
+            if (lane == 0 && row0 + r < N) Y[(size_t)m * N + row0 + r] = f32_to_f16_bits(v);
         }
     }
 }
@@ -151,12 +136,11 @@ template <int MMAX, int R, int U, int WAVES>
 hipError_t launch_gemv_t(const uint16_t* X, int64_t M, const uint32_t* packed,
                          const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y,
                          hipStream_t stream) {
-    // LDS per activation element: 2 B of x plus 8 B of offsets per 32.
-    int64_t kslice = (int64_t)(kLdsBudget / (MMAX * 2.25)) / kGroup * kGroup;
+    // LDS: 2 bytes per activation element.
+    int64_t kslice = (int64_t)(kLdsBudget / (MMAX * 2)) / kGroup * kGroup;
     if (kslice > K) kslice = K;
     if (kslice < kGroup) kslice = kGroup;
-    const size_t lds = (size_t)MMAX * (kslice / 8) * sizeof(uint4) +
-                       (size_t)MMAX * (kslice / 32) * sizeof(float2);
+    const size_t lds = (size_t)MMAX * (kslice / 8) * sizeof(uint4);
     const int64_t rows_per_block = (int64_t)R * WAVES;
     const int64_t blocks = (N + rows_per_block - 1) / rows_per_block;
     hipLaunchKernelGGL((gemv_kernel<MMAX, R, U, WAVES>), dim3((unsigned)blocks),

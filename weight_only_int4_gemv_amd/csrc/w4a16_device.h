@@ -47,56 +47,45 @@ __device__ __forceinline__ uint4 pair_block(uint32_t x01, uint32_t x23, uint32_t
     return p;
 }
 
-// Sum of the activations a chunk pairs with low-nibble (bits 0-3 of each
-// byte) and high-nibble codes, from a chunk of 4 paired blocks.
-// Returns (sum over x0,x4,x2,x6 ; sum over x1,x5,x3,x7) of the 4 blocks.
-__device__ __forceinline__ float2 chunk_sums(const uint4 (&p)[4]) {
-    const half2_t one = {(_Float16)1.0f, (_Float16)1.0f};
-    float lo = 0.f, hi = 0.f;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        lo = __builtin_amdgcn_fdot2(as_h2(p[b].x), one, lo, false);
-        lo = __builtin_amdgcn_fdot2(as_h2(p[b].z), one, lo, false);
-        hi = __builtin_amdgcn_fdot2(as_h2(p[b].y), one, hi, false);
-        hi = __builtin_amdgcn_fdot2(as_h2(p[b].w), one, hi, false);
-    }
-    return make_float2(lo, hi);
-}
-
-// Dot product of one packed word (8 codes) with its paired activations,
-// codes taken as raw nibbles n = q + 8 read as fp16 subnormals:
-//   (w & 0x000F000F) is the half2 (n0, n4) * 2^-24,
-//   (w & 0x00F000F0) is the half2 (n1, n5) * 2^-20,
-// and the same for (w >> 8).  Two accumulators keep the two scalings:
-//   lo += 2^-24 * sum n x over nibbles 0,4,2,6;  hi += 2^-20 * sum over 1,5,3,7.
-// The offset 8 is removed once per chunk from the activation sums.
-__device__ __forceinline__ void dot_word_nibbles(uint32_t w, const uint4& xp, float& lo,
-                                                 float& hi) {
-    const uint32_t w8 = w >> 8;
-    lo = __builtin_amdgcn_fdot2(as_h2(w & 0x000F000Fu), as_h2(xp.x), lo, false);
-    hi = __builtin_amdgcn_fdot2(as_h2(w & 0x00F000F0u), as_h2(xp.y), hi, false);
-    lo = __builtin_amdgcn_fdot2(as_h2(w8 & 0x000F000Fu), as_h2(xp.z), lo, false);
-    hi = __builtin_amdgcn_fdot2(as_h2(w8 & 0x00F000F0u), as_h2(xp.w), hi, false);
-}
-
-// One packed word -> its 8 dequantized weights fp16(s*q) as 4 half2 in the
-// paired order (w0,w4),(w1,w5),(w2,w6),(w3,w7).  0x6400|n is the fp16 value
-// 1024+n, so (1024+n) - 1032 = n - 8 = q exactly; for the nibbles at bits
-// 4-7 the value is 1024+16n and (1024+16n)/16 - 72 = q exactly.  The final
-// product with the scale is rounded once (to nearest even).
-__device__ __forceinline__ void dequant_word(uint32_t w, half2_t s2, half2_t (&out)[4]) {
+// One packed word -> its 8 codes q = n - 8 as exact fp16 integers, in the
+// paired order (q0,q4),(q1,q5),(q2,q6),(q3,q7).  0x6400|n is the fp16 value
+// 1024+n, so (1024+n) - 1032 = q exactly; for the nibbles at bits 4-7 the
+// value is 1024+16n and (1024+16n)/16 - 72 = q exactly.  Costs one shift,
+// four v_and_or_b32 and four packed-fp16 add/fma.
+__device__ __forceinline__ void codes_word(uint32_t w, half2_t (&q)[4]) {
     const half2_t m1032 = {(_Float16)-1032.0f, (_Float16)-1032.0f};
     const half2_t inv16 = {(_Float16)0.0625f, (_Float16)0.0625f};
     const half2_t m72 = {(_Float16)-72.0f, (_Float16)-72.0f};
     const uint32_t w8 = w >> 8;
-    half2_t q0 = as_h2((w & 0x000F000Fu) | 0x64006400u) + m1032;
-    half2_t q1 = __builtin_elementwise_fma(as_h2((w & 0x00F000F0u) | 0x64006400u), inv16, m72);
-    half2_t q2 = as_h2((w8 & 0x000F000Fu) | 0x64006400u) + m1032;
-    half2_t q3 = __builtin_elementwise_fma(as_h2((w8 & 0x00F000F0u) | 0x64006400u), inv16, m72);
-    out[0] = q0 * s2;
-    out[1] = q1 * s2;
-    out[2] = q2 * s2;
-    out[3] = q3 * s2;
+    q[0] = as_h2((w & 0x000F000Fu) | 0x64006400u) + m1032;
+    q[1] = __builtin_elementwise_fma(as_h2((w & 0x00F000F0u) | 0x64006400u), inv16, m72);
+    q[2] = as_h2((w8 & 0x000F000Fu) | 0x64006400u) + m1032;
+    q[3] = __builtin_elementwise_fma(as_h2((w8 & 0x00F000F0u) | 0x64006400u), inv16, m72);
+}
+
+// acc += sum of the word's 8 products q*x (paired activations xp), each
+// product exact in fp32 (v_dot2_f32_f16), so the rounding error of the
+// accumulation is relative to sum |q x|.
+__device__ __forceinline__ float dot_word(uint32_t w, const uint4& xp, float acc) {
+    half2_t q[4];
+    codes_word(w, q);
+    acc = __builtin_amdgcn_fdot2(q[0], as_h2(xp.x), acc, false);
+    acc = __builtin_amdgcn_fdot2(q[1], as_h2(xp.y), acc, false);
+    acc = __builtin_amdgcn_fdot2(q[2], as_h2(xp.z), acc, false);
+    acc = __builtin_amdgcn_fdot2(q[3], as_h2(xp.w), acc, false);
+    return acc;
+}
+
+// One packed word -> its 8 dequantized weights fp16(s*q) as 4 half2 in the
+// paired order (w0,w4),(w1,w5),(w2,w6),(w3,w7): exact codes (codes_word)
+// times the scale, rounded once to nearest even.
+__device__ __forceinline__ void dequant_word(uint32_t w, half2_t s2, half2_t (&out)[4]) {
+    half2_t q[4];
+    codes_word(w, q);
+    out[0] = q[0] * s2;
+    out[1] = q[1] * s2;
+    out[2] = q[2] * s2;
+    out[3] = q[3] * s2;
 }
 
 }  // namespace w4a16
