@@ -2,9 +2,13 @@
 
 A step is one decode weight sweep of a LLaMA-3-8B-shaped model at M = 1:
 32 layers x (q 4096x4096, k 4096x1024, v 4096x1024, o 4096x4096,
-gate 4096x14336, up 4096x14336, down 14336x4096) = 224 launches of
-w4a16_gemv (shapes written K x N), every layer reading its own weights from
-HBM.  The sweep's launches are captured once in a HIP graph and replayed.
+gate 4096x14336, up 4096x14336, down 14336x4096) (shapes written K x N),
+every layer reading its own weights from HBM.  As serving engines store
+them, q/k/v and gate/up are concatenated along N (they share their input),
+so a layer is 4 launches of w4a16_gemv (qkv 4096x6144, o, gate_up
+4096x28672, down): 128 launches per sweep, the same bytes as 224 separate
+ones (also reported).  The sweep's launches are captured once in a HIP graph
+and replayed.
 
 Prints one JSON line: effective HBM GB/s of the sweep (algorithmic bytes
 N*K/2 + N*K/64 + 2K + 2N per GEMV over the measured time), us per sweep,
@@ -50,6 +54,8 @@ def parse():
     p.add_argument("--workload", default="llama3-8b-sweep", choices=sorted(WORKLOADS))
     p.add_argument("--mode", default="graph", choices=["graph", "eager"],
                    help="replay a captured HIP graph (default) or launch from Python")
+    p.add_argument("--layout", default="fused", choices=["fused", "separate"],
+                   help="qkv and gate_up concatenated (default) or 7 launches per layer")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-layers", type=int, default=16,
                    help="layers of the sweep the CPU oracle is timed on")
@@ -81,33 +87,58 @@ def main() -> int:
 
     # ---- weights: layer 0 drawn on the host, quantized on the GPU; layers
     # 1.. are device copies (each launch reads its own HBM; GEMV time does
-    # not depend on the values).
+    # not depend on the values).  Matrices sharing an input are stored
+    # concatenated along N.
     t0 = time.time()
+    names = [n for n, _, _ in shapes]
+    dims = {n: (K, N) for n, K, N in shapes}
+    fuse = [["q", "k", "v"], ["o"], ["gate", "up"], ["down"]] \
+        if names == ["q", "k", "v", "o", "gate", "up", "down"] else [[n] for n in names]
     host_w = {}
-    layer0 = []
-    for mid, (name, K, N) in enumerate(shapes):
-        W = inputs.weight(N, K, seed=inputs.matrix_seed(2, 0, mid))
-        host_w[name] = W
-        packed, scales = w4a16.quantize(torch.from_numpy(W).to(dev))
-        layer0.append((name, K, N, packed, scales))
+    layer0 = []   # (group name, K, N, packed, scales, [(member, row0, rows)])
+    for gi, group in enumerate(fuse):
+        K = dims[group[0]][0]
+        parts_p, parts_s, members, row0 = [], [], [], 0
+        for name in group:
+            mid = names.index(name)
+            N = dims[name][1]
+            W = inputs.weight(N, K, seed=inputs.matrix_seed(2, 0, mid))
+            host_w[name] = W
+            p, s_ = w4a16.quantize(torch.from_numpy(W).to(dev))
+            parts_p.append(p)
+            parts_s.append(s_)
+            members.append((name, row0, N))
+            row0 += N
+        layer0.append(("_".join(group), K, row0, torch.cat(parts_p), torch.cat(parts_s), members))
+        del parts_p, parts_s
     torch.cuda.synchronize()
-    weights = [layer0] + [[(n, K, N, p.clone(), s.clone()) for (n, K, N, p, s) in layer0]
+    weights = [layer0] + [[(g, K, N, p.clone(), s_.clone(), mem) for (g, K, N, p, s_, mem) in layer0]
                           for _ in range(nlayers - 1)]
     torch.cuda.synchronize()
     xs = {K: torch.from_numpy(inputs.activation(1, K, seed=[1000, 2, K])[0]).to(dev)
           for _, K, _ in shapes}
-    ys = {name: torch.empty((N,), dtype=torch.float16, device=dev) for name, _, N in shapes}
+    ys = {g: torch.empty((N,), dtype=torch.float16, device=dev) for (g, K, N, _, _, _) in layer0}
     setup_s = time.time() - t0
 
-    launches = [(xs[K], p, s, ys[n]) for layer in weights for (n, K, N, p, s) in layer]
-    step_bytes = sum(gemv_bytes(N, K) for layer in weights for (_, K, N, _, _) in layer)
-    weight_bytes = sum(p.numel() * 4 + s.numel() * 2 for layer in weights
-                       for (_, _, _, p, s) in layer)
+    fused_launches = [(xs[K], p, s_, ys[g]) for layer in weights for (g, K, N, p, s_, _) in layer]
+    separate_launches = [(xs[K], p[r0:r0 + n], s_[r0:r0 + n], ys[g][r0:r0 + n])
+                         for layer in weights for (g, K, N, p, s_, mem) in layer
+                         for (_, r0, n) in mem]
+    launches = fused_launches if args.layout == "fused" else separate_launches
+    step_bytes = sum(gemv_bytes(N, K) for layer in weights for (_, K, N, _, _, _) in layer) \
+        if args.layout == "fused" else \
+        sum(gemv_bytes(n, K) for layer in weights for (_, K, _, _, _, mem) in layer
+            for (_, _, n) in mem)
+    weight_bytes = sum(p.numel() * 4 + s_.numel() * 2 for layer in weights
+                       for (_, _, _, p, s_, _) in layer)
 
-    def step():
-        for x, p, s, y in launches:
-            w4a16.gemv(x, p, s, y=y)
+    def make_step(seq):
+        def step():
+            for x, p, s_, y in seq:
+                w4a16.gemv(x, p, s_, y=y)
+        return step
 
+    step = make_step(launches)
     stream = torch.cuda.current_stream()
     step()  # first call: device checks outside any capture
     torch.cuda.synchronize()
@@ -127,16 +158,17 @@ def main() -> int:
         run()
         torch.cuda.synchronize()
         worst = 0.0
-        for (name, K, N, p, s) in layer0:
-            po, so = orc.quantize(host_w[name])
-            assert np.array_equal(p.cpu().numpy().view(np.uint32), po), name
-            assert np.array_equal(s.cpu().numpy().view(np.uint16), so), name
+        for (g, K, N, p, s_, mem) in layer0:
+            po = np.concatenate([orc.quantize(host_w[name])[0] for name, _, _ in mem])
+            so = np.concatenate([orc.quantize(host_w[name])[1] for name, _, _ in mem])
+            assert np.array_equal(p.cpu().numpy().view(np.uint32), po), g
+            assert np.array_equal(s_.cpu().numpy().view(np.uint16), so), g
             x = xs[K].cpu().numpy()[None]
             yref, yabs = orc.matmul(x, po, so)
-            y = ys[name].cpu().numpy().astype(np.float64)[None]
+            y = ys[g].cpu().numpy().astype(np.float64)[None]
             tol = oracle.tolerance(yref, yabs)
             ratio = float((np.abs(y - yref) / tol).max())
-            assert ratio <= 1.0, "%s out of tolerance (%.3f)" % (name, ratio)
+            assert ratio <= 1.0, "%s out of tolerance (%.3f)" % (g, ratio)
             worst = max(worst, ratio)
         parity = {"layer0": "ok", "max_err_over_tol": round(worst, 4)}
 
@@ -158,28 +190,43 @@ def main() -> int:
     n_launch = len(launches)
     avg_launch_us = ms * 1e3 / n_launch
 
-    # ---- per-shape launch durations (graph of every layer's copy of one matrix)
+    # ---- the other layout, and per-shape launch durations (graph of every
+    # layer's copy of one matrix)
+    def time_graph(seq, reps=10):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            make_step(seq)()
+        for _ in range(3):
+            g.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps      # us per replay
+
+    other = None
     per_shape = None
     if not args.no_shapes:
+        other_seq = separate_launches if args.layout == "fused" else fused_launches
+        other_bytes = sum(gemv_bytes(int(p.shape[0]), int(p.shape[1]) * 8) for _, p, _, _ in other_seq)
+        us = time_graph(other_seq)
+        other = {"layout": "separate" if args.layout == "fused" else "fused",
+                 "launches_per_step": len(other_seq), "us_per_sweep": round(us, 2),
+                 "GB/s": round(other_bytes / (us * 1e-6) / 1e9, 1)}
         per_shape = {}
-        for mid, (name, K, N) in enumerate(shapes):
-            seq = [(xs[K], layer[mid][3], layer[mid][4], ys[name]) for layer in weights]
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                for x, p, s, y in seq:
-                    w4a16.gemv(x, p, s, y=y)
-            for _ in range(3):
-                g.replay()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            reps = 10
-            e0.record(stream)
-            for _ in range(reps):
-                g.replay()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            us = e0.elapsed_time(e1) * 1e3 / (reps * len(seq))
-            per_shape[name] = {"K": K, "N": N, "us": round(us, 3),
-                               "GB/s": round(gemv_bytes(N, K) / (us * 1e-6) / 1e9, 1)}
+        for gi, (g, K, N, _, _, mem) in enumerate(layer0):
+            seqs = {g: [(xs[K], layer[gi][3], layer[gi][4], ys[g]) for layer in weights]}
+            if len(mem) > 1:
+                for (name, r0, n) in mem:
+                    seqs[name] = [(xs[K], layer[gi][3][r0:r0 + n], layer[gi][4][r0:r0 + n],
+                                   ys[g][r0:r0 + n]) for layer in weights]
+            for name, seq in seqs.items():
+                n_rows = int(seq[0][1].shape[0])
+                us = time_graph(seq) / len(seq)
+                per_shape[name] = {"K": K, "N": n_rows, "us": round(us, 3),
+                                   "GB/s": round(gemv_bytes(n_rows, K) / (us * 1e-6) / 1e9, 1)}
 
     # ---- CPU oracle on a bounded sample of the same sweep
     cpu = None
@@ -190,6 +237,7 @@ def main() -> int:
         for name, K, N in shapes:
             po, so = orc.quantize(host_w[name])
             host.append((K, N, po, so, xs[K].cpu().numpy()[None]))
+        # same bytes as one layer of the sweep in either layout
         nl = max(1, min(args.cpu_layers, nlayers))
         c0 = time.perf_counter()
         cbytes = 0
@@ -221,10 +269,13 @@ def main() -> int:
         "dtype": "fp16",
         "data": "synthetic: N(0,0.02) weights with 0.1% N(0,0.5) outliers, N(0,1) activations; "
                 "layer 0 drawn and quantized, layers 1.. device copies",
-        "config": {"workload": "%s decode weight sweep, M=1, %d layers x %d GEMVs (%s)"
+        "config": {"workload": "%s decode weight sweep, M=1, %d layers x %d matrices (%s)"
                                % (args.workload.split("-sweep")[0], nlayers, len(shapes),
                                   ", ".join("%s %dx%d" % s for s in shapes)),
-                   "M": 1, "launches_per_step": n_launch, "bytes_per_step": step_bytes,
+                   "M": 1, "layout": args.layout,
+                   "launch_groups": ["+".join(x[-1][i][0] for i in range(len(x[-1])))
+                                     for x in layer0],
+                   "launches_per_step": n_launch, "bytes_per_step": step_bytes,
                    "weight_bytes_resident": weight_bytes, "mode": args.mode,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(step_bytes / n_launch / (avg_launch_us * 1e-6)
@@ -237,6 +288,7 @@ def main() -> int:
                      "avg_launch_us": round(avg_launch_us, 3),
                      "bytes_per_launch_avg": step_bytes // n_launch},
         "cpu_baseline": cpu,
+        "other_layout": other,
         "per_shape": per_shape,
         "parity": parity,
         "wall_s_timed": round(wall, 4),

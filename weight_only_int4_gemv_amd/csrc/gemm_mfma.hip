@@ -107,6 +107,7 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
         }
     };
 
+    const CodeConsts kc = code_consts();
     float4_t acc[TM][TN];
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm)
@@ -136,7 +137,7 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
                 half2_t h[4];
-                dequant_word(words[kk], s2, h);
+                dequant_word(words[kk], s2, h, kc);
                 bf[tn][kk] = (half8_t){h[0].x, h[0].y, h[1].x, h[1].y,
                                        h[2].x, h[2].y, h[3].x, h[3].y};
             }

@@ -28,9 +28,21 @@ namespace w4a16 {
 
 namespace {
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+// Sum over the 64 lanes with DPP row operations (gfx9 wave64 pattern):
+// butterflies inside quads, mirrors inside 16-lane rows, then row broadcasts
+// 15 and 31.  The total ends in lane 63.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_add(float v) {
+    const int moved = __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, false);
+    return v + __int_as_float(moved);
+}
+__device__ __forceinline__ float wave_sum_lane63(float v) {
+    v = dpp_add<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+    v = dpp_add<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+    v = dpp_add<0x141, 0xF>(v);  // row_half_mirror
+    v = dpp_add<0x140, 0xF>(v);  // row_mirror: every lane holds its row's sum
+    v = dpp_add<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+    v = dpp_add<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
     return v;
 }
 
@@ -39,11 +51,23 @@ __device__ __forceinline__ float wave_sum(float v) {
 __device__ __forceinline__ void stage_activations(const uint16_t* __restrict__ X, int M, int K,
                                                   int k0, int ks, uint4* xs) {
     const int nblk = ks >> 3;
-    for (int i = threadIdx.x; i < M * nblk; i += blockDim.x) {
-        const int m = i / nblk;
-        const int b = i - m * nblk;
-        const uint4 v = reinterpret_cast<const uint4*>(X + (size_t)m * K + k0)[b];
-        xs[m * nblk + b] = pair_block(v.x, v.y, v.z, v.w);
+    const int total = M * nblk;
+    constexpr int B = 4;  // loads issued before the first store
+    for (int i0 = threadIdx.x; i0 < total; i0 += B * blockDim.x) {
+        uint4 v[B];
+#pragma unroll
+        for (int j = 0; j < B; ++j) {
+            const int i = i0 + j * blockDim.x;
+            if (i < total) {
+                const int m = i / nblk;
+                v[j] = reinterpret_cast<const uint4*>(X + (size_t)m * K + k0)[i - m * nblk];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < B; ++j) {
+            const int i = i0 + j * blockDim.x;
+            if (i < total) xs[i] = pair_block(v[j].x, v[j].y, v[j].z, v[j].w);
+        }
     }
 }
 
@@ -62,10 +86,15 @@ __global__ __launch_bounds__(WAVES * kWave) void gemv_kernel(
     const int ngroups = K >> 7;   // scales per weight row
     const int row0 = (blockIdx.x * WAVES + wave) * R;
 
-    int rows[R];
+    size_t wrow[R], srow[R];
 #pragma unroll
-    for (int r = 0; r < R; ++r) rows[r] = min(row0 + r, N - 1);  // tail rows re-read row N-1
+    for (int r = 0; r < R; ++r) {
+        const int row = min(row0 + r, N - 1);  // tail rows re-read row N-1, never stored
+        wrow[r] = (size_t)row * nchunks;
+        srow[r] = (size_t)row * ngroups;
+    }
 
+    const CodeConsts kc = code_consts();
     float acc[MMAX][R];
 #pragma unroll
     for (int m = 0; m < MMAX; ++m)
@@ -76,44 +105,58 @@ __global__ __launch_bounds__(WAVES * kWave) void gemv_kernel(
         const int ks = min(kslice, K - k0);
         const int c0 = k0 >> 5;          // first chunk of the slice
         const int nch = ks >> 5;
-        uint4* xs = lds;
-        if (k0 > 0) __syncthreads();     // previous slice fully consumed
-        stage_activations(X, M, K, k0, ks, xs);
-        __syncthreads();
+        const int nsteps = (nch + kWave - 1) / kWave;  // same for every lane
 
-        for (int cbase = lane; cbase < nch; cbase += U * kWave) {
-            // All U*R loads are issued before the first is used; a step past
-            // the slice end re-reads the last chunk (in bounds) and is skipped.
-            uint4 w[U][R];
-            uint16_t sb[U][R];
+        // U steps of R rows: lane takes chunk lane + 64*step.  A step past the
+        // slice end re-reads the last chunk (in bounds) and is not used.
+        auto load = [&](int s0, uint4 (&w)[U][R], uint16_t (&sb)[U][R]) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int cc = c0 + min(cbase + u * kWave, nch - 1);
+                const int cc = c0 + min(lane + (s0 + u) * kWave, nch - 1);
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
-                    w[u][r] = packed[(size_t)rows[r] * nchunks + cc];
-                    sb[u][r] = scales[(size_t)rows[r] * ngroups + (cc >> 2)];
+                    w[u][r] = packed[wrow[r] + cc];
+                    sb[u][r] = scales[srow[r] + (cc >> 2)];
                 }
             }
+        };
+        auto compute = [&](int s0, const uint4 (&w)[U][R], const uint16_t (&sb)[U][R]) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int c = cbase + u * kWave;
+                const int c = lane + (s0 + u) * kWave;
                 if (c >= nch) break;
 #pragma unroll
                 for (int m = 0; m < MMAX; ++m) {
                     if (m >= M) break;
-                    const uint4* xp = xs + m * (ks >> 3) + c * 4;
+                    const uint4* xp = lds + m * (ks >> 3) + c * 4;
                     const uint4 x0 = xp[0], x1 = xp[1], x2 = xp[2], x3 = xp[3];
 #pragma unroll
                     for (int r = 0; r < R; ++r) {
-                        float part = dot_word(w[u][r].x, x0, 0.0f);
-                        part = dot_word(w[u][r].y, x1, part);
-                        part = dot_word(w[u][r].z, x2, part);
-                        part = dot_word(w[u][r].w, x3, part);
+                        float part = dot_word(w[u][r].x, x0, 0.0f, kc);
+                        part = dot_word(w[u][r].y, x1, part, kc);
+                        part = dot_word(w[u][r].z, x2, part, kc);
+                        part = dot_word(w[u][r].w, x3, part, kc);
                         acc[m][r] = fmaf(f16_bits_to_f32(sb[u][r]), part, acc[m][r]);
                     }
                 }
             }
+        };
+
+        uint4 wa[U][R], wb[U][R];
+        uint16_t sa[U][R], sbb[U][R];
+        // Weight loads go out before the activations are staged, so HBM is
+        // busy while the block waits on its barrier.
+        load(0, wa, sa);
+        if (k0 > 0) __syncthreads();     // previous slice fully consumed
+        stage_activations(X, M, K, k0, ks, lds);
+        __syncthreads();
+
+        for (int s0 = 0; s0 < nsteps; s0 += 2 * U) {
+            if (s0 + U < nsteps) load(s0 + U, wb, sbb);
+            compute(s0, wa, sa);
+            if (s0 + U >= nsteps) break;
+            if (s0 + 2 * U < nsteps) load(s0 + 2 * U, wa, sa);
+            compute(s0 + U, wb, sbb);
         }
     }
 
@@ -122,8 +165,122 @@ __global__ __launch_bounds__(WAVES * kWave) void gemv_kernel(
         if (m >= M) break;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const float v = wave_sum(acc[m][r]);
-            if (lane == 0 && row0 + r < N) Y[(size_t)m * N + row0 + r] = f32_to_f16_bits(v);
+            const float v = wave_sum_lane63(acc[m][r]);
+            if (lane == kWave - 1 && row0 + r < N) Y[(size_t)m * N + row0 + r] = f32_to_f16_bits(v);
+        }
+    }
+}
+
+// Persistent variant for activations that fit LDS whole (M*K*2 bytes within
+// the budget).  Each block stages X once; each wave then walks row groups
+// g, g + G, g + 2G, ... (G = waves in the grid) of R rows, and the
+// (row group, chunk step) iterations form one stream with a ring of P
+// prefetched steps, so loads for the next row group are in flight while the
+// current one finishes and is reduced.  Weights and scales are read with
+// raw buffer loads over the rows from the group's first row to the end of
+// the matrix: addressing is scalar plus one 32-bit lane offset, and reads
+// past the last row (tail of the last group, last partial chunk step)
+// return 0 without touching memory.
+template <int MMAX, int R, int P, int WAVES>
+__global__ __launch_bounds__(WAVES * kWave) void gemv_persistent_kernel(
+    const uint16_t* __restrict__ X, int M, const uint4* __restrict__ packed,
+    const uint16_t* __restrict__ scales, uint16_t* __restrict__ Y, int N, int K) {
+    extern __shared__ uint4 lds[];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int nchunks = K >> 5;
+    const int nsteps = (nchunks + kWave - 1) / kWave;     // chunk steps per row group
+    const int total_rg = (N + R - 1) / R;
+    const int stride_rg = gridDim.x * WAVES;
+    if (nchunks == 0) return;  // K == 0 is launched on gemv_kernel, which writes the zeros
+    const uint32_t wrow_bytes = (uint32_t)K / 2;
+    const uint32_t srow_bytes = (uint32_t)K / 64;
+    const CodeConsts kc = code_consts();
+
+    // load cursor (wave-uniform)
+    int lrg = blockIdx.x * WAVES + wave;
+    int ls = 0;
+    __amdgpu_buffer_rsrc_t wr, sr;
+    auto set_rsrc = [&]() {
+        const int64_t row0 = (int64_t)lrg * R;
+        const int64_t rows_left = (int64_t)N - row0;
+        wr = buffer_rsrc(reinterpret_cast<const char*>(packed) + row0 * wrow_bytes,
+                         (uint64_t)rows_left * wrow_bytes);
+        sr = buffer_rsrc(reinterpret_cast<const char*>(scales) + row0 * srow_bytes,
+                         (uint64_t)rows_left * srow_bytes);
+    };
+    uint4 w[P][R];
+    uint16_t sb[P][R];
+    auto load = [&](uint4 (&wd)[R], uint16_t (&sd)[R]) {
+        if (lrg < total_rg) {
+            if (ls == 0) set_rsrc();
+            const int voff_w = lane * 16 + ls * (kWave * 16);
+            const int voff_s = (lane >> 2) * 2 + ls * (kWave / 4 * 2);
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                typedef unsigned v4u __attribute__((ext_vector_type(4)));
+                const v4u v = __builtin_amdgcn_raw_buffer_load_b128(wr, voff_w, r * wrow_bytes, 0);
+                wd[r] = make_uint4(v.x, v.y, v.z, v.w);
+                sd[r] = __builtin_amdgcn_raw_buffer_load_b16(sr, voff_s, r * srow_bytes, 0);
+            }
+        }
+        if (++ls == nsteps) { ls = 0; lrg += stride_rg; }
+    };
+
+#pragma unroll
+    for (int i = 0; i < P; ++i) load(w[i], sb[i]);
+    stage_activations(X, M, K, 0, K, lds);
+    __syncthreads();
+
+    int crg = blockIdx.x * WAVES + wave;   // compute cursor (wave-uniform)
+    int cs = 0;
+    float acc[MMAX][R];
+#pragma unroll
+    for (int m = 0; m < MMAX; ++m)
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[m][r] = 0.0f;
+
+    while (crg < total_rg) {
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+            if (crg < total_rg) {
+                const int c = lane + cs * kWave;
+                if (c < nchunks) {
+#pragma unroll
+                    for (int m = 0; m < MMAX; ++m) {
+                        if (m >= M) break;
+                        const uint4* xp = lds + m * (K >> 3) + c * 4;
+                        const uint4 x0 = xp[0], x1 = xp[1], x2 = xp[2], x3 = xp[3];
+#pragma unroll
+                        for (int r = 0; r < R; ++r) {
+                            float part = dot_word(w[i][r].x, x0, 0.0f, kc);
+                            part = dot_word(w[i][r].y, x1, part, kc);
+                            part = dot_word(w[i][r].z, x2, part, kc);
+                            part = dot_word(w[i][r].w, x3, part, kc);
+                            acc[m][r] = fmaf(f16_bits_to_f32(sb[i][r]), part, acc[m][r]);
+                        }
+                    }
+                }
+                // refill this slot with the step P ahead
+                load(w[i], sb[i]);
+                if (++cs == nsteps) {
+                    // row group complete: reduce over the wave and store
+#pragma unroll
+                    for (int m = 0; m < MMAX; ++m) {
+                        if (m >= M) break;
+#pragma unroll
+                        for (int r = 0; r < R; ++r) {
+                            const float v = wave_sum_lane63(acc[m][r]);
+                            const int row = crg * R + r;
+                            if (lane == kWave - 1 && row < N)
+                                Y[(size_t)m * N + row] = f32_to_f16_bits(v);
+                            acc[m][r] = 0.0f;
+                        }
+                    }
+                    cs = 0;
+                    crg += stride_rg;
+                }
+            }
         }
     }
 }
@@ -150,13 +307,40 @@ hipError_t launch_gemv_t(const uint16_t* X, int64_t M, const uint32_t* packed,
     return hipGetLastError();
 }
 
-// Rows per wave: as many as keep at least two blocks per compute unit.
+template <int MMAX, int R, int P, int WAVES>
+hipError_t launch_persistent_t(const uint16_t* X, int64_t M, const uint32_t* packed,
+                               const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y,
+                               hipStream_t stream, int num_cu, int blocks_per_cu) {
+    const size_t lds = (size_t)MMAX * (K / 8) * sizeof(uint4);
+    const int64_t total_rg = (N + R - 1) / R;
+    int64_t blocks = (total_rg + WAVES - 1) / WAVES;
+    const int64_t cap = (int64_t)num_cu * blocks_per_cu;
+    if (blocks > cap) blocks = cap;
+    hipLaunchKernelGGL((gemv_persistent_kernel<MMAX, R, P, WAVES>), dim3((unsigned)blocks),
+                       dim3(WAVES * kWave), lds, stream, X, (int)M,
+                       reinterpret_cast<const uint4*>(packed), scales, Y, (int)N, (int)K);
+    return hipGetLastError();
+}
+
+// Launch choice (measured on MI355X over the decode layer shapes): whole-X
+// staging with the persistent kernel when it fits; two rows per wave, four
+// steps in flight, two blocks per compute unit, eight waves per block unless
+// there are too few row groups to give every compute unit eight waves.
 template <int MMAX>
 hipError_t launch_gemv_m(const uint16_t* X, int64_t M, const uint32_t* packed,
                          const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y,
                          hipStream_t stream, int num_cu) {
+    if (K > 0 && (int64_t)MMAX * K * 2 <= kLdsBudget) {
+        constexpr int R = MMAX >= 4 ? 1 : 2;
+        const int64_t total_rg = (N + R - 1) / R;
+        if (total_rg >= (int64_t)8 * num_cu)
+            return launch_persistent_t<MMAX, R, 4, 8>(X, M, packed, scales, N, K, Y, stream,
+                                                      num_cu, 2);
+        return launch_persistent_t<MMAX, R, 4, 4>(X, M, packed, scales, N, K, Y, stream, num_cu,
+                                                  2);
+    }
     constexpr int WAVES = 4;
-    if (N >= (int64_t)4 * WAVES * num_cu)
+    if (N >= (int64_t)4 * WAVES * num_cu && MMAX <= 4)
         return launch_gemv_t<MMAX, 4, 2, WAVES>(X, M, packed, scales, N, K, Y, stream);
     if (N >= (int64_t)2 * WAVES * num_cu)
         return launch_gemv_t<MMAX, 2, 2, WAVES>(X, M, packed, scales, N, K, Y, stream);

@@ -47,28 +47,44 @@ __device__ __forceinline__ uint4 pair_block(uint32_t x01, uint32_t x23, uint32_t
     return p;
 }
 
+// Keeps a constant in a VGPR, opaque to the optimizer, so that
+// (w & mask) | magic is selected as one v_and_or_b32 (gfx9 VOP3 encodings
+// take no 32-bit literal, and two SGPR operands exceed the constant bus).
+__device__ __forceinline__ uint32_t in_vgpr(uint32_t v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
+struct CodeConsts {
+    uint32_t m_lo, m_hi, magic;
+};
+__device__ __forceinline__ CodeConsts code_consts() {
+    return CodeConsts{in_vgpr(0x000F000Fu), in_vgpr(0x00F000F0u), in_vgpr(0x64006400u)};
+}
+
 // One packed word -> its 8 codes q = n - 8 as exact fp16 integers, in the
 // paired order (q0,q4),(q1,q5),(q2,q6),(q3,q7).  0x6400|n is the fp16 value
 // 1024+n, so (1024+n) - 1032 = q exactly; for the nibbles at bits 4-7 the
 // value is 1024+16n and (1024+16n)/16 - 72 = q exactly.  Costs one shift,
 // four v_and_or_b32 and four packed-fp16 add/fma.
-__device__ __forceinline__ void codes_word(uint32_t w, half2_t (&q)[4]) {
+__device__ __forceinline__ void codes_word(uint32_t w, const CodeConsts& k, half2_t (&q)[4]) {
     const half2_t m1032 = {(_Float16)-1032.0f, (_Float16)-1032.0f};
     const half2_t inv16 = {(_Float16)0.0625f, (_Float16)0.0625f};
     const half2_t m72 = {(_Float16)-72.0f, (_Float16)-72.0f};
     const uint32_t w8 = w >> 8;
-    q[0] = as_h2((w & 0x000F000Fu) | 0x64006400u) + m1032;
-    q[1] = __builtin_elementwise_fma(as_h2((w & 0x00F000F0u) | 0x64006400u), inv16, m72);
-    q[2] = as_h2((w8 & 0x000F000Fu) | 0x64006400u) + m1032;
-    q[3] = __builtin_elementwise_fma(as_h2((w8 & 0x00F000F0u) | 0x64006400u), inv16, m72);
+    q[0] = as_h2((w & k.m_lo) | k.magic) + m1032;
+    q[1] = __builtin_elementwise_fma(as_h2((w & k.m_hi) | k.magic), inv16, m72);
+    q[2] = as_h2((w8 & k.m_lo) | k.magic) + m1032;
+    q[3] = __builtin_elementwise_fma(as_h2((w8 & k.m_hi) | k.magic), inv16, m72);
 }
 
 // acc += sum of the word's 8 products q*x (paired activations xp), each
 // product exact in fp32 (v_dot2_f32_f16), so the rounding error of the
 // accumulation is relative to sum |q x|.
-__device__ __forceinline__ float dot_word(uint32_t w, const uint4& xp, float acc) {
+__device__ __forceinline__ float dot_word(uint32_t w, const uint4& xp, float acc,
+                                          const CodeConsts& k) {
     half2_t q[4];
-    codes_word(w, q);
+    codes_word(w, k, q);
     acc = __builtin_amdgcn_fdot2(q[0], as_h2(xp.x), acc, false);
     acc = __builtin_amdgcn_fdot2(q[1], as_h2(xp.y), acc, false);
     acc = __builtin_amdgcn_fdot2(q[2], as_h2(xp.z), acc, false);
@@ -76,12 +92,20 @@ __device__ __forceinline__ float dot_word(uint32_t w, const uint4& xp, float acc
     return acc;
 }
 
+// Raw buffer resource over [base, base + bytes) for gfx9 (data format 32;
+// reads past `bytes` return 0 instead of touching memory).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint64_t bytes) {
+    const int n = bytes > 0xFFFFFFFFull ? (int)0xFFFFFFFFu : (int)(uint32_t)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
+}
+
 // One packed word -> its 8 dequantized weights fp16(s*q) as 4 half2 in the
 // paired order (w0,w4),(w1,w5),(w2,w6),(w3,w7): exact codes (codes_word)
 // times the scale, rounded once to nearest even.
-__device__ __forceinline__ void dequant_word(uint32_t w, half2_t s2, half2_t (&out)[4]) {
+__device__ __forceinline__ void dequant_word(uint32_t w, half2_t s2, half2_t (&out)[4],
+                                             const CodeConsts& k) {
     half2_t q[4];
-    codes_word(w, q);
+    codes_word(w, k, q);
     out[0] = q[0] * s2;
     out[1] = q[1] * s2;
     out[2] = q[2] * s2;
