@@ -61,7 +61,93 @@ def parse():
                    help="layers of the sweep the CPU oracle is timed on")
     p.add_argument("--no-check", action="store_true", help="skip the parity check of layer 0")
     p.add_argument("--no-shapes", action="store_true", help="skip per-shape timing")
+    p.add_argument("--no-secondary", action="store_true",
+                   help="skip the quantizer, batched-decode and prefill measurements")
+    p.add_argument("--copy-probe-mib", type=int, default=0,
+                   help="run one plain device copy of this many MiB first (calibrates "
+                        "the FETCH_SIZE / WRITE_SIZE counters against known bytes)")
     return p.parse_args()
+
+
+def secondary(torch, w4a16, inputs, dev, stream):
+    """Other rows of the path on their workload shapes: the quantizer (70B FFN
+    matrix, larger than the Infinity Cache), batched decode M = 1..32 on the
+    8B FFN shapes with both kernel families (locates the VALU/MFMA
+    crossover), and 512-token prefill.  Each figure is the mean of graph
+    replays over enough weight copies to stream from HBM."""
+    out = {}
+
+    def timed(seq_fn, reps=5):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            seq_fn()
+        for _ in range(2):
+            g.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps     # us per replay
+
+    # quantizer: 28672 x 8192 fp16 (470 MB in, 121 MB out)
+    K, N = 8192, 28672
+    W = torch.from_numpy(inputs.weight(N, K, seed=[5, 1, 0])).to(dev)
+    pq = torch.empty((N, K // 8), dtype=torch.int32, device=dev)
+    sq = torch.empty((N, K // 128), dtype=torch.float16, device=dev)
+    w4a16.quantize(W, pq, sq)
+    us = timed(lambda: w4a16.quantize(W, pq, sq))
+    qbytes = N * K * 2 + N * K // 2 + N * (K // 128) * 2
+    out["quantize"] = {"K": K, "N": N, "us": round(us, 2),
+                       "GB/s": round(qbytes / (us * 1e-6) / 1e9, 1),
+                       "frac_of_hbm_peak": round(qbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    del W
+    quantized = {(K, N): (pq, sq)}
+
+    def weights_for(K, N):
+        if (K, N) not in quantized:
+            Wd = torch.from_numpy(inputs.weight(N, K, seed=[5, K, N])).to(dev)
+            quantized[(K, N)] = w4a16.quantize(Wd)
+            del Wd
+        return quantized[(K, N)]
+
+    # batched decode on the 8B FFN shapes
+    batched = {}
+    for (K, N) in [(4096, 14336), (14336, 4096)]:
+        p0, s0 = weights_for(K, N)
+        copies = [(p0.clone(), s0.clone()) for _ in range(12)]      # 364 MB of weights
+        for M in [1, 2, 4, 8, 16, 32]:
+            X = torch.from_numpy(inputs.activation(M, K, seed=[6, M, K])).to(dev)
+            Y = torch.empty((M, N), dtype=torch.float16, device=dev)
+            row = {}
+            for algo in ["valu", "mfma"]:
+                us = timed(lambda: [w4a16.gemm(X, p, s_, algo=algo, Y=Y) for p, s_ in copies]) \
+                    / len(copies)
+                b = gemv_bytes(N, K, M)
+                row[algo] = {"us": round(us, 3), "GB/s": round(b / (us * 1e-6) / 1e9, 1),
+                             "TFLOP/s": round(2 * M * N * K / (us * 1e-6) / 1e12, 2)}
+            row["auto_picks"] = "valu" if M <= w4a16.valu_max_m() else "mfma"
+            batched["%dx%d M=%d" % (K, N, M)] = row
+        del copies
+    out["batched_decode"] = batched
+
+    # prefill, M = 512
+    prefill = {}
+    for (K, N) in [(4096, 14336), (14336, 4096), (8192, 28672)]:
+        p0, s0 = weights_for(K, N)
+        copies = [(p0, s0)] + [(p0.clone(), s0.clone()) for _ in range(3)]
+        X = torch.from_numpy(inputs.activation(512, K, seed=[7, K])).to(dev)
+        Y = torch.empty((512, N), dtype=torch.float16, device=dev)
+        us = timed(lambda: [w4a16.gemm(X, p, s_, Y=Y) for p, s_ in copies]) / len(copies)
+        tf = 2 * 512 * N * K / (us * 1e-6) / 1e12
+        prefill["%dx%d M=512" % (K, N)] = {"us": round(us, 2), "TFLOP/s": round(tf, 1),
+                                           "frac_of_mfma_f16_peak":
+                                               round(tf / MFMA_F16_PEAK_TFLOPS, 4)}
+        del copies
+    out["prefill"] = prefill
+    quantized.clear()
+    return out
 
 
 def main() -> int:
@@ -80,6 +166,16 @@ def main() -> int:
     w4a16.library()  # the built HIP library; an error if absent
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    if args.copy_probe_mib > 0:
+        src = torch.ones(args.copy_probe_mib << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print("[copy-probe] one copy of %d bytes (read) + %d bytes (write)"
+              % (src.numel() * 4, dst.numel() * 4), file=sys.stderr, flush=True)
+        del src, dst
 
     shape_attr, layers_attr = WORKLOADS[args.workload]
     shapes = getattr(inputs, shape_attr)
@@ -252,6 +348,10 @@ def main() -> int:
                          "us per full sweep extrapolated: %.0f"
                          % (nl, nlayers, nl * len(shapes), csec, csec / nl * nlayers * 1e6)}
 
+    sec = None
+    if not args.no_secondary:
+        sec = secondary(torch, w4a16, inputs, dev, stream)
+
     out = {
         "metric": "W4A16 GEMV effective HBM GB/s (% of peak) + us per 8B-shaped decode weight sweep",
         "value": round(gbs, 1),
@@ -291,6 +391,7 @@ def main() -> int:
         "other_layout": other,
         "per_shape": per_shape,
         "parity": parity,
+        "secondary": sec,
         "wall_s_timed": round(wall, 4),
         "setup_s": round(setup_s, 1),
     }

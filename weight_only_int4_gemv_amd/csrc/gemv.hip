@@ -172,16 +172,23 @@ __global__ __launch_bounds__(WAVES * kWave) void gemv_kernel(
 }
 
 // Persistent variant for activations that fit LDS whole (M*K*2 bytes within
-// the budget).  Each block stages X once; each wave then walks row groups
-// g, g + G, g + 2G, ... (G = waves in the grid) of R rows, and the
+// the budget).  Each block stages X once; each wave then walks its row
+// groups g, g + G, g + 2G, ... (G = waves in the grid) of R rows, and the
 // (row group, chunk step) iterations form one stream with a ring of P
 // prefetched steps, so loads for the next row group are in flight while the
-// current one finishes and is reduced.  Weights and scales are read with
-// raw buffer loads over the rows from the group's first row to the end of
-// the matrix: addressing is scalar plus one 32-bit lane offset, and reads
-// past the last row (tail of the last group, last partial chunk step)
-// return 0 without touching memory.
-template <int MMAX, int R, int P, int WAVES>
+// current one finishes and is reduced.
+//   - Weights and scales come through raw buffer loads over the rows from
+//     the group's first row to the end of the matrix: scalar addressing plus
+//     one 32-bit lane offset, and reads past the last row return 0 without
+//     touching memory.  Every load is issued unconditionally (steps past the
+//     wave's work use an empty resource), so the compiler's counter waits are
+//     exact and P steps really stay in flight.
+//   - X is loaded into registers before the first weight loads, so staging
+//     it waits only for its own loads.
+//   - A lane whose chunk is past the end of the row (last partial step)
+//     contributes with scale 0 and reads a valid LDS address.
+// XPT: 16-byte activation blocks staged per thread (MMAX*K/8 <= XPT*threads).
+template <int MMAX, int R, int P, int WAVES, int XPT>
 __global__ __launch_bounds__(WAVES * kWave) void gemv_persistent_kernel(
     const uint16_t* __restrict__ X, int M, const uint4* __restrict__ packed,
     const uint16_t* __restrict__ scales, uint16_t* __restrict__ Y, int N, int K) {
@@ -189,50 +196,67 @@ __global__ __launch_bounds__(WAVES * kWave) void gemv_persistent_kernel(
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int nchunks = K >> 5;
+    if (nchunks == 0) return;  // K == 0 is launched on gemv_kernel, which writes the zeros
     const int nsteps = (nchunks + kWave - 1) / kWave;     // chunk steps per row group
     const int total_rg = (N + R - 1) / R;
     const int stride_rg = gridDim.x * WAVES;
-    if (nchunks == 0) return;  // K == 0 is launched on gemv_kernel, which writes the zeros
+    const int first_rg = blockIdx.x * WAVES + wave;
+    const int my_rg = first_rg < total_rg ? (total_rg - 1 - first_rg) / stride_rg + 1 : 0;
+    const int T = my_rg * nsteps;                          // this wave's iterations
     const uint32_t wrow_bytes = (uint32_t)K / 2;
     const uint32_t srow_bytes = (uint32_t)K / 64;
     const CodeConsts kc = code_consts();
 
-    // load cursor (wave-uniform)
-    int lrg = blockIdx.x * WAVES + wave;
-    int ls = 0;
-    __amdgpu_buffer_rsrc_t wr, sr;
-    auto set_rsrc = [&]() {
-        const int64_t row0 = (int64_t)lrg * R;
-        const int64_t rows_left = (int64_t)N - row0;
-        wr = buffer_rsrc(reinterpret_cast<const char*>(packed) + row0 * wrow_bytes,
-                         (uint64_t)rows_left * wrow_bytes);
-        sr = buffer_rsrc(reinterpret_cast<const char*>(scales) + row0 * srow_bytes,
-                         (uint64_t)rows_left * srow_bytes);
-    };
-    uint4 w[P][R];
-    uint16_t sb[P][R];
-    auto load = [&](uint4 (&wd)[R], uint16_t (&sd)[R]) {
-        if (lrg < total_rg) {
-            if (ls == 0) set_rsrc();
-            const int voff_w = lane * 16 + ls * (kWave * 16);
-            const int voff_s = (lane >> 2) * 2 + ls * (kWave / 4 * 2);
+    // X blocks of this thread, loaded first (indices clamped into range).
+    const int xblocks = M * (K >> 3);
+    uint4 xr[XPT];
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                typedef unsigned v4u __attribute__((ext_vector_type(4)));
-                const v4u v = __builtin_amdgcn_raw_buffer_load_b128(wr, voff_w, r * wrow_bytes, 0);
-                wd[r] = make_uint4(v.x, v.y, v.z, v.w);
-                sd[r] = __builtin_amdgcn_raw_buffer_load_b16(sr, voff_s, r * srow_bytes, 0);
-            }
+    for (int i = 0; i < XPT; ++i) {
+        const int e = min((int)threadIdx.x + i * WAVES * kWave, xblocks - 1);
+        const int m = e / (K >> 3);
+        xr[i] = reinterpret_cast<const uint4*>(X + (size_t)m * K)[e - m * (K >> 3)];
+    }
+
+    // load cursor (wave-uniform): iteration tl -> (row group lrg, step ls)
+    int tl = 0, lrg = first_rg, ls = 0;
+    __amdgpu_buffer_rsrc_t wr = buffer_rsrc(packed, 0), sr = buffer_rsrc(scales, 0);
+    auto load = [&](uint4 (&wd)[R], uint16_t (&sd)[R]) {
+        if (ls == 0) {
+            // new row group (or past the wave's work: an empty resource)
+            const bool live = tl < T;
+            const int64_t row0 = (int64_t)lrg * R;
+            const int64_t rows_left = live ? (int64_t)N - row0 : 0;
+            wr = buffer_rsrc(reinterpret_cast<const char*>(packed) + (live ? row0 * wrow_bytes : 0),
+                             (uint64_t)rows_left * wrow_bytes);
+            sr = buffer_rsrc(reinterpret_cast<const char*>(scales) + (live ? row0 * srow_bytes : 0),
+                             (uint64_t)rows_left * srow_bytes);
         }
+        const int voff_w = lane * 16 + ls * (kWave * 16);
+        const int voff_s = (lane >> 2) * 2 + ls * (kWave / 4 * 2);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            typedef unsigned v4u __attribute__((ext_vector_type(4)));
+            const v4u v = __builtin_amdgcn_raw_buffer_load_b128(wr, voff_w, r * wrow_bytes, 0);
+            wd[r] = make_uint4(v.x, v.y, v.z, v.w);
+            sd[r] = __builtin_amdgcn_raw_buffer_load_b16(sr, voff_s, r * srow_bytes, 0);
+        }
+        ++tl;
         if (++ls == nsteps) { ls = 0; lrg += stride_rg; }
     };
 
+    uint4 w[P][R];
+    uint16_t sb[P][R];
 #pragma unroll
     for (int i = 0; i < P; ++i) load(w[i], sb[i]);
-    stage_activations(X, M, K, 0, K, lds);
+
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+        const int e = (int)threadIdx.x + i * WAVES * kWave;
+        if (e < xblocks) lds[e] = pair_block(xr[i].x, xr[i].y, xr[i].z, xr[i].w);
+    }
     __syncthreads();
 
-    int crg = blockIdx.x * WAVES + wave;   // compute cursor (wave-uniform)
+    int crg = first_rg;   // compute cursor (wave-uniform)
     int cs = 0;
     float acc[MMAX][R];
 #pragma unroll
@@ -240,30 +264,34 @@ __global__ __launch_bounds__(WAVES * kWave) void gemv_persistent_kernel(
 #pragma unroll
         for (int r = 0; r < R; ++r) acc[m][r] = 0.0f;
 
-    while (crg < total_rg) {
+    for (int t0 = 0; t0 < T; t0 += P) {
 #pragma unroll
         for (int i = 0; i < P; ++i) {
-            if (crg < total_rg) {
-                const int c = lane + cs * kWave;
-                if (c < nchunks) {
+            const int c = lane + cs * kWave;
+            const bool valid = c < nchunks;
+            const int cx = min(c, nchunks - 1);
+            // Steps past the wave's work (the ring's tail) skip the arithmetic;
+            // the branch is wave-uniform and holds no loads.
 #pragma unroll
-                    for (int m = 0; m < MMAX; ++m) {
-                        if (m >= M) break;
-                        const uint4* xp = lds + m * (K >> 3) + c * 4;
-                        const uint4 x0 = xp[0], x1 = xp[1], x2 = xp[2], x3 = xp[3];
+            for (int m = 0; m < MMAX; ++m) {
+                if (m >= M || t0 + i >= T) break;
+                const uint4* xp = lds + m * (K >> 3) + cx * 4;
+                const uint4 x0 = xp[0], x1 = xp[1], x2 = xp[2], x3 = xp[3];
 #pragma unroll
-                        for (int r = 0; r < R; ++r) {
-                            float part = dot_word(w[i][r].x, x0, 0.0f, kc);
-                            part = dot_word(w[i][r].y, x1, part, kc);
-                            part = dot_word(w[i][r].z, x2, part, kc);
-                            part = dot_word(w[i][r].w, x3, part, kc);
-                            acc[m][r] = fmaf(f16_bits_to_f32(sb[i][r]), part, acc[m][r]);
-                        }
-                    }
+                for (int r = 0; r < R; ++r) {
+                    float part = dot_word(w[i][r].x, x0, 0.0f, kc);
+                    part = dot_word(w[i][r].y, x1, part, kc);
+                    part = dot_word(w[i][r].z, x2, part, kc);
+                    part = dot_word(w[i][r].w, x3, part, kc);
+                    const float sc = valid ? f16_bits_to_f32(sb[i][r]) : 0.0f;
+                    acc[m][r] = fmaf(sc, part, acc[m][r]);
                 }
-                // refill this slot with the step P ahead
-                load(w[i], sb[i]);
-                if (++cs == nsteps) {
+            }
+            // refill this slot with the step P ahead
+            load(w[i], sb[i]);
+            if (++cs == nsteps) {
+                cs = 0;
+                if (t0 + i < T) {
                     // row group complete: reduce over the wave and store
 #pragma unroll
                     for (int m = 0; m < MMAX; ++m) {
@@ -277,9 +305,8 @@ __global__ __launch_bounds__(WAVES * kWave) void gemv_persistent_kernel(
                             acc[m][r] = 0.0f;
                         }
                     }
-                    cs = 0;
-                    crg += stride_rg;
                 }
+                crg += stride_rg;
             }
         }
     }
@@ -307,37 +334,54 @@ hipError_t launch_gemv_t(const uint16_t* X, int64_t M, const uint32_t* packed,
     return hipGetLastError();
 }
 
-template <int MMAX, int R, int P, int WAVES>
-hipError_t launch_persistent_t(const uint16_t* X, int64_t M, const uint32_t* packed,
-                               const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y,
-                               hipStream_t stream, int num_cu, int blocks_per_cu) {
+template <int MMAX, int R, int P, int WAVES, int XPT>
+hipError_t launch_persistent_xpt(const uint16_t* X, int64_t M, const uint32_t* packed,
+                                 const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y,
+                                 hipStream_t stream, int64_t blocks) {
     const size_t lds = (size_t)MMAX * (K / 8) * sizeof(uint4);
-    const int64_t total_rg = (N + R - 1) / R;
-    int64_t blocks = (total_rg + WAVES - 1) / WAVES;
-    const int64_t cap = (int64_t)num_cu * blocks_per_cu;
-    if (blocks > cap) blocks = cap;
-    hipLaunchKernelGGL((gemv_persistent_kernel<MMAX, R, P, WAVES>), dim3((unsigned)blocks),
+    hipLaunchKernelGGL((gemv_persistent_kernel<MMAX, R, P, WAVES, XPT>), dim3((unsigned)blocks),
                        dim3(WAVES * kWave), lds, stream, X, (int)M,
                        reinterpret_cast<const uint4*>(packed), scales, Y, (int)N, (int)K);
     return hipGetLastError();
 }
 
-// Launch choice (measured on MI355X over the decode layer shapes): whole-X
-// staging with the persistent kernel when it fits; two rows per wave, four
-// steps in flight, two blocks per compute unit, eight waves per block unless
-// there are too few row groups to give every compute unit eight waves.
+// Grid: at most blocks_per_cu blocks per compute unit, sized so that every
+// wave gets the same number of row groups.
+template <int MMAX, int R, int P, int WAVES>
+hipError_t launch_persistent_t(const uint16_t* X, int64_t M, const uint32_t* packed,
+                               const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y,
+                               hipStream_t stream, int num_cu, int blocks_per_cu) {
+    const int64_t total_rg = (N + R - 1) / R;
+    const int64_t max_waves = (int64_t)num_cu * blocks_per_cu * WAVES;
+    const int64_t per_wave = (total_rg + max_waves - 1) / max_waves;
+    const int64_t waves = (total_rg + per_wave - 1) / per_wave;
+    const int64_t blocks = (waves + WAVES - 1) / WAVES;
+    const int64_t need = (int64_t)MMAX * (K / 8);             // x blocks to stage
+    const int64_t threads = (int64_t)WAVES * kWave;
+    if (need <= threads)
+        return launch_persistent_xpt<MMAX, R, P, WAVES, 1>(X, M, packed, scales, N, K, Y, stream, blocks);
+    if (need <= 2 * threads)
+        return launch_persistent_xpt<MMAX, R, P, WAVES, 2>(X, M, packed, scales, N, K, Y, stream, blocks);
+    if (need <= 4 * threads)
+        return launch_persistent_xpt<MMAX, R, P, WAVES, 4>(X, M, packed, scales, N, K, Y, stream, blocks);
+    if (need <= 8 * threads)
+        return launch_persistent_xpt<MMAX, R, P, WAVES, 8>(X, M, packed, scales, N, K, Y, stream, blocks);
+    return launch_persistent_xpt<MMAX, R, P, WAVES, 16>(X, M, packed, scales, N, K, Y, stream, blocks);
+}
+
+// Launch choice (measured on MI355X over the decode layer shapes, K x N from
+// 4096x1024 to 8192x28672): whole-X staging with the persistent kernel when
+// it fits; two rows per wave, two steps in flight, four waves per block and
+// four blocks per compute unit.  Deeper rings (P = 4, 8) and eight-wave
+// blocks measured slower.
 template <int MMAX>
 hipError_t launch_gemv_m(const uint16_t* X, int64_t M, const uint32_t* packed,
                          const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y,
                          hipStream_t stream, int num_cu) {
     if (K > 0 && (int64_t)MMAX * K * 2 <= kLdsBudget) {
         constexpr int R = MMAX >= 4 ? 1 : 2;
-        const int64_t total_rg = (N + R - 1) / R;
-        if (total_rg >= (int64_t)8 * num_cu)
-            return launch_persistent_t<MMAX, R, 4, 8>(X, M, packed, scales, N, K, Y, stream,
-                                                      num_cu, 2);
-        return launch_persistent_t<MMAX, R, 4, 4>(X, M, packed, scales, N, K, Y, stream, num_cu,
-                                                  2);
+        return launch_persistent_t<MMAX, R, 2, 4>(X, M, packed, scales, N, K, Y, stream, num_cu,
+                                                  4);
     }
     constexpr int WAVES = 4;
     if (N >= (int64_t)4 * WAVES * num_cu && MMAX <= 4)
