@@ -28,6 +28,9 @@ namespace w4a16 {
 
 namespace {
 
+// Cache policy of the weight stream: non-temporal (the loads' slc/nt bit).
+constexpr int kStreamLoad = 2;
+
 // Sum over the 64 lanes with DPP row operations (gfx9 wave64 pattern):
 // butterflies inside quads, mirrors inside 16-lane rows, then row broadcasts
 // 15 and 31.  The total ends in lane 63.
@@ -236,16 +239,23 @@ __global__ __launch_bounds__(WAVES * kWave) void gemv_persistent_kernel(
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             typedef unsigned v4u __attribute__((ext_vector_type(4)));
-            const v4u v = __builtin_amdgcn_raw_buffer_load_b128(wr, voff_w, r * wrow_bytes, 0);
+            // streamed once: non-temporal (kStreamLoad) keeps them from
+            // displacing reusable lines in L2
+            const v4u v = __builtin_amdgcn_raw_buffer_load_b128(wr, voff_w, r * wrow_bytes,
+                                                                 kStreamLoad);
             wd[r] = make_uint4(v.x, v.y, v.z, v.w);
-            sd[r] = __builtin_amdgcn_raw_buffer_load_b16(sr, voff_s, r * srow_bytes, 0);
+            sd[r] = __builtin_amdgcn_raw_buffer_load_b16(sr, voff_s, r * srow_bytes, kStreamLoad);
         }
         ++tl;
         if (++ls == nsteps) { ls = 0; lrg += stride_rg; }
     };
 
-    uint4 w[P][R];
-    uint16_t sb[P][R];
+    // Ring of Q = P + 1 slots: iteration t computes slot t % Q after issuing
+    // the load of iteration t + P into slot (t + P) % Q, the slot iteration
+    // t - 1 consumed, so P steps stay in flight while a step is multiplied.
+    constexpr int Q = P + 1;
+    uint4 w[Q][R];
+    uint16_t sb[Q][R];
 #pragma unroll
     for (int i = 0; i < P; ++i) load(w[i], sb[i]);
 
@@ -264,9 +274,10 @@ __global__ __launch_bounds__(WAVES * kWave) void gemv_persistent_kernel(
 #pragma unroll
         for (int r = 0; r < R; ++r) acc[m][r] = 0.0f;
 
-    for (int t0 = 0; t0 < T; t0 += P) {
+    for (int t0 = 0; t0 < T; t0 += Q) {
 #pragma unroll
-        for (int i = 0; i < P; ++i) {
+        for (int i = 0; i < Q; ++i) {
+            load(w[(i + P) % Q], sb[(i + P) % Q]);   // iteration t0 + i + P
             const int c = lane + cs * kWave;
             const bool valid = c < nchunks;
             const int cx = min(c, nchunks - 1);
@@ -287,8 +298,6 @@ __global__ __launch_bounds__(WAVES * kWave) void gemv_persistent_kernel(
                     acc[m][r] = fmaf(sc, part, acc[m][r]);
                 }
             }
-            // refill this slot with the step P ahead
-            load(w[i], sb[i]);
             if (++cs == nsteps) {
                 cs = 0;
                 if (t0 + i < T) {
@@ -370,18 +379,23 @@ hipError_t launch_persistent_t(const uint16_t* X, int64_t M, const uint32_t* pac
 }
 
 // Launch choice (measured on MI355X over the decode layer shapes, K x N from
-// 4096x1024 to 8192x28672): whole-X staging with the persistent kernel when
-// it fits; two rows per wave, two steps in flight, four waves per block and
-// four blocks per compute unit.  Deeper rings (P = 4, 8) and eight-wave
-// blocks measured slower.
+// 4096x1024 to 8192x28672, with the (P+1)-slot ring and non-temporal loads):
+// whole-X staging with the persistent kernel when it fits; two rows per
+// wave; for K up to 8192 one step in flight, four waves per block, six
+// blocks per compute unit; for longer rows (K >= 12288, where the per-block
+// activation copy is larger) two steps in flight, eight waves per block,
+// two blocks per compute unit.
 template <int MMAX>
 hipError_t launch_gemv_m(const uint16_t* X, int64_t M, const uint32_t* packed,
                          const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y,
                          hipStream_t stream, int num_cu) {
     if (K > 0 && (int64_t)MMAX * K * 2 <= kLdsBudget) {
         constexpr int R = MMAX >= 4 ? 1 : 2;
-        return launch_persistent_t<MMAX, R, 2, 4>(X, M, packed, scales, N, K, Y, stream, num_cu,
-                                                  4);
+        if (K >= 12288)
+            return launch_persistent_t<MMAX, R, 2, 8>(X, M, packed, scales, N, K, Y, stream,
+                                                      num_cu, 2);
+        return launch_persistent_t<MMAX, R, 1, 4>(X, M, packed, scales, N, K, Y, stream, num_cu,
+                                                  6);
     }
     constexpr int WAVES = 4;
     if (N >= (int64_t)4 * WAVES * num_cu && MMAX <= 4)
