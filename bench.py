@@ -56,6 +56,9 @@ def parse():
                    help="replay a captured HIP graph (default) or launch from Python")
     p.add_argument("--layout", default="fused", choices=["fused", "separate"],
                    help="qkv and gate_up concatenated (default) or 7 launches per layer")
+    p.add_argument("--launch", default="gemv", choices=["gemv", "chain"],
+                   help="one w4a16_gemv launch per matrix, or w4a16_gemv_chain: the "
+                        "sweep's matrices as dependent stages, 64 per launch")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-layers", type=int, default=16,
                    help="layers of the sweep the CPU oracle is timed on")
@@ -234,7 +237,17 @@ def main() -> int:
                 w4a16.gemv(x, p, s_, y=y)
         return step
 
-    step = make_step(launches)
+    sync = w4a16.chain_sync_buffer(dev)
+
+    def make_chain_step(seq):
+        parts = [seq[i:i + w4a16.CHAIN_MAX] for i in range(0, len(seq), w4a16.CHAIN_MAX)]
+
+        def step():
+            for part in parts:
+                w4a16.gemv_chain(part, sync)
+        return step
+
+    step = make_step(launches) if args.launch == "gemv" else make_chain_step(launches)
     stream = torch.cuda.current_stream()
     step()  # first call: device checks outside any capture
     torch.cuda.synchronize()
@@ -304,7 +317,28 @@ def main() -> int:
 
     other = None
     per_shape = None
+    other_launch = None
     if not args.no_shapes:
+        g2 = torch.cuda.CUDAGraph()
+        alt = make_chain_step(launches) if args.launch == "gemv" else make_step(launches)
+        alt()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g2):
+            alt()
+        for _ in range(3):
+            g2.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(10):
+            g2.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / 10
+        other_launch = {"launch": "chain" if args.launch == "gemv" else "gemv",
+                        "us_per_sweep": round(us, 2),
+                        "GB/s": round(step_bytes / (us * 1e-6) / 1e9, 1),
+                        "sync_words_nonzero": int((sync != 0).sum().item())}
+        del g2
         other_seq = separate_launches if args.layout == "fused" else fused_launches
         other_bytes = sum(gemv_bytes(int(p.shape[0]), int(p.shape[1]) * 8) for _, p, _, _ in other_seq)
         us = time_graph(other_seq)
@@ -375,7 +409,10 @@ def main() -> int:
                    "M": 1, "layout": args.layout,
                    "launch_groups": ["+".join(x[-1][i][0] for i in range(len(x[-1])))
                                      for x in layer0],
-                   "launches_per_step": n_launch, "bytes_per_step": step_bytes,
+                   "launch": args.launch,
+                   "launches_per_step": n_launch if args.launch == "gemv" else
+                   (n_launch + w4a16.CHAIN_MAX - 1) // w4a16.CHAIN_MAX,
+                   "gemvs_per_step": n_launch, "bytes_per_step": step_bytes,
                    "weight_bytes_resident": weight_bytes, "mode": args.mode,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(step_bytes / n_launch / (avg_launch_us * 1e-6)
@@ -389,6 +426,7 @@ def main() -> int:
                      "bytes_per_launch_avg": step_bytes // n_launch},
         "cpu_baseline": cpu,
         "other_layout": other,
+        "other_launch": other_launch,
         "per_shape": per_shape,
         "parity": parity,
         "secondary": sec,

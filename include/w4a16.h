@@ -119,6 +119,44 @@ int w4a16_gemm(const uint16_t* X, int64_t M, const uint32_t* packed, const uint1
 int w4a16_gemm_ex(const uint16_t* X, int64_t M, const uint32_t* packed, const uint16_t* scales,
                   int64_t N, int64_t K, uint16_t* Y, int algo, void* stream);
 
+/* ---- Dependent decode sequence ([BENCH] §二: every decode step streams
+ * the layers' matrices one after another, each fed by the one before).
+ * Runs stages[0..count) as if w4a16_gemv were called on each in order on
+ * `stream`, in ONE launch: stage s may read the output of any earlier stage
+ * as its x (e.g. stages[s].x == stages[s-1].y).  Outputs are bit-identical
+ * to separate w4a16_gemv calls.  The grid synchronizes between stages
+ * through `sync`, and the weights of the next stage are already streaming
+ * while the grid waits.
+ *   stages   HOST array of `count` stage descriptors (copied at the call)
+ *   count    0 .. W4A16_CHAIN_MAX (0 enqueues nothing)
+ *   sync     DEVICE buffer of W4A16_CHAIN_SYNC_WORDS uint32, owned by the
+ *            caller, all zero before the first call; every call leaves it
+ *            zero again.  Word W4A16_CHAIN_ERR_WORD becomes non-zero (and
+ *            stays so) if a wait between stages ever gives up; it is never
+ *            cleared by the library.  Calls sharing one `sync` buffer must not
+ *            overlap in time (stream-ordered calls are fine).
+ * Per stage: 128 <= K <= 32768, K % 128 == 0, 1 <= N <= 2^24; x, packed
+ * 16-byte aligned; scales, y 2-byte aligned; y must not overlap any
+ * stage's packed or scales, or its own stage's x (outputs of different
+ * stages may alias each other and later stages' inputs: stages run in
+ * order).
+ * The GPU must be otherwise idle enough for the grid (sized from occupancy)
+ * to be co-resident, as on a dedicated decode stream. */
+#define W4A16_CHAIN_MAX 64
+#define W4A16_CHAIN_SYNC_WORDS 128
+#define W4A16_CHAIN_ERR_WORD 65
+
+typedef struct {
+    const uint16_t* x;       /* fp16 [K] */
+    const uint32_t* packed;  /* uint32 [N, K/8] */
+    const uint16_t* scales;  /* fp16 [N, K/128] */
+    uint16_t* y;             /* fp16 [N] */
+    int64_t N;
+    int64_t K;
+} w4a16_gemv_stage;
+
+int w4a16_gemv_chain(const w4a16_gemv_stage* stages, int count, uint32_t* sync, void* stream);
+
 /* Largest M that W4A16_ALGO_AUTO sends to the VALU path. */
 int64_t w4a16_valu_max_m(void);
 

@@ -137,3 +137,31 @@ def test_binding_rejects_bad_tensors():
         w4a16.gemm(torch.zeros(2, 128, dtype=torch.float32),
                    torch.zeros(4, 16, dtype=torch.int32),
                    torch.zeros(4, 1, dtype=torch.float16))
+
+
+def test_chain_validation(lib):
+    from weight_only_int4_gemv_amd.w4a16 import GemvStage
+    A, B, C, D, S = FAKE, FAKE * 4, FAKE * 8, FAKE * 12, FAKE * 16
+    ch = lib.w4a16_gemv_chain
+
+    def arr(*stages):
+        a = (GemvStage * len(stages))()
+        for i, s in enumerate(stages):
+            a[i] = s
+        return a
+    ok = GemvStage(A, B, C, D, 16, 128)
+    assert ch(arr(ok), 0, S, None) == OK                      # empty: nothing enqueued
+    assert ch(arr(ok), -1, S, None) == INVALID
+    assert ch(arr(ok), 65, S, None) == INVALID
+    assert ch(arr(ok), 1, None, None) == INVALID
+    assert ch(arr(ok), 1, S + 2, None) == MISALIGNED
+    assert ch(arr(GemvStage(A, B, C, D, 16, 100)), 1, S, None) == SHAPE
+    assert ch(arr(GemvStage(A, B, C, D, 16, 0)), 1, S, None) == SHAPE
+    assert ch(arr(GemvStage(A, B, C, D, 16, 32768 + 128)), 1, S, None) == INVALID
+    assert ch(arr(GemvStage(A, B, C, D, 0, 128)), 1, S, None) == INVALID
+    assert ch(arr(GemvStage(A + 8, B, C, D, 16, 128)), 1, S, None) == MISALIGNED
+    assert ch(arr(GemvStage(A, B, C, A + 64, 16, 128)), 1, S, None) == INVALID   # y on own x
+    assert ch(arr(GemvStage(A, B, C, B, 16, 128)), 1, S, None) == INVALID       # y on packed
+    assert ch(arr(GemvStage(A, B, C, D, 16, 128), GemvStage(A, B + 1024, D, D + 256, 16, 128)),
+              2, S, None) == INVALID                                           # y on scales
+    assert ch(arr(GemvStage(A, B, C, D, 16, 128)), 1, D, None) == INVALID      # sync on y

@@ -140,6 +140,58 @@ int w4a16_gemm_ex(const uint16_t* X, int64_t M, const uint32_t* packed, const ui
     return linear(X, M, packed, scales, N, K, Y, algo, stream);
 }
 
+int w4a16_gemv_chain(const w4a16_gemv_stage* stages, int count, uint32_t* sync, void* stream) {
+    static_assert(W4A16_CHAIN_MAX == w4a16::kChainMax, "chain limit");
+    static_assert(W4A16_CHAIN_SYNC_WORDS == w4a16::kChainSyncWords, "sync words");
+    static_assert(W4A16_CHAIN_ERR_WORD == w4a16::kChainErrWord, "error word");
+    if (count < 0 || count > W4A16_CHAIN_MAX) return W4A16_ERR_INVALID_ARG;
+    if (count == 0) return W4A16_OK;
+    if (!stages || !sync) return W4A16_ERR_INVALID_ARG;
+    if (!aligned(sync, 4)) return W4A16_ERR_MISALIGNED;
+    const size_t sync_bytes = (size_t)W4A16_CHAIN_SYNC_WORDS * 4;
+    w4a16::ChainArgs args;
+    memset(&args, 0, sizeof(args));
+    int64_t max_k = 0;
+    for (int s = 0; s < count; ++s) {
+        const w4a16_gemv_stage& st = stages[s];
+        if (st.N < 1 || st.N > kMaxRows || st.K < 0 || st.K > 32768) return W4A16_ERR_INVALID_ARG;
+        if (st.K % W4A16_GROUP != 0 || st.K == 0) return W4A16_ERR_SHAPE;
+        if (!st.x || !st.packed || !st.scales || !st.y) return W4A16_ERR_INVALID_ARG;
+        if (!aligned(st.x, 16) || !aligned(st.packed, 16) || !aligned(st.scales, 2) ||
+            !aligned(st.y, 2))
+            return W4A16_ERR_MISALIGNED;
+        if (st.K > max_k) max_k = st.K;
+    }
+    for (int s = 0; s < count; ++s) {
+        const w4a16_gemv_stage& a = stages[s];
+        const size_t yb = (size_t)a.N * 2;
+        if (overlap(a.y, yb, a.x, (size_t)a.K * 2) || overlap(a.y, yb, sync, sync_bytes) ||
+            overlap(a.x, (size_t)a.K * 2, sync, sync_bytes))
+            return W4A16_ERR_INVALID_ARG;
+        for (int t = 0; t < count; ++t) {
+            const w4a16_gemv_stage& b = stages[t];
+            // Stages run in order, so outputs may alias each other and later
+            // inputs; weights are prefetched across stages, so no output may
+            // alias any stage's weights.
+            if (overlap(a.y, yb, b.packed, (size_t)b.N * b.K / 2) ||
+                overlap(a.y, yb, b.scales, (size_t)b.N * (b.K / W4A16_GROUP) * 2))
+                return W4A16_ERR_INVALID_ARG;
+            if (overlap(sync, sync_bytes, b.packed, (size_t)b.N * b.K / 2) ||
+                overlap(sync, sync_bytes, b.scales, (size_t)b.N * (b.K / W4A16_GROUP) * 2))
+                return W4A16_ERR_INVALID_ARG;
+        }
+        args.st[s] = w4a16::ChainStageDev{a.x, a.packed, a.scales, a.y, (int)a.N, (int)a.K};
+    }
+    args.count = count;
+    args.sync = sync;
+    int num_cu = 0;
+    const int st = current_device(&num_cu);
+    if (st != W4A16_OK) return st;
+    int blocks = 0;
+    return status_of(w4a16::launch_gemv_chain(args, max_k, static_cast<hipStream_t>(stream),
+                                              num_cu, &blocks));
+}
+
 int64_t w4a16_valu_max_m(void) { return kValuMaxM; }
 
 const char* w4a16_status_string(int status) {

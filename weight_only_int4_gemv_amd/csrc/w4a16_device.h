@@ -112,4 +112,25 @@ __device__ __forceinline__ void dequant_word(uint32_t w, half2_t s2, half2_t (&o
     out[3] = q[3] * s2;
 }
 
+// Cache policy of the weight stream: non-temporal (the loads' slc/nt bit).
+constexpr int kStreamLoad = 2;
+
+// Sum over the 64 lanes with DPP row operations (gfx9 wave64 pattern):
+// butterflies inside quads, mirrors inside 16-lane rows, then row broadcasts
+// 15 and 31.  The total ends in lane 63.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_add(float v) {
+    const int moved = __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, false);
+    return v + __int_as_float(moved);
+}
+__device__ __forceinline__ float wave_sum_lane63(float v) {
+    v = dpp_add<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+    v = dpp_add<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+    v = dpp_add<0x141, 0xF>(v);  // row_half_mirror
+    v = dpp_add<0x140, 0xF>(v);  // row_mirror: every lane holds its row's sum
+    v = dpp_add<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+    v = dpp_add<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+    return v;
+}
+
 }  // namespace w4a16

@@ -21,4 +21,28 @@ hipError_t launch_gemm_mfma(const uint16_t* X, int64_t M, const uint32_t* packed
                             const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y,
                             hipStream_t stream, int num_cu);
 
+// Dependent sequence of M = 1 GEMVs in one launch (gemv_chain.hip).
+constexpr int kChainMax = 64;           // stages per launch (kernel-argument size)
+constexpr int kChainDoneWord = kChainMax;
+constexpr int kChainErrWord = kChainMax + 1;
+constexpr int kChainSyncWords = 128;
+
+struct ChainStageDev {
+    const uint16_t* x;
+    const uint32_t* packed;
+    const uint16_t* scales;
+    uint16_t* y;
+    int N;
+    int K;
+};
+struct ChainArgs {
+    ChainStageDev st[kChainMax];
+    int count;
+    uint32_t* sync;
+};
+
+// Launches a co-resident grid; *blocks_out receives its size.
+hipError_t launch_gemv_chain(const ChainArgs& args, int64_t max_k, hipStream_t stream,
+                             int num_cu, int* blocks_out);
+
 }  // namespace w4a16

@@ -26,6 +26,17 @@ _i64 = ctypes.c_int64
 _lib = None
 
 
+CHAIN_MAX = 64
+CHAIN_SYNC_WORDS = 128
+CHAIN_ERR_WORD = 65
+
+
+class GemvStage(ctypes.Structure):
+    """w4a16_gemv_stage of include/w4a16.h."""
+    _fields_ = [("x", _p), ("packed", _p), ("scales", _p), ("y", _p),
+                ("N", _i64), ("K", _i64)]
+
+
 class W4A16Error(RuntimeError):
     """A non-zero status from the library."""
 
@@ -53,6 +64,8 @@ def library() -> ctypes.CDLL:
         for f in (lib.w4a16_quantize, lib.w4a16_gemv, lib.w4a16_gemm, lib.w4a16_gemm_ex):
             f.restype = ctypes.c_int
         lib.w4a16_valu_max_m.restype = ctypes.c_int64
+        lib.w4a16_gemv_chain.argtypes = [ctypes.POINTER(GemvStage), ctypes.c_int, _p, _p]
+        lib.w4a16_gemv_chain.restype = ctypes.c_int
         lib.w4a16_status_string.argtypes = [ctypes.c_int]
         lib.w4a16_status_string.restype = ctypes.c_char_p
         _lib = lib
@@ -161,6 +174,38 @@ def gemm(X: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, algo=None,
                                               scales.data_ptr(), N, K, Y.data_ptr(),
                                               _ALGOS[algo], _stream()))
     return Y
+
+
+def chain_sync_buffer(device="cuda") -> torch.Tensor:
+    """A zeroed sync buffer for gemv_chain (W4A16_CHAIN_SYNC_WORDS int32)."""
+    return torch.zeros(CHAIN_SYNC_WORDS, dtype=torch.int32, device=device)
+
+
+def gemv_chain(stages, sync: torch.Tensor) -> None:
+    """Run a dependent sequence of decode GEMVs in one launch.
+
+    stages: list of (x [K], packed [N, K/8], scales [N, K/128], y [N]) device
+    tensors; x of a stage may be the y of an earlier stage (or a view of it).
+    sync: int32 [CHAIN_SYNC_WORDS] device tensor from chain_sync_buffer().
+    """
+    lib = library()
+    if len(stages) > CHAIN_MAX:
+        raise ValueError("at most %d stages per call" % CHAIN_MAX)
+    _need(sync, "sync", torch.int32, 1)
+    if sync.shape[0] < CHAIN_SYNC_WORDS:
+        raise ValueError("sync needs %d words" % CHAIN_SYNC_WORDS)
+    arr = (GemvStage * max(1, len(stages)))()
+    for i, (x, packed, scales, y) in enumerate(stages):
+        N, K = _weights(packed, scales)
+        _need(x, "x", torch.float16, 1)
+        _need(y, "y", torch.float16, 1)
+        if x.shape[0] != K or y.shape[0] != N:
+            raise ValueError("stage %d: x has %d elements (K = %d), y %d (N = %d)"
+                             % (i, x.shape[0], K, y.shape[0], N))
+        arr[i] = GemvStage(x.data_ptr(), packed.data_ptr(), scales.data_ptr(), y.data_ptr(),
+                           N, K)
+    _check("w4a16_gemv_chain", lib.w4a16_gemv_chain(arr, len(stages), sync.data_ptr(),
+                                                    _stream()))
 
 
 def valu_max_m() -> int:
