@@ -224,6 +224,14 @@ def test_gemm_ragged_m(w4, orc, M, algo):
     check_linear(w4, orc, M, 300, 640, seed=([6], [6, M]), algo=algo, name="ragged")
 
 
+@pytest.mark.parametrize("M", [3, 16, 17, 33, 64])
+@pytest.mark.parametrize("N,K", [(5, 128), (40, 256), (50, 5120), (1000, 4224)])
+def test_mfma_long_rows(w4, orc, M, N, K):
+    """K > N: the K groups are split over waves (fewer groups than waves at
+    K = 128 and 256), ragged N and M tiles."""
+    check_linear(w4, orc, M, N, K, seed=([8, N, K], [8, N, K, M]), algo="mfma", name="long rows")
+
+
 @pytest.mark.parametrize("K,N", [(4096, 14336), (14336, 4096), (8192, 28672)])
 def test_prefill_512(w4, orc, K, N):
     check_linear(w4, orc, 512, N, K, seed=[5, K, N], algo="auto", name="prefill")
@@ -302,7 +310,8 @@ def test_empty_m_and_n(w4):
     assert Y.shape == (3, 0)
 
 
-@pytest.mark.parametrize("M,algo", [(1, "gemv"), (3, "valu"), (20, "mfma"), (130, "mfma")])
+@pytest.mark.parametrize("M,algo", [(1, "gemv"), (3, "valu"), (20, "mfma"), (64, "mfma"),
+                                    (130, "mfma")])
 def test_outputs_stay_inside_their_buffer(w4, orc, M, algo):
     """Canary words around Y must survive (no out-of-bounds stores)."""
     N, K = 333, 768
@@ -322,9 +331,10 @@ def test_outputs_stay_inside_their_buffer(w4, orc, M, algo):
     assert not np.isnan(buf[pad:pad + M * N].cpu().numpy()).any()
 
 
-@pytest.mark.parametrize("M,algo", [(1, "gemv"), (8, "valu"), (32, "mfma"), (512, "mfma")])
-def test_deterministic_and_stream_ordered(w4, orc, M, algo):
-    N, K = 2048, 2048
+@pytest.mark.parametrize("M,algo,N", [(1, "gemv", 2048), (8, "valu", 2048), (32, "mfma", 2048),
+                                      (16, "mfma", 1024), (512, "mfma", 2048)])
+def test_deterministic_and_stream_ordered(w4, orc, M, algo, N):
+    K = 2048
     W, X = inputs.weight_and_activation(N, K, M, seed=[24, M])
     packed, scales = orc.quantize(W)
     pd, sd, Xd = packed_to_dev(packed), scales_to_dev(scales), dev(X)

@@ -14,7 +14,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libw4a16.so")
-SOURCES = ["api.hip", "quantize.hip", "gemv.hip", "gemv_chain.hip", "gemm_mfma.hip"]
+SOURCES = ["api.hip", "quantize.hip", "gemv.hip", "gemv_chain.hip", "gemm_mfma.hip",
+           "gemm_skinny.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -225,6 +225,10 @@ hipError_t launch_mfma_t(const uint16_t* X, int64_t M, const uint32_t* packed,
 hipError_t launch_gemm_mfma(const uint16_t* X, int64_t M, const uint32_t* packed,
                             const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y,
                             hipStream_t stream, int num_cu) {
+    // Few rows and K > N (few output tiles, long rows): the streaming kernel
+    // with the K groups split over waves.
+    if (M <= 64 && K > N && K <= kSkinnyMaxK)
+        return launch_gemm_skinny(X, M, packed, scales, N, K, Y, stream, num_cu);
     // Few rows: one 16- or 32-row tile, waves split K; enough column tiles
     // to give every compute unit work.
     if (M <= 16) {
@@ -238,7 +242,13 @@ hipError_t launch_gemm_mfma(const uint16_t* X, int64_t M, const uint32_t* packed
         return launch_mfma_t<2, 1, 1, 1, 4>(X, M, packed, scales, N, K, Y, stream);
     }
     if (M <= 64) return launch_mfma_t<2, 2, 2, 2, 1>(X, M, packed, scales, N, K, Y, stream);
-    return launch_mfma_t<4, 4, 2, 2, 1>(X, M, packed, scales, N, K, Y, stream);
+    // Prefill: 128 x 128 block tiles (eight 16-row tiles by two 16-column
+    // tiles per wave, four waves across N) when they fill the compute units,
+    // else 128 x 64.
+    const int64_t tiles128 = ((M + 127) / 128) * ((N + 127) / 128);
+    if (tiles128 >= num_cu)
+        return launch_mfma_t<8, 2, 1, 4, 1>(X, M, packed, scales, N, K, Y, stream);
+    return launch_mfma_t<4, 2, 2, 2, 1>(X, M, packed, scales, N, K, Y, stream);
 }
 
 }  // namespace w4a16

@@ -21,6 +21,13 @@ hipError_t launch_gemm_mfma(const uint16_t* X, int64_t M, const uint32_t* packed
                             const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y,
                             hipStream_t stream, int num_cu);
 
+// MFMA path for few rows of X (gemm_skinny.hip): weights streamed once,
+// waves split K.  Requires K <= kSkinnyMaxK (32-bit buffer offsets).
+constexpr int64_t kSkinnyMaxK = (int64_t)1 << 24;
+hipError_t launch_gemm_skinny(const uint16_t* X, int64_t M, const uint32_t* packed,
+                              const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y,
+                              hipStream_t stream, int num_cu);
+
 // Dependent sequence of M = 1 GEMVs in one launch (gemv_chain.hip).
 constexpr int kChainMax = 64;           // stages per launch (kernel-argument size)
 constexpr int kChainDoneWord = kChainMax;
