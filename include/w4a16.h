@@ -135,7 +135,7 @@ int w4a16_gemm_ex(const uint16_t* X, int64_t M, const uint32_t* packed, const ui
  *            stays so) if a wait between stages ever gives up; it is never
  *            cleared by the library.  Calls sharing one `sync` buffer must not
  *            overlap in time (stream-ordered calls are fine).
- * Per stage: 128 <= K <= 32768, K % 128 == 0, 1 <= N <= 2^24; x, packed
+ * Per stage: 128 <= K <= 32768, K % 128 == 0, 1 <= N <= 2^20; x, packed
  * 16-byte aligned; scales, y 2-byte aligned; y must not overlap any
  * stage's packed or scales, or its own stage's x (outputs of different
  * stages may alias each other and later stages' inputs: stages run in
@@ -143,8 +143,8 @@ int w4a16_gemm_ex(const uint16_t* X, int64_t M, const uint32_t* packed, const ui
  * The GPU must be otherwise idle enough for the grid (sized from occupancy)
  * to be co-resident, as on a dedicated decode stream. */
 #define W4A16_CHAIN_MAX 64
-#define W4A16_CHAIN_SYNC_WORDS 128
-#define W4A16_CHAIN_ERR_WORD 65
+#define W4A16_CHAIN_SYNC_WORDS 1024
+#define W4A16_CHAIN_ERR_WORD 0
 
 typedef struct {
     const uint16_t* x;       /* fp16 [K] */

@@ -159,6 +159,7 @@ def test_chain_validation(lib):
     assert ch(arr(GemvStage(A, B, C, D, 16, 0)), 1, S, None) == SHAPE
     assert ch(arr(GemvStage(A, B, C, D, 16, 32768 + 128)), 1, S, None) == INVALID
     assert ch(arr(GemvStage(A, B, C, D, 0, 128)), 1, S, None) == INVALID
+    assert ch(arr(GemvStage(A, B, C, D, (1 << 20) + 1, 128)), 1, S, None) == INVALID
     assert ch(arr(GemvStage(A + 8, B, C, D, 16, 128)), 1, S, None) == MISALIGNED
     assert ch(arr(GemvStage(A, B, C, A + 64, 16, 128)), 1, S, None) == INVALID   # y on own x
     assert ch(arr(GemvStage(A, B, C, B, 16, 128)), 1, S, None) == INVALID       # y on packed

@@ -151,16 +151,18 @@ int w4a16_gemv_chain(const w4a16_gemv_stage* stages, int count, uint32_t* sync, 
     const size_t sync_bytes = (size_t)W4A16_CHAIN_SYNC_WORDS * 4;
     w4a16::ChainArgs args;
     memset(&args, 0, sizeof(args));
-    int64_t max_k = 0;
+    int64_t max_k = 0, max_n = 0;
     for (int s = 0; s < count; ++s) {
         const w4a16_gemv_stage& st = stages[s];
-        if (st.N < 1 || st.N > kMaxRows || st.K < 0 || st.K > 32768) return W4A16_ERR_INVALID_ARG;
+        if (st.N < 1 || st.N > w4a16::kChainMaxN || st.K < 0 || st.K > w4a16::kChainMaxK)
+            return W4A16_ERR_INVALID_ARG;
         if (st.K % W4A16_GROUP != 0 || st.K == 0) return W4A16_ERR_SHAPE;
         if (!st.x || !st.packed || !st.scales || !st.y) return W4A16_ERR_INVALID_ARG;
         if (!aligned(st.x, 16) || !aligned(st.packed, 16) || !aligned(st.scales, 2) ||
             !aligned(st.y, 2))
             return W4A16_ERR_MISALIGNED;
         if (st.K > max_k) max_k = st.K;
+        if (st.N > max_n) max_n = st.N;
     }
     for (int s = 0; s < count; ++s) {
         const w4a16_gemv_stage& a = stages[s];
@@ -183,12 +185,13 @@ int w4a16_gemv_chain(const w4a16_gemv_stage* stages, int count, uint32_t* sync, 
         args.st[s] = w4a16::ChainStageDev{a.x, a.packed, a.scales, a.y, (int)a.N, (int)a.K};
     }
     args.count = count;
+    args.x_vecs = (int)(max_k / 8);
     args.sync = sync;
     int num_cu = 0;
     const int st = current_device(&num_cu);
     if (st != W4A16_OK) return st;
     int blocks = 0;
-    return status_of(w4a16::launch_gemv_chain(args, max_k, static_cast<hipStream_t>(stream),
+    return status_of(w4a16::launch_gemv_chain(args, max_n, static_cast<hipStream_t>(stream),
                                               num_cu, &blocks));
 }
 

@@ -30,9 +30,13 @@ hipError_t launch_gemm_skinny(const uint16_t* X, int64_t M, const uint32_t* pack
 
 // Dependent sequence of M = 1 GEMVs in one launch (gemv_chain.hip).
 constexpr int kChainMax = 64;           // stages per launch (kernel-argument size)
-constexpr int kChainDoneWord = kChainMax;
-constexpr int kChainErrWord = kChainMax + 1;
-constexpr int kChainSyncWords = 128;
+constexpr int kChainMaxK = 32768;       // x of a stage is held in LDS
+constexpr int64_t kChainMaxN = (int64_t)1 << 20;
+constexpr int kChainLineWords = 64;     // sync counters 256 bytes apart
+constexpr int kChainLeaves = 8;         // first level of the arrival tree
+constexpr int kChainErrWord = 0;
+constexpr int kChainSyncWords = 1024;
+static_assert((3 + kChainLeaves) * kChainLineWords <= kChainSyncWords, "sync layout");
 
 struct ChainStageDev {
     const uint16_t* x;
@@ -45,11 +49,13 @@ struct ChainStageDev {
 struct ChainArgs {
     ChainStageDev st[kChainMax];
     int count;
+    int x_vecs;          // LDS x capacity in 16-byte vectors (max K / 8)
     uint32_t* sync;
 };
 
-// Launches a co-resident grid; *blocks_out receives its size.
-hipError_t launch_gemv_chain(const ChainArgs& args, int64_t max_k, hipStream_t stream,
+// Launches one block per compute unit (co-resident); *blocks_out receives
+// the grid size.  max_n: the largest N of the stages.
+hipError_t launch_gemv_chain(const ChainArgs& args, int64_t max_n, hipStream_t stream,
                              int num_cu, int* blocks_out);
 
 }  // namespace w4a16

@@ -27,8 +27,8 @@ _lib = None
 
 
 CHAIN_MAX = 64
-CHAIN_SYNC_WORDS = 128
-CHAIN_ERR_WORD = 65
+CHAIN_SYNC_WORDS = 1024
+CHAIN_ERR_WORD = 0
 
 
 class GemvStage(ctypes.Structure):
