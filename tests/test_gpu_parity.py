@@ -243,7 +243,7 @@ def test_70b_ffn_decode(w4, orc):
 
 # -------------------------------------------------------------- exact cases
 
-@pytest.mark.parametrize("algo", ["gemv", "valu", "mfma"])
+@pytest.mark.parametrize("algo", ["gemv", "valu", "mfma", "mfma-4rows"])
 def test_one_hot_activations_are_exact(w4, orc, algo):
     """x = e_k reproduces fp16(s*q) of column k exactly, for every k of two
     groups: checks nibble order, word order and scale indexing."""
@@ -262,6 +262,14 @@ def test_one_hot_activations_are_exact(w4, orc, algo):
                 x[0, k] = 1
                 rows.append(run_linear(w4, x, packed, scales, "gemv")[0])
             Y = np.stack(rows)
+        elif algo == "mfma-4rows":
+            # four rows per call: the 4x4x4 matrix-core GEMV
+            parts = []
+            for i in range(0, len(ks), 4):
+                X = np.zeros((4, K), dtype=np.float16)
+                X[np.arange(4), ks[i:i + 4]] = 1
+                parts.append(run_linear(w4, X, packed, scales, "mfma"))
+            Y = np.concatenate(parts)
         else:
             X = np.zeros((len(ks), K), dtype=np.float16)
             X[np.arange(len(ks)), ks] = 1
@@ -310,8 +318,8 @@ def test_empty_m_and_n(w4):
     assert Y.shape == (3, 0)
 
 
-@pytest.mark.parametrize("M,algo", [(1, "gemv"), (3, "valu"), (20, "mfma"), (64, "mfma"),
-                                    (130, "mfma")])
+@pytest.mark.parametrize("M,algo", [(1, "gemv"), (3, "valu"), (3, "mfma"), (20, "mfma"),
+                                    (64, "mfma"), (130, "mfma")])
 def test_outputs_stay_inside_their_buffer(w4, orc, M, algo):
     """Canary words around Y must survive (no out-of-bounds stores)."""
     N, K = 333, 768
@@ -331,8 +339,8 @@ def test_outputs_stay_inside_their_buffer(w4, orc, M, algo):
     assert not np.isnan(buf[pad:pad + M * N].cpu().numpy()).any()
 
 
-@pytest.mark.parametrize("M,algo,N", [(1, "gemv", 2048), (8, "valu", 2048), (32, "mfma", 2048),
-                                      (16, "mfma", 1024), (512, "mfma", 2048)])
+@pytest.mark.parametrize("M,algo,N", [(1, "gemv", 2048), (8, "valu", 2048), (4, "mfma", 2048),
+                                      (32, "mfma", 2048), (16, "mfma", 1024), (512, "mfma", 2048)])
 def test_deterministic_and_stream_ordered(w4, orc, M, algo, N):
     K = 2048
     W, X = inputs.weight_and_activation(N, K, M, seed=[24, M])

@@ -16,7 +16,7 @@ constexpr int64_t kMaxRows = (int64_t)1 << 24;
 constexpr int64_t kMaxK = ((int64_t)1 << 31) - 128;
 
 // Largest M sent to the VALU path by W4A16_ALGO_AUTO.
-constexpr int64_t kValuMaxM = 8;
+constexpr int64_t kValuMaxM = 2;
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 

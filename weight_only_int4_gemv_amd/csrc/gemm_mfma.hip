@@ -225,6 +225,10 @@ hipError_t launch_mfma_t(const uint16_t* X, int64_t M, const uint32_t* packed,
 hipError_t launch_gemm_mfma(const uint16_t* X, int64_t M, const uint32_t* packed,
                             const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y,
                             hipStream_t stream, int num_cu) {
+    // Up to four rows: the streaming GEMV on 4x4x4 matrix-core blocks while
+    // x fits in LDS (K == 0, all outputs zero, stays on the tiled kernel).
+    if (M <= kMfma4MaxM && K > 0 && M * K * 2 <= kMfma4MaxXBytes)
+        return launch_gemv_mfma4(X, M, packed, scales, N, K, Y, stream, num_cu);
     // Few rows and K > N (few output tiles, long rows): the streaming kernel
     // with the K groups split over waves.
     if (M <= 64 && K > N && K <= kSkinnyMaxK)

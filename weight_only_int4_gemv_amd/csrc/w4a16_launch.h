@@ -21,6 +21,14 @@ hipError_t launch_gemm_mfma(const uint16_t* X, int64_t M, const uint32_t* packed
                             const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y,
                             hipStream_t stream, int num_cu);
 
+// MFMA GEMV for M <= 4 with x resident in LDS (gemv_mfma4.hip): the weight
+// stream of the VALU GEMV, products on v_mfma_f32_4x4x4_16b_f16.
+constexpr int64_t kMfma4MaxM = 4;
+constexpr int64_t kMfma4MaxXBytes = 128 * 1024;
+hipError_t launch_gemv_mfma4(const uint16_t* X, int64_t M, const uint32_t* packed,
+                             const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y,
+                             hipStream_t stream, int num_cu);
+
 // MFMA path for few rows of X (gemm_skinny.hip): weights streamed once,
 // waves split K.  Requires K <= kSkinnyMaxK (32-bit buffer offsets).
 constexpr int64_t kSkinnyMaxK = (int64_t)1 << 24;
