@@ -13,8 +13,7 @@ and replayed.
 Prints one JSON line: effective HBM GB/s of the sweep (algorithmic bytes
 N*K/2 + N*K/64 + 2K + 2N per GEMV over the measured time), us per sweep,
 the roofline of the launch with the largest share of the sweep (gate_up), and
-the CPU oracle timed on a sample of the
-same sweep.
+the CPU oracle timed on a sample of the same sweep.
 
     python bench.py [--steps 20] [--warmup 5] [--workload llama3-8b-sweep]
 """
