@@ -131,6 +131,34 @@ def test_quantize_edge_values(w4, orc):
     check_quantize(w4, orc, W, "edge values")
 
 
+def test_quantize_ties_and_near_ties(w4, orc):
+    """Quotients w/s that are exact half-integers (round half to even) and
+    values one fp16 step either side of them, for scales 2^e (e = -14..0)
+    and for scales that are not powers of two."""
+    rows = []
+    rng = np.random.default_rng(78)
+    for e in range(-14, 1):
+        s = 2.0 ** e
+        a = np.float16(7 * s)                      # absmax: s = fp16(a / 7) = 2^e
+        ties = np.array([(k + 0.5) * s for k in range(-7, 6)], dtype=np.float64)
+        vals = np.concatenate([ties, -ties]).astype(np.float16)
+        up = np.nextafter(vals, np.float16(np.inf))
+        dn = np.nextafter(vals, np.float16(-np.inf))
+        g = np.concatenate([vals, up, dn])
+        g = np.resize(np.concatenate([g, rng.permutation(g)]), 127)
+        rows.append(np.concatenate([[a], g]).astype(np.float16))
+    for a in (0.1, 0.37, 1.9, 5.3, 200.0):         # s not a power of two
+        s = float(np.float16(np.float16(a) / 7.0))
+        ties = np.array([(k + 0.5) * s for k in range(-7, 6)])
+        vals = ties.astype(np.float16)             # ties up to fp16 rounding
+        up = np.nextafter(vals, np.float16(np.inf))
+        g = np.resize(np.concatenate([vals, up, -vals, -up]), 127)
+        rows.append(np.concatenate([[np.float16(a)], g]).astype(np.float16))
+    W = np.stack(rows)
+    W = np.concatenate([W, W[:, ::-1]], axis=1)    # K = 256
+    check_quantize(w4, orc, np.ascontiguousarray(W), "ties")
+
+
 def test_quantize_empty_and_deterministic(w4, orc):
     say("quantize empty")
     p, s = w4.quantize(torch.empty((0, 256), dtype=torch.float16, device="cuda"))

@@ -12,72 +12,130 @@
 //     magnitudes is the order of their bit patterns);
 //   - s = fp16_rne(a / 7) with an IEEE fp32 division; double rounding
 //     fp32 -> fp16 cannot change the result (24 >= 2*11 + 2);
-//   - q = clamp(rint(w / s), -8, 7) with an IEEE fp32 division and rint
-//     (half to even): for fp16 w and s a non-tie quotient is at least
-//     2^-15 (relative) away from a tie, so the fp32 quotient rounds to the
-//     same integer as the exact one.
+//   - q = clamp(rint(w / s), -8, 7) with rint (half to even) of the quotient
+//     rounded to fp32: for fp16 w and s a non-tie quotient is at least 2^-15
+//     (relative) away from a tie, so the fp32 quotient rounds to the same
+//     integer as the exact one.  The quotient is first formed as w * rcp(s)
+//     (v_rcp_f32, relative error below 2^-22; |w / s| <= 7.004, or < 10.5
+//     when s is an fp16 subnormal, so the product is within 3e-6 of w / s):
+//     it can round differently from w / s only if it lies within 3e-6 of a
+//     half-integer; a lane that sees a product within 2e-5 of one (about 2 in
+//     10^5 elements of Gaussian weights, and every exact tie) redoes its 8
+//     elements with the IEEE fp32 division.
 #include "w4a16_device.h"
 #include "w4a16_launch.h"
 
 namespace w4a16 {
 
+namespace {
+// max over the 16 lanes of a DPP row (quad butterflies, then half-row and
+// row mirrors); every lane of the row receives it.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_max(uint32_t v) {
+    return max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ uint32_t row_max16(uint32_t v) {
+    v = dpp_max<0xB1>(v);   // quad_perm [1,0,3,2]
+    v = dpp_max<0x4E>(v);   // quad_perm [2,3,0,1]
+    v = dpp_max<0x141>(v);  // row_half_mirror
+    v = dpp_max<0x140>(v);  // row_mirror
+    return v;
+}
+
+// One lane's 8 elements of a group -> its packed word, and the group scale.
+__device__ __forceinline__ uint32_t quantize8(const uint4& v, uint16_t& s_bits) {
+    uint32_t m = 0;
+    m = max(m, v.x & 0x7FFFu);
+    m = max(m, (v.x >> 16) & 0x7FFFu);
+    m = max(m, v.y & 0x7FFFu);
+    m = max(m, (v.y >> 16) & 0x7FFFu);
+    m = max(m, v.z & 0x7FFFu);
+    m = max(m, (v.z >> 16) & 0x7FFFu);
+    m = max(m, v.w & 0x7FFFu);
+    m = max(m, (v.w >> 16) & 0x7FFFu);
+    m = row_max16(m);
+    const float a = f16_bits_to_f32((uint16_t)m);
+    s_bits = f32_to_f16_bits(a / 7.0f);  // 2^(4-1) - 1 = 7, IEEE division
+    const float s = f16_bits_to_f32(s_bits);
+    if (s == 0.0f) return 0x88888888u;   // every code 0 (all 16 lanes alike)
+    const uint32_t h[4] = {v.x, v.y, v.z, v.w};
+    const float inv = __builtin_amdgcn_rcpf(s);
+    uint32_t word = 0;
+    bool near_tie = false;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float w = f16_bits_to_f32((uint16_t)(h[i >> 1] >> (16 * (i & 1))));
+        const float t = w * inv;
+        const float r = rintf(t);
+        near_tie |= fabsf(t - r) > 0.49998f;
+        // code = clamp(r, -8, 7) + 8, exact small integers in fp32
+        const float c = __builtin_amdgcn_fmed3f(r + 8.0f, 0.0f, 15.0f);
+        word |= (uint32_t)c << (4 * i);
+    }
+    if (near_tie) {
+        word = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float w = f16_bits_to_f32((uint16_t)(h[i >> 1] >> (16 * (i & 1))));
+            const float r = fminf(fmaxf(rintf(w / s), -8.0f), 7.0f);
+            word |= ((uint32_t)((int)r + 8) & 0xFu) << (4 * i);
+        }
+    }
+    return word;
+}
+}  // namespace
+
+// Each 16-lane row of a wave quantizes one group per step; the loads of U
+// steps (groups g, g + stride, ...) are issued together.  All 16 lanes of a
+// row share g, so the row reductions only ever combine lanes that are
+// active together.
+template <int U>
 __global__ __launch_bounds__(256) void quantize_kernel(const uint4* __restrict__ W,
                                                        uint32_t* __restrict__ packed,
                                                        uint16_t* __restrict__ scales,
                                                        int64_t total_groups) {
     const int lane16 = threadIdx.x & 15;
     const int64_t stride = (int64_t)gridDim.x * (blockDim.x / 16);
-    // The 16 lanes of a group always share g, so the row reductions below
-    // only ever combine lanes that are active together.
+    typedef unsigned v4u __attribute__((ext_vector_type(4)));
+    const v4u* Wv = reinterpret_cast<const v4u*>(W);
     for (int64_t g = (int64_t)blockIdx.x * (blockDim.x / 16) + (threadIdx.x >> 4);
-         g < total_groups; g += stride) {
-        const uint4 v = W[g * 16 + lane16];  // 8 fp16 of this group
-        uint32_t m = 0;
-        m = max(m, v.x & 0x7FFFu);
-        m = max(m, (v.x >> 16) & 0x7FFFu);
-        m = max(m, v.y & 0x7FFFu);
-        m = max(m, (v.y >> 16) & 0x7FFFu);
-        m = max(m, v.z & 0x7FFFu);
-        m = max(m, (v.z >> 16) & 0x7FFFu);
-        m = max(m, v.w & 0x7FFFu);
-        m = max(m, (v.w >> 16) & 0x7FFFu);
-        // max over the 16 lanes of this group
-        m = max(m, (uint32_t)__shfl_xor((int)m, 1, 16));
-        m = max(m, (uint32_t)__shfl_xor((int)m, 2, 16));
-        m = max(m, (uint32_t)__shfl_xor((int)m, 4, 16));
-        m = max(m, (uint32_t)__shfl_xor((int)m, 8, 16));
-
-        const float a = f16_bits_to_f32((uint16_t)m);
-        const uint16_t s_bits = f32_to_f16_bits(a / 7.0f);  // 2^(4-1) - 1 = 7
-        const float s = f16_bits_to_f32(s_bits);
-
-        uint32_t word = 0x88888888u;  // every code 0 when s == 0
-        if (s != 0.0f) {
-            const uint32_t h[4] = {v.x, v.y, v.z, v.w};
-            word = 0;
+         g < total_groups; g += U * stride) {
+        v4u a[U];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const uint16_t b = (uint16_t)(h[i >> 1] >> (16 * (i & 1)));
-                float r = rintf(f16_bits_to_f32(b) / s);
-                r = fminf(fmaxf(r, -8.0f), 7.0f);
-                word |= ((uint32_t)((int)r + 8) & 0xFu) << (4 * i);
+        for (int u = 0; u < U; ++u) {
+            // W is read once: non-temporal loads
+            a[u] = (v4u){0u, 0u, 0u, 0u};
+            if (g + u * stride < total_groups)
+                a[u] = __builtin_nontemporal_load(Wv + (g + u * stride) * 16 + lane16);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t gu = g + u * stride;
+            if (gu < total_groups) {
+                uint16_t sb;
+                const uint32_t word = quantize8(make_uint4(a[u].x, a[u].y, a[u].z, a[u].w), sb);
+                packed[gu * 16 + lane16] = word;
+                if (lane16 == 0) scales[gu] = sb;
             }
         }
-        packed[g * 16 + lane16] = word;
-        if (lane16 == 0) scales[g] = s_bits;
     }
+}
+
+template <int U>
+hipError_t launch_quantize_t(const uint16_t* W, int64_t groups, uint32_t* packed,
+                             uint16_t* scales, hipStream_t stream, int64_t max_blocks) {
+    int64_t blocks = (groups + 16 * U - 1) / (16 * U);   // 16 groups per block and step
+    if (blocks > max_blocks) blocks = max_blocks;        // grid-stride beyond this
+    hipLaunchKernelGGL((quantize_kernel<U>), dim3((unsigned)blocks), dim3(256), 0, stream,
+                       reinterpret_cast<const uint4*>(W), packed, scales, groups);
+    return hipGetLastError();
 }
 
 hipError_t launch_quantize(const uint16_t* W, int64_t N, int64_t K, uint32_t* packed,
                            uint16_t* scales, hipStream_t stream) {
     const int64_t groups = N * (K / kGroup);
     if (groups == 0) return hipSuccess;
-    const int threads = 256;                  // 16 groups per block
-    int64_t blocks = (groups + 15) / 16;
-    if (blocks > 65536) blocks = 65536;  // grid-stride beyond this
-    hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream,
-                       reinterpret_cast<const uint4*>(W), packed, scales, groups);
-    return hipGetLastError();
+    return launch_quantize_t<2>(W, groups, packed, scales, stream, 65536);
 }
 
 }  // namespace w4a16
