@@ -51,9 +51,11 @@ __global__ __launch_bounds__(WK * kWave) void gemm_skinny_kernel(
     const __amdgpu_buffer_rsrc_t empty = buffer_rsrc(packed, 0);
 
     typedef unsigned v4u __attribute__((ext_vector_type(4)));
+    // scales in 32-bit slots: 16-bit slots would be packed in pairs, and
+    // packing waits for both loads
     struct Slot {
         v4u b[TN];
-        uint16_t s[TN];
+        uint32_t s[TN];
         v4u a[TM][4];
     };
     // Blocks start their K ranges at different groups so that they do not
@@ -102,7 +104,7 @@ __global__ __launch_bounds__(WK * kWave) void gemm_skinny_kernel(
             half8_t bf[TN][4];
 #pragma unroll
             for (int tn = 0; tn < TN; ++tn) {
-                const _Float16 sh = __builtin_bit_cast(_Float16, sl.s[tn]);
+                const _Float16 sh = __builtin_bit_cast(_Float16, (uint16_t)sl.s[tn]);
                 const half2_t s2 = {sh, sh};
                 const uint32_t words[4] = {sl.b[tn].x, sl.b[tn].y, sl.b[tn].z, sl.b[tn].w};
 #pragma unroll

@@ -57,7 +57,7 @@ template <int MT, int U, int P, int WAVES>
 __global__ __launch_bounds__(WAVES * kWave) void gemv_mfma4_kernel(
     const uint16_t* __restrict__ X, int M, const uint32_t* __restrict__ packed,
     const uint16_t* __restrict__ scales, uint16_t* __restrict__ Y, int N, int K) {
-    extern __shared__ uint4 lds[];                    // [M][K/8] paired x
+    extern __shared__ uint4 lds[];                    // [M][K/8 + 1] paired x
     constexpr int Q = P + 1;
     constexpr int kRows = 4;
     constexpr int kStepK = 512 * U;                   // k per step
@@ -72,6 +72,7 @@ __global__ __launch_bounds__(WAVES * kWave) void gemv_mfma4_kernel(
     const int my_rg = first_rg < total_rg ? (total_rg - 1 - first_rg) / stride_rg + 1 : 0;
     const int T = my_rg * nsteps;
     const int xblk = K >> 3;                          // 8-element blocks per x row
+    const int xstride = xblk + 1;                     // 16-byte pad: rows start 4 banks apart
     const uint32_t wrow = (uint32_t)K / 2, srow = (uint32_t)K / 64;
     const CodeConsts kc = code_consts();
 
@@ -88,7 +89,7 @@ __global__ __launch_bounds__(WAVES * kWave) void gemv_mfma4_kernel(
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int i = i0 + j * WAVES * kWave;
-                if (i < total) lds[i] = pair_block(v[j].x, v[j].y, v[j].z, v[j].w);
+                if (i < total) lds[i + i / xblk] = pair_block(v[j].x, v[j].y, v[j].z, v[j].w);
             }
         }
     }
@@ -97,7 +98,9 @@ __global__ __launch_bounds__(WAVES * kWave) void gemv_mfma4_kernel(
     int tl = 0, lrg = first_rg, ls = 0;
     __amdgpu_buffer_rsrc_t wr = buffer_rsrc(packed, 0), sr = buffer_rsrc(scales, 0);
     typedef unsigned v4u __attribute__((ext_vector_type(4)));
-    auto load = [&](v4u (&wd)[U], uint16_t (&sd)[U]) {
+    // scales in 32-bit slots: 16-bit slots would be packed in pairs, and
+    // packing waits for both loads
+    auto load = [&](v4u (&wd)[U], uint32_t (&sd)[U]) {
         if (ls == 0) {
             const bool live = tl < T;
             const int64_t row0 = (int64_t)lrg * kRows;
@@ -123,7 +126,7 @@ __global__ __launch_bounds__(WAVES * kWave) void gemv_mfma4_kernel(
     };
 
     v4u wq[Q][U];
-    uint16_t sq[Q][U];
+    uint32_t sq[Q][U];
 #pragma unroll
     for (int i = 0; i < P; ++i) load(wq[i], sq[i]);
     __syncthreads();
@@ -154,7 +157,7 @@ __global__ __launch_bounds__(WAVES * kWave) void gemv_mfma4_kernel(
 #pragma unroll
                         for (int t = 0; t < MT; ++t) {
                             const int m = t * 4 + c;
-                            const uint4 xv = m < M ? lds[m * xblk + blk + w] : make_uint4(0, 0, 0, 0);
+                            const uint4 xv = m < M ? lds[m * xstride + blk + w] : make_uint4(0, 0, 0, 0);
                             const half4_t a0 = as_h4(xv.x, xv.y);
                             const half4_t a1 = as_h4(xv.z, xv.w);
                             if (w == 0)
@@ -165,7 +168,7 @@ __global__ __launch_bounds__(WAVES * kWave) void gemv_mfma4_kernel(
                             d[t] = __builtin_amdgcn_mfma_f32_4x4x4f16(a1, b1, d[t], 0, 0, 0);
                         }
                     }
-                    const float sc = valid ? f16_bits_to_f32(sq[i][u]) : 0.0f;
+                    const float sc = valid ? f16_bits_to_f32((uint16_t)sq[i][u]) : 0.0f;
 #pragma unroll
                     for (int t = 0; t < MT; ++t) {
                         acc[t][0] = fmaf(sc, d[t][0], acc[t][0]);
@@ -202,7 +205,7 @@ template <int MT, int U, int P, int WAVES>
 hipError_t launch_mfma4_t(const uint16_t* X, int64_t M, const uint32_t* packed,
                           const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y,
                           hipStream_t stream, int num_cu, int blocks_per_cu) {
-    const size_t lds = (size_t)M * K * 2;
+    const size_t lds = (size_t)M * (K / 8 + 1) * 16;
     const int64_t total_rg = (N + 3) / 4;
     const int64_t max_waves = (int64_t)num_cu * blocks_per_cu * WAVES;
     // balanced persistent grid: every wave gets the same number of row groups
