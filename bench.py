@@ -60,7 +60,10 @@ def parse():
                    help="one w4a16_gemv launch per matrix, or w4a16_gemv_chain: the "
                         "sweep's matrices as dependent stages, 64 per launch")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-layers", type=int, default=16,
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="CPU oracle baseline: layers are timed until this many seconds "
+                        "have passed (at least one layer, at most --cpu-layers)")
+    p.add_argument("--cpu-layers", type=int, default=128,
                    help="layers of the sweep the CPU oracle is timed on")
     p.add_argument("--no-check", action="store_true", help="skip the parity check of layer 0")
     p.add_argument("--no-shapes", action="store_true", help="skip per-shape timing")
@@ -423,20 +426,23 @@ def main() -> int:
         for name, K, N in shapes:
             po, so = orc.quantize(host_w[name])
             host.append((K, N, po, so, xs[K].cpu().numpy()[None]))
-        # same bytes as one layer of the sweep in either layout
-        nl = max(1, min(args.cpu_layers, nlayers))
+        # same bytes as one layer of the sweep in either layout; whole layers
+        # until --cpu-seconds have passed
         c0 = time.perf_counter()
         cbytes = 0
-        for _ in range(nl):
+        nl = 0
+        while nl < max(1, args.cpu_layers) and (nl == 0 or
+                                                 time.perf_counter() - c0 < args.cpu_seconds):
             for K, N, po, so, x in host:
                 orc.matmul(x, po, so)
                 cbytes += gemv_bytes(N, K)
+            nl += 1
         csec = time.perf_counter() - c0
         cpu = {"value": round(cbytes / csec / 1e9, 3), "unit": "GB/s", "cores": orc.num_threads(),
                "kind": "oracle",
-               "sample": "%d of %d layers (%d GEMVs, same shapes), fp64 oracle, %.1f s; "
-                         "us per full sweep extrapolated: %.0f"
-                         % (nl, nlayers, nl * len(shapes), csec, csec / nl * nlayers * 1e6)}
+               "sample": "%d layers of the sweep's shapes (%d GEMVs; the sweep has %d layers), "
+                         "fp64 oracle, %.1f s; us per full sweep extrapolated: %.0f"
+                         % (nl, nl * len(shapes), nlayers, csec, csec / nl * nlayers * 1e6)}
 
     sec = None
     if not args.no_secondary:
