@@ -260,6 +260,20 @@ def test_mfma_long_rows(w4, orc, M, N, K):
     check_linear(w4, orc, M, N, K, seed=([8, N, K], [8, N, K, M]), algo="mfma", name="long rows")
 
 
+BATCHED_SHAPES = [(1, 128), (100, 2176), (4104, 2176), (9000, 1152), (30000, 640),
+                  (40000, 256), (300, 14464)]
+
+
+@pytest.mark.parametrize("M", [5, 12, 16, 20, 32])
+@pytest.mark.parametrize("N,K", BATCHED_SHAPES)
+def test_batched_rows_and_chunks(w4, orc, M, N, K):
+    """Batched decode kernel: rows per block from 1 to 128 (and beyond, more
+    blocks than compute units at N = 40000), every wave-grid class, partial
+    16-row tiles, K ragged against the 1024/2048-wide X chunks (one group,
+    a chunk plus one group, 113 groups), 16- and 32-row X tiles."""
+    check_linear(w4, orc, M, N, K, seed=([9, N, K], [9, N, K, M]), algo="mfma", name="batched")
+
+
 @pytest.mark.parametrize("K,N", [(4096, 14336), (14336, 4096), (8192, 28672)])
 def test_prefill_512(w4, orc, K, N):
     check_linear(w4, orc, 512, N, K, seed=[5, K, N], algo="auto", name="prefill")

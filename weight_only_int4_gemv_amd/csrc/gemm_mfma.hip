@@ -229,6 +229,9 @@ hipError_t launch_gemm_mfma(const uint16_t* X, int64_t M, const uint32_t* packed
     // x fits in LDS (K == 0, all outputs zero, stays on the tiled kernel).
     if (M <= kMfma4MaxM && K > 0 && M * K * 2 <= kMfma4MaxXBytes)
         return launch_gemv_mfma4(X, M, packed, scales, N, K, Y, stream, num_cu);
+    // Batched decode: blocks own contiguous weight rows, X through LDS.
+    if (M <= kBatchedMaxM && K > 0 && K <= kBatchedMaxK)
+        return launch_gemm_batched(X, M, packed, scales, N, K, Y, stream, num_cu);
     // Few rows and K > N (few output tiles, long rows): the streaming kernel
     // with the K groups split over waves.
     if (M <= 64 && K > N && K <= kSkinnyMaxK)

@@ -370,6 +370,12 @@ hipError_t launch_gemv_m(const uint16_t* X, int64_t M, const uint32_t* packed,
                          hipStream_t stream, int num_cu) {
     if (K > 0 && (int64_t)MMAX * K * 2 <= kLdsBudget) {
         constexpr int R = MMAX >= 4 ? 1 : 2;
+        // Measured on gfx950 for M = 1: long rows (K = 14336) run best with
+        // 8 waves per block, 2 blocks per CU and one step in flight (7.9 us
+        // against 8.6 us with two steps in flight).
+        if (MMAX == 1 && K >= 12288)
+            return launch_persistent_t<1, 2, 1, 8>(X, M, packed, scales, N, K, Y, stream, num_cu,
+                                                   2);
         if (K >= 12288)
             return launch_persistent_t<MMAX, R, 2, 8>(X, M, packed, scales, N, K, Y, stream,
                                                       num_cu, 2);

@@ -29,6 +29,15 @@ hipError_t launch_gemv_mfma4(const uint16_t* X, int64_t M, const uint32_t* packe
                              const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y,
                              hipStream_t stream, int num_cu);
 
+// MFMA path for batched decode, M <= 32 (gemm_batched.hip): blocks own
+// contiguous weight rows, X staged through LDS in chunks of K.  Requires
+// K <= kBatchedMaxK (32-bit buffer offsets).
+constexpr int64_t kBatchedMaxM = 32;
+constexpr int64_t kBatchedMaxK = (int64_t)1 << 24;
+hipError_t launch_gemm_batched(const uint16_t* X, int64_t M, const uint32_t* packed,
+                               const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y,
+                               hipStream_t stream, int num_cu);
+
 // MFMA path for few rows of X (gemm_skinny.hip): weights streamed once,
 // waves split K.  Requires K <= kSkinnyMaxK (32-bit buffer offsets).
 constexpr int64_t kSkinnyMaxK = (int64_t)1 << 24;
