@@ -75,7 +75,7 @@ extern "C" {
 typedef enum {
     W4A16_OK = 0,
     W4A16_ERR_INVALID_ARG = 1, /* NULL pointer, negative size, size overflow, overlapping output */
-    W4A16_ERR_SHAPE = 2,       /* K % 128 != 0 */
+    W4A16_ERR_SHAPE = 2,       /* K % 128 != 0, or K not a multiple of the group */
     W4A16_ERR_MISALIGNED = 3,  /* alignment rule above violated */
     W4A16_ERR_DEVICE = 4,      /* no HIP device, or the current device is not gfx950 */
     W4A16_ERR_LAUNCH = 5       /* the HIP runtime rejected a launch */
@@ -118,6 +118,26 @@ int w4a16_gemm(const uint16_t* X, int64_t M, const uint32_t* packed, const uint1
  * tolerance; used to measure the VALU/MFMA crossover. */
 int w4a16_gemm_ex(const uint16_t* X, int64_t M, const uint32_t* packed, const uint16_t* scales,
                   int64_t N, int64_t K, uint16_t* Y, int algo, void* stream);
+
+/* ---- Group size as a parameter ([QUANT] sub-section 3 granularity table:
+ * group 128 is the default, group 32 for outlier-sensitive layers; [QUANT]
+ * GPTQ section, group_size table: 256, 128, 64 and 32 trade scale storage,
+ * 1.6 % to 12.5 %, against accuracy).  Same quantizer, layout and linear
+ * layer as above with `group` elements per scale along K:
+ *     scales[n*(K/group) + g] = fp16 bits of s[n][g],  g = k / group
+ *     Y[m,n] = sum_k X[m,k] * s[n,k/group] * q[n,k]
+ * group must be 32, 64, 128 or 256 (else W4A16_ERR_INVALID_ARG) and divide
+ * K (else W4A16_ERR_SHAPE); K % 128 == 0 as everywhere.  group == 128 gives
+ * exactly the functions above.  For other groups the linear layer runs on the
+ * VALU path for every M (the matrix-core kernels read one scale per 128
+ * elements).  Scales bytes: N*(K/group)*2 (0 for bad arguments). */
+size_t w4a16_scales_bytes_g(int64_t N, int64_t K, int64_t group);
+int w4a16_quantize_g(const uint16_t* W, int64_t N, int64_t K, int64_t group,
+                     uint32_t* packed, uint16_t* scales, void* stream);
+int w4a16_gemv_g(const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
+                 int64_t N, int64_t K, int64_t group, uint16_t* y, void* stream);
+int w4a16_gemm_g(const uint16_t* X, int64_t M, const uint32_t* packed, const uint16_t* scales,
+                 int64_t N, int64_t K, int64_t group, uint16_t* Y, void* stream);
 
 /* ---- Dependent decode sequence ([BENCH] §二: every decode step streams
  * the layers' matrices one after another, each fed by the one before).

@@ -304,8 +304,63 @@ def pin_matmul_exact(o) -> list:
     return fails
 
 
+def pin_group_sizes(o) -> list:
+    """Group size as a parameter ([QUANT] sub-section 3 granularity table;
+    [QUANT] GPTQ section, group_size table with its extra-storage column,
+    fp16 scale bytes per INT4 code byte: 12.5 % at 32, 6.3 % at 64, 1.6 % at
+    256).  For each group size: every scale is the
+    exact RNE(absmax/7) of its own slice of `group` elements, every code the
+    brute-force nearest code against it, the dequantizer s[k // group] * q,
+    and tiny products equal the exact rational sums."""
+    fails = []
+    printed = {32: 12.5, 64: 6.3, 256: 1.6}           # storage column of the table, in %
+    for group in (32, 64, 256):
+        N, K = 24, 768
+        W = inputs.weight(N, K, seed=[97, group, 0])
+        W[0, :group] = np.float16(0)                    # an all-zero group
+        W[1, group:2 * group] *= np.float16(1e-3)       # a small-scale group
+        packed, scales = o.quantize(W, group=group)
+        if scales.shape != (N, K // group):
+            fails.append("group %d: scales shape %s" % (group, scales.shape))
+            continue
+        codes = codes_from_bytes(packed)
+        want = brute_force_codes(W, scales, group=group)
+        if not (codes == want).all():
+            fails.append("group %d: %d codes differ from the nearest code"
+                         % (group, (codes != want).sum()))
+        a = np.abs(W.astype(np.float64)).reshape(N, K // group, group).max(axis=2)
+        want_s = np.array([[exact_rne_f16(Fraction(float(v)) / 7) for v in row] for row in a],
+                          dtype=np.uint16)
+        if not (scales == want_s).all():
+            fails.append("group %d: scales differ from exact RNE(absmax/7)" % group)
+        deq = o.dequantize(packed, scales, group=group)
+        s64 = np.repeat(scales.view(np.float16).astype(np.float64), group, axis=1)
+        if not (deq == s64 * codes).all():
+            fails.append("group %d: dequantize differs from s * code" % group)
+        pct = 100.0 * scales.nbytes / packed.nbytes      # scale bytes per INT4 byte
+        if abs(pct - printed[group]) > 0.06:
+            fails.append("group %d: scale storage %.3f %% of the codes vs %.1f %% printed"
+                         % (group, pct, printed[group]))
+        # a tiny product against the exact rational sum
+        M, n_, k_ = 2, 3, 2 * group
+        Wt, Xt = inputs.weight_and_activation(n_, k_, M, seed=[97, group, 1])
+        pt, st = o.quantize(Wt, group=group)
+        Y, _ = o.matmul(Xt, pt, st, group=group)
+        ct = codes_from_bytes(pt)
+        sv = st.view(np.float16).astype(np.float64)
+        for m in range(M):
+            for n in range(n_):
+                terms = [Fraction(float(Xt[m, k])) * Fraction(float(sv[n, k // group])) *
+                         int(ct[n, k]) for k in range(k_)]
+                exact = sum(terms, Fraction(0))
+                bound = k_ * 2.0 ** -53 * float(sum((abs(t) for t in terms), Fraction(0)))
+                if abs(Fraction(Y[m, n]) - exact) > Fraction(bound):
+                    fails.append("group %d: matmul (%d,%d) off the exact sum" % (group, m, n))
+    return fails
+
+
 ALL_PINS = [pin_f16_codec, pin_scale_every_fp16, pin_hand_worked, pin_codes_nearest,
-            pin_invariants, pin_matmul_exact]
+            pin_invariants, pin_matmul_exact, pin_group_sizes]
 
 
 def run_all(o) -> dict:

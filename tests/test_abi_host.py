@@ -33,7 +33,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for fn in ["w4a16_quantize", "w4a16_gemv", "w4a16_gemm", "w4a16_gemm_ex",
                "w4a16_packed_bytes", "w4a16_scales_bytes", "w4a16_status_string",
-               "w4a16_valu_max_m"]:
+               "w4a16_valu_max_m", "w4a16_quantize_g", "w4a16_gemv_g", "w4a16_gemm_g",
+               "w4a16_scales_bytes_g"]:
         assert fn in names
 
 
@@ -116,12 +117,54 @@ def test_linear_validation(lib):
     assert gv(A, B, C, 0, 128, None, None) == OK
 
 
+def test_group_size_validation(lib):
+    """Group size as a parameter: 32, 64, 128, 256 accepted, anything else is an
+    invalid argument; K must be a multiple of the group; scale bytes follow
+    N*(K/group)*2; the matrix-core path takes group 128 only."""
+    sb = lib.w4a16_scales_bytes_g
+    assert sb(4096, 4096, 32) == 4096 * 128 * 2
+    assert sb(4096, 4096, 64) == 4096 * 64 * 2
+    assert sb(4096, 4096, 128) == lib.w4a16_scales_bytes(4096, 4096)
+    assert sb(4096, 4096, 256) == 4096 * 16 * 2
+    assert sb(4, 384, 256) == 0        # 384 % 256 != 0
+    assert sb(4, 128, 48) == 0 and sb(4, 128, 16) == 0 and sb(4, 128, 512) == 0
+    q = lib.w4a16_quantize_g
+    assert q(FAKE, 4, 128, 16, FAKE * 2, FAKE * 3, None) == INVALID
+    assert q(FAKE, 4, 128, 96, FAKE * 2, FAKE * 3, None) == INVALID
+    assert q(FAKE, 4, 384, 256, FAKE * 2, FAKE * 3, None) == SHAPE
+    assert q(FAKE, 4, 100, 32, FAKE * 2, FAKE * 3, None) == SHAPE
+    # scales of 4 x 128 at group 32 take 32 bytes: placed 24 bytes before
+    # packed they overlap it, at group 128 (8 bytes) they would not
+    assert q(FAKE, 4, 128, 32, FAKE * 2, FAKE * 2 - 24, None) == INVALID
+    assert lib.w4a16_scales_bytes_g(4, 128, 128) == 8
+    assert q(None, 0, 256, 256, None, None, None) == OK
+    A, B, C, D = FAKE, FAKE * 4, FAKE * 8, FAKE * 12
+    gv, gm = lib.w4a16_gemv_g, lib.w4a16_gemm_g
+    assert gv(A, B, C, 16, 128, 100, D, None) == INVALID
+    assert gv(A, B, C, 16, 384, 256, D, None) == SHAPE
+    assert gm(A, 2, B, C, 16, 128, 0, D, None) == INVALID
+    # Y 40 bytes after the scales: inside their 128 bytes at group 32
+    # (16 rows x 4 groups), past their 32 bytes at group 128
+    assert gm(A, 2, B, C, 16, 128, 32, C + 40, None) == INVALID
+    assert gm(None, 0, None, None, 16, 256, 256, None, None) == OK
+    # the binding infers the group from the scales' shape and checks it
+    import torch
+    with pytest.raises(ValueError):
+        w4a16.quantize(torch.zeros(4, 128, dtype=torch.float16), group=48)
+    with pytest.raises(ValueError):
+        w4a16.gemv(torch.zeros(256, dtype=torch.float16),
+                   torch.zeros(4, 32, dtype=torch.int32),
+                   torch.zeros(4, 3, dtype=torch.float16))       # 256 / 3: no group
+
+
 @pytest.mark.skipif(__import__("torch").cuda.device_count() > 0,
                     reason="with a GPU present valid arguments would launch")
 def test_valid_arguments_without_device_report_device_error(lib):
     A, B, C, D = FAKE, FAKE * 4, FAKE * 8, FAKE * 12
     assert lib.w4a16_gemm(A, 2, B, C, 16, 128, D, None) == DEVICE
     assert lib.w4a16_quantize(A, 4, 128, B, C, None) == DEVICE
+    assert lib.w4a16_quantize_g(A, 4, 256, 64, B, C, None) == DEVICE
+    assert lib.w4a16_gemm_g(A, 2, B, C, 16, 256, 256, D, None) == DEVICE
 
 
 def test_binding_rejects_bad_tensors():

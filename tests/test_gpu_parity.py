@@ -401,3 +401,90 @@ def test_deterministic_and_stream_ordered(w4, orc, M, algo, N):
                 outs.append(w4.gemm(Xd, pd, sd, algo=algo))
     torch.cuda.synchronize()
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[1], outs[2])
+
+
+# ------------------------------------------------------- group size as a parameter
+
+GROUP_SIZES = [32, 64, 256]
+
+
+@pytest.mark.parametrize("group", GROUP_SIZES)
+@pytest.mark.parametrize("N,K", [(37, 768), (129, 1536), (4096, 4096), (300, 14336)])
+def test_quantize_group_sizes_bit_exact(w4, orc, group, N, K):
+    """w4a16_quantize_g against the oracle at the same group size: every code
+    and scale bit-exact, including an all-zero and a tiny-scale group."""
+    say("quantize group=%d N=%d K=%d" % (group, N, K))
+    W = inputs.weight(N, K, seed=[21, group, N, K])
+    W[0, :group] = np.float16(0)
+    W[min(1, N - 1), group:2 * group] *= np.float16(1e-4)
+    pg, sg = w4.quantize(dev(W), group=group)
+    torch.cuda.synchronize()
+    po, so = orc.quantize(W, group=group)
+    got_s = sg.cpu().numpy().view(np.uint16)
+    got_p = pg.cpu().numpy().view(np.uint32)
+    assert got_s.shape == (N, K // group)
+    bad_s = np.argwhere(got_s != so)
+    assert bad_s.size == 0, "%d scales differ, first at %s" % (len(bad_s), bad_s[0])
+    bad_p = np.argwhere(got_p != po)
+    assert bad_p.size == 0, "%d words differ, first at %s" % (len(bad_p), bad_p[0])
+
+
+def check_linear_group(w4, orc, M, N, K, group, seed, algo=None):
+    say("linear group=%d M=%d N=%d K=%d algo=%s" % (group, M, N, K, algo))
+    W = inputs.weight(N, K, seed=[22, group, N, K])
+    packed, scales = orc.quantize(W, group=group)
+    X = inputs.activation(M, K, seed=seed)
+    if M == 1 and algo == "gemv":
+        Y = w4.gemv(dev(X)[0], packed_to_dev(packed), scales_to_dev(scales)).cpu().numpy()[None]
+    else:
+        Y = w4.gemm(dev(X), packed_to_dev(packed), scales_to_dev(scales), algo=algo).cpu().numpy()
+    torch.cuda.synchronize()
+    assert Y.shape == (M, N)
+    Yref, Yabs = orc.matmul(X, packed, scales, group=group)
+    tol = oracle.tolerance(Yref, Yabs)
+    err = np.abs(Y.astype(np.float64) - Yref)
+    bad = np.argwhere(~(err <= tol))
+    assert bad.size == 0, "%d outputs out of tolerance, first %s: got %r want %r" % (
+        len(bad), bad[0], Y[tuple(bad[0])], Yref[tuple(bad[0])])
+
+
+@pytest.mark.parametrize("group", GROUP_SIZES)
+@pytest.mark.parametrize("M,algo", [(1, "gemv"), (2, None), (3, "valu"), (8, None), (13, None)])
+@pytest.mark.parametrize("N,K", [(300, 1536), (1001, 4096), (64, 14336)])
+def test_linear_group_sizes(w4, orc, group, M, algo, N, K):
+    """GEMV and the VALU GEMM (every M, both launch families: whole-x staging
+    for the persistent kernel, K slices for M = 8) at other group sizes."""
+    check_linear_group(w4, orc, M, N, K, group, seed=[23, group, M, N, K], algo=algo)
+
+
+@pytest.mark.parametrize("group", GROUP_SIZES)
+def test_linear_group_sizes_layer_shape(w4, orc, group):
+    """M = 1 on the LLaMA-3-8B gate shape (4096 x 14336) at each group size."""
+    check_linear_group(w4, orc, 1, 14336, 4096, group, seed=[24, group], algo="gemv")
+
+
+@pytest.mark.parametrize("group", GROUP_SIZES)
+def test_group_sizes_one_hot_exact(w4, orc, group):
+    """One-hot activations select fp16(s[k // group] * q[k]) bit-exactly: the
+    scale of every group is read for the right codes."""
+    N, K = 24, 1024
+    W = inputs.weight(N, K, seed=[25, group])
+    packed, scales = orc.quantize(W, group=group)
+    ks = np.arange(0, K, 7)
+    X = np.zeros((len(ks), K), dtype=np.float16)
+    X[np.arange(len(ks)), ks] = np.float16(1.0)
+    say("one-hot group=%d" % group)
+    for m0 in range(0, len(ks), 8):
+        Y = w4.gemm(dev(X[m0:m0 + 8]), packed_to_dev(packed), scales_to_dev(scales)).cpu().numpy()
+        torch.cuda.synchronize()
+        deq = orc.dequantize(packed, scales, group=group)[:, ks[m0:m0 + 8]].T
+        want = deq.astype(np.float16)
+        assert (Y.view(np.uint16) == want.view(np.uint16)).all()
+
+
+def test_group_sizes_reject_matrix_cores(w4, orc):
+    W = inputs.weight(16, 256, seed=[26])
+    packed, scales = orc.quantize(W, group=64)
+    X = inputs.activation(4, 256, seed=[26, 1])
+    with pytest.raises(ValueError):
+        w4.gemm(dev(X), packed_to_dev(packed), scales_to_dev(scales), algo="mfma")

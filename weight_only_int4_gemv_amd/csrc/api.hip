@@ -63,14 +63,29 @@ int check_sizes(int64_t M, int64_t N, int64_t K) {
     return W4A16_OK;
 }
 
+// Group sizes the kernels take: 32, 64, 128 or 256 elements per scale, and
+// K a multiple of the group (K % 128 == 0 is required for every group).
+int check_group(int64_t group, int64_t K) {
+    if (group != 32 && group != 64 && group != 128 && group != 256) return W4A16_ERR_INVALID_ARG;
+    if (K % group != 0) return W4A16_ERR_SHAPE;
+    return W4A16_OK;
+}
+
+// log2(group / 32): the GEMV reads one scale per 2^gshift 32-code chunks.
+int group_shift(int64_t group) { return group == 32 ? 0 : group == 64 ? 1 : group == 128 ? 2 : 3; }
+
 int status_of(hipError_t e) { return e == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH; }
 
 int linear(const uint16_t* X, int64_t M, const uint32_t* packed, const uint16_t* scales,
-           int64_t N, int64_t K, uint16_t* Y, int algo, void* stream) {
+           int64_t N, int64_t K, int64_t group, uint16_t* Y, int algo, void* stream) {
     int st = check_sizes(M, N, K);
+    if (st != W4A16_OK) return st;
+    st = check_group(group, K);
     if (st != W4A16_OK) return st;
     if (algo != W4A16_ALGO_AUTO && algo != W4A16_ALGO_VALU && algo != W4A16_ALGO_MFMA)
         return W4A16_ERR_INVALID_ARG;
+    // the matrix-core kernels read one scale per 128 elements
+    if (algo == W4A16_ALGO_MFMA && group != W4A16_GROUP) return W4A16_ERR_INVALID_ARG;
     if (M == 0 || N == 0) return W4A16_OK;
     // With K == 0 the inputs hold no bytes and may be NULL; they are never read.
     if (!Y || (K > 0 && (!X || !packed || !scales))) return W4A16_ERR_INVALID_ARG;
@@ -79,15 +94,41 @@ int linear(const uint16_t* X, int64_t M, const uint32_t* packed, const uint16_t*
     const size_t y_bytes = (size_t)M * N * 2;
     if (overlap(Y, y_bytes, X, (size_t)M * K * 2) ||
         overlap(Y, y_bytes, packed, (size_t)N * K / 2) ||
-        overlap(Y, y_bytes, scales, (size_t)N * (K / W4A16_GROUP) * 2))
+        overlap(Y, y_bytes, scales, (size_t)N * (K / group) * 2))
         return W4A16_ERR_INVALID_ARG;
     int num_cu = 0;
     st = current_device(&num_cu);
     if (st != W4A16_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const bool valu = algo == W4A16_ALGO_VALU || (algo == W4A16_ALGO_AUTO && M <= kValuMaxM);
-    if (valu) return status_of(w4a16::launch_gemv_valu(X, M, packed, scales, N, K, Y, s, num_cu));
+    const bool valu = algo == W4A16_ALGO_VALU || group != W4A16_GROUP ||
+                      (algo == W4A16_ALGO_AUTO && M <= kValuMaxM);
+    if (valu)
+        return status_of(w4a16::launch_gemv_valu(X, M, packed, scales, N, K, Y, s, num_cu,
+                                                 group_shift(group)));
     return status_of(w4a16::launch_gemm_mfma(X, M, packed, scales, N, K, Y, s, num_cu));
+}
+
+int quantize(const uint16_t* W, int64_t N, int64_t K, int64_t group, uint32_t* packed,
+             uint16_t* scales, void* stream) {
+    int st = check_sizes(0, N, K);
+    if (st != W4A16_OK) return st;
+    st = check_group(group, K);
+    if (st != W4A16_OK) return st;
+    if (N == 0 || K == 0) return W4A16_OK;
+    if (!W || !packed || !scales) return W4A16_ERR_INVALID_ARG;
+    if (!aligned(W, 16) || !aligned(packed, 16) || !aligned(scales, 2))
+        return W4A16_ERR_MISALIGNED;
+    const size_t w_bytes = (size_t)N * K * 2;
+    const size_t p_bytes = (size_t)N * K / 2;
+    const size_t s_bytes = (size_t)N * (K / group) * 2;
+    if (overlap(packed, p_bytes, W, w_bytes) || overlap(scales, s_bytes, W, w_bytes) ||
+        overlap(packed, p_bytes, scales, s_bytes))
+        return W4A16_ERR_INVALID_ARG;
+    int num_cu = 0;
+    st = current_device(&num_cu);
+    if (st != W4A16_OK) return st;
+    return status_of(w4a16::launch_quantize(W, N, K, group, packed, scales,
+                                            static_cast<hipStream_t>(stream)));
 }
 
 }  // namespace
@@ -100,44 +141,47 @@ size_t w4a16_packed_bytes(int64_t N, int64_t K) {
 }
 
 size_t w4a16_scales_bytes(int64_t N, int64_t K) {
-    if (check_sizes(0, N, K) != W4A16_OK) return 0;
-    return (size_t)N * (size_t)(K / W4A16_GROUP) * 2;
+    return w4a16_scales_bytes_g(N, K, W4A16_GROUP);
+}
+
+size_t w4a16_scales_bytes_g(int64_t N, int64_t K, int64_t group) {
+    if (check_sizes(0, N, K) != W4A16_OK || check_group(group, K) != W4A16_OK) return 0;
+    return (size_t)N * (size_t)(K / group) * 2;
 }
 
 int w4a16_quantize(const uint16_t* W, int64_t N, int64_t K, uint32_t* packed, uint16_t* scales,
                    void* stream) {
-    int st = check_sizes(0, N, K);
-    if (st != W4A16_OK) return st;
-    if (N == 0 || K == 0) return W4A16_OK;
-    if (!W || !packed || !scales) return W4A16_ERR_INVALID_ARG;
-    if (!aligned(W, 16) || !aligned(packed, 16) || !aligned(scales, 2))
-        return W4A16_ERR_MISALIGNED;
-    const size_t w_bytes = (size_t)N * K * 2;
-    const size_t p_bytes = (size_t)N * K / 2;
-    const size_t s_bytes = (size_t)N * (K / W4A16_GROUP) * 2;
-    if (overlap(packed, p_bytes, W, w_bytes) || overlap(scales, s_bytes, W, w_bytes) ||
-        overlap(packed, p_bytes, scales, s_bytes))
-        return W4A16_ERR_INVALID_ARG;
-    int num_cu = 0;
-    st = current_device(&num_cu);
-    if (st != W4A16_OK) return st;
-    return status_of(w4a16::launch_quantize(W, N, K, packed, scales,
-                                            static_cast<hipStream_t>(stream)));
+    return quantize(W, N, K, W4A16_GROUP, packed, scales, stream);
+}
+
+int w4a16_quantize_g(const uint16_t* W, int64_t N, int64_t K, int64_t group, uint32_t* packed,
+                     uint16_t* scales, void* stream) {
+    return quantize(W, N, K, group, packed, scales, stream);
 }
 
 int w4a16_gemv(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, int64_t N,
                int64_t K, uint16_t* y, void* stream) {
-    return linear(x, 1, packed, scales, N, K, y, W4A16_ALGO_VALU, stream);
+    return linear(x, 1, packed, scales, N, K, W4A16_GROUP, y, W4A16_ALGO_VALU, stream);
+}
+
+int w4a16_gemv_g(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, int64_t N,
+                 int64_t K, int64_t group, uint16_t* y, void* stream) {
+    return linear(x, 1, packed, scales, N, K, group, y, W4A16_ALGO_VALU, stream);
 }
 
 int w4a16_gemm(const uint16_t* X, int64_t M, const uint32_t* packed, const uint16_t* scales,
                int64_t N, int64_t K, uint16_t* Y, void* stream) {
-    return linear(X, M, packed, scales, N, K, Y, W4A16_ALGO_AUTO, stream);
+    return linear(X, M, packed, scales, N, K, W4A16_GROUP, Y, W4A16_ALGO_AUTO, stream);
+}
+
+int w4a16_gemm_g(const uint16_t* X, int64_t M, const uint32_t* packed, const uint16_t* scales,
+                 int64_t N, int64_t K, int64_t group, uint16_t* Y, void* stream) {
+    return linear(X, M, packed, scales, N, K, group, Y, W4A16_ALGO_AUTO, stream);
 }
 
 int w4a16_gemm_ex(const uint16_t* X, int64_t M, const uint32_t* packed, const uint16_t* scales,
                   int64_t N, int64_t K, uint16_t* Y, int algo, void* stream) {
-    return linear(X, M, packed, scales, N, K, Y, algo, stream);
+    return linear(X, M, packed, scales, N, K, W4A16_GROUP, Y, algo, stream);
 }
 
 int w4a16_gemv_chain(const w4a16_gemv_stage* stages, int count, uint32_t* sync, void* stream) {
@@ -200,8 +244,8 @@ int64_t w4a16_valu_max_m(void) { return kValuMaxM; }
 const char* w4a16_status_string(int status) {
     switch (status) {
         case W4A16_OK: return "ok";
-        case W4A16_ERR_INVALID_ARG: return "invalid argument (null pointer, negative or too large size, overlapping output, unknown algo)";
-        case W4A16_ERR_SHAPE: return "K must be a multiple of 128";
+        case W4A16_ERR_INVALID_ARG: return "invalid argument (null pointer, negative or too large size, overlapping output, unknown algo or group size)";
+        case W4A16_ERR_SHAPE: return "K must be a multiple of 128 and of the group size";
         case W4A16_ERR_MISALIGNED: return "misaligned pointer (W, X, x, packed need 16 bytes; scales, Y, y need 2)";
         case W4A16_ERR_DEVICE: return "no HIP device, or the current device is not gfx950";
         case W4A16_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";

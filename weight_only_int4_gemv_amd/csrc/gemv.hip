@@ -60,12 +60,13 @@ __device__ __forceinline__ void stage_activations(const uint16_t* __restrict__ X
 template <int MMAX, int R, int U, int WAVES>
 __global__ __launch_bounds__(WAVES * kWave) void gemv_kernel(
     const uint16_t* __restrict__ X, int M, const uint4* __restrict__ packed,
-    const uint16_t* __restrict__ scales, uint16_t* __restrict__ Y, int N, int K, int kslice) {
+    const uint16_t* __restrict__ scales, uint16_t* __restrict__ Y, int N, int K, int kslice,
+    int gshift) {
     extern __shared__ uint4 lds[];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    const int nchunks = K >> 5;   // 16-byte chunks per weight row
-    const int ngroups = K >> 7;   // scales per weight row
+    const int nchunks = K >> 5;                   // 16-byte chunks per weight row
+    const int ngroups = K >> (5 + gshift);        // scales per weight row (2^gshift chunks each)
     const int row0 = (blockIdx.x * WAVES + wave) * R;
 
     size_t wrow[R], srow[R];
@@ -98,7 +99,7 @@ __global__ __launch_bounds__(WAVES * kWave) void gemv_kernel(
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
                     w[u][r] = packed[wrow[r] + cc];
-                    sb[u][r] = scales[srow[r] + (cc >> 2)];
+                    sb[u][r] = scales[srow[r] + (cc >> gshift)];
                 }
             }
         };
@@ -173,7 +174,7 @@ __global__ __launch_bounds__(WAVES * kWave) void gemv_kernel(
 template <int MMAX, int R, int P, int WAVES, int XPT>
 __global__ __launch_bounds__(WAVES * kWave) void gemv_persistent_kernel(
     const uint16_t* __restrict__ X, int M, const uint4* __restrict__ packed,
-    const uint16_t* __restrict__ scales, uint16_t* __restrict__ Y, int N, int K) {
+    const uint16_t* __restrict__ scales, uint16_t* __restrict__ Y, int N, int K, int gshift) {
     extern __shared__ uint4 lds[];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -186,7 +187,7 @@ __global__ __launch_bounds__(WAVES * kWave) void gemv_persistent_kernel(
     const int my_rg = first_rg < total_rg ? (total_rg - 1 - first_rg) / stride_rg + 1 : 0;
     const int T = my_rg * nsteps;                          // this wave's iterations
     const uint32_t wrow_bytes = (uint32_t)K / 2;
-    const uint32_t srow_bytes = (uint32_t)K / 64;
+    const uint32_t srow_bytes = (uint32_t)(K >> (5 + gshift)) * 2;   // one scale per 2^gshift chunks
     const CodeConsts kc = code_consts();
 
     // X blocks of this thread, loaded first (indices clamped into range).
@@ -214,7 +215,7 @@ __global__ __launch_bounds__(WAVES * kWave) void gemv_persistent_kernel(
                              (uint64_t)rows_left * srow_bytes);
         }
         const int voff_w = lane * 16 + ls * (kWave * 16);
-        const int voff_s = (lane >> 2) * 2 + ls * (kWave / 4 * 2);
+        const int voff_s = ((lane + ls * kWave) >> gshift) * 2;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             typedef unsigned v4u __attribute__((ext_vector_type(4)));
@@ -307,7 +308,7 @@ constexpr int kLdsBudget = 64 * 1024;
 template <int MMAX, int R, int U, int WAVES>
 hipError_t launch_gemv_t(const uint16_t* X, int64_t M, const uint32_t* packed,
                          const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y,
-                         hipStream_t stream) {
+                         hipStream_t stream, int gshift = 2) {
     // LDS: 2 bytes per activation element.
     int64_t kslice = (int64_t)(kLdsBudget / (MMAX * 2)) / kGroup * kGroup;
     if (kslice > K) kslice = K;
@@ -318,18 +319,18 @@ hipError_t launch_gemv_t(const uint16_t* X, int64_t M, const uint32_t* packed,
     hipLaunchKernelGGL((gemv_kernel<MMAX, R, U, WAVES>), dim3((unsigned)blocks),
                        dim3(WAVES * kWave), lds, stream, X, (int)M,
                        reinterpret_cast<const uint4*>(packed), scales, Y, (int)N, (int)K,
-                       (int)kslice);
+                       (int)kslice, gshift);
     return hipGetLastError();
 }
 
 template <int MMAX, int R, int P, int WAVES, int XPT>
 hipError_t launch_persistent_xpt(const uint16_t* X, int64_t M, const uint32_t* packed,
                                  const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y,
-                                 hipStream_t stream, int64_t blocks) {
+                                 hipStream_t stream, int64_t blocks, int gshift) {
     const size_t lds = (size_t)MMAX * (K / 8) * sizeof(uint4);
     hipLaunchKernelGGL((gemv_persistent_kernel<MMAX, R, P, WAVES, XPT>), dim3((unsigned)blocks),
                        dim3(WAVES * kWave), lds, stream, X, (int)M,
-                       reinterpret_cast<const uint4*>(packed), scales, Y, (int)N, (int)K);
+                       reinterpret_cast<const uint4*>(packed), scales, Y, (int)N, (int)K, gshift);
     return hipGetLastError();
 }
 
@@ -338,7 +339,8 @@ hipError_t launch_persistent_xpt(const uint16_t* X, int64_t M, const uint32_t* p
 template <int MMAX, int R, int P, int WAVES>
 hipError_t launch_persistent_t(const uint16_t* X, int64_t M, const uint32_t* packed,
                                const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y,
-                               hipStream_t stream, int num_cu, int blocks_per_cu) {
+                               hipStream_t stream, int num_cu, int blocks_per_cu,
+                               int gshift = 2) {
     const int64_t total_rg = (N + R - 1) / R;
     const int64_t max_waves = (int64_t)num_cu * blocks_per_cu * WAVES;
     const int64_t per_wave = (total_rg + max_waves - 1) / max_waves;
@@ -347,14 +349,14 @@ hipError_t launch_persistent_t(const uint16_t* X, int64_t M, const uint32_t* pac
     const int64_t need = (int64_t)MMAX * (K / 8);             // x blocks to stage
     const int64_t threads = (int64_t)WAVES * kWave;
     if (need <= threads)
-        return launch_persistent_xpt<MMAX, R, P, WAVES, 1>(X, M, packed, scales, N, K, Y, stream, blocks);
+        return launch_persistent_xpt<MMAX, R, P, WAVES, 1>(X, M, packed, scales, N, K, Y, stream, blocks, gshift);
     if (need <= 2 * threads)
-        return launch_persistent_xpt<MMAX, R, P, WAVES, 2>(X, M, packed, scales, N, K, Y, stream, blocks);
+        return launch_persistent_xpt<MMAX, R, P, WAVES, 2>(X, M, packed, scales, N, K, Y, stream, blocks, gshift);
     if (need <= 4 * threads)
-        return launch_persistent_xpt<MMAX, R, P, WAVES, 4>(X, M, packed, scales, N, K, Y, stream, blocks);
+        return launch_persistent_xpt<MMAX, R, P, WAVES, 4>(X, M, packed, scales, N, K, Y, stream, blocks, gshift);
     if (need <= 8 * threads)
-        return launch_persistent_xpt<MMAX, R, P, WAVES, 8>(X, M, packed, scales, N, K, Y, stream, blocks);
-    return launch_persistent_xpt<MMAX, R, P, WAVES, 16>(X, M, packed, scales, N, K, Y, stream, blocks);
+        return launch_persistent_xpt<MMAX, R, P, WAVES, 8>(X, M, packed, scales, N, K, Y, stream, blocks, gshift);
+    return launch_persistent_xpt<MMAX, R, P, WAVES, 16>(X, M, packed, scales, N, K, Y, stream, blocks, gshift);
 }
 
 // Launch choice (measured on MI355X over the decode layer shapes, K x N from
@@ -367,7 +369,7 @@ hipError_t launch_persistent_t(const uint16_t* X, int64_t M, const uint32_t* pac
 template <int MMAX>
 hipError_t launch_gemv_m(const uint16_t* X, int64_t M, const uint32_t* packed,
                          const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y,
-                         hipStream_t stream, int num_cu) {
+                         hipStream_t stream, int num_cu, int gshift) {
     if (K > 0 && (int64_t)MMAX * K * 2 <= kLdsBudget) {
         constexpr int R = MMAX >= 4 ? 1 : 2;
         // Measured on gfx950 for M = 1: long rows (K = 14336) run best with
@@ -375,34 +377,34 @@ hipError_t launch_gemv_m(const uint16_t* X, int64_t M, const uint32_t* packed,
         // against 8.6 us with two steps in flight).
         if (MMAX == 1 && K >= 12288)
             return launch_persistent_t<1, 2, 1, 8>(X, M, packed, scales, N, K, Y, stream, num_cu,
-                                                   2);
+                                                   2, gshift);
         if (K >= 12288)
             return launch_persistent_t<MMAX, R, 2, 8>(X, M, packed, scales, N, K, Y, stream,
-                                                      num_cu, 2);
+                                                      num_cu, 2, gshift);
         return launch_persistent_t<MMAX, R, 1, 4>(X, M, packed, scales, N, K, Y, stream, num_cu,
-                                                  6);
+                                                  6, gshift);
     }
     constexpr int WAVES = 4;
     if (N >= (int64_t)4 * WAVES * num_cu && MMAX <= 4)
-        return launch_gemv_t<MMAX, 4, 2, WAVES>(X, M, packed, scales, N, K, Y, stream);
+        return launch_gemv_t<MMAX, 4, 2, WAVES>(X, M, packed, scales, N, K, Y, stream, gshift);
     if (N >= (int64_t)2 * WAVES * num_cu)
-        return launch_gemv_t<MMAX, 2, 2, WAVES>(X, M, packed, scales, N, K, Y, stream);
-    return launch_gemv_t<MMAX, 1, 4, WAVES>(X, M, packed, scales, N, K, Y, stream);
+        return launch_gemv_t<MMAX, 2, 2, WAVES>(X, M, packed, scales, N, K, Y, stream, gshift);
+    return launch_gemv_t<MMAX, 1, 4, WAVES>(X, M, packed, scales, N, K, Y, stream, gshift);
 }
 
 }  // namespace
 
 hipError_t launch_gemv_valu(const uint16_t* X, int64_t M, const uint32_t* packed,
                             const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y,
-                            hipStream_t stream, int num_cu) {
-    if (M == 1) return launch_gemv_m<1>(X, M, packed, scales, N, K, Y, stream, num_cu);
-    if (M == 2) return launch_gemv_m<2>(X, M, packed, scales, N, K, Y, stream, num_cu);
-    if (M <= 4) return launch_gemv_m<4>(X, M, packed, scales, N, K, Y, stream, num_cu);
+                            hipStream_t stream, int num_cu, int gshift) {
+    if (M == 1) return launch_gemv_m<1>(X, M, packed, scales, N, K, Y, stream, num_cu, gshift);
+    if (M == 2) return launch_gemv_m<2>(X, M, packed, scales, N, K, Y, stream, num_cu, gshift);
+    if (M <= 4) return launch_gemv_m<4>(X, M, packed, scales, N, K, Y, stream, num_cu, gshift);
     // M > 8 is split into slices of at most 8 activation rows.
     for (int64_t m0 = 0; m0 < M; m0 += 8) {
         const int64_t mm = (M - m0 < 8) ? (M - m0) : 8;
         hipError_t e = launch_gemv_m<8>(X + m0 * K, mm, packed, scales, N, K, Y + m0 * N,
-                                        stream, num_cu);
+                                        stream, num_cu, gshift);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

@@ -1,11 +1,14 @@
 // quantize.hip — RTN symmetric INT4 quantizer, one fp16 scale per group of
-// 128 along K, packed eight codes per uint32 ([QUANT] sub-section 2
-// equations, sub-section 3 per-group listing; [INT4] INT4 paragraph).
+// G elements along K (G = 128 by default; 32, 64 and 256 as in [QUANT]'s
+// granularity table and GPTQ group_size table), packed eight codes per
+// uint32 ([QUANT] sub-section 2 equations, sub-section 3 per-group listing;
+// [INT4] INT4 paragraph).
 //
-// Work split: one 16-lane DPP row of a wave per (row, group).  Each lane loads
-// 16 bytes (8 fp16), the row reduces the absolute maximum, and each lane
-// writes the one packed word its 8 elements form; 16 lanes write the group's
-// 64 contiguous bytes.  HBM traffic per element: 2 B in, 0.5 + 1/64 B out.
+// Work split: G/8 consecutive lanes of a wave per (row, group).  Each lane
+// loads 16 bytes (8 fp16), the lanes reduce the absolute maximum with DPP
+// (and one cross-row swap for G = 256), and each lane writes the one packed
+// word its 8 elements form; the group's lanes write its G/2 contiguous
+// bytes.  HBM traffic per element: 2 B in, 0.5 + 2/G B out.
 //
 // Bit-exactness:
 //   - |w| is compared as the integer w & 0x7FFF (order of finite fp16
@@ -34,15 +37,24 @@ template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_max(uint32_t v) {
     return max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false));
 }
-__device__ __forceinline__ uint32_t row_max16(uint32_t v) {
-    v = dpp_max<0xB1>(v);   // quad_perm [1,0,3,2]
-    v = dpp_max<0x4E>(v);   // quad_perm [2,3,0,1]
-    v = dpp_max<0x141>(v);  // row_half_mirror
-    v = dpp_max<0x140>(v);  // row_mirror
+// max over the LG lanes of a group (LG = 4, 8, 16 or 32 consecutive lanes);
+// every lane of the group receives it.  Quad butterflies, then the half-row
+// and row mirrors (each lane meets the lane its mirror maps it to, which
+// after the quad step carries that quad's maximum), then a swap of the two
+// 16-lane rows of a 32-lane group.
+template <int LG>
+__device__ __forceinline__ uint32_t group_max(uint32_t v) {
+    static_assert(LG == 4 || LG == 8 || LG == 16 || LG == 32, "lanes per group");
+    v = dpp_max<0xB1>(v);                                   // quad_perm [1,0,3,2]
+    v = dpp_max<0x4E>(v);                                   // quad_perm [2,3,0,1]
+    if constexpr (LG >= 8) v = dpp_max<0x141>(v);           // row_half_mirror
+    if constexpr (LG >= 16) v = dpp_max<0x140>(v);          // row_mirror
+    if constexpr (LG == 32) v = max(v, (uint32_t)__shfl_xor((int)v, 16));
     return v;
 }
 
 // One lane's 8 elements of a group -> its packed word, and the group scale.
+template <int LG>
 __device__ __forceinline__ uint32_t quantize8(const uint4& v, uint16_t& s_bits) {
     uint32_t m = 0;
     m = max(m, v.x & 0x7FFFu);
@@ -53,11 +65,11 @@ __device__ __forceinline__ uint32_t quantize8(const uint4& v, uint16_t& s_bits) 
     m = max(m, (v.z >> 16) & 0x7FFFu);
     m = max(m, v.w & 0x7FFFu);
     m = max(m, (v.w >> 16) & 0x7FFFu);
-    m = row_max16(m);
+    m = group_max<LG>(m);
     const float a = f16_bits_to_f32((uint16_t)m);
     s_bits = f32_to_f16_bits(a / 7.0f);  // 2^(4-1) - 1 = 7, IEEE division
     const float s = f16_bits_to_f32(s_bits);
-    if (s == 0.0f) return 0x88888888u;   // every code 0 (all 16 lanes alike)
+    if (s == 0.0f) return 0x88888888u;   // every code 0 (all lanes of the group alike)
     const uint32_t h[4] = {v.x, v.y, v.z, v.w};
     const float inv = __builtin_amdgcn_rcpf(s);
     uint32_t word = 0;
@@ -85,20 +97,20 @@ __device__ __forceinline__ uint32_t quantize8(const uint4& v, uint16_t& s_bits) 
 }
 }  // namespace
 
-// Each 16-lane row of a wave quantizes one group per step; the loads of U
-// steps (groups g, g + stride, ...) are issued together.  All 16 lanes of a
-// row share g, so the row reductions only ever combine lanes that are
-// active together.
-template <int U>
+// Each LG-lane slice of a wave quantizes one group per step; the loads of U
+// steps (groups g, g + stride, ...) are issued together.  All LG lanes of a
+// slice share g, so the reductions only ever combine lanes that are active
+// together.
+template <int LG, int U>
 __global__ __launch_bounds__(256) void quantize_kernel(const uint4* __restrict__ W,
                                                        uint32_t* __restrict__ packed,
                                                        uint16_t* __restrict__ scales,
                                                        int64_t total_groups) {
-    const int lane16 = threadIdx.x & 15;
-    const int64_t stride = (int64_t)gridDim.x * (blockDim.x / 16);
+    const int lg = threadIdx.x & (LG - 1);              // lane within the group
+    const int64_t stride = (int64_t)gridDim.x * (blockDim.x / LG);
     typedef unsigned v4u __attribute__((ext_vector_type(4)));
     const v4u* Wv = reinterpret_cast<const v4u*>(W);
-    for (int64_t g = (int64_t)blockIdx.x * (blockDim.x / 16) + (threadIdx.x >> 4);
+    for (int64_t g = (int64_t)blockIdx.x * (blockDim.x / LG) + (threadIdx.x / LG);
          g < total_groups; g += U * stride) {
         v4u a[U];
 #pragma unroll
@@ -106,36 +118,45 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint4* __restrict__
             // W is read once: non-temporal loads
             a[u] = (v4u){0u, 0u, 0u, 0u};
             if (g + u * stride < total_groups)
-                a[u] = __builtin_nontemporal_load(Wv + (g + u * stride) * 16 + lane16);
+                a[u] = __builtin_nontemporal_load(Wv + (g + u * stride) * LG + lg);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t gu = g + u * stride;
             if (gu < total_groups) {
                 uint16_t sb;
-                const uint32_t word = quantize8(make_uint4(a[u].x, a[u].y, a[u].z, a[u].w), sb);
-                packed[gu * 16 + lane16] = word;
-                if (lane16 == 0) scales[gu] = sb;
+                const uint32_t word =
+                    quantize8<LG>(make_uint4(a[u].x, a[u].y, a[u].z, a[u].w), sb);
+                packed[gu * LG + lg] = word;
+                if (lg == 0) scales[gu] = sb;
             }
         }
     }
 }
 
-template <int U>
+template <int LG, int U>
 hipError_t launch_quantize_t(const uint16_t* W, int64_t groups, uint32_t* packed,
                              uint16_t* scales, hipStream_t stream, int64_t max_blocks) {
-    int64_t blocks = (groups + 16 * U - 1) / (16 * U);   // 16 groups per block and step
+    constexpr int per_block = 256 / LG;                  // groups per block and step
+    int64_t blocks = (groups + per_block * U - 1) / (per_block * U);
     if (blocks > max_blocks) blocks = max_blocks;        // grid-stride beyond this
-    hipLaunchKernelGGL((quantize_kernel<U>), dim3((unsigned)blocks), dim3(256), 0, stream,
+    hipLaunchKernelGGL((quantize_kernel<LG, U>), dim3((unsigned)blocks), dim3(256), 0, stream,
                        reinterpret_cast<const uint4*>(W), packed, scales, groups);
     return hipGetLastError();
 }
 
-hipError_t launch_quantize(const uint16_t* W, int64_t N, int64_t K, uint32_t* packed,
-                           uint16_t* scales, hipStream_t stream) {
-    const int64_t groups = N * (K / kGroup);
+hipError_t launch_quantize(const uint16_t* W, int64_t N, int64_t K, int64_t group,
+                           uint32_t* packed, uint16_t* scales, hipStream_t stream) {
+    const int64_t groups = N * (K / group);
     if (groups == 0) return hipSuccess;
-    return launch_quantize_t<2>(W, groups, packed, scales, stream, 65536);
+    // the same 16 bytes per lane and two groups' loads in flight for every G
+    switch (group) {
+        case 32: return launch_quantize_t<4, 2>(W, groups, packed, scales, stream, 65536);
+        case 64: return launch_quantize_t<8, 2>(W, groups, packed, scales, stream, 65536);
+        case 128: return launch_quantize_t<16, 2>(W, groups, packed, scales, stream, 65536);
+        case 256: return launch_quantize_t<32, 2>(W, groups, packed, scales, stream, 65536);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace w4a16

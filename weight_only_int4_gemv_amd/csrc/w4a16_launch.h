@@ -8,13 +8,15 @@
 
 namespace w4a16 {
 
-hipError_t launch_quantize(const uint16_t* W, int64_t N, int64_t K, uint32_t* packed,
-                           uint16_t* scales, hipStream_t stream);
+// group: 32, 64, 128 or 256 elements per scale.
+hipError_t launch_quantize(const uint16_t* W, int64_t N, int64_t K, int64_t group,
+                           uint32_t* packed, uint16_t* scales, hipStream_t stream);
 
-// VALU dot-product path, any M (M > 8 runs in slices of 8 rows).
+// VALU dot-product path, any M (M > 8 runs in slices of 8 rows).  gshift:
+// log2(group / 32), one scale per 2^gshift 32-code chunks (2 = group 128).
 hipError_t launch_gemv_valu(const uint16_t* X, int64_t M, const uint32_t* packed,
                             const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y,
-                            hipStream_t stream, int num_cu);
+                            hipStream_t stream, int num_cu, int gshift = 2);
 
 // MFMA path, any M.
 hipError_t launch_gemm_mfma(const uint16_t* X, int64_t M, const uint32_t* packed,

@@ -61,7 +61,13 @@ def library() -> ctypes.CDLL:
         lib.w4a16_gemv.argtypes = [_p, _p, _p, _i64, _i64, _p, _p]
         lib.w4a16_gemm.argtypes = [_p, _i64, _p, _p, _i64, _i64, _p, _p]
         lib.w4a16_gemm_ex.argtypes = [_p, _i64, _p, _p, _i64, _i64, _p, ctypes.c_int, _p]
-        for f in (lib.w4a16_quantize, lib.w4a16_gemv, lib.w4a16_gemm, lib.w4a16_gemm_ex):
+        lib.w4a16_scales_bytes_g.argtypes = [_i64, _i64, _i64]
+        lib.w4a16_scales_bytes_g.restype = ctypes.c_size_t
+        lib.w4a16_quantize_g.argtypes = [_p, _i64, _i64, _i64, _p, _p, _p]
+        lib.w4a16_gemv_g.argtypes = [_p, _p, _p, _i64, _i64, _i64, _p, _p]
+        lib.w4a16_gemm_g.argtypes = [_p, _i64, _p, _p, _i64, _i64, _i64, _p, _p]
+        for f in (lib.w4a16_quantize, lib.w4a16_gemv, lib.w4a16_gemm, lib.w4a16_gemm_ex,
+                  lib.w4a16_quantize_g, lib.w4a16_gemv_g, lib.w4a16_gemm_g):
             f.restype = ctypes.c_int
         lib.w4a16_valu_max_m.restype = ctypes.c_int64
         lib.w4a16_gemv_chain.argtypes = [ctypes.POINTER(GemvStage), ctypes.c_int, _p, _p]
@@ -102,45 +108,66 @@ def packed_bytes(N: int, K: int) -> int:
     return library().w4a16_packed_bytes(N, K)
 
 
-def scales_bytes(N: int, K: int) -> int:
-    return library().w4a16_scales_bytes(N, K)
+GROUPS = (32, 64, 128, 256)   # elements per scale the kernels take
 
 
-def quantize(W: torch.Tensor, packed: torch.Tensor = None, scales: torch.Tensor = None):
-    """W fp16 [N, K] -> (packed int32 [N, K/8] holding uint32 words, scales fp16 [N, K/128])."""
+def scales_bytes(N: int, K: int, group: int = W4A16_GROUP) -> int:
+    return library().w4a16_scales_bytes_g(N, K, group)
+
+
+def _check_group(group: int, K: int) -> None:
+    if group not in GROUPS:
+        raise ValueError("group must be one of %s, got %r" % (GROUPS, group))
+    if K % W4A16_GROUP or K % group:
+        raise ValueError("K = %d is not a multiple of %d and of the group %d"
+                         % (K, W4A16_GROUP, group))
+
+
+def quantize(W: torch.Tensor, packed: torch.Tensor = None, scales: torch.Tensor = None,
+             group: int = W4A16_GROUP):
+    """W fp16 [N, K] -> (packed int32 [N, K/8] holding uint32 words, scales fp16
+    [N, K/group]); group 32, 64, 128 (default) or 256."""
     lib = library()
     _need(W, "W", torch.float16, 2)
     N, K = W.shape
-    if K % W4A16_GROUP:
-        raise ValueError("K = %d is not a multiple of %d" % (K, W4A16_GROUP))
+    _check_group(group, K)
     if packed is None:
         packed = torch.empty((N, K // 8), dtype=torch.int32, device=W.device)
     if scales is None:
-        scales = torch.empty((N, K // W4A16_GROUP), dtype=torch.float16, device=W.device)
+        scales = torch.empty((N, K // group), dtype=torch.float16, device=W.device)
     _need(packed, "packed", torch.int32, 2)
     _need(scales, "scales", torch.float16, 2)
-    if tuple(packed.shape) != (N, K // 8) or tuple(scales.shape) != (N, K // W4A16_GROUP):
+    if tuple(packed.shape) != (N, K // 8) or tuple(scales.shape) != (N, K // group):
         raise ValueError("output shapes do not match W")
-    _check("w4a16_quantize", lib.w4a16_quantize(W.data_ptr(), N, K, packed.data_ptr(),
-                                                scales.data_ptr(), _stream()))
+    if group == W4A16_GROUP:
+        st = lib.w4a16_quantize(W.data_ptr(), N, K, packed.data_ptr(), scales.data_ptr(),
+                                _stream())
+    else:
+        st = lib.w4a16_quantize_g(W.data_ptr(), N, K, group, packed.data_ptr(),
+                                  scales.data_ptr(), _stream())
+    _check("w4a16_quantize", st)
     return packed, scales
 
 
 def _weights(packed: torch.Tensor, scales: torch.Tensor):
+    """(N, K, group) of a packed weight; the group follows from the scales'
+    shape [N, K/group]."""
     _need(packed, "packed", torch.int32, 2)
     _need(scales, "scales", torch.float16, 2)
     N, K = packed.shape[0], packed.shape[1] * 8
-    if tuple(scales.shape) != (N, K // W4A16_GROUP):
+    ng = scales.shape[1]
+    group = K // ng if ng > 0 and K % ng == 0 else 0
+    if scales.shape[0] != N or (K > 0 and group not in GROUPS) or (K == 0 and ng != 0):
         raise ValueError("scales shape %s does not match packed %s"
                          % (tuple(scales.shape), tuple(packed.shape)))
-    return N, K
+    return N, K, (group if K > 0 else W4A16_GROUP)
 
 
 def gemv(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,
          y: torch.Tensor = None) -> torch.Tensor:
     """x fp16 [K] -> y fp16 [N] (decode GEMV, M = 1)."""
     lib = library()
-    N, K = _weights(packed, scales)
+    N, K, group = _weights(packed, scales)
     _need(x, "x", torch.float16, 1)
     if x.shape[0] != K:
         raise ValueError("x has %d elements, K = %d" % (x.shape[0], K))
@@ -149,16 +176,22 @@ def gemv(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,
     _need(y, "y", torch.float16, 1)
     if y.shape[0] != N:
         raise ValueError("y has %d elements, N = %d" % (y.shape[0], N))
-    _check("w4a16_gemv", lib.w4a16_gemv(x.data_ptr(), packed.data_ptr(), scales.data_ptr(), N, K,
-                                        y.data_ptr(), _stream()))
+    if group == W4A16_GROUP:
+        st = lib.w4a16_gemv(x.data_ptr(), packed.data_ptr(), scales.data_ptr(), N, K,
+                            y.data_ptr(), _stream())
+    else:
+        st = lib.w4a16_gemv_g(x.data_ptr(), packed.data_ptr(), scales.data_ptr(), N, K, group,
+                              y.data_ptr(), _stream())
+    _check("w4a16_gemv", st)
     return y
 
 
 def gemm(X: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, algo=None,
          Y: torch.Tensor = None) -> torch.Tensor:
-    """X fp16 [M, K] -> Y fp16 [M, N].  algo: None/'auto', 'valu' or 'mfma'."""
+    """X fp16 [M, K] -> Y fp16 [M, N].  algo: None/'auto', 'valu' or 'mfma'
+    ('mfma' needs group 128: the matrix-core kernels read one scale per 128)."""
     lib = library()
-    N, K = _weights(packed, scales)
+    N, K, group = _weights(packed, scales)
     _need(X, "X", torch.float16, 2)
     M = X.shape[0]
     if X.shape[1] != K:
@@ -170,9 +203,16 @@ def gemm(X: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, algo=None,
     _need(Y, "Y", torch.float16, 2)
     if tuple(Y.shape) != (M, N):
         raise ValueError("Y shape %s, want %s" % (tuple(Y.shape), (M, N)))
-    _check("w4a16_gemm_ex", lib.w4a16_gemm_ex(X.data_ptr(), M, packed.data_ptr(),
-                                              scales.data_ptr(), N, K, Y.data_ptr(),
-                                              _ALGOS[algo], _stream()))
+    if group == W4A16_GROUP:
+        st = lib.w4a16_gemm_ex(X.data_ptr(), M, packed.data_ptr(), scales.data_ptr(), N, K,
+                               Y.data_ptr(), _ALGOS[algo], _stream())
+    else:
+        if algo == "mfma":
+            raise ValueError("algo 'mfma' needs group %d, the weights have group %d"
+                             % (W4A16_GROUP, group))
+        st = lib.w4a16_gemm_g(X.data_ptr(), M, packed.data_ptr(), scales.data_ptr(), N, K,
+                              group, Y.data_ptr(), _stream())
+    _check("w4a16_gemm", st)
     return Y
 
 
@@ -196,7 +236,9 @@ def gemv_chain(stages, sync: torch.Tensor) -> None:
         raise ValueError("sync needs %d words" % CHAIN_SYNC_WORDS)
     arr = (GemvStage * max(1, len(stages)))()
     for i, (x, packed, scales, y) in enumerate(stages):
-        N, K = _weights(packed, scales)
+        N, K, group = _weights(packed, scales)
+        if group != W4A16_GROUP:
+            raise ValueError("stage %d: gemv_chain takes group %d weights" % (i, W4A16_GROUP))
         _need(x, "x", torch.float16, 1)
         _need(y, "y", torch.float16, 1)
         if x.shape[0] != K or y.shape[0] != N:
