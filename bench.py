@@ -79,8 +79,9 @@ def secondary(torch, w4a16, inputs, dev, stream):
     """Other rows of the path on their workload shapes: the quantizer (70B FFN
     matrix, larger than the Infinity Cache), batched decode M = 1..32 on the
     8B FFN shapes with both kernel families (locates the VALU/MFMA
-    crossover), and 512-token prefill.  Each figure is the mean of graph
-    replays over enough weight copies to stream from HBM."""
+    crossover), 512-token prefill, and the decode GEMV and quantizer at group
+    sizes 32..256.  Each figure is the mean of graph replays over enough
+    weight copies to stream from HBM."""
     out = {}
 
     def timed(seq_fn, reps=5):
@@ -152,6 +153,28 @@ def secondary(torch, w4a16, inputs, dev, stream):
                                                round(tf / MFMA_F16_PEAK_TFLOPS, 4)}
         del copies
     out["prefill"] = prefill
+
+    # group size as a parameter: decode GEMV (M = 1) on the 8B gate shape and
+    # the quantizer, per group size (scale bytes N*K*2/group)
+    groups = {}
+    K, N = 4096, 14336
+    Wg = torch.from_numpy(inputs.weight(N, K, seed=[8, K, N])).to(dev)
+    x = torch.from_numpy(inputs.activation(1, K, seed=[8, 1])).to(dev)[0]
+    y = torch.empty((N,), dtype=torch.float16, device=dev)
+    for group in (32, 64, 128, 256):
+        pg, sg = w4a16.quantize(Wg, group=group)
+        qus = timed(lambda: w4a16.quantize(Wg, pg, sg, group=group))
+        copies = [(pg, sg)] + [(pg.clone(), sg.clone()) for _ in range(11)]
+        us = timed(lambda: [w4a16.gemv(x, p, s_, y=y) for p, s_ in copies]) / len(copies)
+        b = N * K // 2 + N * (K // group) * 2 + 2 * K + 2 * N
+        qb = N * K * 2 + N * K // 2 + N * (K // group) * 2
+        groups["group %d" % group] = {
+            "gemv_us": round(us, 3), "gemv_GB/s": round(b / (us * 1e-6) / 1e9, 1),
+            "gemv_frac_of_hbm_peak": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "quantize_us": round(qus, 2), "quantize_GB/s": round(qb / (qus * 1e-6) / 1e9, 1)}
+        del copies
+    out["group_sizes_%dx%d" % (K, N)] = groups
+    del Wg
     quantized.clear()
     return out
 
