@@ -139,6 +139,26 @@ int w4a16_gemv_g(const uint16_t* x, const uint32_t* packed, const uint16_t* scal
 int w4a16_gemm_g(const uint16_t* X, int64_t M, const uint32_t* packed, const uint16_t* scales,
                  int64_t N, int64_t K, int64_t group, uint16_t* Y, void* stream);
 
+/* ---- Act-order column order ([QUANT] GPTQ section, act_order: columns are
+ * quantized in an order perm (by Hessian diagonal) and, for inference, the
+ * weight is kept in that order and the activations are permuted the same
+ * way).  perm is a DEVICE int32 [K], 16-byte aligned; column j of the stored
+ * weight is column perm[j] of W, groups of 128 are taken along the stored
+ * order, and an index outside [0, K) reads as 0 (W or x).
+ *   w4a16_quantize_perm:  packed/scales of W[:, perm]   (same as
+ *                         w4a16_quantize on the column-permuted W)
+ *   w4a16_gemv_perm:      y[n] = sum_j x[perm[j]] * ŵ[n,j]
+ *   w4a16_gemm_perm:      Y[m,n] = sum_j X[m, perm[j]] * ŵ[n,j]  (VALU
+ *                         path for every M)
+ * A NULL perm with K > 0 is W4A16_ERR_INVALID_ARG; outputs must not overlap
+ * perm. */
+int w4a16_quantize_perm(const uint16_t* W, const int32_t* perm, int64_t N, int64_t K,
+                        uint32_t* packed, uint16_t* scales, void* stream);
+int w4a16_gemv_perm(const uint16_t* x, const int32_t* perm, const uint32_t* packed,
+                    const uint16_t* scales, int64_t N, int64_t K, uint16_t* y, void* stream);
+int w4a16_gemm_perm(const uint16_t* X, int64_t M, const int32_t* perm, const uint32_t* packed,
+                    const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y, void* stream);
+
 /* ---- Dependent decode sequence ([BENCH] §二: every decode step streams
  * the layers' matrices one after another, each fed by the one before).
  * Runs stages[0..count) as if w4a16_gemv were called on each in order on

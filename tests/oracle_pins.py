@@ -359,8 +359,47 @@ def pin_group_sizes(o) -> list:
     return fails
 
 
+def pin_act_order(o) -> list:
+    """Act order ([QUANT] GPTQ section: columns quantized in the order perm,
+    the weight kept in that order, activations permuted alike at inference).
+    The reference is the composition quantize(W[:, perm]) and
+    matmul(X[:, perm], ...).  Pinned by: the identity order gives the plain
+    product; an exact rational product taken the other way round (dequantize
+    the stored weight, put its columns back in W's order, multiply with the
+    unpermuted X) gives the same outputs; every scale is RNE(absmax/7) of the
+    128 columns perm[128g .. 128g+127] of W."""
+    fails = []
+    rng = np.random.default_rng(77)
+    N, K, M = 6, 384, 3
+    W, X = inputs.weight_and_activation(N, K, M, seed=[96, 0, 0])
+    ident = np.arange(K)
+    p0, s0 = o.quantize(W)
+    pi, si = o.quantize(np.ascontiguousarray(W[:, ident]))
+    if not ((p0 == pi).all() and (s0 == si).all()):
+        fails.append("identity order changes the quantized weight")
+    perm = rng.permutation(K)
+    pp, sp = o.quantize(np.ascontiguousarray(W[:, perm]))
+    Y, _ = o.matmul(np.ascontiguousarray(X[:, perm]), pp, sp)
+    deq = o.dequantize(pp, sp)                     # columns in the stored order
+    inv = np.argsort(perm)
+    back = deq[:, inv]                              # columns in W's order
+    for m in range(M):
+        for n in range(N):
+            terms = [Fraction(float(X[m, k])) * Fraction(float(back[n, k])) for k in range(K)]
+            exact = sum(terms, Fraction(0))
+            bound = K * 2.0 ** -53 * float(sum((abs(t) for t in terms), Fraction(0)))
+            if abs(Fraction(Y[m, n]) - exact) > Fraction(bound):
+                fails.append("act order: (%d,%d) differs from the unpermuted product" % (m, n))
+    a = np.abs(W.astype(np.float64))[:, perm].reshape(N, K // 128, 128).max(axis=2)
+    want_s = np.array([[exact_rne_f16(Fraction(float(v)) / 7) for v in row] for row in a],
+                      dtype=np.uint16)
+    if not (sp == want_s).all():
+        fails.append("act order: scales are not RNE(absmax/7) of the permuted groups")
+    return fails
+
+
 ALL_PINS = [pin_f16_codec, pin_scale_every_fp16, pin_hand_worked, pin_codes_nearest,
-            pin_invariants, pin_matmul_exact, pin_group_sizes]
+            pin_invariants, pin_matmul_exact, pin_group_sizes, pin_act_order]
 
 
 def run_all(o) -> dict:

@@ -34,7 +34,8 @@ def test_header_declares_the_boundary():
     for fn in ["w4a16_quantize", "w4a16_gemv", "w4a16_gemm", "w4a16_gemm_ex",
                "w4a16_packed_bytes", "w4a16_scales_bytes", "w4a16_status_string",
                "w4a16_valu_max_m", "w4a16_quantize_g", "w4a16_gemv_g", "w4a16_gemm_g",
-               "w4a16_scales_bytes_g"]:
+               "w4a16_scales_bytes_g", "w4a16_quantize_perm", "w4a16_gemv_perm",
+               "w4a16_gemm_perm"]:
         assert fn in names
 
 
@@ -157,6 +158,29 @@ def test_group_size_validation(lib):
                    torch.zeros(4, 3, dtype=torch.float16))       # 256 / 3: no group
 
 
+def test_act_order_validation(lib):
+    """Act-order entry points: perm is required for K > 0, 16-byte aligned,
+    and no output may overlap it."""
+    A, B, C, D, P = FAKE, FAKE * 4, FAKE * 8, FAKE * 12, FAKE * 16
+    q, gv, gm = lib.w4a16_quantize_perm, lib.w4a16_gemv_perm, lib.w4a16_gemm_perm
+    assert q(A, None, 4, 128, B, C, None) == INVALID
+    assert q(A, P + 4, 4, 128, B, C, None) == MISALIGNED
+    assert q(A, B + 64, 4, 128, B, C, None) == INVALID        # packed overlaps perm
+    assert q(A, P, 4, 100, B, C, None) == SHAPE
+    assert q(None, None, 0, 128, None, None, None) == OK
+    assert gv(A, None, B, C, 16, 128, D, None) == INVALID
+    assert gv(A, P + 8, B, C, 16, 128, D, None) == MISALIGNED
+    assert gv(A, P, B, C, 16, 128, P + 2, None) == INVALID      # y overlaps perm
+    assert gm(A, 2, None, B, C, 16, 128, D, None) == INVALID
+    assert gm(A, 2, P, B, C, 16, 130, D, None) == SHAPE
+    assert gm(None, 0, None, None, None, 16, 128, None, None) == OK
+    import torch
+    with pytest.raises(ValueError):
+        w4a16.gemv(torch.zeros(128, dtype=torch.float16),
+                   torch.zeros(4, 16, dtype=torch.int32), torch.zeros(4, 1, dtype=torch.float16),
+                   perm=torch.zeros(128, dtype=torch.int64))
+
+
 @pytest.mark.skipif(__import__("torch").cuda.device_count() > 0,
                     reason="with a GPU present valid arguments would launch")
 def test_valid_arguments_without_device_report_device_error(lib):
@@ -165,6 +189,7 @@ def test_valid_arguments_without_device_report_device_error(lib):
     assert lib.w4a16_quantize(A, 4, 128, B, C, None) == DEVICE
     assert lib.w4a16_quantize_g(A, 4, 256, 64, B, C, None) == DEVICE
     assert lib.w4a16_gemm_g(A, 2, B, C, 16, 256, 256, D, None) == DEVICE
+    assert lib.w4a16_gemv_perm(A, FAKE * 16, B, C, 16, 128, D, None) == DEVICE
 
 
 def test_binding_rejects_bad_tensors():

@@ -488,3 +488,95 @@ def test_group_sizes_reject_matrix_cores(w4, orc):
     X = inputs.activation(4, 256, seed=[26, 1])
     with pytest.raises(ValueError):
         w4.gemm(dev(X), packed_to_dev(packed), scales_to_dev(scales), algo="mfma")
+
+
+# ------------------------------------------------------- act-order column order
+
+def perm_of(kind: str, K: int, seed) -> np.ndarray:
+    rng = np.random.default_rng(seed)
+    if kind == "identity":
+        return np.arange(K, dtype=np.int32)
+    if kind == "reverse":
+        return np.arange(K - 1, -1, -1, dtype=np.int32)
+    return rng.permutation(K).astype(np.int32)
+
+
+@pytest.mark.parametrize("kind", ["identity", "reverse", "random"])
+@pytest.mark.parametrize("N,K", [(37, 384), (300, 4096), (129, 14336)])
+def test_quantize_act_order_bit_exact(w4, orc, kind, N, K):
+    """w4a16_quantize_perm = the oracle's quantizer on W[:, perm], bit for bit."""
+    say("quantize act-order %s N=%d K=%d" % (kind, N, K))
+    W = inputs.weight(N, K, seed=[31, N, K])
+    perm = perm_of(kind, K, [31, K])
+    pg, sg = w4.quantize(dev(W), perm=dev(perm))
+    torch.cuda.synchronize()
+    po, so = orc.quantize(np.ascontiguousarray(W[:, perm]))
+    assert (sg.cpu().numpy().view(np.uint16) == so).all()
+    assert (pg.cpu().numpy().view(np.uint32) == po).all()
+
+
+@pytest.mark.parametrize("kind", ["identity", "random"])
+@pytest.mark.parametrize("M", [1, 2, 3, 8, 13])
+@pytest.mark.parametrize("N,K", [(300, 1536), (1001, 4096), (64, 14336)])
+def test_linear_act_order(w4, orc, kind, M, N, K):
+    """y = X[:, perm] . Ŵpᵀ on the VALU path (persistent kernel with whole-x
+    staging, and K slices for M = 8, 13 at K = 14336) against the oracle on
+    the gathered activations."""
+    say("linear act-order %s M=%d N=%d K=%d" % (kind, M, N, K))
+    W = inputs.weight(N, K, seed=[32, N, K])
+    perm = perm_of(kind, K, [32, K])
+    packed, scales = orc.quantize(np.ascontiguousarray(W[:, perm]))
+    X = inputs.activation(M, K, seed=[32, M, N, K])
+    if M == 1:
+        Y = w4.gemv(dev(X)[0], packed_to_dev(packed), scales_to_dev(scales),
+                    perm=dev(perm)).cpu().numpy()[None]
+    else:
+        Y = w4.gemm(dev(X), packed_to_dev(packed), scales_to_dev(scales),
+                    perm=dev(perm)).cpu().numpy()
+    torch.cuda.synchronize()
+    Yref, Yabs = orc.matmul(np.ascontiguousarray(X[:, perm]), packed, scales)
+    tol = oracle.tolerance(Yref, Yabs)
+    err = np.abs(Y.astype(np.float64) - Yref)
+    bad = np.argwhere(~(err <= tol))
+    assert bad.size == 0, "%d outputs out of tolerance, first %s" % (len(bad), bad[0])
+
+
+def test_act_order_one_hot_exact(w4, orc):
+    """A one-hot x at position k selects stored column inv[k]: fp16(s*q) exactly."""
+    N, K = 40, 512
+    W = inputs.weight(N, K, seed=[33])
+    perm = perm_of("random", K, [33])
+    packed, scales = orc.quantize(np.ascontiguousarray(W[:, perm]))
+    deq = orc.dequantize(packed, scales)
+    inv = np.argsort(perm)
+    say("act-order one-hot")
+    for k in [0, 1, 127, 128, 300, 511]:
+        x = np.zeros(K, dtype=np.float16)
+        x[k] = np.float16(1.0)
+        y = w4.gemv(dev(x), packed_to_dev(packed), scales_to_dev(scales), perm=dev(perm))
+        torch.cuda.synchronize()
+        want = deq[:, inv[k]].astype(np.float16)
+        assert (y.cpu().numpy().view(np.uint16) == want.view(np.uint16)).all(), k
+
+
+def test_act_order_out_of_range_index_reads_zero(w4, orc):
+    """perm entries outside [0, K) read as 0 (documented), in both the
+    quantizer and the GEMV; no access leaves the buffers."""
+    N, K = 16, 256
+    W = inputs.weight(N, K, seed=[34])
+    X = inputs.activation(1, K, seed=[34, 1])
+    perm = perm_of("random", K, [34]).copy()
+    perm[5], perm[130], perm[200] = -1, K, 1 << 30
+    Wz = np.ascontiguousarray(W[:, np.clip(perm, 0, K - 1)])
+    Wz[:, [5, 130, 200]] = np.float16(0)
+    pg, sg = w4.quantize(dev(W), perm=dev(perm))
+    torch.cuda.synchronize()
+    po, so = orc.quantize(Wz)
+    assert (pg.cpu().numpy().view(np.uint32) == po).all()
+    assert (sg.cpu().numpy().view(np.uint16) == so).all()
+    Xz = np.ascontiguousarray(X[:, np.clip(perm, 0, K - 1)])
+    Xz[:, [5, 130, 200]] = np.float16(0)
+    y = w4.gemv(dev(X)[0], pg, sg, perm=dev(perm)).cpu().numpy()[None]
+    torch.cuda.synchronize()
+    Yref, Yabs = orc.matmul(Xz, po, so)
+    assert (np.abs(y.astype(np.float64) - Yref) <= oracle.tolerance(Yref, Yabs)).all()

@@ -76,59 +76,70 @@ int group_shift(int64_t group) { return group == 32 ? 0 : group == 64 ? 1 : grou
 
 int status_of(hipError_t e) { return e == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH; }
 
+// perm: NULL, or the act-order column order (device int32 [K]).
 int linear(const uint16_t* X, int64_t M, const uint32_t* packed, const uint16_t* scales,
-           int64_t N, int64_t K, int64_t group, uint16_t* Y, int algo, void* stream) {
+           int64_t N, int64_t K, int64_t group, uint16_t* Y, int algo, void* stream,
+           const int32_t* perm = nullptr, bool with_perm = false) {
     int st = check_sizes(M, N, K);
     if (st != W4A16_OK) return st;
     st = check_group(group, K);
     if (st != W4A16_OK) return st;
     if (algo != W4A16_ALGO_AUTO && algo != W4A16_ALGO_VALU && algo != W4A16_ALGO_MFMA)
         return W4A16_ERR_INVALID_ARG;
-    // the matrix-core kernels read one scale per 128 elements
-    if (algo == W4A16_ALGO_MFMA && group != W4A16_GROUP) return W4A16_ERR_INVALID_ARG;
+    // the matrix-core kernels read one scale per 128 elements and no perm
+    if (algo == W4A16_ALGO_MFMA && (group != W4A16_GROUP || with_perm))
+        return W4A16_ERR_INVALID_ARG;
     if (M == 0 || N == 0) return W4A16_OK;
     // With K == 0 the inputs hold no bytes and may be NULL; they are never read.
-    if (!Y || (K > 0 && (!X || !packed || !scales))) return W4A16_ERR_INVALID_ARG;
-    if (!aligned(X, 16) || !aligned(packed, 16) || !aligned(scales, 2) || !aligned(Y, 2))
+    if (!Y || (K > 0 && (!X || !packed || !scales || (with_perm && !perm))))
+        return W4A16_ERR_INVALID_ARG;
+    if (!aligned(X, 16) || !aligned(packed, 16) || !aligned(scales, 2) || !aligned(Y, 2) ||
+        !aligned(perm, 16))
         return W4A16_ERR_MISALIGNED;
     const size_t y_bytes = (size_t)M * N * 2;
     if (overlap(Y, y_bytes, X, (size_t)M * K * 2) ||
         overlap(Y, y_bytes, packed, (size_t)N * K / 2) ||
-        overlap(Y, y_bytes, scales, (size_t)N * (K / group) * 2))
+        overlap(Y, y_bytes, scales, (size_t)N * (K / group) * 2) ||
+        (with_perm && overlap(Y, y_bytes, perm, (size_t)K * 4)))
         return W4A16_ERR_INVALID_ARG;
     int num_cu = 0;
     st = current_device(&num_cu);
     if (st != W4A16_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const bool valu = algo == W4A16_ALGO_VALU || group != W4A16_GROUP ||
+    const bool valu = algo == W4A16_ALGO_VALU || group != W4A16_GROUP || with_perm ||
                       (algo == W4A16_ALGO_AUTO && M <= kValuMaxM);
     if (valu)
         return status_of(w4a16::launch_gemv_valu(X, M, packed, scales, N, K, Y, s, num_cu,
-                                                 group_shift(group)));
+                                                 group_shift(group),
+                                                 with_perm ? perm : nullptr));
     return status_of(w4a16::launch_gemm_mfma(X, M, packed, scales, N, K, Y, s, num_cu));
 }
 
 int quantize(const uint16_t* W, int64_t N, int64_t K, int64_t group, uint32_t* packed,
-             uint16_t* scales, void* stream) {
+             uint16_t* scales, void* stream, const int32_t* perm = nullptr,
+             bool with_perm = false) {
     int st = check_sizes(0, N, K);
     if (st != W4A16_OK) return st;
     st = check_group(group, K);
     if (st != W4A16_OK) return st;
     if (N == 0 || K == 0) return W4A16_OK;
-    if (!W || !packed || !scales) return W4A16_ERR_INVALID_ARG;
-    if (!aligned(W, 16) || !aligned(packed, 16) || !aligned(scales, 2))
+    if (!W || !packed || !scales || (with_perm && !perm)) return W4A16_ERR_INVALID_ARG;
+    if (!aligned(W, 16) || !aligned(packed, 16) || !aligned(scales, 2) || !aligned(perm, 16))
         return W4A16_ERR_MISALIGNED;
     const size_t w_bytes = (size_t)N * K * 2;
     const size_t p_bytes = (size_t)N * K / 2;
     const size_t s_bytes = (size_t)N * (K / group) * 2;
     if (overlap(packed, p_bytes, W, w_bytes) || overlap(scales, s_bytes, W, w_bytes) ||
-        overlap(packed, p_bytes, scales, s_bytes))
+        overlap(packed, p_bytes, scales, s_bytes) ||
+        (with_perm && (overlap(packed, p_bytes, perm, (size_t)K * 4) ||
+                       overlap(scales, s_bytes, perm, (size_t)K * 4))))
         return W4A16_ERR_INVALID_ARG;
     int num_cu = 0;
     st = current_device(&num_cu);
     if (st != W4A16_OK) return st;
     return status_of(w4a16::launch_quantize(W, N, K, group, packed, scales,
-                                            static_cast<hipStream_t>(stream)));
+                                            static_cast<hipStream_t>(stream),
+                                            with_perm ? perm : nullptr));
 }
 
 }  // namespace
@@ -182,6 +193,23 @@ int w4a16_gemm_g(const uint16_t* X, int64_t M, const uint32_t* packed, const uin
 int w4a16_gemm_ex(const uint16_t* X, int64_t M, const uint32_t* packed, const uint16_t* scales,
                   int64_t N, int64_t K, uint16_t* Y, int algo, void* stream) {
     return linear(X, M, packed, scales, N, K, W4A16_GROUP, Y, algo, stream);
+}
+
+int w4a16_quantize_perm(const uint16_t* W, const int32_t* perm, int64_t N, int64_t K,
+                        uint32_t* packed, uint16_t* scales, void* stream) {
+    return quantize(W, N, K, W4A16_GROUP, packed, scales, stream, perm, true);
+}
+
+int w4a16_gemv_perm(const uint16_t* x, const int32_t* perm, const uint32_t* packed,
+                    const uint16_t* scales, int64_t N, int64_t K, uint16_t* y, void* stream) {
+    return linear(x, 1, packed, scales, N, K, W4A16_GROUP, y, W4A16_ALGO_VALU, stream, perm,
+                  true);
+}
+
+int w4a16_gemm_perm(const uint16_t* X, int64_t M, const int32_t* perm, const uint32_t* packed,
+                    const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y, void* stream) {
+    return linear(X, M, packed, scales, N, K, W4A16_GROUP, Y, W4A16_ALGO_AUTO, stream, perm,
+                  true);
 }
 
 int w4a16_gemv_chain(const w4a16_gemv_stage* stages, int count, uint32_t* sync, void* stream) {

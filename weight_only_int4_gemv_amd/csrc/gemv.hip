@@ -28,10 +28,30 @@ namespace w4a16 {
 
 namespace {
 
+// The 8 activations of row m at positions col0 .. col0+7 of the weight's
+// column order.  Without perm they are X[m, col0 .. col0+7]; with perm (the
+// act-order layout, [QUANT] GPTQ section: columns quantized and stored in
+// the order perm, activations permuted the same way at inference) they are
+// X[m, perm[col0 + i]], and an index outside [0, K) reads as 0.
+__device__ __forceinline__ uint4 x_block(const uint16_t* __restrict__ X, int m, int K, int col0,
+                                         const int* __restrict__ perm) {
+    const uint16_t* row = X + (size_t)m * K;
+    if (perm == nullptr) return reinterpret_cast<const uint4*>(row + col0)[0];
+    const int4 p0 = reinterpret_cast<const int4*>(perm + col0)[0];
+    const int4 p1 = reinterpret_cast<const int4*>(perm + col0)[1];
+    const int idx[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+    uint32_t h[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) h[i] = (uint32_t)idx[i] < (uint32_t)K ? row[idx[i]] : 0u;
+    return make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                      h[6] | (h[7] << 16));
+}
+
 // Stage activation rows [0, M) x elements [k0, k0 + ks) into LDS:
 //   xs[m * (ks/8) + b] = paired 8-element block b of the slice.
 __device__ __forceinline__ void stage_activations(const uint16_t* __restrict__ X, int M, int K,
-                                                  int k0, int ks, uint4* xs) {
+                                                  int k0, int ks, uint4* xs,
+                                                  const int* __restrict__ perm) {
     const int nblk = ks >> 3;
     const int total = M * nblk;
     constexpr int B = 4;  // loads issued before the first store
@@ -42,7 +62,7 @@ __device__ __forceinline__ void stage_activations(const uint16_t* __restrict__ X
             const int i = i0 + j * blockDim.x;
             if (i < total) {
                 const int m = i / nblk;
-                v[j] = reinterpret_cast<const uint4*>(X + (size_t)m * K + k0)[i - m * nblk];
+                v[j] = x_block(X, m, K, k0 + (i - m * nblk) * 8, perm);
             }
         }
 #pragma unroll
@@ -61,7 +81,7 @@ template <int MMAX, int R, int U, int WAVES>
 __global__ __launch_bounds__(WAVES * kWave) void gemv_kernel(
     const uint16_t* __restrict__ X, int M, const uint4* __restrict__ packed,
     const uint16_t* __restrict__ scales, uint16_t* __restrict__ Y, int N, int K, int kslice,
-    int gshift) {
+    int gshift, const int* __restrict__ perm) {
     extern __shared__ uint4 lds[];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
@@ -131,7 +151,7 @@ __global__ __launch_bounds__(WAVES * kWave) void gemv_kernel(
         // busy while the block waits on its barrier.
         load(0, wa, sa);
         if (k0 > 0) __syncthreads();     // previous slice fully consumed
-        stage_activations(X, M, K, k0, ks, lds);
+        stage_activations(X, M, K, k0, ks, lds, perm);
         __syncthreads();
 
         for (int s0 = 0; s0 < nsteps; s0 += 2 * U) {
@@ -174,7 +194,8 @@ __global__ __launch_bounds__(WAVES * kWave) void gemv_kernel(
 template <int MMAX, int R, int P, int WAVES, int XPT>
 __global__ __launch_bounds__(WAVES * kWave) void gemv_persistent_kernel(
     const uint16_t* __restrict__ X, int M, const uint4* __restrict__ packed,
-    const uint16_t* __restrict__ scales, uint16_t* __restrict__ Y, int N, int K, int gshift) {
+    const uint16_t* __restrict__ scales, uint16_t* __restrict__ Y, int N, int K, int gshift,
+    const int* __restrict__ perm) {
     extern __shared__ uint4 lds[];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -197,7 +218,7 @@ __global__ __launch_bounds__(WAVES * kWave) void gemv_persistent_kernel(
     for (int i = 0; i < XPT; ++i) {
         const int e = min((int)threadIdx.x + i * WAVES * kWave, xblocks - 1);
         const int m = e / (K >> 3);
-        xr[i] = reinterpret_cast<const uint4*>(X + (size_t)m * K)[e - m * (K >> 3)];
+        xr[i] = x_block(X, m, K, (e - m * (K >> 3)) * 8, perm);
     }
 
     // load cursor (wave-uniform): iteration tl -> (row group lrg, step ls)
@@ -308,7 +329,7 @@ constexpr int kLdsBudget = 64 * 1024;
 template <int MMAX, int R, int U, int WAVES>
 hipError_t launch_gemv_t(const uint16_t* X, int64_t M, const uint32_t* packed,
                          const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y,
-                         hipStream_t stream, int gshift = 2) {
+                         hipStream_t stream, int gshift = 2, const int* perm = nullptr) {
     // LDS: 2 bytes per activation element.
     int64_t kslice = (int64_t)(kLdsBudget / (MMAX * 2)) / kGroup * kGroup;
     if (kslice > K) kslice = K;
@@ -319,18 +340,20 @@ hipError_t launch_gemv_t(const uint16_t* X, int64_t M, const uint32_t* packed,
     hipLaunchKernelGGL((gemv_kernel<MMAX, R, U, WAVES>), dim3((unsigned)blocks),
                        dim3(WAVES * kWave), lds, stream, X, (int)M,
                        reinterpret_cast<const uint4*>(packed), scales, Y, (int)N, (int)K,
-                       (int)kslice, gshift);
+                       (int)kslice, gshift, perm);
     return hipGetLastError();
 }
 
 template <int MMAX, int R, int P, int WAVES, int XPT>
 hipError_t launch_persistent_xpt(const uint16_t* X, int64_t M, const uint32_t* packed,
                                  const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y,
-                                 hipStream_t stream, int64_t blocks, int gshift) {
+                                 hipStream_t stream, int64_t blocks, int gshift,
+                                 const int* perm) {
     const size_t lds = (size_t)MMAX * (K / 8) * sizeof(uint4);
     hipLaunchKernelGGL((gemv_persistent_kernel<MMAX, R, P, WAVES, XPT>), dim3((unsigned)blocks),
                        dim3(WAVES * kWave), lds, stream, X, (int)M,
-                       reinterpret_cast<const uint4*>(packed), scales, Y, (int)N, (int)K, gshift);
+                       reinterpret_cast<const uint4*>(packed), scales, Y, (int)N, (int)K, gshift,
+                       perm);
     return hipGetLastError();
 }
 
@@ -340,7 +363,7 @@ template <int MMAX, int R, int P, int WAVES>
 hipError_t launch_persistent_t(const uint16_t* X, int64_t M, const uint32_t* packed,
                                const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y,
                                hipStream_t stream, int num_cu, int blocks_per_cu,
-                               int gshift = 2) {
+                               int gshift = 2, const int* perm = nullptr) {
     const int64_t total_rg = (N + R - 1) / R;
     const int64_t max_waves = (int64_t)num_cu * blocks_per_cu * WAVES;
     const int64_t per_wave = (total_rg + max_waves - 1) / max_waves;
@@ -349,14 +372,19 @@ hipError_t launch_persistent_t(const uint16_t* X, int64_t M, const uint32_t* pac
     const int64_t need = (int64_t)MMAX * (K / 8);             // x blocks to stage
     const int64_t threads = (int64_t)WAVES * kWave;
     if (need <= threads)
-        return launch_persistent_xpt<MMAX, R, P, WAVES, 1>(X, M, packed, scales, N, K, Y, stream, blocks, gshift);
+        return launch_persistent_xpt<MMAX, R, P, WAVES, 1>(X, M, packed, scales, N, K, Y, stream, blocks, gshift,
+                                                             perm);
     if (need <= 2 * threads)
-        return launch_persistent_xpt<MMAX, R, P, WAVES, 2>(X, M, packed, scales, N, K, Y, stream, blocks, gshift);
+        return launch_persistent_xpt<MMAX, R, P, WAVES, 2>(X, M, packed, scales, N, K, Y, stream, blocks, gshift,
+                                                             perm);
     if (need <= 4 * threads)
-        return launch_persistent_xpt<MMAX, R, P, WAVES, 4>(X, M, packed, scales, N, K, Y, stream, blocks, gshift);
+        return launch_persistent_xpt<MMAX, R, P, WAVES, 4>(X, M, packed, scales, N, K, Y, stream, blocks, gshift,
+                                                             perm);
     if (need <= 8 * threads)
-        return launch_persistent_xpt<MMAX, R, P, WAVES, 8>(X, M, packed, scales, N, K, Y, stream, blocks, gshift);
-    return launch_persistent_xpt<MMAX, R, P, WAVES, 16>(X, M, packed, scales, N, K, Y, stream, blocks, gshift);
+        return launch_persistent_xpt<MMAX, R, P, WAVES, 8>(X, M, packed, scales, N, K, Y, stream, blocks, gshift,
+                                                             perm);
+    return launch_persistent_xpt<MMAX, R, P, WAVES, 16>(X, M, packed, scales, N, K, Y, stream, blocks, gshift,
+                                                             perm);
 }
 
 // Launch choice (measured on MI355X over the decode layer shapes, K x N from
@@ -369,7 +397,7 @@ hipError_t launch_persistent_t(const uint16_t* X, int64_t M, const uint32_t* pac
 template <int MMAX>
 hipError_t launch_gemv_m(const uint16_t* X, int64_t M, const uint32_t* packed,
                          const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y,
-                         hipStream_t stream, int num_cu, int gshift) {
+                         hipStream_t stream, int num_cu, int gshift, const int* perm) {
     if (K > 0 && (int64_t)MMAX * K * 2 <= kLdsBudget) {
         constexpr int R = MMAX >= 4 ? 1 : 2;
         // Measured on gfx950 for M = 1: long rows (K = 14336) run best with
@@ -377,34 +405,40 @@ hipError_t launch_gemv_m(const uint16_t* X, int64_t M, const uint32_t* packed,
         // against 8.6 us with two steps in flight).
         if (MMAX == 1 && K >= 12288)
             return launch_persistent_t<1, 2, 1, 8>(X, M, packed, scales, N, K, Y, stream, num_cu,
-                                                   2, gshift);
+                                                   2, gshift, perm);
         if (K >= 12288)
             return launch_persistent_t<MMAX, R, 2, 8>(X, M, packed, scales, N, K, Y, stream,
-                                                      num_cu, 2, gshift);
+                                                      num_cu, 2, gshift, perm);
         return launch_persistent_t<MMAX, R, 1, 4>(X, M, packed, scales, N, K, Y, stream, num_cu,
-                                                  6, gshift);
+                                                  6, gshift, perm);
     }
     constexpr int WAVES = 4;
     if (N >= (int64_t)4 * WAVES * num_cu && MMAX <= 4)
-        return launch_gemv_t<MMAX, 4, 2, WAVES>(X, M, packed, scales, N, K, Y, stream, gshift);
+        return launch_gemv_t<MMAX, 4, 2, WAVES>(X, M, packed, scales, N, K, Y, stream, gshift,
+                                                perm);
     if (N >= (int64_t)2 * WAVES * num_cu)
-        return launch_gemv_t<MMAX, 2, 2, WAVES>(X, M, packed, scales, N, K, Y, stream, gshift);
-    return launch_gemv_t<MMAX, 1, 4, WAVES>(X, M, packed, scales, N, K, Y, stream, gshift);
+        return launch_gemv_t<MMAX, 2, 2, WAVES>(X, M, packed, scales, N, K, Y, stream, gshift,
+                                                perm);
+    return launch_gemv_t<MMAX, 1, 4, WAVES>(X, M, packed, scales, N, K, Y, stream, gshift,
+                                                perm);
 }
 
 }  // namespace
 
 hipError_t launch_gemv_valu(const uint16_t* X, int64_t M, const uint32_t* packed,
                             const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y,
-                            hipStream_t stream, int num_cu, int gshift) {
-    if (M == 1) return launch_gemv_m<1>(X, M, packed, scales, N, K, Y, stream, num_cu, gshift);
-    if (M == 2) return launch_gemv_m<2>(X, M, packed, scales, N, K, Y, stream, num_cu, gshift);
-    if (M <= 4) return launch_gemv_m<4>(X, M, packed, scales, N, K, Y, stream, num_cu, gshift);
+                            hipStream_t stream, int num_cu, int gshift, const int* perm) {
+    if (M == 1)
+        return launch_gemv_m<1>(X, M, packed, scales, N, K, Y, stream, num_cu, gshift, perm);
+    if (M == 2)
+        return launch_gemv_m<2>(X, M, packed, scales, N, K, Y, stream, num_cu, gshift, perm);
+    if (M <= 4)
+        return launch_gemv_m<4>(X, M, packed, scales, N, K, Y, stream, num_cu, gshift, perm);
     // M > 8 is split into slices of at most 8 activation rows.
     for (int64_t m0 = 0; m0 < M; m0 += 8) {
         const int64_t mm = (M - m0 < 8) ? (M - m0) : 8;
         hipError_t e = launch_gemv_m<8>(X + m0 * K, mm, packed, scales, N, K, Y + m0 * N,
-                                        stream, num_cu, gshift);
+                                        stream, num_cu, gshift, perm);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

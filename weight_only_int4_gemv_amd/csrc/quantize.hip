@@ -101,11 +101,17 @@ __device__ __forceinline__ uint32_t quantize8(const uint4& v, uint16_t& s_bits) 
 // steps (groups g, g + stride, ...) are issued together.  All LG lanes of a
 // slice share g, so the reductions only ever combine lanes that are active
 // together.
+//
+// perm (act-order layout, [QUANT] GPTQ section: columns quantized and stored
+// in the order perm): NULL, or device int32 [K]; column j of the output is
+// column perm[j] of W (an index outside [0, K) reads as 0), gathered with
+// 2-byte loads instead of one 16-byte load per lane.
 template <int LG, int U>
 __global__ __launch_bounds__(256) void quantize_kernel(const uint4* __restrict__ W,
                                                        uint32_t* __restrict__ packed,
                                                        uint16_t* __restrict__ scales,
-                                                       int64_t total_groups) {
+                                                       int64_t total_groups, int K,
+                                                       const int* __restrict__ perm) {
     const int lg = threadIdx.x & (LG - 1);              // lane within the group
     const int64_t stride = (int64_t)gridDim.x * (blockDim.x / LG);
     typedef unsigned v4u __attribute__((ext_vector_type(4)));
@@ -117,8 +123,25 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint4* __restrict__
         for (int u = 0; u < U; ++u) {
             // W is read once: non-temporal loads
             a[u] = (v4u){0u, 0u, 0u, 0u};
-            if (g + u * stride < total_groups)
-                a[u] = __builtin_nontemporal_load(Wv + (g + u * stride) * LG + lg);
+            const int64_t gu = g + u * stride;
+            if (gu < total_groups) {
+                if (perm == nullptr) {
+                    a[u] = __builtin_nontemporal_load(Wv + gu * LG + lg);
+                } else {
+                    const int64_t gpr = K / (LG * 8);            // groups per row
+                    const int64_t n = gu / gpr;
+                    const int col = (int)(gu - n * gpr) * (LG * 8) + lg * 8;
+                    const uint16_t* row = reinterpret_cast<const uint16_t*>(W) + n * K;
+                    uint32_t h[8];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const int p = perm[col + i];
+                        h[i] = (uint32_t)p < (uint32_t)K ? row[p] : 0u;
+                    }
+                    a[u] = (v4u){h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                                 h[6] | (h[7] << 16)};
+                }
+            }
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -135,26 +158,29 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint4* __restrict__
 }
 
 template <int LG, int U>
-hipError_t launch_quantize_t(const uint16_t* W, int64_t groups, uint32_t* packed,
-                             uint16_t* scales, hipStream_t stream, int64_t max_blocks) {
+hipError_t launch_quantize_t(const uint16_t* W, int64_t groups, int64_t K, const int* perm,
+                             uint32_t* packed, uint16_t* scales, hipStream_t stream,
+                             int64_t max_blocks) {
     constexpr int per_block = 256 / LG;                  // groups per block and step
     int64_t blocks = (groups + per_block * U - 1) / (per_block * U);
     if (blocks > max_blocks) blocks = max_blocks;        // grid-stride beyond this
     hipLaunchKernelGGL((quantize_kernel<LG, U>), dim3((unsigned)blocks), dim3(256), 0, stream,
-                       reinterpret_cast<const uint4*>(W), packed, scales, groups);
+                       reinterpret_cast<const uint4*>(W), packed, scales, groups, (int)K, perm);
     return hipGetLastError();
 }
 
 hipError_t launch_quantize(const uint16_t* W, int64_t N, int64_t K, int64_t group,
-                           uint32_t* packed, uint16_t* scales, hipStream_t stream) {
+                           uint32_t* packed, uint16_t* scales, hipStream_t stream,
+                           const int* perm) {
     const int64_t groups = N * (K / group);
     if (groups == 0) return hipSuccess;
     // the same 16 bytes per lane and two groups' loads in flight for every G
+    constexpr int64_t kMaxBlocks = 65536;
     switch (group) {
-        case 32: return launch_quantize_t<4, 2>(W, groups, packed, scales, stream, 65536);
-        case 64: return launch_quantize_t<8, 2>(W, groups, packed, scales, stream, 65536);
-        case 128: return launch_quantize_t<16, 2>(W, groups, packed, scales, stream, 65536);
-        case 256: return launch_quantize_t<32, 2>(W, groups, packed, scales, stream, 65536);
+        case 32: return launch_quantize_t<4, 2>(W, groups, K, perm, packed, scales, stream, kMaxBlocks);
+        case 64: return launch_quantize_t<8, 2>(W, groups, K, perm, packed, scales, stream, kMaxBlocks);
+        case 128: return launch_quantize_t<16, 2>(W, groups, K, perm, packed, scales, stream, kMaxBlocks);
+        case 256: return launch_quantize_t<32, 2>(W, groups, K, perm, packed, scales, stream, kMaxBlocks);
         default: return hipErrorInvalidValue;
     }
 }

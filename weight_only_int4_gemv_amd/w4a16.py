@@ -66,8 +66,12 @@ def library() -> ctypes.CDLL:
         lib.w4a16_quantize_g.argtypes = [_p, _i64, _i64, _i64, _p, _p, _p]
         lib.w4a16_gemv_g.argtypes = [_p, _p, _p, _i64, _i64, _i64, _p, _p]
         lib.w4a16_gemm_g.argtypes = [_p, _i64, _p, _p, _i64, _i64, _i64, _p, _p]
+        lib.w4a16_quantize_perm.argtypes = [_p, _p, _i64, _i64, _p, _p, _p]
+        lib.w4a16_gemv_perm.argtypes = [_p, _p, _p, _p, _i64, _i64, _p, _p]
+        lib.w4a16_gemm_perm.argtypes = [_p, _i64, _p, _p, _p, _i64, _i64, _p, _p]
         for f in (lib.w4a16_quantize, lib.w4a16_gemv, lib.w4a16_gemm, lib.w4a16_gemm_ex,
-                  lib.w4a16_quantize_g, lib.w4a16_gemv_g, lib.w4a16_gemm_g):
+                  lib.w4a16_quantize_g, lib.w4a16_gemv_g, lib.w4a16_gemm_g,
+                  lib.w4a16_quantize_perm, lib.w4a16_gemv_perm, lib.w4a16_gemm_perm):
             f.restype = ctypes.c_int
         lib.w4a16_valu_max_m.restype = ctypes.c_int64
         lib.w4a16_gemv_chain.argtypes = [ctypes.POINTER(GemvStage), ctypes.c_int, _p, _p]
@@ -123,14 +127,27 @@ def _check_group(group: int, K: int) -> None:
                          % (K, W4A16_GROUP, group))
 
 
+def _perm(perm, K: int):
+    """Checks an act-order column order: int32 [K] on the GPU."""
+    _need(perm, "perm", torch.int32, 1)
+    if perm.shape[0] != K:
+        raise ValueError("perm has %d entries, K = %d" % (perm.shape[0], K))
+    return perm
+
+
 def quantize(W: torch.Tensor, packed: torch.Tensor = None, scales: torch.Tensor = None,
-             group: int = W4A16_GROUP):
+             group: int = W4A16_GROUP, perm: torch.Tensor = None):
     """W fp16 [N, K] -> (packed int32 [N, K/8] holding uint32 words, scales fp16
-    [N, K/group]); group 32, 64, 128 (default) or 256."""
+    [N, K/group]); group 32, 64, 128 (default) or 256.  perm (int32 [K], act
+    order, group 128 only): quantize the column-permuted W[:, perm]."""
     lib = library()
     _need(W, "W", torch.float16, 2)
     N, K = W.shape
     _check_group(group, K)
+    if perm is not None:
+        _perm(perm, K)
+        if group != W4A16_GROUP:
+            raise ValueError("act order takes group %d" % W4A16_GROUP)
     if packed is None:
         packed = torch.empty((N, K // 8), dtype=torch.int32, device=W.device)
     if scales is None:
@@ -139,7 +156,10 @@ def quantize(W: torch.Tensor, packed: torch.Tensor = None, scales: torch.Tensor 
     _need(scales, "scales", torch.float16, 2)
     if tuple(packed.shape) != (N, K // 8) or tuple(scales.shape) != (N, K // group):
         raise ValueError("output shapes do not match W")
-    if group == W4A16_GROUP:
+    if perm is not None:
+        st = lib.w4a16_quantize_perm(W.data_ptr(), perm.data_ptr(), N, K, packed.data_ptr(),
+                                     scales.data_ptr(), _stream())
+    elif group == W4A16_GROUP:
         st = lib.w4a16_quantize(W.data_ptr(), N, K, packed.data_ptr(), scales.data_ptr(),
                                 _stream())
     else:
@@ -164,8 +184,9 @@ def _weights(packed: torch.Tensor, scales: torch.Tensor):
 
 
 def gemv(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,
-         y: torch.Tensor = None) -> torch.Tensor:
-    """x fp16 [K] -> y fp16 [N] (decode GEMV, M = 1)."""
+         y: torch.Tensor = None, perm: torch.Tensor = None) -> torch.Tensor:
+    """x fp16 [K] -> y fp16 [N] (decode GEMV, M = 1).  perm: act-order column
+    order of the weight (int32 [K]); column j meets x[perm[j]]."""
     lib = library()
     N, K, group = _weights(packed, scales)
     _need(x, "x", torch.float16, 1)
@@ -176,7 +197,13 @@ def gemv(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,
     _need(y, "y", torch.float16, 1)
     if y.shape[0] != N:
         raise ValueError("y has %d elements, N = %d" % (y.shape[0], N))
-    if group == W4A16_GROUP:
+    if perm is not None:
+        _perm(perm, K)
+        if group != W4A16_GROUP:
+            raise ValueError("act order takes group %d" % W4A16_GROUP)
+        st = lib.w4a16_gemv_perm(x.data_ptr(), perm.data_ptr(), packed.data_ptr(),
+                                 scales.data_ptr(), N, K, y.data_ptr(), _stream())
+    elif group == W4A16_GROUP:
         st = lib.w4a16_gemv(x.data_ptr(), packed.data_ptr(), scales.data_ptr(), N, K,
                             y.data_ptr(), _stream())
     else:
@@ -187,9 +214,10 @@ def gemv(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,
 
 
 def gemm(X: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, algo=None,
-         Y: torch.Tensor = None) -> torch.Tensor:
+         Y: torch.Tensor = None, perm: torch.Tensor = None) -> torch.Tensor:
     """X fp16 [M, K] -> Y fp16 [M, N].  algo: None/'auto', 'valu' or 'mfma'
-    ('mfma' needs group 128: the matrix-core kernels read one scale per 128)."""
+    ('mfma' needs group 128 and no perm).  perm: act-order column order
+    (int32 [K]), run on the VALU path."""
     lib = library()
     N, K, group = _weights(packed, scales)
     _need(X, "X", torch.float16, 2)
@@ -203,7 +231,13 @@ def gemm(X: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, algo=None,
     _need(Y, "Y", torch.float16, 2)
     if tuple(Y.shape) != (M, N):
         raise ValueError("Y shape %s, want %s" % (tuple(Y.shape), (M, N)))
-    if group == W4A16_GROUP:
+    if perm is not None:
+        _perm(perm, K)
+        if group != W4A16_GROUP or algo == "mfma":
+            raise ValueError("act order takes group %d and the VALU path" % W4A16_GROUP)
+        st = lib.w4a16_gemm_perm(X.data_ptr(), M, perm.data_ptr(), packed.data_ptr(),
+                                 scales.data_ptr(), N, K, Y.data_ptr(), _stream())
+    elif group == W4A16_GROUP:
         st = lib.w4a16_gemm_ex(X.data_ptr(), M, packed.data_ptr(), scales.data_ptr(), N, K,
                                Y.data_ptr(), _ALGOS[algo], _stream())
     else:
