@@ -79,8 +79,8 @@ def secondary(torch, w4a16, inputs, dev, stream):
     """Other rows of the path on their workload shapes: the quantizer (70B FFN
     matrix, larger than the Infinity Cache), batched decode M = 1..32 on the
     8B FFN shapes with both kernel families (locates the VALU/MFMA
-    crossover), 512-token prefill, and the decode GEMV and quantizer at group
-    sizes 32..256.  Each figure is the mean of graph replays over enough
+    crossover), 512-token prefill, the decode GEMV and quantizer at group
+    sizes 32..256, and the decode GEMV with an act-order activation gather.  Each figure is the mean of graph replays over enough
     weight copies to stream from HBM."""
     out = {}
 
@@ -175,6 +175,24 @@ def secondary(torch, w4a16, inputs, dev, stream):
         del copies
     out["group_sizes_%dx%d" % (K, N)] = groups
     del Wg
+
+    # act order: M = 1 GEMV with the activation gather, against the plain GEMV
+    act = {}
+    for (K, N) in [(4096, 14336), (14336, 4096)]:
+        p0, s0 = weights_for(K, N)
+        copies = [(p0, s0)] + [(p0.clone(), s0.clone()) for _ in range(11)]
+        x = torch.from_numpy(inputs.activation(1, K, seed=[9, K])).to(dev)[0]
+        y = torch.empty((N,), dtype=torch.float16, device=dev)
+        perm = torch.randperm(K, generator=torch.Generator().manual_seed(K)).to(
+            device=dev, dtype=torch.int32)
+        plain = timed(lambda: [w4a16.gemv(x, p, s_, y=y) for p, s_ in copies]) / len(copies)
+        gather = timed(lambda: [w4a16.gemv(x, p, s_, y=y, perm=perm) for p, s_ in copies]) \
+            / len(copies)
+        b = gemv_bytes(N, K) + 4 * K
+        act["%dx%d" % (K, N)] = {"plain_us": round(plain, 3), "perm_us": round(gather, 3),
+                                 "perm_GB/s": round(b / (gather * 1e-6) / 1e9, 1)}
+        del copies
+    out["act_order_m1"] = act
     quantized.clear()
     return out
 
