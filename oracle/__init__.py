@@ -53,8 +53,12 @@ class Oracle:
         lib.oracle_matmul.argtypes = [_p, _i64, _p, _p, _i64, _i64, _i64, _p, _p]
         lib.oracle_matmul_sampled.argtypes = [_p, _i64, _p, _p, _i64, _i64, _i64, _p, _p, _i64,
                                               _p, _p]
+        lib.oracle_quantize_asym.argtypes = [_p, _i64, _i64, _i64, _p, _p, _p]
+        lib.oracle_dequantize_asym.argtypes = [_p, _p, _p, _i64, _i64, _i64, _p]
+        lib.oracle_matmul_asym.argtypes = [_p, _i64, _p, _p, _p, _i64, _i64, _i64, _p, _p]
         for f in (lib.oracle_quantize, lib.oracle_dequantize, lib.oracle_matmul,
-                  lib.oracle_matmul_sampled):
+                  lib.oracle_matmul_sampled, lib.oracle_quantize_asym,
+                  lib.oracle_dequantize_asym, lib.oracle_matmul_asym):
             f.restype = ctypes.c_int
         lib.oracle_num_threads.restype = ctypes.c_int
         self.lib = lib
@@ -130,6 +134,54 @@ class Oracle:
                                             _ptr(Y), _ptr(Yabs))
         if rc != 0:
             raise ValueError("oracle_matmul_sampled: bad sizes or indices")
+        return Y, Yabs
+
+    # -- asymmetric INT4 ---------------------------------------------------
+    def quantize_asym(self, W: np.ndarray, group: int = 128):
+        """W: fp16 [N, K] -> (packed uint32 [N, K/8] with nibbles q in [0, 15],
+        scales uint16 bits [N, K/group], zero points int16 [N, K/group])."""
+        W = _bits16(W)
+        N, K = W.shape
+        packed = np.zeros((N, K // 8), dtype=np.uint32)
+        scales = np.zeros((N, K // group), dtype=np.uint16)
+        zeros = np.zeros((N, K // group), dtype=np.int16)
+        rc = self.lib.oracle_quantize_asym(_ptr(W), N, K, group, _ptr(packed), _ptr(scales),
+                                           _ptr(zeros))
+        if rc != 0:
+            raise ValueError("oracle_quantize_asym: bad sizes N=%d K=%d group=%d" % (N, K, group))
+        return packed, scales, zeros
+
+    def dequantize_asym(self, packed, scales, zeros, group: int = 128) -> np.ndarray:
+        """Exact Ŵ = s*(q - z) as float64 [N, K]."""
+        packed = np.ascontiguousarray(packed, dtype=np.uint32)
+        scales = _bits16(scales)
+        zeros = np.ascontiguousarray(zeros, dtype=np.int16)
+        N, K = packed.shape[0], packed.shape[1] * 8
+        out = np.empty((N, K), dtype=np.float64)
+        rc = self.lib.oracle_dequantize_asym(_ptr(packed), _ptr(scales), _ptr(zeros), N, K,
+                                             group, _ptr(out))
+        if rc != 0:
+            raise ValueError("oracle_dequantize_asym: bad sizes")
+        return out
+
+    def matmul_asym(self, X, packed, scales, zeros, group: int = 128):
+        """(Y, Yabs) of X·Ŵᵀ with the asymmetric Ŵ = s*(q - z)."""
+        X = _bits16(X)
+        if X.ndim == 1:
+            X = X.reshape(1, -1)
+        packed = np.ascontiguousarray(packed, dtype=np.uint32)
+        scales = _bits16(scales)
+        zeros = np.ascontiguousarray(zeros, dtype=np.int16)
+        M, K = X.shape
+        N = packed.shape[0]
+        if packed.shape[1] * 8 != K:
+            raise ValueError("K mismatch")
+        Y = np.empty((M, N), dtype=np.float64)
+        Yabs = np.empty((M, N), dtype=np.float64)
+        rc = self.lib.oracle_matmul_asym(_ptr(X), M, _ptr(packed), _ptr(scales), _ptr(zeros),
+                                         N, K, group, _ptr(Y), _ptr(Yabs))
+        if rc != 0:
+            raise ValueError("oracle_matmul_asym: bad sizes")
         return Y, Yabs
 
     def num_threads(self) -> int:

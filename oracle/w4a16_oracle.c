@@ -28,7 +28,10 @@
  *   - the scale is stored as fp16, and q is computed against that stored
  *     scale, with the exact quotient w/s;
  *   - a group whose fp16 scale is 0 stores scale 0 and q = 0 everywhere;
- *   - eight nibbles per little-endian uint32, element 8j+i in bits 4i..4i+3.
+ *   - eight nibbles per little-endian uint32, element 8j+i in bits 4i..4i+3;
+ *   - asymmetric INT4 (see oracle_quantize_asym): the same rounding, the
+ *     scale stored as fp16 and z taken against it, z stored as int16, and
+ *     a zero-scale group stored as s = 0, z = 0, q = 0.
  *
  * Build: cc -O2 -fno-fast-math -ffp-contract=off -fopenmp -shared -fPIC.
  */
@@ -201,6 +204,119 @@ int oracle_matmul_sampled(const uint16_t* X, int64_t M, const uint32_t* packed,
     for (int64_t i = 0; i < count; i++)
         dot_row(X + rows[i] * K, packed + cols[i] * (K / 8), scales + cols[i] * ng, K, group,
                 &Y[i], &Yabs[i]);
+    return 0;
+}
+
+/* ------------------------------------------------ asymmetric INT4 */
+
+/* Per-group asymmetric INT4 quantization ([QUANT] sub-section 2, the
+ * asymmetric equations: s = (max - min) / (2^b - 1), z = -round(min / s),
+ * x_q = clamp(round(x / s) + z, 0, 2^b - 1), INT4 range [0, 15]):
+ *   s is stored as fp16 (RNE of the exact (max - min) / 15; max - min is
+ *   exact in binary64, fp16 values being multiples of 2^-24 below 2^16),
+ *   z = -round_half_even(min / s) against the stored s (an integer; it lies
+ *   in [0, 15] when the group holds both signs and can be far outside for a
+ *   one-signed group with a narrow range, |z| <= 15 * 2^11 * (1 + 2^-11)),
+ *   q = clamp(round_half_even(w / s) + z, 0, 15);
+ *   a group whose fp16 scale is 0 stores s = 0, z = 0 and q = 0.
+ * Dequantized: s * (q - z). */
+static void quantize_group_asym(const uint16_t* w, int64_t g, uint16_t* scale_bits,
+                                int16_t* zero, uint8_t* q)
+{
+    double mx = -INFINITY, mn = INFINITY;
+    for (int64_t i = 0; i < g; i++) {
+        double v = oracle_f64_from_f16(w[i]);
+        if (v > mx) mx = v;
+        if (v < mn) mn = v;
+    }
+    uint16_t s16 = oracle_f16_from_f64((mx - mn) / 15.0); /* 2^4 - 1 = 15 */
+    double s = oracle_f64_from_f16(s16);
+    *scale_bits = s16;
+    if (s == 0.0) {
+        *zero = 0;
+        for (int64_t i = 0; i < g; i++) q[i] = 0;
+        return;
+    }
+    double z = -nearbyint(mn / s);                        /* RNE in FE_TONEAREST */
+    *zero = (int16_t)z;
+    for (int64_t i = 0; i < g; i++) {
+        double r = nearbyint(oracle_f64_from_f16(w[i]) / s) + z;
+        if (r < 0.0) r = 0.0;
+        if (r > 15.0) r = 15.0;
+        q[i] = (uint8_t)r;
+    }
+}
+
+/* W fp16 [N,K] -> packed uint32 [N, K/8] (nibble = q in [0, 15], element
+ * 8j+i in bits 4i..4i+3 of word j), scales fp16 [N, K/group], zero points
+ * int16 [N, K/group]. */
+int oracle_quantize_asym(const uint16_t* W, int64_t N, int64_t K, int64_t group,
+                         uint32_t* packed, uint16_t* scales, int16_t* zeros)
+{
+    if (N < 0 || K < 0 || group <= 0 || group % 8 != 0 || K % group != 0) return -1;
+    if (fegetround() != FE_TONEAREST) return -1;
+    int64_t ng = K / group;
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; n++) {
+        uint8_t* q = (uint8_t*)malloc((size_t)group);
+        for (int64_t gi = 0; gi < ng; gi++) {
+            quantize_group_asym(W + n * K + gi * group, group, &scales[n * ng + gi],
+                                &zeros[n * ng + gi], q);
+            for (int64_t j = 0; j < group / 8; j++) {
+                uint32_t word = 0;
+                for (int i = 0; i < 8; i++) word |= ((uint32_t)q[8 * j + i] & 0xFu) << (4 * i);
+                packed[n * (K / 8) + (gi * group) / 8 + j] = word;
+            }
+        }
+        free(q);
+    }
+    return 0;
+}
+
+/* Nibble of element k of a row (0..15). */
+static int nibble_at(const uint32_t* row_words, int64_t k)
+{
+    return (int)((row_words[k / 8] >> (4 * (k % 8))) & 0xFu);
+}
+
+/* Ŵ[n,k] = s[n, k/group] * (q[n,k] - z[n, k/group]), exact in binary64
+ * (an 11-bit significand times an integer below 2^16). */
+int oracle_dequantize_asym(const uint32_t* packed, const uint16_t* scales, const int16_t* zeros,
+                           int64_t N, int64_t K, int64_t group, double* What)
+{
+    if (N < 0 || K < 0 || group <= 0 || group % 8 != 0 || K % group != 0) return -1;
+    int64_t ng = K / group;
+    for (int64_t n = 0; n < N; n++)
+        for (int64_t k = 0; k < K; k++)
+            What[n * K + k] = oracle_f64_from_f16(scales[n * ng + k / group]) *
+                              (double)(nibble_at(packed + n * (K / 8), k) -
+                                       zeros[n * ng + k / group]);
+    return 0;
+}
+
+/* Y = X·Ŵᵀ and Yabs = sum |X Ŵ| with the asymmetric Ŵ, binary64 (each
+ * product exact: 11-bit x 11-bit x 16-bit significands fit 53 bits). */
+int oracle_matmul_asym(const uint16_t* X, int64_t M, const uint32_t* packed,
+                       const uint16_t* scales, const int16_t* zeros, int64_t N, int64_t K,
+                       int64_t group, double* Y, double* Yabs)
+{
+    if (M < 0 || N < 0 || K < 0 || group <= 0 || group % 8 != 0 || K % group != 0) return -1;
+    int64_t ng = K / group;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t m = 0; m < M; m++)
+        for (int64_t n = 0; n < N; n++) {
+            double sum = 0.0, sum_abs = 0.0;
+            for (int64_t k = 0; k < K; k++) {
+                double what = oracle_f64_from_f16(scales[n * ng + k / group]) *
+                              (double)(nibble_at(packed + n * (K / 8), k) -
+                                       zeros[n * ng + k / group]);
+                double prod = oracle_f64_from_f16(X[m * K + k]) * what;
+                sum += prod;
+                sum_abs += fabs(prod);
+            }
+            Y[m * N + n] = sum;
+            Yabs[m * N + n] = sum_abs;
+        }
     return 0;
 }
 

@@ -19,6 +19,10 @@ What each pin compares against:
                           s/4, mean e^2 = s^2/12 ([QUANT] sub-section 2)
   * matmul                exact rational dot products (fractions) within the
                           binary64 summation bound; one-hot activations
+  * asymmetric INT4       exact RNE((max - min)/15) and z = -RNE(min/s),
+                          brute-force nearest level s (q - z), error bound,
+                          z in [0, 15] for two-signed groups, a hand-worked
+                          group ([QUANT] sub-section 2)
 """
 from __future__ import annotations
 
@@ -398,8 +402,126 @@ def pin_act_order(o) -> list:
     return fails
 
 
+def _asym_cases():
+    """Groups of 128 for the asymmetric pins: skewed rows, then hand-set
+    groups (two-signed, one-signed positive and negative with narrow ranges,
+    constant, all-zero, a tiny range that rounds the fp16 scale to 0, the
+    fp16 extremes)."""
+    N, K = 12, 512
+    W = inputs.weight_skewed(N, K, seed=[95, 0, 0])
+    r = np.arange(128, dtype=np.float64)
+    W[0, 0:128] = (10.0 + r / 254.0).astype(np.float16)          # one-signed, narrow
+    W[0, 128:256] = (-3.0 - r / 127.0).astype(np.float16)        # one-signed negative
+    W[1, 0:128] = np.float16(0.75)                                # constant: range 0
+    W[1, 128:256] = np.float16(0)                                 # all zero
+    W[1, 256:384] = np.float16(1.0)
+    W[1, 256] = np.float16(1.0009765625)                          # range 2^-10: s = RNE(2^-10/15)
+    W[2, 0:128] = np.float16(2.0 ** -24)
+    W[2, 0] = np.float16(0)                                       # range 2^-24: s16 = 0
+    W[2, 128:256] = np.float16(0)
+    W[2, 128] = np.float16(65504.0)
+    W[2, 129] = np.float16(-65504.0)                              # widest range
+    return W
+
+
+def _rne_int(f: Fraction) -> int:
+    """Round half to even of an exact fraction (Python's round on Fraction)."""
+    return round(f)
+
+
+def pin_asymmetric(o) -> list:
+    """Asymmetric INT4 ([QUANT] sub-section 2, asymmetric equations:
+    s = (max - min) / 15, z = -round(min / s), q = clamp(round(w / s) + z,
+    0, 15), codes in [0, 15]; dequantized s (q - z)).  Pinned by: the scale is
+    the exact RNE of (max - min) / 15 found by nearest-value search; z is the
+    exact rational RNE of -min / s; every code is the brute-force nearest
+    level s (q - z), q in [0, 15], ties to the even multiple of s; the
+    rounding error is at most s / 2 plus what the clamp cuts off above;
+    z lies in [0, 15] for two-signed groups; a hand-worked group; the tiny
+    product equals the exact rational sum."""
+    fails = []
+    W = _asym_cases()
+    N, K = W.shape
+    packed, scales, zeros = o.quantize_asym(W)
+    if scales.shape != (N, K // 128) or zeros.shape != (N, K // 128):
+        return ["asym: shapes %s %s" % (scales.shape, zeros.shape)]
+    # nibbles, unpacked independently of the oracle (8 per word, low first)
+    nib = np.zeros((N, K), dtype=np.int64)
+    for i in range(8):
+        nib[:, i::8] = (packed.astype(np.int64) >> (4 * i)) & 0xF
+    deq = o.dequantize_asym(packed, scales, zeros)
+    for n in range(N):
+        for g in range(K // 128):
+            w = [Fraction(float(v)) for v in W[n, 128 * g:128 * (g + 1)]]
+            mx, mn = max(w), min(w)
+            s_bits = exact_rne_f16((mx - mn) / 15)
+            if scales[n, g] != s_bits:
+                fails.append("asym (%d,%d): scale %#06x, want %#06x"
+                             % (n, g, scales[n, g], s_bits))
+                continue
+            s = Fraction(float(np.uint16(s_bits).view(np.float16)))
+            z = 0 if s == 0 else -_rne_int(mn / s)
+            if zeros[n, g] != z:
+                fails.append("asym (%d,%d): zero %d, want %d" % (n, g, zeros[n, g], z))
+                continue
+            if s != 0 and mn < 0 < mx and not 0 <= z <= 15:
+                fails.append("asym (%d,%d): two-signed group with z = %d" % (n, g, z))
+            for i, wv in enumerate(w):
+                q = int(nib[n, 128 * g + i])
+                if s == 0:
+                    want = 0
+                else:
+                    # nearest level s (c - z) over the 16 codes, ties to even (c - z)
+                    want = min(range(16), key=lambda c: (abs(wv - s * (c - z)), (c - z) % 2))
+                if q != want:
+                    fails.append("asym (%d,%d,%d): code %d, want %d" % (n, g, i, q, want))
+                    break
+                what = s * (q - z)
+                if Fraction(float(deq[n, 128 * g + i])) != what:
+                    fails.append("asym (%d,%d,%d): dequantized %r, want s (q - z)"
+                                 % (n, g, i, deq[n, 128 * g + i]))
+                    break
+                if s != 0:
+                    cut = max(Fraction(0), wv - s * (15 - z))   # above the top level
+                    if abs(wv - what) > s / 2 + cut:
+                        fails.append("asym (%d,%d,%d): error above s/2" % (n, g, i))
+                        break
+    # hand-worked group: 128 values -1.5, 6.0 and 0.5-steps; range 7.5 so
+    # s = 0.5 exactly, z = -round(-3) = 3; 2.25 -> round(4.5) = 4 (even) -> 7
+    # -> 2.0; 2.75 -> round(5.5) = 6 -> 9 -> 3.0; -1.5 -> 0; 6.0 -> 15
+    hw = np.full((1, 128), 0.0, dtype=np.float16)
+    hw[0, :4] = [-1.5, 6.0, 2.25, 2.75]
+    ph, sh, zh = o.quantize_asym(hw)
+    qh = [(int(ph[0, 0]) >> (4 * i)) & 0xF for i in range(4)]
+    if int(sh[0, 0]) != 0x3800 or int(zh[0, 0]) != 3 or qh != [0, 15, 7, 9]:
+        fails.append("asym hand-worked: s %#06x z %d codes %s (want 0x3800, 3, [0,15,7,9])"
+                     % (sh[0, 0], zh[0, 0], qh))
+    q0 = (int(ph[0, 1]) >> 0) & 0xF                                  # 0.0 -> 0 + 3
+    if q0 != 3:
+        fails.append("asym hand-worked: 0.0 gives code %d, want 3" % q0)
+    # a tiny product against the exact rational sum
+    M, n_, k_ = 2, 3, 256
+    Wt = inputs.weight_skewed(n_, k_, seed=[95, 1, 0])
+    Xt = inputs.activation(M, k_, seed=[1000, 95, 1, 0])
+    pt, st, zt = o.quantize_asym(Wt)
+    Y, Yabs = o.matmul_asym(Xt, pt, st, zt)
+    dt = o.dequantize_asym(pt, st, zt)
+    for m in range(M):
+        for n in range(n_):
+            terms = [Fraction(float(Xt[m, k])) * Fraction(float(dt[n, k])) for k in range(k_)]
+            exact = sum(terms, Fraction(0))
+            absum = sum((abs(t) for t in terms), Fraction(0))
+            bound = k_ * 2.0 ** -53 * float(absum)
+            if abs(Fraction(Y[m, n]) - exact) > Fraction(bound):
+                fails.append("asym: matmul (%d,%d) off the exact sum" % (m, n))
+            if abs(Fraction(Yabs[m, n]) - absum) > Fraction(bound):
+                fails.append("asym: matmul |.| sum (%d,%d) off" % (m, n))
+    return fails
+
+
 ALL_PINS = [pin_f16_codec, pin_scale_every_fp16, pin_hand_worked, pin_codes_nearest,
-            pin_invariants, pin_matmul_exact, pin_group_sizes, pin_act_order]
+            pin_invariants, pin_matmul_exact, pin_group_sizes, pin_act_order,
+            pin_asymmetric]
 
 
 def run_all(o) -> dict:

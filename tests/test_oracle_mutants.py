@@ -36,6 +36,27 @@ MUTANTS = [
     ("matmul wrong sign", "acc += t;", "acc -= t;"),
     ("activation index transposed", "dot_row(X + m * K, packed + n * (K / 8)",
      "dot_row(X + (M - 1 - m) * K, packed + n * (K / 8)"),
+    ("asym: zero point sign flipped", "double z = -nearbyint(mn / s);",
+     "double z = nearbyint(mn / s);"),
+    ("asym: zero point by floor", "double z = -nearbyint(mn / s);",
+     "double z = -floor(mn / s);"),
+    ("asym: range over 16 levels", "oracle_f16_from_f64((mx - mn) / 15.0)",
+     "oracle_f16_from_f64((mx - mn) / 16.0)"),
+    ("asym: range from absmax", "oracle_f16_from_f64((mx - mn) / 15.0)",
+     "oracle_f16_from_f64((mx > -mn ? mx : -mn) / 15.0)"),
+    ("asym: zero added before rounding", "double r = nearbyint(oracle_f64_from_f16(w[i]) / s) + z;",
+     "double r = nearbyint(oracle_f64_from_f16(w[i]) / s + z + 0.5);"),
+    ("asym: clamp at 14", "if (r > 15.0) r = 15.0;", "if (r > 14.0) r = 14.0;"),
+    ("asym: offset-binary nibble", "word |= ((uint32_t)q[8 * j + i] & 0xFu) << (4 * i);",
+     "word |= ((uint32_t)(q[8 * j + i] + 8) & 0xFu) << (4 * i);"),
+    ("asym: dequantize ignores z",
+     "What[n * K + k] = oracle_f64_from_f16(scales[n * ng + k / group]) *\n"
+     "                              (double)(nibble_at(packed + n * (K / 8), k) -\n"
+     "                                       zeros[n * ng + k / group]);",
+     "What[n * K + k] = oracle_f64_from_f16(scales[n * ng + k / group]) *\n"
+     "                              (double)(nibble_at(packed + n * (K / 8), k));"),
+    ("asym: matmul zero of the next group", "zeros[n * ng + k / group]);\n                double prod",
+     "zeros[n * ng + (k / group + 1) % ng]);\n                double prod"),
 ]
 
 

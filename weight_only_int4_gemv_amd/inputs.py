@@ -75,6 +75,17 @@ def weight(n: int, k: int, seed) -> np.ndarray:
     return out
 
 
+def weight_skewed(n: int, k: int, seed) -> np.ndarray:
+    """W fp16 [n, k] with a mean far from zero, for asymmetric INT4: the
+    fp16 values of ``weight(n, k, seed)`` plus a per-row offset, uniform on
+    [-0.05, 0.05] (generator seeded with (seed..., 2**20)), summed in
+    float32 and rounded to fp16.  With sigma 0.02 most 128-element groups
+    stay two-signed and some rows are nearly one-signed."""
+    rng = np.random.default_rng(_seed_list(seed) + [2 ** 20])
+    off = rng.uniform(-0.05, 0.05, size=(n, 1)).astype(np.float32)
+    return (weight(n, k, seed).astype(np.float32) + off).astype(np.float16)
+
+
 def activation(m: int, k: int, seed) -> np.ndarray:
     """X fp16 [m, k] ~ N(0, 1)."""
     rng = np.random.default_rng(_seed_list(seed))
