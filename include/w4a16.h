@@ -159,6 +159,40 @@ int w4a16_gemv_perm(const uint16_t* x, const int32_t* perm, const uint32_t* pack
 int w4a16_gemm_perm(const uint16_t* X, int64_t M, const int32_t* perm, const uint32_t* packed,
                     const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y, void* stream);
 
+/* ---- Asymmetric INT4 ([QUANT] sub-section 2, asymmetric equations: scale
+ * (max - min) / 15, zero point z = -round(min / s), codes clamp(round(w / s)
+ * + z, 0, 15), INT4 range [0, 15]; the same section's guidance puts skewed
+ * weight distributions, e.g. the FFN down projection, on this form).
+ * Per group of `group` elements along K (32, 64, 128 or 256):
+ *     s    = fp16 RNE of (max - min) / 15 (exact max - min)
+ *     z    = -RNE(min / s), an integer, against the stored fp16 s
+ *     q    = clamp(RNE(w / s) + z, 0, 15), stored as the nibble itself
+ *            (no offset), element 8j+i in bits 4i..4i+3 of word j
+ *     ŵ    = s * (q - z)
+ *   a group whose scale rounds to 0 (range below 2^-24 * 7.5) stores s = 0,
+ *   z = 0 and q = 0.  z lies in [0, 15] when the group holds both signs;
+ *   a one-signed group with a narrow range can have |z| up to 32752.
+ *   zeros: int16 [N, K/group], laid out like the scales (N*(K/group)*2
+ *   bytes = w4a16_scales_bytes_g), 2-byte aligned.
+ *   perm: NULL (columns in W's order) or the act-order column order as for
+ *   the *_perm functions (device int32 [K], 16-byte aligned).
+ *   w4a16_quantize_asym: W fp16 [N, K] -> packed, scales, zeros (outputs must
+ *                        not overlap each other, W or perm)
+ *   w4a16_gemv_asym:     y[n] = sum_j x[perm[j]] * ŵ[n,j]      (x[j] without perm)
+ *   w4a16_gemm_asym:     Y[m,n] = sum_j X[m, perm[j]] * ŵ[n,j]  (VALU path for
+ *                        every M)
+ * Errors as for w4a16_gemm_g; a NULL zeros with K > 0 is
+ * W4A16_ERR_INVALID_ARG; Y must not overlap zeros. */
+int w4a16_quantize_asym(const uint16_t* W, const int32_t* perm, int64_t N, int64_t K,
+                        int64_t group, uint32_t* packed, uint16_t* scales, int16_t* zeros,
+                        void* stream);
+int w4a16_gemv_asym(const uint16_t* x, const int32_t* perm, const uint32_t* packed,
+                    const uint16_t* scales, const int16_t* zeros, int64_t N, int64_t K,
+                    int64_t group, uint16_t* y, void* stream);
+int w4a16_gemm_asym(const uint16_t* X, int64_t M, const int32_t* perm, const uint32_t* packed,
+                    const uint16_t* scales, const int16_t* zeros, int64_t N, int64_t K,
+                    int64_t group, uint16_t* Y, void* stream);
+
 /* ---- Dependent decode sequence ([BENCH] §二: every decode step streams
  * the layers' matrices one after another, each fed by the one before).
  * Runs stages[0..count) as if w4a16_gemv were called on each in order on

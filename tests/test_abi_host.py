@@ -35,7 +35,8 @@ def test_header_declares_the_boundary():
                "w4a16_packed_bytes", "w4a16_scales_bytes", "w4a16_status_string",
                "w4a16_valu_max_m", "w4a16_quantize_g", "w4a16_gemv_g", "w4a16_gemm_g",
                "w4a16_scales_bytes_g", "w4a16_quantize_perm", "w4a16_gemv_perm",
-               "w4a16_gemm_perm"]:
+               "w4a16_gemm_perm", "w4a16_quantize_asym", "w4a16_gemv_asym",
+               "w4a16_gemm_asym"]:
         assert fn in names
 
 
@@ -181,6 +182,42 @@ def test_act_order_validation(lib):
                    perm=torch.zeros(128, dtype=torch.int64))
 
 
+def test_asymmetric_validation(lib):
+    """Asymmetric entry points: zeros required for K > 0 and 2-byte aligned,
+    perm optional, no output overlapping another output or an input, group
+    checked as for the group-size entry points, no matrix-core path."""
+    A, B, C, D, P, Z = FAKE, FAKE * 4, FAKE * 8, FAKE * 12, FAKE * 16, FAKE * 20
+    q, gv, gm = lib.w4a16_quantize_asym, lib.w4a16_gemv_asym, lib.w4a16_gemm_asym
+    assert q(A, None, 4, 128, 128, B, C, None, None) == INVALID        # no zeros
+    assert q(A, None, 4, 128, 128, B, C, Z + 1, None) == MISALIGNED
+    assert q(A, None, 4, 128, 128, B, C, C + 4, None) == INVALID       # zeros overlap scales
+    assert q(A, None, 4, 128, 128, B, C, B + 8, None) == INVALID       # zeros overlap packed
+    assert q(A, None, 4, 128, 128, B, C, A + 16, None) == INVALID      # zeros overlap W
+    assert q(A, P, 4, 128, 128, B, C, P + 16, None) == INVALID         # zeros overlap perm
+    assert q(A, P + 4, 4, 128, 128, B, C, Z, None) == MISALIGNED
+    assert q(A, None, 4, 128, 48, B, C, Z, None) == INVALID            # group
+    assert q(A, None, 4, 192, 128, B, C, Z, None) == SHAPE
+    assert q(A, None, 4, 384, 256, B, C, Z, None) == SHAPE
+    assert q(None, None, 0, 128, 128, None, None, None, None) == OK
+    assert gv(A, None, B, C, None, 16, 128, 128, D, None) == INVALID   # no zeros
+    assert gv(A, None, B, C, Z + 1, 16, 128, 128, D, None) == MISALIGNED
+    assert gv(A, None, B, C, Z, 16, 128, 128, Z + 2, None) == INVALID  # y overlaps zeros
+    assert gv(A, P, B, C, Z, 16, 128, 128, P + 2, None) == INVALID     # y overlaps perm
+    assert gv(A, None, B, C, Z, 16, 128, 64 + 1, D, None) == INVALID
+    assert gm(A, 2, None, B, C, None, 16, 128, 128, D, None) == INVALID
+    assert gm(A, 2, None, B, C, Z, 16, 130, 128, D, None) == SHAPE
+    assert gm(A, -1, None, B, C, Z, 16, 128, 128, D, None) == INVALID
+    assert gm(None, 0, None, None, None, None, 16, 128, 128, None, None) == OK
+    import torch
+    with pytest.raises(ValueError):
+        w4a16.quantize_asym(torch.zeros(4, 128, dtype=torch.float16), group=48)
+    with pytest.raises(ValueError):
+        w4a16.gemv_asym(torch.zeros(128, dtype=torch.float16),
+                        torch.zeros(4, 16, dtype=torch.int32),
+                        torch.zeros(4, 1, dtype=torch.float16),
+                        torch.zeros(4, 1, dtype=torch.int32))       # zeros must be int16
+
+
 @pytest.mark.skipif(__import__("torch").cuda.device_count() > 0,
                     reason="with a GPU present valid arguments would launch")
 def test_valid_arguments_without_device_report_device_error(lib):
@@ -190,6 +227,8 @@ def test_valid_arguments_without_device_report_device_error(lib):
     assert lib.w4a16_quantize_g(A, 4, 256, 64, B, C, None) == DEVICE
     assert lib.w4a16_gemm_g(A, 2, B, C, 16, 256, 256, D, None) == DEVICE
     assert lib.w4a16_gemv_perm(A, FAKE * 16, B, C, 16, 128, D, None) == DEVICE
+    assert lib.w4a16_quantize_asym(A, None, 4, 128, 128, B, C, FAKE * 20, None) == DEVICE
+    assert lib.w4a16_gemm_asym(A, 2, None, B, C, FAKE * 20, 16, 128, 64, D, None) == DEVICE
 
 
 def test_binding_rejects_bad_tensors():

@@ -580,3 +580,168 @@ def test_act_order_out_of_range_index_reads_zero(w4, orc):
     torch.cuda.synchronize()
     Yref, Yabs = orc.matmul(Xz, po, so)
     assert (np.abs(y.astype(np.float64) - Yref) <= oracle.tolerance(Yref, Yabs)).all()
+
+
+# ------------------------------------------------------------ asymmetric INT4
+
+def asym_weight(N, K, seed, plant=True, extremes=False):
+    """Skewed layer-like weights; with plant, the first rows get groups that
+    exercise every branch of the asymmetric path: one-signed groups whose
+    zero point lies beyond +-1000 (about -2700 and +1550), a one-signed group
+    near z = -300, a constant group (range 0), an all-zero group, a range that
+    rounds the fp16 scale to 0, exact ties, and with extremes the fp16
+    extremes (quantizer tests only: outputs of such a row overflow fp16)."""
+    W = inputs.weight_skewed(N, K, seed=seed)
+    if not plant:
+        return W
+    r = np.arange(K, dtype=np.float64)
+    if N > 0:
+        W[0] = (20.0 + (r % 8) / 64.0).astype(np.float16)                   # z ~ -2700
+    if N > 1:
+        W[1] = (-12.0 - (r % 16) / 128.0).astype(np.float16)                # z = 1551
+    if N > 2:
+        W[2] = (10.0 + (r % 128) / 254.0).astype(np.float16)                # z ~ -300
+    if N > 3:
+        W[3, :] = np.float16(0.75)                                           # constant
+        W[3, 64:] = np.float16(0)                                            # all zero
+    if N > 4:
+        W[4, :] = np.float16(2.0 ** -24)
+        W[4, ::64] = np.float16(0)                                           # s16 = 0
+    if N > 5 and extremes:
+        W[5, :] = np.float16(0)
+        W[5, 0], W[5, 1] = np.float16(65504.0), np.float16(-65504.0)         # widest range
+    if N > 6:
+        # range 7.5 -> s = 0.5, z = 3: 2.25 and 2.75 are exact ties of w / s
+        W[6, :] = np.float16(2.25)
+        W[6, 0::32], W[6, 1::32], W[6, 2::32] = np.float16(-1.5), np.float16(6.0), np.float16(2.75)
+    return W
+
+
+def check_quantize_asym(w4, orc, W, group, perm=None, name=""):
+    N, K = W.shape
+    say("quantize asym %s group=%d N=%d K=%d perm=%s" % (name, group, N, K, perm is not None))
+    pg, sg, zg = w4.quantize_asym(dev(W), group=group,
+                                  perm=None if perm is None else dev(perm))
+    torch.cuda.synchronize()
+    Wo = W if perm is None else np.ascontiguousarray(W[:, perm])
+    po, so, zo = orc.quantize_asym(Wo, group=group)
+    got_s = sg.cpu().numpy().view(np.uint16)
+    got_z = zg.cpu().numpy()
+    got_p = pg.cpu().numpy().view(np.uint32)
+    bad = np.argwhere(got_s != so)
+    assert bad.size == 0, "%d scales differ, first at %s" % (len(bad), bad[0])
+    bad = np.argwhere(got_z != zo)
+    assert bad.size == 0, "%d zeros differ, first at %s: %d vs %d" % (
+        len(bad), bad[0], got_z[tuple(bad[0])], zo[tuple(bad[0])])
+    bad = np.argwhere(got_p != po)
+    assert bad.size == 0, "%d words differ, first at %s (%#x vs %#x)" % (
+        len(bad), bad[0], got_p[tuple(bad[0])], po[tuple(bad[0])])
+    return po, so, zo
+
+
+@pytest.mark.parametrize("group", [32, 64, 128, 256])
+@pytest.mark.parametrize("N,K", [(7, 256), (37, 768), (129, 1536), (4096, 4096), (300, 14336)])
+def test_quantize_asym_bit_exact(w4, orc, group, N, K):
+    """w4a16_quantize_asym against the oracle: codes, scales and zero points
+    bit-exact, planted edge groups included."""
+    check_quantize_asym(w4, orc, asym_weight(N, K, [41, group, N, K], extremes=True), group)
+
+
+def test_quantize_asym_every_range(w4, orc):
+    """One group per positive finite fp16 value v with min 0 and max v (and
+    one with min -v and max 0): the scale RNE(v / 15) at every binade,
+    subnormal and zero scales included, and z at both ends."""
+    v = np.arange(1, 0x7C00, dtype=np.uint16).view(np.float16)
+    G = len(v)
+    W = np.zeros((2 * G, 128), dtype=np.float16)
+    W[:G, 5] = v
+    W[G:, 9] = -v
+    W[:G, 17] = (v.astype(np.float64) * 0.37).astype(np.float16)
+    W[G:, 17] = (-v.astype(np.float64) * 0.61).astype(np.float16)
+    check_quantize_asym(w4, orc, W, 128, name="every range")
+
+
+@pytest.mark.parametrize("kind", ["reverse", "random"])
+@pytest.mark.parametrize("group", [64, 128])
+def test_quantize_asym_act_order(w4, orc, kind, group):
+    W = asym_weight(129, 4096, [42, group], extremes=True)
+    check_quantize_asym(w4, orc, W, group, perm=perm_of(kind, 4096, [42, group]), name=kind)
+
+
+def check_linear_asym(w4, orc, M, N, K, group, seed, perm_kind=None, plant=True):
+    say("linear asym group=%d M=%d N=%d K=%d perm=%s" % (group, M, N, K, perm_kind))
+    W = asym_weight(N, K, seed, plant=plant)
+    perm = None if perm_kind is None else perm_of(perm_kind, K, seed)
+    Wo = W if perm is None else np.ascontiguousarray(W[:, perm])
+    packed, scales, zeros = orc.quantize_asym(Wo, group=group)
+    X = inputs.activation(M, K, seed=[1000] + list(seed))
+    pd, sd, zd = packed_to_dev(packed), scales_to_dev(scales), dev(zeros)
+    permd = None if perm is None else dev(perm)
+    if M == 1:
+        Y = w4.gemv_asym(dev(X)[0], pd, sd, zd, perm=permd).cpu().numpy()[None]
+    else:
+        Y = w4.gemm_asym(dev(X), pd, sd, zd, perm=permd).cpu().numpy()
+    torch.cuda.synchronize()
+    assert Y.shape == (M, N)
+    Xo = X if perm is None else np.ascontiguousarray(X[:, perm])
+    Yref, Yabs = orc.matmul_asym(Xo, packed, scales, zeros, group=group)
+    tol = oracle.tolerance(Yref, Yabs)
+    err = np.abs(Y.astype(np.float64) - Yref)
+    bad = np.argwhere(~(err <= tol))
+    assert bad.size == 0, "%d outputs out of tolerance, first %s: got %r want %r tol %r" % (
+        len(bad), bad[0], Y[tuple(bad[0])], Yref[tuple(bad[0])], tol[tuple(bad[0])])
+
+
+@pytest.mark.parametrize("group", [32, 128, 256])
+@pytest.mark.parametrize("M", [1, 2, 3, 8, 13])
+@pytest.mark.parametrize("N,K", [(300, 1536), (1001, 4096), (64, 14336)])
+def test_linear_asym(w4, orc, group, M, N, K):
+    """Asymmetric GEMV / VALU GEMM for every M family (persistent kernel with
+    whole-x staging; K slices for M = 8, 13 at K = 14336), planted groups with
+    |z| > 1000 (the chunk-sum correction) included."""
+    check_linear_asym(w4, orc, M, N, K, group, [43, group, M, N, K])
+
+
+@pytest.mark.parametrize("name,K,N", [("llama down", 14336, 4096), ("llama gate", 4096, 14336),
+                                      ("qwen down", 18944, 3584)])
+def test_linear_asym_layer_shapes(w4, orc, name, K, N):
+    """M = 1 on full decode layer shapes, group 128 (the down projection is
+    the skewed layer asymmetric INT4 is meant for)."""
+    check_linear_asym(w4, orc, 1, N, K, 128, [44, N, K], plant=False)
+
+
+@pytest.mark.parametrize("M", [1, 4])
+def test_linear_asym_act_order(w4, orc, M):
+    check_linear_asym(w4, orc, M, 515, 4096, 128, [45, M], perm_kind="random")
+
+
+def test_asym_one_hot_exact(w4, orc):
+    """One-hot activations select fp16(s * (q - z)) bit-exactly where
+    |q - z| < 2^13 (the fp32 product s * (q - z) is then exact)."""
+    N, K = 24, 1024
+    W = asym_weight(N, K, [46], plant=False)
+    packed, scales, zeros = orc.quantize_asym(W, group=64)
+    ks = np.arange(0, K, 5)
+    X = np.zeros((len(ks), K), dtype=np.float16)
+    X[np.arange(len(ks)), ks] = np.float16(1.0)
+    assert np.abs(zeros.astype(np.int64)).max() < 2 ** 12
+    say("asym one-hot")
+    pd, sd, zd = packed_to_dev(packed), scales_to_dev(scales), dev(zeros)
+    deq = orc.dequantize_asym(packed, scales, zeros, group=64)
+    for m0 in range(0, len(ks), 8):
+        Y = w4.gemm_asym(dev(X[m0:m0 + 8]), pd, sd, zd).cpu().numpy()
+        torch.cuda.synchronize()
+        want = deq[:, ks[m0:m0 + 8]].T.astype(np.float16)
+        assert (Y.view(np.uint16) == want.view(np.uint16)).all()
+
+
+def test_asym_empty_and_k_zero(w4):
+    say("asym empty / K = 0")
+    p, s, z = w4.quantize_asym(torch.empty((0, 256), dtype=torch.float16, device="cuda"))
+    assert p.shape == (0, 32) and s.shape == (0, 2) and z.shape == (0, 2)
+    Y = w4.gemm_asym(torch.empty((3, 0), dtype=torch.float16, device="cuda"),
+                     torch.empty((5, 0), dtype=torch.int32, device="cuda"),
+                     torch.empty((5, 0), dtype=torch.float16, device="cuda"),
+                     torch.empty((5, 0), dtype=torch.int16, device="cuda"))
+    torch.cuda.synchronize()
+    assert Y.shape == (3, 5) and (Y.cpu().numpy() == 0).all()

@@ -76,70 +76,84 @@ int group_shift(int64_t group) { return group == 32 ? 0 : group == 64 ? 1 : grou
 
 int status_of(hipError_t e) { return e == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH; }
 
-// perm: NULL, or the act-order column order (device int32 [K]).
+// perm: NULL, or the act-order column order (device int32 [K]).  zeros
+// (asym): the int16 zero points of asymmetric weights, [N, K/group].
 int linear(const uint16_t* X, int64_t M, const uint32_t* packed, const uint16_t* scales,
            int64_t N, int64_t K, int64_t group, uint16_t* Y, int algo, void* stream,
-           const int32_t* perm = nullptr, bool with_perm = false) {
+           const int32_t* perm = nullptr, bool with_perm = false,
+           const int16_t* zeros = nullptr, bool asym = false) {
     int st = check_sizes(M, N, K);
     if (st != W4A16_OK) return st;
     st = check_group(group, K);
     if (st != W4A16_OK) return st;
     if (algo != W4A16_ALGO_AUTO && algo != W4A16_ALGO_VALU && algo != W4A16_ALGO_MFMA)
         return W4A16_ERR_INVALID_ARG;
-    // the matrix-core kernels read one scale per 128 elements and no perm
-    if (algo == W4A16_ALGO_MFMA && (group != W4A16_GROUP || with_perm))
+    // the matrix-core kernels read one scale per 128 elements, no perm and
+    // no zero points
+    if (algo == W4A16_ALGO_MFMA && (group != W4A16_GROUP || with_perm || asym))
         return W4A16_ERR_INVALID_ARG;
     if (M == 0 || N == 0) return W4A16_OK;
     // With K == 0 the inputs hold no bytes and may be NULL; they are never read.
-    if (!Y || (K > 0 && (!X || !packed || !scales || (with_perm && !perm))))
+    if (!Y || (K > 0 && (!X || !packed || !scales || (with_perm && !perm) || (asym && !zeros))))
         return W4A16_ERR_INVALID_ARG;
     if (!aligned(X, 16) || !aligned(packed, 16) || !aligned(scales, 2) || !aligned(Y, 2) ||
-        !aligned(perm, 16))
+        !aligned(perm, 16) || !aligned(zeros, 2))
         return W4A16_ERR_MISALIGNED;
     const size_t y_bytes = (size_t)M * N * 2;
+    const size_t s_bytes = (size_t)N * (K / group) * 2;
     if (overlap(Y, y_bytes, X, (size_t)M * K * 2) ||
-        overlap(Y, y_bytes, packed, (size_t)N * K / 2) ||
-        overlap(Y, y_bytes, scales, (size_t)N * (K / group) * 2) ||
-        (with_perm && overlap(Y, y_bytes, perm, (size_t)K * 4)))
+        overlap(Y, y_bytes, packed, (size_t)N * K / 2) || overlap(Y, y_bytes, scales, s_bytes) ||
+        (with_perm && overlap(Y, y_bytes, perm, (size_t)K * 4)) ||
+        (asym && overlap(Y, y_bytes, zeros, s_bytes)))
         return W4A16_ERR_INVALID_ARG;
     int num_cu = 0;
     st = current_device(&num_cu);
     if (st != W4A16_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const bool valu = algo == W4A16_ALGO_VALU || group != W4A16_GROUP || with_perm ||
+    const bool valu = algo == W4A16_ALGO_VALU || group != W4A16_GROUP || with_perm || asym ||
                       (algo == W4A16_ALGO_AUTO && M <= kValuMaxM);
     if (valu)
         return status_of(w4a16::launch_gemv_valu(X, M, packed, scales, N, K, Y, s, num_cu,
                                                  group_shift(group),
-                                                 with_perm ? perm : nullptr));
+                                                 with_perm ? perm : nullptr,
+                                                 asym ? zeros : nullptr));
     return status_of(w4a16::launch_gemm_mfma(X, M, packed, scales, N, K, Y, s, num_cu));
 }
 
 int quantize(const uint16_t* W, int64_t N, int64_t K, int64_t group, uint32_t* packed,
              uint16_t* scales, void* stream, const int32_t* perm = nullptr,
-             bool with_perm = false) {
+             bool with_perm = false, int16_t* zeros = nullptr, bool asym = false) {
     int st = check_sizes(0, N, K);
     if (st != W4A16_OK) return st;
     st = check_group(group, K);
     if (st != W4A16_OK) return st;
     if (N == 0 || K == 0) return W4A16_OK;
-    if (!W || !packed || !scales || (with_perm && !perm)) return W4A16_ERR_INVALID_ARG;
-    if (!aligned(W, 16) || !aligned(packed, 16) || !aligned(scales, 2) || !aligned(perm, 16))
+    if (!W || !packed || !scales || (with_perm && !perm) || (asym && !zeros))
+        return W4A16_ERR_INVALID_ARG;
+    if (!aligned(W, 16) || !aligned(packed, 16) || !aligned(scales, 2) || !aligned(perm, 16) ||
+        !aligned(zeros, 2))
         return W4A16_ERR_MISALIGNED;
     const size_t w_bytes = (size_t)N * K * 2;
     const size_t p_bytes = (size_t)N * K / 2;
     const size_t s_bytes = (size_t)N * (K / group) * 2;
-    if (overlap(packed, p_bytes, W, w_bytes) || overlap(scales, s_bytes, W, w_bytes) ||
-        overlap(packed, p_bytes, scales, s_bytes) ||
-        (with_perm && (overlap(packed, p_bytes, perm, (size_t)K * 4) ||
-                       overlap(scales, s_bytes, perm, (size_t)K * 4))))
-        return W4A16_ERR_INVALID_ARG;
+    const size_t perm_bytes = with_perm ? (size_t)K * 4 : 0;
+    const size_t z_bytes = asym ? s_bytes : 0;
+    // outputs: packed, scales, zeros; inputs: W, perm
+    const void* outs[3] = {packed, scales, zeros};
+    const size_t out_bytes[3] = {p_bytes, s_bytes, z_bytes};
+    for (int i = 0; i < 3; ++i) {
+        if (overlap(outs[i], out_bytes[i], W, w_bytes) ||
+            overlap(outs[i], out_bytes[i], perm, perm_bytes))
+            return W4A16_ERR_INVALID_ARG;
+        for (int j = i + 1; j < 3; ++j)
+            if (overlap(outs[i], out_bytes[i], outs[j], out_bytes[j])) return W4A16_ERR_INVALID_ARG;
+    }
     int num_cu = 0;
     st = current_device(&num_cu);
     if (st != W4A16_OK) return st;
     return status_of(w4a16::launch_quantize(W, N, K, group, packed, scales,
                                             static_cast<hipStream_t>(stream),
-                                            with_perm ? perm : nullptr));
+                                            with_perm ? perm : nullptr, asym ? zeros : nullptr));
 }
 
 }  // namespace
@@ -212,6 +226,26 @@ int w4a16_gemm_perm(const uint16_t* X, int64_t M, const int32_t* perm, const uin
                   true);
 }
 
+int w4a16_quantize_asym(const uint16_t* W, const int32_t* perm, int64_t N, int64_t K,
+                        int64_t group, uint32_t* packed, uint16_t* scales, int16_t* zeros,
+                        void* stream) {
+    return quantize(W, N, K, group, packed, scales, stream, perm, perm != nullptr, zeros, true);
+}
+
+int w4a16_gemv_asym(const uint16_t* x, const int32_t* perm, const uint32_t* packed,
+                    const uint16_t* scales, const int16_t* zeros, int64_t N, int64_t K,
+                    int64_t group, uint16_t* y, void* stream) {
+    return linear(x, 1, packed, scales, N, K, group, y, W4A16_ALGO_VALU, stream, perm,
+                  perm != nullptr, zeros, true);
+}
+
+int w4a16_gemm_asym(const uint16_t* X, int64_t M, const int32_t* perm, const uint32_t* packed,
+                    const uint16_t* scales, const int16_t* zeros, int64_t N, int64_t K,
+                    int64_t group, uint16_t* Y, void* stream) {
+    return linear(X, M, packed, scales, N, K, group, Y, W4A16_ALGO_AUTO, stream, perm,
+                  perm != nullptr, zeros, true);
+}
+
 int w4a16_gemv_chain(const w4a16_gemv_stage* stages, int count, uint32_t* sync, void* stream) {
     static_assert(W4A16_CHAIN_MAX == w4a16::kChainMax, "chain limit");
     static_assert(W4A16_CHAIN_SYNC_WORDS == w4a16::kChainSyncWords, "sync words");
@@ -274,7 +308,7 @@ const char* w4a16_status_string(int status) {
         case W4A16_OK: return "ok";
         case W4A16_ERR_INVALID_ARG: return "invalid argument (null pointer, negative or too large size, overlapping output, unknown algo or group size)";
         case W4A16_ERR_SHAPE: return "K must be a multiple of 128 and of the group size";
-        case W4A16_ERR_MISALIGNED: return "misaligned pointer (W, X, x, packed need 16 bytes; scales, Y, y need 2)";
+        case W4A16_ERR_MISALIGNED: return "misaligned pointer (W, X, x, packed, perm need 16 bytes; scales, zeros, Y, y need 2)";
         case W4A16_ERR_DEVICE: return "no HIP device, or the current device is not gfx950";
         case W4A16_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
         default: return "unknown status";

@@ -21,6 +21,13 @@
 // Precision: every product q*x is exact in fp32, so accumulation error is
 // relative to sum |q x| (within the 1e-3 sum |x w| allowance for every K);
 // a one-hot x reproduces fp16(s*q) exactly.
+//
+// Asymmetric INT4 ([QUANT] sub-section 2, asymmetric equations: w = s (n - z)
+// with the nibble n in [0, 15] and an integer zero point z per group): the
+// codes are formed as n - zc, exact fp16 integers, with zc = clamp(z, -1000,
+// 1000) folded into the two bias constants of the code trick, so the products
+// stay exact; a group with |z| > 1000 (one-signed with a narrow range, where
+// every |n - z| > 985) adds (zc - z) * sum(x over the chunk).
 #include "w4a16_device.h"
 #include "w4a16_launch.h"
 
@@ -73,15 +80,73 @@ __device__ __forceinline__ void stage_activations(const uint16_t* __restrict__ X
     }
 }
 
+// Codes n - zc of one packed word as exact fp16 integers in the paired
+// order (the code trick of codes_word with the bias constants -1024 - zc and
+// -64 - zc, |zc| <= 1000: operands and results are integers below 2^11).
+__device__ __forceinline__ float dot_word_zp(uint32_t w, const uint4& xp, float acc,
+                                             const CodeConsts& k, half2_t blo, half2_t bhi) {
+    const half2_t inv16 = {(_Float16)0.0625f, (_Float16)0.0625f};
+    const uint32_t w8 = w >> 8;
+    const half2_t q0 = as_h2((w & k.m_lo) | k.magic) + blo;
+    const half2_t q1 = __builtin_elementwise_fma(as_h2((w & k.m_hi) | k.magic), inv16, bhi);
+    const half2_t q2 = as_h2((w8 & k.m_lo) | k.magic) + blo;
+    const half2_t q3 = __builtin_elementwise_fma(as_h2((w8 & k.m_hi) | k.magic), inv16, bhi);
+    acc = __builtin_amdgcn_fdot2(q0, as_h2(xp.x), acc, false);
+    acc = __builtin_amdgcn_fdot2(q1, as_h2(xp.y), acc, false);
+    acc = __builtin_amdgcn_fdot2(q2, as_h2(xp.z), acc, false);
+    acc = __builtin_amdgcn_fdot2(q3, as_h2(xp.w), acc, false);
+    return acc;
+}
+
+constexpr int kZeroClamp = 1000;
+
+// sum_k x_k * (n_k - z) over one 16-byte chunk of 32 codes (activations
+// x0..x3 in the paired order).  Symmetric weights (ASYM false) have
+// n_k - 8 instead and ignore z.
+template <bool ASYM>
+__device__ __forceinline__ float chunk_dot(const uint4& w, const uint4& x0, const uint4& x1,
+                                           const uint4& x2, const uint4& x3, int z,
+                                           const CodeConsts& kc) {
+    if constexpr (!ASYM) {
+        float part = dot_word(w.x, x0, 0.0f, kc);
+        part = dot_word(w.y, x1, part, kc);
+        part = dot_word(w.z, x2, part, kc);
+        return dot_word(w.w, x3, part, kc);
+    } else {
+        const int zc = min(max(z, -kZeroClamp), kZeroClamp);
+        const _Float16 zh = (_Float16)zc;                       // exact
+        const _Float16 lo = (_Float16)-1024.0f - zh, hi = (_Float16)-64.0f - zh;
+        const half2_t blo = {lo, lo}, bhi = {hi, hi};
+        float part = dot_word_zp(w.x, x0, 0.0f, kc, blo, bhi);
+        part = dot_word_zp(w.y, x1, part, kc, blo, bhi);
+        part = dot_word_zp(w.z, x2, part, kc, blo, bhi);
+        part = dot_word_zp(w.w, x3, part, kc, blo, bhi);
+        if (zc != z) {
+            // sum of the chunk's 32 activations, each exact in fp32
+            const half2_t one = {(_Float16)1.0f, (_Float16)1.0f};
+            float xs = 0.0f;
+            const uint32_t xv[16] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w,
+                                     x2.x, x2.y, x2.z, x2.w, x3.x, x3.y, x3.z, x3.w};
+#pragma unroll
+            for (int i = 0; i < 16; ++i) xs = __builtin_amdgcn_fdot2(one, as_h2(xv[i]), xs, false);
+            part = fmaf((float)(zc - z), xs, part);
+        }
+        return part;
+    }
+}
+
 }  // namespace
 
 // MMAX: activation rows handled (M <= MMAX at run time).  R: weight rows per
-// wave.  U: chunk steps loaded ahead.  WAVES: waves per block.
-template <int MMAX, int R, int U, int WAVES>
+// wave.  U: chunk steps loaded ahead.  WAVES: waves per block.  ASYM: the
+// asymmetric layout, one int16 zero point per group in `zeros` (laid out like
+// the scales); NULL and unused otherwise.
+template <int MMAX, int R, int U, int WAVES, bool ASYM>
 __global__ __launch_bounds__(WAVES * kWave) void gemv_kernel(
     const uint16_t* __restrict__ X, int M, const uint4* __restrict__ packed,
-    const uint16_t* __restrict__ scales, uint16_t* __restrict__ Y, int N, int K, int kslice,
-    int gshift, const int* __restrict__ perm) {
+    const uint16_t* __restrict__ scales, const int16_t* __restrict__ zeros,
+    uint16_t* __restrict__ Y, int N, int K, int kslice, int gshift,
+    const int* __restrict__ perm) {
     extern __shared__ uint4 lds[];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
@@ -112,7 +177,7 @@ __global__ __launch_bounds__(WAVES * kWave) void gemv_kernel(
 
         // U steps of R rows: lane takes chunk lane + 64*step.  A step past the
         // slice end re-reads the last chunk (in bounds) and is not used.
-        auto load = [&](int s0, uint4 (&w)[U][R], uint16_t (&sb)[U][R]) {
+        auto load = [&](int s0, uint4 (&w)[U][R], uint16_t (&sb)[U][R], int16_t (&zb)[U][R]) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int cc = c0 + min(lane + (s0 + u) * kWave, nch - 1);
@@ -120,10 +185,12 @@ __global__ __launch_bounds__(WAVES * kWave) void gemv_kernel(
                 for (int r = 0; r < R; ++r) {
                     w[u][r] = packed[wrow[r] + cc];
                     sb[u][r] = scales[srow[r] + (cc >> gshift)];
+                    zb[u][r] = ASYM ? zeros[srow[r] + (cc >> gshift)] : (int16_t)0;
                 }
             }
         };
-        auto compute = [&](int s0, const uint4 (&w)[U][R], const uint16_t (&sb)[U][R]) {
+        auto compute = [&](int s0, const uint4 (&w)[U][R], const uint16_t (&sb)[U][R],
+                           const int16_t (&zb)[U][R]) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int c = lane + (s0 + u) * kWave;
@@ -135,10 +202,7 @@ __global__ __launch_bounds__(WAVES * kWave) void gemv_kernel(
                     const uint4 x0 = xp[0], x1 = xp[1], x2 = xp[2], x3 = xp[3];
 #pragma unroll
                     for (int r = 0; r < R; ++r) {
-                        float part = dot_word(w[u][r].x, x0, 0.0f, kc);
-                        part = dot_word(w[u][r].y, x1, part, kc);
-                        part = dot_word(w[u][r].z, x2, part, kc);
-                        part = dot_word(w[u][r].w, x3, part, kc);
+                        const float part = chunk_dot<ASYM>(w[u][r], x0, x1, x2, x3, zb[u][r], kc);
                         acc[m][r] = fmaf(f16_bits_to_f32(sb[u][r]), part, acc[m][r]);
                     }
                 }
@@ -147,19 +211,20 @@ __global__ __launch_bounds__(WAVES * kWave) void gemv_kernel(
 
         uint4 wa[U][R], wb[U][R];
         uint16_t sa[U][R], sbb[U][R];
+        int16_t za[U][R], zbb[U][R];
         // Weight loads go out before the activations are staged, so HBM is
         // busy while the block waits on its barrier.
-        load(0, wa, sa);
+        load(0, wa, sa, za);
         if (k0 > 0) __syncthreads();     // previous slice fully consumed
         stage_activations(X, M, K, k0, ks, lds, perm);
         __syncthreads();
 
         for (int s0 = 0; s0 < nsteps; s0 += 2 * U) {
-            if (s0 + U < nsteps) load(s0 + U, wb, sbb);
-            compute(s0, wa, sa);
+            if (s0 + U < nsteps) load(s0 + U, wb, sbb, zbb);
+            compute(s0, wa, sa, za);
             if (s0 + U >= nsteps) break;
-            if (s0 + 2 * U < nsteps) load(s0 + 2 * U, wa, sa);
-            compute(s0 + U, wb, sbb);
+            if (s0 + 2 * U < nsteps) load(s0 + 2 * U, wa, sa, za);
+            compute(s0 + U, wb, sbb, zbb);
         }
     }
 
@@ -191,11 +256,11 @@ __global__ __launch_bounds__(WAVES * kWave) void gemv_kernel(
 //   - A lane whose chunk is past the end of the row (last partial step)
 //     contributes with scale 0 and reads a valid LDS address.
 // XPT: 16-byte activation blocks staged per thread (MMAX*K/8 <= XPT*threads).
-template <int MMAX, int R, int P, int WAVES, int XPT>
+template <int MMAX, int R, int P, int WAVES, int XPT, bool ASYM>
 __global__ __launch_bounds__(WAVES * kWave) void gemv_persistent_kernel(
     const uint16_t* __restrict__ X, int M, const uint4* __restrict__ packed,
-    const uint16_t* __restrict__ scales, uint16_t* __restrict__ Y, int N, int K, int gshift,
-    const int* __restrict__ perm) {
+    const uint16_t* __restrict__ scales, const int16_t* __restrict__ zeros,
+    uint16_t* __restrict__ Y, int N, int K, int gshift, const int* __restrict__ perm) {
     extern __shared__ uint4 lds[];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -224,7 +289,8 @@ __global__ __launch_bounds__(WAVES * kWave) void gemv_persistent_kernel(
     // load cursor (wave-uniform): iteration tl -> (row group lrg, step ls)
     int tl = 0, lrg = first_rg, ls = 0;
     __amdgpu_buffer_rsrc_t wr = buffer_rsrc(packed, 0), sr = buffer_rsrc(scales, 0);
-    auto load = [&](uint4 (&wd)[R], uint16_t (&sd)[R]) {
+    __amdgpu_buffer_rsrc_t zr = buffer_rsrc(zeros, 0);
+    auto load = [&](uint4 (&wd)[R], uint16_t (&sd)[R], int16_t (&zd)[R]) {
         if (ls == 0) {
             // new row group (or past the wave's work: an empty resource)
             const bool live = tl < T;
@@ -234,6 +300,9 @@ __global__ __launch_bounds__(WAVES * kWave) void gemv_persistent_kernel(
                              (uint64_t)rows_left * wrow_bytes);
             sr = buffer_rsrc(reinterpret_cast<const char*>(scales) + (live ? row0 * srow_bytes : 0),
                              (uint64_t)rows_left * srow_bytes);
+            if constexpr (ASYM)
+                zr = buffer_rsrc(reinterpret_cast<const char*>(zeros) + (live ? row0 * srow_bytes : 0),
+                                 (uint64_t)rows_left * srow_bytes);
         }
         const int voff_w = lane * 16 + ls * (kWave * 16);
         const int voff_s = ((lane + ls * kWave) >> gshift) * 2;
@@ -246,6 +315,9 @@ __global__ __launch_bounds__(WAVES * kWave) void gemv_persistent_kernel(
                                                                  kStreamLoad);
             wd[r] = make_uint4(v.x, v.y, v.z, v.w);
             sd[r] = __builtin_amdgcn_raw_buffer_load_b16(sr, voff_s, r * srow_bytes, kStreamLoad);
+            zd[r] = ASYM ? (int16_t)__builtin_amdgcn_raw_buffer_load_b16(zr, voff_s, r * srow_bytes,
+                                                                         kStreamLoad)
+                         : (int16_t)0;
         }
         ++tl;
         if (++ls == nsteps) { ls = 0; lrg += stride_rg; }
@@ -257,8 +329,9 @@ __global__ __launch_bounds__(WAVES * kWave) void gemv_persistent_kernel(
     constexpr int Q = P + 1;
     uint4 w[Q][R];
     uint16_t sb[Q][R];
+    int16_t zb[Q][R];
 #pragma unroll
-    for (int i = 0; i < P; ++i) load(w[i], sb[i]);
+    for (int i = 0; i < P; ++i) load(w[i], sb[i], zb[i]);
 
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
@@ -278,7 +351,7 @@ __global__ __launch_bounds__(WAVES * kWave) void gemv_persistent_kernel(
     for (int t0 = 0; t0 < T; t0 += Q) {
 #pragma unroll
         for (int i = 0; i < Q; ++i) {
-            load(w[(i + P) % Q], sb[(i + P) % Q]);   // iteration t0 + i + P
+            load(w[(i + P) % Q], sb[(i + P) % Q], zb[(i + P) % Q]);   // iteration t0 + i + P
             const int c = lane + cs * kWave;
             const bool valid = c < nchunks;
             const int cx = min(c, nchunks - 1);
@@ -291,10 +364,7 @@ __global__ __launch_bounds__(WAVES * kWave) void gemv_persistent_kernel(
                 const uint4 x0 = xp[0], x1 = xp[1], x2 = xp[2], x3 = xp[3];
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
-                    float part = dot_word(w[i][r].x, x0, 0.0f, kc);
-                    part = dot_word(w[i][r].y, x1, part, kc);
-                    part = dot_word(w[i][r].z, x2, part, kc);
-                    part = dot_word(w[i][r].w, x3, part, kc);
+                    const float part = chunk_dot<ASYM>(w[i][r], x0, x1, x2, x3, zb[i][r], kc);
                     const float sc = valid ? f16_bits_to_f32(sb[i][r]) : 0.0f;
                     acc[m][r] = fmaf(sc, part, acc[m][r]);
                 }
@@ -326,10 +396,10 @@ namespace {
 
 constexpr int kLdsBudget = 64 * 1024;
 
-template <int MMAX, int R, int U, int WAVES>
+template <int MMAX, int R, int U, int WAVES, bool ASYM>
 hipError_t launch_gemv_t(const uint16_t* X, int64_t M, const uint32_t* packed,
-                         const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y,
-                         hipStream_t stream, int gshift = 2, const int* perm = nullptr) {
+                         const uint16_t* scales, const int16_t* zeros, int64_t N, int64_t K,
+                         uint16_t* Y, hipStream_t stream, int gshift, const int* perm) {
     // LDS: 2 bytes per activation element.
     int64_t kslice = (int64_t)(kLdsBudget / (MMAX * 2)) / kGroup * kGroup;
     if (kslice > K) kslice = K;
@@ -337,33 +407,33 @@ hipError_t launch_gemv_t(const uint16_t* X, int64_t M, const uint32_t* packed,
     const size_t lds = (size_t)MMAX * (kslice / 8) * sizeof(uint4);
     const int64_t rows_per_block = (int64_t)R * WAVES;
     const int64_t blocks = (N + rows_per_block - 1) / rows_per_block;
-    hipLaunchKernelGGL((gemv_kernel<MMAX, R, U, WAVES>), dim3((unsigned)blocks),
+    hipLaunchKernelGGL((gemv_kernel<MMAX, R, U, WAVES, ASYM>), dim3((unsigned)blocks),
                        dim3(WAVES * kWave), lds, stream, X, (int)M,
-                       reinterpret_cast<const uint4*>(packed), scales, Y, (int)N, (int)K,
+                       reinterpret_cast<const uint4*>(packed), scales, zeros, Y, (int)N, (int)K,
                        (int)kslice, gshift, perm);
     return hipGetLastError();
 }
 
-template <int MMAX, int R, int P, int WAVES, int XPT>
+template <int MMAX, int R, int P, int WAVES, int XPT, bool ASYM>
 hipError_t launch_persistent_xpt(const uint16_t* X, int64_t M, const uint32_t* packed,
-                                 const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y,
-                                 hipStream_t stream, int64_t blocks, int gshift,
-                                 const int* perm) {
+                                 const uint16_t* scales, const int16_t* zeros, int64_t N,
+                                 int64_t K, uint16_t* Y, hipStream_t stream, int64_t blocks,
+                                 int gshift, const int* perm) {
     const size_t lds = (size_t)MMAX * (K / 8) * sizeof(uint4);
-    hipLaunchKernelGGL((gemv_persistent_kernel<MMAX, R, P, WAVES, XPT>), dim3((unsigned)blocks),
-                       dim3(WAVES * kWave), lds, stream, X, (int)M,
-                       reinterpret_cast<const uint4*>(packed), scales, Y, (int)N, (int)K, gshift,
-                       perm);
+    hipLaunchKernelGGL((gemv_persistent_kernel<MMAX, R, P, WAVES, XPT, ASYM>),
+                       dim3((unsigned)blocks), dim3(WAVES * kWave), lds, stream, X, (int)M,
+                       reinterpret_cast<const uint4*>(packed), scales, zeros, Y, (int)N, (int)K,
+                       gshift, perm);
     return hipGetLastError();
 }
 
 // Grid: at most blocks_per_cu blocks per compute unit, sized so that every
 // wave gets the same number of row groups.
-template <int MMAX, int R, int P, int WAVES>
+template <int MMAX, int R, int P, int WAVES, bool ASYM>
 hipError_t launch_persistent_t(const uint16_t* X, int64_t M, const uint32_t* packed,
-                               const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y,
-                               hipStream_t stream, int num_cu, int blocks_per_cu,
-                               int gshift = 2, const int* perm = nullptr) {
+                               const uint16_t* scales, const int16_t* zeros, int64_t N,
+                               int64_t K, uint16_t* Y, hipStream_t stream, int num_cu,
+                               int blocks_per_cu, int gshift, const int* perm) {
     const int64_t total_rg = (N + R - 1) / R;
     const int64_t max_waves = (int64_t)num_cu * blocks_per_cu * WAVES;
     const int64_t per_wave = (total_rg + max_waves - 1) / max_waves;
@@ -371,20 +441,15 @@ hipError_t launch_persistent_t(const uint16_t* X, int64_t M, const uint32_t* pac
     const int64_t blocks = (waves + WAVES - 1) / WAVES;
     const int64_t need = (int64_t)MMAX * (K / 8);             // x blocks to stage
     const int64_t threads = (int64_t)WAVES * kWave;
-    if (need <= threads)
-        return launch_persistent_xpt<MMAX, R, P, WAVES, 1>(X, M, packed, scales, N, K, Y, stream, blocks, gshift,
-                                                             perm);
-    if (need <= 2 * threads)
-        return launch_persistent_xpt<MMAX, R, P, WAVES, 2>(X, M, packed, scales, N, K, Y, stream, blocks, gshift,
-                                                             perm);
-    if (need <= 4 * threads)
-        return launch_persistent_xpt<MMAX, R, P, WAVES, 4>(X, M, packed, scales, N, K, Y, stream, blocks, gshift,
-                                                             perm);
-    if (need <= 8 * threads)
-        return launch_persistent_xpt<MMAX, R, P, WAVES, 8>(X, M, packed, scales, N, K, Y, stream, blocks, gshift,
-                                                             perm);
-    return launch_persistent_xpt<MMAX, R, P, WAVES, 16>(X, M, packed, scales, N, K, Y, stream, blocks, gshift,
-                                                             perm);
+#define W4A16_PERSISTENT(XPT)                                                                  \
+    launch_persistent_xpt<MMAX, R, P, WAVES, XPT, ASYM>(X, M, packed, scales, zeros, N, K, Y,  \
+                                                        stream, blocks, gshift, perm)
+    if (need <= threads) return W4A16_PERSISTENT(1);
+    if (need <= 2 * threads) return W4A16_PERSISTENT(2);
+    if (need <= 4 * threads) return W4A16_PERSISTENT(4);
+    if (need <= 8 * threads) return W4A16_PERSISTENT(8);
+    return W4A16_PERSISTENT(16);
+#undef W4A16_PERSISTENT
 }
 
 // Launch choice (measured on MI355X over the decode layer shapes, K x N from
@@ -394,54 +459,71 @@ hipError_t launch_persistent_t(const uint16_t* X, int64_t M, const uint32_t* pac
 // blocks per compute unit; for longer rows (K >= 12288, where the per-block
 // activation copy is larger) two steps in flight, eight waves per block,
 // two blocks per compute unit.
-template <int MMAX>
+template <int MMAX, bool ASYM>
 hipError_t launch_gemv_m(const uint16_t* X, int64_t M, const uint32_t* packed,
-                         const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y,
-                         hipStream_t stream, int num_cu, int gshift, const int* perm) {
+                         const uint16_t* scales, const int16_t* zeros, int64_t N, int64_t K,
+                         uint16_t* Y, hipStream_t stream, int num_cu, int gshift,
+                         const int* perm) {
     if (K > 0 && (int64_t)MMAX * K * 2 <= kLdsBudget) {
         constexpr int R = MMAX >= 4 ? 1 : 2;
         // Measured on gfx950 for M = 1: long rows (K = 14336) run best with
         // 8 waves per block, 2 blocks per CU and one step in flight (7.9 us
         // against 8.6 us with two steps in flight).
         if (MMAX == 1 && K >= 12288)
-            return launch_persistent_t<1, 2, 1, 8>(X, M, packed, scales, N, K, Y, stream, num_cu,
-                                                   2, gshift, perm);
+            return launch_persistent_t<1, 2, 1, 8, ASYM>(X, M, packed, scales, zeros, N, K, Y,
+                                                         stream, num_cu, 2, gshift, perm);
         if (K >= 12288)
-            return launch_persistent_t<MMAX, R, 2, 8>(X, M, packed, scales, N, K, Y, stream,
-                                                      num_cu, 2, gshift, perm);
-        return launch_persistent_t<MMAX, R, 1, 4>(X, M, packed, scales, N, K, Y, stream, num_cu,
-                                                  6, gshift, perm);
+            return launch_persistent_t<MMAX, R, 2, 8, ASYM>(X, M, packed, scales, zeros, N, K, Y,
+                                                            stream, num_cu, 2, gshift, perm);
+        return launch_persistent_t<MMAX, R, 1, 4, ASYM>(X, M, packed, scales, zeros, N, K, Y,
+                                                        stream, num_cu, 6, gshift, perm);
     }
     constexpr int WAVES = 4;
     if (N >= (int64_t)4 * WAVES * num_cu && MMAX <= 4)
-        return launch_gemv_t<MMAX, 4, 2, WAVES>(X, M, packed, scales, N, K, Y, stream, gshift,
-                                                perm);
+        return launch_gemv_t<MMAX, 4, 2, WAVES, ASYM>(X, M, packed, scales, zeros, N, K, Y,
+                                                      stream, gshift, perm);
     if (N >= (int64_t)2 * WAVES * num_cu)
-        return launch_gemv_t<MMAX, 2, 2, WAVES>(X, M, packed, scales, N, K, Y, stream, gshift,
-                                                perm);
-    return launch_gemv_t<MMAX, 1, 4, WAVES>(X, M, packed, scales, N, K, Y, stream, gshift,
-                                                perm);
+        return launch_gemv_t<MMAX, 2, 2, WAVES, ASYM>(X, M, packed, scales, zeros, N, K, Y,
+                                                      stream, gshift, perm);
+    return launch_gemv_t<MMAX, 1, 4, WAVES, ASYM>(X, M, packed, scales, zeros, N, K, Y, stream,
+                                                  gshift, perm);
+}
+
+template <bool ASYM>
+hipError_t launch_gemv_a(const uint16_t* X, int64_t M, const uint32_t* packed,
+                         const uint16_t* scales, const int16_t* zeros, int64_t N, int64_t K,
+                         uint16_t* Y, hipStream_t stream, int num_cu, int gshift,
+                         const int* perm) {
+    if (M == 1)
+        return launch_gemv_m<1, ASYM>(X, M, packed, scales, zeros, N, K, Y, stream, num_cu,
+                                      gshift, perm);
+    if (M == 2)
+        return launch_gemv_m<2, ASYM>(X, M, packed, scales, zeros, N, K, Y, stream, num_cu,
+                                      gshift, perm);
+    if (M <= 4)
+        return launch_gemv_m<4, ASYM>(X, M, packed, scales, zeros, N, K, Y, stream, num_cu,
+                                      gshift, perm);
+    // M > 8 is split into slices of at most 8 activation rows.
+    for (int64_t m0 = 0; m0 < M; m0 += 8) {
+        const int64_t mm = (M - m0 < 8) ? (M - m0) : 8;
+        hipError_t e = launch_gemv_m<8, ASYM>(X + m0 * K, mm, packed, scales, zeros, N, K,
+                                              Y + m0 * N, stream, num_cu, gshift, perm);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace
 
 hipError_t launch_gemv_valu(const uint16_t* X, int64_t M, const uint32_t* packed,
                             const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y,
-                            hipStream_t stream, int num_cu, int gshift, const int* perm) {
-    if (M == 1)
-        return launch_gemv_m<1>(X, M, packed, scales, N, K, Y, stream, num_cu, gshift, perm);
-    if (M == 2)
-        return launch_gemv_m<2>(X, M, packed, scales, N, K, Y, stream, num_cu, gshift, perm);
-    if (M <= 4)
-        return launch_gemv_m<4>(X, M, packed, scales, N, K, Y, stream, num_cu, gshift, perm);
-    // M > 8 is split into slices of at most 8 activation rows.
-    for (int64_t m0 = 0; m0 < M; m0 += 8) {
-        const int64_t mm = (M - m0 < 8) ? (M - m0) : 8;
-        hipError_t e = launch_gemv_m<8>(X + m0 * K, mm, packed, scales, N, K, Y + m0 * N,
-                                        stream, num_cu, gshift, perm);
-        if (e != hipSuccess) return e;
-    }
-    return hipSuccess;
+                            hipStream_t stream, int num_cu, int gshift, const int* perm,
+                            const int16_t* zeros) {
+    if (zeros != nullptr)
+        return launch_gemv_a<true>(X, M, packed, scales, zeros, N, K, Y, stream, num_cu, gshift,
+                                   perm);
+    return launch_gemv_a<false>(X, M, packed, scales, nullptr, N, K, Y, stream, num_cu, gshift,
+                                perm);
 }
 
 }  // namespace w4a16

@@ -1,14 +1,16 @@
-// quantize.hip — RTN symmetric INT4 quantizer, one fp16 scale per group of
+// quantize.hip — RTN INT4 quantizers (symmetric, and asymmetric with a zero
+// point per group), one fp16 scale per group of
 // G elements along K (G = 128 by default; 32, 64 and 256 as in [QUANT]'s
 // granularity table and GPTQ group_size table), packed eight codes per
 // uint32 ([QUANT] sub-section 2 equations, sub-section 3 per-group listing;
 // [INT4] INT4 paragraph).
 //
 // Work split: G/8 consecutive lanes of a wave per (row, group).  Each lane
-// loads 16 bytes (8 fp16), the lanes reduce the absolute maximum with DPP
-// (and one cross-row swap for G = 256), and each lane writes the one packed
-// word its 8 elements form; the group's lanes write its G/2 contiguous
-// bytes.  HBM traffic per element: 2 B in, 0.5 + 2/G B out.
+// loads 16 bytes (8 fp16), the lanes reduce the absolute maximum (the
+// asymmetric quantizer: the maximum and the minimum) with DPP (and one
+// cross-row swap for G = 256), and each lane writes the one packed word its
+// 8 elements form; the group's lanes write its G/2 contiguous bytes.  HBM
+// traffic per element: 2 B in, 0.5 + 2/G B out (0.5 + 4/G with zero points).
 //
 // Bit-exactness:
 //   - |w| is compared as the integer w & 0x7FFF (order of finite fp16
@@ -95,6 +97,94 @@ __device__ __forceinline__ uint32_t quantize8(const uint4& v, uint16_t& s_bits) 
     }
     return word;
 }
+
+// ---- asymmetric INT4 ([QUANT] sub-section 2, asymmetric equations) ----
+//   s = fp16_rne((max - min) / 15), z = -rint(min / s), q = clamp(rint(w / s)
+//   + z, 0, 15), stored as the nibble q itself; s = 0 (a group whose range
+//   rounds to 0) stores z = 0 and q = 0.
+// Bit-exactness, all in binary64 (full-rate vector fp64 on gfx950):
+//   - max - min of two fp16 values is exact (at most 40 significant bits);
+//     the IEEE division by 15 and the rounding to fp16 below give the RNE
+//     of the exact quotient: (max - min) / 15 is either dyadic (then exact in
+//     binary64) or has the period-4 binary expansion of 1/15, which never
+//     puts a 53-bit rounding on a fp16 tie;
+//   - min / s and w / s lie within 2^15 in magnitude (|z| <= 32752), and a
+//     quotient of two fp16 values that is not a tie is at least 2^-23 away
+//     from one: the IEEE division, or w * (1 / s) (error below 2^-36), round
+//     to the same integer as the exact quotient; a lane whose product lies
+//     within 2^-30 of a tie (exact ties only) redoes its 8 elements with the
+//     division.
+
+// fp16 bits of the round-to-nearest-even of v (0 <= v < 65520): the integer
+// rint(v / u) times the fp16 spacing u = 2^(e - 10) at v's binade (2^-24
+// below 2^-14), both scalings by powers of two exact.
+__device__ __forceinline__ uint16_t f16_rne_from_f64(double v) {
+    if (v == 0.0) return 0;
+    const uint64_t b = (uint64_t)__double_as_longlong(v);
+    int e = (int)((b >> 52) & 0x7FF) - 1023;      // v > 0 is a normal binary64
+    if (e < -14) e = -14;
+    const double m = rint(ldexp(v, 10 - e));      // at most 2^11
+    return f32_to_f16_bits((float)ldexp(m, e - 10));
+}
+
+// Order-preserving key of a finite fp16 bit pattern (sign-magnitude to
+// offset binary: -0 just below +0), and its inverse.
+__device__ __forceinline__ uint32_t f16_key(uint32_t h) {
+    return h ^ ((h & 0x8000u) ? 0xFFFFu : 0x8000u);
+}
+__device__ __forceinline__ uint32_t f16_from_key(uint32_t k) {
+    return k ^ ((k & 0x8000u) ? 0x8000u : 0xFFFFu);
+}
+
+// One lane's 8 elements of a group -> its packed word (nibbles q in
+// [0, 15]), and the group's scale and zero point.
+template <int LG>
+__device__ __forceinline__ uint32_t quantize8_asym(const uint4& v, uint16_t& s_bits,
+                                                   int16_t& zero) {
+    const uint32_t h[8] = {v.x & 0xFFFFu, v.x >> 16, v.y & 0xFFFFu, v.y >> 16,
+                           v.z & 0xFFFFu, v.z >> 16, v.w & 0xFFFFu, v.w >> 16};
+    uint32_t kmax = 0, kmin_c = 0;                      // max key, max of 0xFFFF - key
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t key = f16_key(h[i]);
+        kmax = max(kmax, key);
+        kmin_c = max(kmin_c, 0xFFFFu - key);
+    }
+    kmax = group_max<LG>(kmax);
+    kmin_c = group_max<LG>(kmin_c);
+    const double mx = (double)f16_bits_to_f32((uint16_t)f16_from_key(kmax));
+    const double mn = (double)f16_bits_to_f32((uint16_t)f16_from_key(0xFFFFu - kmin_c));
+    s_bits = f16_rne_from_f64((mx - mn) / 15.0);         // 2^4 - 1 = 15
+    const double s = (double)f16_bits_to_f32(s_bits);
+    if (s == 0.0) {
+        zero = 0;
+        return 0u;                                       // every code 0
+    }
+    const double z = -rint(mn / s);
+    zero = (int16_t)(int)z;
+    const double inv = 1.0 / s;
+    uint32_t word = 0;
+    bool near_tie = false;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const double t = (double)f16_bits_to_f32((uint16_t)h[i]) * inv;
+        const double r = rint(t);
+        near_tie |= fabs(t - r) > 0.5 - 0x1p-30;
+        const double c = fmin(fmax(r + z, 0.0), 15.0);
+        word |= (uint32_t)(int)c << (4 * i);
+    }
+    if (near_tie) {
+        word = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const double r = rint((double)f16_bits_to_f32((uint16_t)h[i]) / s);
+            const double c = fmin(fmax(r + z, 0.0), 15.0);
+            word |= (uint32_t)(int)c << (4 * i);
+        }
+    }
+    return word;
+}
+
 }  // namespace
 
 // Each LG-lane slice of a wave quantizes one group per step; the loads of U
@@ -106,10 +196,14 @@ __device__ __forceinline__ uint32_t quantize8(const uint4& v, uint16_t& s_bits) 
 // in the order perm): NULL, or device int32 [K]; column j of the output is
 // column perm[j] of W (an index outside [0, K) reads as 0), gathered with
 // 2-byte loads instead of one 16-byte load per lane.
-template <int LG, int U>
+//
+// ASYM: the asymmetric quantizer, which also writes one int16 zero point per
+// group to `zeros` (laid out like the scales).
+template <int LG, int U, bool ASYM>
 __global__ __launch_bounds__(256) void quantize_kernel(const uint4* __restrict__ W,
                                                        uint32_t* __restrict__ packed,
                                                        uint16_t* __restrict__ scales,
+                                                       int16_t* __restrict__ zeros,
                                                        int64_t total_groups, int K,
                                                        const int* __restrict__ perm) {
     const int lg = threadIdx.x & (LG - 1);              // lane within the group
@@ -147,11 +241,19 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint4* __restrict__
         for (int u = 0; u < U; ++u) {
             const int64_t gu = g + u * stride;
             if (gu < total_groups) {
+                const uint4 v = make_uint4(a[u].x, a[u].y, a[u].z, a[u].w);
                 uint16_t sb;
-                const uint32_t word =
-                    quantize8<LG>(make_uint4(a[u].x, a[u].y, a[u].z, a[u].w), sb);
-                packed[gu * LG + lg] = word;
-                if (lg == 0) scales[gu] = sb;
+                if constexpr (ASYM) {
+                    int16_t zb;
+                    packed[gu * LG + lg] = quantize8_asym<LG>(v, sb, zb);
+                    if (lg == 0) {
+                        scales[gu] = sb;
+                        zeros[gu] = zb;
+                    }
+                } else {
+                    packed[gu * LG + lg] = quantize8<LG>(v, sb);
+                    if (lg == 0) scales[gu] = sb;
+                }
             }
         }
     }
@@ -159,28 +261,33 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint4* __restrict__
 
 template <int LG, int U>
 hipError_t launch_quantize_t(const uint16_t* W, int64_t groups, int64_t K, const int* perm,
-                             uint32_t* packed, uint16_t* scales, hipStream_t stream,
-                             int64_t max_blocks) {
+                             uint32_t* packed, uint16_t* scales, int16_t* zeros,
+                             hipStream_t stream) {
     constexpr int per_block = 256 / LG;                  // groups per block and step
+    constexpr int64_t kMaxBlocks = 65536;
     int64_t blocks = (groups + per_block * U - 1) / (per_block * U);
-    if (blocks > max_blocks) blocks = max_blocks;        // grid-stride beyond this
-    hipLaunchKernelGGL((quantize_kernel<LG, U>), dim3((unsigned)blocks), dim3(256), 0, stream,
-                       reinterpret_cast<const uint4*>(W), packed, scales, groups, (int)K, perm);
+    if (blocks > kMaxBlocks) blocks = kMaxBlocks;        // grid-stride beyond this
+    const uint4* Wv = reinterpret_cast<const uint4*>(W);
+    if (zeros != nullptr)
+        hipLaunchKernelGGL((quantize_kernel<LG, U, true>), dim3((unsigned)blocks), dim3(256), 0,
+                           stream, Wv, packed, scales, zeros, groups, (int)K, perm);
+    else
+        hipLaunchKernelGGL((quantize_kernel<LG, U, false>), dim3((unsigned)blocks), dim3(256), 0,
+                           stream, Wv, packed, scales, zeros, groups, (int)K, perm);
     return hipGetLastError();
 }
 
 hipError_t launch_quantize(const uint16_t* W, int64_t N, int64_t K, int64_t group,
                            uint32_t* packed, uint16_t* scales, hipStream_t stream,
-                           const int* perm) {
+                           const int* perm, int16_t* zeros) {
     const int64_t groups = N * (K / group);
     if (groups == 0) return hipSuccess;
     // the same 16 bytes per lane and two groups' loads in flight for every G
-    constexpr int64_t kMaxBlocks = 65536;
     switch (group) {
-        case 32: return launch_quantize_t<4, 2>(W, groups, K, perm, packed, scales, stream, kMaxBlocks);
-        case 64: return launch_quantize_t<8, 2>(W, groups, K, perm, packed, scales, stream, kMaxBlocks);
-        case 128: return launch_quantize_t<16, 2>(W, groups, K, perm, packed, scales, stream, kMaxBlocks);
-        case 256: return launch_quantize_t<32, 2>(W, groups, K, perm, packed, scales, stream, kMaxBlocks);
+        case 32: return launch_quantize_t<4, 2>(W, groups, K, perm, packed, scales, zeros, stream);
+        case 64: return launch_quantize_t<8, 2>(W, groups, K, perm, packed, scales, zeros, stream);
+        case 128: return launch_quantize_t<16, 2>(W, groups, K, perm, packed, scales, zeros, stream);
+        case 256: return launch_quantize_t<32, 2>(W, groups, K, perm, packed, scales, zeros, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -9,19 +9,22 @@
 namespace w4a16 {
 
 // group: 32, 64, 128 or 256 elements per scale.  perm: NULL, or device
-// int32 [K] (column j of the result is column perm[j] of W).
+// int32 [K] (column j of the result is column perm[j] of W).  zeros: NULL
+// for the symmetric quantizer, or int16 [N, K/group] for the asymmetric one.
 hipError_t launch_quantize(const uint16_t* W, int64_t N, int64_t K, int64_t group,
                            uint32_t* packed, uint16_t* scales, hipStream_t stream,
-                           const int* perm = nullptr);
+                           const int* perm = nullptr, int16_t* zeros = nullptr);
 
 // VALU dot-product path, any M (M > 8 runs in slices of 8 rows).  gshift:
 // log2(group / 32), one scale per 2^gshift 32-code chunks (2 = group 128).
 // perm (device int32 [K], 16-byte aligned, or NULL): the weight's columns
 // are in the order perm, so column j meets activation X[m, perm[j]].
+// zeros (device int16 [N, K/group], or NULL): asymmetric weights, nibbles n
+// in [0, 15] and w = s (n - z); NULL: symmetric, w = s (n - 8).
 hipError_t launch_gemv_valu(const uint16_t* X, int64_t M, const uint32_t* packed,
                             const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y,
                             hipStream_t stream, int num_cu, int gshift = 2,
-                            const int* perm = nullptr);
+                            const int* perm = nullptr, const int16_t* zeros = nullptr);
 
 // MFMA path, any M.
 hipError_t launch_gemm_mfma(const uint16_t* X, int64_t M, const uint32_t* packed,

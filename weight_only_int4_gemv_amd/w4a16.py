@@ -7,6 +7,8 @@ There is no fallback: a missing library or a non-gfx950 device is an error.
     packed, scales = quantize(W)            # W: fp16 [N, K] on the GPU
     y = gemv(x, packed, scales)             # x: fp16 [K]      -> [N]
     Y = gemm(X, packed, scales)             # X: fp16 [M, K]   -> [M, N]
+    packed, scales, zeros = quantize_asym(W)          # asymmetric INT4
+    Y = gemm_asym(X, packed, scales, zeros)
 """
 from __future__ import annotations
 
@@ -69,9 +71,13 @@ def library() -> ctypes.CDLL:
         lib.w4a16_quantize_perm.argtypes = [_p, _p, _i64, _i64, _p, _p, _p]
         lib.w4a16_gemv_perm.argtypes = [_p, _p, _p, _p, _i64, _i64, _p, _p]
         lib.w4a16_gemm_perm.argtypes = [_p, _i64, _p, _p, _p, _i64, _i64, _p, _p]
+        lib.w4a16_quantize_asym.argtypes = [_p, _p, _i64, _i64, _i64, _p, _p, _p, _p]
+        lib.w4a16_gemv_asym.argtypes = [_p, _p, _p, _p, _p, _i64, _i64, _i64, _p, _p]
+        lib.w4a16_gemm_asym.argtypes = [_p, _i64, _p, _p, _p, _p, _i64, _i64, _i64, _p, _p]
         for f in (lib.w4a16_quantize, lib.w4a16_gemv, lib.w4a16_gemm, lib.w4a16_gemm_ex,
                   lib.w4a16_quantize_g, lib.w4a16_gemv_g, lib.w4a16_gemm_g,
-                  lib.w4a16_quantize_perm, lib.w4a16_gemv_perm, lib.w4a16_gemm_perm):
+                  lib.w4a16_quantize_perm, lib.w4a16_gemv_perm, lib.w4a16_gemm_perm,
+                  lib.w4a16_quantize_asym, lib.w4a16_gemv_asym, lib.w4a16_gemm_asym):
             f.restype = ctypes.c_int
         lib.w4a16_valu_max_m.restype = ctypes.c_int64
         lib.w4a16_gemv_chain.argtypes = [ctypes.POINTER(GemvStage), ctypes.c_int, _p, _p]
@@ -247,6 +253,92 @@ def gemm(X: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, algo=None,
         st = lib.w4a16_gemm_g(X.data_ptr(), M, packed.data_ptr(), scales.data_ptr(), N, K,
                               group, Y.data_ptr(), _stream())
     _check("w4a16_gemm", st)
+    return Y
+
+
+def quantize_asym(W: torch.Tensor, packed: torch.Tensor = None, scales: torch.Tensor = None,
+                  zeros: torch.Tensor = None, group: int = W4A16_GROUP,
+                  perm: torch.Tensor = None):
+    """Asymmetric INT4: W fp16 [N, K] -> (packed int32 [N, K/8] with nibbles
+    q in [0, 15], scales fp16 [N, K/group], zeros int16 [N, K/group]);
+    ŵ = s * (q - z).  perm (int32 [K]): quantize W[:, perm] (act order)."""
+    lib = library()
+    _need(W, "W", torch.float16, 2)
+    N, K = W.shape
+    _check_group(group, K)
+    if perm is not None:
+        _perm(perm, K)
+    if packed is None:
+        packed = torch.empty((N, K // 8), dtype=torch.int32, device=W.device)
+    if scales is None:
+        scales = torch.empty((N, K // group), dtype=torch.float16, device=W.device)
+    if zeros is None:
+        zeros = torch.empty((N, K // group), dtype=torch.int16, device=W.device)
+    _need(packed, "packed", torch.int32, 2)
+    _need(scales, "scales", torch.float16, 2)
+    _need(zeros, "zeros", torch.int16, 2)
+    if (tuple(packed.shape) != (N, K // 8) or tuple(scales.shape) != (N, K // group)
+            or tuple(zeros.shape) != (N, K // group)):
+        raise ValueError("output shapes do not match W")
+    st = lib.w4a16_quantize_asym(W.data_ptr(), perm.data_ptr() if perm is not None else None,
+                                 N, K, group, packed.data_ptr(), scales.data_ptr(),
+                                 zeros.data_ptr(), _stream())
+    _check("w4a16_quantize_asym", st)
+    return packed, scales, zeros
+
+
+def _zeros(zeros: torch.Tensor, scales: torch.Tensor) -> None:
+    _need(zeros, "zeros", torch.int16, 2)
+    if zeros.shape != scales.shape:
+        raise ValueError("zeros shape %s, scales %s" % (tuple(zeros.shape), tuple(scales.shape)))
+
+
+def gemv_asym(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,
+              zeros: torch.Tensor, y: torch.Tensor = None,
+              perm: torch.Tensor = None) -> torch.Tensor:
+    """Asymmetric weights: x fp16 [K] -> y fp16 [N] (M = 1)."""
+    lib = library()
+    N, K, group = _weights(packed, scales)
+    _zeros(zeros, scales)
+    _need(x, "x", torch.float16, 1)
+    if x.shape[0] != K:
+        raise ValueError("x has %d elements, K = %d" % (x.shape[0], K))
+    if y is None:
+        y = torch.empty((N,), dtype=torch.float16, device=x.device)
+    _need(y, "y", torch.float16, 1)
+    if y.shape[0] != N:
+        raise ValueError("y has %d elements, N = %d" % (y.shape[0], N))
+    if perm is not None:
+        _perm(perm, K)
+    st = lib.w4a16_gemv_asym(x.data_ptr(), perm.data_ptr() if perm is not None else None,
+                             packed.data_ptr(), scales.data_ptr(), zeros.data_ptr(), N, K, group,
+                             y.data_ptr(), _stream())
+    _check("w4a16_gemv_asym", st)
+    return y
+
+
+def gemm_asym(X: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,
+              zeros: torch.Tensor, Y: torch.Tensor = None,
+              perm: torch.Tensor = None) -> torch.Tensor:
+    """Asymmetric weights: X fp16 [M, K] -> Y fp16 [M, N] (VALU path)."""
+    lib = library()
+    N, K, group = _weights(packed, scales)
+    _zeros(zeros, scales)
+    _need(X, "X", torch.float16, 2)
+    M = X.shape[0]
+    if X.shape[1] != K:
+        raise ValueError("X has %d columns, K = %d" % (X.shape[1], K))
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float16, device=X.device)
+    _need(Y, "Y", torch.float16, 2)
+    if tuple(Y.shape) != (M, N):
+        raise ValueError("Y shape %s, want %s" % (tuple(Y.shape), (M, N)))
+    if perm is not None:
+        _perm(perm, K)
+    st = lib.w4a16_gemm_asym(X.data_ptr(), M, perm.data_ptr() if perm is not None else None,
+                             packed.data_ptr(), scales.data_ptr(), zeros.data_ptr(), N, K, group,
+                             Y.data_ptr(), _stream())
+    _check("w4a16_gemm_asym", st)
     return Y
 
 
