@@ -80,8 +80,9 @@ def secondary(torch, w4a16, inputs, dev, stream):
     matrix, larger than the Infinity Cache), batched decode M = 1..32 on the
     8B FFN shapes with both kernel families (locates the VALU/MFMA
     crossover), 512-token prefill, the decode GEMV and quantizer at group
-    sizes 32..256, and the decode GEMV with an act-order activation gather.  Each figure is the mean of graph replays over enough
-    weight copies to stream from HBM."""
+    sizes 32..256, the decode GEMV with an act-order activation gather, and
+    the asymmetric-INT4 decode GEMV and quantizer.  Each figure is the mean of
+    graph replays over enough weight copies to stream from HBM."""
     out = {}
 
     def timed(seq_fn, reps=5):
@@ -193,6 +194,31 @@ def secondary(torch, w4a16, inputs, dev, stream):
                                  "perm_GB/s": round(b / (gather * 1e-6) / 1e9, 1)}
         del copies
     out["act_order_m1"] = act
+
+    # asymmetric INT4: M = 1 GEMV (zero points streamed beside the scales)
+    # and the quantizer, against the symmetric GEMV on the same shape
+    asym = {}
+    for (K, N) in [(14336, 4096), (4096, 14336)]:
+        Wd = torch.from_numpy(inputs.weight_skewed(N, K, seed=[10, K, N])).to(dev)
+        pa, sa, za = w4a16.quantize_asym(Wd)
+        qus = timed(lambda: w4a16.quantize_asym(Wd, pa, sa, za))
+        copies = [(pa, sa, za)] + [(pa.clone(), sa.clone(), za.clone()) for _ in range(11)]
+        x = torch.from_numpy(inputs.activation(1, K, seed=[10, K])).to(dev)[0]
+        y = torch.empty((N,), dtype=torch.float16, device=dev)
+        us = timed(lambda: [w4a16.gemv_asym(x, p, s_, z, y=y) for p, s_, z in copies]) \
+            / len(copies)
+        p0, s0 = weights_for(K, N)
+        sym = [(p0, s0)] + [(p0.clone(), s0.clone()) for _ in range(11)]
+        plain = timed(lambda: [w4a16.gemv(x, p, s_, y=y) for p, s_ in sym]) / len(sym)
+        b = gemv_bytes(N, K) + N * (K // 128) * 2
+        qb = N * K * 2 + N * K // 2 + 2 * N * (K // 128) * 2
+        asym["%dx%d" % (K, N)] = {
+            "gemv_us": round(us, 3), "gemv_GB/s": round(b / (us * 1e-6) / 1e9, 1),
+            "gemv_frac_of_hbm_peak": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "symmetric_gemv_us": round(plain, 3),
+            "quantize_us": round(qus, 2), "quantize_GB/s": round(qb / (qus * 1e-6) / 1e9, 1)}
+        del copies, sym, Wd
+    out["asymmetric_m1"] = asym
     quantized.clear()
     return out
 
