@@ -56,9 +56,14 @@ class Oracle:
         lib.oracle_quantize_asym.argtypes = [_p, _i64, _i64, _i64, _p, _p, _p]
         lib.oracle_dequantize_asym.argtypes = [_p, _p, _p, _i64, _i64, _i64, _p]
         lib.oracle_matmul_asym.argtypes = [_p, _i64, _p, _p, _p, _i64, _i64, _i64, _p, _p]
+        lib.oracle_quantize_q4_0.argtypes = [_p, _i64, _i64, _p]
+        lib.oracle_dequantize_q4_0.argtypes = [_p, _i64, _i64, _p]
+        lib.oracle_matmul_q4_0.argtypes = [_p, _i64, _p, _i64, _i64, _p, _p]
         for f in (lib.oracle_quantize, lib.oracle_dequantize, lib.oracle_matmul,
                   lib.oracle_matmul_sampled, lib.oracle_quantize_asym,
-                  lib.oracle_dequantize_asym, lib.oracle_matmul_asym):
+                  lib.oracle_dequantize_asym, lib.oracle_matmul_asym,
+                  lib.oracle_quantize_q4_0, lib.oracle_dequantize_q4_0,
+                  lib.oracle_matmul_q4_0):
             f.restype = ctypes.c_int
         lib.oracle_num_threads.restype = ctypes.c_int
         self.lib = lib
@@ -182,6 +187,42 @@ class Oracle:
                                          N, K, group, _ptr(Y), _ptr(Yabs))
         if rc != 0:
             raise ValueError("oracle_matmul_asym: bad sizes")
+        return Y, Yabs
+
+    # -- Q4_0 blocks -------------------------------------------------------
+    def quantize_q4_0(self, W: np.ndarray) -> np.ndarray:
+        """W fp16 [N, K] -> Q4_0 blocks, uint8 [N, K/32 * 18]."""
+        W = _bits16(W)
+        N, K = W.shape
+        blocks = np.zeros((N, K // 32 * 18), dtype=np.uint8)
+        rc = self.lib.oracle_quantize_q4_0(_ptr(W), N, K, _ptr(blocks))
+        if rc != 0:
+            raise ValueError("oracle_quantize_q4_0: bad sizes N=%d K=%d" % (N, K))
+        return blocks
+
+    def dequantize_q4_0(self, blocks: np.ndarray, K: int) -> np.ndarray:
+        blocks = np.ascontiguousarray(blocks, dtype=np.uint8)
+        N = blocks.shape[0]
+        out = np.empty((N, K), dtype=np.float64)
+        rc = self.lib.oracle_dequantize_q4_0(_ptr(blocks), N, K, _ptr(out))
+        if rc != 0:
+            raise ValueError("oracle_dequantize_q4_0: bad sizes")
+        return out
+
+    def matmul_q4_0(self, X: np.ndarray, blocks: np.ndarray):
+        X = _bits16(X)
+        if X.ndim == 1:
+            X = X.reshape(1, -1)
+        blocks = np.ascontiguousarray(blocks, dtype=np.uint8)
+        M, K = X.shape
+        N = blocks.shape[0]
+        if blocks.shape[1] != K // 32 * 18:
+            raise ValueError("K mismatch")
+        Y = np.empty((M, N), dtype=np.float64)
+        Yabs = np.empty((M, N), dtype=np.float64)
+        rc = self.lib.oracle_matmul_q4_0(_ptr(X), M, _ptr(blocks), N, K, _ptr(Y), _ptr(Yabs))
+        if rc != 0:
+            raise ValueError("oracle_matmul_q4_0: bad sizes")
         return Y, Yabs
 
     def num_threads(self) -> int:

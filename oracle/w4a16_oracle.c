@@ -31,7 +31,9 @@
  *   - eight nibbles per little-endian uint32, element 8j+i in bits 4i..4i+3;
  *   - asymmetric INT4 (see oracle_quantize_asym): the same rounding, the
  *     scale stored as fp16 and z taken against it, z stored as int16, and
- *     a zero-scale group stored as s = 0, z = 0, q = 0.
+ *     a zero-scale group stored as s = 0, z = 0, q = 0;
+ *   - Q4_0 blocks (see oracle_quantize_q4_0): scale d = absmax / 7 as for
+ *     the symmetric form, and the dequantizer's adjacent-pair nibble order.
  *
  * Build: cc -O2 -fno-fast-math -ffp-contract=off -fopenmp -shared -fPIC.
  */
@@ -316,6 +318,81 @@ int oracle_matmul_asym(const uint16_t* X, int64_t M, const uint32_t* packed,
             }
             Y[m * N + n] = sum;
             Yabs[m * N + n] = sum_abs;
+        }
+    return 0;
+}
+
+/* ----------------------------------------------------- Q4_0 blocks */
+
+/* Q4_0 block layout ([QUANT] GGUF section: type table, Q4_0 = 32 elements
+ * per block, 18 bytes, symmetric with a per-block scale; the section's
+ * Q4_0 dequantizer): per row, K/32 consecutive blocks of
+ *   bytes 0-1   d, the fp16 scale, little-endian
+ *   bytes 2-17  byte 2+i holds element 2i in its low nibble and element
+ *               2i+1 in its high nibble, each as q + 8
+ * with the symmetric quantizer of this file on groups of 32 (d = RNE(absmax
+ * / 7), q = clamp(RNE(w/d), -8, 7)).  Dequantized: d * (nibble - 8). */
+#define Q4_0_BLOCK 32
+#define Q4_0_BYTES 18
+
+int oracle_quantize_q4_0(const uint16_t* W, int64_t N, int64_t K, uint8_t* blocks)
+{
+    if (N < 0 || K < 0 || K % Q4_0_BLOCK != 0) return -1;
+    if (fegetround() != FE_TONEAREST) return -1;
+    const int64_t nb = K / Q4_0_BLOCK;
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; n++) {
+        int8_t q[Q4_0_BLOCK];
+        for (int64_t b = 0; b < nb; b++) {
+            uint16_t d;
+            quantize_group(W + n * K + b * Q4_0_BLOCK, Q4_0_BLOCK, &d, q);
+            uint8_t* blk = blocks + (n * nb + b) * Q4_0_BYTES;
+            blk[0] = (uint8_t)(d & 0xFF);
+            blk[1] = (uint8_t)(d >> 8);
+            for (int i = 0; i < Q4_0_BLOCK / 2; i++)
+                blk[2 + i] = (uint8_t)(((q[2 * i] + 8) & 0xF) | (((q[2 * i + 1] + 8) & 0xF) << 4));
+        }
+    }
+    return 0;
+}
+
+/* Element k of row n of a Q4_0 matrix, dequantized (exact in binary64). */
+static double q4_0_weight(const uint8_t* blocks, int64_t nb, int64_t n, int64_t k)
+{
+    const uint8_t* blk = blocks + (n * nb + k / Q4_0_BLOCK) * Q4_0_BYTES;
+    const uint16_t d = (uint16_t)(blk[0] | (blk[1] << 8));
+    const int j = (int)(k % Q4_0_BLOCK);
+    const uint8_t byte = blk[2 + j / 2];
+    const int nib = (j % 2 == 0) ? (byte & 0xF) : (byte >> 4);
+    return oracle_f64_from_f16(d) * (double)(nib - 8);
+}
+
+int oracle_dequantize_q4_0(const uint8_t* blocks, int64_t N, int64_t K, double* What)
+{
+    if (N < 0 || K < 0 || K % Q4_0_BLOCK != 0) return -1;
+    const int64_t nb = K / Q4_0_BLOCK;
+    for (int64_t n = 0; n < N; n++)
+        for (int64_t k = 0; k < K; k++) What[n * K + k] = q4_0_weight(blocks, nb, n, k);
+    return 0;
+}
+
+/* Y = X·Ŵᵀ and Yabs = sum |X Ŵ| with Ŵ read from Q4_0 blocks (binary64). */
+int oracle_matmul_q4_0(const uint16_t* X, int64_t M, const uint8_t* blocks, int64_t N, int64_t K,
+                       double* Y, double* Yabs)
+{
+    if (M < 0 || N < 0 || K < 0 || K % Q4_0_BLOCK != 0) return -1;
+    const int64_t nb = K / Q4_0_BLOCK;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t m = 0; m < M; m++)
+        for (int64_t n = 0; n < N; n++) {
+            double total = 0.0, total_abs = 0.0;
+            for (int64_t k = 0; k < K; k++) {
+                const double term = oracle_f64_from_f16(X[m * K + k]) * q4_0_weight(blocks, nb, n, k);
+                total += term;
+                total_abs += fabs(term);
+            }
+            Y[m * N + n] = total;
+            Yabs[m * N + n] = total_abs;
         }
     return 0;
 }

@@ -23,6 +23,9 @@ What each pin compares against:
                           brute-force nearest level s (q - z), error bound,
                           z in [0, 15] for two-signed groups, a hand-worked
                           group ([QUANT] sub-section 2)
+  * Q4_0 blocks           18 bytes per 32 elements, the GGUF dequantizer's
+                          byte layout decoded independently, exact block
+                          scales and nearest codes, a hand-worked block
 """
 from __future__ import annotations
 
@@ -519,9 +522,72 @@ def pin_asymmetric(o) -> list:
     return fails
 
 
+def pin_q4_0(o) -> list:
+    """Q4_0 blocks ([QUANT] GGUF section: the type table gives Q4_0 as 32
+    elements in 18 bytes, symmetric with a per-block scale; the section's
+    Q4_0 dequantizer reads d as little-endian fp16 from the first two bytes
+    and element 2i / 2i+1 from the low / high nibble of byte 2+i, minus 8).
+    Pinned by: 18 bytes per 32 elements; a numpy decode of the bytes as the
+    dequantizer describes them equals d * (brute-force nearest code) with
+    d the exact RNE(absmax/7) of each 32-element block; a hand-worked block;
+    the oracle's dequantizer and product against the exact values."""
+    fails = []
+    N, K = 9, 512
+    W = inputs.weight(N, K, seed=[94, 0, 0])
+    W[0, :32] = np.float16(0)                                   # all-zero block
+    W[1, 32:64] *= np.float16(1e-4)                              # tiny scale
+    blocks = o.quantize_q4_0(W)
+    if blocks.shape != (N, K // 32 * 18):
+        return ["q4_0: shape %s, want %s" % (blocks.shape, (N, K // 32 * 18))]
+    blk = blocks.reshape(N, K // 32, 18)
+    d_bits = blk[:, :, 0].astype(np.uint16) | (blk[:, :, 1].astype(np.uint16) << 8)
+    a = np.abs(W.astype(np.float64)).reshape(N, K // 32, 32).max(axis=2)
+    want_d = np.array([[exact_rne_f16(Fraction(float(v)) / 7) for v in row] for row in a],
+                      dtype=np.uint16)
+    if not (d_bits == want_d).all():
+        fails.append("q4_0: %d block scales differ from exact RNE(absmax/7)"
+                     % (d_bits != want_d).sum())
+    q = blk[:, :, 2:]
+    codes = np.empty((N, K // 32, 32), dtype=np.int64)
+    codes[:, :, 0::2] = (q & 0xF).astype(np.int64) - 8
+    codes[:, :, 1::2] = (q >> 4).astype(np.int64) - 8
+    codes = codes.reshape(N, K)
+    want = brute_force_codes(W, want_d, group=32)
+    if not (codes == want).all():
+        fails.append("q4_0: %d decoded codes differ from the nearest code" % (codes != want).sum())
+    d64 = np.repeat(d_bits.view(np.float16).astype(np.float64), 32, axis=1)
+    deq = o.dequantize_q4_0(blocks, K)
+    if not (deq == d64 * codes).all():
+        fails.append("q4_0: dequantizer differs from d * (nibble - 8)")
+    # hand-worked block: absmax 3.5 -> d = 0.5 (0x3800); 3.5 -> 7 (nibble 15),
+    # -3.5 -> -7 (1): byte 0x1F; 1.25 and 0.75 -> round(2.5), round(1.5) = 2
+    # (10, 10): 0xAA; zeros -> 8: 0x88; -1.75 -> round(-3.5) = -4 (4) low,
+    # -0.25 -> round(-0.5) = 0 (8) high: 0x84
+    hw = np.zeros((1, 32), dtype=np.float16)
+    hw[0, [0, 1, 2, 3, 30, 31]] = [3.5, -3.5, 1.25, 0.75, -1.75, -0.25]
+    want_b = [0x00, 0x38, 0x1F, 0xAA] + [0x88] * 13 + [0x84]
+    got_b = [int(v) for v in o.quantize_q4_0(hw)[0]]
+    if got_b != want_b:
+        fails.append("q4_0 hand-worked block: %s, want %s" % (got_b, want_b))
+    # a tiny product against the exact rational sum
+    M, n_, k_ = 2, 3, 96
+    Wt, Xt = inputs.weight_and_activation(n_, k_, M, seed=[94, 1])
+    bt = o.quantize_q4_0(Wt)
+    Y, _ = o.matmul_q4_0(Xt, bt)
+    dt = o.dequantize_q4_0(bt, k_)
+    for m in range(M):
+        for n in range(n_):
+            terms = [Fraction(float(Xt[m, k])) * Fraction(float(dt[n, k])) for k in range(k_)]
+            exact = sum(terms, Fraction(0))
+            bound = k_ * 2.0 ** -53 * float(sum((abs(t) for t in terms), Fraction(0)))
+            if abs(Fraction(Y[m, n]) - exact) > Fraction(bound):
+                fails.append("q4_0: matmul (%d,%d) off the exact sum" % (m, n))
+    return fails
+
+
 ALL_PINS = [pin_f16_codec, pin_scale_every_fp16, pin_hand_worked, pin_codes_nearest,
             pin_invariants, pin_matmul_exact, pin_group_sizes, pin_act_order,
-            pin_asymmetric]
+            pin_asymmetric, pin_q4_0]
 
 
 def run_all(o) -> dict:

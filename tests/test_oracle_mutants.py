@@ -55,6 +55,16 @@ MUTANTS = [
      "                                       zeros[n * ng + k / group]);",
      "What[n * K + k] = oracle_f64_from_f16(scales[n * ng + k / group]) *\n"
      "                              (double)(nibble_at(packed + n * (K / 8), k));"),
+    ("q4_0: nibbles of a byte swapped",
+     "blk[2 + i] = (uint8_t)(((q[2 * i] + 8) & 0xF) | (((q[2 * i + 1] + 8) & 0xF) << 4));",
+     "blk[2 + i] = (uint8_t)(((q[2 * i + 1] + 8) & 0xF) | (((q[2 * i] + 8) & 0xF) << 4));"),
+    ("q4_0: scale big-endian", "blk[0] = (uint8_t)(d & 0xFF);\n            blk[1] = (uint8_t)(d >> 8);",
+     "blk[1] = (uint8_t)(d & 0xFF);\n            blk[0] = (uint8_t)(d >> 8);"),
+    ("q4_0: dequantizer reads the high nibble first",
+     "const int nib = (j % 2 == 0) ? (byte & 0xF) : (byte >> 4);",
+     "const int nib = (j % 2 == 0) ? (byte >> 4) : (byte & 0xF);"),
+    ("q4_0: dequantizer offset 7", "return oracle_f64_from_f16(d) * (double)(nib - 8);",
+     "return oracle_f64_from_f16(d) * (double)(nib - 7);"),
     ("asym: matmul zero of the next group", "zeros[n * ng + k / group]);\n                double prod",
      "zeros[n * ng + (k / group + 1) % ng]);\n                double prod"),
 ]
