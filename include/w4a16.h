@@ -193,6 +193,37 @@ int w4a16_gemm_asym(const uint16_t* X, int64_t M, const int32_t* perm, const uin
                     const uint16_t* scales, const int16_t* zeros, int64_t N, int64_t K,
                     int64_t group, uint16_t* Y, void* stream);
 
+/* ---- Q4_0 block layout ([QUANT] GGUF section: the type table's Q4_0
+ * entry, 32 elements in 18 bytes, symmetric with one scale per block; the
+ * section's Q4_0 dequantizer for the byte order; its llama.cpp part credits
+ * block-major layouts with 20-30 % more memory-bound throughput on CPUs).
+ * Each row of W is K/32 consecutive blocks of 18 bytes:
+ *     bytes 0-1   d = fp16 RNE(absmax / 7) of the block's 32 elements,
+ *                 little-endian
+ *     byte 2+i    element 2i in bits 0-3, element 2i+1 in bits 4-7, each
+ *                 as q + 8, q = clamp(RNE(w / d), -8, 7)
+ * i.e. the symmetric quantizer at group 32, with each group's scale placed
+ * in front of its 16 code bytes instead of in a separate array.
+ * Ŵ[n, k] = d * q.  The blocks take N*(K/32)*18 bytes; the buffer must
+ * hold w4a16_q4_0_bytes(N, K) bytes, that size rounded up to a multiple of
+ * 16 (0 for bad sizes): the linear layer reads the padding with its
+ * 16-byte loads and ignores it; the quantizer never writes it.
+ *   w4a16_quantize_q4_0: W fp16 [N, K] (16-byte aligned) -> blocks (16-byte
+ *                        aligned, not overlapping W)
+ *   w4a16_gemv_q4_0:     y[n] = sum_k x[k] * Ŵ[n,k]
+ *   w4a16_gemm_q4_0:     Y = X·Ŵᵀ, any M (VALU path; X rows in slices that
+ *                        fit the staged-activation budget)
+ * K % 128 == 0 as everywhere (else W4A16_ERR_SHAPE); the linear layer also
+ * needs K <= 32768 (x is staged whole in LDS), else W4A16_ERR_INVALID_ARG.
+ * X, x 16-byte aligned; Y, y 2-byte aligned and not overlapping X or the
+ * blocks buffer. */
+size_t w4a16_q4_0_bytes(int64_t N, int64_t K);
+int w4a16_quantize_q4_0(const uint16_t* W, int64_t N, int64_t K, uint8_t* blocks, void* stream);
+int w4a16_gemv_q4_0(const uint16_t* x, const uint8_t* blocks, int64_t N, int64_t K, uint16_t* y,
+                    void* stream);
+int w4a16_gemm_q4_0(const uint16_t* X, int64_t M, const uint8_t* blocks, int64_t N, int64_t K,
+                    uint16_t* Y, void* stream);
+
 /* ---- Dependent decode sequence ([BENCH] §二: every decode step streams
  * the layers' matrices one after another, each fed by the one before).
  * Runs stages[0..count) as if w4a16_gemv were called on each in order on

@@ -36,7 +36,8 @@ def test_header_declares_the_boundary():
                "w4a16_valu_max_m", "w4a16_quantize_g", "w4a16_gemv_g", "w4a16_gemm_g",
                "w4a16_scales_bytes_g", "w4a16_quantize_perm", "w4a16_gemv_perm",
                "w4a16_gemm_perm", "w4a16_quantize_asym", "w4a16_gemv_asym",
-               "w4a16_gemm_asym"]:
+               "w4a16_gemm_asym", "w4a16_q4_0_bytes", "w4a16_quantize_q4_0",
+               "w4a16_gemv_q4_0", "w4a16_gemm_q4_0"]:
         assert fn in names
 
 
@@ -218,6 +219,32 @@ def test_asymmetric_validation(lib):
                         torch.zeros(4, 1, dtype=torch.int32))       # zeros must be int16
 
 
+def test_q4_0_validation(lib):
+    """Q4_0 entry points: sizes (18 bytes per 32 elements), alignment,
+    overlap, the K limit of the staged-activation GEMV."""
+    A, B, D = FAKE, FAKE * 4, FAKE * 12
+    assert lib.w4a16_q4_0_bytes(4096, 4096) == 4096 * 128 * 18
+    assert lib.w4a16_q4_0_bytes(1, 128) == 80                        # 72 rounded up to 16
+    assert lib.w4a16_q4_0_bytes(3, 100) == 0 and lib.w4a16_q4_0_bytes(-1, 128) == 0
+    q, gv, gm = lib.w4a16_quantize_q4_0, lib.w4a16_gemv_q4_0, lib.w4a16_gemm_q4_0
+    assert q(A, 4, 100, B, None) == SHAPE
+    assert q(A, 4, 128, None, None) == INVALID
+    assert q(A, 4, 128, B + 2, None) == MISALIGNED
+    assert q(A, 4, 128, A + 64, None) == INVALID                     # blocks overlap W
+    assert q(None, 0, 128, None, None) == OK
+    assert gv(A, B, 16, 128, None, None) == INVALID
+    assert gv(A, B + 8, 16, 128, D, None) == MISALIGNED
+    assert gv(A, B, 16, 128, B + 2, None) == INVALID                 # y overlaps blocks
+    assert gv(A, B, 16, 32768 + 128, D, None) == INVALID             # K beyond the LDS budget
+    assert gv(A, B, 16, 200, D, None) == SHAPE
+    assert gm(A, -1, B, 16, 128, D, None) == INVALID
+    assert gm(None, 0, None, 16, 128, None, None) == OK
+    import torch
+    with pytest.raises(ValueError):
+        w4a16.gemv_q4_0(torch.zeros(128, dtype=torch.float16),
+                        torch.zeros(4, 70, dtype=torch.uint8))       # not whole blocks
+
+
 @pytest.mark.skipif(__import__("torch").cuda.device_count() > 0,
                     reason="with a GPU present valid arguments would launch")
 def test_valid_arguments_without_device_report_device_error(lib):
@@ -229,6 +256,8 @@ def test_valid_arguments_without_device_report_device_error(lib):
     assert lib.w4a16_gemv_perm(A, FAKE * 16, B, C, 16, 128, D, None) == DEVICE
     assert lib.w4a16_quantize_asym(A, None, 4, 128, 128, B, C, FAKE * 20, None) == DEVICE
     assert lib.w4a16_gemm_asym(A, 2, None, B, C, FAKE * 20, 16, 128, 64, D, None) == DEVICE
+    assert lib.w4a16_quantize_q4_0(A, 4, 128, B, None) == DEVICE
+    assert lib.w4a16_gemm_q4_0(A, 3, B, 16, 256, D, None) == DEVICE
 
 
 def test_binding_rejects_bad_tensors():

@@ -745,3 +745,119 @@ def test_asym_empty_and_k_zero(w4):
                      torch.empty((5, 0), dtype=torch.int16, device="cuda"))
     torch.cuda.synchronize()
     assert Y.shape == (3, 5) and (Y.cpu().numpy() == 0).all()
+
+
+# ------------------------------------------------------------ Q4_0 blocks
+
+Q40_QUANT_SHAPES = [(1, 128), (37, 384), (129, 1152), (4096, 4096), (300, 14336)]
+
+
+@pytest.mark.parametrize("N,K", Q40_QUANT_SHAPES)
+def test_quantize_q4_0_bit_exact(w4, orc, N, K):
+    """w4a16_quantize_q4_0 against the oracle byte for byte (all-zero and
+    tiny-scale blocks planted), and against the GPU's own group-32 split
+    layout: each block is that layout's scale followed by its 16 code bytes."""
+    say("quantize q4_0 N=%d K=%d" % (N, K))
+    W = inputs.weight(N, K, seed=[51, N, K])
+    W[0, :32] = np.float16(0)
+    W[N - 1, K - 32:] *= np.float16(1e-4)
+    bg = w4.quantize_q4_0(dev(W))
+    pg, sg = w4.quantize(dev(W), group=32)
+    torch.cuda.synchronize()
+    got = bg.cpu().numpy()
+    want = orc.quantize_q4_0(W)
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, "%d bytes differ, first at %s" % (len(bad), bad[0])
+    split = np.concatenate([sg.cpu().numpy().view(np.uint8).reshape(N, K // 32, 2),
+                            pg.cpu().numpy().view(np.uint8).reshape(N, K // 32, 16)], axis=2)
+    assert (split.reshape(N, -1) == got).all()
+
+
+def q4_0_to_dev(w4, blocks: np.ndarray):
+    """Oracle blocks into a device buffer with the library's 16-byte padding."""
+    N = blocks.shape[0]
+    out = w4.q4_0_blocks(N, blocks.shape[1] // 18 * 32)
+    out.copy_(torch.from_numpy(np.ascontiguousarray(blocks)))
+    return out
+
+
+def check_linear_q4_0(w4, orc, M, N, K, seed):
+    say("linear q4_0 M=%d N=%d K=%d" % (M, N, K))
+    W = inputs.weight(N, K, seed=[52] + list(seed))
+    blocks = orc.quantize_q4_0(W)
+    X = inputs.activation(M, K, seed=[53] + list(seed))
+    bd = q4_0_to_dev(w4, blocks)
+    if M == 1:
+        Y = w4.gemv_q4_0(dev(X)[0], bd).cpu().numpy()[None]
+    else:
+        Y = w4.gemm_q4_0(dev(X), bd).cpu().numpy()
+    torch.cuda.synchronize()
+    assert Y.shape == (M, N)
+    Yref, Yabs = orc.matmul_q4_0(X, blocks)
+    tol = oracle.tolerance(Yref, Yabs)
+    err = np.abs(Y.astype(np.float64) - Yref)
+    bad = np.argwhere(~(err <= tol))
+    assert bad.size == 0, "%d outputs out of tolerance, first %s: got %r want %r tol %r" % (
+        len(bad), bad[0], Y[tuple(bad[0])], Yref[tuple(bad[0])], tol[tuple(bad[0])])
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 5, 8, 13])
+@pytest.mark.parametrize("N,K", [(1, 128), (7, 256), (37, 384), (300, 1152), (1001, 4096),
+                                 (515, 3584), (64, 14336), (33, 32768)])
+def test_linear_q4_0(w4, orc, M, N, K):
+    """Rows of 18-byte blocks start at every 2-byte offset mod 16 (K = 384:
+    216-byte rows), partial last wave steps (K = 384, 1152, 3584), odd N
+    (a row group with one row), K up to the 32768 limit, M in slices."""
+    check_linear_q4_0(w4, orc, M, N, K, [M, N, K])
+
+
+@pytest.mark.parametrize("name,K,N", [("llama gate", 4096, 14336), ("llama down", 14336, 4096),
+                                      ("qwen gate", 3584, 18944), ("qwen down", 18944, 3584)])
+def test_gemv_q4_0_layer_shapes(w4, orc, name, K, N):
+    check_linear_q4_0(w4, orc, 1, N, K, [7, N, K])
+
+
+def test_q4_0_one_hot_exact(w4, orc):
+    """One-hot x selects fp16(d * q) bit-exactly: block scale and nibble order."""
+    N, K = 40, 1024
+    W = inputs.weight(N, K, seed=[54])
+    blocks = orc.quantize_q4_0(W)
+    deq = orc.dequantize_q4_0(blocks, K)
+    ks = np.arange(0, K, 3)
+    X = np.zeros((len(ks), K), dtype=np.float16)
+    X[np.arange(len(ks)), ks] = np.float16(1.0)
+    say("q4_0 one-hot")
+    bd = q4_0_to_dev(w4, blocks)
+    for m0 in range(0, len(ks), 8):
+        Y = w4.gemm_q4_0(dev(X[m0:m0 + 8]), bd).cpu().numpy()
+        torch.cuda.synchronize()
+        want = deq[:, ks[m0:m0 + 8]].T.astype(np.float16)
+        assert (Y.view(np.uint16) == want.view(np.uint16)).all()
+
+
+def test_q4_0_outputs_stay_inside_their_buffer(w4, orc):
+    N, K, M = 333, 1152, 3
+    W, X = inputs.weight_and_activation(N, K, M, seed=[55])
+    blocks = orc.quantize_q4_0(W)
+    pad = 4096
+    buf = torch.full((pad + M * N + pad,), float("nan"), dtype=torch.float16, device="cuda")
+    Y = buf[pad:pad + M * N].view(M, N)
+    say("q4_0 canary")
+    w4.gemm_q4_0(dev(X), q4_0_to_dev(w4, blocks), Y=Y)
+    b = buf.cpu().numpy().view(np.uint16)
+    nan_bits = np.float16("nan").view(np.uint16)
+    assert (b[:pad] == nan_bits).all() and (b[pad + M * N:] == nan_bits).all()
+    assert not np.isnan(buf[pad:pad + M * N].cpu().numpy()).any()
+
+
+def test_q4_0_empty_and_k_zero(w4):
+    say("q4_0 empty / K = 0")
+    b = w4.quantize_q4_0(torch.empty((0, 256), dtype=torch.float16, device="cuda"))
+    assert b.shape == (0, 144)
+    Y = w4.gemm_q4_0(torch.empty((3, 0), dtype=torch.float16, device="cuda"),
+                     torch.empty((5, 0), dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    assert Y.shape == (3, 5) and (Y.cpu().numpy() == 0).all()
+    with pytest.raises(ValueError):                  # storage without the padding
+        w4.gemv_q4_0(torch.zeros(128, dtype=torch.float16, device="cuda"),
+                     torch.zeros((1, 72), dtype=torch.uint8, device="cuda"))

@@ -156,9 +156,64 @@ int quantize(const uint16_t* W, int64_t N, int64_t K, int64_t group, uint32_t* p
                                             with_perm ? perm : nullptr, asym ? zeros : nullptr));
 }
 
+// Q4_0 buffer: N rows of K/32 blocks of 18 bytes, rounded up to 16 bytes.
+size_t q4_0_bytes(int64_t N, int64_t K) {
+    return ((size_t)N * (size_t)(K / 32) * 18 + 15) & ~(size_t)15;
+}
+
+int linear_q4_0(const uint16_t* X, int64_t M, const uint8_t* blocks, int64_t N, int64_t K,
+                uint16_t* Y, void* stream) {
+    int st = check_sizes(M, N, K);
+    if (st != W4A16_OK) return st;
+    if (K > w4a16::kQ40MaxK) return W4A16_ERR_INVALID_ARG;
+    if (M == 0 || N == 0) return W4A16_OK;
+    if (!Y || (K > 0 && (!X || !blocks))) return W4A16_ERR_INVALID_ARG;
+    if (!aligned(X, 16) || !aligned(blocks, 16) || !aligned(Y, 2)) return W4A16_ERR_MISALIGNED;
+    const size_t y_bytes = (size_t)M * N * 2;
+    if (overlap(Y, y_bytes, X, (size_t)M * K * 2) || overlap(Y, y_bytes, blocks, q4_0_bytes(N, K)))
+        return W4A16_ERR_INVALID_ARG;
+    int num_cu = 0;
+    st = current_device(&num_cu);
+    if (st != W4A16_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // K == 0: the split-layout kernel writes the zeros (it reads no weights)
+    if (K == 0)
+        return status_of(w4a16::launch_gemv_valu(X, M, nullptr, nullptr, N, 0, Y, s, num_cu));
+    return status_of(w4a16::launch_gemv_q4_0(X, M, blocks, N, K, Y, s, num_cu));
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t w4a16_q4_0_bytes(int64_t N, int64_t K) {
+    if (check_sizes(0, N, K) != W4A16_OK) return 0;
+    return q4_0_bytes(N, K);
+}
+
+int w4a16_quantize_q4_0(const uint16_t* W, int64_t N, int64_t K, uint8_t* blocks, void* stream) {
+    int st = check_sizes(0, N, K);
+    if (st != W4A16_OK) return st;
+    if (N == 0 || K == 0) return W4A16_OK;
+    if (!W || !blocks) return W4A16_ERR_INVALID_ARG;
+    if (!aligned(W, 16) || !aligned(blocks, 16)) return W4A16_ERR_MISALIGNED;
+    if (overlap(blocks, q4_0_bytes(N, K), W, (size_t)N * K * 2)) return W4A16_ERR_INVALID_ARG;
+    int num_cu = 0;
+    st = current_device(&num_cu);
+    if (st != W4A16_OK) return st;
+    return status_of(w4a16::launch_quantize_q4_0(W, N, K, blocks, static_cast<hipStream_t>(stream)));
+}
+
+int w4a16_gemv_q4_0(const uint16_t* x, const uint8_t* blocks, int64_t N, int64_t K, uint16_t* y,
+                    void* stream) {
+    return linear_q4_0(x, 1, blocks, N, K, y, stream);
+}
+
+int w4a16_gemm_q4_0(const uint16_t* X, int64_t M, const uint8_t* blocks, int64_t N, int64_t K,
+                    uint16_t* Y, void* stream) {
+    return linear_q4_0(X, M, blocks, N, K, Y, stream);
+}
+
 
 size_t w4a16_packed_bytes(int64_t N, int64_t K) {
     if (check_sizes(0, N, K) != W4A16_OK) return 0;

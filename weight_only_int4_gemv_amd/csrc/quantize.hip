@@ -259,6 +259,58 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint4* __restrict__
     }
 }
 
+// Q4_0 blocks ([QUANT] GGUF section, Q4_0: 32 elements in 18 bytes, the
+// fp16 scale d then 16 code bytes with element 2i in the low nibble of byte
+// 2+i): the symmetric quantizer on groups of 32 (four lanes per block, as
+// for G = 32), each lane storing its packed word at byte 2 + 4*lane of the
+// block as two 16-bit halves (blocks are only 2-byte aligned) and the
+// block's first lane storing d.
+template <int U>
+__global__ __launch_bounds__(256) void quantize_q4_0_kernel(const uint4* __restrict__ W,
+                                                            uint16_t* __restrict__ blocks,
+                                                            int64_t total_blocks) {
+    constexpr int LG = 4;
+    const int lg = threadIdx.x & (LG - 1);
+    const int64_t stride = (int64_t)gridDim.x * (blockDim.x / LG);
+    typedef unsigned v4u __attribute__((ext_vector_type(4)));
+    const v4u* Wv = reinterpret_cast<const v4u*>(W);
+    for (int64_t g = (int64_t)blockIdx.x * (blockDim.x / LG) + (threadIdx.x / LG);
+         g < total_blocks; g += U * stride) {
+        v4u a[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t gu = g + u * stride;
+            a[u] = gu < total_blocks ? __builtin_nontemporal_load(Wv + gu * LG + lg)
+                                     : (v4u){0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t gu = g + u * stride;
+            if (gu < total_blocks) {
+                uint16_t d;
+                const uint32_t word = quantize8<LG>(make_uint4(a[u].x, a[u].y, a[u].z, a[u].w), d);
+                uint16_t* blk = blocks + gu * 9;             // 18 bytes = 9 halves
+                blk[1 + 2 * lg] = (uint16_t)(word & 0xFFFFu);
+                blk[2 + 2 * lg] = (uint16_t)(word >> 16);
+                if (lg == 0) blk[0] = d;
+            }
+        }
+    }
+}
+
+hipError_t launch_quantize_q4_0(const uint16_t* W, int64_t N, int64_t K, uint8_t* blocks,
+                                hipStream_t stream) {
+    const int64_t total = N * (K / 32);
+    if (total == 0) return hipSuccess;
+    constexpr int U = 2, per_block = 256 / 4;
+    int64_t grid = (total + per_block * U - 1) / (per_block * U);
+    if (grid > 65536) grid = 65536;
+    hipLaunchKernelGGL((quantize_q4_0_kernel<U>), dim3((unsigned)grid), dim3(256), 0, stream,
+                       reinterpret_cast<const uint4*>(W), reinterpret_cast<uint16_t*>(blocks),
+                       total);
+    return hipGetLastError();
+}
+
 template <int LG, int U>
 hipError_t launch_quantize_t(const uint16_t* W, int64_t groups, int64_t K, const int* perm,
                              uint32_t* packed, uint16_t* scales, int16_t* zeros,

@@ -15,6 +15,15 @@ hipError_t launch_quantize(const uint16_t* W, int64_t N, int64_t K, int64_t grou
                            uint32_t* packed, uint16_t* scales, hipStream_t stream,
                            const int* perm = nullptr, int16_t* zeros = nullptr);
 
+// Q4_0 blocks: N rows of K/32 blocks of 18 bytes (fp16 d, then 16 code
+// bytes) in a buffer rounded up to 16 bytes; `blocks` 16-byte aligned.  The
+// GEMV stages x whole in LDS: 0 < K <= kQ40MaxK.
+constexpr int64_t kQ40MaxK = 32768;
+hipError_t launch_quantize_q4_0(const uint16_t* W, int64_t N, int64_t K, uint8_t* blocks,
+                                hipStream_t stream);
+hipError_t launch_gemv_q4_0(const uint16_t* X, int64_t M, const uint8_t* blocks, int64_t N,
+                            int64_t K, uint16_t* Y, hipStream_t stream, int num_cu);
+
 // VALU dot-product path, any M (M > 8 runs in slices of 8 rows).  gshift:
 // log2(group / 32), one scale per 2^gshift 32-code chunks (2 = group 128).
 // perm (device int32 [K], 16-byte aligned, or NULL): the weight's columns

@@ -74,6 +74,13 @@ def library() -> ctypes.CDLL:
         lib.w4a16_quantize_asym.argtypes = [_p, _p, _i64, _i64, _i64, _p, _p, _p, _p]
         lib.w4a16_gemv_asym.argtypes = [_p, _p, _p, _p, _p, _i64, _i64, _i64, _p, _p]
         lib.w4a16_gemm_asym.argtypes = [_p, _i64, _p, _p, _p, _p, _i64, _i64, _i64, _p, _p]
+        lib.w4a16_q4_0_bytes.argtypes = [_i64, _i64]
+        lib.w4a16_q4_0_bytes.restype = ctypes.c_size_t
+        lib.w4a16_quantize_q4_0.argtypes = [_p, _i64, _i64, _p, _p]
+        lib.w4a16_gemv_q4_0.argtypes = [_p, _p, _i64, _i64, _p, _p]
+        lib.w4a16_gemm_q4_0.argtypes = [_p, _i64, _p, _i64, _i64, _p, _p]
+        for f in (lib.w4a16_quantize_q4_0, lib.w4a16_gemv_q4_0, lib.w4a16_gemm_q4_0):
+            f.restype = ctypes.c_int
         for f in (lib.w4a16_quantize, lib.w4a16_gemv, lib.w4a16_gemm, lib.w4a16_gemm_ex,
                   lib.w4a16_quantize_g, lib.w4a16_gemv_g, lib.w4a16_gemm_g,
                   lib.w4a16_quantize_perm, lib.w4a16_gemv_perm, lib.w4a16_gemm_perm,
@@ -339,6 +346,88 @@ def gemm_asym(X: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,
                              packed.data_ptr(), scales.data_ptr(), zeros.data_ptr(), N, K, group,
                              Y.data_ptr(), _stream())
     _check("w4a16_gemm_asym", st)
+    return Y
+
+
+Q4_0_BLOCK_BYTES = 18      # fp16 d + 16 code bytes per 32 elements
+
+
+def q4_0_blocks(N: int, K: int, device="cuda") -> torch.Tensor:
+    """An uninitialised Q4_0 buffer: a uint8 [N, K/32 * 18] view of storage
+    rounded up to 16 bytes (the padding the library's 16-byte loads read)."""
+    nbytes = N * (K // 32) * Q4_0_BLOCK_BYTES
+    flat = torch.empty(((nbytes + 15) // 16 * 16,), dtype=torch.uint8, device=device)
+    return flat[:nbytes].view(N, K // 32 * Q4_0_BLOCK_BYTES)
+
+
+def _q4_0_storage(blocks: torch.Tensor) -> None:
+    need = (blocks.numel() + 15) // 16 * 16
+    have = blocks.untyped_storage().nbytes() - blocks.storage_offset()
+    if have < need:
+        raise ValueError("the Q4_0 buffer needs %d bytes of storage (blocks rounded up to 16), "
+                         "has %d; allocate it with q4_0_blocks()" % (need, have))
+
+
+def quantize_q4_0(W: torch.Tensor, blocks: torch.Tensor = None) -> torch.Tensor:
+    """W fp16 [N, K] -> Q4_0 blocks, uint8 [N, K/32 * 18] (see q4_0_blocks)."""
+    lib = library()
+    _need(W, "W", torch.float16, 2)
+    N, K = W.shape
+    if K % W4A16_GROUP:
+        raise ValueError("K = %d is not a multiple of %d" % (K, W4A16_GROUP))
+    if blocks is None:
+        blocks = q4_0_blocks(N, K, device=W.device)
+    _need(blocks, "blocks", torch.uint8, 2)
+    if tuple(blocks.shape) != (N, K // 32 * Q4_0_BLOCK_BYTES):
+        raise ValueError("blocks shape %s, want %s"
+                         % (tuple(blocks.shape), (N, K // 32 * Q4_0_BLOCK_BYTES)))
+    _q4_0_storage(blocks)
+    _check("w4a16_quantize_q4_0",
+           lib.w4a16_quantize_q4_0(W.data_ptr(), N, K, blocks.data_ptr(), _stream()))
+    return blocks
+
+
+def _q4_0_shape(blocks: torch.Tensor):
+    _need(blocks, "blocks", torch.uint8, 2)
+    N, nbytes = blocks.shape
+    if nbytes % Q4_0_BLOCK_BYTES:
+        raise ValueError("blocks rows of %d bytes are not whole 18-byte blocks" % nbytes)
+    _q4_0_storage(blocks)
+    return N, nbytes // Q4_0_BLOCK_BYTES * 32
+
+
+def gemv_q4_0(x: torch.Tensor, blocks: torch.Tensor, y: torch.Tensor = None) -> torch.Tensor:
+    """Q4_0 weights: x fp16 [K] -> y fp16 [N]."""
+    lib = library()
+    N, K = _q4_0_shape(blocks)
+    _need(x, "x", torch.float16, 1)
+    if x.shape[0] != K:
+        raise ValueError("x has %d elements, K = %d" % (x.shape[0], K))
+    if y is None:
+        y = torch.empty((N,), dtype=torch.float16, device=x.device)
+    _need(y, "y", torch.float16, 1)
+    if y.shape[0] != N:
+        raise ValueError("y has %d elements, N = %d" % (y.shape[0], N))
+    _check("w4a16_gemv_q4_0", lib.w4a16_gemv_q4_0(x.data_ptr(), blocks.data_ptr(), N, K,
+                                                  y.data_ptr(), _stream()))
+    return y
+
+
+def gemm_q4_0(X: torch.Tensor, blocks: torch.Tensor, Y: torch.Tensor = None) -> torch.Tensor:
+    """Q4_0 weights: X fp16 [M, K] -> Y fp16 [M, N]."""
+    lib = library()
+    N, K = _q4_0_shape(blocks)
+    _need(X, "X", torch.float16, 2)
+    M = X.shape[0]
+    if X.shape[1] != K:
+        raise ValueError("X has %d columns, K = %d" % (X.shape[1], K))
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float16, device=X.device)
+    _need(Y, "Y", torch.float16, 2)
+    if tuple(Y.shape) != (M, N):
+        raise ValueError("Y shape %s, want %s" % (tuple(Y.shape), (M, N)))
+    _check("w4a16_gemm_q4_0", lib.w4a16_gemm_q4_0(X.data_ptr(), M, blocks.data_ptr(), N, K,
+                                                  Y.data_ptr(), _stream()))
     return Y
 
 
