@@ -80,8 +80,9 @@ def secondary(torch, w4a16, inputs, dev, stream):
     matrix, larger than the Infinity Cache), batched decode M = 1..32 on the
     8B FFN shapes with both kernel families (locates the VALU/MFMA
     crossover), 512-token prefill, the decode GEMV and quantizer at group
-    sizes 32..256, the decode GEMV with an act-order activation gather, and
-    the asymmetric-INT4 decode GEMV and quantizer.  Each figure is the mean of
+    sizes 32..256, the decode GEMV with an act-order activation gather, the
+    asymmetric-INT4 decode GEMV and quantizer, and the Q4_0 block layout
+    against the split layout at group 32.  Each figure is the mean of
     graph replays over enough weight copies to stream from HBM."""
     out = {}
 
@@ -219,6 +220,35 @@ def secondary(torch, w4a16, inputs, dev, stream):
             "quantize_us": round(qus, 2), "quantize_GB/s": round(qb / (qus * 1e-6) / 1e9, 1)}
         del copies, sym, Wd
     out["asymmetric_m1"] = asym
+
+    # Q4_0 blocks (scale in front of each 32-element block) against the split
+    # layout at the same information content (group 32): M = 1 GEMV and the
+    # quantizer
+    q40 = {}
+    for (K, N) in [(4096, 14336), (14336, 4096)]:
+        Wd = torch.from_numpy(inputs.weight(N, K, seed=[11, K, N])).to(dev)
+        bq = w4a16.quantize_q4_0(Wd)
+        qus = timed(lambda: w4a16.quantize_q4_0(Wd, bq))
+        copies = [bq]
+        for _ in range(11):
+            c = w4a16.q4_0_blocks(N, K, device=dev)
+            c.copy_(bq)
+            copies.append(c)
+        x = torch.from_numpy(inputs.activation(1, K, seed=[11, K])).to(dev)[0]
+        y = torch.empty((N,), dtype=torch.float16, device=dev)
+        us = timed(lambda: [w4a16.gemv_q4_0(x, b_, y=y) for b_ in copies]) / len(copies)
+        pg, sg = w4a16.quantize(Wd, group=32)
+        split = [(pg, sg)] + [(pg.clone(), sg.clone()) for _ in range(11)]
+        sus = timed(lambda: [w4a16.gemv(x, p, s_, y=y) for p, s_ in split]) / len(split)
+        b = N * (K // 32) * 18 + 2 * K + 2 * N
+        qb = N * K * 2 + N * (K // 32) * 18
+        q40["%dx%d" % (K, N)] = {
+            "gemv_us": round(us, 3), "gemv_GB/s": round(b / (us * 1e-6) / 1e9, 1),
+            "gemv_frac_of_hbm_peak": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "split_group32_gemv_us": round(sus, 3),
+            "quantize_us": round(qus, 2), "quantize_GB/s": round(qb / (qus * 1e-6) / 1e9, 1)}
+        del copies, split, Wd
+    out["q4_0_m1"] = q40
     quantized.clear()
     return out
 
