@@ -179,8 +179,9 @@ int w4a16_gemm_perm(const uint16_t* X, int64_t M, const int32_t* perm, const uin
  *   w4a16_quantize_asym: W fp16 [N, K] -> packed, scales, zeros (outputs must
  *                        not overlap each other, W or perm)
  *   w4a16_gemv_asym:     y[n] = sum_j x[perm[j]] * ŵ[n,j]      (x[j] without perm)
- *   w4a16_gemm_asym:     Y[m,n] = sum_j X[m, perm[j]] * ŵ[n,j]  (VALU path for
- *                        every M)
+ *   w4a16_gemm_asym:     Y[m,n] = sum_j X[m, perm[j]] * ŵ[n,j]  (the VALU
+ *                        path for M <= w4a16_valu_max_m(), for group != 128
+ *                        and with perm; the matrix cores otherwise)
  * Errors as for w4a16_gemm_g; a NULL zeros with K > 0 is
  * W4A16_ERR_INVALID_ARG; Y must not overlap zeros. */
 int w4a16_quantize_asym(const uint16_t* W, const int32_t* perm, int64_t N, int64_t K,

@@ -702,6 +702,16 @@ def test_linear_asym(w4, orc, group, M, N, K):
     check_linear_asym(w4, orc, M, N, K, group, [43, group, M, N, K])
 
 
+@pytest.mark.parametrize("M", [3, 16, 17, 32, 33, 64, 65, 200, 512])
+@pytest.mark.parametrize("N,K", [(300, 4096), (64, 14336), (1000, 1152)])
+def test_linear_asym_matrix_cores(w4, orc, M, N, K):
+    """M > 2 at group 128 runs on the tiled matrix-core kernel (every tile
+    shape family: 16- and 32-row tiles with K split over waves, 64-row,
+    128-row prefill tiles), planted |z| > 1000 groups (the ones-MFMA
+    correction) included."""
+    check_linear_asym(w4, orc, M, N, K, 128, [47, M, N, K])
+
+
 @pytest.mark.parametrize("name,K,N", [("llama down", 14336, 4096), ("llama gate", 4096, 14336),
                                       ("qwen down", 18944, 3584)])
 def test_linear_asym_layer_shapes(w4, orc, name, K, N):

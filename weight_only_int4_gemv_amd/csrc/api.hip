@@ -88,10 +88,9 @@ int linear(const uint16_t* X, int64_t M, const uint32_t* packed, const uint16_t*
     if (st != W4A16_OK) return st;
     if (algo != W4A16_ALGO_AUTO && algo != W4A16_ALGO_VALU && algo != W4A16_ALGO_MFMA)
         return W4A16_ERR_INVALID_ARG;
-    // the matrix-core kernels read one scale per 128 elements, no perm and
-    // no zero points
-    if (algo == W4A16_ALGO_MFMA && (group != W4A16_GROUP || with_perm || asym))
-        return W4A16_ERR_INVALID_ARG;
+    // the matrix-core kernels read one scale per 128 elements and no perm
+    const bool mfma_capable = group == W4A16_GROUP && !with_perm;
+    if (algo == W4A16_ALGO_MFMA && !mfma_capable) return W4A16_ERR_INVALID_ARG;
     if (M == 0 || N == 0) return W4A16_OK;
     // With K == 0 the inputs hold no bytes and may be NULL; they are never read.
     if (!Y || (K > 0 && (!X || !packed || !scales || (with_perm && !perm) || (asym && !zeros))))
@@ -110,13 +109,16 @@ int linear(const uint16_t* X, int64_t M, const uint32_t* packed, const uint16_t*
     st = current_device(&num_cu);
     if (st != W4A16_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const bool valu = algo == W4A16_ALGO_VALU || group != W4A16_GROUP || with_perm || asym ||
+    const bool valu = algo == W4A16_ALGO_VALU || !mfma_capable ||
                       (algo == W4A16_ALGO_AUTO && M <= kValuMaxM);
     if (valu)
         return status_of(w4a16::launch_gemv_valu(X, M, packed, scales, N, K, Y, s, num_cu,
                                                  group_shift(group),
                                                  with_perm ? perm : nullptr,
                                                  asym ? zeros : nullptr));
+    if (asym)
+        return status_of(w4a16::launch_gemm_mfma_asym(X, M, packed, scales, zeros, N, K, Y, s,
+                                                      num_cu));
     return status_of(w4a16::launch_gemm_mfma(X, M, packed, scales, N, K, Y, s, num_cu));
 }
 

@@ -23,6 +23,14 @@
 // Precision: fp16(s*q) has relative error <= 2^-11, so |y - y_exact| <=
 // 2^-11 sum |x w| plus fp32 accumulation error, inside the 1e-3 sum |x w|
 // allowance for every K.
+//
+// Asymmetric weights (ASYM, [QUANT] sub-section 2: w = s (n - z), nibble n
+// in [0, 15], an integer zero point z per group): B holds the exact codes
+// n - zc (codes_word_zp, zc = z clamped to +-1000), each group's products
+// are summed by the MFMAs in fp32 and scaled once in fp32, as the GEMV does
+// (so no fp16 product s (n - z) can overflow); a group with |z| > 1000 adds
+// s (zc - z) times the group's activation sums, which one more MFMA per
+// k-step against a B of ones forms (only in waves that hold such a group).
 #include "w4a16_device.h"
 #include "w4a16_launch.h"
 
@@ -33,10 +41,11 @@ constexpr int kLdaHalfs = 136;             // staged A row: 128 halves + 8 pad (
 constexpr int kLdaVec = kLdaHalfs / 8;     // in uint4
 }  // namespace
 
-template <int TM, int TN, int WM, int WN, int WK>
+template <int TM, int TN, int WM, int WN, int WK, bool ASYM>
 __global__ __launch_bounds__(WM * WN * WK * kWave) void gemm_mfma_kernel(
     const uint16_t* __restrict__ X, int M, const uint4* __restrict__ packed,
-    const uint16_t* __restrict__ scales, uint16_t* __restrict__ Y, int N, int K) {
+    const uint16_t* __restrict__ scales, const int16_t* __restrict__ zeros,
+    uint16_t* __restrict__ Y, int N, int K) {
     constexpr int NT = WM * WN * WK * kWave;
     constexpr int BM = 16 * TM * WM;
     constexpr int BN = 16 * TN * WN;
@@ -93,16 +102,18 @@ __global__ __launch_bounds__(WM * WN * WK * kWave) void gemm_mfma_kernel(
             }
         }
     };
-    auto load_b = [&](int step, uint4 (&bw)[TN], uint32_t (&bs)[TN]) {
+    auto load_b = [&](int step, uint4 (&bw)[TN], uint32_t (&bs)[TN], int (&bz)[TN]) {
         const int g = step * WK + wk;
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) {
             if (g < ngroups) {
                 bw[tn] = packed[(size_t)brow[tn] * nchunks + g * 4 + j];
                 bs[tn] = scales[(size_t)brow[tn] * ngroups + g];
+                bz[tn] = ASYM ? (int)zeros[(size_t)brow[tn] * ngroups + g] : 0;
             } else {
                 bw[tn] = make_uint4(0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u);
                 bs[tn] = 0;
+                bz[tn] = 0;
             }
         }
     };
@@ -117,15 +128,86 @@ __global__ __launch_bounds__(WM * WN * WK * kWave) void gemm_mfma_kernel(
     uint4 a_regs[A_PER_THREAD];
     uint4 bw[TN], bw_next[TN];
     uint32_t bs[TN], bs_next[TN];
+    int bz[TN], bz_next[TN];
     load_a(0, a_regs);
-    load_b(0, bw, bs);
+    load_b(0, bw, bs, bz);
 
     for (int step = 0; step < nsteps; ++step) {
         store_a(a_regs);
         __syncthreads();
         if (step + 1 < nsteps) {
             load_a(step + 1, a_regs);
-            load_b(step + 1, bw_next, bs_next);
+            load_b(step + 1, bw_next, bs_next, bz_next);
+        }
+        const uint4* abase = lds + (wk * BM + wm * TM * 16 + l16) * kLdaVec + 4 * j;
+        if constexpr (ASYM) {
+            // exact codes n - zc; the group's products scaled once in fp32
+            half8_t bq[TN][4];
+            float sf[TN], cf[TN];
+            bool wide = false;
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn) {
+                const ZeroBias zb = zero_bias(bz[tn]);
+                sf[tn] = f16_bits_to_f32((uint16_t)bs[tn]);
+                cf[tn] = sf[tn] * (float)(zb.zc - bz[tn]);      // exact: |zc - z| < 2^15
+                wide |= zb.zc != bz[tn];
+                const uint32_t words[4] = {bw[tn].x, bw[tn].y, bw[tn].z, bw[tn].w};
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    half2_t q[4];
+                    codes_word_zp(words[kk], kc, zb, q);
+                    bq[tn][kk] = (half8_t){q[0].x, q[0].y, q[1].x, q[1].y,
+                                           q[2].x, q[2].y, q[3].x, q[3].y};
+                }
+            }
+            float4_t d[TM][TN];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+                for (int tm = 0; tm < TM; ++tm) {
+                    const half8_t af = __builtin_bit_cast(half8_t, abase[tm * 16 * kLdaVec + kk]);
+#pragma unroll
+                    for (int tn = 0; tn < TN; ++tn)
+                        d[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                            af, bq[tn][kk], kk == 0 ? (float4_t){0.f, 0.f, 0.f, 0.f} : d[tm][tn],
+                            0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+                for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        acc[tm][tn][r] = fmaf(sf[tn], d[tm][tn][r], acc[tm][tn][r]);
+            if (__any(wide)) {
+                // activation sums of the group's 128 k for this wave's rows
+                const _Float16 one = (_Float16)1.0f;
+                const half8_t ones = {one, one, one, one, one, one, one, one};
+                float4_t xs[TM];
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                    for (int tm = 0; tm < TM; ++tm)
+                        xs[tm] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                            __builtin_bit_cast(half8_t, abase[tm * 16 * kLdaVec + kk]), ones,
+                            kk == 0 ? (float4_t){0.f, 0.f, 0.f, 0.f} : xs[tm], 0, 0, 0);
+#pragma unroll
+                for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+                    for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            acc[tm][tn][r] = fmaf(cf[tn], xs[tm][r], acc[tm][tn][r]);
+            }
+            __syncthreads();
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn) {
+                bw[tn] = bw_next[tn];
+                bs[tn] = bs_next[tn];
+                bz[tn] = bz_next[tn];
+            }
+            continue;
         }
         // B fragments of this wave's group: [tn][kk]
         half8_t bf[TN][4];
@@ -142,7 +224,6 @@ __global__ __launch_bounds__(WM * WN * WK * kWave) void gemm_mfma_kernel(
                                        h[2].x, h[2].y, h[3].x, h[3].y};
             }
         }
-        const uint4* abase = lds + (wk * BM + wm * TM * 16 + l16) * kLdaVec + 4 * j;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
@@ -160,6 +241,7 @@ __global__ __launch_bounds__(WM * WN * WK * kWave) void gemm_mfma_kernel(
         for (int tn = 0; tn < TN; ++tn) {
             bw[tn] = bw_next[tn];
             bs[tn] = bs_next[tn];
+            bz[tn] = bz_next[tn];
         }
     }
 
@@ -204,27 +286,56 @@ __global__ __launch_bounds__(WM * WN * WK * kWave) void gemm_mfma_kernel(
 
 namespace {
 
-template <int TM, int TN, int WM, int WN, int WK>
+template <int TM, int TN, int WM, int WN, int WK, bool ASYM = false>
 hipError_t launch_mfma_t(const uint16_t* X, int64_t M, const uint32_t* packed,
                          const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y,
-                         hipStream_t stream) {
+                         hipStream_t stream, const int16_t* zeros = nullptr) {
     constexpr int BM = 16 * TM * WM;
     constexpr int BN = 16 * TN * WN;
     const size_t a_bytes = (size_t)WK * BM * kLdaVec * sizeof(uint4);
     const size_t red_bytes = (size_t)(WK - 1) * WM * WN * TM * TN * 64 * sizeof(float4_t);
     const size_t lds = a_bytes > red_bytes ? a_bytes : red_bytes;
+    auto kern = gemm_mfma_kernel<TM, TN, WM, WN, WK, ASYM>;
     if (lds > 64 * 1024) {
-        const hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void*>(gemm_mfma_kernel<TM, TN, WM, WN, WK>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 (int)lds);
         if (e != hipSuccess) return e;
     }
     const dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM));
-    hipLaunchKernelGGL((gemm_mfma_kernel<TM, TN, WM, WN, WK>), grid, dim3(WM * WN * WK * kWave),
-                       lds, stream, X,
-                       (int)M, reinterpret_cast<const uint4*>(packed), scales, Y, (int)N,
-                       (int)K);
+    hipLaunchKernelGGL(kern, grid, dim3(WM * WN * WK * kWave), lds, stream, X, (int)M,
+                       reinterpret_cast<const uint4*>(packed), scales, zeros, Y, (int)N, (int)K);
     return hipGetLastError();
+}
+
+// Tile shapes by M for the tiled kernel (the symmetric path sends M <= 64
+// to the other kernels first when they apply).
+template <bool ASYM>
+hipError_t launch_tiled(const uint16_t* X, int64_t M, const uint32_t* packed,
+                        const uint16_t* scales, const int16_t* zeros, int64_t N, int64_t K,
+                        uint16_t* Y, hipStream_t stream, int num_cu) {
+    // Few rows: one 16- or 32-row tile, waves split K; enough column tiles
+    // to give every compute unit work.
+    if (M <= 16) {
+        if (N >= (int64_t)64 * num_cu)
+            return launch_mfma_t<1, 2, 1, 1, 4, ASYM>(X, M, packed, scales, N, K, Y, stream, zeros);
+        return launch_mfma_t<1, 1, 1, 1, 4, ASYM>(X, M, packed, scales, N, K, Y, stream, zeros);
+    }
+    if (M <= 32) {
+        if (N >= (int64_t)64 * num_cu)
+            return launch_mfma_t<2, 2, 1, 1, 4, ASYM>(X, M, packed, scales, N, K, Y, stream, zeros);
+        return launch_mfma_t<2, 1, 1, 1, 4, ASYM>(X, M, packed, scales, N, K, Y, stream, zeros);
+    }
+    if (M <= 64)
+        return launch_mfma_t<2, 2, 2, 2, 1, ASYM>(X, M, packed, scales, N, K, Y, stream, zeros);
+    // Prefill: 128 x 128 block tiles (eight 16-row tiles by two 16-column
+    // tiles per wave, four waves across N) when they fill the compute units,
+    // else 128 x 64 tiles with eight waves, two over K (measured on gfx950,
+    // M = 512 on 14336 x 4096: 127 us against 155 us with four waves).
+    const int64_t tiles128 = ((M + 127) / 128) * ((N + 127) / 128);
+    if (tiles128 >= num_cu)
+        return launch_mfma_t<8, 2, 1, 4, 1, ASYM>(X, M, packed, scales, N, K, Y, stream, zeros);
+    return launch_mfma_t<4, 2, 2, 2, 2, ASYM>(X, M, packed, scales, N, K, Y, stream, zeros);
 }
 
 }  // namespace
@@ -243,27 +354,13 @@ hipError_t launch_gemm_mfma(const uint16_t* X, int64_t M, const uint32_t* packed
     // with the K groups split over waves.
     if (M <= 64 && K > N && K <= kSkinnyMaxK)
         return launch_gemm_skinny(X, M, packed, scales, N, K, Y, stream, num_cu);
-    // Few rows: one 16- or 32-row tile, waves split K; enough column tiles
-    // to give every compute unit work.
-    if (M <= 16) {
-        if (N >= (int64_t)64 * num_cu)
-            return launch_mfma_t<1, 2, 1, 1, 4>(X, M, packed, scales, N, K, Y, stream);
-        return launch_mfma_t<1, 1, 1, 1, 4>(X, M, packed, scales, N, K, Y, stream);
-    }
-    if (M <= 32) {
-        if (N >= (int64_t)64 * num_cu)
-            return launch_mfma_t<2, 2, 1, 1, 4>(X, M, packed, scales, N, K, Y, stream);
-        return launch_mfma_t<2, 1, 1, 1, 4>(X, M, packed, scales, N, K, Y, stream);
-    }
-    if (M <= 64) return launch_mfma_t<2, 2, 2, 2, 1>(X, M, packed, scales, N, K, Y, stream);
-    // Prefill: 128 x 128 block tiles (eight 16-row tiles by two 16-column
-    // tiles per wave, four waves across N) when they fill the compute units,
-    // else 128 x 64 tiles with eight waves, two over K (measured on gfx950,
-    // M = 512 on 14336 x 4096: 127 us against 155 us with four waves).
-    const int64_t tiles128 = ((M + 127) / 128) * ((N + 127) / 128);
-    if (tiles128 >= num_cu)
-        return launch_mfma_t<8, 2, 1, 4, 1>(X, M, packed, scales, N, K, Y, stream);
-    return launch_mfma_t<4, 2, 2, 2, 2>(X, M, packed, scales, N, K, Y, stream);
+    return launch_tiled<false>(X, M, packed, scales, nullptr, N, K, Y, stream, num_cu);
+}
+
+hipError_t launch_gemm_mfma_asym(const uint16_t* X, int64_t M, const uint32_t* packed,
+                                 const uint16_t* scales, const int16_t* zeros, int64_t N,
+                                 int64_t K, uint16_t* Y, hipStream_t stream, int num_cu) {
+    return launch_tiled<true>(X, M, packed, scales, zeros, N, K, Y, stream, num_cu);
 }
 
 }  // namespace w4a16

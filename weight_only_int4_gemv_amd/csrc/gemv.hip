@@ -80,25 +80,18 @@ __device__ __forceinline__ void stage_activations(const uint16_t* __restrict__ X
     }
 }
 
-// Codes n - zc of one packed word as exact fp16 integers in the paired
-// order (the code trick of codes_word with the bias constants -1024 - zc and
-// -64 - zc, |zc| <= 1000: operands and results are integers below 2^11).
+// acc += sum of the 8 products x * (n - zc) of one packed word (exact fp16
+// codes from codes_word_zp, exact products in v_dot2_f32_f16).
 __device__ __forceinline__ float dot_word_zp(uint32_t w, const uint4& xp, float acc,
-                                             const CodeConsts& k, half2_t blo, half2_t bhi) {
-    const half2_t inv16 = {(_Float16)0.0625f, (_Float16)0.0625f};
-    const uint32_t w8 = w >> 8;
-    const half2_t q0 = as_h2((w & k.m_lo) | k.magic) + blo;
-    const half2_t q1 = __builtin_elementwise_fma(as_h2((w & k.m_hi) | k.magic), inv16, bhi);
-    const half2_t q2 = as_h2((w8 & k.m_lo) | k.magic) + blo;
-    const half2_t q3 = __builtin_elementwise_fma(as_h2((w8 & k.m_hi) | k.magic), inv16, bhi);
-    acc = __builtin_amdgcn_fdot2(q0, as_h2(xp.x), acc, false);
-    acc = __builtin_amdgcn_fdot2(q1, as_h2(xp.y), acc, false);
-    acc = __builtin_amdgcn_fdot2(q2, as_h2(xp.z), acc, false);
-    acc = __builtin_amdgcn_fdot2(q3, as_h2(xp.w), acc, false);
+                                             const CodeConsts& k, const ZeroBias& b) {
+    half2_t q[4];
+    codes_word_zp(w, k, b, q);
+    acc = __builtin_amdgcn_fdot2(q[0], as_h2(xp.x), acc, false);
+    acc = __builtin_amdgcn_fdot2(q[1], as_h2(xp.y), acc, false);
+    acc = __builtin_amdgcn_fdot2(q[2], as_h2(xp.z), acc, false);
+    acc = __builtin_amdgcn_fdot2(q[3], as_h2(xp.w), acc, false);
     return acc;
 }
-
-constexpr int kZeroClamp = 1000;
 
 // sum_k x_k * (n_k - z) over one 16-byte chunk of 32 codes (activations
 // x0..x3 in the paired order).  Symmetric weights (ASYM false) have
@@ -113,15 +106,12 @@ __device__ __forceinline__ float chunk_dot(const uint4& w, const uint4& x0, cons
         part = dot_word(w.z, x2, part, kc);
         return dot_word(w.w, x3, part, kc);
     } else {
-        const int zc = min(max(z, -kZeroClamp), kZeroClamp);
-        const _Float16 zh = (_Float16)zc;                       // exact
-        const _Float16 lo = (_Float16)-1024.0f - zh, hi = (_Float16)-64.0f - zh;
-        const half2_t blo = {lo, lo}, bhi = {hi, hi};
-        float part = dot_word_zp(w.x, x0, 0.0f, kc, blo, bhi);
-        part = dot_word_zp(w.y, x1, part, kc, blo, bhi);
-        part = dot_word_zp(w.z, x2, part, kc, blo, bhi);
-        part = dot_word_zp(w.w, x3, part, kc, blo, bhi);
-        if (zc != z) {
+        const ZeroBias b = zero_bias(z);
+        float part = dot_word_zp(w.x, x0, 0.0f, kc, b);
+        part = dot_word_zp(w.y, x1, part, kc, b);
+        part = dot_word_zp(w.z, x2, part, kc, b);
+        part = dot_word_zp(w.w, x3, part, kc, b);
+        if (b.zc != z) {
             // sum of the chunk's 32 activations, each exact in fp32
             const half2_t one = {(_Float16)1.0f, (_Float16)1.0f};
             float xs = 0.0f;
@@ -129,7 +119,7 @@ __device__ __forceinline__ float chunk_dot(const uint4& w, const uint4& x0, cons
                                      x2.x, x2.y, x2.z, x2.w, x3.x, x3.y, x3.z, x3.w};
 #pragma unroll
             for (int i = 0; i < 16; ++i) xs = __builtin_amdgcn_fdot2(one, as_h2(xv[i]), xs, false);
-            part = fmaf((float)(zc - z), xs, part);
+            part = fmaf((float)(b.zc - z), xs, part);
         }
         return part;
     }

@@ -78,6 +78,32 @@ __device__ __forceinline__ void codes_word(uint32_t w, const CodeConsts& k, half
     q[3] = __builtin_elementwise_fma(as_h2((w8 & k.m_hi) | k.magic), inv16, m72);
 }
 
+// Asymmetric codes: n - zc for the nibbles n of one word, exact fp16
+// integers in the paired order, with the bias constants -1024 - zc (low
+// nibbles, after the 0x6400 trick) and -64 - zc (high nibbles, after the
+// division by 16).  |zc| <= kZeroClamp keeps every operand and result an
+// integer below 2^11.
+constexpr int kZeroClamp = 1000;
+struct ZeroBias {
+    half2_t lo, hi;
+    int zc;       // the clamped zero point the biases encode
+};
+__device__ __forceinline__ ZeroBias zero_bias(int z) {
+    const int zc = min(max(z, -kZeroClamp), kZeroClamp);
+    const _Float16 zh = (_Float16)zc;                       // exact
+    const _Float16 lo = (_Float16)-1024.0f - zh, hi = (_Float16)-64.0f - zh;
+    return ZeroBias{(half2_t){lo, lo}, (half2_t){hi, hi}, zc};
+}
+__device__ __forceinline__ void codes_word_zp(uint32_t w, const CodeConsts& k, const ZeroBias& b,
+                                              half2_t (&q)[4]) {
+    const half2_t inv16 = {(_Float16)0.0625f, (_Float16)0.0625f};
+    const uint32_t w8 = w >> 8;
+    q[0] = as_h2((w & k.m_lo) | k.magic) + b.lo;
+    q[1] = __builtin_elementwise_fma(as_h2((w & k.m_hi) | k.magic), inv16, b.hi);
+    q[2] = as_h2((w8 & k.m_lo) | k.magic) + b.lo;
+    q[3] = __builtin_elementwise_fma(as_h2((w8 & k.m_hi) | k.magic), inv16, b.hi);
+}
+
 // acc += sum of the word's 8 products q*x (paired activations xp), each
 // product exact in fp32 (v_dot2_f32_f16), so the rounding error of the
 // accumulation is relative to sum |q x|.

@@ -40,6 +40,12 @@ hipError_t launch_gemm_mfma(const uint16_t* X, int64_t M, const uint32_t* packed
                             const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y,
                             hipStream_t stream, int num_cu);
 
+// MFMA path for asymmetric weights (zeros: int16 [N, K/128]), any M: the
+// tiled kernel with exact codes n - z and per-group fp32 scaling.
+hipError_t launch_gemm_mfma_asym(const uint16_t* X, int64_t M, const uint32_t* packed,
+                                 const uint16_t* scales, const int16_t* zeros, int64_t N,
+                                 int64_t K, uint16_t* Y, hipStream_t stream, int num_cu);
+
 // MFMA GEMV for M <= 4 with x resident in LDS (gemv_mfma4.hip): the weight
 // stream of the VALU GEMV, products on v_mfma_f32_4x4x4_16b_f16.
 constexpr int64_t kMfma4MaxM = 4;

@@ -327,7 +327,8 @@ def gemv_asym(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,
 def gemm_asym(X: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,
               zeros: torch.Tensor, Y: torch.Tensor = None,
               perm: torch.Tensor = None) -> torch.Tensor:
-    """Asymmetric weights: X fp16 [M, K] -> Y fp16 [M, N] (VALU path)."""
+    """Asymmetric weights: X fp16 [M, K] -> Y fp16 [M, N] (VALU path for
+    small M, other group sizes and perm; matrix cores otherwise)."""
     lib = library()
     N, K, group = _weights(packed, scales)
     _zeros(zeros, scales)
