@@ -213,11 +213,24 @@ def secondary(torch, w4a16, inputs, dev, stream):
         plain = timed(lambda: [w4a16.gemv(x, p, s_, y=y) for p, s_ in sym]) / len(sym)
         b = gemv_bytes(N, K) + N * (K // 128) * 2
         qb = N * K * 2 + N * K // 2 + 2 * N * (K // 128) * 2
-        asym["%dx%d" % (K, N)] = {
+        row = {
             "gemv_us": round(us, 3), "gemv_GB/s": round(b / (us * 1e-6) / 1e9, 1),
             "gemv_frac_of_hbm_peak": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             "symmetric_gemv_us": round(plain, 3),
             "quantize_us": round(qus, 2), "quantize_GB/s": round(qb / (qus * 1e-6) / 1e9, 1)}
+        # batched decode and prefill with asymmetric weights (matrix cores)
+        for M in (16, 512):
+            X = torch.from_numpy(inputs.activation(M, K, seed=[10, M, K])).to(dev)
+            Y = torch.empty((M, N), dtype=torch.float16, device=dev)
+            few = copies[:4] if M == 512 else copies
+            a_us = timed(lambda: [w4a16.gemm_asym(X, p, s_, z, Y=Y) for p, s_, z in few]) \
+                / len(few)
+            fews = sym[:4] if M == 512 else sym
+            s_us = timed(lambda: [w4a16.gemm(X, p, s_, Y=Y) for p, s_ in fews]) / len(fews)
+            row["M=%d_us" % M] = round(a_us, 2)
+            row["M=%d_symmetric_us" % M] = round(s_us, 2)
+            row["M=%d_TFLOP/s" % M] = round(2 * M * N * K / (a_us * 1e-6) / 1e12, 1)
+        asym["%dx%d" % (K, N)] = row
         del copies, sym, Wd
     out["asymmetric_m1"] = asym
 
