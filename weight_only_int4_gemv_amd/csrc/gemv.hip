@@ -28,6 +28,8 @@
 // 1000) folded into the two bias constants of the code trick, so the products
 // stay exact; a group with |z| > 1000 (one-signed with a narrow range, where
 // every |n - z| > 985) adds (zc - z) * sum(x over the chunk).
+#include <atomic>
+
 #include "w4a16_device.h"
 #include "w4a16_launch.h"
 
@@ -404,36 +406,60 @@ hipError_t launch_gemv_t(const uint16_t* X, int64_t M, const uint32_t* packed,
     return hipGetLastError();
 }
 
+// Grid: a whole number b of blocks per compute unit, b at most
+// blocks_per_cu and at most what one compute unit holds at once (the
+// runtime's occupancy for this kernel and LDS size), so that with
+// grid-stride row groups every compute unit gets the same work to within
+// one row group per wave and no block waits for a second round.  Measured
+// on gfx950, M = 1: 4096x28672 12.4-12.5 us with 2048 blocks against
+// 13.8-14.2 us with 1195 (4.67 blocks per CU leave the CUs with a fifth
+// block 7 % more work), 4096x14336 7.5-7.8 us against 8.6-8.9 us with 896.
+// Fewer row groups than waves on the chip: one wave per row group.
 template <int MMAX, int R, int P, int WAVES, int XPT, bool ASYM>
 hipError_t launch_persistent_xpt(const uint16_t* X, int64_t M, const uint32_t* packed,
                                  const uint16_t* scales, const int16_t* zeros, int64_t N,
-                                 int64_t K, uint16_t* Y, hipStream_t stream, int64_t blocks,
-                                 int gshift, const int* perm) {
+                                 int64_t K, uint16_t* Y, hipStream_t stream, int num_cu,
+                                 int blocks_per_cu, int gshift, const int* perm) {
     const size_t lds = (size_t)MMAX * (K / 8) * sizeof(uint4);
-    hipLaunchKernelGGL((gemv_persistent_kernel<MMAX, R, P, WAVES, XPT, ASYM>),
-                       dim3((unsigned)blocks), dim3(WAVES * kWave), lds, stream, X, (int)M,
+    auto kern = gemv_persistent_kernel<MMAX, R, P, WAVES, XPT, ASYM>;
+    // resident blocks per CU for the last LDS size seen (lds << 8 | blocks)
+    static std::atomic<uint64_t> occ_cache{0};
+    uint64_t c = occ_cache.load(std::memory_order_relaxed);
+    int resident = (int)(c & 0xFF);
+    if ((c >> 8) != (uint64_t)lds || resident == 0) {
+        int nb = 0;
+        const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &nb, reinterpret_cast<const void*>(kern), WAVES * kWave, lds);
+        if (e != hipSuccess) return e;
+        resident = nb < 1 ? 1 : (nb > 255 ? 255 : nb);
+        occ_cache.store(((uint64_t)lds << 8) | (uint64_t)resident, std::memory_order_relaxed);
+    }
+    const int64_t total_rg = (N + R - 1) / R;
+    const int64_t per_cu = (int64_t)num_cu * WAVES;
+    int64_t blocks = (total_rg + WAVES - 1) / WAVES;
+    if (total_rg >= per_cu) {
+        int64_t b = total_rg / per_cu;
+        if (b > blocks_per_cu) b = blocks_per_cu;
+        if (b > resident) b = resident;
+        blocks = b * num_cu;
+    }
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(WAVES * kWave), lds, stream, X, (int)M,
                        reinterpret_cast<const uint4*>(packed), scales, zeros, Y, (int)N, (int)K,
                        gshift, perm);
     return hipGetLastError();
 }
 
-// Grid: at most blocks_per_cu blocks per compute unit, sized so that every
-// wave gets the same number of row groups.
 template <int MMAX, int R, int P, int WAVES, bool ASYM>
 hipError_t launch_persistent_t(const uint16_t* X, int64_t M, const uint32_t* packed,
                                const uint16_t* scales, const int16_t* zeros, int64_t N,
                                int64_t K, uint16_t* Y, hipStream_t stream, int num_cu,
                                int blocks_per_cu, int gshift, const int* perm) {
-    const int64_t total_rg = (N + R - 1) / R;
-    const int64_t max_waves = (int64_t)num_cu * blocks_per_cu * WAVES;
-    const int64_t per_wave = (total_rg + max_waves - 1) / max_waves;
-    const int64_t waves = (total_rg + per_wave - 1) / per_wave;
-    const int64_t blocks = (waves + WAVES - 1) / WAVES;
     const int64_t need = (int64_t)MMAX * (K / 8);             // x blocks to stage
     const int64_t threads = (int64_t)WAVES * kWave;
 #define W4A16_PERSISTENT(XPT)                                                                  \
     launch_persistent_xpt<MMAX, R, P, WAVES, XPT, ASYM>(X, M, packed, scales, zeros, N, K, Y,  \
-                                                        stream, blocks, gshift, perm)
+                                                        stream, num_cu, blocks_per_cu, gshift, \
+                                                        perm)
     if (need <= threads) return W4A16_PERSISTENT(1);
     if (need <= 2 * threads) return W4A16_PERSISTENT(2);
     if (need <= 4 * threads) return W4A16_PERSISTENT(4);
@@ -445,10 +471,10 @@ hipError_t launch_persistent_t(const uint16_t* X, int64_t M, const uint32_t* pac
 // Launch choice (measured on MI355X over the decode layer shapes, K x N from
 // 4096x1024 to 8192x28672, with the (P+1)-slot ring and non-temporal loads):
 // whole-X staging with the persistent kernel when it fits; two rows per
-// wave; for K up to 8192 one step in flight, four waves per block, six
-// blocks per compute unit; for longer rows (K >= 12288, where the per-block
-// activation copy is larger) two steps in flight, eight waves per block,
-// two blocks per compute unit.
+// wave; for K up to 8192 one step in flight, four waves per block, up to
+// eight blocks per compute unit; for longer rows (K >= 12288, where the
+// per-block activation copy is larger) eight waves per block, up to two
+// blocks per compute unit.
 template <int MMAX, bool ASYM>
 hipError_t launch_gemv_m(const uint16_t* X, int64_t M, const uint32_t* packed,
                          const uint16_t* scales, const int16_t* zeros, int64_t N, int64_t K,
@@ -466,7 +492,7 @@ hipError_t launch_gemv_m(const uint16_t* X, int64_t M, const uint32_t* packed,
             return launch_persistent_t<MMAX, R, 2, 8, ASYM>(X, M, packed, scales, zeros, N, K, Y,
                                                             stream, num_cu, 2, gshift, perm);
         return launch_persistent_t<MMAX, R, 1, 4, ASYM>(X, M, packed, scales, zeros, N, K, Y,
-                                                        stream, num_cu, 6, gshift, perm);
+                                                        stream, num_cu, 8, gshift, perm);
     }
     constexpr int WAVES = 4;
     if (N >= (int64_t)4 * WAVES * num_cu && MMAX <= 4)

@@ -227,11 +227,14 @@ template <int MMAX, int R, int WAVES>
 hipError_t launch_q4_0_t(const uint16_t* X, int64_t M, const uint8_t* blocks, int64_t N,
                          int64_t K, uint16_t* Y, hipStream_t stream, int num_cu,
                          int blocks_per_cu) {
+    // a whole number of blocks per compute unit (as for the split layout)
     const int64_t total_rg = (N + R - 1) / R;
-    const int64_t max_waves = (int64_t)num_cu * blocks_per_cu * WAVES;
-    const int64_t per_wave = (total_rg + max_waves - 1) / max_waves;
-    const int64_t waves = (total_rg + per_wave - 1) / per_wave;
-    const int64_t grid = (waves + WAVES - 1) / WAVES;
+    const int64_t per_cu = (int64_t)num_cu * WAVES;
+    int64_t grid = (total_rg + WAVES - 1) / WAVES;
+    if (total_rg >= per_cu) {
+        const int64_t b = total_rg / per_cu;
+        grid = (b > blocks_per_cu ? blocks_per_cu : b) * num_cu;
+    }
     const int64_t need = (int64_t)MMAX * (K / 8);
     const int64_t threads = (int64_t)WAVES * kWave;
 #define W4A16_Q40(XPT) launch_q4_0_xpt<MMAX, R, WAVES, XPT>(X, M, blocks, N, K, Y, stream, grid)
@@ -244,14 +247,14 @@ hipError_t launch_q4_0_t(const uint16_t* X, int64_t M, const uint8_t* blocks, in
 }
 
 // The launch shapes of the split-layout GEMV: up to 8192 elements per row,
-// four waves per block and six blocks per compute unit; longer rows eight
+// four waves per block and up to eight blocks per compute unit; longer rows eight
 // waves and two blocks.
 template <int MMAX>
 hipError_t launch_q4_0_m(const uint16_t* X, int64_t M, const uint8_t* blocks, int64_t N,
                          int64_t K, uint16_t* Y, hipStream_t stream, int num_cu) {
     constexpr int R = MMAX >= 4 ? 1 : 2;
     if (K >= 12288) return launch_q4_0_t<MMAX, R, 8>(X, M, blocks, N, K, Y, stream, num_cu, 2);
-    return launch_q4_0_t<MMAX, R, 4>(X, M, blocks, N, K, Y, stream, num_cu, 6);
+    return launch_q4_0_t<MMAX, R, 4>(X, M, blocks, N, K, Y, stream, num_cu, 8);
 }
 
 }  // namespace
