@@ -491,8 +491,11 @@ hipError_t launch_gemv_m(const uint16_t* X, int64_t M, const uint32_t* packed,
         if (K >= 12288)
             return launch_persistent_t<MMAX, R, 2, 8, ASYM>(X, M, packed, scales, zeros, N, K, Y,
                                                             stream, num_cu, 2, gshift, perm);
+        // Every block gathers its own copy of x through perm, so act-order
+        // launches use fewer blocks (4096x14336: 15.3 us with 8 per CU).
         return launch_persistent_t<MMAX, R, 1, 4, ASYM>(X, M, packed, scales, zeros, N, K, Y,
-                                                        stream, num_cu, 8, gshift, perm);
+                                                        stream, num_cu, perm ? 4 : 8, gshift,
+                                                        perm);
     }
     constexpr int WAVES = 4;
     if (N >= (int64_t)4 * WAVES * num_cu && MMAX <= 4)
