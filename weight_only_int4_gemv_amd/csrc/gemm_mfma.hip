@@ -42,7 +42,8 @@ constexpr int kLdaVec = kLdaHalfs / 8;     // in uint4
 }  // namespace
 
 template <int TM, int TN, int WM, int WN, int WK, bool ASYM>
-__global__ __launch_bounds__(WM * WN * WK * kWave) void gemm_mfma_kernel(
+__global__ __launch_bounds__(WM * WN * WK * kWave)
+__attribute__((amdgpu_waves_per_eu(ASYM ? 1 : 2))) void gemm_mfma_kernel(
     const uint16_t* __restrict__ X, int M, const uint4* __restrict__ packed,
     const uint16_t* __restrict__ scales, const int16_t* __restrict__ zeros,
     uint16_t* __restrict__ Y, int N, int K) {
@@ -50,11 +51,14 @@ __global__ __launch_bounds__(WM * WN * WK * kWave) void gemm_mfma_kernel(
     constexpr int BM = 16 * TM * WM;
     constexpr int BN = 16 * TN * WN;
     constexpr int A_VECS = WK * BM * 16;              // uint4 of A per stage (WK groups)
-    constexpr int A_PER_THREAD = (A_VECS + NT - 1) / NT;
-    extern __shared__ uint4 lds[];                    // [WK][BM][kLdaVec]
+    constexpr int A_PER_THREAD = A_VECS / NT;
+    constexpr int A_PER_SLOT = BM * 16 / NT;          // consecutive stage vectors of one group
+    static_assert(A_VECS % NT == 0 && (BM * 16) % NT == 0, "A staging must tile the block");
+    constexpr int LDS_STAGE = WK * BM * kLdaVec;      // uint4 per A buffer
+    extern __shared__ uint4 lds[];                    // [2][WK][BM][kLdaVec]
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     const int wk = wave % WK;
     const int wn = (wave / WK) % WN;
     const int wm = wave / (WK * WN);
@@ -63,57 +67,87 @@ __global__ __launch_bounds__(WM * WN * WK * kWave) void gemm_mfma_kernel(
     const int m_blk = blockIdx.y * BM;
     const int n_blk = blockIdx.x * BN;
     const int ngroups = K >> 7;
-    const int nchunks = K >> 5;
     const int nsteps = (ngroups + WK - 1) / WK;
+    const uint32_t wrow = (uint32_t)K / 2;            // bytes per weight row
+    const uint32_t srow = (uint32_t)ngroups * 2;      // bytes per scale (and zero) row
 
-    int brow[TN];
+    // Byte offsets of this thread's loads from the block's first row, fixed
+    // for the whole K loop (32-bit: the launcher keeps BM rows of X and BN
+    // rows of codes below 2^31 bytes).  Rows past M or N are clamped to the
+    // last row: they only feed outputs that are never stored.
+    uint32_t a_off[A_PER_THREAD], a_lds[A_PER_THREAD];
 #pragma unroll
-    for (int tn = 0; tn < TN; ++tn) brow[tn] = min(n_blk + (wn * TN + tn) * 16 + l16, N - 1);
+    for (int i = 0; i < A_PER_THREAD; ++i) {
+        const int slot = i / A_PER_SLOT;
+        const int rem = (i % A_PER_SLOT) * NT + (int)threadIdx.x;
+        const int row = rem >> 4;
+        const int blk = rem & 15;
+        const uint32_t m = (uint32_t)(min(m_blk + row, M - 1) - m_blk);
+        a_off[i] = m * (uint32_t)K * 2u + (uint32_t)(slot * 256 + blk * 16);
+        a_lds[i] = (uint32_t)((slot * BM + row) * kLdaVec + blk);
+    }
+    uint32_t b_off[TN], s_off[TN];
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) {
+        const uint32_t r = (uint32_t)(min(n_blk + (wn * TN + tn) * 16 + l16, N - 1) - n_blk);
+        b_off[tn] = r * wrow + (uint32_t)j * 16u;
+        s_off[tn] = r * srow;
+    }
+    // Buffer resources over the block's rows; loads take the per-thread
+    // offset in a VGPR and the step's offset in an SGPR.
+    typedef unsigned v4u __attribute__((ext_vector_type(4)));
+    const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(
+        reinterpret_cast<const char*>(X) + (size_t)m_blk * K * 2, (uint64_t)(M - m_blk) * K * 2);
+    const __amdgpu_buffer_rsrc_t pr = buffer_rsrc(
+        reinterpret_cast<const char*>(packed) + (size_t)n_blk * wrow, (uint64_t)(N - n_blk) * wrow);
+    const __amdgpu_buffer_rsrc_t sr = buffer_rsrc(
+        reinterpret_cast<const char*>(scales) + (size_t)n_blk * srow, (uint64_t)(N - n_blk) * srow);
+    const __amdgpu_buffer_rsrc_t zr =
+        ASYM ? buffer_rsrc(reinterpret_cast<const char*>(zeros) + (size_t)n_blk * srow,
+                           (uint64_t)(N - n_blk) * srow)
+             : sr;
 
-    // A staging: element e of the stage is (group slot, row, 8-block)
+    // A staging: vector i of the stage is (group slot, row, 8-block).  A
+    // slot past the last group keeps its previous (finite) values; the B of
+    // such a group is zero.
     auto load_a = [&](int step, uint4 (&regs)[A_PER_THREAD]) {
+        const int soff = step * (WK * 256);
 #pragma unroll
-        for (int i = 0; i < A_PER_THREAD; ++i) {
-            const int e = threadIdx.x + i * NT;
-            regs[i] = make_uint4(0, 0, 0, 0);
-            if (e < A_VECS) {
-                const int slot = e / (BM * 16);
-                const int rem = e - slot * BM * 16;
-                const int row = rem >> 4;
-                const int blk = rem & 15;
-                const int g = step * WK + slot;
-                const int m = m_blk + row;
-                if (g < ngroups && m < M)
-                    regs[i] = reinterpret_cast<const uint4*>(X + (size_t)m * K)[g * 16 + blk];
+        for (int i = 0; i < A_PER_THREAD; ++i)
+            if (step * WK + i / A_PER_SLOT < ngroups) {
+                const v4u v = __builtin_amdgcn_raw_buffer_load_b128(xr, a_off[i], soff, 0);
+                regs[i] = make_uint4(v.x, v.y, v.z, v.w);
             }
-        }
     };
-    auto store_a = [&](const uint4 (&regs)[A_PER_THREAD]) {
+    auto store_a = [&](int buf, const uint4 (&regs)[A_PER_THREAD]) {
+        uint4* dst = lds + buf * LDS_STAGE;
 #pragma unroll
-        for (int i = 0; i < A_PER_THREAD; ++i) {
-            const int e = threadIdx.x + i * NT;
-            if (e < A_VECS) {
-                const int slot = e / (BM * 16);
-                const int rem = e - slot * BM * 16;
-                const int row = rem >> 4;
-                const int blk = rem & 15;
-                const uint4 v = regs[i];
-                lds[(slot * BM + row) * kLdaVec + blk] = pair_block(v.x, v.y, v.z, v.w);
-            }
-        }
+        for (int i = 0; i < A_PER_THREAD; ++i)
+            dst[a_lds[i]] = pair_block(regs[i].x, regs[i].y, regs[i].z, regs[i].w);
     };
-    auto load_b = [&](int step, uint4 (&bw)[TN], uint32_t (&bs)[TN], int (&bz)[TN]) {
+    struct BRegs {
+        uint4 w[TN];
+        uint32_t s[TN];
+        int z[TN];
+    };
+    auto load_b = [&](int step, BRegs& b) {
         const int g = step * WK + wk;
+        if (g < ngroups) {
 #pragma unroll
-        for (int tn = 0; tn < TN; ++tn) {
-            if (g < ngroups) {
-                bw[tn] = packed[(size_t)brow[tn] * nchunks + g * 4 + j];
-                bs[tn] = scales[(size_t)brow[tn] * ngroups + g];
-                bz[tn] = ASYM ? (int)zeros[(size_t)brow[tn] * ngroups + g] : 0;
-            } else {
-                bw[tn] = make_uint4(0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u);
-                bs[tn] = 0;
-                bz[tn] = 0;
+            for (int tn = 0; tn < TN; ++tn) {
+                const v4u v = __builtin_amdgcn_raw_buffer_load_b128(pr, b_off[tn], g * 64, 0);
+                b.w[tn] = make_uint4(v.x, v.y, v.z, v.w);
+                b.s[tn] = __builtin_amdgcn_raw_buffer_load_b16(sr, s_off[tn], g * 2, 0);
+                b.z[tn] = ASYM ? (int)(int16_t)__builtin_amdgcn_raw_buffer_load_b16(
+                                     zr, s_off[tn], g * 2, 0)
+                               : 0;
+            }
+        } else {
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn) {
+                b.w[tn] = make_uint4(0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u);
+                b.s[tn] = 0;
+                b.z[tn] = 0;
             }
         }
     };
@@ -125,21 +159,17 @@ __global__ __launch_bounds__(WM * WN * WK * kWave) void gemm_mfma_kernel(
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = (float4_t){0.f, 0.f, 0.f, 0.f};
 
+    // One step: multiply the group(s) of step s (A in LDS buffer s & 1, B in
+    // cur), then store the A of step s + 1 (in registers since step s - 1)
+    // to the other buffer and load A and B of step s + 2.  One barrier per
+    // step orders both buffers.
     uint4 a_regs[A_PER_THREAD];
-    uint4 bw[TN], bw_next[TN];
-    uint32_t bs[TN], bs_next[TN];
-    int bz[TN], bz_next[TN];
-    load_a(0, a_regs);
-    load_b(0, bw, bs, bz);
-
-    for (int step = 0; step < nsteps; ++step) {
-        store_a(a_regs);
-        __syncthreads();
-        if (step + 1 < nsteps) {
-            load_a(step + 1, a_regs);
-            load_b(step + 1, bw_next, bs_next, bz_next);
-        }
-        const uint4* abase = lds + (wk * BM + wm * TM * 16 + l16) * kLdaVec + 4 * j;
+#pragma unroll
+    for (int i = 0; i < A_PER_THREAD; ++i) a_regs[i] = make_uint4(0, 0, 0, 0);
+    BRegs b0, b1;
+    auto step_body = [&](int step, BRegs& cur) {
+        const uint4* abase =
+            lds + (step & 1) * LDS_STAGE + (wk * BM + wm * TM * 16 + l16) * kLdaVec + 4 * j;
         if constexpr (ASYM) {
             // exact codes n - zc; the group's products scaled once in fp32
             half8_t bq[TN][4];
@@ -147,11 +177,11 @@ __global__ __launch_bounds__(WM * WN * WK * kWave) void gemm_mfma_kernel(
             bool wide = false;
 #pragma unroll
             for (int tn = 0; tn < TN; ++tn) {
-                const ZeroBias zb = zero_bias(bz[tn]);
-                sf[tn] = f16_bits_to_f32((uint16_t)bs[tn]);
-                cf[tn] = sf[tn] * (float)(zb.zc - bz[tn]);      // exact: |zc - z| < 2^15
-                wide |= zb.zc != bz[tn];
-                const uint32_t words[4] = {bw[tn].x, bw[tn].y, bw[tn].z, bw[tn].w};
+                const ZeroBias zb = zero_bias(cur.z[tn]);
+                sf[tn] = f16_bits_to_f32((uint16_t)cur.s[tn]);
+                cf[tn] = sf[tn] * (float)(zb.zc - cur.z[tn]);   // exact: |zc - z| < 2^15
+                wide |= zb.zc != cur.z[tn];
+                const uint32_t words[4] = {cur.w[tn].x, cur.w[tn].y, cur.w[tn].z, cur.w[tn].w};
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) {
                     half2_t q[4];
@@ -200,49 +230,56 @@ __global__ __launch_bounds__(WM * WN * WK * kWave) void gemm_mfma_kernel(
                         for (int r = 0; r < 4; ++r)
                             acc[tm][tn][r] = fmaf(cf[tn], xs[tm][r], acc[tm][tn][r]);
             }
-            __syncthreads();
+        } else {
+            // B fragments of this wave's group: [tn][kk]
+            half8_t bf[TN][4];
 #pragma unroll
             for (int tn = 0; tn < TN; ++tn) {
-                bw[tn] = bw_next[tn];
-                bs[tn] = bs_next[tn];
-                bz[tn] = bz_next[tn];
-            }
-            continue;
-        }
-        // B fragments of this wave's group: [tn][kk]
-        half8_t bf[TN][4];
+                const _Float16 sh = __builtin_bit_cast(_Float16, (uint16_t)cur.s[tn]);
+                const half2_t s2 = {sh, sh};
+                const uint32_t words[4] = {cur.w[tn].x, cur.w[tn].y, cur.w[tn].z, cur.w[tn].w};
 #pragma unroll
-        for (int tn = 0; tn < TN; ++tn) {
-            const _Float16 sh = __builtin_bit_cast(_Float16, (uint16_t)bs[tn]);
-            const half2_t s2 = {sh, sh};
-            const uint32_t words[4] = {bw[tn].x, bw[tn].y, bw[tn].z, bw[tn].w};
+                for (int kk = 0; kk < 4; ++kk) {
+                    half2_t h[4];
+                    dequant_word(words[kk], s2, h, kc);
+                    bf[tn][kk] = (half8_t){h[0].x, h[0].y, h[1].x, h[1].y,
+                                           h[2].x, h[2].y, h[3].x, h[3].y};
+                }
+            }
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
-                half2_t h[4];
-                dequant_word(words[kk], s2, h, kc);
-                bf[tn][kk] = (half8_t){h[0].x, h[0].y, h[1].x, h[1].y,
-                                       h[2].x, h[2].y, h[3].x, h[3].y};
+#pragma unroll
+                for (int tm = 0; tm < TM; ++tm) {
+                    const uint4 av = abase[tm * 16 * kLdaVec + kk];
+                    const half8_t af = __builtin_bit_cast(half8_t, av);
+#pragma unroll
+                    for (int tn = 0; tn < TN; ++tn)
+                        acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[tn][kk],
+                                                                             acc[tm][tn], 0, 0, 0);
+                }
             }
         }
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-#pragma unroll
-            for (int tm = 0; tm < TM; ++tm) {
-                const uint4 av = abase[tm * 16 * kLdaVec + kk];
-                const half8_t af = __builtin_bit_cast(half8_t, av);
-#pragma unroll
-                for (int tn = 0; tn < TN; ++tn)
-                    acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[tn][kk],
-                                                                         acc[tm][tn], 0, 0, 0);
+        if (step + 1 < nsteps) {
+            store_a((step + 1) & 1, a_regs);
+            if (step + 2 < nsteps) {
+                load_a(step + 2, a_regs);
+                load_b(step + 2, cur);    // cur is consumed; it next serves step s + 2
             }
         }
         __syncthreads();
-#pragma unroll
-        for (int tn = 0; tn < TN; ++tn) {
-            bw[tn] = bw_next[tn];
-            bs[tn] = bs_next[tn];
-            bz[tn] = bz_next[tn];
-        }
+    };
+
+    load_a(0, a_regs);
+    load_b(0, b0);
+    store_a(0, a_regs);
+    if (nsteps > 1) {
+        load_a(1, a_regs);
+        load_b(1, b1);
+    }
+    __syncthreads();
+    for (int step = 0; step < nsteps; step += 2) {
+        step_body(step, b0);
+        if (step + 1 < nsteps) step_body(step + 1, b1);
     }
 
     if constexpr (WK > 1) {
@@ -292,7 +329,7 @@ hipError_t launch_mfma_t(const uint16_t* X, int64_t M, const uint32_t* packed,
                          hipStream_t stream, const int16_t* zeros = nullptr) {
     constexpr int BM = 16 * TM * WM;
     constexpr int BN = 16 * TN * WN;
-    const size_t a_bytes = (size_t)WK * BM * kLdaVec * sizeof(uint4);
+    const size_t a_bytes = (size_t)2 * WK * BM * kLdaVec * sizeof(uint4);   // two A buffers
     const size_t red_bytes = (size_t)(WK - 1) * WM * WN * TM * TN * 64 * sizeof(float4_t);
     const size_t lds = a_bytes > red_bytes ? a_bytes : red_bytes;
     auto kern = gemm_mfma_kernel<TM, TN, WM, WN, WK, ASYM>;
@@ -314,6 +351,9 @@ template <bool ASYM>
 hipError_t launch_tiled(const uint16_t* X, int64_t M, const uint32_t* packed,
                         const uint16_t* scales, const int16_t* zeros, int64_t N, int64_t K,
                         uint16_t* Y, hipStream_t stream, int num_cu) {
+    if (K > kTiledMaxK)
+        return launch_gemv_valu(X, M, packed, scales, N, K, Y, stream, num_cu, 2, nullptr,
+                                ASYM ? zeros : nullptr);
     // Few rows: one 16- or 32-row tile, waves split K; enough column tiles
     // to give every compute unit work.
     if (M <= 16) {

@@ -42,6 +42,9 @@ hipError_t launch_gemm_mfma(const uint16_t* X, int64_t M, const uint32_t* packed
 
 // MFMA path for asymmetric weights (zeros: int16 [N, K/128]), any M: the
 // tiled kernel with exact codes n - z and per-group fp32 scaling.
+// The tiled kernel addresses a block's rows with 32-bit offsets; rows
+// longer than kTiledMaxK elements run on the VALU path instead.
+constexpr int64_t kTiledMaxK = (int64_t)1 << 22;
 hipError_t launch_gemm_mfma_asym(const uint16_t* X, int64_t M, const uint32_t* packed,
                                  const uint16_t* scales, const int16_t* zeros, int64_t N,
                                  int64_t K, uint16_t* Y, hipStream_t stream, int num_cu);
