@@ -258,5 +258,13 @@ def get() -> Oracle:
 
 
 def tolerance(y_ref: np.ndarray, y_abs: np.ndarray) -> np.ndarray:
-    """Allowed |y - y_ref| per output element: 1e-3 * sum_k |x_k w_k| + 2^-10 |y_ref|."""
-    return 1e-3 * np.asarray(y_abs) + 2.0 ** -10 * np.abs(np.asarray(y_ref))
+    """Allowed |y - y_ref| per output element:
+    1e-3 * sum_k |x_k w_k| + max(2^-10 |y_ref|, 2^-24).
+
+    The second term is the allowance for storing y in fp16 (two half-ulps
+    of a normal fp16 value).  Below the smallest normal fp16 (2^-14) the
+    fp16 grid is uniform with step 2^-24, so there it is one step: even the
+    correctly rounded fp16(y_ref) can sit 2^-25 from y_ref, which 2^-10
+    |y_ref| alone would not allow."""
+    return 1e-3 * np.asarray(y_abs) + np.maximum(2.0 ** -10 * np.abs(np.asarray(y_ref)),
+                                                 2.0 ** -24)
