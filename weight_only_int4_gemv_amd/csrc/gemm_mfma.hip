@@ -368,13 +368,21 @@ hipError_t launch_tiled(const uint16_t* X, int64_t M, const uint32_t* packed,
     }
     if (M <= 64)
         return launch_mfma_t<2, 2, 2, 2, 1, ASYM>(X, M, packed, scales, N, K, Y, stream, zeros);
-    // Prefill: 128 x 128 block tiles (eight 16-row tiles by two 16-column
-    // tiles per wave, four waves across N) when they fill the compute units,
-    // else 128 x 64 tiles with eight waves, two over K (measured on gfx950,
-    // M = 512 on 14336 x 4096: 127 us against 155 us with four waves).
+    // Prefill: when 128 x 128 tiles fill the compute units, 128 x 256 block
+    // tiles (eight 16-row by two 16-column tiles per wave, eight waves across
+    // N: each staged X tile serves 256 columns; M = 512 on 4096 x 14336 at
+    // 76 us against 81 us with 128 x 128 blocks, on 8192 x 28672 316 against
+    // 338 us) — asymmetric weights keep 128 x 128 blocks of four waves, whose
+    // registers do not fit two waves per SIMD; else 128 x 64 tiles with eight
+    // waves, two over K (M = 512 on 14336 x 4096: 127 us against 155 us with
+    // four waves, before the double-buffered staging).
     const int64_t tiles128 = ((M + 127) / 128) * ((N + 127) / 128);
-    if (tiles128 >= num_cu)
-        return launch_mfma_t<8, 2, 1, 4, 1, ASYM>(X, M, packed, scales, N, K, Y, stream, zeros);
+    if (tiles128 >= num_cu) {
+        if constexpr (ASYM)
+            return launch_mfma_t<8, 2, 1, 4, 1, ASYM>(X, M, packed, scales, N, K, Y, stream,
+                                                      zeros);
+        return launch_mfma_t<8, 2, 1, 8, 1, ASYM>(X, M, packed, scales, N, K, Y, stream, zeros);
+    }
     return launch_mfma_t<4, 2, 2, 2, 2, ASYM>(X, M, packed, scales, N, K, Y, stream, zeros);
 }
 
