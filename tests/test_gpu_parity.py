@@ -728,11 +728,20 @@ def test_linear_asym(w4, orc, group, M, N, K):
 @pytest.mark.parametrize("M", [3, 16, 17, 32, 33, 64, 65, 200, 512])
 @pytest.mark.parametrize("N,K", [(300, 4096), (64, 14336), (1000, 1152)])
 def test_linear_asym_matrix_cores(w4, orc, M, N, K):
-    """M > 2 at group 128 runs on the tiled matrix-core kernel (every tile
-    shape family: 16- and 32-row tiles with K split over waves, 64-row,
-    128-row prefill tiles), planted |z| > 1000 groups (the ones-MFMA
-    correction) included."""
+    """M > 2 at group 128 runs on the matrix cores: the batched decode kernel
+    up to 32 rows, the tiled kernel above (64-row and 128-row prefill
+    tiles), planted |z| > 1000 groups (the ones-MFMA correction) included."""
     check_linear_asym(w4, orc, M, N, K, 128, [47, M, N, K])
+
+
+@pytest.mark.parametrize("M", [5, 16, 20, 32])
+@pytest.mark.parametrize("N,K", [(4104, 2176), (9000, 1152), (30000, 1152), (300, 14464)])
+def test_linear_asym_batched_wave_grids(w4, orc, M, N, K):
+    """Asymmetric weights on the batched decode kernel: every wave-grid class
+    (rows per block 17, 36 and 118: two, four and eight 16-row tiles), K
+    ragged against the staged X chunks, 16- and 32-row X tiles, planted
+    |z| > 1000 groups."""
+    check_linear_asym(w4, orc, M, N, K, 128, [48, M, N, K])
 
 
 @pytest.mark.parametrize("name,K,N", [("llama down", 14336, 4096), ("llama gate", 4096, 14336),

@@ -37,6 +37,14 @@
 // Rows past M read a clamped row of the staged X (their outputs are never
 // stored); rows past the block's range and k past K read 0 through buffer
 // bounds, and groups past K are skipped.
+//
+// Asymmetric weights (ASYM, [QUANT] sub-section 2: w = s (n - z), nibble n
+// in [0, 15], an int16 zero point z per row and group): the zero points are
+// staged beside the scales, the B operand holds the exact codes n - zc
+// (codes_word_zp, zc = z clamped to +-1000), and a group with |z| > 1000
+// adds s (zc - z) times the group's activation sums, which one more MFMA
+// per k-step against a B of ones forms (only in waves that hold such a
+// group), as the tiled kernel does.
 #include "w4a16_device.h"
 #include "w4a16_launch.h"
 
@@ -50,11 +58,11 @@ constexpr int kBatchedScales = 4;                   // staged scales per thread 
 // MT: 16-row tiles of X; TN: 16-row weight tiles per wave; WR x WKS: wave
 // grid; GPW: groups per wave and chunk (chunk = GPW * WKS groups); Q: weight
 // ring slots (power of two).
-template <int MT, int TN, int WR, int WKS, int GPW, int Q>
+template <int MT, int TN, int WR, int WKS, int GPW, int Q, bool ASYM>
 __global__ __launch_bounds__(WR * WKS * kWave) void gemm_batched_kernel(
     const uint16_t* __restrict__ X, int M, const uint32_t* __restrict__ packed,
-    const uint16_t* __restrict__ scales, uint16_t* __restrict__ Y, int N, int K,
-    int rows_per_block) {
+    const uint16_t* __restrict__ scales, const int16_t* __restrict__ zeros,
+    uint16_t* __restrict__ Y, int N, int K, int rows_per_block) {
     constexpr int NT = WR * WKS * kWave;
     constexpr int P = Q - 1;                          // groups in flight ahead of use
     constexpr int U = Q > GPW ? Q / GPW : 1;          // chunks per unrolled body
@@ -72,6 +80,7 @@ __global__ __launch_bounds__(WR * WKS * kWave) void gemm_batched_kernel(
     static_assert(SBUF <= SV * NT, "scale chunk exceeds the staging registers");
     extern __shared__ uint4 lds[];                    // 2 x [xrows][XSTRIDE] paired X,
                                                       // then 2 x [SROWS][GC] scales
+                                                      // (and as many zero points)
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -87,6 +96,7 @@ __global__ __launch_bounds__(WR * WKS * kWave) void gemm_batched_kernel(
     const int xbuf = xrows * XSTRIDE;
     const int xtotal = xrows * CBLK;
     uint16_t* const slds = reinterpret_cast<uint16_t*>(lds + 2 * xbuf);
+    int16_t* const zlds = reinterpret_cast<int16_t*>(slds + 2 * SBUF);
     const int c_first = (int)(blockIdx.x % (unsigned)nchunks);
     const uint32_t wrow = (uint32_t)K / 2, srow = (uint32_t)K / 64;
     const uint32_t xbytes = (uint32_t)M * (uint32_t)K * 2u;
@@ -98,6 +108,8 @@ __global__ __launch_bounds__(WR * WKS * kWave) void gemm_batched_kernel(
         reinterpret_cast<const char*>(packed) + (size_t)r0 * wrow, (uint64_t)nrows * wrow);
     const __amdgpu_buffer_rsrc_t sr = buffer_rsrc(
         reinterpret_cast<const char*>(scales) + (size_t)r0 * srow, sbytes);
+    const __amdgpu_buffer_rsrc_t zr =
+        ASYM ? buffer_rsrc(reinterpret_cast<const char*>(zeros) + (size_t)r0 * srow, sbytes) : sr;
     const __amdgpu_buffer_rsrc_t empty = buffer_rsrc(packed, 0);
     const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(X, xbytes);
 
@@ -112,7 +124,7 @@ __global__ __launch_bounds__(WR * WKS * kWave) void gemm_batched_kernel(
     // start runs the same code (chunks past the end load nothing), so the
     // compiler knows at every weight wait exactly which loads are younger.
     v4u xv[XV];
-    uint32_t sv[SV];
+    uint32_t sv[SV], zv[SV];
     auto x_load = [&](int cc) {
         const bool live = cc < nchunks;
         const int c = chunk_of(cc);
@@ -133,6 +145,7 @@ __global__ __launch_bounds__(WR * WKS * kWave) void gemm_batched_kernel(
                                      ? (uint32_t)(e / GC) * srow + (uint32_t)(c * GC + e % GC) * 2u
                                      : sbytes;
             sv[i] = __builtin_amdgcn_raw_buffer_load_b16(sr, off, 0, 0);
+            zv[i] = ASYM ? __builtin_amdgcn_raw_buffer_load_b16(zr, off, 0, 0) : 0u;
         }
     };
     auto x_store = [&](int buf) {
@@ -146,7 +159,10 @@ __global__ __launch_bounds__(WR * WKS * kWave) void gemm_batched_kernel(
 #pragma unroll
         for (int i = 0; i < SV; ++i) {
             const int e = threadIdx.x + i * NT;
-            if (e < SBUF) slds[buf * SBUF + e] = (uint16_t)sv[i];
+            if (e < SBUF) {
+                slds[buf * SBUF + e] = (uint16_t)sv[i];
+                if constexpr (ASYM) zlds[buf * SBUF + e] = (int16_t)(uint16_t)zv[i];
+            }
         }
     };
 
@@ -204,6 +220,16 @@ __global__ __launch_bounds__(WR * WKS * kWave) void gemm_batched_kernel(
                 if (cc < nchunks && cbase + gl < ngroups) {   // wave-uniform
                     const Slot& sl = ring[sidx % Q];
                     const uint4* xb = lds + buf * xbuf + gl * 16 + 4 * j;
+                    ZeroBias zb[TN];
+                    bool wide = false;
+                    if constexpr (ASYM) {
+#pragma unroll
+                        for (int tn = 0; tn < TN; ++tn) {
+                            const int z = zlds[buf * SBUF + (16 * (wr + WR * tn) + l16) * GC + gl];
+                            zb[tn] = zero_bias(z);
+                            wide |= zb[tn].zc != z;
+                        }
+                    }
                     float4_t d[MT][TN];
 #pragma unroll
                     for (int kk = 0; kk < 4; ++kk) {
@@ -211,7 +237,10 @@ __global__ __launch_bounds__(WR * WKS * kWave) void gemm_batched_kernel(
 #pragma unroll
                         for (int tn = 0; tn < TN; ++tn) {
                             half2_t q[4];
-                            codes_word(sl.w[tn][kk], kcst, q);
+                            if constexpr (ASYM)
+                                codes_word_zp(sl.w[tn][kk], kcst, zb[tn], q);
+                            else
+                                codes_word(sl.w[tn][kk], kcst, q);
                             bq[tn] = (half8_t){q[0].x, q[0].y, q[1].x, q[1].y,
                                                q[2].x, q[2].y, q[3].x, q[3].y};
                         }
@@ -235,6 +264,35 @@ __global__ __launch_bounds__(WR * WKS * kWave) void gemm_batched_kernel(
 #pragma unroll
                             for (int r = 0; r < 4; ++r)
                                 acc[mt][tn][r] = fmaf(sc, d[mt][tn][r], acc[mt][tn][r]);
+                    }
+                    if constexpr (ASYM) {
+                        if (__any(wide)) {
+                            // activation sums of the group's 128 k for each X row
+                            const _Float16 one = (_Float16)1.0f;
+                            const half8_t ones = {one, one, one, one, one, one, one, one};
+                            float4_t xs[MT];
+#pragma unroll
+                            for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                                for (int mt = 0; mt < MT; ++mt)
+                                    xs[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                                        __builtin_bit_cast(half8_t, xb[xrow_off[mt] + kk]), ones,
+                                        kk == 0 ? (float4_t){0.f, 0.f, 0.f, 0.f} : xs[mt], 0, 0,
+                                        0);
+#pragma unroll
+                            for (int tn = 0; tn < TN; ++tn) {
+                                const int row = 16 * (wr + WR * tn) + l16;
+                                const int z = zlds[buf * SBUF + row * GC + gl];
+                                const float cf =
+                                    f16_bits_to_f32(slds[buf * SBUF + row * GC + gl]) *
+                                    (float)(zb[tn].zc - z);
+#pragma unroll
+                                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                                    for (int r = 0; r < 4; ++r)
+                                        acc[mt][tn][r] = fmaf(cf, xs[mt][r], acc[mt][tn][r]);
+                            }
+                        }
                     }
                 }
             }
@@ -277,28 +335,28 @@ __global__ __launch_bounds__(WR * WKS * kWave) void gemm_batched_kernel(
     }
 }
 
-template <int MT, int TN, int WR, int WKS, int GPW, int Q>
+template <int MT, int TN, int WR, int WKS, int GPW, int Q, bool ASYM>
 hipError_t launch_batched_t(const uint16_t* X, int64_t M, const uint32_t* packed,
-                            const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y,
-                            hipStream_t stream, int64_t rows_per_block) {
+                            const uint16_t* scales, const int16_t* zeros, int64_t N, int64_t K,
+                            uint16_t* Y, hipStream_t stream, int64_t rows_per_block) {
     constexpr int NT = WR * WKS * kWave;
     constexpr int64_t KC = (int64_t)GPW * WKS * kGroup;
     const int64_t xrows = M < 16 * MT ? M : 16 * MT;
     if (rows_per_block > 16 * WR * TN || M > 16 * MT) return hipErrorInvalidValue;
     const size_t x_lds = (size_t)2 * xrows * (KC / 8 + 1) * 16 +
-                         (size_t)2 * (16 * WR * TN) * (KC / kGroup) * 2;
+                         (size_t)(ASYM ? 2 : 1) * 2 * (16 * WR * TN) * (KC / kGroup) * 2;
     const size_t red_lds = (size_t)(WKS - 1) * WR * MT * TN * kWave * sizeof(float4_t);
     const size_t lds = x_lds > red_lds ? x_lds : red_lds;
     if (lds > 64 * 1024) {
         const hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void*>(gemm_batched_kernel<MT, TN, WR, WKS, GPW, Q>),
+            reinterpret_cast<const void*>(gemm_batched_kernel<MT, TN, WR, WKS, GPW, Q, ASYM>),
             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
     const int64_t blocks = (N + rows_per_block - 1) / rows_per_block;
-    hipLaunchKernelGGL((gemm_batched_kernel<MT, TN, WR, WKS, GPW, Q>), dim3((unsigned)blocks),
-                       dim3(NT), lds, stream, X, (int)M, packed, scales, Y, (int)N, (int)K,
-                       (int)rows_per_block);
+    hipLaunchKernelGGL((gemm_batched_kernel<MT, TN, WR, WKS, GPW, Q, ASYM>),
+                       dim3((unsigned)blocks), dim3(NT), lds, stream, X, (int)M, packed, scales,
+                       zeros, Y, (int)N, (int)K, (int)rows_per_block);
     return hipGetLastError();
 }
 
@@ -308,30 +366,42 @@ hipError_t launch_batched_t(const uint16_t* X, int64_t M, const uint32_t* packed
 // 16, 32): two 16-row tiles per wave with a 2 x 4 wave grid for 17..64 rows a
 // block, four tiles for more, eight waves over K for at most 16 rows (the
 // down projection); four ring slots, two for the widest tiles.
-template <int MT>
+template <int MT, bool ASYM>
 hipError_t launch_batched_m(const uint16_t* X, int64_t M, const uint32_t* packed,
-                            const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y,
-                            hipStream_t stream, int num_cu) {
+                            const uint16_t* scales, const int16_t* zeros, int64_t N, int64_t K,
+                            uint16_t* Y, hipStream_t stream, int num_cu) {
     // one block per compute unit, rows split evenly; at most 128 rows a block
     int64_t rpb = (N + num_cu - 1) / num_cu;
     if (rpb > 128) rpb = 128;
     const int64_t tiles = (rpb + 15) / 16;
     constexpr int G = 16 / MT;                        // groups per chunk
     if (tiles <= 1)
-        return launch_batched_t<MT, 1, 1, 8, G / 8, 4 / MT>(X, M, packed, scales, N, K, Y, stream,
-                                                            rpb);
+        return launch_batched_t<MT, 1, 1, 8, G / 8, 4 / MT, ASYM>(X, M, packed, scales, zeros, N,
+                                                                  K, Y, stream, rpb);
     if (tiles <= 2)
-        return launch_batched_t<MT, 2, 1, 8, G / 8, 4>(X, M, packed, scales, N, K, Y, stream, rpb);
+        return launch_batched_t<MT, 2, 1, 8, G / 8, 4, ASYM>(X, M, packed, scales, zeros, N, K,
+                                                             Y, stream, rpb);
     if (tiles <= 4)
-        return launch_batched_t<MT, 2, 2, 4, G / 4, 4>(X, M, packed, scales, N, K, Y, stream, rpb);
-    return launch_batched_t<MT, 4, 2, 4, G / 4, 2>(X, M, packed, scales, N, K, Y, stream, rpb);
+        return launch_batched_t<MT, 2, 2, 4, G / 4, 4, ASYM>(X, M, packed, scales, zeros, N, K,
+                                                             Y, stream, rpb);
+    return launch_batched_t<MT, 4, 2, 4, G / 4, 2, ASYM>(X, M, packed, scales, zeros, N, K, Y,
+                                                         stream, rpb);
 }
 
 hipError_t launch_gemm_batched(const uint16_t* X, int64_t M, const uint32_t* packed,
                                const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y,
                                hipStream_t stream, int num_cu) {
-    if (M <= 16) return launch_batched_m<1>(X, M, packed, scales, N, K, Y, stream, num_cu);
-    return launch_batched_m<2>(X, M, packed, scales, N, K, Y, stream, num_cu);
+    if (M <= 16)
+        return launch_batched_m<1, false>(X, M, packed, scales, nullptr, N, K, Y, stream, num_cu);
+    return launch_batched_m<2, false>(X, M, packed, scales, nullptr, N, K, Y, stream, num_cu);
+}
+
+hipError_t launch_gemm_batched_asym(const uint16_t* X, int64_t M, const uint32_t* packed,
+                                    const uint16_t* scales, const int16_t* zeros, int64_t N,
+                                    int64_t K, uint16_t* Y, hipStream_t stream, int num_cu) {
+    if (M <= 16)
+        return launch_batched_m<1, true>(X, M, packed, scales, zeros, N, K, Y, stream, num_cu);
+    return launch_batched_m<2, true>(X, M, packed, scales, zeros, N, K, Y, stream, num_cu);
 }
 
 }  // namespace w4a16

@@ -408,6 +408,9 @@ hipError_t launch_gemm_mfma(const uint16_t* X, int64_t M, const uint32_t* packed
 hipError_t launch_gemm_mfma_asym(const uint16_t* X, int64_t M, const uint32_t* packed,
                                  const uint16_t* scales, const int16_t* zeros, int64_t N,
                                  int64_t K, uint16_t* Y, hipStream_t stream, int num_cu) {
+    // Batched decode: blocks own contiguous weight rows, X through LDS.
+    if (M <= kBatchedMaxM && K > 0 && K <= kBatchedMaxK)
+        return launch_gemm_batched_asym(X, M, packed, scales, zeros, N, K, Y, stream, num_cu);
     return launch_tiled<true>(X, M, packed, scales, zeros, N, K, Y, stream, num_cu);
 }
 

@@ -65,6 +65,10 @@ constexpr int64_t kBatchedMaxK = (int64_t)1 << 24;
 hipError_t launch_gemm_batched(const uint16_t* X, int64_t M, const uint32_t* packed,
                                const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y,
                                hipStream_t stream, int num_cu);
+// The same for asymmetric weights (zeros: int16 [N, K/128]).
+hipError_t launch_gemm_batched_asym(const uint16_t* X, int64_t M, const uint32_t* packed,
+                                    const uint16_t* scales, const int16_t* zeros, int64_t N,
+                                    int64_t K, uint16_t* Y, hipStream_t stream, int num_cu);
 
 // MFMA path for few rows of X (gemm_skinny.hip): weights streamed once,
 // waves split K.  Requires K <= kSkinnyMaxK (32-bit buffer offsets).
