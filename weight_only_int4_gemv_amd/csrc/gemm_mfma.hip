@@ -381,7 +381,9 @@ hipError_t launch_tiled(const uint16_t* X, int64_t M, const uint32_t* packed,
         if constexpr (ASYM)
             return launch_mfma_t<8, 2, 1, 4, 1, ASYM>(X, M, packed, scales, N, K, Y, stream,
                                                       zeros);
-        return launch_mfma_t<8, 2, 1, 8, 1, ASYM>(X, M, packed, scales, N, K, Y, stream, zeros);
+        else
+            return launch_mfma_t<8, 2, 1, 8, 1, ASYM>(X, M, packed, scales, N, K, Y, stream,
+                                                      zeros);
     }
     return launch_mfma_t<4, 2, 2, 2, 2, ASYM>(X, M, packed, scales, N, K, Y, stream, zeros);
 }
