@@ -373,9 +373,7 @@ hipError_t launch_tiled(const uint16_t* X, int64_t M, const uint32_t* packed,
     // N: each staged X tile serves 256 columns; M = 512 on 4096 x 14336 at
     // 76 us against 81 us with 128 x 128 blocks, on 8192 x 28672 316 against
     // 338 us) — asymmetric weights keep 128 x 128 blocks of four waves, whose
-    // registers do not fit two waves per SIMD; else 128 x 64 tiles with eight
-    // waves, two over K (M = 512 on 14336 x 4096: 127 us against 155 us with
-    // four waves, before the double-buffered staging).
+    // registers do not fit two waves per SIMD.
     const int64_t tiles128 = ((M + 127) / 128) * ((N + 127) / 128);
     if (tiles128 >= num_cu) {
         if constexpr (ASYM)
@@ -385,7 +383,14 @@ hipError_t launch_tiled(const uint16_t* X, int64_t M, const uint32_t* packed,
             return launch_mfma_t<8, 2, 1, 8, 1, ASYM>(X, M, packed, scales, N, K, Y, stream,
                                                       zeros);
     }
-    return launch_mfma_t<4, 2, 2, 2, 2, ASYM>(X, M, packed, scales, N, K, Y, stream, zeros);
+    // Else 128 x 64 block tiles, eight waves, two over K: for symmetric
+    // weights four waves across N with 128 x 16 wave tiles (M = 512 on
+    // 14336 x 4096: 110 us against 117 us with 64 x 32 wave tiles, which the
+    // asymmetric kernel keeps: its 128 x 16 tiles would spill).
+    if constexpr (ASYM)
+        return launch_mfma_t<4, 2, 2, 2, 2, ASYM>(X, M, packed, scales, N, K, Y, stream, zeros);
+    else
+        return launch_mfma_t<8, 1, 1, 4, 2, ASYM>(X, M, packed, scales, N, K, Y, stream, zeros);
 }
 
 }  // namespace
