@@ -302,6 +302,43 @@ def test_prefill_wide_tiles_ragged(w4, orc, M, N, K):
     assert bad.size == 0, "%d outputs out of tolerance, first %s" % (len(bad), bad[0])
 
 
+@pytest.mark.parametrize("M,N,K,algo", [(1, 64, 512, "gemv"), (3, 64, 512, "valu"),
+                                         (3, 64, 512, "mfma"), (16, 64, 512, "mfma"),
+                                         (40, 64, 512, "mfma"), (65, 64, 512, "mfma"),
+                                         (512, 64, 512, "mfma"), (256, 16384, 256, "mfma")])
+def test_largest_fp16_weights_stay_finite(w4, orc, M, N, K, algo):
+    """Groups whose absmax is the largest finite fp16 (65504) get s = 9360,
+    and s * 7 = 65520 is a tie that rounds to infinity in fp16.  Every kernel
+    family (GEMV, VALU, 4x4x4, batched, streaming, both tiled block shapes)
+    must keep these weights finite and match the oracle within tolerance
+    (the kernels that form fp16 weights clamp them to +-65504: error 16 in
+    65520, 2.4e-4 relative)."""
+    W = inputs.weight(N, K, seed=[35, N, K])
+    W[::3, 5] = np.float16(65504.0)
+    W[1::3, K // 2 + 3] = np.float16(-65504.0)
+    W[2::7, K - 7] = np.float16(65472.0)                  # s = 9352: 7 s = 65464 stays finite
+    packed, scales = orc.quantize(W)
+    assert (scales.view(np.uint16) == 0x7092).any()      # s = 9360 present
+    X = (inputs.activation(M, K, seed=[36, M]).astype(np.float32) * 2.0 ** -8).astype(np.float16)
+    say("largest weights %s M=%d N=%d K=%d" % (algo, M, N, K))
+    Y = run_linear(w4, X, packed, scales, algo)
+    torch.cuda.synchronize()
+    Yref, Yabs = orc.matmul(X, packed, scales)
+    assert np.isfinite(Yref).all() and np.abs(Yref).max() < 60000
+    got = Y.astype(np.float64)
+    assert np.isfinite(got).all(), "%d non-finite outputs" % (~np.isfinite(got)).sum()
+    bad = np.argwhere(~(np.abs(got - Yref) <= oracle.tolerance(Yref, Yabs)))
+    assert bad.size == 0, "%d outputs out of tolerance, first %s" % (len(bad), bad[0])
+
+
+def test_tiled_rows_past_32bit_offsets_fall_back(w4, orc):
+    """Rows longer than 2^22 elements do not fit the tiled kernel's 32-bit
+    block offsets; with 65 rows of X (past the batched and streaming
+    kernels) such a product runs on the VALU path and still matches."""
+    M, N, K = 65, 8, (1 << 22) + 128
+    check_linear(w4, orc, M, N, K, seed=([33, K], [34, K]), algo="mfma", name="long K")
+
+
 def test_70b_ffn_decode(w4, orc):
     check_linear(w4, orc, 1, 28672, 8192, seed=[5, 1, 8192], algo="auto", name="70b m1")
 

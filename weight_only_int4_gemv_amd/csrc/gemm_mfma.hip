@@ -33,6 +33,7 @@
 // k-step against a B of ones forms (only in waves that hold such a group).
 #include "w4a16_device.h"
 #include "w4a16_launch.h"
+#include "w4a16_fp16_weights.h"
 
 namespace w4a16 {
 
@@ -167,7 +168,7 @@ __attribute__((amdgpu_waves_per_eu(ASYM ? 1 : 2))) void gemm_mfma_kernel(
 #pragma unroll
     for (int i = 0; i < A_PER_THREAD; ++i) a_regs[i] = make_uint4(0, 0, 0, 0);
     BRegs b0, b1;
-    auto step_body = [&](int step, BRegs& cur) {
+    auto step_body = [&](int step, BRegs& cur, auto clamp) {
         const uint4* abase =
             lds + (step & 1) * LDS_STAGE + (wk * BM + wm * TM * 16 + l16) * kLdaVec + 4 * j;
         if constexpr (ASYM) {
@@ -232,32 +233,37 @@ __attribute__((amdgpu_waves_per_eu(ASYM ? 1 : 2))) void gemm_mfma_kernel(
             }
         } else {
             // B fragments of this wave's group: [tn][kk]
-            half8_t bf[TN][4];
+            auto mma = [&](auto clamp) {
+                half8_t bf[TN][4];
 #pragma unroll
-            for (int tn = 0; tn < TN; ++tn) {
-                const _Float16 sh = __builtin_bit_cast(_Float16, (uint16_t)cur.s[tn]);
-                const half2_t s2 = {sh, sh};
-                const uint32_t words[4] = {cur.w[tn].x, cur.w[tn].y, cur.w[tn].z, cur.w[tn].w};
+                for (int tn = 0; tn < TN; ++tn) {
+                    const _Float16 sh = __builtin_bit_cast(_Float16, (uint16_t)cur.s[tn]);
+                    const half2_t s2 = {sh, sh};
+                    const uint32_t words[4] = {cur.w[tn].x, cur.w[tn].y, cur.w[tn].z,
+                                               cur.w[tn].w};
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk) {
+                        half2_t h[4];
+                        dequant_word(words[kk], s2, h, kc);
+                        bf[tn][kk] = (half8_t){h[0].x, h[0].y, h[1].x, h[1].y,
+                                               h[2].x, h[2].y, h[3].x, h[3].y};
+                    }
+                }
+                if constexpr (decltype(clamp)::value) clamp_fp16_weights(bf);
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) {
-                    half2_t h[4];
-                    dequant_word(words[kk], s2, h, kc);
-                    bf[tn][kk] = (half8_t){h[0].x, h[0].y, h[1].x, h[1].y,
-                                           h[2].x, h[2].y, h[3].x, h[3].y};
+#pragma unroll
+                    for (int tm = 0; tm < TM; ++tm) {
+                        const uint4 av = abase[tm * 16 * kLdaVec + kk];
+                        const half8_t af = __builtin_bit_cast(half8_t, av);
+#pragma unroll
+                        for (int tn = 0; tn < TN; ++tn)
+                            acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                                af, bf[tn][kk], acc[tm][tn], 0, 0, 0);
+                    }
                 }
-            }
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-#pragma unroll
-                for (int tm = 0; tm < TM; ++tm) {
-                    const uint4 av = abase[tm * 16 * kLdaVec + kk];
-                    const half8_t af = __builtin_bit_cast(half8_t, av);
-#pragma unroll
-                    for (int tn = 0; tn < TN; ++tn)
-                        acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[tn][kk],
-                                                                             acc[tm][tn], 0, 0, 0);
-                }
-            }
+            };
+            mma(clamp);
         }
         if (step + 1 < nsteps) {
             store_a((step + 1) & 1, a_regs);
@@ -269,6 +275,27 @@ __attribute__((amdgpu_waves_per_eu(ASYM ? 1 : 2))) void gemm_mfma_kernel(
         __syncthreads();
     };
 
+    // Does any row of this block hold a group whose scale reaches 9360 (the
+    // one case where fp16(s * q) can overflow)?  The block's scales are one
+    // contiguous span, scanned once; the K loop below then exists in two
+    // copies and the common one carries no check.
+    bool huge = false;
+    if constexpr (!ASYM) {
+        const uint32_t span = (uint32_t)min(BN, N - n_blk) * srow;
+        if ((reinterpret_cast<uintptr_t>(scales) & 15) == 0 && (srow & 15) == 0) {
+            for (uint32_t off = threadIdx.x * 16u; off < span; off += NT * 16u) {
+                const v4u v = __builtin_amdgcn_raw_buffer_load_b128(sr, off, 0, 0);
+                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    huge |= (w[i] & 0xFFFFu) >= kHugeScaleBits || (w[i] >> 16) >= kHugeScaleBits;
+            }
+        } else {
+            for (uint32_t off = threadIdx.x * 2u; off < span; off += NT * 2u)
+                huge |= __builtin_amdgcn_raw_buffer_load_b16(sr, off, 0, 0) >= kHugeScaleBits;
+        }
+    }
+
     load_a(0, a_regs);
     load_b(0, b0);
     store_a(0, a_regs);
@@ -276,11 +303,24 @@ __attribute__((amdgpu_waves_per_eu(ASYM ? 1 : 2))) void gemm_mfma_kernel(
         load_a(1, a_regs);
         load_b(1, b1);
     }
+    // block-wide OR of the scan: one word per wave, read after the barrier
+    __shared__ uint32_t huge_waves[NT / kWave];
+    const bool wave_huge = __any(huge);
+    if (lane == 0) huge_waves[wave] = wave_huge ? 1u : 0u;
     __syncthreads();
-    for (int step = 0; step < nsteps; step += 2) {
-        step_body(step, b0);
-        if (step + 1 < nsteps) step_body(step + 1, b1);
-    }
+    huge = false;
+#pragma unroll
+    for (int w = 0; w < NT / kWave; ++w) huge |= huge_waves[w] != 0u;
+    auto k_loop = [&](auto clamp) {
+        for (int step = 0; step < nsteps; step += 2) {
+            step_body(step, b0, clamp);
+            if (step + 1 < nsteps) step_body(step + 1, b1, clamp);
+        }
+    };
+    if (!ASYM && huge)
+        k_loop(std::integral_constant<bool, !ASYM>{});
+    else
+        k_loop(std::false_type{});
 
     if constexpr (WK > 1) {
         // Sum the WK partial tiles: waves wk > 0 publish, wave wk == 0 adds.

@@ -20,6 +20,7 @@
 //     wave's range use an empty buffer resource, and rows past M or N read 0.
 #include "w4a16_device.h"
 #include "w4a16_launch.h"
+#include "w4a16_fp16_weights.h"
 
 namespace w4a16 {
 
@@ -101,32 +102,40 @@ __global__ __launch_bounds__(WK * kWave) void gemm_skinny_kernel(
             load(t0 + i + P, ring[(i + P) % Q]);
             if (t0 + i >= Tw) continue;                  // wave-uniform
             const Slot& sl = ring[i];
-            half8_t bf[TN][4];
+            auto mma = [&](auto clamp) {
+                half8_t bf[TN][4];
 #pragma unroll
-            for (int tn = 0; tn < TN; ++tn) {
-                const _Float16 sh = __builtin_bit_cast(_Float16, (uint16_t)sl.s[tn]);
-                const half2_t s2 = {sh, sh};
-                const uint32_t words[4] = {sl.b[tn].x, sl.b[tn].y, sl.b[tn].z, sl.b[tn].w};
+                for (int tn = 0; tn < TN; ++tn) {
+                    const _Float16 sh = __builtin_bit_cast(_Float16, (uint16_t)sl.s[tn]);
+                    const half2_t s2 = {sh, sh};
+                    const uint32_t words[4] = {sl.b[tn].x, sl.b[tn].y, sl.b[tn].z, sl.b[tn].w};
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    half2_t h[4];
-                    dequant_word(words[kk], s2, h, kc);
-                    bf[tn][kk] = (half8_t){h[0].x, h[0].y, h[1].x, h[1].y,
-                                           h[2].x, h[2].y, h[3].x, h[3].y};
+                    for (int kk = 0; kk < 4; ++kk) {
+                        half2_t h[4];
+                        dequant_word(words[kk], s2, h, kc);
+                        bf[tn][kk] = (half8_t){h[0].x, h[0].y, h[1].x, h[1].y,
+                                               h[2].x, h[2].y, h[3].x, h[3].y};
+                    }
                 }
-            }
+                if constexpr (decltype(clamp)::value) clamp_fp16_weights(bf);
 #pragma unroll
-            for (int tm = 0; tm < TM; ++tm) {
+                for (int tm = 0; tm < TM; ++tm) {
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    const v4u v = sl.a[tm][kk];
-                    const half8_t af = __builtin_bit_cast(half8_t, pair_block(v.x, v.y, v.z, v.w));
+                    for (int kk = 0; kk < 4; ++kk) {
+                        const v4u v = sl.a[tm][kk];
+                        const half8_t af =
+                            __builtin_bit_cast(half8_t, pair_block(v.x, v.y, v.z, v.w));
 #pragma unroll
-                    for (int tn = 0; tn < TN; ++tn)
-                        acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[tn][kk],
-                                                                             acc[tm][tn], 0, 0, 0);
+                        for (int tn = 0; tn < TN; ++tn)
+                            acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                                af, bf[tn][kk], acc[tm][tn], 0, 0, 0);
+                    }
                 }
-            }
+            };
+            if (any_largest_scale(sl.s))
+                mma(std::true_type{});
+            else
+                mma(std::false_type{});
         }
     }
 
