@@ -168,7 +168,7 @@ __attribute__((amdgpu_waves_per_eu(ASYM ? 1 : 2))) void gemm_mfma_kernel(
 #pragma unroll
     for (int i = 0; i < A_PER_THREAD; ++i) a_regs[i] = make_uint4(0, 0, 0, 0);
     BRegs b0, b1;
-    auto step_body = [&](int step, BRegs& cur, auto clamp) {
+    auto step_body = [&](int step, BRegs& cur, auto clamp) __attribute__((always_inline)) {
         const uint4* abase =
             lds + (step & 1) * LDS_STAGE + (wk * BM + wm * TM * 16 + l16) * kLdaVec + 4 * j;
         if constexpr (ASYM) {
@@ -233,7 +233,7 @@ __attribute__((amdgpu_waves_per_eu(ASYM ? 1 : 2))) void gemm_mfma_kernel(
             }
         } else {
             // B fragments of this wave's group: [tn][kk]
-            auto mma = [&](auto clamp) {
+            auto mma = [&](auto clamp) __attribute__((always_inline)) {
                 half8_t bf[TN][4];
 #pragma unroll
                 for (int tn = 0; tn < TN; ++tn) {
@@ -311,16 +311,23 @@ __attribute__((amdgpu_waves_per_eu(ASYM ? 1 : 2))) void gemm_mfma_kernel(
     huge = false;
 #pragma unroll
     for (int w = 0; w < NT / kWave; ++w) huge |= huge_waves[w] != 0u;
-    auto k_loop = [&](auto clamp) {
+    auto k_loop = [&](auto clamp) __attribute__((always_inline)) {
         for (int step = 0; step < nsteps; step += 2) {
             step_body(step, b0, clamp);
             if (step + 1 < nsteps) step_body(step + 1, b1, clamp);
         }
     };
-    if (!ASYM && huge)
-        k_loop(std::integral_constant<bool, !ASYM>{});
-    else
+    if constexpr (ASYM) {
         k_loop(std::false_type{});
+    } else {
+        // one call site per instantiation, so each copy is inlined (a lambda
+        // called from two sites can stay a call, with its captured arrays in
+        // scratch memory)
+        if (huge)
+            k_loop(std::true_type{});
+        else
+            k_loop(std::false_type{});
+    }
 
     if constexpr (WK > 1) {
         // Sum the WK partial tiles: waves wk > 0 publish, wave wk == 0 adds.

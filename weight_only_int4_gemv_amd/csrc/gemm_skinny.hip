@@ -102,7 +102,7 @@ __global__ __launch_bounds__(WK * kWave) void gemm_skinny_kernel(
             load(t0 + i + P, ring[(i + P) % Q]);
             if (t0 + i >= Tw) continue;                  // wave-uniform
             const Slot& sl = ring[i];
-            auto mma = [&](auto clamp) {
+            auto mma = [&](auto clamp) __attribute__((always_inline)) {
                 half8_t bf[TN][4];
 #pragma unroll
                 for (int tn = 0; tn < TN; ++tn) {
