@@ -305,14 +305,16 @@ def test_prefill_wide_tiles_ragged(w4, orc, M, N, K):
 @pytest.mark.parametrize("M,N,K,algo", [(1, 64, 512, "gemv"), (3, 64, 512, "valu"),
                                          (3, 64, 512, "mfma"), (16, 64, 512, "mfma"),
                                          (40, 64, 512, "mfma"), (65, 64, 512, "mfma"),
-                                         (512, 64, 512, "mfma"), (256, 16384, 256, "mfma")])
+                                         (512, 64, 512, "mfma"), (256, 16384, 256, "mfma"),
+                                         (65, 64, 1024, "mfma"), (512, 8192, 1024, "mfma")])
 def test_largest_fp16_weights_stay_finite(w4, orc, M, N, K, algo):
     """Groups whose absmax is the largest finite fp16 (65504) get s = 9360,
     and s * 7 = 65520 is a tie that rounds to infinity in fp16.  Every kernel
     family (GEMV, VALU, 4x4x4, batched, streaming, both tiled block shapes)
     must keep these weights finite and match the oracle within tolerance
     (the kernels that form fp16 weights clamp them to +-65504: error 16 in
-    65520, 2.4e-4 relative)."""
+    65520, 2.4e-4 relative).  K = 1024 gives rows of eight scales, which the
+    tiled kernel's scale scan reads 16 bytes at a time."""
     W = inputs.weight(N, K, seed=[35, N, K])
     W[::3, 5] = np.float16(65504.0)
     W[1::3, K // 2 + 3] = np.float16(-65504.0)
