@@ -783,6 +783,30 @@ def test_linear_asym_batched_wave_grids(w4, orc, M, N, K):
     check_linear_asym(w4, orc, M, N, K, 128, [48, M, N, K])
 
 
+@pytest.mark.parametrize("M,N,K", [(65, 300, 1024), (65, 300, 512), (512, 8192, 1024)])
+def test_linear_asym_large_scales(w4, orc, M, N, K):
+    """Asymmetric weights with scales of 64 and more (the tiled kernel's
+    slow copy: fp16 weights s * (n - zc) clamped to +-65504), including
+    groups that hold +-65504, against the oracle (rows of eight scales:
+    the 16-byte scale scan; of four: the 2-byte one; both block shapes)."""
+    rng = np.random.default_rng([49, M, N, K])
+    W = (rng.standard_normal((N, K)) * 3000.0).astype(np.float16)
+    W[::5, 7] = np.float16(65504.0)
+    W[1::5, K - 9] = np.float16(-65504.0)
+    packed, scales, zeros = orc.quantize_asym(W, group=128)
+    assert (scales.view(np.float16).astype(np.float32) >= 64.0).any()
+    X = (inputs.activation(M, K, seed=[50, M]).astype(np.float32) * 2.0 ** -12).astype(np.float16)
+    say("asym large scales M=%d N=%d K=%d" % (M, N, K))
+    Y = w4.gemm_asym(dev(X), packed_to_dev(packed), scales_to_dev(scales), dev(zeros))
+    torch.cuda.synchronize()
+    Yref, Yabs = orc.matmul_asym(X, packed, scales, zeros, group=128)
+    assert np.abs(Yref).max() < 30000
+    got = Y.cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all()
+    bad = np.argwhere(~(np.abs(got - Yref) <= oracle.tolerance(Yref, Yabs)))
+    assert bad.size == 0, "%d outputs out of tolerance, first %s" % (len(bad), bad[0])
+
+
 @pytest.mark.parametrize("name,K,N", [("llama down", 14336, 4096), ("llama gate", 4096, 14336),
                                       ("qwen down", 18944, 3584)])
 def test_linear_asym_layer_shapes(w4, orc, name, K, N):

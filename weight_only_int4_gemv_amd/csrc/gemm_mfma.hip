@@ -44,7 +44,7 @@ constexpr int kLdaVec = kLdaHalfs / 8;     // in uint4
 
 template <int TM, int TN, int WM, int WN, int WK, bool ASYM>
 __global__ __launch_bounds__(WM * WN * WK * kWave)
-__attribute__((amdgpu_waves_per_eu(ASYM ? 1 : 2))) void gemm_mfma_kernel(
+__attribute__((amdgpu_waves_per_eu(2))) void gemm_mfma_kernel(
     const uint16_t* __restrict__ X, int M, const uint4* __restrict__ packed,
     const uint16_t* __restrict__ scales, const int16_t* __restrict__ zeros,
     uint16_t* __restrict__ Y, int N, int K) {
@@ -172,65 +172,108 @@ __attribute__((amdgpu_waves_per_eu(ASYM ? 1 : 2))) void gemm_mfma_kernel(
         const uint4* abase =
             lds + (step & 1) * LDS_STAGE + (wk * BM + wm * TM * 16 + l16) * kLdaVec + 4 * j;
         if constexpr (ASYM) {
-            // exact codes n - zc; the group's products scaled once in fp32
-            half8_t bq[TN][4];
-            float sf[TN], cf[TN];
-            bool wide = false;
+            // Common blocks (every scale below 64, every |z| <= 1000): fp16
+            // weights s * (n - z) from the exact codes n - z, |s (n - z)| <
+            // 64 * 1015 stays in the fp16 range; multiplied as the symmetric
+            // weights are.  The slow copy keeps the codes exact and scales
+            // each group's MFMA sums in fp32 (ŵ itself may exceed the fp16
+            // range there), over half of the wave's row tiles at a time to
+            // bound the temporaries; a group with |z| > 1000 adds s (zc - z)
+            // times the group's activation sums (an MFMA against ones).
+            auto mma = [&](auto slow) __attribute__((always_inline)) {
+                if constexpr (!decltype(slow)::value) {
+                    half8_t bf[TN][4];
 #pragma unroll
-            for (int tn = 0; tn < TN; ++tn) {
-                const ZeroBias zb = zero_bias(cur.z[tn]);
-                sf[tn] = f16_bits_to_f32((uint16_t)cur.s[tn]);
-                cf[tn] = sf[tn] * (float)(zb.zc - cur.z[tn]);   // exact: |zc - z| < 2^15
-                wide |= zb.zc != cur.z[tn];
-                const uint32_t words[4] = {cur.w[tn].x, cur.w[tn].y, cur.w[tn].z, cur.w[tn].w};
+                    for (int tn = 0; tn < TN; ++tn) {
+                        const ZeroBias zb = zero_bias(cur.z[tn]);
+                        const _Float16 sh = __builtin_bit_cast(_Float16, (uint16_t)cur.s[tn]);
+                        const half2_t s2 = {sh, sh};
+                        const uint32_t words[4] = {cur.w[tn].x, cur.w[tn].y, cur.w[tn].z,
+                                                   cur.w[tn].w};
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    half2_t q[4];
-                    codes_word_zp(words[kk], kc, zb, q);
-                    bq[tn][kk] = (half8_t){q[0].x, q[0].y, q[1].x, q[1].y,
-                                           q[2].x, q[2].y, q[3].x, q[3].y};
+                        for (int kk = 0; kk < 4; ++kk) {
+                            half2_t q[4];
+                            codes_word_zp(words[kk], kc, zb, q);
+                            const half2_t h0 = q[0] * s2, h1 = q[1] * s2, h2 = q[2] * s2,
+                                          h3 = q[3] * s2;
+                            bf[tn][kk] = (half8_t){h0.x, h0.y, h1.x, h1.y,
+                                                   h2.x, h2.y, h3.x, h3.y};
+                        }
+                    }
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+                        for (int tm = 0; tm < TM; ++tm) {
+                            const half8_t af =
+                                __builtin_bit_cast(half8_t, abase[tm * 16 * kLdaVec + kk]);
+#pragma unroll
+                            for (int tn = 0; tn < TN; ++tn)
+                                acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                                    af, bf[tn][kk], acc[tm][tn], 0, 0, 0);
+                        }
+                    }
+                } else {
+                    half8_t bq[TN][4];
+                    float sf[TN], cf[TN];
+                    bool wide = false;
+#pragma unroll
+                    for (int tn = 0; tn < TN; ++tn) {
+                        const ZeroBias zb = zero_bias(cur.z[tn]);
+                        sf[tn] = f16_bits_to_f32((uint16_t)cur.s[tn]);
+                        cf[tn] = sf[tn] * (float)(zb.zc - cur.z[tn]);
+                        wide |= zb.zc != cur.z[tn];
+                        const uint32_t words[4] = {cur.w[tn].x, cur.w[tn].y, cur.w[tn].z,
+                                                   cur.w[tn].w};
+#pragma unroll
+                        for (int kk = 0; kk < 4; ++kk) {
+                            half2_t q[4];
+                            codes_word_zp(words[kk], kc, zb, q);
+                            bq[tn][kk] = (half8_t){q[0].x, q[0].y, q[1].x, q[1].y,
+                                                   q[2].x, q[2].y, q[3].x, q[3].y};
+                        }
+                    }
+                    constexpr int TH = TM > 1 ? TM / 2 : 1;
+                    const _Float16 one = (_Float16)1.0f;
+                    const half8_t ones = {one, one, one, one, one, one, one, one};
+                    const bool any_wide = __any(wide);
+#pragma unroll
+                    for (int t0 = 0; t0 < TM; t0 += TH) {
+                        // d: the group's products per row tile; xs: its
+                        // activation sums (only used where |z| > 1000)
+                        float4_t d[TH][TN], xs[TH];
+#pragma unroll
+                        for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+                            for (int th = 0; th < TH; ++th) {
+                                const half8_t af = __builtin_bit_cast(
+                                    half8_t, abase[(t0 + th) * 16 * kLdaVec + kk]);
+#pragma unroll
+                                for (int tn = 0; tn < TN; ++tn)
+                                    d[th][tn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                                        af, bq[tn][kk],
+                                        kk == 0 ? (float4_t){0.f, 0.f, 0.f, 0.f} : d[th][tn], 0,
+                                        0, 0);
+                                if (any_wide)
+                                    xs[th] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                                        af, ones,
+                                        kk == 0 ? (float4_t){0.f, 0.f, 0.f, 0.f} : xs[th], 0, 0,
+                                        0);
+                            }
+                        }
+#pragma unroll
+                        for (int th = 0; th < TH; ++th)
+#pragma unroll
+                            for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+                                for (int r = 0; r < 4; ++r) {
+                                    float v = fmaf(sf[tn], d[th][tn][r], acc[t0 + th][tn][r]);
+                                    if (any_wide) v = fmaf(cf[tn], xs[th][r], v);
+                                    acc[t0 + th][tn][r] = v;
+                                }
+                    }
                 }
-            }
-            float4_t d[TM][TN];
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-#pragma unroll
-                for (int tm = 0; tm < TM; ++tm) {
-                    const half8_t af = __builtin_bit_cast(half8_t, abase[tm * 16 * kLdaVec + kk]);
-#pragma unroll
-                    for (int tn = 0; tn < TN; ++tn)
-                        d[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                            af, bq[tn][kk], kk == 0 ? (float4_t){0.f, 0.f, 0.f, 0.f} : d[tm][tn],
-                            0, 0, 0);
-                }
-            }
-#pragma unroll
-            for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-                for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        acc[tm][tn][r] = fmaf(sf[tn], d[tm][tn][r], acc[tm][tn][r]);
-            if (__any(wide)) {
-                // activation sums of the group's 128 k for this wave's rows
-                const _Float16 one = (_Float16)1.0f;
-                const half8_t ones = {one, one, one, one, one, one, one, one};
-                float4_t xs[TM];
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-                    for (int tm = 0; tm < TM; ++tm)
-                        xs[tm] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                            __builtin_bit_cast(half8_t, abase[tm * 16 * kLdaVec + kk]), ones,
-                            kk == 0 ? (float4_t){0.f, 0.f, 0.f, 0.f} : xs[tm], 0, 0, 0);
-#pragma unroll
-                for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-                    for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            acc[tm][tn][r] = fmaf(cf[tn], xs[tm][r], acc[tm][tn][r]);
-            }
+            };
+            mma(clamp);
         } else {
             // B fragments of this wave's group: [tn][kk]
             auto mma = [&](auto clamp) __attribute__((always_inline)) {
@@ -275,24 +318,42 @@ __attribute__((amdgpu_waves_per_eu(ASYM ? 1 : 2))) void gemm_mfma_kernel(
         __syncthreads();
     };
 
-    // Does any row of this block hold a group whose scale reaches 9360 (the
-    // one case where fp16(s * q) can overflow)?  The block's scales are one
-    // contiguous span, scanned once; the K loop below then exists in two
-    // copies and the common one carries no check.
+    // Does any row of this block need the slow copy of the K loop?  For
+    // symmetric weights: a group whose scale reaches 9360, the one case where
+    // fp16(s * q) can overflow.  For asymmetric weights: a scale of 64 or
+    // more (s * (n - z) may then leave the fp16 range) or a zero point
+    // beyond +-1000 (codes n - z no longer exact in fp16).  The block's scales (and
+    // zero points) are one contiguous span each, scanned once; the K loop
+    // below exists in two copies and the common one carries no check.
+    constexpr uint32_t kSlowScale = ASYM ? 0x5400u : kHugeScaleBits;   // 64 : 9360
     bool huge = false;
-    if constexpr (!ASYM) {
+    {
         const uint32_t span = (uint32_t)min(BN, N - n_blk) * srow;
-        if ((reinterpret_cast<uintptr_t>(scales) & 15) == 0 && (srow & 15) == 0) {
+        auto slow_z = [&](uint32_t zbits) {
+            const int z = (int)(int16_t)(uint16_t)zbits;
+            return ASYM && (z > kZeroClamp || z < -kZeroClamp);
+        };
+        if ((reinterpret_cast<uintptr_t>(scales) & 15) == 0 &&
+            (!ASYM || (reinterpret_cast<uintptr_t>(zeros) & 15) == 0) && (srow & 15) == 0) {
             for (uint32_t off = threadIdx.x * 16u; off < span; off += NT * 16u) {
                 const v4u v = __builtin_amdgcn_raw_buffer_load_b128(sr, off, 0, 0);
                 const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    huge |= (w[i] & 0xFFFFu) >= kHugeScaleBits || (w[i] >> 16) >= kHugeScaleBits;
+                    huge |= (w[i] & 0xFFFFu) >= kSlowScale || (w[i] >> 16) >= kSlowScale;
+                if constexpr (ASYM) {
+                    const v4u zv = __builtin_amdgcn_raw_buffer_load_b128(zr, off, 0, 0);
+                    const uint32_t zw[4] = {zv.x, zv.y, zv.z, zv.w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        huge |= slow_z(zw[i] & 0xFFFFu) || slow_z(zw[i] >> 16);
+                }
             }
         } else {
-            for (uint32_t off = threadIdx.x * 2u; off < span; off += NT * 2u)
-                huge |= __builtin_amdgcn_raw_buffer_load_b16(sr, off, 0, 0) >= kHugeScaleBits;
+            for (uint32_t off = threadIdx.x * 2u; off < span; off += NT * 2u) {
+                huge |= __builtin_amdgcn_raw_buffer_load_b16(sr, off, 0, 0) >= kSlowScale;
+                if constexpr (ASYM) huge |= slow_z(__builtin_amdgcn_raw_buffer_load_b16(zr, off, 0, 0));
+            }
         }
     }
 
@@ -317,17 +378,13 @@ __attribute__((amdgpu_waves_per_eu(ASYM ? 1 : 2))) void gemm_mfma_kernel(
             if (step + 1 < nsteps) step_body(step + 1, b1, clamp);
         }
     };
-    if constexpr (ASYM) {
+    // one call site per instantiation, so each copy is inlined (a lambda
+    // called from two sites can stay a call, with its captured arrays in
+    // scratch memory)
+    if (huge)
+        k_loop(std::true_type{});
+    else
         k_loop(std::false_type{});
-    } else {
-        // one call site per instantiation, so each copy is inlined (a lambda
-        // called from two sites can stay a call, with its captured arrays in
-        // scratch memory)
-        if (huge)
-            k_loop(std::true_type{});
-        else
-            k_loop(std::false_type{});
-    }
 
     if constexpr (WK > 1) {
         // Sum the WK partial tiles: waves wk > 0 publish, wave wk == 0 adds.
@@ -419,25 +476,22 @@ hipError_t launch_tiled(const uint16_t* X, int64_t M, const uint32_t* packed,
     // tiles (eight 16-row by two 16-column tiles per wave, eight waves across
     // N: each staged X tile serves 256 columns; M = 512 on 4096 x 14336 at
     // 76 us against 81 us with 128 x 128 blocks, on 8192 x 28672 316 against
-    // 338 us) — asymmetric weights keep 128 x 128 blocks of four waves, whose
-    // registers do not fit two waves per SIMD.
+    // 338 us).
     const int64_t tiles128 = ((M + 127) / 128) * ((N + 127) / 128);
     if (tiles128 >= num_cu) {
+        // asymmetric weights: 128 x 16 wave tiles (the exact slow copy of
+        // the loop does not fit two waves per SIMD with 128 x 32 tiles)
         if constexpr (ASYM)
-            return launch_mfma_t<8, 2, 1, 4, 1, ASYM>(X, M, packed, scales, N, K, Y, stream,
+            return launch_mfma_t<8, 1, 1, 8, 1, ASYM>(X, M, packed, scales, N, K, Y, stream,
                                                       zeros);
         else
             return launch_mfma_t<8, 2, 1, 8, 1, ASYM>(X, M, packed, scales, N, K, Y, stream,
                                                       zeros);
     }
-    // Else 128 x 64 block tiles, eight waves, two over K: for symmetric
-    // weights four waves across N with 128 x 16 wave tiles (M = 512 on
-    // 14336 x 4096: 110 us against 117 us with 64 x 32 wave tiles, which the
-    // asymmetric kernel keeps: its 128 x 16 tiles would spill).
-    if constexpr (ASYM)
-        return launch_mfma_t<4, 2, 2, 2, 2, ASYM>(X, M, packed, scales, N, K, Y, stream, zeros);
-    else
-        return launch_mfma_t<8, 1, 1, 4, 2, ASYM>(X, M, packed, scales, N, K, Y, stream, zeros);
+    // Else 128 x 64 block tiles, eight waves, two over K, four across N with
+    // 128 x 16 wave tiles (M = 512 on 14336 x 4096: 110 us against 117 us
+    // with 64 x 32 wave tiles).
+    return launch_mfma_t<8, 1, 1, 4, 2, ASYM>(X, M, packed, scales, N, K, Y, stream, zeros);
 }
 
 }  // namespace
