@@ -17,20 +17,26 @@
 //
 // Block: WM x WN x WK waves.  A wave computes a (16 TM) x (16 TN) tile;
 // WK > 1 splits the groups of K over waves (for few output tiles) and the
-// partial tiles are summed through LDS at the end.  The next group's A
-// slices and B words are loaded into registers while the current one is
-// multiplied.
+// partial tiles are summed through LDS at the end.  Every load offset is a
+// per-thread 32-bit offset from the block's first row, fixed for the whole
+// K loop (rows past M or N clamped to the last row), so the loop has no
+// masking; X is double-buffered in LDS (one barrier per K step) and the B
+// registers of two steps alternate.
 // Precision: fp16(s*q) has relative error <= 2^-11, so |y - y_exact| <=
 // 2^-11 sum |x w| plus fp32 accumulation error, inside the 1e-3 sum |x w|
-// allowance for every K.
+// allowance for every K.  The block scans its scales once: a group with
+// absmax 65504 (s = 9360, 7 s rounds to infinity in fp16) sends the block to
+// a second copy of the K loop that clamps its fp16 weights to +-65504.
 //
 // Asymmetric weights (ASYM, [QUANT] sub-section 2: w = s (n - z), nibble n
-// in [0, 15], an integer zero point z per group): B holds the exact codes
-// n - zc (codes_word_zp, zc = z clamped to +-1000), each group's products
-// are summed by the MFMAs in fp32 and scaled once in fp32, as the GEMV does
-// (so no fp16 product s (n - z) can overflow); a group with |z| > 1000 adds
-// s (zc - z) times the group's activation sums, which one more MFMA per
-// k-step against a B of ones forms (only in waves that hold such a group).
+// in [0, 15], an integer zero point z per group): where the block's scales
+// are all below 64 and its zero points within +-1000, B holds fp16(s (n - z))
+// formed from the exact codes n - z (codes_word_zp), multiplied as the
+// symmetric weights are.  Otherwise (s (n - z) may leave the fp16 range) the
+// block runs an exact copy of the loop: B holds the codes n - zc (zc = z
+// clamped to +-1000), each group's MFMA sums are scaled once in fp32, and a
+// group with |z| > 1000 adds s (zc - z) times the group's activation sums,
+// which an MFMA against a B of ones forms in the same pass.
 #include "w4a16_device.h"
 #include "w4a16_launch.h"
 #include "w4a16_fp16_weights.h"
