@@ -17,7 +17,10 @@
 //     (pair_block) to match;
 //   - the (group) iterations run through a ring of P+1 register slots,
 //     loads for group t+P issued before group t is multiplied; loads past a
-//     wave's range use an empty buffer resource, and rows past M or N read 0.
+//     wave's range use an empty buffer resource, and rows past M or N read 0;
+//   - a wave whose group holds absmax 65504 (s = 9360: 7 s rounds to
+//     infinity in fp16) runs a copy of the step that clamps its fp16
+//     weights to +-65504 (error 16 in 65520).
 #include "w4a16_device.h"
 #include "w4a16_launch.h"
 #include "w4a16_fp16_weights.h"
