@@ -783,6 +783,15 @@ def test_linear_asym_batched_wave_grids(w4, orc, M, N, K):
     check_linear_asym(w4, orc, M, N, K, 128, [48, M, N, K])
 
 
+@pytest.mark.parametrize("M,N,K", [(512, 8192, 1024), (300, 11000, 640)])
+def test_linear_asym_prefill_fp16_weights(w4, orc, M, N, K):
+    """Prefill-sized asymmetric products whose blocks all take the fp16
+    weight copy (skewed layer-like weights: scales below 64, zero points in
+    [0, 15]) on the tiled kernel's wide-grid branch (enough 128-row tiles to
+    fill the compute units), M and N ragged in the second case."""
+    check_linear_asym(w4, orc, M, N, K, 128, [51, M, N, K], plant=False)
+
+
 @pytest.mark.parametrize("M,N,K", [(65, 300, 1024), (65, 300, 512), (512, 8192, 1024)])
 def test_linear_asym_large_scales(w4, orc, M, N, K):
     """Asymmetric weights with scales of 64 and more (the tiled kernel's
