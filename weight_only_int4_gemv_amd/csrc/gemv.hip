@@ -247,8 +247,12 @@ __global__ __launch_bounds__(WAVES * kWave) void gemv_kernel(
 //     it waits only for its own loads.
 //   - A lane whose chunk is past the end of the row (last partial step)
 //     contributes with scale 0 and reads a valid LDS address.
+//   - PERM (act order): X is staged unpaired with 16-byte loads, issued with
+//     the matching 16-byte loads of perm (one memory round trip), and the
+//     block then gathers x[perm[j]] from LDS (an index outside [0, K) reads
+//     0) into the paired layout; the raw copy takes a second LDS region.
 // XPT: 16-byte activation blocks staged per thread (MMAX*K/8 <= XPT*threads).
-template <int MMAX, int R, int P, int WAVES, int XPT, bool ASYM>
+template <int MMAX, int R, int P, int WAVES, int XPT, bool ASYM, bool PERM>
 __global__ __launch_bounds__(WAVES * kWave) void gemv_persistent_kernel(
     const uint16_t* __restrict__ X, int M, const uint4* __restrict__ packed,
     const uint16_t* __restrict__ scales, const int16_t* __restrict__ zeros,
@@ -271,11 +275,19 @@ __global__ __launch_bounds__(WAVES * kWave) void gemv_persistent_kernel(
     // X blocks of this thread, loaded first (indices clamped into range).
     const int xblocks = M * (K >> 3);
     uint4 xr[XPT];
+    int4 pr[PERM ? XPT : 1][2];
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
         const int e = min((int)threadIdx.x + i * WAVES * kWave, xblocks - 1);
         const int m = e / (K >> 3);
-        xr[i] = x_block(X, m, K, (e - m * (K >> 3)) * 8, perm);
+        const int col0 = (e - m * (K >> 3)) * 8;
+        if constexpr (PERM) {
+            xr[i] = x_block(X, m, K, col0, nullptr);          // unpermuted, contiguous
+            pr[i][0] = reinterpret_cast<const int4*>(perm + col0)[0];
+            pr[i][1] = reinterpret_cast<const int4*>(perm + col0)[1];
+        } else {
+            xr[i] = x_block(X, m, K, col0, perm);
+        }
     }
 
     // load cursor (wave-uniform): iteration tl -> (row group lrg, step ls)
@@ -325,10 +337,37 @@ __global__ __launch_bounds__(WAVES * kWave) void gemv_persistent_kernel(
 #pragma unroll
     for (int i = 0; i < P; ++i) load(w[i], sb[i], zb[i]);
 
+    if constexpr (PERM) {
+        // raw X in the second region, then the gather through perm from LDS
+        uint4* const raw = lds + xblocks;
 #pragma unroll
-    for (int i = 0; i < XPT; ++i) {
-        const int e = (int)threadIdx.x + i * WAVES * kWave;
-        if (e < xblocks) lds[e] = pair_block(xr[i].x, xr[i].y, xr[i].z, xr[i].w);
+        for (int i = 0; i < XPT; ++i) {
+            const int e = (int)threadIdx.x + i * WAVES * kWave;
+            if (e < xblocks) raw[e] = xr[i];
+        }
+        __syncthreads();
+        const uint16_t* const rawh = reinterpret_cast<const uint16_t*>(raw);
+#pragma unroll
+        for (int i = 0; i < XPT; ++i) {
+            const int e = (int)threadIdx.x + i * WAVES * kWave;
+            if (e < xblocks) {
+                const int m = e / (K >> 3);
+                const int idx[8] = {pr[i][0].x, pr[i][0].y, pr[i][0].z, pr[i][0].w,
+                                    pr[i][1].x, pr[i][1].y, pr[i][1].z, pr[i][1].w};
+                uint32_t h[8];
+#pragma unroll
+                for (int b = 0; b < 8; ++b)
+                    h[b] = (uint32_t)idx[b] < (uint32_t)K ? rawh[m * K + idx[b]] : 0u;
+                lds[e] = pair_block(h[0] | (h[1] << 16), h[2] | (h[3] << 16),
+                                    h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < XPT; ++i) {
+            const int e = (int)threadIdx.x + i * WAVES * kWave;
+            if (e < xblocks) lds[e] = pair_block(xr[i].x, xr[i].y, xr[i].z, xr[i].w);
+        }
     }
     __syncthreads();
 
@@ -415,13 +454,38 @@ hipError_t launch_gemv_t(const uint16_t* X, int64_t M, const uint32_t* packed,
 // 13.8-14.2 us with 1195 (4.67 blocks per CU leave the CUs with a fifth
 // block 7 % more work), 4096x14336 7.5-7.8 us against 8.6-8.9 us with 896.
 // Fewer row groups than waves on the chip: one wave per row group.
+template <int MMAX, int R, int P, int WAVES, int XPT, bool ASYM, bool PERM>
+hipError_t launch_persistent_kern(const uint16_t* X, int64_t M, const uint32_t* packed,
+                                  const uint16_t* scales, const int16_t* zeros, int64_t N,
+                                  int64_t K, uint16_t* Y, hipStream_t stream, int num_cu,
+                                  int blocks_per_cu, int gshift, const int* perm);
+
 template <int MMAX, int R, int P, int WAVES, int XPT, bool ASYM>
 hipError_t launch_persistent_xpt(const uint16_t* X, int64_t M, const uint32_t* packed,
                                  const uint16_t* scales, const int16_t* zeros, int64_t N,
                                  int64_t K, uint16_t* Y, hipStream_t stream, int num_cu,
                                  int blocks_per_cu, int gshift, const int* perm) {
-    const size_t lds = (size_t)MMAX * (K / 8) * sizeof(uint4);
-    auto kern = gemv_persistent_kernel<MMAX, R, P, WAVES, XPT, ASYM>;
+    if (perm != nullptr)
+        return launch_persistent_kern<MMAX, R, P, WAVES, XPT, ASYM, true>(
+            X, M, packed, scales, zeros, N, K, Y, stream, num_cu, blocks_per_cu, gshift, perm);
+    return launch_persistent_kern<MMAX, R, P, WAVES, XPT, ASYM, false>(
+        X, M, packed, scales, zeros, N, K, Y, stream, num_cu, blocks_per_cu, gshift, perm);
+}
+
+template <int MMAX, int R, int P, int WAVES, int XPT, bool ASYM, bool PERM>
+hipError_t launch_persistent_kern(const uint16_t* X, int64_t M, const uint32_t* packed,
+                                  const uint16_t* scales, const int16_t* zeros, int64_t N,
+                                  int64_t K, uint16_t* Y, hipStream_t stream, int num_cu,
+                                  int blocks_per_cu, int gshift, const int* perm) {
+    // paired X; with perm also the raw copy it is gathered from
+    const size_t lds = (size_t)(PERM ? 2 : 1) * MMAX * (K / 8) * sizeof(uint4);
+    auto kern = gemv_persistent_kernel<MMAX, R, P, WAVES, XPT, ASYM, PERM>;
+    if (lds > 64 * 1024) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 (int)lds);
+        if (e != hipSuccess) return e;
+    }
     // resident blocks per CU for the last LDS size seen (lds << 8 | blocks)
     static std::atomic<uint64_t> occ_cache{0};
     uint64_t c = occ_cache.load(std::memory_order_relaxed);
