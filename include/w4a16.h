@@ -109,7 +109,13 @@ int w4a16_gemv(const uint16_t* x, const uint32_t* packed, const uint16_t* scales
 
 /* Batched decode / prefill ([BENCH] §一 prompt of 512 tokens, §二 prefill):
  *   X in : fp16 [M, K];  Y out: fp16 [M, N];  Y = X·Ŵᵀ.
- * Picks the kernel by M (W4A16_ALGO_AUTO). */
+ * Picks the kernel by M (W4A16_ALGO_AUTO).
+ * Accuracy (every entry point of the linear layer): fp32 accumulation, y
+ * rounded to fp16 (RNE); |y - y_exact| <= 1e-3 sum_k |x_k ŵ_k| +
+ * max(2^-10 |y_exact|, 2^-24) per element.  The matrix-core kernels that
+ * multiply fp16 weights fp16(s*q) clamp them to +-65504 (only a group whose
+ * absmax is 65504 reaches 7*s = 65520), within that bound; an output whose
+ * exact value exceeds the fp16 range is +-infinity. */
 int w4a16_gemm(const uint16_t* X, int64_t M, const uint32_t* packed, const uint16_t* scales,
                int64_t N, int64_t K, uint16_t* Y, void* stream);
 
