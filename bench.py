@@ -468,6 +468,28 @@ def main() -> int:
     n_launch = len(launches)
     avg_launch_us = ms * 1e3 / n_launch
 
+    # ---- the same sweep launched the other way (eager launches from the
+    # host against graph replays), outside the timed region
+    if args.mode == "graph":
+        other_run, other_name = step, "eager"
+    else:
+        og = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(og):
+            step()
+        other_run, other_name = og.replay, "graph"
+    for _ in range(3):
+        other_run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(10):
+        other_run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / 10
+    other_mode = {"mode": other_name, "us_per_sweep": round(us, 2),
+                  "GB/s": round(step_bytes / (us * 1e-6) / 1e9, 1)}
+
     # ---- the other layout, and per-shape launch durations (graph of every
     # layer's copy of one matrix)
     def time_graph(seq, reps=10):
@@ -593,6 +615,7 @@ def main() -> int:
         "cpu_baseline": cpu,
         "other_layout": other,
         "other_launch": other_launch,
+        "other_mode": other_mode,
         "per_shape": per_shape,
         "parity": parity,
         "secondary": sec,
