@@ -468,6 +468,21 @@ def main() -> int:
     n_launch = len(launches)
     avg_launch_us = ms * 1e3 / n_launch
 
+    # ---- spread: 20 single-step samples after the timed region (each step
+    # bracketed by its own events)
+    samples = []
+    for _ in range(20):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        run()
+        b.record(stream)
+        samples.append((a, b))
+    torch.cuda.synchronize()
+    sample_us = np.sort(np.array([a.elapsed_time(b) * 1e3 for a, b in samples]))
+    step_spread = {"n": len(sample_us), "p10_us": round(float(np.percentile(sample_us, 10)), 2),
+                   "p50_us": round(float(np.percentile(sample_us, 50)), 2),
+                   "p90_us": round(float(np.percentile(sample_us, 90)), 2)}
+
     # ---- the same sweep launched the other way (eager launches from the
     # host against graph replays), outside the timed region
     if args.mode == "graph":
@@ -616,6 +631,7 @@ def main() -> int:
         "other_layout": other,
         "other_launch": other_launch,
         "other_mode": other_mode,
+        "step_samples": step_spread,
         "per_shape": per_shape,
         "parity": parity,
         "secondary": sec,
