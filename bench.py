@@ -597,6 +597,27 @@ def main() -> int:
 
     roofline = dominant_roofline(per_shape, layer0, step_bytes, n_launch, avg_launch_us)
 
+    # ---- the box's streaming bandwidth as a second denominator: a 1 GiB
+    # device copy (1 GiB read + 1 GiB written), best of 5
+    src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(5):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        dst.copy_(src)
+        b.record(stream)
+        torch.cuda.synchronize()
+        t = a.elapsed_time(b) * 1e-3
+        best = t if best is None else min(best, t)
+    copy_gbs = 2 * src.numel() * 4 / best / 1e9
+    del src, dst
+    stream_copy = {"bytes": 2 << 30, "GB/s": round(copy_gbs, 1),
+                   "dominant_launch_frac_of_it": (round(roofline["achieved"] / copy_gbs, 4)
+                                                  if roofline else None)}
+
     out = {
         "metric": "W4A16 GEMV effective HBM GB/s (% of peak) + us per 8B-shaped decode weight sweep",
         "value": round(gbs, 1),
@@ -632,6 +653,7 @@ def main() -> int:
         "other_launch": other_launch,
         "other_mode": other_mode,
         "step_samples": step_spread,
+        "stream_copy": stream_copy,
         "per_shape": per_shape,
         "parity": parity,
         "secondary": sec,
