@@ -16,13 +16,8 @@ import pytest
 
 from weight_only_int4_gemv_amd import build as B
 
-# Kernels allowed a few bytes of scratch, with the reason.
-ALLOWED = {
-    # VALU path for 5..8 rows of X with rows too long for LDS (K slices), four
-    # weight rows per wave: 8 x 4 accumulators plus the ring exceed the
-    # register file by a few registers; a rare shape, not on the hot path.
-    r"gemv_kernelILi8ELi4ELi2ELi4ELb[01]E",
-}
+# Kernels allowed scratch, with the reason (none).
+ALLOWED = set()
 
 
 def _metadata(src: str, tmp: str):

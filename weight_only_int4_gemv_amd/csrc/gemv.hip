@@ -562,9 +562,13 @@ hipError_t launch_gemv_m(const uint16_t* X, int64_t M, const uint32_t* packed,
                                                         perm);
     }
     constexpr int WAVES = 4;
-    if (N >= (int64_t)4 * WAVES * num_cu && MMAX <= 4)
-        return launch_gemv_t<MMAX, 4, 2, WAVES, ASYM>(X, M, packed, scales, zeros, N, K, Y,
-                                                      stream, gshift, perm);
+    if constexpr (MMAX <= 4) {
+        // four rows per wave only for up to four rows of X (more would not
+        // fit the register file)
+        if (N >= (int64_t)4 * WAVES * num_cu)
+            return launch_gemv_t<MMAX, 4, 2, WAVES, ASYM>(X, M, packed, scales, zeros, N, K, Y,
+                                                          stream, gshift, perm);
+    }
     if (N >= (int64_t)2 * WAVES * num_cu)
         return launch_gemv_t<MMAX, 2, 2, WAVES, ASYM>(X, M, packed, scales, zeros, N, K, Y,
                                                       stream, gshift, perm);
