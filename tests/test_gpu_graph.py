@@ -46,15 +46,16 @@ def test_graph_replays_match_eager(M, algo):
     assert (err <= oracle.tolerance(yref, yabs)).all()
 
 
-@pytest.mark.parametrize("case", ["wide-prefill", "asym-tiled", "act-order"])
+@pytest.mark.parametrize("case", ["wide-prefill", "asym-tiled", "act-order", "4x4x4-k-split"])
 def test_graph_replays_match_eager_more_paths(case):
     """The 128 x 256 prefill blocks (with their scale scan), the asymmetric
-    tiled kernel and the act-order GEMV (x gathered through LDS) under graph
-    replay: every replay equals the eager result bit for bit."""
+    tiled kernel, the act-order GEMV (x gathered through LDS) and the 4x4x4
+    GEMV with two waves per row group (partial sums through LDS) under
+    graph replay: every replay equals the eager result bit for bit."""
     from weight_only_int4_gemv_amd import w4a16
     assert torch.cuda.is_available()
     M, N, K = {"wide-prefill": (512, 8192, 1024), "asym-tiled": (96, 1536, 2304),
-               "act-order": (1, 1536, 2304)}[case]
+               "act-order": (1, 1536, 2304), "4x4x4-k-split": (4, 1536, 14336)}[case]
     W, X = inputs.weight_and_activation(N, K, M, seed=[33, M])
     print("[case] graph %s M=%d N=%d K=%d" % (case, M, N, K), flush=True)
     Wd, Xd = torch.from_numpy(W).cuda(), torch.from_numpy(X).cuda()

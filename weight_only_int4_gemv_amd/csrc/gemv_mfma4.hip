@@ -28,6 +28,16 @@
 // the loads of step t + P are issued before step t is multiplied; loads past
 // the wave's work use an empty buffer resource, rows past N and codes past K
 // read as 0 and are given scale 0.
+//
+// Few row groups for the compute units (short N, long K: the down
+// projection has N / 4 = 1024 row groups, one wave per SIMD): KS > 1 waves
+// share each row group, wave part p taking the steps p, p + KS, ... (the
+// same number for every part; steps past K load nothing useful and get
+// scale 0).  A block then works through batches of WAVES / KS row groups,
+// the same number of batches for every wave of the block, and at the end of
+// each batch parts 1 .. KS-1 leave their partial sums in LDS, part 0 adds
+// them in that order and stores: two barriers per batch, reached by every
+// wave.
 #include "w4a16_device.h"
 #include "w4a16_launch.h"
 
@@ -53,11 +63,14 @@ __device__ __forceinline__ float block_sum(float v) {
 }
 }  // namespace
 
-template <int MT, int U, int P, int WAVES>
+template <int MT, int U, int P, int WAVES, int KS>
 __global__ __launch_bounds__(WAVES * kWave) void gemv_mfma4_kernel(
     const uint16_t* __restrict__ X, int M, const uint32_t* __restrict__ packed,
     const uint16_t* __restrict__ scales, uint16_t* __restrict__ Y, int N, int K) {
-    extern __shared__ uint4 lds[];                    // [M][K/8 + 1] paired x
+    extern __shared__ uint4 lds[];                    // [M][K/8 + 1] paired x, then
+                                                      // (KS > 1) partial sums
+    static_assert(WAVES % KS == 0, "waves per row group must divide the block");
+    constexpr int RGB = WAVES / KS;                   // row groups per block and batch
     constexpr int Q = P + 1;
     constexpr int kRows = 4;
     constexpr int kStepK = 512 * U;                   // k per step
@@ -65,12 +78,17 @@ __global__ __launch_bounds__(WAVES * kWave) void gemv_mfma4_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int b = lane >> 2;
     const int c = lane & 3;
+    const int part = wave % KS;                       // this wave's share of the K steps
     const int nsteps = (K + kStepK - 1) / kStepK;
+    const int spw = (nsteps + KS - 1) / KS;           // steps per wave and row group
     const int total_rg = (N + kRows - 1) / kRows;
-    const int stride_rg = gridDim.x * WAVES;
-    const int first_rg = blockIdx.x * WAVES + wave;
-    const int my_rg = first_rg < total_rg ? (total_rg - 1 - first_rg) / stride_rg + 1 : 0;
-    const int T = my_rg * nsteps;
+    const int stride_rg = gridDim.x * RGB;
+    const int first_rg = blockIdx.x * RGB + wave / KS;
+    // KS == 1: each wave's own row groups.  KS > 1: the block's batches,
+    // counted from its first row group, so every wave runs the same loop.
+    const int sched_rg = KS == 1 ? first_rg : (int)blockIdx.x * RGB;
+    const int my_rg = sched_rg < total_rg ? (total_rg - 1 - sched_rg) / stride_rg + 1 : 0;
+    const int T = my_rg * spw;
     const int xblk = K >> 3;                          // 8-element blocks per x row
     const int xstride = xblk + 1;                     // 16-byte pad: rows start 4 banks apart
     const uint32_t wrow = (uint32_t)K / 2, srow = (uint32_t)K / 64;
@@ -102,8 +120,8 @@ __global__ __launch_bounds__(WAVES * kWave) void gemv_mfma4_kernel(
     // packing waits for both loads
     auto load = [&](v4u (&wd)[U], uint32_t (&sd)[U]) {
         if (ls == 0) {
-            const bool live = tl < T;
             const int64_t row0 = (int64_t)lrg * kRows;
+            const bool live = tl < T && row0 < N;
             const int64_t rows_left = live ? (int64_t)N - row0 : 0;
             wr = buffer_rsrc(reinterpret_cast<const char*>(packed) + (live ? row0 * wrow : 0),
                              (uint64_t)rows_left * wrow);
@@ -112,14 +130,14 @@ __global__ __launch_bounds__(WAVES * kWave) void gemv_mfma4_kernel(
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int k = ls * kStepK + u * 512 + b * 32;          // this lane's first k
+            const int k = (part + KS * ls) * kStepK + u * 512 + b * 32;   // this lane's first k
             const uint32_t kk = (uint32_t)min(k, K);               // past K: reads as 0
             wd[u] = __builtin_amdgcn_raw_buffer_load_b128(wr, c * wrow + kk / 2, 0, kStreamLoad);
             sd[u] = __builtin_amdgcn_raw_buffer_load_b16(sr, c * srow + (kk >> 7) * 2, 0,
                                                          kStreamLoad);
         }
         ++tl;
-        if (++ls == nsteps) {
+        if (++ls == spw) {
             ls = 0;
             lrg += stride_rg;
         }
@@ -143,7 +161,7 @@ __global__ __launch_bounds__(WAVES * kWave) void gemv_mfma4_kernel(
             if (t0 + i < T) {                                      // wave-uniform
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
-                    const int k = cs * kStepK + u * 512 + b * 32;
+                    const int k = (part + KS * cs) * kStepK + u * 512 + b * 32;
                     const bool valid = k < K;
                     const int blk = min(k, K - 32) >> 3;           // x of a valid chunk
                     const uint32_t words[4] = {wq[i][u].x, wq[i][u].y, wq[i][u].z, wq[i][u].w};
@@ -178,22 +196,43 @@ __global__ __launch_bounds__(WAVES * kWave) void gemv_mfma4_kernel(
                     }
                 }
             }
-            if (++cs == nsteps) {
+            if (++cs == spw) {
                 cs = 0;
-                if (t0 + i < T) {
-                    // row group complete: add the 16 blocks, lanes 0..3 store
-                    const int row = crg * kRows + c;
+                if (t0 + i < T) {                                  // block-uniform for KS > 1
+                    if constexpr (KS > 1) {
+                        // parts 1 .. KS-1 publish, part 0 adds them in order
+                        float4_t* red = reinterpret_cast<float4_t*>(lds + M * xstride) +
+                                        (size_t)(wave / KS) * (KS - 1) * MT * kWave;
+                        if (part > 0) {
 #pragma unroll
-                    for (int t = 0; t < MT; ++t) {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const float v = block_sum(acc[t][r]);
-                            const int m = t * 4 + r;
-                            if (lane < 4 && m < M && row < N)
-                                Y[(size_t)m * N + row] = f32_to_f16_bits(v);
+                            for (int t = 0; t < MT; ++t)
+                                red[((part - 1) * MT + t) * kWave + lane] = acc[t];
                         }
-                        acc[t] = (float4_t){0.f, 0.f, 0.f, 0.f};
+                        __syncthreads();
+                        if (part == 0) {
+                            for (int p = 1; p < KS; ++p)
+#pragma unroll
+                                for (int t = 0; t < MT; ++t)
+                                    acc[t] += red[((p - 1) * MT + t) * kWave + lane];
+                        }
                     }
+                    if (part == 0) {
+                        // row group complete: add the 16 blocks, lanes 0..3 store
+                        const int row = crg * kRows + c;
+#pragma unroll
+                        for (int t = 0; t < MT; ++t) {
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) {
+                                const float v = block_sum(acc[t][r]);
+                                const int m = t * 4 + r;
+                                if (lane < 4 && m < M && row < N)
+                                    Y[(size_t)m * N + row] = f32_to_f16_bits(v);
+                            }
+                        }
+                    }
+#pragma unroll
+                    for (int t = 0; t < MT; ++t) acc[t] = (float4_t){0.f, 0.f, 0.f, 0.f};
+                    if constexpr (KS > 1) __syncthreads();         // partial sums read
                 }
                 crg += stride_rg;
             }
@@ -201,26 +240,34 @@ __global__ __launch_bounds__(WAVES * kWave) void gemv_mfma4_kernel(
     }
 }
 
-template <int MT, int U, int P, int WAVES>
+template <int MT, int U, int P, int WAVES, int KS>
 hipError_t launch_mfma4_t(const uint16_t* X, int64_t M, const uint32_t* packed,
                           const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y,
                           hipStream_t stream, int num_cu, int blocks_per_cu) {
-    const size_t lds = (size_t)M * (K / 8 + 1) * 16;
+    const size_t lds = (size_t)M * (K / 8 + 1) * 16 +
+                       (size_t)(WAVES / KS) * (KS - 1) * MT * kWave * sizeof(float4_t);
     const int64_t total_rg = (N + 3) / 4;
-    const int64_t max_waves = (int64_t)num_cu * blocks_per_cu * WAVES;
-    // balanced persistent grid: every wave gets the same number of row groups
-    const int64_t per_wave = (total_rg + max_waves - 1) / max_waves;
-    const int64_t waves = (total_rg + per_wave - 1) / per_wave;
-    const int64_t blocks = (waves + WAVES - 1) / WAVES;
+    int64_t blocks;
+    if constexpr (KS == 1) {
+        // balanced persistent grid: every wave gets the same number of row groups
+        const int64_t max_waves = (int64_t)num_cu * blocks_per_cu * WAVES;
+        const int64_t per_wave = (total_rg + max_waves - 1) / max_waves;
+        const int64_t waves = (total_rg + per_wave - 1) / per_wave;
+        blocks = (waves + WAVES - 1) / WAVES;
+    } else {
+        // batches of WAVES / KS row groups, at most blocks_per_cu blocks per CU
+        blocks = (total_rg + WAVES / KS - 1) / (WAVES / KS);
+        if (blocks > (int64_t)num_cu * blocks_per_cu) blocks = (int64_t)num_cu * blocks_per_cu;
+    }
+    auto kern = gemv_mfma4_kernel<MT, U, P, WAVES, KS>;
     if (lds > 64 * 1024) {
-        const hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void*>(gemv_mfma4_kernel<MT, U, P, WAVES>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((gemv_mfma4_kernel<MT, U, P, WAVES>), dim3((unsigned)blocks),
-                       dim3(WAVES * kWave), lds, stream, X, (int)M, packed, scales, Y, (int)N,
-                       (int)K);
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(WAVES * kWave), lds, stream, X, (int)M,
+                       packed, scales, Y, (int)N, (int)K);
     return hipGetLastError();
 }
 
@@ -228,11 +275,17 @@ hipError_t launch_gemv_mfma4(const uint16_t* X, int64_t M, const uint32_t* packe
                              const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y,
                              hipStream_t stream, int num_cu) {
     // Measured on gfx950 (4096 x 14336 and 14336 x 4096, M = 4): two loads
-    // per step and two steps in flight; eight waves per block while x is
-    // small, else four waves and two blocks per compute unit.
-    if (M * K * 2 <= 64 * 1024)
-        return launch_mfma4_t<1, 2, 2, 8>(X, M, packed, scales, N, K, Y, stream, num_cu, 1);
-    return launch_mfma4_t<1, 2, 2, 4>(X, M, packed, scales, N, K, Y, stream, num_cu, 2);
+    // per step and two steps in flight; eight waves per block, one block per
+    // compute unit, when x is small and there are row groups for eight waves
+    // a CU; otherwise (the down projection: 1024 row groups, K = 14336) two
+    // waves per row group, each taking every second step, which doubles the
+    // waves a CU runs.
+    const int64_t total_rg = (N + 3) / 4;
+    const bool small_x = M * K * 2 <= 64 * 1024;
+    if (small_x && total_rg >= (int64_t)8 * num_cu)
+        return launch_mfma4_t<1, 2, 2, 8, 1>(X, M, packed, scales, N, K, Y, stream, num_cu, 1);
+    return launch_mfma4_t<1, 2, 2, 8, 2>(X, M, packed, scales, N, K, Y, stream, num_cu,
+                                         small_x ? 2 : 1);
 }
 
 }  // namespace w4a16
