@@ -22,12 +22,15 @@
 //   - q = clamp(rint(w / s), -8, 7) with rint (half to even) of the quotient
 //     rounded to fp32: for fp16 w and s a non-tie quotient is at least 2^-15
 //     (relative) away from a tie, so the fp32 quotient rounds to the same
-//     integer as the exact one.  The quotient is first formed as w * rcp(s)
-//     (v_rcp_f32, relative error below 2^-22; |w / s| <= 7.004, or < 10.5
-//     when s is an fp16 subnormal, so the product is within 3e-6 of w / s):
-//     it can round differently from w / s only if it lies within 3e-6 of a
-//     half-integer; a lane that sees a product within 2e-5 of one (about 2 in
-//     10^5 elements of Gaussian weights, and every exact tie) redoes its 8
+//     integer as the exact one.  The code plus 8 is first formed as
+//     u = fma(w, rcp(s), 8) (v_rcp_f32, relative error below 2^-22;
+//     |w / s| <= 7.004, or < 10.5 when s is an fp16 subnormal, so w * rcp(s)
+//     is within 3e-6 of w / s, and the fma's one rounding of a value below
+//     32 adds at most 2^-20): u is within 4e-6 of w / s + 8, and rint(u) -
+//     8 can differ from rint(w / s) only if u lies within 4e-6 of a
+//     half-integer (8 is even, so away from ties the shift commutes with
+//     rounding); a lane that sees a u within 2e-5 of one (about 2 in 10^5
+//     elements of Gaussian weights, and every exact tie) redoes its 8
 //     elements with the IEEE fp32 division.
 #include "w4a16_device.h"
 #include "w4a16_launch.h"
@@ -82,11 +85,11 @@ __device__ __forceinline__ uint32_t quantize8(const uint4& v, uint16_t& s_bits) 
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const float w = f16_bits_to_f32((uint16_t)(h[i >> 1] >> (16 * (i & 1))));
-        const float t = w * inv;
-        const float r = rintf(t);
-        near_tie |= fabsf(t - r) > 0.49998f;
-        // code = clamp(r, -8, 7) + 8, exact small integers in fp32
-        const float c = __builtin_amdgcn_fmed3f(r + 8.0f, 0.0f, 15.0f);
+        const float u = fmaf(w, inv, 8.0f);       // w / s + 8, within 4e-6
+        const float r = rintf(u);
+        near_tie |= fabsf(u - r) > 0.49998f;
+        // code = clamp(rint(w / s), -8, 7) + 8 = clamp(r, 0, 15), exact in fp32
+        const float c = __builtin_amdgcn_fmed3f(r, 0.0f, 15.0f);
         word |= (uint32_t)c << (4 * i);
     }
     if (near_tie) {
