@@ -298,6 +298,19 @@ def stored_traffic(shape: str):
     return None if ent is None else int(ent["traffic_bytes"])
 
 
+def host_cpu_model() -> str:
+    """The host CPU's model name (/proc/cpuinfo), for the CPU baseline."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def dominant_roofline(per_shape, layer0, step_bytes, n_launch, avg_launch_us):
     """Roofline of the launch with the largest share of the sweep's time,
     timed live (HIP events around graph replays of that launch on the
@@ -586,7 +599,7 @@ def main() -> int:
             nl += 1
         csec = time.perf_counter() - c0
         cpu = {"value": round(cbytes / csec / 1e9, 3), "unit": "GB/s", "cores": orc.num_threads(),
-               "kind": "oracle",
+               "cpu_model": host_cpu_model(), "kind": "oracle",
                "sample": "%d layers of the sweep's shapes (%d GEMVs; the sweep has %d layers), "
                          "fp64 oracle, %.1f s; us per full sweep extrapolated: %.0f"
                          % (nl, nl * len(shapes), nlayers, csec, csec / nl * nlayers * 1e6)}

@@ -87,7 +87,10 @@ enum {
     W4A16_ALGO_MFMA = 2  /* force the MFMA path, any M */
 };
 
-/* Byte sizes of the packed weights (N*K/2) and the scales (N*(K/128)*2).
+/* Byte sizes of the packed weights (N*K/2) and the scales (N*(K/128)*2):
+ * [QUANT] sub-section 3's per-group listing stores two 4-bit codes per byte
+ * and one fp16 scale per group of 128 along in_features (its 3.1 % scale
+ * overhead is 2 bytes per 64 code bytes).
  * Return 0 for negative sizes, K % 128 != 0 or overflow. */
 size_t w4a16_packed_bytes(int64_t N, int64_t K);
 size_t w4a16_scales_bytes(int64_t N, int64_t K);
@@ -121,7 +124,9 @@ int w4a16_gemm(const uint16_t* X, int64_t M, const uint32_t* packed, const uint1
 
 /* w4a16_gemm with the kernel family forced by `algo` (W4A16_ALGO_*); an
  * unknown algo is W4A16_ERR_INVALID_ARG.  Results of every algo meet the same
- * tolerance; used to measure the VALU/MFMA crossover. */
+ * tolerance; used to measure the VALU/MFMA crossover.  The operation is
+ * w4a16_gemm's ([BENCH] §二: decode at one token, prefill at 512); only the
+ * kernel family that computes it is chosen here. */
 int w4a16_gemm_ex(const uint16_t* X, int64_t M, const uint32_t* packed, const uint16_t* scales,
                   int64_t N, int64_t K, uint16_t* Y, int algo, void* stream);
 

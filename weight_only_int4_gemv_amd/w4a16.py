@@ -437,12 +437,28 @@ def chain_sync_buffer(device="cuda") -> torch.Tensor:
     return torch.zeros(CHAIN_SYNC_WORDS, dtype=torch.int32, device=device)
 
 
-def gemv_chain(stages, sync: torch.Tensor) -> None:
+class W4A16ChainError(RuntimeError):
+    """A wait between the stages of a gemv_chain launch gave up: the grid was
+    not co-resident (the GPU was shared), so outputs may be stale."""
+
+
+def chain_error(sync: torch.Tensor) -> bool:
+    """True when the sticky error word of a gemv_chain sync buffer is set
+    (reads the word: synchronizes with the current stream)."""
+    return int(sync[CHAIN_ERR_WORD].item()) != 0
+
+
+def gemv_chain(stages, sync: torch.Tensor, check: bool = True) -> None:
     """Run a dependent sequence of decode GEMVs in one launch.
 
     stages: list of (x [K], packed [N, K/8], scales [N, K/128], y [N]) device
     tensors; x of a stage may be the y of an earlier stage (or a view of it).
     sync: int32 [CHAIN_SYNC_WORDS] device tensor from chain_sync_buffer().
+    check: after the launch, read the sync buffer's error word (this waits
+    for the launch) and raise W4A16ChainError if a wait between stages gave
+    up.  Skipped while the current stream is being captured into a graph;
+    callers that replay a graph (or pass check=False) test chain_error(sync)
+    themselves.
     """
     lib = library()
     if len(stages) > CHAIN_MAX:
@@ -464,6 +480,9 @@ def gemv_chain(stages, sync: torch.Tensor) -> None:
                            N, K)
     _check("w4a16_gemv_chain", lib.w4a16_gemv_chain(arr, len(stages), sync.data_ptr(),
                                                     _stream()))
+    if check and not torch.cuda.is_current_stream_capturing() and chain_error(sync):
+        raise W4A16ChainError("w4a16_gemv_chain: a wait between stages gave up (error word "
+                              "set); the outputs may be stale")
 
 
 def valu_max_m() -> int:
