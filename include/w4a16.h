@@ -274,6 +274,25 @@ typedef struct {
 
 int w4a16_gemv_chain(const w4a16_gemv_stage* stages, int count, uint32_t* sync, void* stream);
 
+/* w4a16_gemv_chain for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same stages, outputs and rules, with the counters in the
+ * library's own array instead of a caller buffer.
+ *   status   DEVICE uint32, 4-byte aligned, owned by the caller: written by
+ *            every call, 0 when every wait between stages completed, non-zero
+ *            when one gave up (the grid was not co-resident; outputs may then
+ *            be stale).  Must not overlap any stage's tensors.
+ * The array is W4A16_CHAIN_SYNC_WORDS uint32 per GPU, zero when the library
+ * is loaded and returned to zero (error word included) by every call; it
+ * lives until the process ends.  The limit is the one of w4a16_gemv_chain:
+ * count above W4A16_CHAIN_MAX is W4A16_ERR_INVALID_ARG.  Nothing is
+ * allocated and no memory is cleared from the host (no memset node).  All
+ * calls of a process on one GPU share its array: calls that overlap in time
+ * on one GPU (e.g. on two streams) race and must not be made; stream-ordered
+ * calls and graph replays are fine. */
+int w4a16_gemv_chain_noalloc(const w4a16_gemv_stage* stages, int count, uint32_t* status,
+                             void* stream);
+
 /* Largest M that W4A16_ALGO_AUTO sends to the VALU path. */
 int64_t w4a16_valu_max_m(void);
 

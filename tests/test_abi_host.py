@@ -37,7 +37,8 @@ def test_header_declares_the_boundary():
                "w4a16_scales_bytes_g", "w4a16_quantize_perm", "w4a16_gemv_perm",
                "w4a16_gemm_perm", "w4a16_quantize_asym", "w4a16_gemv_asym",
                "w4a16_gemm_asym", "w4a16_q4_0_bytes", "w4a16_quantize_q4_0",
-               "w4a16_gemv_q4_0", "w4a16_gemm_q4_0"]:
+               "w4a16_gemv_q4_0", "w4a16_gemm_q4_0", "w4a16_gemv_chain",
+               "w4a16_gemv_chain_noalloc"]:
         assert fn in names
 
 
@@ -302,3 +303,25 @@ def test_chain_validation(lib):
     assert ch(arr(GemvStage(A, B, C, D, 16, 128), GemvStage(A, B + 1024, D, D + 256, 16, 128)),
               2, S, None) == INVALID                                           # y on scales
     assert ch(arr(GemvStage(A, B, C, D, 16, 128)), 1, D, None) == INVALID      # sync on y
+
+
+def test_chain_noalloc_validation(lib):
+    """The no-allocation chain validates like w4a16_gemv_chain, plus its status
+    word (required, 4-byte aligned, not on any stage tensor)."""
+    from weight_only_int4_gemv_amd.w4a16 import GemvStage
+    A, B, C, D, S = FAKE, FAKE * 4, FAKE * 8, FAKE * 12, FAKE * 16
+    ch = lib.w4a16_gemv_chain_noalloc
+    a = (GemvStage * 1)()
+    a[0] = GemvStage(A, B, C, D, 16, 128)
+    assert ch(a, 0, S, None) == OK                       # empty: nothing enqueued
+    assert ch(a, -1, S, None) == INVALID
+    assert ch(a, 65, S, None) == INVALID                 # beyond the counters' stage limit
+    assert ch(a, 1, None, None) == INVALID               # status is required
+    assert ch(a, 1, S + 2, None) == MISALIGNED
+    assert ch(a, 1, D, None) == INVALID                  # status on an output
+    assert ch(a, 1, B + 64, None) == INVALID             # status on the weights
+    b = (GemvStage * 1)()
+    b[0] = GemvStage(A, B, C, D, 16, 100)
+    assert ch(b, 1, S, None) == SHAPE
+    assert ch(a, 1, S, None) in (DEVICE, OK)             # valid: only the device is left
+

@@ -303,17 +303,20 @@ int w4a16_gemm_asym(const uint16_t* X, int64_t M, const int32_t* perm, const uin
                   perm != nullptr, zeros, true);
 }
 
-int w4a16_gemv_chain(const w4a16_gemv_stage* stages, int count, uint32_t* sync, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validates a chain of stages and fills `args`.  `extra`, `extra_bytes`: a
+// caller buffer the chain writes (the sync buffer or the status word) that
+// must not overlap any stage's tensors; NULL for none.
+int chain_args(const w4a16_gemv_stage* stages, int count, const void* extra, size_t extra_bytes,
+               w4a16::ChainArgs* args, int64_t* max_n_out) {
     static_assert(W4A16_CHAIN_MAX == w4a16::kChainMax, "chain limit");
     static_assert(W4A16_CHAIN_SYNC_WORDS == w4a16::kChainSyncWords, "sync words");
     static_assert(W4A16_CHAIN_ERR_WORD == w4a16::kChainErrWord, "error word");
-    if (count < 0 || count > W4A16_CHAIN_MAX) return W4A16_ERR_INVALID_ARG;
-    if (count == 0) return W4A16_OK;
-    if (!stages || !sync) return W4A16_ERR_INVALID_ARG;
-    if (!aligned(sync, 4)) return W4A16_ERR_MISALIGNED;
-    const size_t sync_bytes = (size_t)W4A16_CHAIN_SYNC_WORDS * 4;
-    w4a16::ChainArgs args;
-    memset(&args, 0, sizeof(args));
+    if (!stages) return W4A16_ERR_INVALID_ARG;
+    memset(args, 0, sizeof(*args));
     int64_t max_k = 0, max_n = 0;
     for (int s = 0; s < count; ++s) {
         const w4a16_gemv_stage& st = stages[s];
@@ -330,8 +333,8 @@ int w4a16_gemv_chain(const w4a16_gemv_stage* stages, int count, uint32_t* sync, 
     for (int s = 0; s < count; ++s) {
         const w4a16_gemv_stage& a = stages[s];
         const size_t yb = (size_t)a.N * 2;
-        if (overlap(a.y, yb, a.x, (size_t)a.K * 2) || overlap(a.y, yb, sync, sync_bytes) ||
-            overlap(a.x, (size_t)a.K * 2, sync, sync_bytes))
+        if (overlap(a.y, yb, a.x, (size_t)a.K * 2) || overlap(a.y, yb, extra, extra_bytes) ||
+            overlap(a.x, (size_t)a.K * 2, extra, extra_bytes))
             return W4A16_ERR_INVALID_ARG;
         for (int t = 0; t < count; ++t) {
             const w4a16_gemv_stage& b = stages[t];
@@ -341,21 +344,59 @@ int w4a16_gemv_chain(const w4a16_gemv_stage* stages, int count, uint32_t* sync, 
             if (overlap(a.y, yb, b.packed, (size_t)b.N * b.K / 2) ||
                 overlap(a.y, yb, b.scales, (size_t)b.N * (b.K / W4A16_GROUP) * 2))
                 return W4A16_ERR_INVALID_ARG;
-            if (overlap(sync, sync_bytes, b.packed, (size_t)b.N * b.K / 2) ||
-                overlap(sync, sync_bytes, b.scales, (size_t)b.N * (b.K / W4A16_GROUP) * 2))
+            if (overlap(extra, extra_bytes, b.packed, (size_t)b.N * b.K / 2) ||
+                overlap(extra, extra_bytes, b.scales, (size_t)b.N * (b.K / W4A16_GROUP) * 2))
                 return W4A16_ERR_INVALID_ARG;
         }
-        args.st[s] = w4a16::ChainStageDev{a.x, a.packed, a.scales, a.y, (int)a.N, (int)a.K};
+        args->st[s] = w4a16::ChainStageDev{a.x, a.packed, a.scales, a.y, (int)a.N, (int)a.K};
     }
-    args.count = count;
-    args.x_vecs = (int)(max_k / 8);
+    args->count = count;
+    args->x_vecs = (int)(max_k / 8);
+    *max_n_out = max_n;
+    return W4A16_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int w4a16_gemv_chain(const w4a16_gemv_stage* stages, int count, uint32_t* sync, void* stream) {
+    if (count < 0 || count > W4A16_CHAIN_MAX) return W4A16_ERR_INVALID_ARG;
+    if (count == 0) return W4A16_OK;
+    if (!sync) return W4A16_ERR_INVALID_ARG;
+    if (!aligned(sync, 4)) return W4A16_ERR_MISALIGNED;
+    w4a16::ChainArgs args;
+    int64_t max_n = 0;
+    int st = chain_args(stages, count, sync, (size_t)W4A16_CHAIN_SYNC_WORDS * 4, &args, &max_n);
+    if (st != W4A16_OK) return st;
     args.sync = sync;
     int num_cu = 0;
-    const int st = current_device(&num_cu);
+    st = current_device(&num_cu);
     if (st != W4A16_OK) return st;
     int blocks = 0;
     return status_of(w4a16::launch_gemv_chain(args, max_n, static_cast<hipStream_t>(stream),
                                               num_cu, &blocks));
+}
+
+int w4a16_gemv_chain_noalloc(const w4a16_gemv_stage* stages, int count, uint32_t* status,
+                             void* stream) {
+    if (count < 0 || count > W4A16_CHAIN_MAX) return W4A16_ERR_INVALID_ARG;
+    if (count == 0) return W4A16_OK;
+    if (!status) return W4A16_ERR_INVALID_ARG;
+    if (!aligned(status, 4)) return W4A16_ERR_MISALIGNED;
+    w4a16::ChainArgs args;
+    int64_t max_n = 0;
+    int st = chain_args(stages, count, status, 4, &args, &max_n);
+    if (st != W4A16_OK) return st;
+    args.status = status;
+    int num_cu = 0;
+    st = current_device(&num_cu);
+    if (st != W4A16_OK) return st;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return W4A16_ERR_DEVICE;
+    return status_of(w4a16::launch_gemv_chain_noalloc(args, max_n,
+                                                      static_cast<hipStream_t>(stream), num_cu,
+                                                      dev));
 }
 
 int64_t w4a16_valu_max_m(void) { return kValuMaxM; }

@@ -29,6 +29,8 @@
 // of hanging; once the error word is set no later wait polls again.  The
 // last block to finish returns every counter to zero, so the buffer is ready
 // for the next call (and for graph replays).
+#include <mutex>
+
 #include "w4a16_device.h"
 #include "w4a16_launch.h"
 
@@ -174,6 +176,12 @@ __global__ __launch_bounds__((W + C) * kWave) void gemv_chain_kernel(ChainArgs a
             if (lane == 0) {
                 const uint32_t prev = sync_add(&sync[kDoneWord], 1u);
                 if (prev == gridDim.x - 1) {
+                    // every wait of this call is over: hand its error word to
+                    // the caller's status word and clear it, when asked to
+                    if (a.status != nullptr) {
+                        sync_store(a.status, sync_load(&sync[kChainErrWord]));
+                        sync_store(&sync[kChainErrWord], 0u);
+                    }
                     // every block is past every wait: return the counters to zero
                     sync_store(&sync[kRootWord], 0u);
                     for (int l = 0; l < kChainLeaves; ++l)
@@ -352,6 +360,45 @@ hipError_t launch_gemv_chain(const ChainArgs& args, int64_t max_n, hipStream_t s
     // 12 compute + 4 control waves, 4 iterations in flight: the fastest of
     // the shapes measured on the LLaMA-3-8B decode sweep.
     return launch_chain_t<12, 4, 4>(args, max_n, stream, num_cu, blocks_out);
+}
+
+// ---------------------------------------------------------------------
+// Counters for callers that cannot allocate device memory: one array per
+// device, loaded zeroed with the library and returned to zero by every call
+// (the last block clears the counters and, because args.status is set, the
+// error word).  The array's name is only a host-side handle: its device
+// address is looked up once per device and only that address is used.
+namespace {
+static __device__ __align__(256) uint32_t scratch[kChainSyncWords];
+
+constexpr int kMaxScratchDevices = 64;
+uint32_t* g_scratch[kMaxScratchDevices];
+std::mutex g_scratch_mutex;
+
+hipError_t scratch_address(int device, uint32_t** out) {
+    if (device < 0 || device >= kMaxScratchDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch[device] == nullptr) {
+        // `device` is the current device: the lookup returns its copy
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        g_scratch[device] = static_cast<uint32_t*>(p);
+    }
+    *out = g_scratch[device];
+    return hipSuccess;
+}
+}  // namespace
+
+hipError_t launch_gemv_chain_noalloc(ChainArgs& args, int64_t max_n, hipStream_t stream,
+                                     int num_cu, int device) {
+    if (args.status == nullptr) return hipErrorInvalidValue;
+    uint32_t* sync = nullptr;
+    const hipError_t e = scratch_address(device, &sync);
+    if (e != hipSuccess) return e;
+    args.sync = sync;
+    return launch_chain_t<12, 4, 4>(args, max_n, stream, num_cu, nullptr);
 }
 
 }  // namespace w4a16

@@ -100,11 +100,21 @@ struct ChainArgs {
     int count;
     int x_vecs;          // LDS x capacity in 16-byte vectors (max K / 8)
     uint32_t* sync;
+    // NULL: the error word stays set in `sync` (sticky).  Otherwise the last
+    // block writes this call's error word here and clears it in `sync`.
+    uint32_t* status;
 };
 
 // Launches one block per compute unit (co-resident); *blocks_out receives
 // the grid size.  max_n: the largest N of the stages.
 hipError_t launch_gemv_chain(const ChainArgs& args, int64_t max_n, hipStream_t stream,
                              int num_cu, int* blocks_out);
+
+// The same with the counters in the library's own per-device array (fixed
+// size kChainSyncWords words, zero when the library is loaded and after every
+// call); args.sync is filled in here, args.status must be set.  `device` is
+// the current HIP device.
+hipError_t launch_gemv_chain_noalloc(ChainArgs& args, int64_t max_n, hipStream_t stream,
+                                     int num_cu, int device);
 
 }  // namespace w4a16

@@ -89,6 +89,8 @@ def library() -> ctypes.CDLL:
         lib.w4a16_valu_max_m.restype = ctypes.c_int64
         lib.w4a16_gemv_chain.argtypes = [ctypes.POINTER(GemvStage), ctypes.c_int, _p, _p]
         lib.w4a16_gemv_chain.restype = ctypes.c_int
+        lib.w4a16_gemv_chain_noalloc.argtypes = [ctypes.POINTER(GemvStage), ctypes.c_int, _p, _p]
+        lib.w4a16_gemv_chain_noalloc.restype = ctypes.c_int
         lib.w4a16_status_string.argtypes = [ctypes.c_int]
         lib.w4a16_status_string.restype = ctypes.c_char_p
         _lib = lib
@@ -448,6 +450,38 @@ def chain_error(sync: torch.Tensor) -> bool:
     return int(sync[CHAIN_ERR_WORD].item()) != 0
 
 
+def _chain_stages(stages):
+    arr = (GemvStage * max(1, len(stages)))()
+    for i, (x, packed, scales, y) in enumerate(stages):
+        N, K, group = _weights(packed, scales)
+        if group != W4A16_GROUP:
+            raise ValueError("stage %d: gemv_chain takes group %d weights" % (i, W4A16_GROUP))
+        _need(x, "x", torch.float16, 1)
+        _need(y, "y", torch.float16, 1)
+        if x.shape[0] != K or y.shape[0] != N:
+            raise ValueError("stage %d: x has %d elements (K = %d), y %d (N = %d)"
+                             % (i, x.shape[0], K, y.shape[0], N))
+        arr[i] = GemvStage(x.data_ptr(), packed.data_ptr(), scales.data_ptr(), y.data_ptr(),
+                           N, K)
+    return arr
+
+
+def gemv_chain_noalloc(stages, status: torch.Tensor) -> None:
+    """w4a16_gemv_chain_noalloc: gemv_chain with the library's own counters
+    (no sync buffer).  status: int32 [1] device tensor; after the launch it
+    holds 0, or non-zero when a wait between stages gave up (the caller reads
+    it when convenient)."""
+    lib = library()
+    if len(stages) > CHAIN_MAX:
+        raise ValueError("at most %d stages per call" % CHAIN_MAX)
+    _need(status, "status", torch.int32, 1)
+    if status.shape[0] < 1:
+        raise ValueError("status needs one element")
+    arr = _chain_stages(stages)
+    _check("w4a16_gemv_chain_noalloc",
+           lib.w4a16_gemv_chain_noalloc(arr, len(stages), status.data_ptr(), _stream()))
+
+
 def gemv_chain(stages, sync: torch.Tensor, check: bool = True) -> None:
     """Run a dependent sequence of decode GEMVs in one launch.
 
@@ -466,18 +500,7 @@ def gemv_chain(stages, sync: torch.Tensor, check: bool = True) -> None:
     _need(sync, "sync", torch.int32, 1)
     if sync.shape[0] < CHAIN_SYNC_WORDS:
         raise ValueError("sync needs %d words" % CHAIN_SYNC_WORDS)
-    arr = (GemvStage * max(1, len(stages)))()
-    for i, (x, packed, scales, y) in enumerate(stages):
-        N, K, group = _weights(packed, scales)
-        if group != W4A16_GROUP:
-            raise ValueError("stage %d: gemv_chain takes group %d weights" % (i, W4A16_GROUP))
-        _need(x, "x", torch.float16, 1)
-        _need(y, "y", torch.float16, 1)
-        if x.shape[0] != K or y.shape[0] != N:
-            raise ValueError("stage %d: x has %d elements (K = %d), y %d (N = %d)"
-                             % (i, x.shape[0], K, y.shape[0], N))
-        arr[i] = GemvStage(x.data_ptr(), packed.data_ptr(), scales.data_ptr(), y.data_ptr(),
-                           N, K)
+    arr = _chain_stages(stages)
     _check("w4a16_gemv_chain", lib.w4a16_gemv_chain(arr, len(stages), sync.data_ptr(),
                                                     _stream()))
     if check and not torch.cuda.is_current_stream_capturing() and chain_error(sync):
