@@ -75,7 +75,84 @@ def parse():
     return p.parse_args()
 
 
-def secondary(torch, w4a16, inputs, dev, stream):
+def fused_groups(names):
+    """Launch groups of a layer: matrices that share an input are stored
+    concatenated along N (q/k/v and gate/up)."""
+    if names == ["q", "k", "v", "o", "gate", "up", "down"]:
+        return [["q", "k", "v"], ["o"], ["gate", "up"], ["down"]]
+    return [[n] for n in names]
+
+
+def sweep_row(torch, w4a16, inputs, dev, workload, case_id):
+    """Another model's decode weight sweep (fused layout, graph replays):
+    us per sweep, GB/s and the dominant launch, for the secondary rows."""
+    shape_attr, layers_attr = WORKLOADS[workload]
+    shapes = getattr(inputs, shape_attr)
+    nlayers = getattr(inputs, layers_attr)
+    names = [n for n, _, _ in shapes]
+    dims = {n: (K, N) for n, K, N in shapes}
+    layer0 = []
+    for group in fused_groups(names):
+        K = dims[group[0]][0]
+        ps, ss = [], []
+        for name in group:
+            W = inputs.weight(dims[name][1], K, seed=inputs.matrix_seed(case_id, 0,
+                                                                      names.index(name)))
+            p, s_ = w4a16.quantize(torch.from_numpy(W).to(dev))
+            ps.append(p)
+            ss.append(s_)
+        layer0.append(("_".join(group), K, torch.cat(ps), torch.cat(ss)))
+    layers = [layer0] + [[(g, K, p.clone(), s_.clone()) for (g, K, p, s_) in layer0]
+                         for _ in range(nlayers - 1)]
+    xs = {K: torch.from_numpy(inputs.activation(1, K, seed=[1000, case_id, K])[0]).to(dev)
+          for _, K, _ in shapes}
+    ys = {g: torch.empty((p.shape[0],), dtype=torch.float16, device=dev)
+          for (g, K, p, _) in layer0}
+    seq = [(xs[K], p, s_, ys[g]) for layer in layers for (g, K, p, s_) in layer]
+    nbytes = sum(gemv_bytes(p.shape[0], K) for layer in layers for (_, K, p, _) in layer)
+
+    def timed(sub, reps=10):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for x, p, s_, y in sub:
+                w4a16.gemv(x, p, s_, y=y)
+        for _ in range(3):
+            g.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    us = timed(seq)
+    per_group = {}
+    for (g, K, p, _) in layer0:
+        sub = [t for t in seq if t[3] is ys[g]]
+        gus = timed(sub) / len(sub)
+        per_group[g] = {"K": K, "N": int(p.shape[0]), "us": round(gus, 3),
+                        "GB/s": round(gemv_bytes(p.shape[0], K) / (gus * 1e-6) / 1e9, 1)}
+    dom = max(per_group, key=lambda g: per_group[g]["us"] * nlayers)
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"workload": workload, "layers": nlayers, "launches_per_sweep": len(seq),
+            "bytes_per_sweep": nbytes, "us_per_sweep": round(us, 2), "GB/s": round(gbs, 1),
+            "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "per_launch": per_group,
+            "dominant_launch": dom,
+            "dominant_frac_of_hbm_peak": round(per_group[dom]["GB/s"] / HBM_PEAK_GBS, 4)}
+
+
+def weight_copies(p0, s0, min_bytes=600 << 20, extra=()):
+    """Copies of one quantized matrix (the original first) whose packed
+    weights and scales add up to at least min_bytes (more than twice the
+    256 MB Infinity Cache), so that every timed launch reads from HBM."""
+    one = p0.numel() * 4 + s0.numel() * 2 + sum(t.numel() * t.element_size() for t in extra)
+    n = max(2, -(-min_bytes // one))
+    return [(p0, s0, *extra)] + [(p0.clone(), s0.clone(), *[t.clone() for t in extra])
+                                 for _ in range(n - 1)]
+
+
+def secondary(torch, w4a16, inputs, dev, stream, main_workload="llama3-8b-sweep"):
     """Other rows of the path on their workload shapes: the quantizer (70B FFN
     matrix, larger than the Infinity Cache), batched decode M = 1..32 on the
     8B FFN shapes with both kernel families (locates the VALU/MFMA
@@ -125,8 +202,8 @@ def secondary(torch, w4a16, inputs, dev, stream):
     batched = {}
     for (K, N) in [(4096, 14336), (14336, 4096)]:
         p0, s0 = weights_for(K, N)
-        copies = [(p0.clone(), s0.clone()) for _ in range(12)]      # 364 MB of weights
-        for M in [1, 2, 4, 8, 16, 32]:
+        copies = weight_copies(p0, s0)                              # >= 600 MB of weights
+        for M in [1, 2, 3, 4, 8, 16, 32]:
             X = torch.from_numpy(inputs.activation(M, K, seed=[6, M, K])).to(dev)
             Y = torch.empty((M, N), dtype=torch.float16, device=dev)
             row = {}
@@ -145,7 +222,7 @@ def secondary(torch, w4a16, inputs, dev, stream):
     prefill = {}
     for (K, N) in [(4096, 14336), (14336, 4096), (8192, 28672)]:
         p0, s0 = weights_for(K, N)
-        copies = [(p0, s0)] + [(p0.clone(), s0.clone()) for _ in range(3)]
+        copies = weight_copies(p0, s0)                              # >= 600 MB of weights
         X = torch.from_numpy(inputs.activation(512, K, seed=[7, K])).to(dev)
         Y = torch.empty((512, N), dtype=torch.float16, device=dev)
         us = timed(lambda: [w4a16.gemm(X, p, s_, Y=Y) for p, s_ in copies]) / len(copies)
@@ -166,7 +243,7 @@ def secondary(torch, w4a16, inputs, dev, stream):
     for group in (32, 64, 128, 256):
         pg, sg = w4a16.quantize(Wg, group=group)
         qus = timed(lambda: w4a16.quantize(Wg, pg, sg, group=group))
-        copies = [(pg, sg)] + [(pg.clone(), sg.clone()) for _ in range(11)]
+        copies = weight_copies(pg, sg)
         us = timed(lambda: [w4a16.gemv(x, p, s_, y=y) for p, s_ in copies]) / len(copies)
         b = N * K // 2 + N * (K // group) * 2 + 2 * K + 2 * N
         qb = N * K * 2 + N * K // 2 + N * (K // group) * 2
@@ -182,7 +259,7 @@ def secondary(torch, w4a16, inputs, dev, stream):
     act = {}
     for (K, N) in [(4096, 14336), (14336, 4096)]:
         p0, s0 = weights_for(K, N)
-        copies = [(p0, s0)] + [(p0.clone(), s0.clone()) for _ in range(11)]
+        copies = weight_copies(p0, s0)
         x = torch.from_numpy(inputs.activation(1, K, seed=[9, K])).to(dev)[0]
         y = torch.empty((N,), dtype=torch.float16, device=dev)
         perm = torch.randperm(K, generator=torch.Generator().manual_seed(K)).to(
@@ -203,13 +280,13 @@ def secondary(torch, w4a16, inputs, dev, stream):
         Wd = torch.from_numpy(inputs.weight_skewed(N, K, seed=[10, K, N])).to(dev)
         pa, sa, za = w4a16.quantize_asym(Wd)
         qus = timed(lambda: w4a16.quantize_asym(Wd, pa, sa, za))
-        copies = [(pa, sa, za)] + [(pa.clone(), sa.clone(), za.clone()) for _ in range(11)]
+        copies = weight_copies(pa, sa, extra=(za,))
         x = torch.from_numpy(inputs.activation(1, K, seed=[10, K])).to(dev)[0]
         y = torch.empty((N,), dtype=torch.float16, device=dev)
         us = timed(lambda: [w4a16.gemv_asym(x, p, s_, z, y=y) for p, s_, z in copies]) \
             / len(copies)
         p0, s0 = weights_for(K, N)
-        sym = [(p0, s0)] + [(p0.clone(), s0.clone()) for _ in range(11)]
+        sym = weight_copies(p0, s0)
         plain = timed(lambda: [w4a16.gemv(x, p, s_, y=y) for p, s_ in sym]) / len(sym)
         b = gemv_bytes(N, K) + N * (K // 128) * 2
         qb = N * K * 2 + N * K // 2 + 2 * N * (K // 128) * 2
@@ -222,10 +299,10 @@ def secondary(torch, w4a16, inputs, dev, stream):
         for M in (16, 512):
             X = torch.from_numpy(inputs.activation(M, K, seed=[10, M, K])).to(dev)
             Y = torch.empty((M, N), dtype=torch.float16, device=dev)
-            few = copies[:4] if M == 512 else copies
+            few = copies
             a_us = timed(lambda: [w4a16.gemm_asym(X, p, s_, z, Y=Y) for p, s_, z in few]) \
                 / len(few)
-            fews = sym[:4] if M == 512 else sym
+            fews = sym
             s_us = timed(lambda: [w4a16.gemm(X, p, s_, Y=Y) for p, s_ in fews]) / len(fews)
             row["M=%d_us" % M] = round(a_us, 2)
             row["M=%d_symmetric_us" % M] = round(s_us, 2)
@@ -243,7 +320,7 @@ def secondary(torch, w4a16, inputs, dev, stream):
         bq = w4a16.quantize_q4_0(Wd)
         qus = timed(lambda: w4a16.quantize_q4_0(Wd, bq))
         copies = [bq]
-        for _ in range(11):
+        for _ in range(max(1, -(-(600 << 20) // bq.numel()) - 1)):
             c = w4a16.q4_0_blocks(N, K, device=dev)
             c.copy_(bq)
             copies.append(c)
@@ -251,7 +328,7 @@ def secondary(torch, w4a16, inputs, dev, stream):
         y = torch.empty((N,), dtype=torch.float16, device=dev)
         us = timed(lambda: [w4a16.gemv_q4_0(x, b_, y=y) for b_ in copies]) / len(copies)
         pg, sg = w4a16.quantize(Wd, group=32)
-        split = [(pg, sg)] + [(pg.clone(), sg.clone()) for _ in range(11)]
+        split = weight_copies(pg, sg)
         sus = timed(lambda: [w4a16.gemv(x, p, s_, y=y) for p, s_ in split]) / len(split)
         b = N * (K // 32) * 18 + 2 * K + 2 * N
         qb = N * K * 2 + N * (K // 32) * 18
@@ -263,6 +340,11 @@ def secondary(torch, w4a16, inputs, dev, stream):
         del copies, split, Wd
     out["q4_0_m1"] = q40
     quantized.clear()
+
+    # the other model's decode weight sweep (Qwen-2.5-7B beside LLaMA-3-8B)
+    other = "qwen2.5-7b-sweep" if main_workload == "llama3-8b-sweep" else "llama3-8b-sweep"
+    out["sweep_" + other] = sweep_row(torch, w4a16, inputs, dev, other,
+                                      3 if other.startswith("qwen") else 2)
     return out
 
 
@@ -373,8 +455,7 @@ def main() -> int:
     t0 = time.time()
     names = [n for n, _, _ in shapes]
     dims = {n: (K, N) for n, K, N in shapes}
-    fuse = [["q", "k", "v"], ["o"], ["gate", "up"], ["down"]] \
-        if names == ["q", "k", "v", "o", "gate", "up", "down"] else [[n] for n in names]
+    fuse = fused_groups(names)
     host_w = {}
     layer0 = []   # (group name, K, N, packed, scales, [(member, row0, rows)])
     for gi, group in enumerate(fuse):
@@ -606,7 +687,7 @@ def main() -> int:
 
     sec = None
     if not args.no_secondary:
-        sec = secondary(torch, w4a16, inputs, dev, stream)
+        sec = secondary(torch, w4a16, inputs, dev, stream, args.workload)
 
     roofline = dominant_roofline(per_shape, layer0, step_bytes, n_launch, avg_launch_us)
 

@@ -293,6 +293,46 @@ def test_prefill_512(w4, orc, K, N):
     check_linear(w4, orc, 512, N, K, seed=[5, K, N], algo="auto", name="prefill")
 
 
+def whole_reference(orc, X16: np.ndarray, packed: np.ndarray, scales: np.ndarray):
+    """(Y, Yabs) for every output of a workload-size product: the oracle's
+    exact dequantized weights (binary64 s*q) multiplied by X in a float64
+    matrix product (a library primitive), and |X| times |W| for the
+    tolerance.  The product's own rounding, at most about K 2^-53 sum|x w|,
+    is below 1e-9 of the allowance."""
+    What = orc.dequantize(packed, scales)
+    Xf = X16.astype(np.float64)
+    Y = Xf @ What.T
+    np.abs(What, out=What)
+    Yabs = np.abs(Xf) @ What.T
+    return Y, Yabs
+
+
+WHOLE_CASES = [(32, 4096, 14336, "auto"), (32, 14336, 4096, "auto"),
+               (16, 14336, 4096, "auto"), (512, 4096, 14336, "auto"),
+               (512, 14336, 4096, "auto"), (512, 8192, 28672, "auto")]
+
+
+@pytest.mark.parametrize("M,K,N,algo", WHOLE_CASES,
+                         ids=["M%d-%dx%d" % (c[0], c[1], c[2]) for c in WHOLE_CASES])
+def test_workload_size_whole_output(w4, orc, M, K, N, algo):
+    """Batched decode (M = 16, 32 on the FFN shapes) and the 512-token
+    prefill (both FFN shapes and the 70B FFN) compared on EVERY output, in
+    the launch configuration the benchmark times (the automatic choice), so
+    that each block-tile family and every tile of these grids is checked."""
+    say("whole output M=%d K=%d N=%d algo=%s" % (M, K, N, algo))
+    _, packed, scales = layer(N, K, (7, K, N))
+    X = inputs.activation(M, K, seed=[7, K, N, M])
+    Y = run_linear(w4, X, packed, scales, algo)
+    torch.cuda.synchronize()
+    assert Y.shape == (M, N)
+    Yref, Yabs = whole_reference(orc, X, packed, scales)
+    tol = oracle.tolerance(Yref, Yabs)
+    err = np.abs(Y.astype(np.float64) - Yref)
+    bad = np.argwhere(~(err <= tol))
+    assert bad.size == 0, "%d of %d outputs out of tolerance, first %s: got %r want %r tol %r" % (
+        len(bad), Y.size, bad[0], Y[tuple(bad[0])], Yref[tuple(bad[0])], tol[tuple(bad[0])])
+
+
 @pytest.mark.parametrize("M,N,K", [(520, 6600, 384), (129, 33000, 256), (512, 32776, 128)])
 def test_prefill_wide_tiles_ragged(w4, orc, M, N, K):
     """Enough 128-row by 128-column tiles to fill the compute units, so the
