@@ -214,6 +214,16 @@ def secondary(torch, w4a16, inputs, dev, stream, main_workload="llama3-8b-sweep"
                 row[algo] = {"us": round(us, 3), "GB/s": round(b / (us * 1e-6) / 1e9, 1),
                              "TFLOP/s": round(2 * M * N * K / (us * 1e-6) / 1e12, 2)}
             row["auto_picks"] = "valu" if M <= w4a16.valu_max_m() else "mfma"
+            # K split over blocks through a workspace (w4a16_gemm_ws), where
+            # the library splits the shape
+            if w4a16.library().w4a16_gemm_workspace_bytes(M, N, K) > 0:
+                ws = w4a16.gemm_workspace(M, N, K, device=dev)
+                us = timed(lambda: [w4a16.gemm_ws(X, p, s_, ws, Y=Y) for p, s_ in copies]) \
+                    / len(copies)
+                b = gemv_bytes(N, K, M)
+                row["mfma_split_k"] = {"us": round(us, 3), "GB/s": round(b / (us * 1e-6) / 1e9, 1),
+                                       "TFLOP/s": round(2 * M * N * K / (us * 1e-6) / 1e12, 2),
+                                       "workspace_bytes": int(ws.numel())}
             batched["%dx%d M=%d" % (K, N, M)] = row
         del copies
     out["batched_decode"] = batched

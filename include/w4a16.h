@@ -130,6 +130,32 @@ int w4a16_gemm(const uint16_t* X, int64_t M, const uint32_t* packed, const uint1
 int w4a16_gemm_ex(const uint16_t* X, int64_t M, const uint32_t* packed, const uint16_t* scales,
                   int64_t N, int64_t K, uint16_t* Y, int algo, void* stream);
 
+/* ---- Batched decode with K split over blocks ([BENCH] §二: decode of a few
+ * tokens is one pass over the weights; the FFN down projection has K = 3.5 N,
+ * so one block per compute unit would own 16 of its rows and read all of X
+ * for them).  w4a16_gemm with a caller workspace: for the shapes that
+ * w4a16_gemm_workspace_bytes reports a non-zero size for, blocks own more
+ * rows and one slice of K each, store fp32 partial tiles in the workspace,
+ * and the last slice of each row block to finish adds them in slice order
+ * (deterministic) and writes Y.  Other shapes run exactly as w4a16_gemm and
+ * ignore the workspace.  Same accuracy bound as w4a16_gemm; the sum order
+ * differs, so results are not bit-identical to it.
+ *   workspace  DEVICE, 256-byte aligned, at least
+ *              w4a16_gemm_workspace_bytes(M, N, K) bytes, owned by the caller,
+ *              all zero before its first use; every call leaves its counters
+ *              zero again, so it is reused without clearing.  Calls sharing a
+ *              workspace must not overlap in time (stream-ordered calls and
+ *              graph replays are fine).  It must not overlap X, Y or the
+ *              weights.
+ * w4a16_gemm_workspace_bytes returns 0 for shapes that do not split, for
+ * invalid sizes and when the current device is not gfx950 (the split depends
+ * on the compute-unit count).  A workspace smaller than required is
+ * W4A16_ERR_INVALID_ARG. */
+size_t w4a16_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+int w4a16_gemm_ws(const uint16_t* X, int64_t M, const uint32_t* packed, const uint16_t* scales,
+                  int64_t N, int64_t K, uint16_t* Y, void* workspace, size_t workspace_bytes,
+                  void* stream);
+
 /* ---- Group size as a parameter ([QUANT] sub-section 3 granularity table:
  * group 128 is the default, group 32 for outlier-sensitive layers; [QUANT]
  * GPTQ section, group_size table: 256, 128, 64 and 32 trade scale storage,

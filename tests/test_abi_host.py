@@ -38,7 +38,7 @@ def test_header_declares_the_boundary():
                "w4a16_gemm_perm", "w4a16_quantize_asym", "w4a16_gemv_asym",
                "w4a16_gemm_asym", "w4a16_q4_0_bytes", "w4a16_quantize_q4_0",
                "w4a16_gemv_q4_0", "w4a16_gemm_q4_0", "w4a16_gemv_chain",
-               "w4a16_gemv_chain_noalloc"]:
+               "w4a16_gemv_chain_noalloc", "w4a16_gemm_ws", "w4a16_gemm_workspace_bytes"]:
         assert fn in names
 
 
@@ -324,4 +324,21 @@ def test_chain_noalloc_validation(lib):
     b[0] = GemvStage(A, B, C, D, 16, 100)
     assert ch(b, 1, S, None) == SHAPE
     assert ch(a, 1, S, None) in (DEVICE, OK)             # valid: only the device is left
+
+
+def test_gemm_ws_validation(lib):
+    """Sizes are checked before the device; the split plan (and so the
+    workspace size) needs a gfx950 device, so without one the size is 0 and
+    valid calls report the device error."""
+    A, B, C, D, S = FAKE, FAKE * 4, FAKE * 8, FAKE * 12, FAKE * 16
+    f = lib.w4a16_gemm_ws
+    n = lib.w4a16_gemm_workspace_bytes(16, 4096, 14336)
+    assert n == 0 or n > 4096          # 0 without a gfx950 device
+    assert lib.w4a16_gemm_workspace_bytes(-1, 4096, 14336) == 0
+    assert lib.w4a16_gemm_workspace_bytes(16, 4096, 100) == 0
+    assert f(A, -1, B, C, 16, 128, D, S, 4096, None) == INVALID
+    assert f(A, 4, B, C, 16, 100, D, S, 4096, None) == SHAPE
+    assert f(A, 0, B, C, 16, 128, D, S, 4096, None) == OK      # empty: nothing enqueued
+    assert f(None, 4, B, C, 16, 128, D, S, 4096, None) == INVALID
+    assert f(A, 4, B, C, 16, 128, D, S, 4096, None) in (DEVICE, OK)
 

@@ -1028,3 +1028,90 @@ def test_q4_0_empty_and_k_zero(w4):
     with pytest.raises(ValueError):                  # storage without the padding
         w4.gemv_q4_0(torch.zeros(128, dtype=torch.float16, device="cuda"),
                      torch.zeros((1, 72), dtype=torch.uint8, device="cuda"))
+
+
+# ------------------------------------------------------ split-K batched decode
+
+WS_CASES = [(5, 14336, 4096), (8, 14336, 4096), (16, 14336, 4096), (17, 14336, 4096),
+            (32, 14336, 4096), (16, 18944, 3584), (32, 18944, 3584), (9, 16384, 4000),
+            (32, 2048, 300), (3, 14336, 4096), (16, 4096, 14336)]
+
+
+@pytest.mark.parametrize("M,K,N", WS_CASES, ids=["M%d-%dx%d" % c for c in WS_CASES])
+def test_gemm_ws_split_k(w4, orc, M, K, N):
+    """w4a16_gemm_ws on the long-K batched-decode shapes that it splits over
+    blocks (and shapes it does not split, which run as w4a16_gemm): every
+    output within the tolerance of the oracle, the workspace counters back
+    to zero after the call, and a second call bit-identical to the first
+    (the slices are summed in a fixed order)."""
+    say("gemm_ws M=%d K=%d N=%d" % (M, K, N))
+    _, packed, scales = layer(N, K, (8, K, N))
+    X = inputs.activation(M, K, seed=[8, K, N, M])
+    nws = w4.library().w4a16_gemm_workspace_bytes(M, N, K)
+    ws = w4.gemm_workspace(M, N, K)
+    Xd, pd, sd = dev(X), packed_to_dev(packed), scales_to_dev(scales)
+    Y1 = w4.gemm_ws(Xd, pd, sd, ws).cpu().numpy()
+    Y2 = w4.gemm_ws(Xd, pd, sd, ws).cpu().numpy()
+    torch.cuda.synchronize()
+    assert np.array_equal(Y1.view(np.uint16), Y2.view(np.uint16)), "not deterministic"
+    if nws:
+        assert int(ws[:4096].view(torch.int32).abs().sum().item()) == 0, "counters not zero"
+    if M * N * K <= 6e8:
+        Yref, Yabs = orc.matmul(X, packed, scales)
+    else:
+        Yref, Yabs = whole_reference(orc, X, packed, scales)
+    tol = oracle.tolerance(Yref, Yabs)
+    err = np.abs(Y1.astype(np.float64) - Yref)
+    bad = np.argwhere(~(err <= tol))
+    assert bad.size == 0, "%d outputs out of tolerance, first %s" % (len(bad), bad[0])
+
+
+def test_gemm_ws_one_workspace_many_shapes(w4, orc):
+    """One workspace, sized for the largest split, reused across split and
+    unsplit shapes in any order (the counters live at a fixed place for
+    every shape) and under graph replay: every result equal to the first
+    call's of its shape."""
+    shapes = [(16, 14336, 4096), (32, 18944, 3584), (8, 16384, 4000), (16, 4096, 14336),
+              (32, 14336, 4096)]
+    need = max(w4.library().w4a16_gemm_workspace_bytes(M, N, K) for M, K, N in shapes)
+    assert need > 0
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    runs = []
+    for M, K, N in shapes:
+        _, packed, scales = layer(N, K, (8, K, N))
+        X = dev(inputs.activation(M, K, seed=[9, K, N, M]))
+        runs.append((X, packed_to_dev(packed), scales_to_dev(scales)))
+    say("gemm_ws shared workspace")
+    first = [w4.gemm_ws(X, p, s, ws).clone() for X, p, s in runs]
+    for order in ([4, 3, 2, 1, 0], [1, 1, 0, 2, 4, 3]):
+        for i in order:
+            X, p, s = runs[i]
+            got = w4.gemm_ws(X, p, s, ws)
+            assert torch.equal(got.view(torch.int16), first[i].view(torch.int16)), i
+    outs = [torch.empty_like(f) for f in first]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for (X, p, s), o in zip(runs, outs):
+            w4.gemm_ws(X, p, s, ws, Y=o)
+    for rep in range(3):
+        for o in outs:
+            o.fill_(float("nan"))
+        junk = torch.randn(1 << 18, device="cuda").sum()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (o, f) in enumerate(zip(outs, first)):
+            assert torch.equal(o.view(torch.int16), f.view(torch.int16)), (rep, i)
+        del junk
+    assert int(ws[:4096].view(torch.int32).abs().sum().item()) == 0
+
+
+def test_gemm_ws_rejects_small_workspace(w4):
+    M, K, N = 16, 14336, 4096
+    need = w4.library().w4a16_gemm_workspace_bytes(M, N, K)
+    assert need > 4096
+    X = torch.zeros((M, K), dtype=torch.float16, device="cuda")
+    p = torch.zeros((N, K // 8), dtype=torch.int32, device="cuda")
+    s = torch.zeros((N, K // 128), dtype=torch.float16, device="cuda")
+    small = torch.zeros(need - 256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(w4.W4A16Error):
+        w4.gemm_ws(X, p, s, small)

@@ -266,6 +266,63 @@ int w4a16_gemm_ex(const uint16_t* X, int64_t M, const uint32_t* packed, const ui
     return linear(X, M, packed, scales, N, K, W4A16_GROUP, Y, algo, stream);
 }
 
+}  // extern "C"
+
+namespace {
+
+// The K-split plan w4a16_gemm_ws uses: the batched-decode shapes that the
+// automatic choice sends to the batched matrix-core kernel (above the 4x4x4
+// GEMV's rows, at most 32 rows), when the planner splits them.
+w4a16::BatchedSplit ws_plan(int64_t M, int64_t N, int64_t K, int num_cu) {
+    w4a16::BatchedSplit none{};
+    none.ksplit = 1;
+    const bool batched = M > kValuMaxM && M <= w4a16::kBatchedMaxM && K > 0 &&
+                         !(M <= w4a16::kMfma4MaxM && M * K * 2 <= w4a16::kMfma4MaxXBytes);
+    return batched ? w4a16::plan_batched_split(M, N, K, num_cu) : none;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t w4a16_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    if (check_sizes(M, N, K) != W4A16_OK || M == 0 || N == 0) return 0;
+    int num_cu = 0;
+    if (current_device(&num_cu) != W4A16_OK) return 0;
+    const w4a16::BatchedSplit p = ws_plan(M, N, K, num_cu);
+    return p.ksplit > 1 ? p.workspace_bytes : 0;
+}
+
+int w4a16_gemm_ws(const uint16_t* X, int64_t M, const uint32_t* packed, const uint16_t* scales,
+                  int64_t N, int64_t K, uint16_t* Y, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+    int st = check_sizes(M, N, K);
+    if (st != W4A16_OK) return st;
+    if (M == 0 || N == 0) return W4A16_OK;
+    int num_cu = 0;
+    // shapes the planner does not split run as w4a16_gemm (workspace unused)
+    if (K > 0 && (!X || !packed || !scales || !Y)) return W4A16_ERR_INVALID_ARG;
+    st = current_device(&num_cu);
+    if (st != W4A16_OK) return st;
+    const w4a16::BatchedSplit plan = ws_plan(M, N, K, num_cu);
+    if (plan.ksplit < 2) return w4a16_gemm(X, M, packed, scales, N, K, Y, stream);
+    if (!workspace || workspace_bytes < plan.workspace_bytes) return W4A16_ERR_INVALID_ARG;
+    if (!aligned(X, 16) || !aligned(packed, 16) || !aligned(scales, 2) || !aligned(Y, 2) ||
+        !aligned(workspace, 256))
+        return W4A16_ERR_MISALIGNED;
+    const size_t y_bytes = (size_t)M * N * 2, x_bytes = (size_t)M * K * 2;
+    const size_t p_bytes = (size_t)N * K / 2, s_bytes = (size_t)N * (K / W4A16_GROUP) * 2;
+    const size_t w_bytes = plan.workspace_bytes;
+    if (overlap(Y, y_bytes, X, x_bytes) || overlap(Y, y_bytes, packed, p_bytes) ||
+        overlap(Y, y_bytes, scales, s_bytes) || overlap(workspace, w_bytes, X, x_bytes) ||
+        overlap(workspace, w_bytes, Y, y_bytes) || overlap(workspace, w_bytes, packed, p_bytes) ||
+        overlap(workspace, w_bytes, scales, s_bytes))
+        return W4A16_ERR_INVALID_ARG;
+    return status_of(w4a16::launch_gemm_batched_split(X, M, packed, scales, N, K, Y,
+                                                      static_cast<hipStream_t>(stream), plan,
+                                                      workspace));
+}
+
 int w4a16_quantize_perm(const uint16_t* W, const int32_t* perm, int64_t N, int64_t K,
                         uint32_t* packed, uint16_t* scales, void* stream) {
     return quantize(W, N, K, W4A16_GROUP, packed, scales, stream, perm, true);

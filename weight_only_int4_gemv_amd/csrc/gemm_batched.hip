@@ -38,6 +38,17 @@
 // stored); rows past the block's range and k past K read 0 through buffer
 // bounds, and groups past K are skipped.
 //
+// Split K (SPLIT, batched decode with a caller workspace): when a block
+// would own only a few rows of a long-K matrix (the down projection), X is
+// the bulk of what each block reads (every block needs all of X for its
+// rows).  Block (b, k) then owns more rows and only the groups of K-slice k:
+// X per block shrinks by the number of slices.  Each block stores its fp32
+// partial tile to the workspace with device-coherent stores, waits for them
+// and counts itself on its row block's counter; the block that counts last
+// adds the slices' partials in slice order (the same order whichever block
+// is last, so results do not depend on timing), writes Y and returns the
+// counter to zero.  No block ever waits for another.
+//
 // Asymmetric weights (ASYM, [QUANT] sub-section 2: w = s (n - z), nibble n
 // in [0, 15], an int16 zero point z per row and group): the zero points are
 // staged beside the scales, the B operand holds the exact codes n - zc
@@ -53,16 +64,18 @@ namespace w4a16 {
 namespace {
 constexpr int kBatchedXVecs = 8;                    // staged 16-byte vectors per thread and chunk
 constexpr int kBatchedScales = 4;                   // staged scales per thread and chunk
+constexpr int kCoherent = 16;                       // cache policy: coherent at device scope (sc1)
 }  // namespace
 
 // MT: 16-row tiles of X; TN: 16-row weight tiles per wave; WR x WKS: wave
 // grid; GPW: groups per wave and chunk (chunk = GPW * WKS groups); Q: weight
 // ring slots (power of two).
-template <int MT, int TN, int WR, int WKS, int GPW, int Q, bool ASYM>
+template <int MT, int TN, int WR, int WKS, int GPW, int Q, bool ASYM, bool SPLIT>
 __global__ __launch_bounds__(WR * WKS * kWave) void gemm_batched_kernel(
     const uint16_t* __restrict__ X, int M, const uint32_t* __restrict__ packed,
     const uint16_t* __restrict__ scales, const int16_t* __restrict__ zeros,
-    uint16_t* __restrict__ Y, int N, int K, int rows_per_block) {
+    uint16_t* __restrict__ Y, int N, int K, int rows_per_block, int ksplit, int gps,
+    uint32_t* __restrict__ counters, float4_t* __restrict__ partials) {
     constexpr int NT = WR * WKS * kWave;
     constexpr int P = Q - 1;                          // groups in flight ahead of use
     constexpr int U = Q > GPW ? Q / GPW : 1;          // chunks per unrolled body
@@ -88,10 +101,15 @@ __global__ __launch_bounds__(WR * WKS * kWave) void gemm_batched_kernel(
     const int ws = wave / WR;
     const int l16 = lane & 15;
     const int j = lane >> 4;
-    const int r0 = blockIdx.x * rows_per_block;
+    // row block and K slice (groups [g_lo, g_lo + ngroups) of the row)
+    const int rb = SPLIT ? (int)(blockIdx.x / (unsigned)ksplit) : (int)blockIdx.x;
+    const int ks = SPLIT ? (int)(blockIdx.x - (unsigned)rb * (unsigned)ksplit) : 0;
+    const int r0 = rb * rows_per_block;
     const int nrows = min(N - r0, rows_per_block);    // > 0: the grid covers N exactly
     const int xrows = min(M, 16 * MT);
-    const int ngroups = K >> 7;
+    const int g_lo = SPLIT ? ks * gps : 0;
+    const int ngroups = SPLIT ? min(K >> 7, g_lo + gps) - g_lo : (K >> 7);   // > 0
+    const int k_lo = g_lo * kGroup, k_hi = k_lo + ngroups * kGroup;
     const int nchunks = (ngroups + GC - 1) / GC;
     const int xbuf = xrows * XSTRIDE;
     const int xtotal = xrows * CBLK;
@@ -132,8 +150,8 @@ __global__ __launch_bounds__(WR * WKS * kWave) void gemm_batched_kernel(
         for (int i = 0; i < XV; ++i) {
             const int e = threadIdx.x + i * NT;
             const int row = e / CBLK;
-            const int k = c * KC + (e % CBLK) * 8;
-            const uint32_t off = (live && e < xtotal && k < K)
+            const int k = k_lo + c * KC + (e % CBLK) * 8;
+            const uint32_t off = (live && e < xtotal && k < k_hi)
                                      ? ((uint32_t)row * (uint32_t)K + (uint32_t)k) * 2u
                                      : xbytes;
             xv[i] = __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0);
@@ -142,7 +160,8 @@ __global__ __launch_bounds__(WR * WKS * kWave) void gemm_batched_kernel(
         for (int i = 0; i < SV; ++i) {
             const int e = threadIdx.x + i * NT;
             const uint32_t off = (live && e < SBUF)
-                                     ? (uint32_t)(e / GC) * srow + (uint32_t)(c * GC + e % GC) * 2u
+                                     ? (uint32_t)(e / GC) * srow +
+                                           (uint32_t)(g_lo + c * GC + e % GC) * 2u
                                      : sbytes;
             sv[i] = __builtin_amdgcn_raw_buffer_load_b16(sr, off, 0, 0);
             zv[i] = ASYM ? __builtin_amdgcn_raw_buffer_load_b16(zr, off, 0, 0) : 0u;
@@ -172,8 +191,9 @@ __global__ __launch_bounds__(WR * WKS * kWave) void gemm_batched_kernel(
     };
     int lcc = 0, li = 0;                              // load cursor: chunk sequence, group in chunk
     auto load = [&](Slot& sl) {
-        const int g = chunk_of(lcc) * GC + ws + WKS * li;
-        const bool live = lcc < nchunks && g < ngroups;
+        const int gr = chunk_of(lcc) * GC + ws + WKS * li;    // group in the slice
+        const bool live = lcc < nchunks && gr < ngroups;
+        const int g = g_lo + gr;
         const __amdgpu_buffer_rsrc_t w = live ? wr_live : empty;
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) {
@@ -321,6 +341,50 @@ __global__ __launch_bounds__(WR * WKS * kWave) void gemm_batched_kernel(
                 for (int tn = 0; tn < TN; ++tn)
                     acc[mt][tn] += red[((((w - 1) * WR + wr) * MT + mt) * TN + tn) * kWave + lane];
     }
+    if constexpr (SPLIT) {
+        // partial tile of this slice -> workspace, in the lanes' own layout
+        // (the reducing block reads it back the same way)
+        __shared__ uint32_t last_flag;
+        constexpr int PT = WR * TN * MT * kWave;          // float4 per block partial
+        const __amdgpu_buffer_rsrc_t pr = buffer_rsrc(
+            partials + (size_t)rb * ksplit * PT, (uint64_t)ksplit * PT * sizeof(float4_t));
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const uint32_t off =
+                    (uint32_t)((ks * PT + ((wr * TN + tn) * MT + mt) * kWave + lane) * 16);
+                const v4u v = {__float_as_uint(acc[mt][tn][0]), __float_as_uint(acc[mt][tn][1]),
+                               __float_as_uint(acc[mt][tn][2]), __float_as_uint(acc[mt][tn][3])};
+                __builtin_amdgcn_raw_buffer_store_b128(v, pr, off, 0, kCoherent);
+            }
+        __builtin_amdgcn_s_waitcnt(0x0F70);               // vmcnt(0): stores complete
+        __syncthreads();                                  // every wave's stores are complete
+        if (threadIdx.x == 0)
+            last_flag = __hip_atomic_fetch_add(&counters[rb], 1u, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        if (last_flag != (uint32_t)(ksplit - 1)) return;
+        // the last slice of this row block: sum every slice in slice order
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acc[mt][tn] = (float4_t){0.f, 0.f, 0.f, 0.f};
+        for (int sl = 0; sl < ksplit; ++sl) {
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    const uint32_t off =
+                        (uint32_t)((sl * PT + ((wr * TN + tn) * MT + mt) * kWave + lane) * 16);
+                    const v4u v = __builtin_amdgcn_raw_buffer_load_b128(pr, off, 0, kCoherent);
+                    acc[mt][tn] += (float4_t){__uint_as_float(v.x), __uint_as_float(v.y),
+                                              __uint_as_float(v.z), __uint_as_float(v.w)};
+                }
+        }
+        if (threadIdx.x == 0)
+            __hip_atomic_store(&counters[rb], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 #pragma unroll
     for (int tn = 0; tn < TN; ++tn) {
         const int nl = 16 * (wr + WR * tn) + l16;
@@ -335,28 +399,38 @@ __global__ __launch_bounds__(WR * WKS * kWave) void gemm_batched_kernel(
     }
 }
 
-template <int MT, int TN, int WR, int WKS, int GPW, int Q, bool ASYM>
+namespace {
+
+template <int MT, int TN, int WR, int WKS, int GPW, int Q, bool ASYM, bool SPLIT = false>
 hipError_t launch_batched_t(const uint16_t* X, int64_t M, const uint32_t* packed,
                             const uint16_t* scales, const int16_t* zeros, int64_t N, int64_t K,
-                            uint16_t* Y, hipStream_t stream, int64_t rows_per_block) {
+                            uint16_t* Y, hipStream_t stream, int64_t rows_per_block,
+                            const BatchedSplit* split = nullptr) {
     constexpr int NT = WR * WKS * kWave;
     constexpr int64_t KC = (int64_t)GPW * WKS * kGroup;
     const int64_t xrows = M < 16 * MT ? M : 16 * MT;
     if (rows_per_block > 16 * WR * TN || M > 16 * MT) return hipErrorInvalidValue;
+    if (SPLIT && (split == nullptr || split->rows_per_block != rows_per_block ||
+                  split->tile_rows != 16 * WR * TN || split->tile_m != 16 * MT))
+        return hipErrorInvalidValue;
     const size_t x_lds = (size_t)2 * xrows * (KC / 8 + 1) * 16 +
                          (size_t)(ASYM ? 2 : 1) * 2 * (16 * WR * TN) * (KC / kGroup) * 2;
     const size_t red_lds = (size_t)(WKS - 1) * WR * MT * TN * kWave * sizeof(float4_t);
     const size_t lds = x_lds > red_lds ? x_lds : red_lds;
+    auto kern = gemm_batched_kernel<MT, TN, WR, WKS, GPW, Q, ASYM, SPLIT>;
     if (lds > 64 * 1024) {
-        const hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void*>(gemm_batched_kernel<MT, TN, WR, WKS, GPW, Q, ASYM>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 (int)lds);
         if (e != hipSuccess) return e;
     }
-    const int64_t blocks = (N + rows_per_block - 1) / rows_per_block;
-    hipLaunchKernelGGL((gemm_batched_kernel<MT, TN, WR, WKS, GPW, Q, ASYM>),
-                       dim3((unsigned)blocks), dim3(NT), lds, stream, X, (int)M, packed, scales,
-                       zeros, Y, (int)N, (int)K, (int)rows_per_block);
+    const int64_t row_blocks = (N + rows_per_block - 1) / rows_per_block;
+    const int ksplit = SPLIT ? split->ksplit : 1;
+    const int gps = SPLIT ? split->groups_per_slice : 0;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(row_blocks * ksplit)), dim3(NT), lds, stream, X,
+                       (int)M, packed, scales, zeros, Y, (int)N, (int)K, (int)rows_per_block,
+                       ksplit, gps, SPLIT ? split->counters : nullptr,
+                       SPLIT ? reinterpret_cast<float4_t*>(split->partials) : nullptr);
     return hipGetLastError();
 }
 
@@ -366,6 +440,26 @@ hipError_t launch_batched_t(const uint16_t* X, int64_t M, const uint32_t* packed
 // 16, 32): two 16-row tiles per wave with a 2 x 4 wave grid for 17..64 rows a
 // block, four tiles for more, eight waves over K for at most 16 rows (the
 // down projection); four ring slots, two for the widest tiles.
+template <int MT, bool ASYM, bool SPLIT = false>
+hipError_t launch_batched_rows(const uint16_t* X, int64_t M, const uint32_t* packed,
+                               const uint16_t* scales, const int16_t* zeros, int64_t N,
+                               int64_t K, uint16_t* Y, hipStream_t stream, int64_t rpb,
+                               const BatchedSplit* split = nullptr) {
+    const int64_t tiles = (rpb + 15) / 16;
+    constexpr int G = 16 / MT;                        // groups per chunk
+    if (tiles <= 1)
+        return launch_batched_t<MT, 1, 1, 8, G / 8, 4 / MT, ASYM, SPLIT>(
+            X, M, packed, scales, zeros, N, K, Y, stream, rpb, split);
+    if (tiles <= 2)
+        return launch_batched_t<MT, 2, 1, 8, G / 8, 4, ASYM, SPLIT>(
+            X, M, packed, scales, zeros, N, K, Y, stream, rpb, split);
+    if (tiles <= 4)
+        return launch_batched_t<MT, 2, 2, 4, G / 4, 4, ASYM, SPLIT>(
+            X, M, packed, scales, zeros, N, K, Y, stream, rpb, split);
+    return launch_batched_t<MT, 4, 2, 4, G / 4, 2, ASYM, SPLIT>(X, M, packed, scales, zeros, N,
+                                                                K, Y, stream, rpb, split);
+}
+
 template <int MT, bool ASYM>
 hipError_t launch_batched_m(const uint16_t* X, int64_t M, const uint32_t* packed,
                             const uint16_t* scales, const int16_t* zeros, int64_t N, int64_t K,
@@ -373,19 +467,68 @@ hipError_t launch_batched_m(const uint16_t* X, int64_t M, const uint32_t* packed
     // one block per compute unit, rows split evenly; at most 128 rows a block
     int64_t rpb = (N + num_cu - 1) / num_cu;
     if (rpb > 128) rpb = 128;
-    const int64_t tiles = (rpb + 15) / 16;
-    constexpr int G = 16 / MT;                        // groups per chunk
-    if (tiles <= 1)
-        return launch_batched_t<MT, 1, 1, 8, G / 8, 4 / MT, ASYM>(X, M, packed, scales, zeros, N,
-                                                                  K, Y, stream, rpb);
-    if (tiles <= 2)
-        return launch_batched_t<MT, 2, 1, 8, G / 8, 4, ASYM>(X, M, packed, scales, zeros, N, K,
-                                                             Y, stream, rpb);
-    if (tiles <= 4)
-        return launch_batched_t<MT, 2, 2, 4, G / 4, 4, ASYM>(X, M, packed, scales, zeros, N, K,
-                                                             Y, stream, rpb);
-    return launch_batched_t<MT, 4, 2, 4, G / 4, 2, ASYM>(X, M, packed, scales, zeros, N, K, Y,
-                                                         stream, rpb);
+    return launch_batched_rows<MT, ASYM>(X, M, packed, scales, zeros, N, K, Y, stream, rpb);
+}
+
+// The 16-row tiles a block of `rows` rows is launched with (the wave grid of
+// launch_batched_rows): 16, 32, 64 or 128 rows.
+int64_t batched_tile_rows(int64_t rows) {
+    const int64_t tiles = (rows + 15) / 16;
+    return tiles <= 1 ? 16 : tiles <= 2 ? 32 : tiles <= 4 ? 64 : 128;
+}
+
+}  // namespace
+
+BatchedSplit plan_batched_split(int64_t M, int64_t N, int64_t K, int num_cu, int64_t rows,
+                                int ksplit) {
+    BatchedSplit p{};
+    p.ksplit = 1;
+    const int64_t ngroups = K / kGroup;
+    if (M < 1 || M > kBatchedMaxM || N < 1 || ngroups < 2 || K > kBatchedMaxK) return p;
+    if (rows <= 0 || ksplit <= 0) {
+        // Measured on gfx950 (14336 x 4096 and 4096 x 14336, M = 8..32):
+        // split only rows shorter than the K they walk (N < 2K with at most
+        // N / CUs rows a block): 64-row blocks and as many K slices as keep
+        // one block per compute unit.
+        const int64_t per_cu = (N + num_cu - 1) / num_cu;
+        if (K < 2 * N || per_cu > 32) return p;
+        rows = 64;
+        const int64_t row_blocks = (N + rows - 1) / rows;
+        ksplit = (int)(num_cu / row_blocks);          // at most one block per CU
+    }
+    if (rows > 128) rows = 128;
+    if (ksplit > ngroups) ksplit = (int)ngroups;
+    const int64_t gps = (ngroups + ksplit - 1) / ksplit;
+    ksplit = (int)((ngroups + gps - 1) / gps);        // every slice holds a group
+    const int64_t row_blocks = (N + rows - 1) / rows;
+    if (ksplit < 2 || row_blocks > kBatchedSplitCounters) return p;
+    p.ksplit = ksplit;
+    p.groups_per_slice = (int)gps;
+    p.rows_per_block = (int)rows;
+    p.tile_rows = (int)batched_tile_rows(rows);
+    p.tile_m = M <= 16 ? 16 : 32;
+    // the counters always take the same first bytes of the workspace, so a
+    // workspace used for several shapes never has partials where another
+    // shape's counters are
+    p.counter_bytes = (size_t)kBatchedSplitCounters * 4;
+    p.workspace_bytes = p.counter_bytes +
+                        (size_t)row_blocks * ksplit * p.tile_rows * p.tile_m * sizeof(float);
+    return p;
+}
+
+hipError_t launch_gemm_batched_split(const uint16_t* X, int64_t M, const uint32_t* packed,
+                                     const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y,
+                                     hipStream_t stream, const BatchedSplit& plan,
+                                     void* workspace) {
+    if (plan.ksplit < 2) return hipErrorInvalidValue;
+    BatchedSplit p = plan;
+    p.counters = static_cast<uint32_t*>(workspace);
+    p.partials = static_cast<char*>(workspace) + plan.counter_bytes;
+    if (M <= 16)
+        return launch_batched_rows<1, false, true>(X, M, packed, scales, nullptr, N, K, Y, stream,
+                                                   p.rows_per_block, &p);
+    return launch_batched_rows<2, false, true>(X, M, packed, scales, nullptr, N, K, Y, stream,
+                                               p.rows_per_block, &p);
 }
 
 hipError_t launch_gemm_batched(const uint16_t* X, int64_t M, const uint32_t* packed,

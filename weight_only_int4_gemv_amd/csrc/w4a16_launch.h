@@ -70,6 +70,33 @@ hipError_t launch_gemm_batched_asym(const uint16_t* X, int64_t M, const uint32_t
                                     const uint16_t* scales, const int16_t* zeros, int64_t N,
                                     int64_t K, uint16_t* Y, hipStream_t stream, int num_cu);
 
+// Batched decode with K split over blocks (gemm_batched.hip): block (b, k)
+// owns rows_per_block rows and groups [k * groups_per_slice, ...) of K; the
+// fp32 partial tiles go to a caller workspace (counters, then partials) and
+// the last slice of each row block adds them in slice order.
+constexpr int64_t kBatchedSplitCounters = 1024;   // row-block counters at the workspace start
+struct BatchedSplit {
+    int ksplit;              // K slices (1: no split)
+    int groups_per_slice;
+    int rows_per_block;
+    int tile_rows;           // rows of the block's wave tiles (>= rows_per_block)
+    int tile_m;              // 16 or 32 rows of X per tile
+    size_t counter_bytes;    // kBatchedSplitCounters uint32, for every shape
+    size_t workspace_bytes;  // counters + row blocks * slices * tile_rows * tile_m * 4
+    uint32_t* counters;      // filled in by the launcher
+    void* partials;
+};
+// The split used for (M, N, K) on num_cu compute units (rows, ksplit > 0
+// force a shape, for measurements); ksplit == 1 when no split applies.
+BatchedSplit plan_batched_split(int64_t M, int64_t N, int64_t K, int num_cu, int64_t rows = 0,
+                                int ksplit = 0);
+// Requires plan.ksplit > 1 and a workspace of plan.workspace_bytes whose
+// counters are zero (every call leaves them zero).
+hipError_t launch_gemm_batched_split(const uint16_t* X, int64_t M, const uint32_t* packed,
+                                     const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y,
+                                     hipStream_t stream, const BatchedSplit& plan,
+                                     void* workspace);
+
 // MFMA path for few rows of X (gemm_skinny.hip): weights streamed once,
 // waves split K.  Requires K <= kSkinnyMaxK (32-bit buffer offsets).
 constexpr int64_t kSkinnyMaxK = (int64_t)1 << 24;

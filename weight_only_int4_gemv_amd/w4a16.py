@@ -63,6 +63,10 @@ def library() -> ctypes.CDLL:
         lib.w4a16_gemv.argtypes = [_p, _p, _p, _i64, _i64, _p, _p]
         lib.w4a16_gemm.argtypes = [_p, _i64, _p, _p, _i64, _i64, _p, _p]
         lib.w4a16_gemm_ex.argtypes = [_p, _i64, _p, _p, _i64, _i64, _p, ctypes.c_int, _p]
+        lib.w4a16_gemm_workspace_bytes.argtypes = [_i64, _i64, _i64]
+        lib.w4a16_gemm_workspace_bytes.restype = ctypes.c_size_t
+        lib.w4a16_gemm_ws.argtypes = [_p, _i64, _p, _p, _i64, _i64, _p, _p, ctypes.c_size_t, _p]
+        lib.w4a16_gemm_ws.restype = ctypes.c_int
         lib.w4a16_scales_bytes_g.argtypes = [_i64, _i64, _i64]
         lib.w4a16_scales_bytes_g.restype = ctypes.c_size_t
         lib.w4a16_quantize_g.argtypes = [_p, _i64, _i64, _i64, _p, _p, _p]
@@ -262,6 +266,39 @@ def gemm(X: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, algo=None,
         st = lib.w4a16_gemm_g(X.data_ptr(), M, packed.data_ptr(), scales.data_ptr(), N, K,
                               group, Y.data_ptr(), _stream())
     _check("w4a16_gemm", st)
+    return Y
+
+
+def gemm_workspace(M: int, N: int, K: int, device="cuda") -> torch.Tensor:
+    """A zeroed workspace for gemm_ws (uint8, at least 1 byte; the library
+    keeps it reusable across calls)."""
+    n = library().w4a16_gemm_workspace_bytes(M, N, K)
+    return torch.zeros(max(1, n), dtype=torch.uint8, device=device)
+
+
+def gemm_ws(X: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,
+            workspace: torch.Tensor, Y: torch.Tensor = None) -> torch.Tensor:
+    """w4a16_gemm_ws: gemm (automatic kernel choice, group 128) with K split
+    over blocks through `workspace` (from gemm_workspace) where the library
+    splits the shape."""
+    lib = library()
+    N, K, group = _weights(packed, scales)
+    if group != W4A16_GROUP:
+        raise ValueError("gemm_ws takes group %d weights" % W4A16_GROUP)
+    _need(X, "X", torch.float16, 2)
+    M = X.shape[0]
+    if X.shape[1] != K:
+        raise ValueError("X has %d columns, K = %d" % (X.shape[1], K))
+    _need(workspace, "workspace", torch.uint8, 1)
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float16, device=X.device)
+    _need(Y, "Y", torch.float16, 2)
+    if tuple(Y.shape) != (M, N):
+        raise ValueError("Y shape %s, want %s" % (tuple(Y.shape), (M, N)))
+    _check("w4a16_gemm_ws", lib.w4a16_gemm_ws(X.data_ptr(), M, packed.data_ptr(),
+                                              scales.data_ptr(), N, K, Y.data_ptr(),
+                                              workspace.data_ptr(), workspace.numel(),
+                                              _stream()))
     return Y
 
 
