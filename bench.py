@@ -69,6 +69,10 @@ def parse():
     p.add_argument("--no-shapes", action="store_true", help="skip per-shape timing")
     p.add_argument("--no-secondary", action="store_true",
                    help="skip the quantizer, batched-decode and prefill measurements")
+    p.add_argument("--secondary-only", default="",
+                   help="comma list of secondary rows (%s) to run alone, without the "
+                        "sweep (for profiling them); prints their JSON"
+                        % ",".join(SECONDARY_ROWS))
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="run one plain device copy of this many MiB first (calibrates "
                         "the FETCH_SIZE / WRITE_SIZE counters against known bytes)")
@@ -152,7 +156,11 @@ def weight_copies(p0, s0, min_bytes=600 << 20, extra=()):
                                  for _ in range(n - 1)]
 
 
-def secondary(torch, w4a16, inputs, dev, stream, main_workload="llama3-8b-sweep"):
+SECONDARY_ROWS = ["quantize", "batched", "prefill", "groups", "act_order", "asym", "q4_0",
+                  "sweep"]
+
+
+def secondary(torch, w4a16, inputs, dev, stream, main_workload="llama3-8b-sweep", rows=None):
     """Other rows of the path on their workload shapes: the quantizer (70B FFN
     matrix, larger than the Infinity Cache), batched decode M = 1..32 on the
     8B FFN shapes with both kernel families (locates the VALU/MFMA
@@ -162,6 +170,9 @@ def secondary(torch, w4a16, inputs, dev, stream, main_workload="llama3-8b-sweep"
     against the split layout at group 32.  Each figure is the mean of
     graph replays over enough weight copies to stream from HBM."""
     out = {}
+
+    def want(name):
+        return rows is None or name in rows
 
     def timed(seq_fn, reps=5):
         g = torch.cuda.CUDAGraph()
@@ -177,19 +188,21 @@ def secondary(torch, w4a16, inputs, dev, stream, main_workload="llama3-8b-sweep"
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1e3 / reps     # us per replay
 
-    # quantizer: 28672 x 8192 fp16 (470 MB in, 121 MB out)
-    K, N = 8192, 28672
-    W = torch.from_numpy(inputs.weight(N, K, seed=[5, 1, 0])).to(dev)
-    pq = torch.empty((N, K // 8), dtype=torch.int32, device=dev)
-    sq = torch.empty((N, K // 128), dtype=torch.float16, device=dev)
-    w4a16.quantize(W, pq, sq)
-    us = timed(lambda: w4a16.quantize(W, pq, sq))
-    qbytes = N * K * 2 + N * K // 2 + N * (K // 128) * 2
-    out["quantize"] = {"K": K, "N": N, "us": round(us, 2),
-                       "GB/s": round(qbytes / (us * 1e-6) / 1e9, 1),
-                       "frac_of_hbm_peak": round(qbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
-    del W
-    quantized = {(K, N): (pq, sq)}
+    quantized = {}
+    if want("quantize"):
+        # quantizer: 28672 x 8192 fp16 (470 MB in, 121 MB out)
+        K, N = 8192, 28672
+        W = torch.from_numpy(inputs.weight(N, K, seed=[5, 1, 0])).to(dev)
+        pq = torch.empty((N, K // 8), dtype=torch.int32, device=dev)
+        sq = torch.empty((N, K // 128), dtype=torch.float16, device=dev)
+        w4a16.quantize(W, pq, sq)
+        us = timed(lambda: w4a16.quantize(W, pq, sq))
+        qbytes = N * K * 2 + N * K // 2 + N * (K // 128) * 2
+        out["quantize"] = {"K": K, "N": N, "us": round(us, 2),
+                           "GB/s": round(qbytes / (us * 1e-6) / 1e9, 1),
+                           "frac_of_hbm_peak": round(qbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        del W
+        quantized[(K, N)] = (pq, sq)
 
     def weights_for(K, N):
         if (K, N) not in quantized:
@@ -198,163 +211,170 @@ def secondary(torch, w4a16, inputs, dev, stream, main_workload="llama3-8b-sweep"
             del Wd
         return quantized[(K, N)]
 
-    # batched decode on the 8B FFN shapes
-    batched = {}
-    for (K, N) in [(4096, 14336), (14336, 4096)]:
-        p0, s0 = weights_for(K, N)
-        copies = weight_copies(p0, s0)                              # >= 600 MB of weights
-        for M in [1, 2, 3, 4, 8, 16, 32]:
-            X = torch.from_numpy(inputs.activation(M, K, seed=[6, M, K])).to(dev)
-            Y = torch.empty((M, N), dtype=torch.float16, device=dev)
-            row = {}
-            for algo in ["valu", "mfma"]:
-                us = timed(lambda: [w4a16.gemm(X, p, s_, algo=algo, Y=Y) for p, s_ in copies]) \
-                    / len(copies)
-                b = gemv_bytes(N, K, M)
-                row[algo] = {"us": round(us, 3), "GB/s": round(b / (us * 1e-6) / 1e9, 1),
-                             "TFLOP/s": round(2 * M * N * K / (us * 1e-6) / 1e12, 2)}
-            row["auto_picks"] = "valu" if M <= w4a16.valu_max_m() else "mfma"
-            # K split over blocks through a workspace (w4a16_gemm_ws), where
-            # the library splits the shape
-            if w4a16.library().w4a16_gemm_workspace_bytes(M, N, K) > 0:
-                ws = w4a16.gemm_workspace(M, N, K, device=dev)
-                us = timed(lambda: [w4a16.gemm_ws(X, p, s_, ws, Y=Y) for p, s_ in copies]) \
-                    / len(copies)
-                b = gemv_bytes(N, K, M)
-                row["mfma_split_k"] = {"us": round(us, 3), "GB/s": round(b / (us * 1e-6) / 1e9, 1),
-                                       "TFLOP/s": round(2 * M * N * K / (us * 1e-6) / 1e12, 2),
-                                       "workspace_bytes": int(ws.numel())}
-            batched["%dx%d M=%d" % (K, N, M)] = row
-        del copies
-    out["batched_decode"] = batched
+    if want("batched"):
+        # batched decode on the 8B FFN shapes
+        batched = {}
+        for (K, N) in [(4096, 14336), (14336, 4096)]:
+            p0, s0 = weights_for(K, N)
+            copies = weight_copies(p0, s0)                              # >= 600 MB of weights
+            for M in [1, 2, 3, 4, 8, 16, 32]:
+                X = torch.from_numpy(inputs.activation(M, K, seed=[6, M, K])).to(dev)
+                Y = torch.empty((M, N), dtype=torch.float16, device=dev)
+                row = {}
+                for algo in ["valu", "mfma"]:
+                    us = timed(lambda: [w4a16.gemm(X, p, s_, algo=algo, Y=Y) for p, s_ in copies]) \
+                        / len(copies)
+                    b = gemv_bytes(N, K, M)
+                    row[algo] = {"us": round(us, 3), "GB/s": round(b / (us * 1e-6) / 1e9, 1),
+                                 "TFLOP/s": round(2 * M * N * K / (us * 1e-6) / 1e12, 2)}
+                row["auto_picks"] = "valu" if M <= w4a16.valu_max_m() else "mfma"
+                # K split over blocks through a workspace (w4a16_gemm_ws), where
+                # the library splits the shape
+                if w4a16.library().w4a16_gemm_workspace_bytes(M, N, K) > 0:
+                    ws = w4a16.gemm_workspace(M, N, K, device=dev)
+                    us = timed(lambda: [w4a16.gemm_ws(X, p, s_, ws, Y=Y) for p, s_ in copies]) \
+                        / len(copies)
+                    b = gemv_bytes(N, K, M)
+                    row["mfma_split_k"] = {"us": round(us, 3), "GB/s": round(b / (us * 1e-6) / 1e9, 1),
+                                           "TFLOP/s": round(2 * M * N * K / (us * 1e-6) / 1e12, 2),
+                                           "workspace_bytes": int(ws.numel())}
+                batched["%dx%d M=%d" % (K, N, M)] = row
+            del copies
+        out["batched_decode"] = batched
 
-    # prefill, M = 512
-    prefill = {}
-    for (K, N) in [(4096, 14336), (14336, 4096), (8192, 28672)]:
-        p0, s0 = weights_for(K, N)
-        copies = weight_copies(p0, s0)                              # >= 600 MB of weights
-        X = torch.from_numpy(inputs.activation(512, K, seed=[7, K])).to(dev)
-        Y = torch.empty((512, N), dtype=torch.float16, device=dev)
-        us = timed(lambda: [w4a16.gemm(X, p, s_, Y=Y) for p, s_ in copies]) / len(copies)
-        tf = 2 * 512 * N * K / (us * 1e-6) / 1e12
-        prefill["%dx%d M=512" % (K, N)] = {"us": round(us, 2), "TFLOP/s": round(tf, 1),
-                                           "frac_of_mfma_f16_peak":
-                                               round(tf / MFMA_F16_PEAK_TFLOPS, 4)}
-        del copies
-    out["prefill"] = prefill
+    if want("prefill"):
+        # prefill, M = 512
+        prefill = {}
+        for (K, N) in [(4096, 14336), (14336, 4096), (8192, 28672)]:
+            p0, s0 = weights_for(K, N)
+            copies = weight_copies(p0, s0)                              # >= 600 MB of weights
+            X = torch.from_numpy(inputs.activation(512, K, seed=[7, K])).to(dev)
+            Y = torch.empty((512, N), dtype=torch.float16, device=dev)
+            us = timed(lambda: [w4a16.gemm(X, p, s_, Y=Y) for p, s_ in copies]) / len(copies)
+            tf = 2 * 512 * N * K / (us * 1e-6) / 1e12
+            prefill["%dx%d M=512" % (K, N)] = {"us": round(us, 2), "TFLOP/s": round(tf, 1),
+                                               "frac_of_mfma_f16_peak":
+                                                   round(tf / MFMA_F16_PEAK_TFLOPS, 4)}
+            del copies
+        out["prefill"] = prefill
 
-    # group size as a parameter: decode GEMV (M = 1) on the 8B gate shape and
-    # the quantizer, per group size (scale bytes N*K*2/group)
-    groups = {}
-    K, N = 4096, 14336
-    Wg = torch.from_numpy(inputs.weight(N, K, seed=[8, K, N])).to(dev)
-    x = torch.from_numpy(inputs.activation(1, K, seed=[8, 1])).to(dev)[0]
-    y = torch.empty((N,), dtype=torch.float16, device=dev)
-    for group in (32, 64, 128, 256):
-        pg, sg = w4a16.quantize(Wg, group=group)
-        qus = timed(lambda: w4a16.quantize(Wg, pg, sg, group=group))
-        copies = weight_copies(pg, sg)
-        us = timed(lambda: [w4a16.gemv(x, p, s_, y=y) for p, s_ in copies]) / len(copies)
-        b = N * K // 2 + N * (K // group) * 2 + 2 * K + 2 * N
-        qb = N * K * 2 + N * K // 2 + N * (K // group) * 2
-        groups["group %d" % group] = {
-            "gemv_us": round(us, 3), "gemv_GB/s": round(b / (us * 1e-6) / 1e9, 1),
-            "gemv_frac_of_hbm_peak": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-            "quantize_us": round(qus, 2), "quantize_GB/s": round(qb / (qus * 1e-6) / 1e9, 1)}
-        del copies
-    out["group_sizes_%dx%d" % (K, N)] = groups
-    del Wg
-
-    # act order: M = 1 GEMV with the activation gather, against the plain GEMV
-    act = {}
-    for (K, N) in [(4096, 14336), (14336, 4096)]:
-        p0, s0 = weights_for(K, N)
-        copies = weight_copies(p0, s0)
-        x = torch.from_numpy(inputs.activation(1, K, seed=[9, K])).to(dev)[0]
+    if want("groups"):
+        # group size as a parameter: decode GEMV (M = 1) on the 8B gate shape and
+        # the quantizer, per group size (scale bytes N*K*2/group)
+        groups = {}
+        K, N = 4096, 14336
+        Wg = torch.from_numpy(inputs.weight(N, K, seed=[8, K, N])).to(dev)
+        x = torch.from_numpy(inputs.activation(1, K, seed=[8, 1])).to(dev)[0]
         y = torch.empty((N,), dtype=torch.float16, device=dev)
-        perm = torch.randperm(K, generator=torch.Generator().manual_seed(K)).to(
-            device=dev, dtype=torch.int32)
-        plain = timed(lambda: [w4a16.gemv(x, p, s_, y=y) for p, s_ in copies]) / len(copies)
-        gather = timed(lambda: [w4a16.gemv(x, p, s_, y=y, perm=perm) for p, s_ in copies]) \
-            / len(copies)
-        b = gemv_bytes(N, K) + 4 * K
-        act["%dx%d" % (K, N)] = {"plain_us": round(plain, 3), "perm_us": round(gather, 3),
-                                 "perm_GB/s": round(b / (gather * 1e-6) / 1e9, 1)}
-        del copies
-    out["act_order_m1"] = act
+        for group in (32, 64, 128, 256):
+            pg, sg = w4a16.quantize(Wg, group=group)
+            qus = timed(lambda: w4a16.quantize(Wg, pg, sg, group=group))
+            copies = weight_copies(pg, sg)
+            us = timed(lambda: [w4a16.gemv(x, p, s_, y=y) for p, s_ in copies]) / len(copies)
+            b = N * K // 2 + N * (K // group) * 2 + 2 * K + 2 * N
+            qb = N * K * 2 + N * K // 2 + N * (K // group) * 2
+            groups["group %d" % group] = {
+                "gemv_us": round(us, 3), "gemv_GB/s": round(b / (us * 1e-6) / 1e9, 1),
+                "gemv_frac_of_hbm_peak": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "quantize_us": round(qus, 2), "quantize_GB/s": round(qb / (qus * 1e-6) / 1e9, 1)}
+            del copies
+        out["group_sizes_%dx%d" % (K, N)] = groups
+        del Wg
 
-    # asymmetric INT4: M = 1 GEMV (zero points streamed beside the scales)
-    # and the quantizer, against the symmetric GEMV on the same shape
-    asym = {}
-    for (K, N) in [(14336, 4096), (4096, 14336)]:
-        Wd = torch.from_numpy(inputs.weight_skewed(N, K, seed=[10, K, N])).to(dev)
-        pa, sa, za = w4a16.quantize_asym(Wd)
-        qus = timed(lambda: w4a16.quantize_asym(Wd, pa, sa, za))
-        copies = weight_copies(pa, sa, extra=(za,))
-        x = torch.from_numpy(inputs.activation(1, K, seed=[10, K])).to(dev)[0]
-        y = torch.empty((N,), dtype=torch.float16, device=dev)
-        us = timed(lambda: [w4a16.gemv_asym(x, p, s_, z, y=y) for p, s_, z in copies]) \
-            / len(copies)
-        p0, s0 = weights_for(K, N)
-        sym = weight_copies(p0, s0)
-        plain = timed(lambda: [w4a16.gemv(x, p, s_, y=y) for p, s_ in sym]) / len(sym)
-        b = gemv_bytes(N, K) + N * (K // 128) * 2
-        qb = N * K * 2 + N * K // 2 + 2 * N * (K // 128) * 2
-        row = {
-            "gemv_us": round(us, 3), "gemv_GB/s": round(b / (us * 1e-6) / 1e9, 1),
-            "gemv_frac_of_hbm_peak": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-            "symmetric_gemv_us": round(plain, 3),
-            "quantize_us": round(qus, 2), "quantize_GB/s": round(qb / (qus * 1e-6) / 1e9, 1)}
-        # batched decode and prefill with asymmetric weights (matrix cores)
-        for M in (16, 512):
-            X = torch.from_numpy(inputs.activation(M, K, seed=[10, M, K])).to(dev)
-            Y = torch.empty((M, N), dtype=torch.float16, device=dev)
-            few = copies
-            a_us = timed(lambda: [w4a16.gemm_asym(X, p, s_, z, Y=Y) for p, s_, z in few]) \
-                / len(few)
-            fews = sym
-            s_us = timed(lambda: [w4a16.gemm(X, p, s_, Y=Y) for p, s_ in fews]) / len(fews)
-            row["M=%d_us" % M] = round(a_us, 2)
-            row["M=%d_symmetric_us" % M] = round(s_us, 2)
-            row["M=%d_TFLOP/s" % M] = round(2 * M * N * K / (a_us * 1e-6) / 1e12, 1)
-        asym["%dx%d" % (K, N)] = row
-        del copies, sym, Wd
-    out["asymmetric_m1"] = asym
+    if want("act_order"):
+        # act order: M = 1 GEMV with the activation gather, against the plain GEMV
+        act = {}
+        for (K, N) in [(4096, 14336), (14336, 4096)]:
+            p0, s0 = weights_for(K, N)
+            copies = weight_copies(p0, s0)
+            x = torch.from_numpy(inputs.activation(1, K, seed=[9, K])).to(dev)[0]
+            y = torch.empty((N,), dtype=torch.float16, device=dev)
+            perm = torch.randperm(K, generator=torch.Generator().manual_seed(K)).to(
+                device=dev, dtype=torch.int32)
+            plain = timed(lambda: [w4a16.gemv(x, p, s_, y=y) for p, s_ in copies]) / len(copies)
+            gather = timed(lambda: [w4a16.gemv(x, p, s_, y=y, perm=perm) for p, s_ in copies]) \
+                / len(copies)
+            b = gemv_bytes(N, K) + 4 * K
+            act["%dx%d" % (K, N)] = {"plain_us": round(plain, 3), "perm_us": round(gather, 3),
+                                     "perm_GB/s": round(b / (gather * 1e-6) / 1e9, 1)}
+            del copies
+        out["act_order_m1"] = act
 
-    # Q4_0 blocks (scale in front of each 32-element block) against the split
-    # layout at the same information content (group 32): M = 1 GEMV and the
-    # quantizer
-    q40 = {}
-    for (K, N) in [(4096, 14336), (14336, 4096)]:
-        Wd = torch.from_numpy(inputs.weight(N, K, seed=[11, K, N])).to(dev)
-        bq = w4a16.quantize_q4_0(Wd)
-        qus = timed(lambda: w4a16.quantize_q4_0(Wd, bq))
-        copies = [bq]
-        for _ in range(max(1, -(-(600 << 20) // bq.numel()) - 1)):
-            c = w4a16.q4_0_blocks(N, K, device=dev)
-            c.copy_(bq)
-            copies.append(c)
-        x = torch.from_numpy(inputs.activation(1, K, seed=[11, K])).to(dev)[0]
-        y = torch.empty((N,), dtype=torch.float16, device=dev)
-        us = timed(lambda: [w4a16.gemv_q4_0(x, b_, y=y) for b_ in copies]) / len(copies)
-        pg, sg = w4a16.quantize(Wd, group=32)
-        split = weight_copies(pg, sg)
-        sus = timed(lambda: [w4a16.gemv(x, p, s_, y=y) for p, s_ in split]) / len(split)
-        b = N * (K // 32) * 18 + 2 * K + 2 * N
-        qb = N * K * 2 + N * (K // 32) * 18
-        q40["%dx%d" % (K, N)] = {
-            "gemv_us": round(us, 3), "gemv_GB/s": round(b / (us * 1e-6) / 1e9, 1),
-            "gemv_frac_of_hbm_peak": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-            "split_group32_gemv_us": round(sus, 3),
-            "quantize_us": round(qus, 2), "quantize_GB/s": round(qb / (qus * 1e-6) / 1e9, 1)}
-        del copies, split, Wd
-    out["q4_0_m1"] = q40
-    quantized.clear()
+    if want("asym"):
+        # asymmetric INT4: M = 1 GEMV (zero points streamed beside the scales)
+        # and the quantizer, against the symmetric GEMV on the same shape
+        asym = {}
+        for (K, N) in [(14336, 4096), (4096, 14336)]:
+            Wd = torch.from_numpy(inputs.weight_skewed(N, K, seed=[10, K, N])).to(dev)
+            pa, sa, za = w4a16.quantize_asym(Wd)
+            qus = timed(lambda: w4a16.quantize_asym(Wd, pa, sa, za))
+            copies = weight_copies(pa, sa, extra=(za,))
+            x = torch.from_numpy(inputs.activation(1, K, seed=[10, K])).to(dev)[0]
+            y = torch.empty((N,), dtype=torch.float16, device=dev)
+            us = timed(lambda: [w4a16.gemv_asym(x, p, s_, z, y=y) for p, s_, z in copies]) \
+                / len(copies)
+            p0, s0 = weights_for(K, N)
+            sym = weight_copies(p0, s0)
+            plain = timed(lambda: [w4a16.gemv(x, p, s_, y=y) for p, s_ in sym]) / len(sym)
+            b = gemv_bytes(N, K) + N * (K // 128) * 2
+            qb = N * K * 2 + N * K // 2 + 2 * N * (K // 128) * 2
+            row = {
+                "gemv_us": round(us, 3), "gemv_GB/s": round(b / (us * 1e-6) / 1e9, 1),
+                "gemv_frac_of_hbm_peak": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "symmetric_gemv_us": round(plain, 3),
+                "quantize_us": round(qus, 2), "quantize_GB/s": round(qb / (qus * 1e-6) / 1e9, 1)}
+            # batched decode and prefill with asymmetric weights (matrix cores)
+            for M in (16, 512):
+                X = torch.from_numpy(inputs.activation(M, K, seed=[10, M, K])).to(dev)
+                Y = torch.empty((M, N), dtype=torch.float16, device=dev)
+                few = copies
+                a_us = timed(lambda: [w4a16.gemm_asym(X, p, s_, z, Y=Y) for p, s_, z in few]) \
+                    / len(few)
+                fews = sym
+                s_us = timed(lambda: [w4a16.gemm(X, p, s_, Y=Y) for p, s_ in fews]) / len(fews)
+                row["M=%d_us" % M] = round(a_us, 2)
+                row["M=%d_symmetric_us" % M] = round(s_us, 2)
+                row["M=%d_TFLOP/s" % M] = round(2 * M * N * K / (a_us * 1e-6) / 1e12, 1)
+            asym["%dx%d" % (K, N)] = row
+            del copies, sym, Wd
+        out["asymmetric_m1"] = asym
 
-    # the other model's decode weight sweep (Qwen-2.5-7B beside LLaMA-3-8B)
-    other = "qwen2.5-7b-sweep" if main_workload == "llama3-8b-sweep" else "llama3-8b-sweep"
-    out["sweep_" + other] = sweep_row(torch, w4a16, inputs, dev, other,
-                                      3 if other.startswith("qwen") else 2)
+    if want("q4_0"):
+        # Q4_0 blocks (scale in front of each 32-element block) against the split
+        # layout at the same information content (group 32): M = 1 GEMV and the
+        # quantizer
+        q40 = {}
+        for (K, N) in [(4096, 14336), (14336, 4096)]:
+            Wd = torch.from_numpy(inputs.weight(N, K, seed=[11, K, N])).to(dev)
+            bq = w4a16.quantize_q4_0(Wd)
+            qus = timed(lambda: w4a16.quantize_q4_0(Wd, bq))
+            copies = [bq]
+            for _ in range(max(1, -(-(600 << 20) // bq.numel()) - 1)):
+                c = w4a16.q4_0_blocks(N, K, device=dev)
+                c.copy_(bq)
+                copies.append(c)
+            x = torch.from_numpy(inputs.activation(1, K, seed=[11, K])).to(dev)[0]
+            y = torch.empty((N,), dtype=torch.float16, device=dev)
+            us = timed(lambda: [w4a16.gemv_q4_0(x, b_, y=y) for b_ in copies]) / len(copies)
+            pg, sg = w4a16.quantize(Wd, group=32)
+            split = weight_copies(pg, sg)
+            sus = timed(lambda: [w4a16.gemv(x, p, s_, y=y) for p, s_ in split]) / len(split)
+            b = N * (K // 32) * 18 + 2 * K + 2 * N
+            qb = N * K * 2 + N * (K // 32) * 18
+            q40["%dx%d" % (K, N)] = {
+                "gemv_us": round(us, 3), "gemv_GB/s": round(b / (us * 1e-6) / 1e9, 1),
+                "gemv_frac_of_hbm_peak": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "split_group32_gemv_us": round(sus, 3),
+                "quantize_us": round(qus, 2), "quantize_GB/s": round(qb / (qus * 1e-6) / 1e9, 1)}
+            del copies, split, Wd
+        out["q4_0_m1"] = q40
+        quantized.clear()
+
+    if want("sweep"):
+        # the other model's decode weight sweep (Qwen-2.5-7B beside LLaMA-3-8B)
+        other = "qwen2.5-7b-sweep" if main_workload == "llama3-8b-sweep" else "llama3-8b-sweep"
+        out["sweep_" + other] = sweep_row(torch, w4a16, inputs, dev, other,
+                                          3 if other.startswith("qwen") else 2)
     return out
 
 
@@ -453,6 +473,18 @@ def main() -> int:
         print("[copy-probe] one copy of %d bytes (read) + %d bytes (write)"
               % (src.numel() * 4, dst.numel() * 4), file=sys.stderr, flush=True)
         del src, dst
+
+    if args.secondary_only:
+        rows = [r for r in args.secondary_only.split(",") if r]
+        unknown = sorted(set(rows) - set(SECONDARY_ROWS))
+        if unknown:
+            print("unknown secondary rows: %s (choose from %s)" % (unknown, SECONDARY_ROWS),
+                  file=sys.stderr)
+            return 2
+        sec = secondary(torch, w4a16, inputs, dev, torch.cuda.current_stream(), args.workload,
+                        rows=rows)
+        print(json.dumps({"secondary_only": rows, "secondary": sec}), flush=True)
+        return 0
 
     shape_attr, layers_attr = WORKLOADS[args.workload]
     shapes = getattr(inputs, shape_attr)
