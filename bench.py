@@ -266,14 +266,16 @@ def secondary(torch, w4a16, inputs, dev, stream, main_workload="llama3-8b-sweep"
         Wg = torch.from_numpy(inputs.weight(N, K, seed=[8, K, N])).to(dev)
         x = torch.from_numpy(inputs.activation(1, K, seed=[8, 1])).to(dev)[0]
         y = torch.empty((N,), dtype=torch.float16, device=dev)
-        for group in (32, 64, 128, 256):
+        for group in (32, 64, 128, 256, w4a16.PER_CHANNEL):
             pg, sg = w4a16.quantize(Wg, group=group)
             qus = timed(lambda: w4a16.quantize(Wg, pg, sg, group=group))
             copies = weight_copies(pg, sg)
             us = timed(lambda: [w4a16.gemv(x, p, s_, y=y) for p, s_ in copies]) / len(copies)
-            b = N * K // 2 + N * (K // group) * 2 + 2 * K + 2 * N
-            qb = N * K * 2 + N * K // 2 + N * (K // group) * 2
-            groups["group %d" % group] = {
+            ng = w4a16.scales_per_row(K, group)
+            b = N * K // 2 + N * ng * 2 + 2 * K + 2 * N
+            qb = N * K * 2 + N * K // 2 + N * ng * 2
+            label = "per channel" if group == w4a16.PER_CHANNEL else "group %d" % group
+            groups[label] = {
                 "gemv_us": round(us, 3), "gemv_GB/s": round(b / (us * 1e-6) / 1e9, 1),
                 "gemv_frac_of_hbm_peak": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                 "quantize_us": round(qus, 2), "quantize_GB/s": round(qb / (qus * 1e-6) / 1e9, 1)}

@@ -157,17 +157,20 @@ int w4a16_gemm_ws(const uint16_t* X, int64_t M, const uint32_t* packed, const ui
                   void* stream);
 
 /* ---- Group size as a parameter ([QUANT] sub-section 3 granularity table:
- * group 128 is the default, group 32 for outlier-sensitive layers; [QUANT]
- * GPTQ section, group_size table: 256, 128, 64 and 32 trade scale storage,
- * 1.6 % to 12.5 %, against accuracy).  Same quantizer, layout and linear
- * layer as above with `group` elements per scale along K:
+ * group 128 is the default, group 32 for outlier-sensitive layers, per
+ * channel one scale per output row; [QUANT] GPTQ section, group_size table:
+ * 256, 128, 64 and 32 trade scale storage, 1.6 % to 12.5 %, against
+ * accuracy, and -1 is per channel).  Same quantizer, layout and linear layer
+ * as above with `group` elements per scale along K:
  *     scales[n*(K/group) + g] = fp16 bits of s[n][g],  g = k / group
  *     Y[m,n] = sum_k X[m,k] * s[n,k/group] * q[n,k]
- * group must be 32, 64, 128 or 256 (else W4A16_ERR_INVALID_ARG) and divide
- * K (else W4A16_ERR_SHAPE); K % 128 == 0 as everywhere.  group == 128 gives
- * exactly the functions above.  For other groups the linear layer runs on the
- * VALU path for every M (the matrix-core kernels read one scale per 128
- * elements).  Scales bytes: N*(K/group)*2 (0 for bad arguments). */
+ * group must be 32, 64, 128, 256 or W4A16_PER_CHANNEL (else
+ * W4A16_ERR_INVALID_ARG) and divide K (else W4A16_ERR_SHAPE); K % 128 == 0
+ * as everywhere.  W4A16_PER_CHANNEL is the group of the whole row (K
+ * elements): one scale per row, scales[n], absmax over the row.  group ==
+ * 128 gives exactly the functions above.  Scales bytes: N*(K/group)*2, N*2
+ * per channel (0 for bad arguments). */
+#define W4A16_PER_CHANNEL (-1)
 size_t w4a16_scales_bytes_g(int64_t N, int64_t K, int64_t group);
 int w4a16_quantize_g(const uint16_t* W, int64_t N, int64_t K, int64_t group,
                      uint32_t* packed, uint16_t* scales, void* stream);
@@ -200,7 +203,8 @@ int w4a16_gemm_perm(const uint16_t* X, int64_t M, const int32_t* perm, const uin
  * (max - min) / 15, zero point z = -round(min / s), codes clamp(round(w / s)
  * + z, 0, 15), INT4 range [0, 15]; the same section's guidance puts skewed
  * weight distributions, e.g. the FFN down projection, on this form).
- * Per group of `group` elements along K (32, 64, 128 or 256):
+ * Per group of `group` elements along K (32, 64, 128, 256, or the whole row
+ * with W4A16_PER_CHANNEL):
  *     s    = fp16 RNE of (max - min) / 15 (exact max - min)
  *     z    = -RNE(min / s), an integer, against the stored fp16 s
  *     q    = clamp(RNE(w / s) + z, 0, 15), stored as the nibble itself

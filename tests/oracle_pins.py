@@ -366,6 +366,87 @@ def pin_group_sizes(o) -> list:
     return fails
 
 
+def pin_per_channel(o) -> list:
+    """Per-channel scales ([QUANT] sub-section 3 granularity table, per
+    channel: one scale per output row; GPTQ group_size -1): the group is the
+    whole row of K.  Symmetric: every scale the exact RNE(row absmax / 7), a
+    row whose only large value is one outlier takes its scale from it, every
+    code the brute-force nearest code against the row's scale, the
+    dequantizer s[n] * q, tiny products equal to the exact rational sums, and
+    2 bytes of scale per row.  Asymmetric: the scale the exact RNE((row max -
+    row min) / 15), z the exact rational RNE(-min / s), every code the
+    brute-force nearest level."""
+    fails = []
+    N, K = 10, 1152
+    W = inputs.weight(N, K, seed=[93, 0, 0])
+    W[0] = np.float16(0)                                 # all-zero row: s = 0
+    W[1] *= np.float16(1e-3)                              # small-scale row
+    W[2, 700] = np.float16(3.5)                           # one outlier sets the row's scale
+    packed, scales = o.quantize(W, group=K)
+    if scales.shape != (N, 1):
+        return ["per channel: scales shape %s" % (scales.shape,)]
+    a = np.abs(W.astype(np.float64)).max(axis=1)
+    want_s = np.array([exact_rne_f16(Fraction(float(v)) / 7) for v in a], dtype=np.uint16)
+    if not (scales[:, 0] == want_s).all():
+        fails.append("per channel: scales differ from exact RNE(row absmax / 7)")
+    if scales[2, 0] != exact_rne_f16(Fraction(3.5) / 7):
+        fails.append("per channel: the outlier row's scale is not 3.5 / 7")
+    codes = codes_from_bytes(packed)
+    want = brute_force_codes(W, scales, group=K)
+    if not (codes == want).all():
+        fails.append("per channel: %d codes differ from the nearest code" % (codes != want).sum())
+    deq = o.dequantize(packed, scales, group=K)
+    s64 = scales.view(np.float16).astype(np.float64)
+    if not (deq == s64 * codes).all():
+        fails.append("per channel: dequantize differs from s[n] * code")
+    if scales.nbytes != 2 * N:
+        fails.append("per channel: %d scale bytes for %d rows" % (scales.nbytes, N))
+    M, n_, k_ = 2, 3, 256
+    Wt, Xt = inputs.weight_and_activation(n_, k_, M, seed=[93, 1, 0])
+    pt, st = o.quantize(Wt, group=k_)
+    Y, _ = o.matmul(Xt, pt, st, group=k_)
+    ct = codes_from_bytes(pt)
+    sv = st.view(np.float16).astype(np.float64)
+    for m in range(M):
+        for n in range(n_):
+            terms = [Fraction(float(Xt[m, k])) * Fraction(float(sv[n, 0])) * int(ct[n, k])
+                     for k in range(k_)]
+            exact = sum(terms, Fraction(0))
+            bound = k_ * 2.0 ** -53 * float(sum((abs(t) for t in terms), Fraction(0)))
+            if abs(Fraction(Y[m, n]) - exact) > Fraction(bound):
+                fails.append("per channel: matmul (%d,%d) off the exact sum" % (m, n))
+    # asymmetric, one group per row
+    Wa = inputs.weight_skewed(6, 384, seed=[93, 2, 0])
+    Wa[0] = np.float16(0.75)                              # constant row: range 0
+    pa, sa, za = o.quantize_asym(Wa, group=384)
+    if sa.shape != (6, 1) or za.shape != (6, 1):
+        return fails + ["per channel asym: shapes %s %s" % (sa.shape, za.shape)]
+    nib = np.zeros(Wa.shape, dtype=np.int64)
+    for i in range(8):
+        nib[:, i::8] = (pa.astype(np.int64) >> (4 * i)) & 0xF
+    for n in range(Wa.shape[0]):
+        w = [Fraction(float(v)) for v in Wa[n]]
+        mx, mn = max(w), min(w)
+        s_bits = exact_rne_f16((mx - mn) / 15)
+        if sa[n, 0] != s_bits:
+            fails.append("per channel asym row %d: scale %#06x, want %#06x"
+                         % (n, sa[n, 0], s_bits))
+            continue
+        sf = Fraction(float(np.uint16(s_bits).view(np.float16)))
+        z = 0 if sf == 0 else -_rne_int(mn / sf)
+        if za[n, 0] != z:
+            fails.append("per channel asym row %d: zero %d, want %d" % (n, za[n, 0], z))
+            continue
+        for i in range(0, len(w), 7):                    # every 7th element, brute force
+            want_c = 0 if sf == 0 else min(range(16), key=lambda c: (abs(w[i] - sf * (c - z)),
+                                                                     (c - z) % 2))
+            if nib[n, i] != want_c:
+                fails.append("per channel asym (%d,%d): code %d, want %d"
+                             % (n, i, nib[n, i], want_c))
+                break
+    return fails
+
+
 def pin_act_order(o) -> list:
     """Act order ([QUANT] GPTQ section: columns quantized in the order perm,
     the weight kept in that order, activations permuted alike at inference).
@@ -586,7 +667,7 @@ def pin_q4_0(o) -> list:
 
 
 ALL_PINS = [pin_f16_codec, pin_scale_every_fp16, pin_hand_worked, pin_codes_nearest,
-            pin_invariants, pin_matmul_exact, pin_group_sizes, pin_act_order,
+            pin_invariants, pin_matmul_exact, pin_group_sizes, pin_per_channel, pin_act_order,
             pin_asymmetric, pin_q4_0]
 
 

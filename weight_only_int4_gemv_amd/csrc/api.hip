@@ -64,15 +64,25 @@ int check_sizes(int64_t M, int64_t N, int64_t K) {
 }
 
 // Group sizes the kernels take: 32, 64, 128 or 256 elements per scale, and
-// K a multiple of the group (K % 128 == 0 is required for every group).
+// K a multiple of the group (K % 128 == 0 is required for every group); or
+// W4A16_PER_CHANNEL, one scale per row.
 int check_group(int64_t group, int64_t K) {
+    if (group == W4A16_PER_CHANNEL) return W4A16_OK;
     if (group != 32 && group != 64 && group != 128 && group != 256) return W4A16_ERR_INVALID_ARG;
     if (K % group != 0) return W4A16_ERR_SHAPE;
     return W4A16_OK;
 }
 
 // log2(group / 32): the GEMV reads one scale per 2^gshift 32-code chunks.
-int group_shift(int64_t group) { return group == 32 ? 0 : group == 64 ? 1 : group == 128 ? 2 : 3; }
+int group_shift(int64_t group) {
+    if (group == W4A16_PER_CHANNEL) return w4a16::kPerChannelShift;
+    return group == 32 ? 0 : group == 64 ? 1 : group == 128 ? 2 : 3;
+}
+
+// Scales (and zero points) per row.
+int64_t groups_per_row(int64_t K, int64_t group) {
+    return group == W4A16_PER_CHANNEL ? (K > 0 ? 1 : 0) : K / group;
+}
 
 int status_of(hipError_t e) { return e == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH; }
 
@@ -99,7 +109,7 @@ int linear(const uint16_t* X, int64_t M, const uint32_t* packed, const uint16_t*
         !aligned(perm, 16) || !aligned(zeros, 2))
         return W4A16_ERR_MISALIGNED;
     const size_t y_bytes = (size_t)M * N * 2;
-    const size_t s_bytes = (size_t)N * (K / group) * 2;
+    const size_t s_bytes = (size_t)N * groups_per_row(K, group) * 2;
     if (overlap(Y, y_bytes, X, (size_t)M * K * 2) ||
         overlap(Y, y_bytes, packed, (size_t)N * K / 2) || overlap(Y, y_bytes, scales, s_bytes) ||
         (with_perm && overlap(Y, y_bytes, perm, (size_t)K * 4)) ||
@@ -137,7 +147,7 @@ int quantize(const uint16_t* W, int64_t N, int64_t K, int64_t group, uint32_t* p
         return W4A16_ERR_MISALIGNED;
     const size_t w_bytes = (size_t)N * K * 2;
     const size_t p_bytes = (size_t)N * K / 2;
-    const size_t s_bytes = (size_t)N * (K / group) * 2;
+    const size_t s_bytes = (size_t)N * groups_per_row(K, group) * 2;
     const size_t perm_bytes = with_perm ? (size_t)K * 4 : 0;
     const size_t z_bytes = asym ? s_bytes : 0;
     // outputs: packed, scales, zeros; inputs: W, perm
@@ -228,7 +238,7 @@ size_t w4a16_scales_bytes(int64_t N, int64_t K) {
 
 size_t w4a16_scales_bytes_g(int64_t N, int64_t K, int64_t group) {
     if (check_sizes(0, N, K) != W4A16_OK || check_group(group, K) != W4A16_OK) return 0;
-    return (size_t)N * (size_t)(K / group) * 2;
+    return (size_t)N * (size_t)groups_per_row(K, group) * 2;
 }
 
 int w4a16_quantize(const uint16_t* W, int64_t N, int64_t K, uint32_t* packed, uint16_t* scales,

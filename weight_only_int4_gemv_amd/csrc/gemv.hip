@@ -143,7 +143,7 @@ __global__ __launch_bounds__(WAVES * kWave) void gemv_kernel(
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const int nchunks = K >> 5;                   // 16-byte chunks per weight row
-    const int ngroups = K >> (5 + gshift);        // scales per weight row (2^gshift chunks each)
+    const int ngroups = scales_per_row(K, gshift);  // scales per weight row (2^gshift chunks each)
     const int row0 = (blockIdx.x * WAVES + wave) * R;
 
     size_t wrow[R], srow[R];
@@ -269,7 +269,7 @@ __global__ __launch_bounds__(WAVES * kWave) void gemv_persistent_kernel(
     const int my_rg = first_rg < total_rg ? (total_rg - 1 - first_rg) / stride_rg + 1 : 0;
     const int T = my_rg * nsteps;                          // this wave's iterations
     const uint32_t wrow_bytes = (uint32_t)K / 2;
-    const uint32_t srow_bytes = (uint32_t)(K >> (5 + gshift)) * 2;   // one scale per 2^gshift chunks
+    const uint32_t srow_bytes = (uint32_t)scales_per_row(K, gshift) * 2;  // one per 2^gshift chunks
     const CodeConsts kc = code_consts();
 
     // X blocks of this thread, loaded first (indices clamped into range).

@@ -60,9 +60,8 @@ __device__ __forceinline__ uint32_t group_max(uint32_t v) {
     return v;
 }
 
-// One lane's 8 elements of a group -> its packed word, and the group scale.
-template <int LG>
-__device__ __forceinline__ uint32_t quantize8(const uint4& v, uint16_t& s_bits) {
+// |w| of the 8 fp16 values of a lane, as the largest magnitude bit pattern.
+__device__ __forceinline__ uint32_t absmax8(const uint4& v) {
     uint32_t m = 0;
     m = max(m, v.x & 0x7FFFu);
     m = max(m, (v.x >> 16) & 0x7FFFu);
@@ -72,10 +71,27 @@ __device__ __forceinline__ uint32_t quantize8(const uint4& v, uint16_t& s_bits) 
     m = max(m, (v.z >> 16) & 0x7FFFu);
     m = max(m, v.w & 0x7FFFu);
     m = max(m, (v.w >> 16) & 0x7FFFu);
-    m = group_max<LG>(m);
+    return m;
+}
+
+// Scale bits of a group (or row) whose absolute maximum has bit pattern m.
+__device__ __forceinline__ uint16_t scale_of_absmax(uint32_t m) {
     const float a = f16_bits_to_f32((uint16_t)m);
     constexpr float kSeventh = 1.0f / 7.0f;   // 2^(4-1) - 1 = 7; fp32(1/7)
-    s_bits = f32_to_f16_bits(a * kSeventh);   // = fp16_rne(a / 7), see above
+    return f32_to_f16_bits(a * kSeventh);     // = fp16_rne(a / 7), see above
+}
+
+__device__ __forceinline__ uint32_t codes8(const uint4& v, uint16_t s_bits);
+
+// One lane's 8 elements of a group -> its packed word, and the group scale.
+template <int LG>
+__device__ __forceinline__ uint32_t quantize8(const uint4& v, uint16_t& s_bits) {
+    s_bits = scale_of_absmax(group_max<LG>(absmax8(v)));
+    return codes8(v, s_bits);
+}
+
+// The packed word of 8 elements against the scale with bits s_bits.
+__device__ __forceinline__ uint32_t codes8(const uint4& v, uint16_t s_bits) {
     const float s = f16_bits_to_f32(s_bits);
     if (s == 0.0f) return 0x88888888u;   // every code 0 (all lanes of the group alike)
     const uint32_t h[4] = {v.x, v.y, v.z, v.w};
@@ -144,30 +160,49 @@ __device__ __forceinline__ uint32_t f16_from_key(uint32_t k) {
 
 // One lane's 8 elements of a group -> its packed word (nibbles q in
 // [0, 15]), and the group's scale and zero point.
-template <int LG>
-__device__ __forceinline__ uint32_t quantize8_asym(const uint4& v, uint16_t& s_bits,
-                                                   int16_t& zero) {
+// Largest key and largest 0xFFFF - key of a lane's 8 values (the maximum
+// and, complemented, the minimum).
+__device__ __forceinline__ void minmax_keys8(const uint4& v, uint32_t& kmax, uint32_t& kmin_c) {
     const uint32_t h[8] = {v.x & 0xFFFFu, v.x >> 16, v.y & 0xFFFFu, v.y >> 16,
                            v.z & 0xFFFFu, v.z >> 16, v.w & 0xFFFFu, v.w >> 16};
-    uint32_t kmax = 0, kmin_c = 0;                      // max key, max of 0xFFFF - key
+    kmax = 0;
+    kmin_c = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const uint32_t key = f16_key(h[i]);
         kmax = max(kmax, key);
         kmin_c = max(kmin_c, 0xFFFFu - key);
     }
-    kmax = group_max<LG>(kmax);
-    kmin_c = group_max<LG>(kmin_c);
+}
+
+// Scale bits and zero point of a group (or row) from its reduced keys.
+__device__ __forceinline__ void asym_params(uint32_t kmax, uint32_t kmin_c, uint16_t& s_bits,
+                                            int16_t& zero) {
     const double mx = (double)f16_bits_to_f32((uint16_t)f16_from_key(kmax));
     const double mn = (double)f16_bits_to_f32((uint16_t)f16_from_key(0xFFFFu - kmin_c));
     s_bits = f16_rne_from_f64((mx - mn) / 15.0);         // 2^4 - 1 = 15
     const double s = (double)f16_bits_to_f32(s_bits);
-    if (s == 0.0) {
-        zero = 0;
-        return 0u;                                       // every code 0
-    }
-    const double z = -rint(mn / s);
-    zero = (int16_t)(int)z;
+    zero = s == 0.0 ? (int16_t)0 : (int16_t)(int)-rint(mn / s);
+}
+
+__device__ __forceinline__ uint32_t codes8_asym(const uint4& v, uint16_t s_bits, int16_t zero);
+
+template <int LG>
+__device__ __forceinline__ uint32_t quantize8_asym(const uint4& v, uint16_t& s_bits,
+                                                   int16_t& zero) {
+    uint32_t kmax, kmin_c;
+    minmax_keys8(v, kmax, kmin_c);
+    asym_params(group_max<LG>(kmax), group_max<LG>(kmin_c), s_bits, zero);
+    return codes8_asym(v, s_bits, zero);
+}
+
+// The packed word of 8 elements against scale s_bits and zero point zero.
+__device__ __forceinline__ uint32_t codes8_asym(const uint4& v, uint16_t s_bits, int16_t zero) {
+    const uint32_t h[8] = {v.x & 0xFFFFu, v.x >> 16, v.y & 0xFFFFu, v.y >> 16,
+                           v.z & 0xFFFFu, v.z >> 16, v.w & 0xFFFFu, v.w >> 16};
+    const double s = (double)f16_bits_to_f32(s_bits);
+    if (s == 0.0) return 0u;                             // every code 0
+    const double z = (double)zero;
     const double inv = 1.0 / s;
     uint32_t word = 0;
     bool near_tie = false;
@@ -271,6 +306,116 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint4* __restrict__
 // for G = 32), each lane storing its packed word at byte 2 + 4*lane of the
 // block as two 16-bit halves (blocks are only 2-byte aligned) and the
 // block's first lane storing d.
+// ---- per-channel scales ([QUANT] sub-section 3 granularity table, per
+// channel: one scale per output row; the GPTQ section's group_size -1):
+// the group is the whole row.  One kernel reduces each row (absolute maximum,
+// or maximum and minimum keys) to its scale (and zero point); a second forms
+// the codes against it with the same per-element arithmetic as the group
+// quantizer, so both give the bits the group formulas give with G = K.
+
+// The 8 elements of row `row` at columns c0 .. c0+7 of the stored order
+// (W's own columns, or W[:, perm[...]] with an index outside [0, K) read as 0).
+__device__ __forceinline__ uint4 row_load8(const uint16_t* __restrict__ row, int c0, int K,
+                                           const int* __restrict__ perm) {
+    if (perm == nullptr) return *reinterpret_cast<const uint4*>(row + c0);
+    uint32_t h[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int p = perm[c0 + i];
+        h[i] = (uint32_t)p < (uint32_t)K ? row[p] : 0u;
+    }
+    return make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                      h[6] | (h[7] << 16));
+}
+
+// max over the 64 lanes of the wave (every lane receives it)
+__device__ __forceinline__ uint32_t wave_max64(uint32_t v) {
+    v = group_max<32>(v);
+    return max(v, (uint32_t)__shfl_xor((int)v, 32));
+}
+
+template <bool ASYM>
+__global__ __launch_bounds__(256) void row_scale_kernel(const uint16_t* __restrict__ W,
+                                                        int64_t N, int K,
+                                                        uint16_t* __restrict__ scales,
+                                                        int16_t* __restrict__ zeros,
+                                                        const int* __restrict__ perm) {
+    __shared__ uint32_t red[2][4];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int chunks = K >> 3;
+    for (int64_t n = blockIdx.x; n < N; n += gridDim.x) {
+        const uint16_t* row = W + n * (int64_t)K;
+        uint32_t a = 0, b = 0;           // absmax; or max key, max complemented key
+        for (int c = threadIdx.x; c < chunks; c += blockDim.x) {
+            const uint4 v = row_load8(row, c * 8, K, perm);
+            if constexpr (ASYM) {
+                uint32_t ka, kb;
+                minmax_keys8(v, ka, kb);
+                a = max(a, ka);
+                b = max(b, kb);
+            } else {
+                a = max(a, absmax8(v));
+            }
+        }
+        a = wave_max64(a);
+        if constexpr (ASYM) b = wave_max64(b);
+        if (lane == 0) {
+            red[0][wave] = a;
+            red[1][wave] = b;
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            a = max(max(red[0][0], red[0][1]), max(red[0][2], red[0][3]));
+            if constexpr (ASYM) {
+                b = max(max(red[1][0], red[1][1]), max(red[1][2], red[1][3]));
+                uint16_t sb;
+                int16_t zb;
+                asym_params(a, b, sb, zb);
+                scales[n] = sb;
+                zeros[n] = zb;
+            } else {
+                scales[n] = scale_of_absmax(a);
+            }
+        }
+        __syncthreads();                 // red is reused by the next row
+    }
+}
+
+template <bool ASYM>
+__global__ __launch_bounds__(256) void row_codes_kernel(const uint16_t* __restrict__ W,
+                                                        int64_t N, int K,
+                                                        uint32_t* __restrict__ packed,
+                                                        const uint16_t* __restrict__ scales,
+                                                        const int16_t* __restrict__ zeros,
+                                                        const int* __restrict__ perm) {
+    const int wpr = K >> 3;              // packed words per row
+    const int64_t words = N * (int64_t)wpr;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < words;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t n = i / wpr;
+        const int c = (int)(i - n * wpr);
+        const uint4 v = row_load8(W + n * (int64_t)K, c * 8, K, perm);
+        packed[i] = ASYM ? codes8_asym(v, scales[n], zeros[n]) : codes8(v, scales[n]);
+    }
+}
+
+template <bool ASYM>
+hipError_t launch_quantize_rows(const uint16_t* W, int64_t N, int64_t K, uint32_t* packed,
+                                uint16_t* scales, int16_t* zeros, const int* perm,
+                                hipStream_t stream) {
+    const int64_t sblocks = N < 4096 ? N : 4096;
+    hipLaunchKernelGGL((row_scale_kernel<ASYM>), dim3((unsigned)sblocks), dim3(256), 0, stream,
+                       W, N, (int)K, scales, zeros, perm);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t words = N * (K / 8);
+    int64_t cblocks = (words + 255) / 256;
+    if (cblocks > 16384) cblocks = 16384;
+    hipLaunchKernelGGL((row_codes_kernel<ASYM>), dim3((unsigned)cblocks), dim3(256), 0, stream,
+                       W, N, (int)K, packed, scales, zeros, perm);
+    return hipGetLastError();
+}
+
 template <int U>
 __global__ __launch_bounds__(256) void quantize_q4_0_kernel(const uint4* __restrict__ W,
                                                             uint16_t* __restrict__ blocks,
@@ -338,6 +483,11 @@ hipError_t launch_quantize_t(const uint16_t* W, int64_t groups, int64_t K, const
 hipError_t launch_quantize(const uint16_t* W, int64_t N, int64_t K, int64_t group,
                            uint32_t* packed, uint16_t* scales, hipStream_t stream,
                            const int* perm, int16_t* zeros) {
+    if (N == 0 || K == 0) return hipSuccess;
+    if (group == kPerChannel)
+        return zeros != nullptr
+                   ? launch_quantize_rows<true>(W, N, K, packed, scales, zeros, perm, stream)
+                   : launch_quantize_rows<false>(W, N, K, packed, scales, nullptr, perm, stream);
     const int64_t groups = N * (K / group);
     if (groups == 0) return hipSuccess;
     // the same 16 bytes per lane and two groups' loads in flight for every G

@@ -8,7 +8,18 @@
 
 namespace w4a16 {
 
-// group: 32, 64, 128 or 256 elements per scale.  perm: NULL, or device
+// Group size meaning one scale per row (per channel): the whole row of K.
+constexpr int64_t kPerChannel = -1;
+// log2(group / 32) handed to the linear-layer kernels for per-channel
+// scales: every 32-code chunk of a row maps to scale 0 of the row.
+constexpr int kPerChannelShift = 30;
+// Scales per row of a layer with chunk shift gshift (one scale per
+// 2^gshift chunks of 32 codes; 1 for per-channel scales).
+__host__ __device__ inline int scales_per_row(int64_t K, int gshift) {
+    return gshift >= kPerChannelShift ? 1 : (int)(K >> (5 + gshift));
+}
+
+// group: 32, 64, 128 or 256 elements per scale, or kPerChannel.  perm: NULL, or device
 // int32 [K] (column j of the result is column perm[j] of W).  zeros: NULL
 // for the symmetric quantizer, or int16 [N, K/group] for the asymmetric one.
 hipError_t launch_quantize(const uint16_t* W, int64_t N, int64_t K, int64_t group,

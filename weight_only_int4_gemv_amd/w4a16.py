@@ -131,7 +131,13 @@ def packed_bytes(N: int, K: int) -> int:
     return library().w4a16_packed_bytes(N, K)
 
 
-GROUPS = (32, 64, 128, 256)   # elements per scale the kernels take
+PER_CHANNEL = -1                          # one scale per row (W4A16_PER_CHANNEL)
+GROUPS = (32, 64, 128, 256, PER_CHANNEL)   # elements per scale the kernels take
+
+
+def scales_per_row(K: int, group: int) -> int:
+    """Scales (and zero points) per row of a K-wide weight."""
+    return (1 if K > 0 else 0) if group == PER_CHANNEL else K // group
 
 
 def scales_bytes(N: int, K: int, group: int = W4A16_GROUP) -> int:
@@ -141,7 +147,7 @@ def scales_bytes(N: int, K: int, group: int = W4A16_GROUP) -> int:
 def _check_group(group: int, K: int) -> None:
     if group not in GROUPS:
         raise ValueError("group must be one of %s, got %r" % (GROUPS, group))
-    if K % W4A16_GROUP or K % group:
+    if K % W4A16_GROUP or (group != PER_CHANNEL and K % group):
         raise ValueError("K = %d is not a multiple of %d and of the group %d"
                          % (K, W4A16_GROUP, group))
 
@@ -170,10 +176,11 @@ def quantize(W: torch.Tensor, packed: torch.Tensor = None, scales: torch.Tensor 
     if packed is None:
         packed = torch.empty((N, K // 8), dtype=torch.int32, device=W.device)
     if scales is None:
-        scales = torch.empty((N, K // group), dtype=torch.float16, device=W.device)
+        scales = torch.empty((N, scales_per_row(K, group)), dtype=torch.float16,
+                             device=W.device)
     _need(packed, "packed", torch.int32, 2)
     _need(scales, "scales", torch.float16, 2)
-    if tuple(packed.shape) != (N, K // 8) or tuple(scales.shape) != (N, K // group):
+    if tuple(packed.shape) != (N, K // 8) or tuple(scales.shape) != (N, scales_per_row(K, group)):
         raise ValueError("output shapes do not match W")
     if perm is not None:
         st = lib.w4a16_quantize_perm(W.data_ptr(), perm.data_ptr(), N, K, packed.data_ptr(),
@@ -196,6 +203,8 @@ def _weights(packed: torch.Tensor, scales: torch.Tensor):
     N, K = packed.shape[0], packed.shape[1] * 8
     ng = scales.shape[1]
     group = K // ng if ng > 0 and K % ng == 0 else 0
+    if ng == 1 and group not in GROUPS:
+        group = PER_CHANNEL                     # one scale per row
     if scales.shape[0] != N or (K > 0 and group not in GROUPS) or (K == 0 and ng != 0):
         raise ValueError("scales shape %s does not match packed %s"
                          % (tuple(scales.shape), tuple(packed.shape)))
@@ -317,14 +326,16 @@ def quantize_asym(W: torch.Tensor, packed: torch.Tensor = None, scales: torch.Te
     if packed is None:
         packed = torch.empty((N, K // 8), dtype=torch.int32, device=W.device)
     if scales is None:
-        scales = torch.empty((N, K // group), dtype=torch.float16, device=W.device)
+        scales = torch.empty((N, scales_per_row(K, group)), dtype=torch.float16,
+                             device=W.device)
     if zeros is None:
-        zeros = torch.empty((N, K // group), dtype=torch.int16, device=W.device)
+        zeros = torch.empty((N, scales_per_row(K, group)), dtype=torch.int16, device=W.device)
     _need(packed, "packed", torch.int32, 2)
     _need(scales, "scales", torch.float16, 2)
     _need(zeros, "zeros", torch.int16, 2)
-    if (tuple(packed.shape) != (N, K // 8) or tuple(scales.shape) != (N, K // group)
-            or tuple(zeros.shape) != (N, K // group)):
+    ng = scales_per_row(K, group)
+    if (tuple(packed.shape) != (N, K // 8) or tuple(scales.shape) != (N, ng)
+            or tuple(zeros.shape) != (N, ng)):
         raise ValueError("output shapes do not match W")
     st = lib.w4a16_quantize_asym(W.data_ptr(), perm.data_ptr() if perm is not None else None,
                                  N, K, group, packed.data_ptr(), scales.data_ptr(),
