@@ -169,7 +169,10 @@ int w4a16_gemm_ws(const uint16_t* X, int64_t M, const uint32_t* packed, const ui
  * as everywhere.  W4A16_PER_CHANNEL is the group of the whole row (K
  * elements): one scale per row, scales[n], absmax over the row.  group ==
  * 128 gives exactly the functions above.  Scales bytes: N*(K/group)*2, N*2
- * per channel (0 for bad arguments). */
+ * per channel (0 for bad arguments).  w4a16_gemm_g picks the kernel by M
+ * as w4a16_gemm does (the matrix cores above w4a16_valu_max_m(); for groups
+ * other than 128 the tiled matrix-core kernel, whose 128-element K steps
+ * read one scale per 32-element chunk of a lane). */
 #define W4A16_PER_CHANNEL (-1)
 size_t w4a16_scales_bytes_g(int64_t N, int64_t K, int64_t group);
 int w4a16_quantize_g(const uint16_t* W, int64_t N, int64_t K, int64_t group,
@@ -189,7 +192,12 @@ int w4a16_gemm_g(const uint16_t* X, int64_t M, const uint32_t* packed, const uin
  *                         w4a16_quantize on the column-permuted W)
  *   w4a16_gemv_perm:      y[n] = sum_j x[perm[j]] * ŵ[n,j]
  *   w4a16_gemm_perm:      Y[m,n] = sum_j X[m, perm[j]] * ŵ[n,j]  (VALU
- *                         path for every M)
+ *                         path up to w4a16_valu_max_m() rows; above, X is
+ *                         first copied in the order perm, 2 M K bytes taken
+ *                         on the stream from a pool the library keeps per
+ *                         device, and the matrix-core GEMM runs on the copy;
+ *                         under graph capture the VALU path, which allocates
+ *                         nothing; w4a16_linear takes a caller workspace)
  * A NULL perm with K > 0 is W4A16_ERR_INVALID_ARG; outputs must not overlap
  * perm. */
 int w4a16_quantize_perm(const uint16_t* W, const int32_t* perm, int64_t N, int64_t K,
@@ -221,8 +229,8 @@ int w4a16_gemm_perm(const uint16_t* X, int64_t M, const int32_t* perm, const uin
  *                        not overlap each other, W or perm)
  *   w4a16_gemv_asym:     y[n] = sum_j x[perm[j]] * ŵ[n,j]      (x[j] without perm)
  *   w4a16_gemm_asym:     Y[m,n] = sum_j X[m, perm[j]] * ŵ[n,j]  (the VALU
- *                        path for M <= w4a16_valu_max_m(), for group != 128
- *                        and with perm; the matrix cores otherwise)
+ *                        path for M <= w4a16_valu_max_m(), the matrix cores
+ *                        above; with perm as for w4a16_gemm_perm)
  * Errors as for w4a16_gemm_g; a NULL zeros with K > 0 is
  * W4A16_ERR_INVALID_ARG; Y must not overlap zeros. */
 int w4a16_quantize_asym(const uint16_t* W, const int32_t* perm, int64_t N, int64_t K,
@@ -322,6 +330,31 @@ int w4a16_gemv_chain(const w4a16_gemv_stage* stages, int count, uint32_t* sync, 
  * calls and graph replays are fine. */
 int w4a16_gemv_chain_noalloc(const w4a16_gemv_stage* stages, int count, uint32_t* status,
                              void* stream);
+
+/* ---- The linear layer with every option in one call (the forms above
+ * are special cases of it): [QUANT] sub-section 3 granularity (group 32,
+ * 64, 128, 256 or W4A16_PER_CHANNEL), sub-section 2 asymmetric weights
+ * (zeros non-NULL: int16 [N, K/group], ŵ = s (q - z); NULL: symmetric
+ * offset-binary codes, ŵ = s q), GPTQ section act order (perm non-NULL:
+ * device int32 [K], Y[m,n] = sum_j X[m, perm[j]] ŵ[n,j], an index outside
+ * [0, K) reads 0; NULL: Y = X Ŵᵀ).  algo: W4A16_ALGO_* (AUTO picks by M
+ * as w4a16_gemm does; VALU and MFMA force a kernel family, every family
+ * meets the accuracy bound of w4a16_gemm).
+ * workspace: NULL, or device memory of at least
+ * w4a16_linear_workspace_bytes(M, K, perm != NULL) bytes (16-byte aligned,
+ * apart from every operand) that holds the act-order copy of X on the
+ * matrix-core path, so that the call allocates nothing and can be captured
+ * in a graph; with NULL the copy comes from the library's per-device pool
+ * (and a capturing stream takes the VALU path).  The workspace is in use
+ * until the call's work on the stream has finished.  Returns as
+ * w4a16_gemm_g / w4a16_gemm_asym; a workspace smaller than required is
+ * W4A16_ERR_INVALID_ARG.  w4a16_linear_workspace_bytes is 2 M K with a perm
+ * (has_perm != 0), else 0 (0 for invalid sizes). */
+size_t w4a16_linear_workspace_bytes(int64_t M, int64_t K, int has_perm);
+int w4a16_linear(const uint16_t* X, int64_t M, const int32_t* perm, const uint32_t* packed,
+                 const uint16_t* scales, const int16_t* zeros, int64_t N, int64_t K,
+                 int64_t group, uint16_t* Y, int algo, void* workspace, size_t workspace_bytes,
+                 void* stream);
 
 /* Largest M that W4A16_ALGO_AUTO sends to the VALU path. */
 int64_t w4a16_valu_max_m(void);

@@ -38,7 +38,8 @@ def test_header_declares_the_boundary():
                "w4a16_gemm_perm", "w4a16_quantize_asym", "w4a16_gemv_asym",
                "w4a16_gemm_asym", "w4a16_q4_0_bytes", "w4a16_quantize_q4_0",
                "w4a16_gemv_q4_0", "w4a16_gemm_q4_0", "w4a16_gemv_chain",
-               "w4a16_gemv_chain_noalloc", "w4a16_gemm_ws", "w4a16_gemm_workspace_bytes"]:
+               "w4a16_gemv_chain_noalloc", "w4a16_gemm_ws", "w4a16_gemm_workspace_bytes",
+               "w4a16_linear", "w4a16_linear_workspace_bytes"]:
         assert fn in names
 
 
@@ -124,7 +125,7 @@ def test_linear_validation(lib):
 def test_group_size_validation(lib):
     """Group size as a parameter: 32, 64, 128, 256 accepted, anything else is an
     invalid argument; K must be a multiple of the group; scale bytes follow
-    N*(K/group)*2; the matrix-core path takes group 128 only."""
+    N*(K/group)*2."""
     sb = lib.w4a16_scales_bytes_g
     assert sb(4096, 4096, 32) == 4096 * 128 * 2
     assert sb(4096, 4096, 64) == 4096 * 64 * 2
@@ -187,7 +188,7 @@ def test_act_order_validation(lib):
 def test_asymmetric_validation(lib):
     """Asymmetric entry points: zeros required for K > 0 and 2-byte aligned,
     perm optional, no output overlapping another output or an input, group
-    checked as for the group-size entry points, no matrix-core path."""
+    checked as for the group-size entry points."""
     A, B, C, D, P, Z = FAKE, FAKE * 4, FAKE * 8, FAKE * 12, FAKE * 16, FAKE * 20
     q, gv, gm = lib.w4a16_quantize_asym, lib.w4a16_gemv_asym, lib.w4a16_gemm_asym
     assert q(A, None, 4, 128, 128, B, C, None, None) == INVALID        # no zeros
@@ -342,3 +343,42 @@ def test_gemm_ws_validation(lib):
     assert f(None, 4, B, C, 16, 128, D, S, 4096, None) == INVALID
     assert f(A, 4, B, C, 16, 128, D, S, 4096, None) in (DEVICE, OK)
 
+
+def test_linear_general_validation(lib):
+    """w4a16_linear: every option of the linear layer in one call; the
+    act-order workspace is checked (size, alignment, overlap with every
+    operand) before the device; NULL perm and zeros mean none."""
+    A, B, C, D, P, Z, W = (FAKE, FAKE * 4, FAKE * 8, FAKE * 12, FAKE * 16, FAKE * 20,
+                           FAKE * 64)
+    f = lib.w4a16_linear
+    wb = lib.w4a16_linear_workspace_bytes
+    assert wb(512, 4096, 1) == 512 * 4096 * 2
+    assert wb(512, 4096, 0) == 0
+    assert wb(-1, 4096, 1) == 0 and wb(4, 100, 1) == 0
+    need = wb(4, 256, 1)
+    # sizes, group, algo
+    assert f(A, -1, None, B, C, None, 16, 256, 128, D, 0, None, 0, None) == INVALID
+    assert f(A, 4, None, B, C, None, 16, 200, 128, D, 0, None, 0, None) == SHAPE
+    assert f(A, 4, None, B, C, None, 16, 256, 48, D, 0, None, 0, None) == INVALID
+    assert f(A, 4, None, B, C, None, 16, 384, 256, D, 0, None, 0, None) == SHAPE
+    assert f(A, 4, None, B, C, None, 16, 256, 128, D, 9, None, 0, None) == INVALID
+    # misaligned or overlapping operands as for the other forms
+    assert f(A, 4, P + 4, B, C, None, 16, 256, 128, D, 0, None, 0, None) == MISALIGNED
+    assert f(A, 4, None, B, C, Z + 1, 16, 256, 128, D, 0, None, 0, None) == MISALIGNED
+    assert f(A, 4, P, B, C, None, 16, 256, 128, P + 2, 0, None, 0, None) == INVALID
+    assert f(A, 4, None, B, C, Z, 16, 256, 128, Z + 2, 0, None, 0, None) == INVALID
+    # workspace: too small, misaligned, overlapping X, Y, packed, scales, perm, zeros
+    assert f(A, 4, P, B, C, None, 16, 256, 128, D, 2, W, need - 1, None) == INVALID
+    assert f(A, 4, P, B, C, None, 16, 256, 128, D, 2, W + 8, need, None) == MISALIGNED
+    assert f(A, 4, P, B, C, None, 16, 256, 128, D, 2, A + 16, need, None) == INVALID
+    assert f(A, 4, P, B, C, None, 16, 256, 128, D, 2, D - 16, need, None) == INVALID
+    assert f(A, 4, P, B, C, None, 16, 256, 128, D, 2, B + 16, need, None) == INVALID
+    assert f(A, 4, P, B, C, None, 16, 256, 128, D, 2, C - 16, need, None) == INVALID
+    assert f(A, 4, P, B, C, None, 16, 256, 128, D, 2, P - 16, need, None) == INVALID
+    assert f(A, 4, P, B, C, Z, 16, 256, 128, D, 2, Z - 16, need, None) == INVALID
+    # without a perm the workspace is not used and not checked
+    assert f(A, 4, None, B, C, None, 16, 256, 128, D, 2, W + 8, 0, None) in (DEVICE, OK)
+    # valid calls reach the device check
+    assert f(A, 4, P, B, C, Z, 16, 256, 32, D, 2, W, need, None) in (DEVICE, OK)
+    assert f(A, 4, P, B, C, None, 16, 256, -1, D, 0, None, 0, None) in (DEVICE, OK)
+    assert f(None, 0, None, None, None, None, 16, 256, 128, None, 0, None, 0, None) == OK

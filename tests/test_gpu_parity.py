@@ -564,11 +564,13 @@ def check_linear_group(w4, orc, M, N, K, group, seed, algo=None):
 
 
 @pytest.mark.parametrize("group", GROUP_SIZES)
-@pytest.mark.parametrize("M,algo", [(1, "gemv"), (2, None), (3, "valu"), (8, None), (13, None)])
+@pytest.mark.parametrize("M,algo", [(1, "gemv"), (2, None), (3, "valu"), (8, "valu"),
+                                    (13, "valu"), (8, None)])
 @pytest.mark.parametrize("N,K", [(300, 1536), (1001, 4096), (64, 14336)])
 def test_linear_group_sizes(w4, orc, group, M, algo, N, K):
-    """GEMV and the VALU GEMM (every M, both launch families: whole-x staging
-    for the persistent kernel, K slices for M = 8) at other group sizes."""
+    """GEMV and the VALU GEMM (both launch families: whole-x staging for the
+    persistent kernel, K slices for M = 8) at other group sizes, and the
+    automatic choice above two rows (the tiled matrix-core kernel)."""
     check_linear_group(w4, orc, M, N, K, group, seed=[23, group, M, N, K], algo=algo)
 
 
@@ -597,14 +599,6 @@ def test_group_sizes_one_hot_exact(w4, orc, group):
         assert (Y.view(np.uint16) == want.view(np.uint16)).all()
 
 
-def test_group_sizes_reject_matrix_cores(w4, orc):
-    W = inputs.weight(16, 256, seed=[26])
-    packed, scales = orc.quantize(W, group=64)
-    X = inputs.activation(4, 256, seed=[26, 1])
-    with pytest.raises(ValueError):
-        w4.gemm(dev(X), packed_to_dev(packed), scales_to_dev(scales), algo="mfma")
-
-
 # ------------------------------------------------------- act-order column order
 
 def perm_of(kind: str, K: int, seed) -> np.ndarray:
@@ -631,13 +625,15 @@ def test_quantize_act_order_bit_exact(w4, orc, kind, N, K):
 
 
 @pytest.mark.parametrize("kind", ["identity", "random"])
-@pytest.mark.parametrize("M", [1, 2, 3, 8, 13])
+@pytest.mark.parametrize("M,algo", [(1, None), (2, None), (3, "valu"), (8, "valu"), (13, "valu"),
+                                    (8, None)])
 @pytest.mark.parametrize("N,K", [(300, 1536), (1001, 4096), (64, 14336)])
-def test_linear_act_order(w4, orc, kind, M, N, K):
+def test_linear_act_order(w4, orc, kind, M, algo, N, K):
     """y = X[:, perm] . Ŵpᵀ on the VALU path (persistent kernel with whole-x
-    staging, and K slices for M = 8, 13 at K = 14336) against the oracle on
-    the gathered activations."""
-    say("linear act-order %s M=%d N=%d K=%d" % (kind, M, N, K))
+    staging, and K slices for M = 8, 13 at K = 14336) and the automatic
+    choice above two rows (gathered copy of X, matrix cores), against the
+    oracle on the gathered activations."""
+    say("linear act-order %s M=%d N=%d K=%d algo=%s" % (kind, M, N, K, algo))
     W = inputs.weight(N, K, seed=[32, N, K])
     perm = perm_of(kind, K, [32, K])
     packed, scales = orc.quantize(np.ascontiguousarray(W[:, perm]))
@@ -647,7 +643,7 @@ def test_linear_act_order(w4, orc, kind, M, N, K):
                     perm=dev(perm)).cpu().numpy()[None]
     else:
         Y = w4.gemm(dev(X), packed_to_dev(packed), scales_to_dev(scales),
-                    perm=dev(perm)).cpu().numpy()
+                    perm=dev(perm), algo=algo).cpu().numpy()
     torch.cuda.synchronize()
     Yref, Yabs = orc.matmul(np.ascontiguousarray(X[:, perm]), packed, scales)
     tol = oracle.tolerance(Yref, Yabs)
@@ -783,8 +779,9 @@ def test_quantize_asym_act_order(w4, orc, kind, group):
     check_quantize_asym(w4, orc, W, group, perm=perm_of(kind, 4096, [42, group]), name=kind)
 
 
-def check_linear_asym(w4, orc, M, N, K, group, seed, perm_kind=None, plant=True):
-    say("linear asym group=%d M=%d N=%d K=%d perm=%s" % (group, M, N, K, perm_kind))
+def check_linear_asym(w4, orc, M, N, K, group, seed, perm_kind=None, plant=True, algo=None):
+    say("linear asym group=%d M=%d N=%d K=%d perm=%s algo=%s" % (group, M, N, K, perm_kind,
+                                                                  algo))
     W = asym_weight(N, K, seed, plant=plant)
     perm = None if perm_kind is None else perm_of(perm_kind, K, seed)
     Wo = W if perm is None else np.ascontiguousarray(W[:, perm])
@@ -795,7 +792,7 @@ def check_linear_asym(w4, orc, M, N, K, group, seed, perm_kind=None, plant=True)
     if M == 1:
         Y = w4.gemv_asym(dev(X)[0], pd, sd, zd, perm=permd).cpu().numpy()[None]
     else:
-        Y = w4.gemm_asym(dev(X), pd, sd, zd, perm=permd).cpu().numpy()
+        Y = w4.gemm_asym(dev(X), pd, sd, zd, perm=permd, algo=algo).cpu().numpy()
     torch.cuda.synchronize()
     assert Y.shape == (M, N)
     Xo = X if perm is None else np.ascontiguousarray(X[:, perm])
@@ -808,13 +805,15 @@ def check_linear_asym(w4, orc, M, N, K, group, seed, perm_kind=None, plant=True)
 
 
 @pytest.mark.parametrize("group", [32, 128, 256])
-@pytest.mark.parametrize("M", [1, 2, 3, 8, 13])
+@pytest.mark.parametrize("M,algo", [(1, None), (2, None), (3, "valu"), (8, "valu"),
+                                    (13, "valu"), (3, None), (13, None)])
 @pytest.mark.parametrize("N,K", [(300, 1536), (1001, 4096), (64, 14336)])
-def test_linear_asym(w4, orc, group, M, N, K):
+def test_linear_asym(w4, orc, group, M, algo, N, K):
     """Asymmetric GEMV / VALU GEMM for every M family (persistent kernel with
-    whole-x staging; K slices for M = 8, 13 at K = 14336), planted groups with
-    |z| > 1000 (the chunk-sum correction) included."""
-    check_linear_asym(w4, orc, M, N, K, group, [43, group, M, N, K])
+    whole-x staging; K slices for M = 8, 13 at K = 14336) and the automatic
+    choice above two rows (matrix cores), planted groups with |z| > 1000
+    (the chunk-sum correction) included."""
+    check_linear_asym(w4, orc, M, N, K, group, [43, group, M, N, K], algo=algo)
 
 
 @pytest.mark.parametrize("M", [3, 16, 17, 32, 33, 64, 65, 200, 512])
@@ -877,9 +876,9 @@ def test_linear_asym_layer_shapes(w4, orc, name, K, N):
     check_linear_asym(w4, orc, 1, N, K, 128, [44, N, K], plant=False)
 
 
-@pytest.mark.parametrize("M", [1, 4])
-def test_linear_asym_act_order(w4, orc, M):
-    check_linear_asym(w4, orc, M, 515, 4096, 128, [45, M], perm_kind="random")
+@pytest.mark.parametrize("M,algo", [(1, None), (4, "valu"), (4, None), (130, None)])
+def test_linear_asym_act_order(w4, orc, M, algo):
+    check_linear_asym(w4, orc, M, 515, 4096, 128, [45, M], perm_kind="random", algo=algo)
 
 
 def test_asym_one_hot_exact(w4, orc):

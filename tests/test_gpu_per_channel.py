@@ -110,7 +110,8 @@ def check_linear(w4, orc, M, N, K, seed, algo=None, asym=False):
 
 
 @pytest.mark.parametrize("M,algo", [(1, "gemv"), (2, None), (3, None), (8, None), (13, None),
-                                    (16, None), (33, None), (130, None)])
+                                    (16, None), (33, None), (130, None), (8, "valu"),
+                                    (13, "valu")])
 @pytest.mark.parametrize("N,K", [(300, 1536), (1001, 4096), (64, 14336)])
 def test_linear_per_channel(w4, orc, M, algo, N, K):
     check_linear(w4, orc, M, N, K, [63, M, N, K], algo=algo)

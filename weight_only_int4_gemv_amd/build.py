@@ -15,7 +15,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libw4a16.so")
 SOURCES = ["api.hip", "quantize.hip", "gemv.hip", "gemv_chain.hip", "gemm_mfma.hip",
-           "gemm_skinny.hip", "gemv_mfma4.hip", "gemm_batched.hip", "gemv_q4_0.hip"]
+           "gemm_skinny.hip", "gemv_mfma4.hip", "gemm_batched.hip", "gemv_q4_0.hip",
+           "gather_x.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -1,5 +1,8 @@
 // api.hip — the C ABI of include/w4a16.h: host-side validation, device
-// checks and dispatch to the kernels.  Nothing here allocates device memory.
+// checks and dispatch to the kernels.  The one device allocation is the
+// copy of the activations in act-order column order that the matrix-core
+// path of the act-order linear layer reads when the caller passes no
+// workspace: stream-ordered, from a pool the library keeps per device.
 #include <hip/hip_runtime.h>
 
 #include <mutex>
@@ -32,7 +35,11 @@ struct DeviceInfo {
     bool probed = false;
     bool ok = false;
     int num_cu = 0;
+    hipMemPool_t pool = nullptr;   // stream-ordered scratch (act-order copies of X)
 };
+// Memory the pool keeps across synchronizations instead of returning it to
+// the system (larger copies are returned after use).
+constexpr uint64_t kPoolKeepBytes = (uint64_t)512 << 20;
 constexpr int kMaxDevices = 64;
 DeviceInfo g_devices[kMaxDevices];
 std::mutex g_mutex;
@@ -54,6 +61,28 @@ int current_device(int* num_cu) {
     if (!d.ok) return W4A16_ERR_DEVICE;
     *num_cu = d.num_cu;
     return W4A16_OK;
+}
+
+// The library's memory pool on the current device (created on first use).
+hipMemPool_t device_pool() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_mutex);
+    DeviceInfo& d = g_devices[dev];
+    if (d.pool == nullptr) {
+        hipMemPoolProps props;
+        memset(&props, 0, sizeof(props));
+        props.allocType = hipMemAllocationTypePinned;
+        props.handleTypes = hipMemHandleTypeNone;
+        props.location.type = hipMemLocationTypeDevice;
+        props.location.id = dev;
+        hipMemPool_t pool = nullptr;
+        if (hipMemPoolCreate(&pool, &props) != hipSuccess) return nullptr;
+        uint64_t keep = kPoolKeepBytes;
+        (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+        d.pool = pool;
+    }
+    return d.pool;
 }
 
 int check_sizes(int64_t M, int64_t N, int64_t K) {
@@ -91,16 +120,14 @@ int status_of(hipError_t e) { return e == hipSuccess ? W4A16_OK : W4A16_ERR_LAUN
 int linear(const uint16_t* X, int64_t M, const uint32_t* packed, const uint16_t* scales,
            int64_t N, int64_t K, int64_t group, uint16_t* Y, int algo, void* stream,
            const int32_t* perm = nullptr, bool with_perm = false,
-           const int16_t* zeros = nullptr, bool asym = false) {
+           const int16_t* zeros = nullptr, bool asym = false, void* workspace = nullptr,
+           size_t workspace_bytes = 0) {
     int st = check_sizes(M, N, K);
     if (st != W4A16_OK) return st;
     st = check_group(group, K);
     if (st != W4A16_OK) return st;
     if (algo != W4A16_ALGO_AUTO && algo != W4A16_ALGO_VALU && algo != W4A16_ALGO_MFMA)
         return W4A16_ERR_INVALID_ARG;
-    // the matrix-core kernels read one scale per 128 elements and no perm
-    const bool mfma_capable = group == W4A16_GROUP && !with_perm;
-    if (algo == W4A16_ALGO_MFMA && !mfma_capable) return W4A16_ERR_INVALID_ARG;
     if (M == 0 || N == 0) return W4A16_OK;
     // With K == 0 the inputs hold no bytes and may be NULL; they are never read.
     if (!Y || (K > 0 && (!X || !packed || !scales || (with_perm && !perm) || (asym && !zeros))))
@@ -115,21 +142,64 @@ int linear(const uint16_t* X, int64_t M, const uint32_t* packed, const uint16_t*
         (with_perm && overlap(Y, y_bytes, perm, (size_t)K * 4)) ||
         (asym && overlap(Y, y_bytes, zeros, s_bytes)))
         return W4A16_ERR_INVALID_ARG;
+    // workspace (the act-order copy of X): 2 M K bytes, apart from every
+    // operand
+    const size_t xp_bytes = (size_t)M * K * 2;
+    if (workspace != nullptr && with_perm && K > 0) {
+        if (workspace_bytes < xp_bytes) return W4A16_ERR_INVALID_ARG;
+        if (!aligned(workspace, 16)) return W4A16_ERR_MISALIGNED;
+        if (overlap(workspace, xp_bytes, X, xp_bytes) || overlap(workspace, xp_bytes, Y, y_bytes) ||
+            overlap(workspace, xp_bytes, packed, (size_t)N * K / 2) ||
+            overlap(workspace, xp_bytes, scales, s_bytes) ||
+            overlap(workspace, xp_bytes, perm, (size_t)K * 4) ||
+            (asym && overlap(workspace, xp_bytes, zeros, s_bytes)))
+            return W4A16_ERR_INVALID_ARG;
+    }
     int num_cu = 0;
     st = current_device(&num_cu);
     if (st != W4A16_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const bool valu = algo == W4A16_ALGO_VALU || !mfma_capable ||
-                      (algo == W4A16_ALGO_AUTO && M <= kValuMaxM);
+    // Act order on the matrix cores needs a permuted copy of X: in the
+    // caller's workspace, else allocated on the stream from the library's
+    // pool; without a workspace a stream under graph capture keeps the VALU
+    // path, which gathers x itself and allocates nothing.
+    bool capturing = false;
+    if (with_perm && K > 0 && algo != W4A16_ALGO_VALU && workspace == nullptr) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        capturing = hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone;
+    }
+    const bool valu = algo == W4A16_ALGO_VALU || (algo == W4A16_ALGO_AUTO && M <= kValuMaxM) ||
+                      capturing;
     if (valu)
         return status_of(w4a16::launch_gemv_valu(X, M, packed, scales, N, K, Y, s, num_cu,
                                                  group_shift(group),
                                                  with_perm ? perm : nullptr,
                                                  asym ? zeros : nullptr));
-    if (asym)
-        return status_of(w4a16::launch_gemm_mfma_asym(X, M, packed, scales, zeros, N, K, Y, s,
-                                                      num_cu));
-    return status_of(w4a16::launch_gemm_mfma(X, M, packed, scales, N, K, Y, s, num_cu));
+    const uint16_t* Xm = X;
+    void* xp = nullptr;       // pool memory to give back
+    if (with_perm && K > 0) {
+        void* dst = workspace;
+        if (dst == nullptr) {
+            hipMemPool_t pool = device_pool();
+            if (pool == nullptr || hipMallocFromPoolAsync(&xp, xp_bytes, pool, s) != hipSuccess)
+                return W4A16_ERR_LAUNCH;
+            dst = xp;
+        }
+        const hipError_t e =
+            w4a16::launch_gather_x(X, M, K, perm, static_cast<uint16_t*>(dst), s, num_cu);
+        if (e != hipSuccess) {
+            if (xp != nullptr) (void)hipFreeAsync(xp, s);
+            return W4A16_ERR_LAUNCH;
+        }
+        Xm = static_cast<const uint16_t*>(dst);
+    }
+    const hipError_t e =
+        asym ? w4a16::launch_gemm_mfma_asym(Xm, M, packed, scales, zeros, N, K, Y, s, num_cu,
+                                            group_shift(group))
+             : w4a16::launch_gemm_mfma(Xm, M, packed, scales, N, K, Y, s, num_cu,
+                                       group_shift(group));
+    if (xp != nullptr && hipFreeAsync(xp, s) != hipSuccess) return W4A16_ERR_LAUNCH;
+    return status_of(e);
 }
 
 int quantize(const uint16_t* W, int64_t N, int64_t K, int64_t group, uint32_t* packed,
@@ -274,6 +344,19 @@ int w4a16_gemm_g(const uint16_t* X, int64_t M, const uint32_t* packed, const uin
 int w4a16_gemm_ex(const uint16_t* X, int64_t M, const uint32_t* packed, const uint16_t* scales,
                   int64_t N, int64_t K, uint16_t* Y, int algo, void* stream) {
     return linear(X, M, packed, scales, N, K, W4A16_GROUP, Y, algo, stream);
+}
+
+size_t w4a16_linear_workspace_bytes(int64_t M, int64_t K, int has_perm) {
+    if (!has_perm || check_sizes(M, 0, K) != W4A16_OK) return 0;
+    return (size_t)M * (size_t)K * 2;
+}
+
+int w4a16_linear(const uint16_t* X, int64_t M, const int32_t* perm, const uint32_t* packed,
+                 const uint16_t* scales, const int16_t* zeros, int64_t N, int64_t K,
+                 int64_t group, uint16_t* Y, int algo, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+    return linear(X, M, packed, scales, N, K, group, Y, algo, stream, perm, perm != nullptr,
+                  zeros, zeros != nullptr, workspace, workspace_bytes);
 }
 
 }  // extern "C"

@@ -1,8 +1,10 @@
 // gemm_mfma.hip — W4A16 GEMM on the gfx950 matrix cores (batched decode,
 // M >= 16, and prefill, [BENCH] §一 512-token prompt, §二 prefill latency).
 //
-// Y[m,n] = sum_k X[m,k] * fp16(s[n,k/128] * q[n,k]), fp32 accumulation in
-// v_mfma_f32_16x16x32_f16, fp16 output.
+// Y[m,n] = sum_k X[m,k] * fp16(s[n,k/group] * q[n,k]), fp32 accumulation in
+// v_mfma_f32_16x16x32_f16, fp16 output.  group: 32, 64, 128, 256 or the
+// whole row ([QUANT] sub-section 3, granularity), passed as gshift =
+// log2(group / 32); the kernel walks K in steps of 128 either way.
 //
 // Operand mapping of v_mfma_f32_16x16x32_f16 (lane l, j = l/16):
 //   A (16 x 32): row l%16, eight k values of slot j
@@ -53,7 +55,7 @@ __global__ __launch_bounds__(WM * WN * WK * kWave)
 __attribute__((amdgpu_waves_per_eu(2))) void gemm_mfma_kernel(
     const uint16_t* __restrict__ X, int M, const uint4* __restrict__ packed,
     const uint16_t* __restrict__ scales, const int16_t* __restrict__ zeros,
-    uint16_t* __restrict__ Y, int N, int K) {
+    uint16_t* __restrict__ Y, int N, int K, int gshift) {
     constexpr int NT = WM * WN * WK * kWave;
     constexpr int BM = 16 * TM * WM;
     constexpr int BN = 16 * TN * WN;
@@ -73,10 +75,17 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_mfma_kernel(
     const int j = lane >> 4;
     const int m_blk = blockIdx.y * BM;
     const int n_blk = blockIdx.x * BN;
-    const int ngroups = K >> 7;
+    const int ngroups = K >> 7;                       // 128-element steps of K
     const int nsteps = (ngroups + WK - 1) / WK;
     const uint32_t wrow = (uint32_t)K / 2;            // bytes per weight row
-    const uint32_t srow = (uint32_t)ngroups * 2;      // bytes per scale (and zero) row
+    // bytes per scale (and zero) row: one scale per 2^gshift chunks of 32
+    const uint32_t srow = (uint32_t)scales_per_row(K, gshift) * 2;
+    // Lane j's 32 elements of a 128-element step are chunk 4 g + j of its row,
+    // whose scale is number (4 g + j) >> gshift: below group 128 the lane's
+    // share (j >> gshift) is fixed here and the step adds g << (2 - gshift);
+    // from group 128 up every lane of the step reads scale g >> (gshift - 2)
+    // (0 for one scale per row).
+    const uint32_t s_lane = gshift < 2 ? (uint32_t)(j >> gshift) * 2u : 0u;
 
     // Byte offsets of this thread's loads from the block's first row, fixed
     // for the whole K loop (32-bit: the launcher keeps BM rows of X and BN
@@ -98,7 +107,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_mfma_kernel(
     for (int tn = 0; tn < TN; ++tn) {
         const uint32_t r = (uint32_t)(min(n_blk + (wn * TN + tn) * 16 + l16, N - 1) - n_blk);
         b_off[tn] = r * wrow + (uint32_t)j * 16u;
-        s_off[tn] = r * srow;
+        s_off[tn] = r * srow + s_lane;
     }
     // Buffer resources over the block's rows; loads take the per-thread
     // offset in a VGPR and the step's offset in an SGPR.
@@ -140,13 +149,14 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_mfma_kernel(
     auto load_b = [&](int step, BRegs& b) {
         const int g = step * WK + wk;
         if (g < ngroups) {
+            const int sg = gshift <= 2 ? g << (2 - gshift) : g >> (gshift - 2);
 #pragma unroll
             for (int tn = 0; tn < TN; ++tn) {
                 const v4u v = __builtin_amdgcn_raw_buffer_load_b128(pr, b_off[tn], g * 64, 0);
                 b.w[tn] = make_uint4(v.x, v.y, v.z, v.w);
-                b.s[tn] = __builtin_amdgcn_raw_buffer_load_b16(sr, s_off[tn], g * 2, 0);
+                b.s[tn] = __builtin_amdgcn_raw_buffer_load_b16(sr, s_off[tn], sg * 2, 0);
                 b.z[tn] = ASYM ? (int)(int16_t)__builtin_amdgcn_raw_buffer_load_b16(
-                                     zr, s_off[tn], g * 2, 0)
+                                     zr, s_off[tn], sg * 2, 0)
                                : 0;
             }
         } else {
@@ -218,7 +228,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_mfma_kernel(
                                     af, bf[tn][kk], acc[tm][tn], 0, 0, 0);
                         }
                     }
-                } else {
+                } else if (gshift >= 2) {
                     half8_t bq[TN][4];
                     float sf[TN], cf[TN];
                     bool wide = false;
@@ -276,6 +286,79 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_mfma_kernel(
                                     if (any_wide) v = fmaf(cf[tn], xs[th][r], v);
                                     acc[t0 + th][tn][r] = v;
                                 }
+                    }
+                } else {
+                    // Groups of 32 or 64: the four 32-element chunks of a
+                    // step have their own scales, and one MFMA of the common
+                    // mapping sums over the chunks of the lanes j = 0..3.  Here
+                    // the mapping is transposed: MFMA kk takes chunk kk, its
+                    // slot j the vector 4 kk + j of the staged A row and word
+                    // 4 kk + j of the weight row, which lane (l16, kk) loaded
+                    // as its word j; so every MFMA (two for group 64) sums one
+                    // group, scaled once in fp32 with the scale and zero point
+                    // that lane (l16, kk) loaded.
+                    const uint4* abase_t = abase - 3 * j;      // vector j of the row
+                    half8_t bq[TN][4];
+                    float sk[TN][4], ck[TN][4];
+                    bool wide = false;
+#pragma unroll
+                    for (int tn = 0; tn < TN; ++tn) {
+                        const ZeroBias zown = zero_bias(cur.z[tn]);
+                        const float sown = f16_bits_to_f32((uint16_t)cur.s[tn]);
+                        const float cown = sown * (float)(zown.zc - cur.z[tn]);
+                        wide |= zown.zc != cur.z[tn];
+                        const uint32_t words[4] = {cur.w[tn].x, cur.w[tn].y, cur.w[tn].z,
+                                                   cur.w[tn].w};
+#pragma unroll
+                        for (int kk = 0; kk < 4; ++kk) {
+                            const int src = l16 + 16 * kk;
+                            // word 4 kk + j: word j of lane (l16, kk)
+                            uint32_t wt = 0;
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) {
+                                const uint32_t v = (uint32_t)__shfl((int)words[r], src);
+                                wt = r == j ? v : wt;
+                            }
+                            sk[tn][kk] = __shfl(sown, src);
+                            ck[tn][kk] = __shfl(cown, src);
+                            half2_t q[4];
+                            codes_word_zp(wt, kc, zero_bias(__shfl(cur.z[tn], src)), q);
+                            bq[tn][kk] = (half8_t){q[0].x, q[0].y, q[1].x, q[1].y,
+                                                   q[2].x, q[2].y, q[3].x, q[3].y};
+                        }
+                    }
+                    const _Float16 one = (_Float16)1.0f;
+                    const half8_t ones = {one, one, one, one, one, one, one, one};
+                    const bool any_wide = __any(wide);
+                    const int last = (1 << gshift) - 1;   // chunks per group - 1
+#pragma unroll
+                    for (int tm = 0; tm < TM; ++tm) {
+                        float4_t d[TN], xs;
+#pragma unroll
+                        for (int kk = 0; kk < 4; ++kk) {
+                            const bool first = (kk & last) == 0;
+                            const half8_t af =
+                                __builtin_bit_cast(half8_t, abase_t[tm * 16 * kLdaVec + 4 * kk]);
+#pragma unroll
+                            for (int tn = 0; tn < TN; ++tn)
+                                d[tn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                                    af, bq[tn][kk], first ? (float4_t){0.f, 0.f, 0.f, 0.f} : d[tn],
+                                    0, 0, 0);
+                            if (any_wide)
+                                xs = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                                    af, ones, first ? (float4_t){0.f, 0.f, 0.f, 0.f} : xs, 0, 0,
+                                    0);
+                            if ((kk & last) == last) {
+#pragma unroll
+                                for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+                                    for (int r = 0; r < 4; ++r) {
+                                        float v = fmaf(sk[tn][kk], d[tn][r], acc[tm][tn][r]);
+                                        if (any_wide) v = fmaf(ck[tn][kk], xs[r], v);
+                                        acc[tm][tn][r] = v;
+                                    }
+                            }
+                        }
                     }
                 }
             };
@@ -436,7 +519,7 @@ namespace {
 template <int TM, int TN, int WM, int WN, int WK, bool ASYM = false>
 hipError_t launch_mfma_t(const uint16_t* X, int64_t M, const uint32_t* packed,
                          const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y,
-                         hipStream_t stream, const int16_t* zeros = nullptr) {
+                         hipStream_t stream, int gshift, const int16_t* zeros = nullptr) {
     constexpr int BM = 16 * TM * WM;
     constexpr int BN = 16 * TN * WN;
     const size_t a_bytes = (size_t)2 * WK * BM * kLdaVec * sizeof(uint4);   // two A buffers
@@ -451,7 +534,8 @@ hipError_t launch_mfma_t(const uint16_t* X, int64_t M, const uint32_t* packed,
     }
     const dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM));
     hipLaunchKernelGGL(kern, grid, dim3(WM * WN * WK * kWave), lds, stream, X, (int)M,
-                       reinterpret_cast<const uint4*>(packed), scales, zeros, Y, (int)N, (int)K);
+                       reinterpret_cast<const uint4*>(packed), scales, zeros, Y, (int)N, (int)K,
+                       gshift);
     return hipGetLastError();
 }
 
@@ -460,72 +544,75 @@ hipError_t launch_mfma_t(const uint16_t* X, int64_t M, const uint32_t* packed,
 template <bool ASYM>
 hipError_t launch_tiled(const uint16_t* X, int64_t M, const uint32_t* packed,
                         const uint16_t* scales, const int16_t* zeros, int64_t N, int64_t K,
-                        uint16_t* Y, hipStream_t stream, int num_cu) {
+                        uint16_t* Y, hipStream_t stream, int num_cu, int gshift) {
     if (K > kTiledMaxK)
-        return launch_gemv_valu(X, M, packed, scales, N, K, Y, stream, num_cu, 2, nullptr,
+        return launch_gemv_valu(X, M, packed, scales, N, K, Y, stream, num_cu, gshift, nullptr,
                                 ASYM ? zeros : nullptr);
+#define W4A16_TILED(TM, TN, WM, WN, WK) \
+    launch_mfma_t<TM, TN, WM, WN, WK, ASYM>(X, M, packed, scales, N, K, Y, stream, gshift, zeros)
     // Few rows: one 16- or 32-row tile, waves split K; enough column tiles
     // to give every compute unit work.
     if (M <= 16) {
-        if (N >= (int64_t)64 * num_cu)
-            return launch_mfma_t<1, 2, 1, 1, 4, ASYM>(X, M, packed, scales, N, K, Y, stream, zeros);
-        return launch_mfma_t<1, 1, 1, 1, 4, ASYM>(X, M, packed, scales, N, K, Y, stream, zeros);
+        if (N >= (int64_t)64 * num_cu) return W4A16_TILED(1, 2, 1, 1, 4);
+        return W4A16_TILED(1, 1, 1, 1, 4);
     }
     if (M <= 32) {
-        if (N >= (int64_t)64 * num_cu)
-            return launch_mfma_t<2, 2, 1, 1, 4, ASYM>(X, M, packed, scales, N, K, Y, stream, zeros);
-        return launch_mfma_t<2, 1, 1, 1, 4, ASYM>(X, M, packed, scales, N, K, Y, stream, zeros);
+        if (N >= (int64_t)64 * num_cu) return W4A16_TILED(2, 2, 1, 1, 4);
+        return W4A16_TILED(2, 1, 1, 1, 4);
     }
-    if (M <= 64)
-        return launch_mfma_t<2, 2, 2, 2, 1, ASYM>(X, M, packed, scales, N, K, Y, stream, zeros);
+    if (M <= 64) return W4A16_TILED(2, 2, 2, 2, 1);
     // Prefill: when 128 x 128 tiles fill the compute units, 128 x 256 block
     // tiles (eight 16-row by two 16-column tiles per wave, eight waves across
     // N: each staged X tile serves 256 columns; M = 512 on 4096 x 14336 at
     // 76 us against 81 us with 128 x 128 blocks, on 8192 x 28672 316 against
-    // 338 us).
+    // 338 us).  Asymmetric weights: 128 x 16 wave tiles (the exact slow copy
+    // of the loop does not fit two waves per SIMD with 128 x 32 tiles).
     const int64_t tiles128 = ((M + 127) / 128) * ((N + 127) / 128);
     if (tiles128 >= num_cu) {
-        // asymmetric weights: 128 x 16 wave tiles (the exact slow copy of
-        // the loop does not fit two waves per SIMD with 128 x 32 tiles)
         if constexpr (ASYM)
-            return launch_mfma_t<8, 1, 1, 8, 1, ASYM>(X, M, packed, scales, N, K, Y, stream,
-                                                      zeros);
+            return W4A16_TILED(8, 1, 1, 8, 1);
         else
-            return launch_mfma_t<8, 2, 1, 8, 1, ASYM>(X, M, packed, scales, N, K, Y, stream,
-                                                      zeros);
+            return W4A16_TILED(8, 2, 1, 8, 1);
     }
     // Else 128 x 64 block tiles, eight waves, two over K, four across N with
     // 128 x 16 wave tiles (M = 512 on 14336 x 4096: 110 us against 117 us
     // with 64 x 32 wave tiles).
-    return launch_mfma_t<8, 1, 1, 4, 2, ASYM>(X, M, packed, scales, N, K, Y, stream, zeros);
+    return W4A16_TILED(8, 1, 1, 4, 2);
+#undef W4A16_TILED
 }
 
 }  // namespace
 
 hipError_t launch_gemm_mfma(const uint16_t* X, int64_t M, const uint32_t* packed,
                             const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y,
-                            hipStream_t stream, int num_cu) {
-    // Up to four rows: the streaming GEMV on 4x4x4 matrix-core blocks while
-    // x fits in LDS (K == 0, all outputs zero, stays on the tiled kernel).
-    if (M <= kMfma4MaxM && K > 0 && M * K * 2 <= kMfma4MaxXBytes)
-        return launch_gemv_mfma4(X, M, packed, scales, N, K, Y, stream, num_cu);
-    // Batched decode: blocks own contiguous weight rows, X through LDS.
-    if (M <= kBatchedMaxM && K > 0 && K <= kBatchedMaxK)
-        return launch_gemm_batched(X, M, packed, scales, N, K, Y, stream, num_cu);
-    // Few rows and K > N (few output tiles, long rows): the streaming kernel
-    // with the K groups split over waves.
-    if (M <= 64 && K > N && K <= kSkinnyMaxK)
-        return launch_gemm_skinny(X, M, packed, scales, N, K, Y, stream, num_cu);
-    return launch_tiled<false>(X, M, packed, scales, nullptr, N, K, Y, stream, num_cu);
+                            hipStream_t stream, int num_cu, int gshift) {
+    // The streaming kernels below read one scale per 128 elements; other
+    // groups take the tiled kernel for every M.
+    if (gshift == 2) {
+        // Up to four rows: the streaming GEMV on 4x4x4 matrix-core blocks
+        // while x fits in LDS (K == 0, all outputs zero, stays on the tiled
+        // kernel).
+        if (M <= kMfma4MaxM && K > 0 && M * K * 2 <= kMfma4MaxXBytes)
+            return launch_gemv_mfma4(X, M, packed, scales, N, K, Y, stream, num_cu);
+        // Batched decode: blocks own contiguous weight rows, X through LDS.
+        if (M <= kBatchedMaxM && K > 0 && K <= kBatchedMaxK)
+            return launch_gemm_batched(X, M, packed, scales, N, K, Y, stream, num_cu);
+        // Few rows and K > N (few output tiles, long rows): the streaming
+        // kernel with the K groups split over waves.
+        if (M <= 64 && K > N && K <= kSkinnyMaxK)
+            return launch_gemm_skinny(X, M, packed, scales, N, K, Y, stream, num_cu);
+    }
+    return launch_tiled<false>(X, M, packed, scales, nullptr, N, K, Y, stream, num_cu, gshift);
 }
 
 hipError_t launch_gemm_mfma_asym(const uint16_t* X, int64_t M, const uint32_t* packed,
                                  const uint16_t* scales, const int16_t* zeros, int64_t N,
-                                 int64_t K, uint16_t* Y, hipStream_t stream, int num_cu) {
+                                 int64_t K, uint16_t* Y, hipStream_t stream, int num_cu,
+                                 int gshift) {
     // Batched decode: blocks own contiguous weight rows, X through LDS.
-    if (M <= kBatchedMaxM && K > 0 && K <= kBatchedMaxK)
+    if (gshift == 2 && M <= kBatchedMaxM && K > 0 && K <= kBatchedMaxK)
         return launch_gemm_batched_asym(X, M, packed, scales, zeros, N, K, Y, stream, num_cu);
-    return launch_tiled<true>(X, M, packed, scales, zeros, N, K, Y, stream, num_cu);
+    return launch_tiled<true>(X, M, packed, scales, zeros, N, K, Y, stream, num_cu, gshift);
 }
 
 }  // namespace w4a16

@@ -46,19 +46,28 @@ hipError_t launch_gemv_valu(const uint16_t* X, int64_t M, const uint32_t* packed
                             hipStream_t stream, int num_cu, int gshift = 2,
                             const int* perm = nullptr, const int16_t* zeros = nullptr);
 
-// MFMA path, any M.
+// MFMA path, any M.  gshift: log2(group / 32) as for launch_gemv_valu; the
+// streaming kernels (mfma4, batched, skinny) take group 128 (gshift 2),
+// every group runs on the tiled kernel.
 hipError_t launch_gemm_mfma(const uint16_t* X, int64_t M, const uint32_t* packed,
                             const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y,
-                            hipStream_t stream, int num_cu);
+                            hipStream_t stream, int num_cu, int gshift = 2);
 
-// MFMA path for asymmetric weights (zeros: int16 [N, K/128]), any M: the
+// MFMA path for asymmetric weights (zeros: int16 [N, K/group]), any M: the
 // tiled kernel with exact codes n - z and per-group fp32 scaling.
 // The tiled kernel addresses a block's rows with 32-bit offsets; rows
 // longer than kTiledMaxK elements run on the VALU path instead.
 constexpr int64_t kTiledMaxK = (int64_t)1 << 22;
 hipError_t launch_gemm_mfma_asym(const uint16_t* X, int64_t M, const uint32_t* packed,
                                  const uint16_t* scales, const int16_t* zeros, int64_t N,
-                                 int64_t K, uint16_t* Y, hipStream_t stream, int num_cu);
+                                 int64_t K, uint16_t* Y, hipStream_t stream, int num_cu,
+                                 int gshift = 2);
+
+// Activations in the act-order column order (gather_x.hip): Xp[m, j] =
+// X[m, perm[j]], 0 for an index outside [0, K).  X, Xp fp16 [M, K] (16-byte
+// aligned, not overlapping), perm device int32 [K] (16-byte aligned).
+hipError_t launch_gather_x(const uint16_t* X, int64_t M, int64_t K, const int* perm,
+                           uint16_t* Xp, hipStream_t stream, int num_cu);
 
 // MFMA GEMV for M <= 4 with x resident in LDS (gemv_mfma4.hip): the weight
 // stream of the VALU GEMV, products on v_mfma_f32_4x4x4_16b_f16.

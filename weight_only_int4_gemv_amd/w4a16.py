@@ -78,6 +78,11 @@ def library() -> ctypes.CDLL:
         lib.w4a16_quantize_asym.argtypes = [_p, _p, _i64, _i64, _i64, _p, _p, _p, _p]
         lib.w4a16_gemv_asym.argtypes = [_p, _p, _p, _p, _p, _i64, _i64, _i64, _p, _p]
         lib.w4a16_gemm_asym.argtypes = [_p, _i64, _p, _p, _p, _p, _i64, _i64, _i64, _p, _p]
+        lib.w4a16_linear_workspace_bytes.argtypes = [_i64, _i64, ctypes.c_int]
+        lib.w4a16_linear_workspace_bytes.restype = ctypes.c_size_t
+        lib.w4a16_linear.argtypes = [_p, _i64, _p, _p, _p, _p, _i64, _i64, _i64, _p, ctypes.c_int,
+                                     _p, ctypes.c_size_t, _p]
+        lib.w4a16_linear.restype = ctypes.c_int
         lib.w4a16_q4_0_bytes.argtypes = [_i64, _i64]
         lib.w4a16_q4_0_bytes.restype = ctypes.c_size_t
         lib.w4a16_quantize_q4_0.argtypes = [_p, _i64, _i64, _p, _p]
@@ -243,38 +248,80 @@ def gemv(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,
 
 def gemm(X: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, algo=None,
          Y: torch.Tensor = None, perm: torch.Tensor = None) -> torch.Tensor:
-    """X fp16 [M, K] -> Y fp16 [M, N].  algo: None/'auto', 'valu' or 'mfma'
-    ('mfma' needs group 128 and no perm).  perm: act-order column order
-    (int32 [K]), run on the VALU path."""
-    lib = library()
+    """X fp16 [M, K] -> Y fp16 [M, N].  algo: None/'auto', 'valu' or 'mfma'.
+    perm: act-order column order (int32 [K]); Y = X[:, perm] . Ŵᵀ."""
     N, K, group = _weights(packed, scales)
+    if algo not in _ALGOS:
+        raise ValueError("algo must be one of %s" % sorted(k for k in _ALGOS if k))
+    if group == W4A16_GROUP and perm is None:
+        lib = library()
+        X, Y, M = _rows(X, K, N, Y)
+        st = lib.w4a16_gemm_ex(X.data_ptr(), M, packed.data_ptr(), scales.data_ptr(), N, K,
+                               Y.data_ptr(), _ALGOS[algo], _stream())
+        _check("w4a16_gemm", st)
+        return Y
+    if algo in (None, "auto"):
+        lib = library()
+        X, Y, M = _rows(X, K, N, Y)
+        if perm is not None:
+            _perm(perm, K)
+            if group != W4A16_GROUP:
+                return linear(X, packed, scales, perm=perm, Y=Y)
+            st = lib.w4a16_gemm_perm(X.data_ptr(), M, perm.data_ptr(), packed.data_ptr(),
+                                     scales.data_ptr(), N, K, Y.data_ptr(), _stream())
+        else:
+            st = lib.w4a16_gemm_g(X.data_ptr(), M, packed.data_ptr(), scales.data_ptr(), N, K,
+                                  group, Y.data_ptr(), _stream())
+        _check("w4a16_gemm", st)
+        return Y
+    return linear(X, packed, scales, perm=perm, algo=algo, Y=Y)
+
+
+def _rows(X: torch.Tensor, K: int, N: int, Y: torch.Tensor):
     _need(X, "X", torch.float16, 2)
     M = X.shape[0]
     if X.shape[1] != K:
         raise ValueError("X has %d columns, K = %d" % (X.shape[1], K))
-    if algo not in _ALGOS:
-        raise ValueError("algo must be one of %s" % sorted(k for k in _ALGOS if k))
     if Y is None:
         Y = torch.empty((M, N), dtype=torch.float16, device=X.device)
     _need(Y, "Y", torch.float16, 2)
     if tuple(Y.shape) != (M, N):
         raise ValueError("Y shape %s, want %s" % (tuple(Y.shape), (M, N)))
+    return X, Y, M
+
+
+def linear_workspace(M: int, K: int, device="cuda") -> torch.Tensor:
+    """Workspace for linear() with a perm (the act-order copy of X): uint8
+    of w4a16_linear_workspace_bytes(M, K, 1) bytes."""
+    n = library().w4a16_linear_workspace_bytes(M, K, 1)
+    return torch.empty(max(int(n), 1), dtype=torch.uint8, device=device)
+
+
+def linear(X: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,
+           zeros: torch.Tensor = None, perm: torch.Tensor = None, algo=None,
+           Y: torch.Tensor = None, workspace: torch.Tensor = None) -> torch.Tensor:
+    """The linear layer with every option (w4a16_linear): group from the
+    scales' shape, asymmetric weights when zeros is given, act order when
+    perm is given; algo None/'auto', 'valu' or 'mfma'; workspace from
+    linear_workspace() (optional)."""
+    lib = library()
+    N, K, group = _weights(packed, scales)
+    if algo not in _ALGOS:
+        raise ValueError("algo must be one of %s" % sorted(k for k in _ALGOS if k))
+    if zeros is not None:
+        _zeros(zeros, scales)
     if perm is not None:
         _perm(perm, K)
-        if group != W4A16_GROUP or algo == "mfma":
-            raise ValueError("act order takes group %d and the VALU path" % W4A16_GROUP)
-        st = lib.w4a16_gemm_perm(X.data_ptr(), M, perm.data_ptr(), packed.data_ptr(),
-                                 scales.data_ptr(), N, K, Y.data_ptr(), _stream())
-    elif group == W4A16_GROUP:
-        st = lib.w4a16_gemm_ex(X.data_ptr(), M, packed.data_ptr(), scales.data_ptr(), N, K,
-                               Y.data_ptr(), _ALGOS[algo], _stream())
-    else:
-        if algo == "mfma":
-            raise ValueError("algo 'mfma' needs group %d, the weights have group %d"
-                             % (W4A16_GROUP, group))
-        st = lib.w4a16_gemm_g(X.data_ptr(), M, packed.data_ptr(), scales.data_ptr(), N, K,
-                              group, Y.data_ptr(), _stream())
-    _check("w4a16_gemm", st)
+    X, Y, M = _rows(X, K, N, Y)
+    ws, ws_bytes = None, 0
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, 1)
+        ws, ws_bytes = workspace.data_ptr(), workspace.numel()
+    st = lib.w4a16_linear(X.data_ptr(), M, perm.data_ptr() if perm is not None else None,
+                          packed.data_ptr(), scales.data_ptr(),
+                          zeros.data_ptr() if zeros is not None else None, N, K, group,
+                          Y.data_ptr(), _ALGOS[algo], ws, ws_bytes, _stream())
+    _check("w4a16_linear", st)
     return Y
 
 
@@ -376,21 +423,15 @@ def gemv_asym(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,
 
 def gemm_asym(X: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,
               zeros: torch.Tensor, Y: torch.Tensor = None,
-              perm: torch.Tensor = None) -> torch.Tensor:
+              perm: torch.Tensor = None, algo=None) -> torch.Tensor:
     """Asymmetric weights: X fp16 [M, K] -> Y fp16 [M, N] (VALU path for
-    small M, other group sizes and perm; matrix cores otherwise)."""
+    small M, matrix cores above; algo forces one as for gemm)."""
+    if algo not in (None, "auto"):
+        return linear(X, packed, scales, zeros=zeros, perm=perm, algo=algo, Y=Y)
     lib = library()
     N, K, group = _weights(packed, scales)
     _zeros(zeros, scales)
-    _need(X, "X", torch.float16, 2)
-    M = X.shape[0]
-    if X.shape[1] != K:
-        raise ValueError("X has %d columns, K = %d" % (X.shape[1], K))
-    if Y is None:
-        Y = torch.empty((M, N), dtype=torch.float16, device=X.device)
-    _need(Y, "Y", torch.float16, 2)
-    if tuple(Y.shape) != (M, N):
-        raise ValueError("Y shape %s, want %s" % (tuple(Y.shape), (M, N)))
+    X, Y, M = _rows(X, K, N, Y)
     if perm is not None:
         _perm(perm, K)
     st = lib.w4a16_gemm_asym(X.data_ptr(), M, perm.data_ptr() if perm is not None else None,
