@@ -87,10 +87,12 @@ def planted_asym(N, K, seed):
 
 @pytest.mark.parametrize("group", GROUPS)
 @pytest.mark.parametrize("M", [3, 16, 33, 64, 130])
-@pytest.mark.parametrize("N,K", [(300, 1536), (1001, 4096), (64, 14336)])
+@pytest.mark.parametrize("N,K", [(300, 1536), (1001, 4096), (64, 14336), (9000, 1024)])
 def test_mfma_group_sizes(w4, orc, group, M, N, K):
-    """Tiled kernel at every tile family (16, 32, 64 rows with waves over K,
-    128-row prefill blocks) with the group's scale per 32-element chunk."""
+    """Tiled kernel at every tile family (16, 32, 64 rows with eight waves
+    over K for few columns, two across and four over K for N >= 32 per
+    compute unit; 128-row prefill blocks) with the group's scale per
+    32-element chunk."""
     say("mfma %s M=%d N=%d K=%d" % (gname(group), M, N, K))
     W = inputs.weight(N, K, seed=[81, sk(group), N, K])
     packed, scales = orc.quantize(W, group=og(group, K))
@@ -140,10 +142,11 @@ def test_mfma_group_one_hot_exact(w4, orc, group):
 
 @pytest.mark.parametrize("group", [32, 64, 128, 256, PC])
 @pytest.mark.parametrize("M", [3, 16, 40, 130])
-def test_mfma_asym_groups_planted(w4, orc, group, M):
+@pytest.mark.parametrize("N,K", [(200, 2048), (8300, 1024)])
+def test_mfma_asym_groups_planted(w4, orc, group, M, N, K):
     """Asymmetric weights on the matrix cores at every group, with planted
-    rows that send their blocks down the exact slow loop."""
-    N, K = 200, 2048
+    rows that send their blocks down the exact slow loop (few and many
+    column tiles)."""
     say("mfma asym %s M=%d" % (gname(group), M))
     W = planted_asym(N, K, [84, sk(group)])
     packed, scales, zeros = orc.quantize_asym(W, group=og(group, K))

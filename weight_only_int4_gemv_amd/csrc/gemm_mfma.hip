@@ -61,8 +61,11 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_mfma_kernel(
     constexpr int BN = 16 * TN * WN;
     constexpr int A_VECS = WK * BM * 16;              // uint4 of A per stage (WK groups)
     constexpr int A_PER_THREAD = A_VECS / NT;
-    constexpr int A_PER_SLOT = BM * 16 / NT;          // consecutive stage vectors of one group
-    static_assert(A_VECS % NT == 0 && (BM * 16) % NT == 0, "A staging must tile the block");
+    static_assert(A_VECS % NT == 0, "A staging must tile the block");
+    // Stage vector v = i NT + thread is (group slot v / (16 BM), row, 8-block);
+    // when a slot spans whole passes of the block, vector i's slot is the
+    // same for every thread.
+    constexpr bool SLOT_UNIFORM = (BM * 16) % NT == 0;
     constexpr int LDS_STAGE = WK * BM * kLdaVec;      // uint4 per A buffer
     extern __shared__ uint4 lds[];                    // [2][WK][BM][kLdaVec]
 
@@ -92,15 +95,19 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_mfma_kernel(
     // rows of codes below 2^31 bytes).  Rows past M or N are clamped to the
     // last row: they only feed outputs that are never stored.
     uint32_t a_off[A_PER_THREAD], a_lds[A_PER_THREAD];
+    int a_slot[A_PER_THREAD];
 #pragma unroll
     for (int i = 0; i < A_PER_THREAD; ++i) {
-        const int slot = i / A_PER_SLOT;
-        const int rem = (i % A_PER_SLOT) * NT + (int)threadIdx.x;
+        constexpr int per_slot = SLOT_UNIFORM ? (BM * 16) / NT : 1;   // vectors i per slot
+        const int v = i * NT + (int)threadIdx.x;
+        const int slot = SLOT_UNIFORM ? i / per_slot : v / (BM * 16);
+        const int rem = SLOT_UNIFORM ? (i % per_slot) * NT + (int)threadIdx.x : v % (BM * 16);
         const int row = rem >> 4;
         const int blk = rem & 15;
         const uint32_t m = (uint32_t)(min(m_blk + row, M - 1) - m_blk);
         a_off[i] = m * (uint32_t)K * 2u + (uint32_t)(slot * 256 + blk * 16);
         a_lds[i] = (uint32_t)((slot * BM + row) * kLdaVec + blk);
+        a_slot[i] = slot;
     }
     uint32_t b_off[TN], s_off[TN];
 #pragma unroll
@@ -130,7 +137,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_mfma_kernel(
         const int soff = step * (WK * 256);
 #pragma unroll
         for (int i = 0; i < A_PER_THREAD; ++i)
-            if (step * WK + i / A_PER_SLOT < ngroups) {
+            if (step * WK + a_slot[i] < ngroups) {
                 const v4u v = __builtin_amdgcn_raw_buffer_load_b128(xr, a_off[i], soff, 0);
                 regs[i] = make_uint4(v.x, v.y, v.z, v.w);
             }
@@ -231,13 +238,11 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_mfma_kernel(
                 } else if (gshift >= 2) {
                     half8_t bq[TN][4];
                     float sf[TN], cf[TN];
-                    bool wide = false;
 #pragma unroll
                     for (int tn = 0; tn < TN; ++tn) {
                         const ZeroBias zb = zero_bias(cur.z[tn]);
                         sf[tn] = f16_bits_to_f32((uint16_t)cur.s[tn]);
-                        cf[tn] = sf[tn] * (float)(zb.zc - cur.z[tn]);
-                        wide |= zb.zc != cur.z[tn];
+                        cf[tn] = sf[tn] * (float)(zb.zc - cur.z[tn]);   // 0 for |z| <= 1000
                         const uint32_t words[4] = {cur.w[tn].x, cur.w[tn].y, cur.w[tn].z,
                                                    cur.w[tn].w};
 #pragma unroll
@@ -251,11 +256,15 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_mfma_kernel(
                     constexpr int TH = TM > 1 ? TM / 2 : 1;
                     const _Float16 one = (_Float16)1.0f;
                     const half8_t ones = {one, one, one, one, one, one, one, one};
-                    const bool any_wide = __any(wide);
+                    // The activation sums are formed in every wave, also where
+                    // no zero point exceeds +-1000 (cf = 0 there): an MFMA
+                    // skipped by a branch would leave the MFMA results read
+                    // below fewer wait states after it than the matrix core
+                    // needs on the path that skips it.
 #pragma unroll
                     for (int t0 = 0; t0 < TM; t0 += TH) {
                         // d: the group's products per row tile; xs: its
-                        // activation sums (only used where |z| > 1000)
+                        // activation sums
                         float4_t d[TH][TN], xs[TH];
 #pragma unroll
                         for (int kk = 0; kk < 4; ++kk) {
@@ -269,11 +278,9 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_mfma_kernel(
                                         af, bq[tn][kk],
                                         kk == 0 ? (float4_t){0.f, 0.f, 0.f, 0.f} : d[th][tn], 0,
                                         0, 0);
-                                if (any_wide)
-                                    xs[th] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                                        af, ones,
-                                        kk == 0 ? (float4_t){0.f, 0.f, 0.f, 0.f} : xs[th], 0, 0,
-                                        0);
+                                xs[th] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                                    af, ones, kk == 0 ? (float4_t){0.f, 0.f, 0.f, 0.f} : xs[th],
+                                    0, 0, 0);
                             }
                         }
 #pragma unroll
@@ -281,11 +288,10 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_mfma_kernel(
 #pragma unroll
                             for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
-                                for (int r = 0; r < 4; ++r) {
-                                    float v = fmaf(sf[tn], d[th][tn][r], acc[t0 + th][tn][r]);
-                                    if (any_wide) v = fmaf(cf[tn], xs[th][r], v);
-                                    acc[t0 + th][tn][r] = v;
-                                }
+                                for (int r = 0; r < 4; ++r)
+                                    acc[t0 + th][tn][r] =
+                                        fmaf(cf[tn], xs[th][r],
+                                             fmaf(sf[tn], d[th][tn][r], acc[t0 + th][tn][r]));
                     }
                 } else {
                     // Groups of 32 or 64: the four 32-element chunks of a
@@ -300,13 +306,11 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_mfma_kernel(
                     const uint4* abase_t = abase - 3 * j;      // vector j of the row
                     half8_t bq[TN][4];
                     float sk[TN][4], ck[TN][4];
-                    bool wide = false;
 #pragma unroll
                     for (int tn = 0; tn < TN; ++tn) {
                         const ZeroBias zown = zero_bias(cur.z[tn]);
                         const float sown = f16_bits_to_f32((uint16_t)cur.s[tn]);
                         const float cown = sown * (float)(zown.zc - cur.z[tn]);
-                        wide |= zown.zc != cur.z[tn];
                         const uint32_t words[4] = {cur.w[tn].x, cur.w[tn].y, cur.w[tn].z,
                                                    cur.w[tn].w};
 #pragma unroll
@@ -329,37 +333,42 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_mfma_kernel(
                     }
                     const _Float16 one = (_Float16)1.0f;
                     const half8_t ones = {one, one, one, one, one, one, one, one};
-                    const bool any_wide = __any(wide);
-                    const int last = (1 << gshift) - 1;   // chunks per group - 1
+                    // LAST: chunks per group - 1 (0 for group 32, 1 for 64), a
+                    // constant in each copy so that no branch separates an
+                    // MFMA from the fold that reads it (as above).
+                    auto groups = [&](auto last_c) __attribute__((always_inline)) {
+                        constexpr int LAST = decltype(last_c)::value;
 #pragma unroll
-                    for (int tm = 0; tm < TM; ++tm) {
-                        float4_t d[TN], xs;
+                        for (int tm = 0; tm < TM; ++tm) {
+                            float4_t d[TN], xs;
 #pragma unroll
-                        for (int kk = 0; kk < 4; ++kk) {
-                            const bool first = (kk & last) == 0;
-                            const half8_t af =
-                                __builtin_bit_cast(half8_t, abase_t[tm * 16 * kLdaVec + 4 * kk]);
-#pragma unroll
-                            for (int tn = 0; tn < TN; ++tn)
-                                d[tn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                                    af, bq[tn][kk], first ? (float4_t){0.f, 0.f, 0.f, 0.f} : d[tn],
-                                    0, 0, 0);
-                            if (any_wide)
-                                xs = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                                    af, ones, first ? (float4_t){0.f, 0.f, 0.f, 0.f} : xs, 0, 0,
-                                    0);
-                            if ((kk & last) == last) {
+                            for (int kk = 0; kk < 4; ++kk) {
+                                constexpr float4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+                                const bool first = (kk & LAST) == 0;
+                                const half8_t af = __builtin_bit_cast(
+                                    half8_t, abase_t[tm * 16 * kLdaVec + 4 * kk]);
 #pragma unroll
                                 for (int tn = 0; tn < TN; ++tn)
+                                    d[tn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                                        af, bq[tn][kk], first ? zero4 : d[tn], 0, 0, 0);
+                                xs = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                                    af, ones, first ? zero4 : xs, 0, 0, 0);
+                                if ((kk & LAST) == LAST) {
 #pragma unroll
-                                    for (int r = 0; r < 4; ++r) {
-                                        float v = fmaf(sk[tn][kk], d[tn][r], acc[tm][tn][r]);
-                                        if (any_wide) v = fmaf(ck[tn][kk], xs[r], v);
-                                        acc[tm][tn][r] = v;
-                                    }
+                                    for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+                                        for (int r = 0; r < 4; ++r)
+                                            acc[tm][tn][r] = fmaf(
+                                                ck[tn][kk], xs[r],
+                                                fmaf(sk[tn][kk], d[tn][r], acc[tm][tn][r]));
+                                }
                             }
                         }
-                    }
+                    };
+                    if (gshift == 0)
+                        groups(std::integral_constant<int, 0>{});
+                    else
+                        groups(std::integral_constant<int, 1>{});
                 }
             };
             mma(clamp);
@@ -550,17 +559,17 @@ hipError_t launch_tiled(const uint16_t* X, int64_t M, const uint32_t* packed,
                                 ASYM ? zeros : nullptr);
 #define W4A16_TILED(TM, TN, WM, WN, WK) \
     launch_mfma_t<TM, TN, WM, WN, WK, ASYM>(X, M, packed, scales, N, K, Y, stream, gshift, zeros)
-    // Few rows: one 16- or 32-row tile, waves split K; enough column tiles
-    // to give every compute unit work.
-    if (M <= 16) {
-        if (N >= (int64_t)64 * num_cu) return W4A16_TILED(1, 2, 1, 1, 4);
-        return W4A16_TILED(1, 1, 1, 1, 4);
-    }
-    if (M <= 32) {
-        if (N >= (int64_t)64 * num_cu) return W4A16_TILED(2, 2, 1, 1, 4);
-        return W4A16_TILED(2, 1, 1, 1, 4);
-    }
-    if (M <= 64) return W4A16_TILED(2, 2, 2, 2, 1);
+    // Few rows: 16, 32 or 64 rows of X per block and waves splitting K.
+    // With many columns (N >= 32 per compute unit) two waves across 32
+    // columns and four over K; with few (the down projections, K > N) one
+    // 16-column tile per block and eight waves over K, so that each wave
+    // walks fewer groups (14336 x 4096 at group 32, M = 8: 17.8 us against
+    // 26.9 us with four waves; M = 64: 33 us against 106 us with 64 x 64
+    // blocks).
+    const bool wide = N >= (int64_t)32 * num_cu;
+    if (M <= 16) return wide ? W4A16_TILED(1, 1, 1, 2, 4) : W4A16_TILED(1, 1, 1, 1, 8);
+    if (M <= 32) return wide ? W4A16_TILED(2, 1, 1, 2, 4) : W4A16_TILED(2, 1, 1, 1, 8);
+    if (M <= 64) return wide ? W4A16_TILED(2, 1, 1, 2, 4) : W4A16_TILED(2, 2, 1, 1, 8);
     // Prefill: when 128 x 128 tiles fill the compute units, 128 x 256 block
     // tiles (eight 16-row by two 16-column tiles per wave, eight waves across
     // N: each staged X tile serves 256 columns; M = 512 on 4096 x 14336 at
