@@ -279,6 +279,14 @@ def secondary(torch, w4a16, inputs, dev, stream, main_workload="llama3-8b-sweep"
                 "gemv_us": round(us, 3), "gemv_GB/s": round(b / (us * 1e-6) / 1e9, 1),
                 "gemv_frac_of_hbm_peak": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                 "quantize_us": round(qus, 2), "quantize_GB/s": round(qb / (qus * 1e-6) / 1e9, 1)}
+            # batched decode and prefill at this group (the automatic choice:
+            # matrix cores above two rows)
+            for M in (16, 512):
+                X = torch.from_numpy(inputs.activation(M, K, seed=[8, M])).to(dev)
+                Y = torch.empty((M, N), dtype=torch.float16, device=dev)
+                mus = timed(lambda: [w4a16.gemm(X, p, s_, Y=Y) for p, s_ in copies]) / len(copies)
+                groups[label]["M=%d_us" % M] = round(mus, 2)
+                groups[label]["M=%d_TFLOP/s" % M] = round(2 * M * N * K / (mus * 1e-6) / 1e12, 1)
             del copies
         out["group_sizes_%dx%d" % (K, N)] = groups
         del Wg
@@ -299,8 +307,19 @@ def secondary(torch, w4a16, inputs, dev, stream, main_workload="llama3-8b-sweep"
             b = gemv_bytes(N, K) + 4 * K
             act["%dx%d" % (K, N)] = {"plain_us": round(plain, 3), "perm_us": round(gather, 3),
                                      "perm_GB/s": round(b / (gather * 1e-6) / 1e9, 1)}
+            # batched decode and prefill: X gathered in the order perm into a
+            # workspace, then the matrix-core GEMM (w4a16_linear; graph-captured)
+            for M in (16, 512):
+                X = torch.from_numpy(inputs.activation(M, K, seed=[9, M, K])).to(dev)
+                Y = torch.empty((M, N), dtype=torch.float16, device=dev)
+                ws = w4a16.linear_workspace(M, K, device=dev)
+                pus = timed(lambda: [w4a16.linear(X, p, s_, perm=perm, Y=Y, workspace=ws)
+                                     for p, s_ in copies]) / len(copies)
+                qus = timed(lambda: [w4a16.gemm(X, p, s_, Y=Y) for p, s_ in copies]) / len(copies)
+                act["%dx%d" % (K, N)]["M=%d_perm_us" % M] = round(pus, 2)
+                act["%dx%d" % (K, N)]["M=%d_plain_us" % M] = round(qus, 2)
             del copies
-        out["act_order_m1"] = act
+        out["act_order"] = act
 
     if want("asym"):
         # asymmetric INT4: M = 1 GEMV (zero points streamed beside the scales)
@@ -339,7 +358,7 @@ def secondary(torch, w4a16, inputs, dev, stream, main_workload="llama3-8b-sweep"
                 row["M=%d_TFLOP/s" % M] = round(2 * M * N * K / (a_us * 1e-6) / 1e12, 1)
             asym["%dx%d" % (K, N)] = row
             del copies, sym, Wd
-        out["asymmetric_m1"] = asym
+        out["asymmetric"] = asym
 
     if want("q4_0"):
         # Q4_0 blocks (scale in front of each 32-element block) against the split
