@@ -248,13 +248,14 @@ def secondary(torch, w4a16, inputs, dev, stream, main_workload="llama3-8b-sweep"
         for (K, N) in [(4096, 14336), (14336, 4096), (8192, 28672)]:
             p0, s0 = weights_for(K, N)
             copies = weight_copies(p0, s0)                              # >= 600 MB of weights
-            X = torch.from_numpy(inputs.activation(512, K, seed=[7, K])).to(dev)
-            Y = torch.empty((512, N), dtype=torch.float16, device=dev)
-            us = timed(lambda: [w4a16.gemm(X, p, s_, Y=Y) for p, s_ in copies]) / len(copies)
-            tf = 2 * 512 * N * K / (us * 1e-6) / 1e12
-            prefill["%dx%d M=512" % (K, N)] = {"us": round(us, 2), "TFLOP/s": round(tf, 1),
-                                               "frac_of_mfma_f16_peak":
-                                                   round(tf / MFMA_F16_PEAK_TFLOPS, 4)}
+            for M in (512, 256, 128):
+                X = torch.from_numpy(inputs.activation(M, K, seed=[7, K])).to(dev)
+                Y = torch.empty((M, N), dtype=torch.float16, device=dev)
+                us = timed(lambda: [w4a16.gemm(X, p, s_, Y=Y) for p, s_ in copies]) / len(copies)
+                tf = 2 * M * N * K / (us * 1e-6) / 1e12
+                prefill["%dx%d M=%d" % (K, N, M)] = {"us": round(us, 2), "TFLOP/s": round(tf, 1),
+                                                     "frac_of_mfma_f16_peak":
+                                                         round(tf / MFMA_F16_PEAK_TFLOPS, 4)}
             del copies
         out["prefill"] = prefill
 

@@ -333,10 +333,13 @@ def test_workload_size_whole_output(w4, orc, M, K, N, algo):
         len(bad), Y.size, bad[0], Y[tuple(bad[0])], Yref[tuple(bad[0])], tol[tuple(bad[0])])
 
 
-@pytest.mark.parametrize("M,N,K", [(520, 6600, 384), (129, 33000, 256), (512, 32776, 128)])
+@pytest.mark.parametrize("M,N,K", [(520, 6600, 384), (129, 33000, 256), (512, 32776, 128),
+                                   (250, 14400, 256), (100, 14400, 384), (70, 3000, 384),
+                                   (300, 4100, 1152)])
 def test_prefill_wide_tiles_ragged(w4, orc, M, N, K):
-    """Enough 128-row by 128-column tiles to fill the compute units, so the
-    128 x 256 block tiles run: M and N ragged against them, few groups, and
+    """Every prefill block tile on 256 compute units: 128 x 256 blocks (the
+    first three shapes), 128 x 128 and 64 x 128 blocks with two waves over
+    K, and 64 x 64 blocks; M and N ragged against them, few groups, and
     canary words around Y that must survive (no store outside Y)."""
     _, packed, scales = layer(N, K, (31, M, N, K))
     X = inputs.activation(M, K, seed=[32, M, N, K])
