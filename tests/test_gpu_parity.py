@@ -838,12 +838,14 @@ def test_linear_asym_batched_wave_grids(w4, orc, M, N, K):
     check_linear_asym(w4, orc, M, N, K, 128, [48, M, N, K])
 
 
-@pytest.mark.parametrize("M,N,K", [(512, 8192, 1024), (300, 11000, 640)])
+@pytest.mark.parametrize("M,N,K", [(512, 8192, 1024), (300, 11000, 640), (250, 7200, 384),
+                                   (200, 3000, 512)])
 def test_linear_asym_prefill_fp16_weights(w4, orc, M, N, K):
     """Prefill-sized asymmetric products whose blocks all take the fp16
     weight copy (skewed layer-like weights: scales below 64, zero points in
-    [0, 15]) on the tiled kernel's wide-grid branch (enough 128-row tiles to
-    fill the compute units), M and N ragged in the second case."""
+    [0, 15]) on each prefill block tile (128 x 128 blocks when they fill the
+    compute units, 128 x 64 and 64 x 64 blocks with two waves over K), M and
+    N ragged."""
     check_linear_asym(w4, orc, M, N, K, 128, [51, M, N, K], plant=False)
 
 

@@ -570,27 +570,27 @@ hipError_t launch_tiled(const uint16_t* X, int64_t M, const uint32_t* packed,
     if (M <= 16) return wide ? W4A16_TILED(1, 1, 1, 2, 4) : W4A16_TILED(1, 1, 1, 1, 8);
     if (M <= 32) return wide ? W4A16_TILED(2, 1, 1, 2, 4) : W4A16_TILED(2, 1, 1, 1, 8);
     if (M <= 64) return wide ? W4A16_TILED(2, 1, 1, 2, 4) : W4A16_TILED(2, 2, 1, 1, 8);
-    // Prefill.  Asymmetric weights: 128 x 16 wave tiles (the exact slow copy
-    // of the loop does not fit two waves per SIMD with 128 x 32 tiles), in
-    // 128 x 128 blocks when they fill the compute units, else 128 x 64
-    // blocks with two waves over K.
+    // Prefill: the largest block tile that still gives about one block per
+    // compute unit (7/8 of them).
+    auto fills = [&](int64_t bm, int64_t bn) {
+        return ((M + bm - 1) / bm) * ((N + bn - 1) / bn) * 8 >= (int64_t)num_cu * 7;
+    };
     if constexpr (ASYM) {
-        const int64_t tiles128 = ((M + 127) / 128) * ((N + 127) / 128);
-        if (tiles128 >= num_cu) return W4A16_TILED(8, 1, 1, 8, 1);
-        return W4A16_TILED(8, 1, 1, 4, 2);
+        // Asymmetric weights: 16-column wave tiles (the exact slow copy of the
+        // loop does not fit two waves per SIMD with 32 columns): 128 x 128
+        // blocks, 128 x 64 and 64 x 64 blocks with two waves over K.
+        if (fills(128, 128)) return W4A16_TILED(8, 1, 1, 8, 1);
+        if (fills(128, 64)) return W4A16_TILED(8, 1, 1, 4, 2);
+        return W4A16_TILED(4, 1, 1, 4, 2);
     } else {
-        // The largest block tile that still gives about one block per
-        // compute unit (7/8 of them): 128 x 256 (eight waves across N, 128 x
-        // 32 wave tiles), 128 x 128 and 64 x 128 (four waves across N, two
-        // over K), else 64 x 64 (64 x 16 wave tiles, four across N, two
-        // over K).  Measured at M = 512 / 256 / 128 (us): 4096 x 14336
-        // 69 / 45 / 29, 14336 x 4096 95 / 68 / 66, 8192 x 28672 264 / 131 /
-        // 87, 18944 x 3584 120 / 87 / 88, against 67 / 59 / 34, 107 / 99 /
-        // 98, 261 / 131 / 117 and 132 / 130 / 131 with the earlier choice
-        // between 128 x 256 and 128 x 64 blocks.
-        auto fills = [&](int64_t bm, int64_t bn) {
-            return ((M + bm - 1) / bm) * ((N + bn - 1) / bn) * 8 >= (int64_t)num_cu * 7;
-        };
+        // 128 x 256 (eight waves across N, 128 x 32 wave tiles), 128 x 128
+        // and 64 x 128 (four waves across N, two over K), else 64 x 64 (64 x
+        // 16 wave tiles, four across N, two over K).  Measured at M = 512 /
+        // 256 / 128 (us): 4096 x 14336 69 / 45 / 29, 14336 x 4096 95 / 68 /
+        // 66, 8192 x 28672 264 / 131 / 87, 18944 x 3584 120 / 87 / 88,
+        // against 67 / 59 / 34, 107 / 99 / 98, 261 / 131 / 117 and 132 / 130
+        // / 131 with the earlier choice between 128 x 256 and 128 x 64
+        // blocks.
         if (fills(128, 256)) return W4A16_TILED(8, 2, 1, 8, 1);
         if (fills(128, 128)) return W4A16_TILED(8, 2, 1, 4, 2);
         if (fills(64, 128)) return W4A16_TILED(4, 2, 1, 4, 2);
