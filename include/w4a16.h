@@ -137,9 +137,14 @@ int w4a16_gemm_ex(const uint16_t* X, int64_t M, const uint32_t* packed, const ui
  * w4a16_gemm_workspace_bytes reports a non-zero size for, blocks own more
  * rows and one slice of K each, store fp32 partial tiles in the workspace,
  * and the last slice of each row block to finish adds them in slice order
- * (deterministic) and writes Y.  Other shapes run exactly as w4a16_gemm and
- * ignore the workspace.  Same accuracy bound as w4a16_gemm; the sum order
- * differs, so results are not bit-identical to it.
+ * (deterministic) and writes Y.  Prefill ([BENCH] §一/§二, 512-token prompt)
+ * on long-K shapes (more than 64 rows, K > N, too few 128 x 256 output tiles
+ * for the compute units) splits K over blocks the same way, with 128 x 256
+ * partial tiles (w4a16_gemm keeps these shapes unsplit, so that it never
+ * needs memory of its own).  Other shapes run exactly as w4a16_gemm and
+ * ignore the workspace.  Same accuracy
+ * bound as w4a16_gemm; the sum order of split shapes differs, so their
+ * results are not bit-identical to the unsplit kernel's.
  *   workspace  DEVICE, 256-byte aligned, at least
  *              w4a16_gemm_workspace_bytes(M, N, K) bytes, owned by the caller,
  *              all zero before its first use; every call leaves its counters

@@ -115,6 +115,20 @@ int64_t groups_per_row(int64_t K, int64_t group) {
 
 int status_of(hipError_t e) { return e == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH; }
 
+// The K split over blocks of the prefill kernel (w4a16_gemm_ws): symmetric
+// weights, more than 64 rows, K > N (long rows, few output tiles).
+w4a16::TiledSplit tiled_plan(int64_t M, int64_t N, int64_t K, int num_cu, bool asym) {
+    w4a16::TiledSplit none{};
+    none.ksplit = 1;
+    if (asym || K <= N) return none;
+    return w4a16::plan_tiled_split(M, N, K, num_cu);
+}
+
+bool stream_capturing(hipStream_t s) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    return hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone;
+}
+
 // perm: NULL, or the act-order column order (device int32 [K]).  zeros
 // (asym): the int16 zero points of asymmetric weights, [N, K/group].
 int linear(const uint16_t* X, int64_t M, const uint32_t* packed, const uint16_t* scales,
@@ -163,11 +177,9 @@ int linear(const uint16_t* X, int64_t M, const uint32_t* packed, const uint16_t*
     // caller's workspace, else allocated on the stream from the library's
     // pool; without a workspace a stream under graph capture keeps the VALU
     // path, which gathers x itself and allocates nothing.
-    bool capturing = false;
-    if (with_perm && K > 0 && algo != W4A16_ALGO_VALU && workspace == nullptr) {
-        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-        capturing = hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone;
-    }
+    const bool capturing =
+        with_perm && K > 0 && algo != W4A16_ALGO_VALU && workspace == nullptr &&
+        stream_capturing(s);
     const bool valu = algo == W4A16_ALGO_VALU || (algo == W4A16_ALGO_AUTO && M <= kValuMaxM) ||
                       capturing;
     if (valu)
@@ -383,7 +395,9 @@ size_t w4a16_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     int num_cu = 0;
     if (current_device(&num_cu) != W4A16_OK) return 0;
     const w4a16::BatchedSplit p = ws_plan(M, N, K, num_cu);
-    return p.ksplit > 1 ? p.workspace_bytes : 0;
+    if (p.ksplit > 1) return p.workspace_bytes;
+    const w4a16::TiledSplit t = tiled_plan(M, N, K, num_cu, false);
+    return t.ksplit > 1 ? t.workspace_bytes : 0;
 }
 
 int w4a16_gemm_ws(const uint16_t* X, int64_t M, const uint32_t* packed, const uint16_t* scales,
@@ -398,19 +412,25 @@ int w4a16_gemm_ws(const uint16_t* X, int64_t M, const uint32_t* packed, const ui
     st = current_device(&num_cu);
     if (st != W4A16_OK) return st;
     const w4a16::BatchedSplit plan = ws_plan(M, N, K, num_cu);
-    if (plan.ksplit < 2) return w4a16_gemm(X, M, packed, scales, N, K, Y, stream);
-    if (!workspace || workspace_bytes < plan.workspace_bytes) return W4A16_ERR_INVALID_ARG;
+    const w4a16::TiledSplit tplan = tiled_plan(M, N, K, num_cu, false);
+    if (plan.ksplit < 2 && tplan.ksplit < 2) return w4a16_gemm(X, M, packed, scales, N, K, Y, stream);
+    const size_t need = plan.ksplit > 1 ? plan.workspace_bytes : tplan.workspace_bytes;
+    if (!workspace || workspace_bytes < need) return W4A16_ERR_INVALID_ARG;
     if (!aligned(X, 16) || !aligned(packed, 16) || !aligned(scales, 2) || !aligned(Y, 2) ||
         !aligned(workspace, 256))
         return W4A16_ERR_MISALIGNED;
     const size_t y_bytes = (size_t)M * N * 2, x_bytes = (size_t)M * K * 2;
     const size_t p_bytes = (size_t)N * K / 2, s_bytes = (size_t)N * (K / W4A16_GROUP) * 2;
-    const size_t w_bytes = plan.workspace_bytes;
+    const size_t w_bytes = need;
     if (overlap(Y, y_bytes, X, x_bytes) || overlap(Y, y_bytes, packed, p_bytes) ||
         overlap(Y, y_bytes, scales, s_bytes) || overlap(workspace, w_bytes, X, x_bytes) ||
         overlap(workspace, w_bytes, Y, y_bytes) || overlap(workspace, w_bytes, packed, p_bytes) ||
         overlap(workspace, w_bytes, scales, s_bytes))
         return W4A16_ERR_INVALID_ARG;
+    if (plan.ksplit < 2)
+        return status_of(w4a16::launch_gemm_tiled_split(X, M, packed, scales, N, K, Y,
+                                                        static_cast<hipStream_t>(stream), 2, tplan,
+                                                        workspace));
     return status_of(w4a16::launch_gemm_batched_split(X, M, packed, scales, N, K, Y,
                                                       static_cast<hipStream_t>(stream), plan,
                                                       workspace));

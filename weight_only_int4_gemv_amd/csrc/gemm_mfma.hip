@@ -48,14 +48,17 @@ namespace w4a16 {
 namespace {
 constexpr int kLdaHalfs = 136;             // staged A row: 128 halves + 8 pad (bank spread)
 constexpr int kLdaVec = kLdaHalfs / 8;     // in uint4
+constexpr int kCoherentSc1 = 16;           // cache policy: coherent at device scope (sc1)
 }  // namespace
 
-template <int TM, int TN, int WM, int WN, int WK, bool ASYM>
+template <int TM, int TN, int WM, int WN, int WK, bool ASYM, bool SPLIT>
 __global__ __launch_bounds__(WM * WN * WK * kWave)
 __attribute__((amdgpu_waves_per_eu(2))) void gemm_mfma_kernel(
     const uint16_t* __restrict__ X, int M, const uint4* __restrict__ packed,
     const uint16_t* __restrict__ scales, const int16_t* __restrict__ zeros,
-    uint16_t* __restrict__ Y, int N, int K, int gshift) {
+    uint16_t* __restrict__ Y, int N, int K, int gshift, int ksplit, int gps,
+    uint32_t* __restrict__ counters, float4_t* __restrict__ partials) {
+    static_assert(!SPLIT || WK == 1, "the K split sums whole block tiles");
     constexpr int NT = WM * WN * WK * kWave;
     constexpr int BM = 16 * TM * WM;
     constexpr int BN = 16 * TN * WN;
@@ -78,7 +81,10 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_mfma_kernel(
     const int j = lane >> 4;
     const int m_blk = blockIdx.y * BM;
     const int n_blk = blockIdx.x * BN;
-    const int ngroups = K >> 7;                       // 128-element steps of K
+    // K split over blocks (SPLIT): block z of a tile takes the groups
+    // [z gps, z gps + gps) of K (every slice holds at least one).
+    const int g_lo = SPLIT ? (int)blockIdx.z * gps : 0;
+    const int ngroups = SPLIT ? min(K >> 7, g_lo + gps) - g_lo : (K >> 7);   // 128-element steps
     const int nsteps = (ngroups + WK - 1) / WK;
     const uint32_t wrow = (uint32_t)K / 2;            // bytes per weight row
     // bytes per scale (and zero) row: one scale per 2^gshift chunks of 32
@@ -134,7 +140,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_mfma_kernel(
     // slot past the last group keeps its previous (finite) values; the B of
     // such a group is zero.
     auto load_a = [&](int step, uint4 (&regs)[A_PER_THREAD]) {
-        const int soff = step * (WK * 256);
+        const int soff = (g_lo + step * WK) * 256;
 #pragma unroll
         for (int i = 0; i < A_PER_THREAD; ++i)
             if (step * WK + a_slot[i] < ngroups) {
@@ -156,10 +162,11 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_mfma_kernel(
     auto load_b = [&](int step, BRegs& b) {
         const int g = step * WK + wk;
         if (g < ngroups) {
-            const int sg = gshift <= 2 ? g << (2 - gshift) : g >> (gshift - 2);
+            const int ga = g_lo + g;                     // group index along the whole row
+            const int sg = gshift <= 2 ? ga << (2 - gshift) : ga >> (gshift - 2);
 #pragma unroll
             for (int tn = 0; tn < TN; ++tn) {
-                const v4u v = __builtin_amdgcn_raw_buffer_load_b128(pr, b_off[tn], g * 64, 0);
+                const v4u v = __builtin_amdgcn_raw_buffer_load_b128(pr, b_off[tn], ga * 64, 0);
                 b.w[tn] = make_uint4(v.x, v.y, v.z, v.w);
                 b.s[tn] = __builtin_amdgcn_raw_buffer_load_b16(sr, s_off[tn], sg * 2, 0);
                 b.z[tn] = ASYM ? (int)(int16_t)__builtin_amdgcn_raw_buffer_load_b16(
@@ -508,6 +515,57 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_mfma_kernel(
                                        lane];
     }
 
+    if constexpr (SPLIT) {
+        // This slice's partial tile goes to the workspace in the lanes' own
+        // layout with stores coherent at device scope; once they have
+        // completed the block counts itself on its tile's counter, and the
+        // block that counts last adds every slice's partial in slice order
+        // (the same order whichever block is last) and returns the counter
+        // to zero.  No block waits for another.
+        __shared__ uint32_t last_flag;
+        constexpr int PT = WM * WN * TM * TN * kWave;     // float4 per block partial
+        const int tile = (int)(blockIdx.y * gridDim.x + blockIdx.x);
+        const int ks = (int)blockIdx.z;
+        const __amdgpu_buffer_rsrc_t wsr = buffer_rsrc(
+            partials + (size_t)tile * ksplit * PT, (uint64_t)ksplit * PT * sizeof(float4_t));
+        const int wt = wm * WN + wn;
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn) {
+                const uint32_t off =
+                    (uint32_t)((ks * PT + ((wt * TM + tm) * TN + tn) * kWave + lane) * 16);
+                const v4u v = {__float_as_uint(acc[tm][tn][0]), __float_as_uint(acc[tm][tn][1]),
+                               __float_as_uint(acc[tm][tn][2]), __float_as_uint(acc[tm][tn][3])};
+                __builtin_amdgcn_raw_buffer_store_b128(v, wsr, off, 0, kCoherentSc1);
+            }
+        __builtin_amdgcn_s_waitcnt(0x0F70);               // vmcnt(0): stores complete
+        __syncthreads();                                  // every wave's stores are complete
+        if (threadIdx.x == 0)
+            last_flag = __hip_atomic_fetch_add(&counters[tile], 1u, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        if (last_flag != (uint32_t)(ksplit - 1)) return;
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = (float4_t){0.f, 0.f, 0.f, 0.f};
+        for (int sl = 0; sl < ksplit; ++sl) {
+#pragma unroll
+            for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+                for (int tn = 0; tn < TN; ++tn) {
+                    const uint32_t off =
+                        (uint32_t)((sl * PT + ((wt * TM + tm) * TN + tn) * kWave + lane) * 16);
+                    const v4u v = __builtin_amdgcn_raw_buffer_load_b128(wsr, off, 0, kCoherentSc1);
+                    acc[tm][tn] += (float4_t){__uint_as_float(v.x), __uint_as_float(v.y),
+                                              __uint_as_float(v.z), __uint_as_float(v.w)};
+                }
+        }
+        if (threadIdx.x == 0)
+            __hip_atomic_store(&counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) {
 #pragma unroll
@@ -525,26 +583,30 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_mfma_kernel(
 
 namespace {
 
-template <int TM, int TN, int WM, int WN, int WK, bool ASYM = false>
+template <int TM, int TN, int WM, int WN, int WK, bool ASYM = false, bool SPLIT = false>
 hipError_t launch_mfma_t(const uint16_t* X, int64_t M, const uint32_t* packed,
                          const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y,
-                         hipStream_t stream, int gshift, const int16_t* zeros = nullptr) {
+                         hipStream_t stream, int gshift, const int16_t* zeros = nullptr,
+                         const TiledSplit* split = nullptr) {
     constexpr int BM = 16 * TM * WM;
     constexpr int BN = 16 * TN * WN;
     const size_t a_bytes = (size_t)2 * WK * BM * kLdaVec * sizeof(uint4);   // two A buffers
     const size_t red_bytes = (size_t)(WK - 1) * WM * WN * TM * TN * 64 * sizeof(float4_t);
     const size_t lds = a_bytes > red_bytes ? a_bytes : red_bytes;
-    auto kern = gemm_mfma_kernel<TM, TN, WM, WN, WK, ASYM>;
+    auto kern = gemm_mfma_kernel<TM, TN, WM, WN, WK, ASYM, SPLIT>;
     if (lds > 64 * 1024) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
                                                  (int)lds);
         if (e != hipSuccess) return e;
     }
-    const dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM));
+    const dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM),
+                    SPLIT ? (unsigned)split->ksplit : 1u);
     hipLaunchKernelGGL(kern, grid, dim3(WM * WN * WK * kWave), lds, stream, X, (int)M,
                        reinterpret_cast<const uint4*>(packed), scales, zeros, Y, (int)N, (int)K,
-                       gshift);
+                       gshift, SPLIT ? split->ksplit : 1, SPLIT ? split->groups_per_slice : 0,
+                       SPLIT ? split->counters : nullptr,
+                       SPLIT ? reinterpret_cast<float4_t*>(split->partials) : nullptr);
     return hipGetLastError();
 }
 
@@ -600,6 +662,48 @@ hipError_t launch_tiled(const uint16_t* X, int64_t M, const uint32_t* packed,
 }
 
 }  // namespace
+
+TiledSplit plan_tiled_split(int64_t M, int64_t N, int64_t K, int num_cu, int ksplit) {
+    TiledSplit p{};
+    p.ksplit = 1;
+    const int64_t ngroups = K / kGroup;
+    if (M <= 64 || N < 1 || ngroups < 2 || K > kTiledMaxK || num_cu < 1) return p;
+    const int64_t tiles = ((M + 127) / 128) * ((N + 255) / 256);
+    if (tiles > kTiledSplitCounters) return p;
+    int64_t s = ksplit;
+    if (s <= 0) {
+        if (tiles * 8 >= (int64_t)num_cu * 7) return p;          // the tiles fill the CUs
+        // slices to give about 7/8 of the compute units a block, each slice
+        // at least 8 groups (1024 elements of K) long
+        s = ((int64_t)num_cu * 7 + 8 * tiles - 1) / (8 * tiles);
+        const int64_t max_s = ngroups / 8;
+        if (s > max_s) s = max_s;
+    }
+    if (s > ngroups) s = ngroups;
+    if (s < 2) return p;
+    const int64_t gps = (ngroups + s - 1) / s;
+    s = (ngroups + gps - 1) / gps;                               // every slice holds a group
+    if (s < 2) return p;
+    constexpr int64_t kPartialBytes = (int64_t)8 * 8 * 2 * kWave * 16;   // 128 x 256 fp32 tile
+    p.ksplit = (int)s;
+    p.groups_per_slice = (int)gps;
+    p.tiles = (int)tiles;
+    p.counter_bytes = (size_t)kTiledSplitCounters * 4;
+    p.workspace_bytes = p.counter_bytes + (size_t)tiles * s * kPartialBytes;
+    return p;
+}
+
+hipError_t launch_gemm_tiled_split(const uint16_t* X, int64_t M, const uint32_t* packed,
+                                   const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y,
+                                   hipStream_t stream, int gshift, const TiledSplit& plan,
+                                   void* workspace) {
+    if (plan.ksplit < 2 || workspace == nullptr) return hipErrorInvalidValue;
+    TiledSplit p = plan;
+    p.counters = static_cast<uint32_t*>(workspace);
+    p.partials = static_cast<char*>(workspace) + p.counter_bytes;
+    return launch_mfma_t<8, 2, 1, 8, 1, false, true>(X, M, packed, scales, N, K, Y, stream, gshift,
+                                                     nullptr, &p);
+}
 
 hipError_t launch_gemm_mfma(const uint16_t* X, int64_t M, const uint32_t* packed,
                             const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y,
