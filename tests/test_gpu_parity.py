@@ -263,13 +263,14 @@ def test_mfma_long_rows(w4, orc, M, N, K):
 
 @pytest.mark.parametrize("M,N,K", [(4, 1001, 8320), (3, 9002, 14464), (4, 64, 16384),
                                    (1, 64, 512), (2, 4100, 14336), (4, 4096, 14336),
-                                   (4, 14336, 4096)])
+                                   (4, 14336, 4096), (4, 3584, 18944), (4, 700, 19456)])
 def test_mfma4_k_split(w4, orc, M, N, K):
     """The 4x4x4 matrix-core GEMV with two waves per row group (few row
     groups for the CUs, or x above 64 KiB): ragged N, an odd step count
     (the second wave's last step lies past K), several batches per block
-    (N = 9002), x of exactly 128 KiB, a single step (the second wave only
-    pads), and the one-wave-per-row-group launch as a control."""
+    (N = 9002), x of 128 KiB, of 148 KiB (the Qwen-2.5-7B down projection)
+    and of exactly 152 KiB (the largest staged), a single step (the second
+    wave only pads), and the one-wave-per-row-group launch as a control."""
     check_linear(w4, orc, M, N, K, seed=([49, N, K], [49, N, K, M]), algo="mfma",
                  name="4x4x4 k split")
 

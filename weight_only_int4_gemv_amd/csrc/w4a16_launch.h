@@ -98,7 +98,10 @@ hipError_t launch_gather_x(const uint16_t* X, int64_t M, int64_t K, const int* p
 // MFMA GEMV for M <= 4 with x resident in LDS (gemv_mfma4.hip): the weight
 // stream of the VALU GEMV, products on v_mfma_f32_4x4x4_16b_f16.
 constexpr int64_t kMfma4MaxM = 4;
-constexpr int64_t kMfma4MaxXBytes = 128 * 1024;
+// x of up to 152 KiB: with the row padding and the partial sums of two
+// waves per row group the kernel's LDS stays below 160 KiB (M = 4 at K =
+// 18944, the Qwen-2.5-7B down projection, fits).
+constexpr int64_t kMfma4MaxXBytes = 152 * 1024;
 hipError_t launch_gemv_mfma4(const uint16_t* X, int64_t M, const uint32_t* packed,
                              const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y,
                              hipStream_t stream, int num_cu);
