@@ -850,7 +850,27 @@ def test_linear_asym_prefill_fp16_weights(w4, orc, M, N, K):
     check_linear_asym(w4, orc, M, N, K, 128, [51, M, N, K], plant=False)
 
 
-@pytest.mark.parametrize("M,N,K", [(65, 300, 1024), (65, 300, 512), (512, 8192, 1024)])
+def test_linear_asym_wide_prefill_common_and_slow_launches(w4, orc):
+    """Enough 128 x 256 blocks to fill the compute units: the common-copy
+    launch leaves the blocks with planted groups (|z| > 1000, scale 0, ties)
+    to the slow-copy launch, which decides over the same 256 columns; every
+    output is computed exactly once and meets the bound."""
+    M, N, K = 520, 11620, 512
+    W = asym_weight(N, K, [52, N, K])
+    W[[300, 5001, 11611]] = W[[0, 1, 2]]        # planted rows in three more column blocks
+    packed, scales, zeros = orc.quantize_asym(W, group=128)
+    X = inputs.activation(M, K, seed=[52, M])
+    say("asym wide prefill M=%d N=%d K=%d" % (M, N, K))
+    Y = w4.gemm_asym(dev(X), packed_to_dev(packed), scales_to_dev(scales), dev(zeros))
+    torch.cuda.synchronize()
+    Yref, Yabs = orc.matmul_asym(X, packed, scales, zeros, group=128)
+    got = Y.cpu().numpy().astype(np.float64)
+    bad = np.argwhere(~(np.abs(got - Yref) <= oracle.tolerance(Yref, Yabs)))
+    assert bad.size == 0, "%d outputs out of tolerance, first %s" % (len(bad), bad[0])
+
+
+@pytest.mark.parametrize("M,N,K", [(65, 300, 1024), (65, 300, 512), (512, 8192, 1024),
+                                   (520, 11620, 512)])
 def test_linear_asym_large_scales(w4, orc, M, N, K):
     """Asymmetric weights with scales of 64 and more (the tiled kernel's
     slow copy: fp16 weights s * (n - zc) clamped to +-65504), including

@@ -51,14 +51,20 @@ constexpr int kLdaVec = kLdaHalfs / 8;     // in uint4
 constexpr int kCoherentSc1 = 16;           // cache policy: coherent at device scope (sc1)
 }  // namespace
 
-template <int TM, int TN, int WM, int WN, int WK, bool ASYM, bool SPLIT>
+// PART: 0 = both copies of the K loop (the block picks one); 1 = the common
+// copy only (a block that needs the slow copy returns at once); 2 = the slow
+// copy only, deciding over the scale_bn columns around the block (the block
+// tile of the PART 1 launch it completes), so that the two launches split
+// the blocks between them exactly.
+template <int TM, int TN, int WM, int WN, int WK, bool ASYM, bool SPLIT, int PART>
 __global__ __launch_bounds__(WM * WN * WK * kWave)
 __attribute__((amdgpu_waves_per_eu(2))) void gemm_mfma_kernel(
     const uint16_t* __restrict__ X, int M, const uint4* __restrict__ packed,
     const uint16_t* __restrict__ scales, const int16_t* __restrict__ zeros,
     uint16_t* __restrict__ Y, int N, int K, int gshift, int ksplit, int gps,
-    uint32_t* __restrict__ counters, float4_t* __restrict__ partials) {
+    uint32_t* __restrict__ counters, float4_t* __restrict__ partials, int scan_bn) {
     static_assert(!SPLIT || WK == 1, "the K split sums whole block tiles");
+    static_assert(!SPLIT || PART == 0, "the K split runs both copies");
     constexpr int NT = WM * WN * WK * kWave;
     constexpr int BM = 16 * TM * WM;
     constexpr int BN = 16 * TN * WN;
@@ -433,7 +439,20 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_mfma_kernel(
     constexpr uint32_t kSlowScale = ASYM ? 0x5400u : kHugeScaleBits;   // 64 : 9360
     bool huge = false;
     {
-        const uint32_t span = (uint32_t)min(BN, N - n_blk) * srow;
+        // the scanned columns: the block's own, or (PART 2) the scan_bn
+        // columns of the block tile it completes
+        const int n_scan = PART == 2 ? n_blk / scan_bn * scan_bn : n_blk;
+        const int scan_w = PART == 2 ? scan_bn : BN;
+        const uint32_t span = (uint32_t)min(scan_w, N - n_scan) * srow;
+        const __amdgpu_buffer_rsrc_t ssr =
+            PART == 2 ? buffer_rsrc(reinterpret_cast<const char*>(scales) + (size_t)n_scan * srow,
+                                    (uint64_t)(N - n_scan) * srow)
+                      : sr;
+        const __amdgpu_buffer_rsrc_t szr =
+            PART == 2 && ASYM
+                ? buffer_rsrc(reinterpret_cast<const char*>(zeros) + (size_t)n_scan * srow,
+                              (uint64_t)(N - n_scan) * srow)
+                : zr;
         auto slow_z = [&](uint32_t zbits) {
             const int z = (int)(int16_t)(uint16_t)zbits;
             return ASYM && (z > kZeroClamp || z < -kZeroClamp);
@@ -441,13 +460,13 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_mfma_kernel(
         if ((reinterpret_cast<uintptr_t>(scales) & 15) == 0 &&
             (!ASYM || (reinterpret_cast<uintptr_t>(zeros) & 15) == 0) && (srow & 15) == 0) {
             for (uint32_t off = threadIdx.x * 16u; off < span; off += NT * 16u) {
-                const v4u v = __builtin_amdgcn_raw_buffer_load_b128(sr, off, 0, 0);
+                const v4u v = __builtin_amdgcn_raw_buffer_load_b128(ssr, off, 0, 0);
                 const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     huge |= (w[i] & 0xFFFFu) >= kSlowScale || (w[i] >> 16) >= kSlowScale;
                 if constexpr (ASYM) {
-                    const v4u zv = __builtin_amdgcn_raw_buffer_load_b128(zr, off, 0, 0);
+                    const v4u zv = __builtin_amdgcn_raw_buffer_load_b128(szr, off, 0, 0);
                     const uint32_t zw[4] = {zv.x, zv.y, zv.z, zv.w};
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
@@ -456,10 +475,25 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_mfma_kernel(
             }
         } else {
             for (uint32_t off = threadIdx.x * 2u; off < span; off += NT * 2u) {
-                huge |= __builtin_amdgcn_raw_buffer_load_b16(sr, off, 0, 0) >= kSlowScale;
-                if constexpr (ASYM) huge |= slow_z(__builtin_amdgcn_raw_buffer_load_b16(zr, off, 0, 0));
+                huge |= __builtin_amdgcn_raw_buffer_load_b16(ssr, off, 0, 0) >= kSlowScale;
+                if constexpr (ASYM) huge |= slow_z(__builtin_amdgcn_raw_buffer_load_b16(szr, off, 0, 0));
             }
         }
+    }
+    // block-wide OR of the scan: one word per wave, read after the barrier
+    __shared__ uint32_t huge_waves[NT / kWave];
+    auto block_any = [&](bool v) {
+        const bool wave_v = __any(v);
+        if (lane == 0) huge_waves[wave] = wave_v ? 1u : 0u;
+        __syncthreads();
+        bool any = false;
+#pragma unroll
+        for (int w = 0; w < NT / kWave; ++w) any |= huge_waves[w] != 0u;
+        return any;
+    };
+    // the slow-only launch decides before loading anything: most blocks leave
+    if constexpr (PART == 2) {
+        if (!block_any(huge)) return;
     }
 
     load_a(0, a_regs);
@@ -469,14 +503,12 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_mfma_kernel(
         load_a(1, a_regs);
         load_b(1, b1);
     }
-    // block-wide OR of the scan: one word per wave, read after the barrier
-    __shared__ uint32_t huge_waves[NT / kWave];
-    const bool wave_huge = __any(huge);
-    if (lane == 0) huge_waves[wave] = wave_huge ? 1u : 0u;
-    __syncthreads();
-    huge = false;
-#pragma unroll
-    for (int w = 0; w < NT / kWave; ++w) huge |= huge_waves[w] != 0u;
+    if constexpr (PART != 2) {
+        huge = block_any(huge);
+        if (PART == 1 && huge) return;       // left to the slow-only launch
+    } else {
+        __syncthreads();                     // the stage-0 A tile is in LDS
+    }
     auto k_loop = [&](auto clamp) __attribute__((always_inline)) {
         for (int step = 0; step < nsteps; step += 2) {
             step_body(step, b0, clamp);
@@ -486,7 +518,11 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_mfma_kernel(
     // one call site per instantiation, so each copy is inlined (a lambda
     // called from two sites can stay a call, with its captured arrays in
     // scratch memory)
-    if (huge)
+    if constexpr (PART == 1)
+        k_loop(std::false_type{});
+    else if constexpr (PART == 2)
+        k_loop(std::true_type{});
+    else if (huge)
         k_loop(std::true_type{});
     else
         k_loop(std::false_type{});
@@ -583,17 +619,18 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_mfma_kernel(
 
 namespace {
 
-template <int TM, int TN, int WM, int WN, int WK, bool ASYM = false, bool SPLIT = false>
+template <int TM, int TN, int WM, int WN, int WK, bool ASYM = false, bool SPLIT = false,
+          int PART = 0>
 hipError_t launch_mfma_t(const uint16_t* X, int64_t M, const uint32_t* packed,
                          const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y,
                          hipStream_t stream, int gshift, const int16_t* zeros = nullptr,
-                         const TiledSplit* split = nullptr) {
+                         const TiledSplit* split = nullptr, int scan_bn = 0) {
     constexpr int BM = 16 * TM * WM;
     constexpr int BN = 16 * TN * WN;
     const size_t a_bytes = (size_t)2 * WK * BM * kLdaVec * sizeof(uint4);   // two A buffers
     const size_t red_bytes = (size_t)(WK - 1) * WM * WN * TM * TN * 64 * sizeof(float4_t);
     const size_t lds = a_bytes > red_bytes ? a_bytes : red_bytes;
-    auto kern = gemm_mfma_kernel<TM, TN, WM, WN, WK, ASYM, SPLIT>;
+    auto kern = gemm_mfma_kernel<TM, TN, WM, WN, WK, ASYM, SPLIT, PART>;
     if (lds > 64 * 1024) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -606,7 +643,7 @@ hipError_t launch_mfma_t(const uint16_t* X, int64_t M, const uint32_t* packed,
                        reinterpret_cast<const uint4*>(packed), scales, zeros, Y, (int)N, (int)K,
                        gshift, SPLIT ? split->ksplit : 1, SPLIT ? split->groups_per_slice : 0,
                        SPLIT ? split->counters : nullptr,
-                       SPLIT ? reinterpret_cast<float4_t*>(split->partials) : nullptr);
+                       SPLIT ? reinterpret_cast<float4_t*>(split->partials) : nullptr, scan_bn);
     return hipGetLastError();
 }
 
@@ -638,9 +675,22 @@ hipError_t launch_tiled(const uint16_t* X, int64_t M, const uint32_t* packed,
         return ((M + bm - 1) / bm) * ((N + bn - 1) / bn) * 8 >= (int64_t)num_cu * 7;
     };
     if constexpr (ASYM) {
-        // Asymmetric weights: 16-column wave tiles (the exact slow copy of the
-        // loop does not fit two waves per SIMD with 32 columns): 128 x 128
-        // blocks, 128 x 64 and 64 x 64 blocks with two waves over K.
+        // Asymmetric weights.  The exact slow copy of the loop does not fit
+        // two waves per SIMD with 32-column wave tiles, so when 128 x 256
+        // blocks fill the compute units the common copy runs alone in them
+        // (blocks that need the slow copy return at once) and a second launch
+        // of 128 x 128 blocks runs the slow copy where it is needed (its
+        // blocks decide over the 256 columns of the first launch's block, so
+        // every block is computed once; elsewhere they return before loading
+        // anything).  Otherwise 16-column wave tiles with both copies: 128 x
+        // 128 blocks, 128 x 64 and 64 x 64 blocks with two waves over K.
+        if (fills(128, 256)) {
+            const hipError_t e = launch_mfma_t<8, 2, 1, 8, 1, true, false, 1>(
+                X, M, packed, scales, N, K, Y, stream, gshift, zeros);
+            if (e != hipSuccess) return e;
+            return launch_mfma_t<8, 1, 1, 8, 1, true, false, 2>(
+                X, M, packed, scales, N, K, Y, stream, gshift, zeros, nullptr, 256);
+        }
         if (fills(128, 128)) return W4A16_TILED(8, 1, 1, 8, 1);
         if (fills(128, 64)) return W4A16_TILED(8, 1, 1, 4, 2);
         return W4A16_TILED(4, 1, 1, 4, 2);
