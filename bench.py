@@ -792,6 +792,34 @@ def main() -> int:
                    "dominant_launch_frac_of_it": (round(roofline["achieved"] / copy_gbs, 4)
                                                   if roofline else None)}
 
+    # ---- the GPU's floor per dependent launch on one stream: as many
+    # launches of a one-element kernel as the sweep has, captured in a graph
+    # (the gap from one kernel's end to the next one's start is part of every
+    # launch of the sweep, whatever the kernel)
+    tiny = torch.zeros(1, dtype=torch.float32, device=dev)
+    fg = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(fg):
+        for _ in range(n_launch):
+            tiny.add_(1.0)
+    for _ in range(3):
+        fg.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(10):
+        fg.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    floor_us = e0.elapsed_time(e1) * 1e3 / 10
+    del fg, tiny
+    sweep_us = ms * 1e3
+    launch_floor = {"kernel": "one-element add, graph of %d dependent launches" % n_launch,
+                    "us_per_launch": round(floor_us / n_launch, 3),
+                    "us_per_sweep": round(floor_us, 2),
+                    "sweep_us_above_floor": round(sweep_us - floor_us, 2),
+                    "GB/s_above_floor": (round(step_bytes / ((sweep_us - floor_us) * 1e-6) / 1e9, 1)
+                                         if sweep_us > floor_us else None)}
+
     out = {
         "metric": "W4A16 GEMV effective HBM GB/s (% of peak) + us per 8B-shaped decode weight sweep",
         "value": round(gbs, 1),
@@ -828,6 +856,7 @@ def main() -> int:
         "other_mode": other_mode,
         "step_samples": step_spread,
         "stream_copy": stream_copy,
+        "launch_floor": launch_floor,
         "per_shape": per_shape,
         "parity": parity,
         "secondary": sec,

@@ -776,6 +776,37 @@ def test_quantize_asym_every_range(w4, orc):
     check_quantize_asym(w4, orc, W, 128, name="every range")
 
 
+def test_quantize_asym_ties_and_zero_parity(w4, orc):
+    """Groups whose elements sit exactly on half-integers of w / s: the code
+    is rint(w / s) + z, which differs from rint(w / s + z) when z is odd
+    (rint(-2.5) + 3 = 1, rint(0.5) = 0), for every z in [0, 15] and scales
+    1, 1/8 and 3; and groups whose min / s is itself a tie (z from a rounded
+    tie).  Elements a quarter off the half-integers check the ordinary
+    rounding beside them."""
+    rows, want = [], []
+    for s in (1.0, 0.125, 3.0):
+        for z in range(0, 16):
+            base = -z * s                      # min, so that z = -rint(min / s)
+            vals = [base, base + 15 * s]       # range 15 s: the scale is s
+            for off in (0.5, 0.25, 0.75):
+                vals += [(j + off - z) * s for j in range(15)]
+            vals += [base] * (128 - len(vals))
+            rows.append(vals)
+            want.append((s, z))
+        for m in range(0, 8):                  # min / s = -(m + 1/2): a tie for z
+            base = -(m + 0.5) * s
+            vals = [base, base + 15 * s] + [(j + 0.5) * s + base for j in range(15)]
+            vals += [base] * (128 - len(vals))
+            rows.append(vals)
+            want.append((s, m + (m & 1)))      # rint(m + 1/2), half to even
+    W = np.array(rows, dtype=np.float64)
+    assert np.array_equal(W.astype(np.float16).astype(np.float64), W)   # exact in fp16
+    _, so, zo = orc.quantize_asym(W.astype(np.float16), group=128)
+    assert np.array_equal(so.view(np.float16)[:, 0].astype(np.float64), [s for s, _ in want])
+    assert np.array_equal(zo[:, 0], [z for _, z in want])
+    check_quantize_asym(w4, orc, W.astype(np.float16), 128, name="ties")
+
+
 @pytest.mark.parametrize("kind", ["reverse", "random"])
 @pytest.mark.parametrize("group", [64, 128])
 def test_quantize_asym_act_order(w4, orc, kind, group):

@@ -246,7 +246,7 @@ int quantize(const uint16_t* W, int64_t N, int64_t K, int64_t group, uint32_t* p
     st = current_device(&num_cu);
     if (st != W4A16_OK) return st;
     return status_of(w4a16::launch_quantize(W, N, K, group, packed, scales,
-                                            static_cast<hipStream_t>(stream),
+                                            static_cast<hipStream_t>(stream), num_cu,
                                             with_perm ? perm : nullptr, asym ? zeros : nullptr));
 }
 

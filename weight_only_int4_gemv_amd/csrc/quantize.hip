@@ -32,12 +32,19 @@
 //     rounding); a lane that sees a u within 2e-5 of one (about 2 in 10^5
 //     elements of Gaussian weights, and every exact tie) redoes its 8
 //     elements with the IEEE fp32 division.
+#include <atomic>
+
 #include "w4a16_device.h"
 #include "w4a16_launch.h"
 
 namespace w4a16 {
 
 namespace {
+// Group quantizer launch: U groups per lane slice and step, and at most this
+// many resident 256-thread blocks per compute unit (the grid walks the rest).
+constexpr int kQuantizeGroupsPerStep = 2;
+constexpr int kQuantizeBlocksPerCu = 8;
+
 // max over the 16 lanes of a DPP row (quad butterflies, then half-row and
 // row mirrors); every lane of the row receives it.
 template <int CTRL>
@@ -60,18 +67,32 @@ __device__ __forceinline__ uint32_t group_max(uint32_t v) {
     return v;
 }
 
-// |w| of the 8 fp16 values of a lane, as the largest magnitude bit pattern.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ u16x2 as_u16x2(uint32_t w) { return __builtin_bit_cast(u16x2, w); }
+
+// |w| of the 8 fp16 values of a lane, as the largest magnitude bit pattern
+// (sign bits cleared, then 16-bit maxima two at a time).
 __device__ __forceinline__ uint32_t absmax8(const uint4& v) {
-    uint32_t m = 0;
-    m = max(m, v.x & 0x7FFFu);
-    m = max(m, (v.x >> 16) & 0x7FFFu);
-    m = max(m, v.y & 0x7FFFu);
-    m = max(m, (v.y >> 16) & 0x7FFFu);
-    m = max(m, v.z & 0x7FFFu);
-    m = max(m, (v.z >> 16) & 0x7FFFu);
-    m = max(m, v.w & 0x7FFFu);
-    m = max(m, (v.w >> 16) & 0x7FFFu);
-    return m;
+    const u16x2 a = as_u16x2(v.x & 0x7FFF7FFFu), b = as_u16x2(v.y & 0x7FFF7FFFu);
+    const u16x2 c = as_u16x2(v.z & 0x7FFF7FFFu), d = as_u16x2(v.w & 0x7FFF7FFFu);
+    const u16x2 m = __builtin_elementwise_max(__builtin_elementwise_max(a, b),
+                                              __builtin_elementwise_max(c, d));
+    return max((uint32_t)m.x, (uint32_t)m.y);
+}
+
+// Packed word of 8 codes, each an integer-valued float in [0, 15]: codes
+// 0, 2, 4, 6 in the bytes of one word, 1, 3, 5, 7 in another, then the
+// second shifted into the high nibbles (element i at bits 4i).
+__device__ __forceinline__ uint32_t pack_codes8(const float (&c)[8]) {
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        lo = __builtin_amdgcn_cvt_pk_u8_f32(c[2 * j], j, lo);
+        hi = __builtin_amdgcn_cvt_pk_u8_f32(c[2 * j + 1], j, hi);
+    }
+    return lo | (hi << 4);
 }
 
 // Scale bits of a group (or row) whose absolute maximum has bit pattern m.
@@ -96,46 +117,57 @@ __device__ __forceinline__ uint32_t codes8(const uint4& v, uint16_t s_bits) {
     if (s == 0.0f) return 0x88888888u;   // every code 0 (all lanes of the group alike)
     const uint32_t h[4] = {v.x, v.y, v.z, v.w};
     const float inv = __builtin_amdgcn_rcpf(s);
-    uint32_t word = 0;
-    bool near_tie = false;
+    float c[8];
+    float dist = 0.0f;                         // largest |u - rint(u)| of the 8
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const float w = f16_bits_to_f32((uint16_t)(h[i >> 1] >> (16 * (i & 1))));
         const float u = fmaf(w, inv, 8.0f);       // w / s + 8, within 4e-6
         const float r = rintf(u);
-        near_tie |= fabsf(u - r) > 0.49998f;
+        dist = fmaxf(dist, fabsf(u - r));
         // code = clamp(rint(w / s), -8, 7) + 8 = clamp(r, 0, 15), exact in fp32
-        const float c = __builtin_amdgcn_fmed3f(r, 0.0f, 15.0f);
-        word |= (uint32_t)c << (4 * i);
+        c[i] = __builtin_amdgcn_fmed3f(r, 0.0f, 15.0f);
     }
-    if (near_tie) {
-        word = 0;
+    if (dist > 0.49998f) {                     // a half-integer within 2e-5: redo exactly
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const float w = f16_bits_to_f32((uint16_t)(h[i >> 1] >> (16 * (i & 1))));
-            const float r = fminf(fmaxf(rintf(w / s), -8.0f), 7.0f);
-            word |= ((uint32_t)((int)r + 8) & 0xFu) << (4 * i);
+            c[i] = fminf(fmaxf(rintf(w / s), -8.0f), 7.0f) + 8.0f;
         }
     }
-    return word;
+    return pack_codes8(c);
 }
 
 // ---- asymmetric INT4 ([QUANT] sub-section 2, asymmetric equations) ----
 //   s = fp16_rne((max - min) / 15), z = -rint(min / s), q = clamp(rint(w / s)
 //   + z, 0, 15), stored as the nibble q itself; s = 0 (a group whose range
 //   rounds to 0) stores z = 0 and q = 0.
-// Bit-exactness, all in binary64 (full-rate vector fp64 on gfx950):
-//   - max - min of two fp16 values is exact (at most 40 significant bits);
-//     the IEEE division by 15 and the rounding to fp16 below give the RNE
-//     of the exact quotient: (max - min) / 15 is either dyadic (then exact in
-//     binary64) or has the period-4 binary expansion of 1/15, which never
-//     puts a 53-bit rounding on a fp16 tie;
-//   - min / s and w / s lie within 2^15 in magnitude (|z| <= 32752), and a
-//     quotient of two fp16 values that is not a tie is at least 2^-23 away
-//     from one: the IEEE division, or w * (1 / s) (error below 2^-36), round
-//     to the same integer as the exact quotient; a lane whose product lies
-//     within 2^-30 of a tie (exact ties only) redoes its 8 elements with the
-//     division.
+// Bit-exactness:
+//   - the scale in binary64: max - min of two fp16 values is exact (at most
+//     40 significant bits); the IEEE division by 15 and the rounding to fp16
+//     below give the RNE of the exact quotient: (max - min) / 15 is either
+//     dyadic (then exact in binary64) or has the period-4 binary expansion
+//     of 1/15, which never puts a 53-bit rounding on a fp16 tie;
+//   - a quotient a / s of two fp16 values that is not a tie lies at least
+//     2^-13 from one (write a = A 2^e, s = B 2^f with 11-bit integers A, B:
+//     the distance is a nonzero multiple of 2^(e-f) / (2B), and where it
+//     matters, |a / s| >= 1/2, 2^(e-f) >= B / (2A)), and |min / s|, |w / s|
+//     stay below 2^15 (the range is at least one fp16 spacing of min);
+//   - 1/s is formed as r = rcp_f32(s) (relative error below 2^-22) refined
+//     by one binary64 Newton step (relative error below 2^-43);
+//   - z: p = min * r is within 2^-27 of min / s; rint(p) is z unless p lies
+//     within 2^-20 of a half-integer (exact ties only), where the IEEE
+//     division decides;
+//   - codes in fp32: r is split into r_hi = fp32(r) and r_lo = fp32(r -
+//     r_hi), and u = fma(w, r_lo, fma(w, r_hi, z)).  Where |w / s + z| < 15.99
+//     (every code the clamp does not fix), each fma rounds a value below 16
+//     (error at most 2^-21) and r_hi + r_lo misses 1/s by under 2^-43
+//     relative (2^-27 absolute on w / s), so u is within 2^-19.9 of w / s
+//     + z.  rint(u) then equals rint(w / s + z) = rint(w / s) + z unless u is
+//     within 2^-15 of a half-integer, where the lane redoes its 8 elements
+//     with the binary64 division (exact ties among them: rint(w / s) + z
+//     differs from rint(w / s + z) at a tie when z is odd).  Beyond 16 in
+//     magnitude the clamp gives 0 or 15 whatever the rounding.
 
 // fp16 bits of the round-to-nearest-even of v (0 <= v < 65520): the integer
 // rint(v / u) times the fp16 spacing u = 2^(e - 10) at v's binade (2^-24
@@ -149,30 +181,35 @@ __device__ __forceinline__ uint16_t f16_rne_from_f64(double v) {
     return f32_to_f16_bits((float)ldexp(m, e - 10));
 }
 
-// Order-preserving key of a finite fp16 bit pattern (sign-magnitude to
-// offset binary: -0 just below +0), and its inverse.
-__device__ __forceinline__ uint32_t f16_key(uint32_t h) {
-    return h ^ ((h & 0x8000u) ? 0xFFFFu : 0x8000u);
-}
+// Order-preserving key of a finite fp16 bit pattern h (sign-magnitude to
+// offset binary, -0 just below +0): h ^ 0xFFFF when the sign bit is set,
+// else h ^ 0x8000 (formed two at a time below).  Its inverse:
 __device__ __forceinline__ uint32_t f16_from_key(uint32_t k) {
     return k ^ ((k & 0x8000u) ? 0x8000u : 0xFFFFu);
 }
 
-// One lane's 8 elements of a group -> its packed word (nibbles q in
-// [0, 15]), and the group's scale and zero point.
 // Largest key and largest 0xFFFF - key of a lane's 8 values (the maximum
-// and, complemented, the minimum).
+// and, complemented, the minimum), two 16-bit keys at a time: a negative
+// half (sign bit set) has all bits flipped, a positive one its sign bit set.
 __device__ __forceinline__ void minmax_keys8(const uint4& v, uint32_t& kmax, uint32_t& kmin_c) {
-    const uint32_t h[8] = {v.x & 0xFFFFu, v.x >> 16, v.y & 0xFFFFu, v.y >> 16,
-                           v.z & 0xFFFFu, v.z >> 16, v.w & 0xFFFFu, v.w >> 16};
-    kmax = 0;
-    kmin_c = 0;
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    u16x2 hi, lo;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const uint32_t key = f16_key(h[i]);
-        kmax = max(kmax, key);
-        kmin_c = max(kmin_c, 0xFFFFu - key);
+    for (int i = 0; i < 4; ++i) {
+        const i16x2 sgn = __builtin_bit_cast(i16x2, w[i]) >> (short)15;      // 0 or -1 per half
+        const u16x2 key = as_u16x2(w[i] ^ (__builtin_bit_cast(uint32_t, sgn) | 0x80008000u));
+        hi = i == 0 ? key : __builtin_elementwise_max(hi, key);
+        lo = i == 0 ? key : __builtin_elementwise_min(lo, key);
     }
+    kmax = max((uint32_t)hi.x, (uint32_t)hi.y);
+    kmin_c = 0xFFFFu - min((uint32_t)lo.x, (uint32_t)lo.y);
+}
+
+// 1/s to within 2^-43 (relative) for an fp16 scale s > 0: the fp32
+// reciprocal (relative error below 2^-22) and one binary64 Newton step.
+__device__ __forceinline__ double recip_of_scale(double s) {
+    const double r0 = (double)__builtin_amdgcn_rcpf((float)s);
+    return fma(r0, fma(-s, r0, 1.0), r0);
 }
 
 // Scale bits and zero point of a group (or row) from its reduced keys.
@@ -182,7 +219,14 @@ __device__ __forceinline__ void asym_params(uint32_t kmax, uint32_t kmin_c, uint
     const double mn = (double)f16_bits_to_f32((uint16_t)f16_from_key(0xFFFFu - kmin_c));
     s_bits = f16_rne_from_f64((mx - mn) / 15.0);         // 2^4 - 1 = 15
     const double s = (double)f16_bits_to_f32(s_bits);
-    zero = s == 0.0 ? (int16_t)0 : (int16_t)(int)-rint(mn / s);
+    if (s == 0.0) {
+        zero = 0;
+        return;
+    }
+    const double p = mn * recip_of_scale(s);
+    double r = rint(p);
+    if (fabs(p - r) > 0.5 - 0x1p-20) r = rint(mn / s);   // a tie: the division decides
+    zero = (int16_t)(int)-r;
 }
 
 __device__ __forceinline__ uint32_t codes8_asym(const uint4& v, uint16_t s_bits, int16_t zero);
@@ -202,82 +246,88 @@ __device__ __forceinline__ uint32_t codes8_asym(const uint4& v, uint16_t s_bits,
                            v.z & 0xFFFFu, v.z >> 16, v.w & 0xFFFFu, v.w >> 16};
     const double s = (double)f16_bits_to_f32(s_bits);
     if (s == 0.0) return 0u;                             // every code 0
-    const double z = (double)zero;
-    const double inv = 1.0 / s;
-    uint32_t word = 0;
-    bool near_tie = false;
+    const double r = recip_of_scale(s);
+    const float r_hi = (float)r;
+    const float r_lo = (float)(r - (double)r_hi);
+    const float zf = (float)zero;
+    float c[8];
+    float dist = 0.0f;                                   // largest |u - rint(u)|
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const double t = (double)f16_bits_to_f32((uint16_t)h[i]) * inv;
-        const double r = rint(t);
-        near_tie |= fabs(t - r) > 0.5 - 0x1p-30;
-        const double c = fmin(fmax(r + z, 0.0), 15.0);
-        word |= (uint32_t)(int)c << (4 * i);
+        const float w = f16_bits_to_f32((uint16_t)h[i]);
+        const float u = fmaf(w, r_lo, fmaf(w, r_hi, zf));   // w / s + z, within 2^-19.9
+        const float q = rintf(u);
+        dist = fmaxf(dist, fabsf(u - q));
+        c[i] = __builtin_amdgcn_fmed3f(q, 0.0f, 15.0f);
     }
-    if (near_tie) {
-        word = 0;
+    if (dist > 0.5f - 0x1p-15f) {                        // near a half-integer: redo exactly
+        const double z = (double)zero;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const double r = rint((double)f16_bits_to_f32((uint16_t)h[i]) / s);
-            const double c = fmin(fmax(r + z, 0.0), 15.0);
-            word |= (uint32_t)(int)c << (4 * i);
+            const double q = rint((double)f16_bits_to_f32((uint16_t)h[i]) / s);
+            c[i] = (float)fmin(fmax(q + z, 0.0), 15.0);
         }
     }
-    return word;
+    return pack_codes8(c);
 }
 
 }  // namespace
 
-// Each LG-lane slice of a wave quantizes one group per step; the loads of U
-// steps (groups g, g + stride, ...) are issued together.  All LG lanes of a
-// slice share g, so the reductions only ever combine lanes that are active
-// together.
+// Each LG-lane slice of a wave quantizes U groups per step (groups g, g +
+// stride, ..., stride = the slices in the grid); the grid is a few blocks
+// per compute unit and walks the groups in steps of U * stride.  The loads
+// of step t + 1 are issued before step t is quantized (two register sets,
+// the loop unrolled over two steps), and every load is unconditional (a
+// group past the end reloads the last group and stores nothing), so the
+// compiler's counter wait before step t covers exactly step t's loads.  All
+// LG lanes of a slice share g, so the reductions only ever combine lanes
+// that are active together.
 //
 // perm (act-order layout, [QUANT] GPTQ section: columns quantized and stored
 // in the order perm): NULL, or device int32 [K]; column j of the output is
 // column perm[j] of W (an index outside [0, K) reads as 0), gathered with
-// 2-byte loads instead of one 16-byte load per lane.
+// 2-byte loads instead of one 16-byte load per lane (PERM: a copy of the
+// kernel of its own; the gather's loads depend on the perm loads, so its
+// steps do not overlap).
 //
 // ASYM: the asymmetric quantizer, which also writes one int16 zero point per
 // group to `zeros` (laid out like the scales).
-template <int LG, int U, bool ASYM>
+template <int LG, int U, bool ASYM, bool PERM>
 __global__ __launch_bounds__(256) void quantize_kernel(const uint4* __restrict__ W,
                                                        uint32_t* __restrict__ packed,
                                                        uint16_t* __restrict__ scales,
                                                        int16_t* __restrict__ zeros,
                                                        int64_t total_groups, int K,
                                                        const int* __restrict__ perm) {
+    typedef unsigned v4u __attribute__((ext_vector_type(4)));
     const int lg = threadIdx.x & (LG - 1);              // lane within the group
     const int64_t stride = (int64_t)gridDim.x * (blockDim.x / LG);
-    typedef unsigned v4u __attribute__((ext_vector_type(4)));
+    const int64_t step = (int64_t)U * stride;
     const v4u* Wv = reinterpret_cast<const v4u*>(W);
-    for (int64_t g = (int64_t)blockIdx.x * (blockDim.x / LG) + (threadIdx.x / LG);
-         g < total_groups; g += U * stride) {
-        v4u a[U];
+
+    auto load = [&](v4u (&a)[U], int64_t g) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            // W is read once: non-temporal loads
-            a[u] = (v4u){0u, 0u, 0u, 0u};
-            const int64_t gu = g + u * stride;
-            if (gu < total_groups) {
-                if (perm == nullptr) {
-                    a[u] = __builtin_nontemporal_load(Wv + gu * LG + lg);
-                } else {
-                    const int64_t gpr = K / (LG * 8);            // groups per row
-                    const int64_t n = gu / gpr;
-                    const int col = (int)(gu - n * gpr) * (LG * 8) + lg * 8;
-                    const uint16_t* row = reinterpret_cast<const uint16_t*>(W) + n * K;
-                    uint32_t h[8];
+            const int64_t gu = min(g + u * stride, total_groups - 1);
+            if constexpr (!PERM) {
+                a[u] = __builtin_nontemporal_load(Wv + gu * LG + lg);   // W is read once
+            } else {
+                const int64_t gpr = K / (LG * 8);                // groups per row
+                const int64_t n = gu / gpr;
+                const int col = (int)(gu - n * gpr) * (LG * 8) + lg * 8;
+                const uint16_t* row = reinterpret_cast<const uint16_t*>(W) + n * K;
+                uint32_t h[8];
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        const int p = perm[col + i];
-                        h[i] = (uint32_t)p < (uint32_t)K ? row[p] : 0u;
-                    }
-                    a[u] = (v4u){h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
-                                 h[6] | (h[7] << 16)};
+                for (int i = 0; i < 8; ++i) {
+                    const int p = perm[col + i];
+                    h[i] = (uint32_t)p < (uint32_t)K ? row[p] : 0u;
                 }
+                a[u] = (v4u){h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                             h[6] | (h[7] << 16)};
             }
         }
+    };
+    auto work = [&](const v4u (&a)[U], int64_t g) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t gu = g + u * stride;
@@ -297,6 +347,16 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint4* __restrict__
                 }
             }
         }
+    };
+
+    const int64_t g0 = (int64_t)blockIdx.x * (blockDim.x / LG) + (threadIdx.x / LG);
+    v4u a[U], b[U];
+    load(a, g0);
+    for (int64_t g = g0; g < total_groups; g += 2 * step) {
+        load(b, g + step);
+        work(a, g);
+        load(a, g + 2 * step);
+        work(b, g + step);
     }
 }
 
@@ -465,23 +525,42 @@ hipError_t launch_quantize_q4_0(const uint16_t* W, int64_t N, int64_t K, uint8_t
 template <int LG, int U>
 hipError_t launch_quantize_t(const uint16_t* W, int64_t groups, int64_t K, const int* perm,
                              uint32_t* packed, uint16_t* scales, int16_t* zeros,
-                             hipStream_t stream) {
+                             hipStream_t stream, int num_cu) {
     constexpr int per_block = 256 / LG;                  // groups per block and step
-    constexpr int64_t kMaxBlocks = 65536;
-    int64_t blocks = (groups + per_block * U - 1) / (per_block * U);
-    if (blocks > kMaxBlocks) blocks = kMaxBlocks;        // grid-stride beyond this
+    const int64_t need = (groups + per_block * U - 1) / (per_block * U);
     const uint4* Wv = reinterpret_cast<const uint4*>(W);
-    if (zeros != nullptr)
-        hipLaunchKernelGGL((quantize_kernel<LG, U, true>), dim3((unsigned)blocks), dim3(256), 0,
-                           stream, Wv, packed, scales, zeros, groups, (int)K, perm);
-    else
-        hipLaunchKernelGGL((quantize_kernel<LG, U, false>), dim3((unsigned)blocks), dim3(256), 0,
-                           stream, Wv, packed, scales, zeros, groups, (int)K, perm);
+    // one resident round of blocks (the occupancy query's count per CU, at
+    // most kQuantizeBlocksPerCu), walking the groups in grid strides
+#define W4A16_QUANTIZE(ASYM, PERM)                                                                \
+    do {                                                                                          \
+        auto kern = quantize_kernel<LG, U, ASYM, PERM>;                                           \
+        static std::atomic<int> resident{0};                                                      \
+        int r = resident.load(std::memory_order_relaxed);                                         \
+        if (r == 0) {                                                                             \
+            const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(                    \
+                &r, reinterpret_cast<const void*>(kern), 256, 0);                                 \
+            if (e != hipSuccess) return e;                                                        \
+            r = r < 1 ? 1 : (r > kQuantizeBlocksPerCu ? kQuantizeBlocksPerCu : r);                \
+            resident.store(r, std::memory_order_relaxed);                                         \
+        }                                                                                         \
+        const int64_t cap = (int64_t)num_cu * r;                                                  \
+        const int64_t blocks = need < cap ? need : cap;                                           \
+        hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, stream, Wv, packed, scales, \
+                           zeros, groups, (int)K, perm);                                          \
+    } while (0)
+    if (zeros != nullptr) {
+        if (perm != nullptr) W4A16_QUANTIZE(true, true);
+        else W4A16_QUANTIZE(true, false);
+    } else {
+        if (perm != nullptr) W4A16_QUANTIZE(false, true);
+        else W4A16_QUANTIZE(false, false);
+    }
+#undef W4A16_QUANTIZE
     return hipGetLastError();
 }
 
 hipError_t launch_quantize(const uint16_t* W, int64_t N, int64_t K, int64_t group,
-                           uint32_t* packed, uint16_t* scales, hipStream_t stream,
+                           uint32_t* packed, uint16_t* scales, hipStream_t stream, int num_cu,
                            const int* perm, int16_t* zeros) {
     if (N == 0 || K == 0) return hipSuccess;
     if (group == kPerChannel)
@@ -490,12 +569,19 @@ hipError_t launch_quantize(const uint16_t* W, int64_t N, int64_t K, int64_t grou
                    : launch_quantize_rows<false>(W, N, K, packed, scales, nullptr, perm, stream);
     const int64_t groups = N * (K / group);
     if (groups == 0) return hipSuccess;
-    // the same 16 bytes per lane and two groups' loads in flight for every G
+    // the same 16 bytes per lane and U groups' loads a step for every G
+    constexpr int U = kQuantizeGroupsPerStep;
     switch (group) {
-        case 32: return launch_quantize_t<4, 2>(W, groups, K, perm, packed, scales, zeros, stream);
-        case 64: return launch_quantize_t<8, 2>(W, groups, K, perm, packed, scales, zeros, stream);
-        case 128: return launch_quantize_t<16, 2>(W, groups, K, perm, packed, scales, zeros, stream);
-        case 256: return launch_quantize_t<32, 2>(W, groups, K, perm, packed, scales, zeros, stream);
+        case 32:
+            return launch_quantize_t<4, U>(W, groups, K, perm, packed, scales, zeros, stream, num_cu);
+        case 64:
+            return launch_quantize_t<8, U>(W, groups, K, perm, packed, scales, zeros, stream, num_cu);
+        case 128:
+            return launch_quantize_t<16, U>(W, groups, K, perm, packed, scales, zeros, stream,
+                                            num_cu);
+        case 256:
+            return launch_quantize_t<32, U>(W, groups, K, perm, packed, scales, zeros, stream,
+                                            num_cu);
         default: return hipErrorInvalidValue;
     }
 }

@@ -23,7 +23,7 @@ __host__ __device__ inline int scales_per_row(int64_t K, int gshift) {
 // int32 [K] (column j of the result is column perm[j] of W).  zeros: NULL
 // for the symmetric quantizer, or int16 [N, K/group] for the asymmetric one.
 hipError_t launch_quantize(const uint16_t* W, int64_t N, int64_t K, int64_t group,
-                           uint32_t* packed, uint16_t* scales, hipStream_t stream,
+                           uint32_t* packed, uint16_t* scales, hipStream_t stream, int num_cu,
                            const int* perm = nullptr, int16_t* zeros = nullptr);
 
 // Q4_0 blocks: N rows of K/32 blocks of 18 bytes (fp16 d, then 16 code
