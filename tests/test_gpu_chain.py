@@ -55,7 +55,8 @@ def run_dependent(w4, weights, x0, use_chain, sync=None):
     [(4096, 4096)] * 8,
     [(256, 256)] * 64,
     [(128, 128), (128, 3), (128, 128)],
-], ids=["mixed", "square8", "small64", "tiny"])
+    [(3584, 32768), (32768, 1536), (1536, 32770)],
+], ids=["mixed", "square8", "small64", "tiny", "rows16"])
 def test_chain_dependent_bit_identical(w4, shapes):
     # make every stage's K equal the previous N (data flows stage to stage)
     fixed = [shapes[0]]

@@ -217,9 +217,13 @@ def check_linear(w4, orc, M, N, K, seed, algo, name="", full_limit=6e8):
 
 
 @pytest.mark.parametrize("N,K", [(1, 128), (7, 256), (37, 384), (300, 1152), (1000, 2048),
-                                 (2053, 4224)])
+                                 (2053, 4224), (5, 512), (1003, 1536), (37, 18944),
+                                 (32771, 512), (33003, 1536)])
 @pytest.mark.parametrize("algo", ["gemv", "valu", "mfma"])
 def test_linear_m1_small_and_ragged(w4, orc, N, K, algo):
+    """Ragged N.  K = 512 and 1536 (16 and 48 chunks of 32) with at least 128
+    rows per compute unit run the GEMV with four rows side by side, 16 lanes
+    each (fewer rows, or K = 18944, keep 64 lanes per row)."""
     check_linear(w4, orc, 1, N, K, seed=[5, N, K], algo=algo)
 
 

@@ -252,18 +252,29 @@ __global__ __launch_bounds__(WAVES * kWave) void gemv_kernel(
 //     block then gathers x[perm[j]] from LDS (an index outside [0, K) reads
 //     0) into the paired layout; the raw copy takes a second LDS region.
 // XPT: 16-byte activation blocks staged per thread (MMAX*K/8 <= XPT*threads).
-template <int MMAX, int R, int P, int WAVES, int XPT, bool ASYM, bool PERM>
+// LPR: lanes per row.  64: every lane of the wave works on the same R rows,
+// lane l taking chunks l, l + 64, ...; 16: the wave holds four rows side by
+// side per register slot (R * 4 rows a row group), lane l on row l / 16 and
+// chunks l % 16, l % 16 + 16, ..., the sum over each 16-lane segment.  A row
+// of K/32 chunks then fills whole steps when K/32 is a multiple of 16 but not
+// of 64 (K = 3584: 7 steps of 16 lanes instead of 2 steps of 64 with 16 idle
+// lanes in the second); chosen by gemv_lanes_per_row.
+template <int MMAX, int R, int P, int WAVES, int XPT, bool ASYM, bool PERM, int LPR>
 __global__ __launch_bounds__(WAVES * kWave) void gemv_persistent_kernel(
     const uint16_t* __restrict__ X, int M, const uint4* __restrict__ packed,
     const uint16_t* __restrict__ scales, const int16_t* __restrict__ zeros,
     uint16_t* __restrict__ Y, int N, int K, int gshift, const int* __restrict__ perm) {
+    static_assert(LPR == kWave || LPR == 16, "lanes per row");
+    constexpr int S = kWave / LPR;                         // rows side by side
+    constexpr int RG = R * S;                              // rows per row group
     extern __shared__ uint4 lds[];
     const int lane = threadIdx.x & (kWave - 1);
+    const int seg = lane / LPR, li = lane % LPR;           // row within a slot, lane in it
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int nchunks = K >> 5;
     if (nchunks == 0) return;  // K == 0 is launched on gemv_kernel, which writes the zeros
-    const int nsteps = (nchunks + kWave - 1) / kWave;     // chunk steps per row group
-    const int total_rg = (N + R - 1) / R;
+    const int nsteps = (nchunks + LPR - 1) / LPR;          // chunk steps per row group
+    const int total_rg = (N + RG - 1) / RG;
     const int stride_rg = gridDim.x * WAVES;
     const int first_rg = blockIdx.x * WAVES + wave;
     const int my_rg = first_rg < total_rg ? (total_rg - 1 - first_rg) / stride_rg + 1 : 0;
@@ -298,7 +309,7 @@ __global__ __launch_bounds__(WAVES * kWave) void gemv_persistent_kernel(
         if (ls == 0) {
             // new row group (or past the wave's work: an empty resource)
             const bool live = tl < T;
-            const int64_t row0 = (int64_t)lrg * R;
+            const int64_t row0 = (int64_t)lrg * RG;
             const int64_t rows_left = live ? (int64_t)N - row0 : 0;
             wr = buffer_rsrc(reinterpret_cast<const char*>(packed) + (live ? row0 * wrow_bytes : 0),
                              (uint64_t)rows_left * wrow_bytes);
@@ -308,18 +319,22 @@ __global__ __launch_bounds__(WAVES * kWave) void gemv_persistent_kernel(
                 zr = buffer_rsrc(reinterpret_cast<const char*>(zeros) + (live ? row0 * srow_bytes : 0),
                                  (uint64_t)rows_left * srow_bytes);
         }
-        const int voff_w = lane * 16 + ls * (kWave * 16);
-        const int voff_s = ((lane + ls * kWave) >> gshift) * 2;
+        // row r * S + seg of the group: seg in the lane offset, r * S in the
+        // scalar one (both count in the buffer's range check)
+        const int voff_w = seg * (int)wrow_bytes + (li + ls * LPR) * 16;
+        const int voff_s = seg * (int)srow_bytes + ((li + ls * LPR) >> gshift) * 2;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             typedef unsigned v4u __attribute__((ext_vector_type(4)));
             // streamed once: non-temporal (kStreamLoad) keeps them from
             // displacing reusable lines in L2
-            const v4u v = __builtin_amdgcn_raw_buffer_load_b128(wr, voff_w, r * wrow_bytes,
+            const v4u v = __builtin_amdgcn_raw_buffer_load_b128(wr, voff_w, r * S * wrow_bytes,
                                                                  kStreamLoad);
             wd[r] = make_uint4(v.x, v.y, v.z, v.w);
-            sd[r] = __builtin_amdgcn_raw_buffer_load_b16(sr, voff_s, r * srow_bytes, kStreamLoad);
-            zd[r] = ASYM ? (int16_t)__builtin_amdgcn_raw_buffer_load_b16(zr, voff_s, r * srow_bytes,
+            sd[r] = __builtin_amdgcn_raw_buffer_load_b16(sr, voff_s, r * S * srow_bytes,
+                                                         kStreamLoad);
+            zd[r] = ASYM ? (int16_t)__builtin_amdgcn_raw_buffer_load_b16(zr, voff_s,
+                                                                         r * S * srow_bytes,
                                                                          kStreamLoad)
                          : (int16_t)0;
         }
@@ -383,7 +398,7 @@ __global__ __launch_bounds__(WAVES * kWave) void gemv_persistent_kernel(
 #pragma unroll
         for (int i = 0; i < Q; ++i) {
             load(w[(i + P) % Q], sb[(i + P) % Q], zb[(i + P) % Q]);   // iteration t0 + i + P
-            const int c = lane + cs * kWave;
+            const int c = li + cs * LPR;
             const bool valid = c < nchunks;
             const int cx = min(c, nchunks - 1);
             // Steps past the wave's work (the ring's tail) skip the arithmetic;
@@ -409,9 +424,10 @@ __global__ __launch_bounds__(WAVES * kWave) void gemv_persistent_kernel(
                         if (m >= M) break;
 #pragma unroll
                         for (int r = 0; r < R; ++r) {
-                            const float v = wave_sum_lane63(acc[m][r]);
-                            const int row = crg * R + r;
-                            if (lane == kWave - 1 && row < N)
+                            const float v = LPR == kWave ? wave_sum_lane63(acc[m][r])
+                                                         : row16_sum(acc[m][r]);
+                            const int row = crg * RG + r * S + seg;
+                            if (li == LPR - 1 && row < N)
                                 Y[(size_t)m * N + row] = f32_to_f16_bits(v);
                             acc[m][r] = 0.0f;
                         }
@@ -454,7 +470,7 @@ hipError_t launch_gemv_t(const uint16_t* X, int64_t M, const uint32_t* packed,
 // 13.8-14.2 us with 1195 (4.67 blocks per CU leave the CUs with a fifth
 // block 7 % more work), 4096x14336 7.5-7.8 us against 8.6-8.9 us with 896.
 // Fewer row groups than waves on the chip: one wave per row group.
-template <int MMAX, int R, int P, int WAVES, int XPT, bool ASYM, bool PERM>
+template <int MMAX, int R, int P, int WAVES, int XPT, bool ASYM, bool PERM, int LPR>
 hipError_t launch_persistent_kern(const uint16_t* X, int64_t M, const uint32_t* packed,
                                   const uint16_t* scales, const int16_t* zeros, int64_t N,
                                   int64_t K, uint16_t* Y, hipStream_t stream, int num_cu,
@@ -465,21 +481,26 @@ hipError_t launch_persistent_xpt(const uint16_t* X, int64_t M, const uint32_t* p
                                  const uint16_t* scales, const int16_t* zeros, int64_t N,
                                  int64_t K, uint16_t* Y, hipStream_t stream, int num_cu,
                                  int blocks_per_cu, int gshift, const int* perm) {
-    if (perm != nullptr)
-        return launch_persistent_kern<MMAX, R, P, WAVES, XPT, ASYM, true>(
-            X, M, packed, scales, zeros, N, K, Y, stream, num_cu, blocks_per_cu, gshift, perm);
-    return launch_persistent_kern<MMAX, R, P, WAVES, XPT, ASYM, false>(
-        X, M, packed, scales, zeros, N, K, Y, stream, num_cu, blocks_per_cu, gshift, perm);
+#define W4A16_PERSISTENT_KERN(PERM, LPR)                                                     \
+    launch_persistent_kern<MMAX, R, P, WAVES, XPT, ASYM, PERM, LPR>(                         \
+        X, M, packed, scales, zeros, N, K, Y, stream, num_cu, blocks_per_cu, gshift, perm)
+    if constexpr (MMAX == 1) {
+        if (gemv_lanes_per_row(K, N, num_cu) == 16)
+            return perm != nullptr ? W4A16_PERSISTENT_KERN(true, 16)
+                                   : W4A16_PERSISTENT_KERN(false, 16);
+    }
+    return perm != nullptr ? W4A16_PERSISTENT_KERN(true, kWave) : W4A16_PERSISTENT_KERN(false, kWave);
+#undef W4A16_PERSISTENT_KERN
 }
 
-template <int MMAX, int R, int P, int WAVES, int XPT, bool ASYM, bool PERM>
+template <int MMAX, int R, int P, int WAVES, int XPT, bool ASYM, bool PERM, int LPR>
 hipError_t launch_persistent_kern(const uint16_t* X, int64_t M, const uint32_t* packed,
                                   const uint16_t* scales, const int16_t* zeros, int64_t N,
                                   int64_t K, uint16_t* Y, hipStream_t stream, int num_cu,
                                   int blocks_per_cu, int gshift, const int* perm) {
     // paired X; with perm also the raw copy it is gathered from
     const size_t lds = (size_t)(PERM ? 2 : 1) * MMAX * (K / 8) * sizeof(uint4);
-    auto kern = gemv_persistent_kernel<MMAX, R, P, WAVES, XPT, ASYM, PERM>;
+    auto kern = gemv_persistent_kernel<MMAX, R, P, WAVES, XPT, ASYM, PERM, LPR>;
     if (lds > 64 * 1024) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -498,7 +519,8 @@ hipError_t launch_persistent_kern(const uint16_t* X, int64_t M, const uint32_t* 
         resident = nb < 1 ? 1 : (nb > 255 ? 255 : nb);
         occ_cache.store(((uint64_t)lds << 8) | (uint64_t)resident, std::memory_order_relaxed);
     }
-    const int64_t total_rg = (N + R - 1) / R;
+    constexpr int64_t RG = (int64_t)R * (kWave / LPR);        // rows per row group
+    const int64_t total_rg = (N + RG - 1) / RG;
     const int64_t per_cu = (int64_t)num_cu * WAVES;
     int64_t blocks = (total_rg + WAVES - 1) / WAVES;
     if (total_rg >= per_cu) {

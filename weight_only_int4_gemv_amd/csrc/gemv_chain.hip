@@ -4,8 +4,10 @@
 // before it).
 //
 // Stage s computes y_s = x_s * W_s^T exactly as w4a16_gemv does (same lane
-// split, same arithmetic, same reduction order, so the outputs are
-// bit-identical), and x_s may be the output of any earlier stage.
+// split — 64 lanes per row, or 16 with four rows side by side where
+// gemv_lanes_per_row says so —, same arithmetic, same reduction order, so
+// the outputs are bit-identical), and x_s may be the output of any earlier
+// stage.
 //
 // One block per compute unit: W compute waves and C control waves.
 //   - Compute waves stream the weights of all stages through one ring of
@@ -85,14 +87,19 @@ __global__ __launch_bounds__((W + C) * kWave) void gemv_chain_kernel(ChainArgs a
 
     struct Geo {
         int nchunks, nsteps, total_rg, T;
+        int lpr, sh, S, RG;       // lanes per row (1 << sh), rows side by side, rows a group
         uint32_t wrow, srow;
     };
     auto geo = [&](int s, int first_rg) {
         Geo g;
         const int K = a.st[s].K, N = a.st[s].N;
         g.nchunks = K >> 5;
-        g.nsteps = (g.nchunks + kWave - 1) / kWave;
-        g.total_rg = (N + R - 1) / R;
+        g.lpr = gemv_lanes_per_row(K, N, gridDim.x);    // as w4a16_gemv (one block per CU)
+        g.sh = g.lpr == 16 ? 4 : 6;
+        g.S = kWave / g.lpr;
+        g.RG = R * g.S;
+        g.nsteps = (g.nchunks + g.lpr - 1) / g.lpr;
+        g.total_rg = (N + g.RG - 1) / g.RG;
         const int my = first_rg < g.total_rg ? (g.total_rg - 1 - first_rg) / G + 1 : 0;
         g.T = my * g.nsteps;             // the wave's iterations in stage s
         g.wrow = (uint32_t)K / 2;
@@ -110,16 +117,16 @@ __global__ __launch_bounds__((W + C) * kWave) void gemv_chain_kernel(ChainArgs a
             // outputs of stage s held in LDS -> y_s, device-coherent stores
             const Geo g = geo(s, 0);
             const int my_max = (g.total_rg + G - 1) / G;
-            const int per_wave = my_max * R;
+            const int per_wave = my_max * g.RG;
             const __amdgpu_buffer_rsrc_t yr = buffer_rsrc(a.st[s].y, (uint64_t)a.st[s].N * 2);
             for (int e = lane; e < W * per_wave; e += kWave) {
                 const int w = e / per_wave;
                 const int jr = e - w * per_wave;
-                const int i = jr / R;
-                const int r = jr - i * R;
+                const int i = jr / g.RG;
+                const int r = jr - i * g.RG;            // row within the group
                 const int rg = blockIdx.x * W + w + i * G;
                 if (rg < g.total_rg) {
-                    const int row = rg * R + r;
+                    const int row = rg * g.RG + r;
                     __builtin_amdgcn_raw_buffer_store_b16(ybuf[w * ycap + jr], yr, row * 2, 0,
                                                           kCoherent);
                 }
@@ -219,7 +226,7 @@ __global__ __launch_bounds__((W + C) * kWave) void gemv_chain_kernel(ChainArgs a
     auto load = [&](uint4 (&wd)[R], uint16_t (&sd)[R]) {
         if (ls == 0) {
             if (lst < a.count) {
-                const int64_t row0 = (int64_t)lrg * R;
+                const int64_t row0 = (int64_t)lrg * lg.RG;
                 const int64_t rows_left = (int64_t)a.st[lst].N - row0;
                 wr = buffer_rsrc(reinterpret_cast<const char*>(a.st[lst].packed) + row0 * lg.wrow,
                                  (uint64_t)rows_left * lg.wrow);
@@ -232,14 +239,17 @@ __global__ __launch_bounds__((W + C) * kWave) void gemv_chain_kernel(ChainArgs a
         }
         const uint32_t wrow = lst < a.count ? lg.wrow : 0u;
         const uint32_t srow = lst < a.count ? lg.srow : 0u;
-        const int voff_w = lane * 16 + ls * (kWave * 16);
-        const int voff_s = (lane >> 2) * 2 + ls * (kWave / 4 * 2);
+        // row r * S + seg of the group (seg in the lane offset), chunk li + ls * lpr
+        const int seg = lane >> lg.sh, c = (lane & (lg.lpr - 1)) + ls * lg.lpr;
+        const int voff_w = seg * (int)wrow + c * 16;
+        const int voff_s = seg * (int)srow + (c >> 2) * 2;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             typedef unsigned v4u __attribute__((ext_vector_type(4)));
-            const v4u v = __builtin_amdgcn_raw_buffer_load_b128(wr, voff_w, r * wrow, kStreamLoad);
+            const v4u v = __builtin_amdgcn_raw_buffer_load_b128(wr, voff_w, r * lg.S * wrow,
+                                                                 kStreamLoad);
             wd[r] = make_uint4(v.x, v.y, v.z, v.w);
-            sd[r] = __builtin_amdgcn_raw_buffer_load_b16(sr, voff_s, r * srow, kStreamLoad);
+            sd[r] = __builtin_amdgcn_raw_buffer_load_b16(sr, voff_s, r * lg.S * srow, kStreamLoad);
         }
         if (lst < a.count) {
             ++lt;
@@ -289,7 +299,8 @@ __global__ __launch_bounds__((W + C) * kWave) void gemv_chain_kernel(ChainArgs a
             load(w[(i + P) % Q], sb[(i + P) % Q]);
             if (t0 + i < total_T) {                                // wave-uniform
                 enter(cst);
-                const int c = lane + cs * kWave;
+                const int seg = lane >> cg.sh, li = lane & (cg.lpr - 1);
+                const int c = li + cs * cg.lpr;
                 const bool valid = c < cg.nchunks;
                 const int cx = min(c, cg.nchunks - 1);
                 const uint4* xp = lds + cx * 4;
@@ -308,9 +319,10 @@ __global__ __launch_bounds__((W + C) * kWave) void gemv_chain_kernel(ChainArgs a
                     cs = 0;
 #pragma unroll
                     for (int r = 0; r < R; ++r) {
-                        const float v = wave_sum_lane63(acc[r]);
-                        if (lane == kWave - 1)
-                            ybuf[wave * ycap + cj * R + r] = f32_to_f16_bits(v);
+                        const float v = cg.lpr == kWave ? wave_sum_lane63(acc[r])
+                                                        : row16_sum(acc[r]);
+                        if (li == cg.lpr - 1)
+                            ybuf[wave * ycap + cj * cg.RG + r * cg.S + seg] = f32_to_f16_bits(v);
                         acc[r] = 0.0f;
                     }
                     ++cj;
@@ -337,9 +349,19 @@ __global__ __launch_bounds__((W + C) * kWave) void gemv_chain_kernel(ChainArgs a
 template <int W, int C, int P>
 hipError_t launch_chain_t(const ChainArgs& args, int64_t max_n, hipStream_t stream, int num_cu,
                           int* blocks_out) {
+    // rows of a stage a wave finishes before its block writes them: the most
+    // row groups any wave gets, times the rows of a group (as the kernel's
+    // geometry: 2 rows a group, times 4 where 16 lanes share a row)
     const int G = num_cu * W;
-    const int64_t max_rg = (max_n + kChainR - 1) / kChainR;
-    const int ycap = (int)((max_rg + G - 1) / G) * kChainR;
+    int ycap = 0;
+    for (int s = 0; s < args.count; ++s) {
+        const int64_t rgsz =
+            (int64_t)kChainR * (kWave / gemv_lanes_per_row(args.st[s].K, args.st[s].N, num_cu));
+        const int64_t rgs = (args.st[s].N + rgsz - 1) / rgsz;
+        const int64_t rows = (rgs + G - 1) / G * rgsz;
+        if (rows > ycap) ycap = (int)rows;
+    }
+    (void)max_n;
     const size_t lds = (size_t)args.x_vecs * sizeof(uint4) + (size_t)W * ycap * 2;
     if (lds > 160 * 1024) return hipErrorInvalidValue;
     int occ = 0;

@@ -158,5 +158,14 @@ __device__ __forceinline__ float wave_sum_lane63(float v) {
     v = dpp_add<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
     return v;
 }
+// Sum over each 16-lane row (the first four steps above): every lane of a
+// row holds its row's total.
+__device__ __forceinline__ float row16_sum(float v) {
+    v = dpp_add<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+    v = dpp_add<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+    v = dpp_add<0x141, 0xF>(v);  // row_half_mirror
+    v = dpp_add<0x140, 0xF>(v);  // row_mirror
+    return v;
+}
 
 }  // namespace w4a16
