@@ -118,6 +118,17 @@ __device__ __forceinline__ float dot_word(uint32_t w, const uint4& xp, float acc
     return acc;
 }
 
+// Lanes of a wave that share one weight row in the M = 1 GEMV (the
+// persistent kernel and the dependent-sequence kernel use the same split, so
+// their sums are taken in the same order): 64, unless the row's K/32 chunks
+// are a multiple of 16 but not of 64 and the matrix has at least 128 rows
+// per compute unit, then 16 (four rows side by side, so no lane idles in a
+// row's last step; with fewer rows the 8-row groups would leave waves idle).
+__host__ __device__ inline int gemv_lanes_per_row(int64_t K, int64_t N, int num_cu) {
+    const int64_t chunks = K / 32;
+    return (chunks % 64 != 0 && chunks % 16 == 0 && N >= (int64_t)128 * num_cu) ? 16 : 64;
+}
+
 // Raw buffer resource over [base, base + bytes) for gfx9 (data format 32;
 // reads past `bytes` return 0 instead of touching memory).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint64_t bytes) {

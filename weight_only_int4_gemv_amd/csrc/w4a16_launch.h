@@ -35,17 +35,6 @@ hipError_t launch_quantize_q4_0(const uint16_t* W, int64_t N, int64_t K, uint8_t
 hipError_t launch_gemv_q4_0(const uint16_t* X, int64_t M, const uint8_t* blocks, int64_t N,
                             int64_t K, uint16_t* Y, hipStream_t stream, int num_cu);
 
-// Lanes of a wave that share one weight row in the M = 1 GEMV (the
-// persistent kernel and the dependent-sequence kernel use the same split, so
-// their sums are taken in the same order): 64, unless the row's K/32 chunks
-// are a multiple of 16 but not of 64 and the matrix has at least 128 rows
-// per compute unit, then 16 (four rows side by side, so no lane idles in a
-// row's last step; with fewer rows the 8-row groups would leave waves idle).
-__host__ __device__ inline int gemv_lanes_per_row(int64_t K, int64_t N, int num_cu) {
-    const int64_t chunks = K / 32;
-    return (chunks % 64 != 0 && chunks % 16 == 0 && N >= (int64_t)128 * num_cu) ? 16 : 64;
-}
-
 // VALU dot-product path, any M (M > 8 runs in slices of 8 rows).  gshift:
 // log2(group / 32), one scale per 2^gshift 32-code chunks (2 = group 128).
 // perm (device int32 [K], 16-byte aligned, or NULL): the weight's columns
