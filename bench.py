@@ -185,11 +185,19 @@ def secondary(torch, w4a16, inputs, dev, stream, main_workload="llama3-8b-sweep"
         torch.cuda.synchronize()
     del a
 
-    def timed(seq_fn, reps=5):
+    def timed(seq_fn, reps=5, warm_s=0.1):
+        """us per replay of a graph of seq_fn, after replaying it for about
+        warm_s seconds: the clocks drop while the host prepares the next
+        row's weights, and a row timed right away reads slow."""
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             seq_fn()
+        t0 = time.perf_counter()
         for _ in range(2):
+            g.replay()
+        torch.cuda.synchronize()
+        per = (time.perf_counter() - t0) / 2
+        for _ in range(min(500, int(warm_s / max(per, 1e-6)))):
             g.replay()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
