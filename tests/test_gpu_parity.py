@@ -885,14 +885,18 @@ def test_linear_asym_prefill_fp16_weights(w4, orc, M, N, K):
     check_linear_asym(w4, orc, M, N, K, 128, [51, M, N, K], plant=False)
 
 
-def test_linear_asym_wide_prefill_common_and_slow_launches(w4, orc):
-    """Enough 128 x 256 blocks to fill the compute units: the common-copy
-    launch leaves the blocks with planted groups (|z| > 1000, scale 0, ties)
-    to the slow-copy launch, which decides over the same 256 columns; every
-    output is computed exactly once and meets the bound."""
-    M, N, K = 520, 11620, 512
+@pytest.mark.parametrize("M,N,K", [(520, 11620, 512), (512, 8000, 512), (300, 6000, 1152)],
+                         ids=["128x256", "128x128", "64x128"])
+def test_linear_asym_wide_prefill_common_and_slow_launches(w4, orc, M, N, K):
+    """Prefill shapes with planted groups (|z| > 1000, scale 0, ties) in
+    several column blocks, on each asymmetric prefill tiling: where 128 x
+    256 blocks fill the compute units the common-copy launch leaves the
+    blocks with such groups to the slow-copy launch, which decides over the
+    same 256 columns; with fewer blocks (128 x 128 and 128 x 64 block tiles)
+    each block picks its copy.  Every output is computed exactly once and
+    meets the bound."""
     W = asym_weight(N, K, [52, N, K])
-    W[[300, 5001, 11611]] = W[[0, 1, 2]]        # planted rows in three more column blocks
+    W[[N // 40 * 1 + 300, N // 2 + 1, N - 9]] = W[[0, 1, 2]]   # planted rows in more column blocks
     packed, scales, zeros = orc.quantize_asym(W, group=128)
     X = inputs.activation(M, K, seed=[52, M])
     say("asym wide prefill M=%d N=%d K=%d" % (M, N, K))
