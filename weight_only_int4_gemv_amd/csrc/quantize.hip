@@ -212,63 +212,89 @@ __device__ __forceinline__ double recip_of_scale(double s) {
     return fma(r0, fma(-s, r0, 1.0), r0);
 }
 
-// Scale bits and zero point of a group (or row) from its reduced keys.
-__device__ __forceinline__ void asym_params(uint32_t kmax, uint32_t kmin_c, uint16_t& s_bits,
-                                            int16_t& zero) {
+// What the codes of a group need: the scale (binary64 and fp16 bits), 1/s
+// split in two fp32 parts, and the zero point.
+struct AsymCode {
+    double s;
+    float r_hi, r_lo, zf;
+    int16_t zero;
+    uint16_t s_bits;
+};
+__device__ __forceinline__ AsymCode asym_code(uint16_t s_bits, int16_t zero, double r) {
+    AsymCode c;
+    c.s = (double)f16_bits_to_f32(s_bits);
+    c.s_bits = s_bits;
+    c.zero = zero;
+    c.r_hi = (float)r;
+    c.r_lo = (float)(r - (double)c.r_hi);
+    c.zf = (float)zero;
+    return c;
+}
+// ... for a stored scale and zero point
+__device__ __forceinline__ AsymCode asym_code(uint16_t s_bits, int16_t zero) {
+    const double s = (double)f16_bits_to_f32(s_bits);
+    return asym_code(s_bits, zero, s == 0.0 ? 0.0 : recip_of_scale(s));
+}
+
+// Scale, zero point (and reciprocal) of a group (or row) from its reduced
+// keys.
+__device__ __forceinline__ AsymCode asym_params(uint32_t kmax, uint32_t kmin_c) {
     const double mx = (double)f16_bits_to_f32((uint16_t)f16_from_key(kmax));
     const double mn = (double)f16_bits_to_f32((uint16_t)f16_from_key(0xFFFFu - kmin_c));
-    s_bits = f16_rne_from_f64((mx - mn) / 15.0);         // 2^4 - 1 = 15
+    const uint16_t s_bits = f16_rne_from_f64((mx - mn) / 15.0);   // 2^4 - 1 = 15
     const double s = (double)f16_bits_to_f32(s_bits);
-    if (s == 0.0) {
-        zero = 0;
-        return;
-    }
-    const double p = mn * recip_of_scale(s);
-    double r = rint(p);
-    if (fabs(p - r) > 0.5 - 0x1p-20) r = rint(mn / s);   // a tie: the division decides
-    zero = (int16_t)(int)-r;
+    if (s == 0.0) return asym_code(s_bits, 0, 0.0);
+    const double r = recip_of_scale(s);
+    const double p = mn * r;
+    double q = rint(p);
+    if (fabs(p - q) > 0.5 - 0x1p-20) q = rint(mn / s);   // a tie: the division decides
+    return asym_code(s_bits, (int16_t)(int)-q, r);
 }
 
-__device__ __forceinline__ uint32_t codes8_asym(const uint4& v, uint16_t s_bits, int16_t zero);
-
-template <int LG>
-__device__ __forceinline__ uint32_t quantize8_asym(const uint4& v, uint16_t& s_bits,
-                                                   int16_t& zero) {
-    uint32_t kmax, kmin_c;
-    minmax_keys8(v, kmax, kmin_c);
-    asym_params(group_max<LG>(kmax), group_max<LG>(kmin_c), s_bits, zero);
-    return codes8_asym(v, s_bits, zero);
-}
-
-// The packed word of 8 elements against scale s_bits and zero point zero.
-__device__ __forceinline__ uint32_t codes8_asym(const uint4& v, uint16_t s_bits, int16_t zero) {
+// The packed word of 8 elements against a group's scale and zero point.
+__device__ __forceinline__ uint32_t codes8_asym(const uint4& v, const AsymCode& p) {
+    if (p.s == 0.0) return 0u;                           // every code 0
     const uint32_t h[8] = {v.x & 0xFFFFu, v.x >> 16, v.y & 0xFFFFu, v.y >> 16,
                            v.z & 0xFFFFu, v.z >> 16, v.w & 0xFFFFu, v.w >> 16};
-    const double s = (double)f16_bits_to_f32(s_bits);
-    if (s == 0.0) return 0u;                             // every code 0
-    const double r = recip_of_scale(s);
-    const float r_hi = (float)r;
-    const float r_lo = (float)(r - (double)r_hi);
-    const float zf = (float)zero;
     float c[8];
     float dist = 0.0f;                                   // largest |u - rint(u)|
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const float w = f16_bits_to_f32((uint16_t)h[i]);
-        const float u = fmaf(w, r_lo, fmaf(w, r_hi, zf));   // w / s + z, within 2^-19.9
+        const float u = fmaf(w, p.r_lo, fmaf(w, p.r_hi, p.zf));   // w / s + z, within 2^-19.9
         const float q = rintf(u);
         dist = fmaxf(dist, fabsf(u - q));
         c[i] = __builtin_amdgcn_fmed3f(q, 0.0f, 15.0f);
     }
     if (dist > 0.5f - 0x1p-15f) {                        // near a half-integer: redo exactly
-        const double z = (double)zero;
+        const double z = (double)p.zero;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const double q = rint((double)f16_bits_to_f32((uint16_t)h[i]) / s);
+            const double q = rint((double)f16_bits_to_f32((uint16_t)h[i]) / p.s);
             c[i] = (float)fmin(fmax(q + z, 0.0), 15.0);
         }
     }
     return pack_codes8(c);
+}
+
+// EPL elements of a lane (EPL / 8 vectors, all of one group) -> their packed
+// words, and the group's scale and zero point.
+template <int LG, int EPL>
+__device__ __forceinline__ void quantize_asym(const uint4 (&v)[EPL / 8], uint32_t (&words)[EPL / 8],
+                                              uint16_t& s_bits, int16_t& zero) {
+    uint32_t kmax = 0, kmin_c = 0;
+#pragma unroll
+    for (int i = 0; i < EPL / 8; ++i) {
+        uint32_t a, b;
+        minmax_keys8(v[i], a, b);
+        kmax = max(kmax, a);
+        kmin_c = max(kmin_c, b);
+    }
+    const AsymCode p = asym_params(group_max<LG>(kmax), group_max<LG>(kmin_c));
+    s_bits = p.s_bits;
+    zero = p.zero;
+#pragma unroll
+    for (int i = 0; i < EPL / 8; ++i) words[i] = codes8_asym(v[i], p);
 }
 
 }  // namespace
@@ -292,25 +318,32 @@ __device__ __forceinline__ uint32_t codes8_asym(const uint4& v, uint16_t s_bits,
 //
 // ASYM: the asymmetric quantizer, which also writes one int16 zero point per
 // group to `zeros` (laid out like the scales).
-template <int LG, int U, bool ASYM, bool PERM>
+template <int LG, int U, bool ASYM, bool PERM, int EPL>
 __global__ __launch_bounds__(256) void quantize_kernel(const uint4* __restrict__ W,
                                                        uint32_t* __restrict__ packed,
                                                        uint16_t* __restrict__ scales,
                                                        int16_t* __restrict__ zeros,
                                                        int64_t total_groups, int K,
                                                        const int* __restrict__ perm) {
+    static_assert(EPL == 8 || (EPL == 16 && ASYM && !PERM), "elements per lane");
+    constexpr int V = EPL / 8;                           // 16-byte vectors per lane and group
+    constexpr int GV = LG * V;                           // vectors (and packed words) per group
     typedef unsigned v4u __attribute__((ext_vector_type(4)));
     const int lg = threadIdx.x & (LG - 1);              // lane within the group
     const int64_t stride = (int64_t)gridDim.x * (blockDim.x / LG);
     const int64_t step = (int64_t)U * stride;
     const v4u* Wv = reinterpret_cast<const v4u*>(W);
 
-    auto load = [&](v4u (&a)[U], int64_t g) {
+    // vector i of a lane is vector i * LG + lg of its group (contiguous over
+    // the group's lanes for each i)
+    auto load = [&](v4u (&a)[U][V], int64_t g) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t gu = min(g + u * stride, total_groups - 1);
             if constexpr (!PERM) {
-                a[u] = __builtin_nontemporal_load(Wv + gu * LG + lg);   // W is read once
+#pragma unroll
+                for (int i = 0; i < V; ++i)   // W is read once
+                    a[u][i] = __builtin_nontemporal_load(Wv + gu * GV + i * LG + lg);
             } else {
                 const int64_t gpr = K / (LG * 8);                // groups per row
                 const int64_t n = gu / gpr;
@@ -322,27 +355,32 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint4* __restrict__
                     const int p = perm[col + i];
                     h[i] = (uint32_t)p < (uint32_t)K ? row[p] : 0u;
                 }
-                a[u] = (v4u){h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
-                             h[6] | (h[7] << 16)};
+                a[u][0] = (v4u){h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                                h[6] | (h[7] << 16)};
             }
         }
     };
-    auto work = [&](const v4u (&a)[U], int64_t g) {
+    auto work = [&](const v4u (&a)[U][V], int64_t g) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t gu = g + u * stride;
             if (gu < total_groups) {
-                const uint4 v = make_uint4(a[u].x, a[u].y, a[u].z, a[u].w);
+                uint4 v[V];
+#pragma unroll
+                for (int i = 0; i < V; ++i) v[i] = make_uint4(a[u][i].x, a[u][i].y, a[u][i].z, a[u][i].w);
                 uint16_t sb;
                 if constexpr (ASYM) {
                     int16_t zb;
-                    packed[gu * LG + lg] = quantize8_asym<LG>(v, sb, zb);
+                    uint32_t words[V];
+                    quantize_asym<LG, EPL>(v, words, sb, zb);
+#pragma unroll
+                    for (int i = 0; i < V; ++i) packed[gu * GV + i * LG + lg] = words[i];
                     if (lg == 0) {
                         scales[gu] = sb;
                         zeros[gu] = zb;
                     }
                 } else {
-                    packed[gu * LG + lg] = quantize8<LG>(v, sb);
+                    packed[gu * LG + lg] = quantize8<LG>(v[0], sb);
                     if (lg == 0) scales[gu] = sb;
                 }
             }
@@ -350,7 +388,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint4* __restrict__
     };
 
     const int64_t g0 = (int64_t)blockIdx.x * (blockDim.x / LG) + (threadIdx.x / LG);
-    v4u a[U], b[U];
+    v4u a[U][V], b[U][V];
     load(a, g0);
     for (int64_t g = g0; g < total_groups; g += 2 * step) {
         load(b, g + step);
@@ -428,11 +466,9 @@ __global__ __launch_bounds__(256) void row_scale_kernel(const uint16_t* __restri
             a = max(max(red[0][0], red[0][1]), max(red[0][2], red[0][3]));
             if constexpr (ASYM) {
                 b = max(max(red[1][0], red[1][1]), max(red[1][2], red[1][3]));
-                uint16_t sb;
-                int16_t zb;
-                asym_params(a, b, sb, zb);
-                scales[n] = sb;
-                zeros[n] = zb;
+                const AsymCode p = asym_params(a, b);
+                scales[n] = p.s_bits;
+                zeros[n] = p.zero;
             } else {
                 scales[n] = scale_of_absmax(a);
             }
@@ -455,7 +491,7 @@ __global__ __launch_bounds__(256) void row_codes_kernel(const uint16_t* __restri
         const int64_t n = i / wpr;
         const int c = (int)(i - n * wpr);
         const uint4 v = row_load8(W + n * (int64_t)K, c * 8, K, perm);
-        packed[i] = ASYM ? codes8_asym(v, scales[n], zeros[n]) : codes8(v, scales[n]);
+        packed[i] = ASYM ? codes8_asym(v, asym_code(scales[n], zeros[n])) : codes8(v, scales[n]);
     }
 }
 
@@ -522,7 +558,10 @@ hipError_t launch_quantize_q4_0(const uint16_t* W, int64_t N, int64_t K, uint8_t
     return hipGetLastError();
 }
 
-template <int LG, int U>
+// LG: lanes per group; EPL: elements per lane (G = LG * EPL); EPL = 16 only
+// for the asymmetric quantizer without perm, whose per-group scale, zero
+// point and reciprocal then serve 16 elements of each lane instead of 8.
+template <int LG, int U, int EPL = 8>
 hipError_t launch_quantize_t(const uint16_t* W, int64_t groups, int64_t K, const int* perm,
                              uint32_t* packed, uint16_t* scales, int16_t* zeros,
                              hipStream_t stream, int num_cu) {
@@ -531,9 +570,9 @@ hipError_t launch_quantize_t(const uint16_t* W, int64_t groups, int64_t K, const
     const uint4* Wv = reinterpret_cast<const uint4*>(W);
     // one resident round of blocks (the occupancy query's count per CU, at
     // most kQuantizeBlocksPerCu), walking the groups in grid strides
-#define W4A16_QUANTIZE(ASYM, PERM)                                                                \
+#define W4A16_QUANTIZE(ASYM, PERM, E)                                                             \
     do {                                                                                          \
-        auto kern = quantize_kernel<LG, U, ASYM, PERM>;                                           \
+        auto kern = quantize_kernel<LG, U, ASYM, PERM, E>;                                        \
         static std::atomic<int> resident{0};                                                      \
         int r = resident.load(std::memory_order_relaxed);                                         \
         if (r == 0) {                                                                             \
@@ -548,12 +587,14 @@ hipError_t launch_quantize_t(const uint16_t* W, int64_t groups, int64_t K, const
         hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, stream, Wv, packed, scales, \
                            zeros, groups, (int)K, perm);                                          \
     } while (0)
-    if (zeros != nullptr) {
-        if (perm != nullptr) W4A16_QUANTIZE(true, true);
-        else W4A16_QUANTIZE(true, false);
+    if constexpr (EPL == 16) {
+        W4A16_QUANTIZE(true, false, 16);
+    } else if (zeros != nullptr) {
+        if (perm != nullptr) W4A16_QUANTIZE(true, true, 8);
+        else W4A16_QUANTIZE(true, false, 8);
     } else {
-        if (perm != nullptr) W4A16_QUANTIZE(false, true);
-        else W4A16_QUANTIZE(false, false);
+        if (perm != nullptr) W4A16_QUANTIZE(false, true, 8);
+        else W4A16_QUANTIZE(false, false, 8);
     }
 #undef W4A16_QUANTIZE
     return hipGetLastError();
@@ -569,8 +610,24 @@ hipError_t launch_quantize(const uint16_t* W, int64_t N, int64_t K, int64_t grou
                    : launch_quantize_rows<false>(W, N, K, packed, scales, nullptr, perm, stream);
     const int64_t groups = N * (K / group);
     if (groups == 0) return hipSuccess;
-    // the same 16 bytes per lane and U groups' loads a step for every G
+    // the same 16 bytes per lane and U groups' loads a step for every G;
+    // the asymmetric quantizer without perm takes 32 bytes per lane from
+    // group 64 up
     constexpr int U = kQuantizeGroupsPerStep;
+    if (zeros != nullptr && perm == nullptr) {
+        switch (group) {
+            case 64:
+                return launch_quantize_t<4, U, 16>(W, groups, K, perm, packed, scales, zeros,
+                                                   stream, num_cu);
+            case 128:
+                return launch_quantize_t<8, U, 16>(W, groups, K, perm, packed, scales, zeros,
+                                                   stream, num_cu);
+            case 256:
+                return launch_quantize_t<16, U, 16>(W, groups, K, perm, packed, scales, zeros,
+                                                    stream, num_cu);
+            default: break;
+        }
+    }
     switch (group) {
         case 32:
             return launch_quantize_t<4, U>(W, groups, K, perm, packed, scales, zeros, stream, num_cu);
