@@ -56,7 +56,7 @@ constexpr int kCoherentSc1 = 16;           // cache policy: coherent at device s
 // copy only, deciding over the scale_bn columns around the block (the block
 // tile of the PART 1 launch it completes), so that the two launches split
 // the blocks between them exactly.
-template <int TM, int TN, int WM, int WN, int WK, bool ASYM, bool SPLIT, int PART>
+template <int TM, int TN, int WM, int WN, int WK, bool ASYM, bool SPLIT, int PART, bool SST>
 __global__ __launch_bounds__(WM * WN * WK * kWave)
 __attribute__((amdgpu_waves_per_eu(2))) void gemm_mfma_kernel(
     const uint16_t* __restrict__ X, int M, const uint4* __restrict__ packed,
@@ -76,7 +76,17 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_mfma_kernel(
     // same for every thread.
     constexpr bool SLOT_UNIFORM = (BM * 16) % NT == 0;
     constexpr int LDS_STAGE = WK * BM * kLdaVec;      // uint4 per A buffer
-    extern __shared__ uint4 lds[];                    // [2][WK][BM][kLdaVec]
+    extern __shared__ uint4 lds[];                    // [2][WK][BM][kLdaVec], then (SST)
+                                                      // [2][kinds][WK][BN] scales, zero points
+    // SST (one scale per step or fewer, group >= 128): the scales (and zero
+    // points) of a step are staged through LDS beside its A tile, one 2-byte
+    // load per column and group slot for the whole block, instead of one per
+    // lane, row and step (the lanes of a column would otherwise issue the
+    // same scattered 2-byte loads from every wave).
+    constexpr int KINDS = ASYM ? 2 : 1;
+    constexpr int SCOLS = WK * BN;                    // scales per step and block
+    constexpr int S_PER_THREAD = SST ? (KINDS * SCOLS + NT - 1) / NT : 1;
+    static_assert(!SST || BN % kWave == 0, "a wave stages one kind and group slot");
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
@@ -142,6 +152,49 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_mfma_kernel(
                            (uint64_t)(N - n_blk) * srow)
              : sr;
 
+    // Scale staging entries of this thread (SST): entry e = thread + i NT is
+    // (kind, group slot, column); a wave's entries are of one kind.
+    uint16_t* const slds = reinterpret_cast<uint16_t*>(lds + 2 * LDS_STAGE);
+    uint32_t st_row[S_PER_THREAD];
+    int st_slot[S_PER_THREAD], st_idx[S_PER_THREAD];
+    bool st_zero[S_PER_THREAD], st_live[S_PER_THREAD];
+#pragma unroll
+    for (int i = 0; i < S_PER_THREAD; ++i) {
+        // kind, slot and liveness from the wave's first entry (BN is a
+        // multiple of the wave, so they are the same for all its lanes)
+        const int e_wave = __builtin_amdgcn_readfirstlane(((int)threadIdx.x & ~(kWave - 1)) + i * NT);
+        const int col = ((int)threadIdx.x + i * NT) % BN;
+        st_live[i] = e_wave < KINDS * SCOLS;
+        st_zero[i] = e_wave >= SCOLS;
+        st_slot[i] = (e_wave % SCOLS) / BN;
+        st_row[i] = (uint32_t)(min(n_blk + col, N - 1) - n_blk) * srow;
+        st_idx[i] = ((st_zero[i] ? 1 : 0) * WK + st_slot[i]) * BN + col;
+    }
+    // Entries past the last group read 0 through an empty resource (scale 0,
+    // zero point 0: such a group's codes are 8 and its A slot stale, so its
+    // product must vanish).
+    const __amdgpu_buffer_rsrc_t s_empty = buffer_rsrc(scales, 0);
+    uint32_t s_regs[S_PER_THREAD];
+    auto load_s = [&](int step) {
+        if constexpr (SST) {
+#pragma unroll
+            for (int i = 0; i < S_PER_THREAD; ++i) {
+                const int g = step * WK + st_slot[i];
+                const int sg = (g_lo + g) >> (gshift - 2);
+                const bool live = st_live[i] && g < ngroups;      // wave-uniform
+                s_regs[i] = __builtin_amdgcn_raw_buffer_load_b16(
+                    live ? (st_zero[i] ? zr : sr) : s_empty, st_row[i] + (uint32_t)sg * 2u, 0, 0);
+            }
+        }
+    };
+    auto store_s = [&](int buf) {
+        if constexpr (SST) {
+#pragma unroll
+            for (int i = 0; i < S_PER_THREAD; ++i)
+                if (st_live[i]) slds[buf * KINDS * SCOLS + st_idx[i]] = (uint16_t)s_regs[i];
+        }
+    };
+
     // A staging: vector i of the stage is (group slot, row, 8-block).  A
     // slot past the last group keeps its previous (finite) values; the B of
     // such a group is zero.
@@ -174,10 +227,15 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_mfma_kernel(
             for (int tn = 0; tn < TN; ++tn) {
                 const v4u v = __builtin_amdgcn_raw_buffer_load_b128(pr, b_off[tn], ga * 64, 0);
                 b.w[tn] = make_uint4(v.x, v.y, v.z, v.w);
-                b.s[tn] = __builtin_amdgcn_raw_buffer_load_b16(sr, s_off[tn], sg * 2, 0);
-                b.z[tn] = ASYM ? (int)(int16_t)__builtin_amdgcn_raw_buffer_load_b16(
-                                     zr, s_off[tn], sg * 2, 0)
-                               : 0;
+                if constexpr (SST) {
+                    b.s[tn] = 0;                         // read from LDS in the step
+                    b.z[tn] = 0;
+                } else {
+                    b.s[tn] = __builtin_amdgcn_raw_buffer_load_b16(sr, s_off[tn], sg * 2, 0);
+                    b.z[tn] = ASYM ? (int)(int16_t)__builtin_amdgcn_raw_buffer_load_b16(
+                                         zr, s_off[tn], sg * 2, 0)
+                                   : 0;
+                }
             }
         } else {
 #pragma unroll
@@ -207,6 +265,14 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_mfma_kernel(
     auto step_body = [&](int step, BRegs& cur, auto clamp) __attribute__((always_inline)) {
         const uint4* abase =
             lds + (step & 1) * LDS_STAGE + (wk * BM + wm * TM * 16 + l16) * kLdaVec + 4 * j;
+        if constexpr (SST) {
+            const uint16_t* sb = slds + (step & 1) * KINDS * SCOLS + wk * BN + wn * TN * 16 + l16;
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn) {
+                cur.s[tn] = sb[tn * 16];
+                if constexpr (ASYM) cur.z[tn] = (int)(int16_t)sb[WK * BN + tn * 16];
+            }
+        }
         if constexpr (ASYM) {
             // Common blocks (every scale below 64, every |z| <= 1000): fp16
             // weights s * (n - z) from the exact codes n - z, |s (n - z)| <
@@ -421,8 +487,10 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_mfma_kernel(
         }
         if (step + 1 < nsteps) {
             store_a((step + 1) & 1, a_regs);
+            store_s((step + 1) & 1);
             if (step + 2 < nsteps) {
                 load_a(step + 2, a_regs);
+                load_s(step + 2);
                 load_b(step + 2, cur);    // cur is consumed; it next serves step s + 2
             }
         }
@@ -497,10 +565,13 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_mfma_kernel(
     }
 
     load_a(0, a_regs);
+    load_s(0);
     load_b(0, b0);
     store_a(0, a_regs);
+    store_s(0);
     if (nsteps > 1) {
         load_a(1, a_regs);
+        load_s(1);
         load_b(1, b1);
     }
     if constexpr (PART != 2) {
@@ -620,17 +691,18 @@ __attribute__((amdgpu_waves_per_eu(2))) void gemm_mfma_kernel(
 namespace {
 
 template <int TM, int TN, int WM, int WN, int WK, bool ASYM = false, bool SPLIT = false,
-          int PART = 0>
-hipError_t launch_mfma_t(const uint16_t* X, int64_t M, const uint32_t* packed,
-                         const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y,
-                         hipStream_t stream, int gshift, const int16_t* zeros = nullptr,
-                         const TiledSplit* split = nullptr, int scan_bn = 0) {
+          int PART = 0, bool SST = false>
+hipError_t launch_mfma_sst(const uint16_t* X, int64_t M, const uint32_t* packed,
+                           const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y,
+                           hipStream_t stream, int gshift, const int16_t* zeros,
+                           const TiledSplit* split, int scan_bn) {
     constexpr int BM = 16 * TM * WM;
     constexpr int BN = 16 * TN * WN;
     const size_t a_bytes = (size_t)2 * WK * BM * kLdaVec * sizeof(uint4);   // two A buffers
+    const size_t s_bytes = SST ? (size_t)2 * (ASYM ? 2 : 1) * WK * BN * 2 : 0;   // staged scales
     const size_t red_bytes = (size_t)(WK - 1) * WM * WN * TM * TN * 64 * sizeof(float4_t);
-    const size_t lds = a_bytes > red_bytes ? a_bytes : red_bytes;
-    auto kern = gemm_mfma_kernel<TM, TN, WM, WN, WK, ASYM, SPLIT, PART>;
+    const size_t lds = a_bytes + s_bytes > red_bytes ? a_bytes + s_bytes : red_bytes;
+    auto kern = gemm_mfma_kernel<TM, TN, WM, WN, WK, ASYM, SPLIT, PART, SST>;
     if (lds > 64 * 1024) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -645,6 +717,29 @@ hipError_t launch_mfma_t(const uint16_t* X, int64_t M, const uint32_t* packed,
                        SPLIT ? split->counters : nullptr,
                        SPLIT ? reinterpret_cast<float4_t*>(split->partials) : nullptr, scan_bn);
     return hipGetLastError();
+}
+
+// The prefill tiles (more than 64 rows of X) stage the scales through LDS
+// for group 128, and the scales and zero points of asymmetric weights for
+// every group from 128 up (one scale per step or fewer); smaller groups and
+// the few-row tiles load them per lane.  Measured at M = 512 (graph replays,
+// bit-identical outputs): asymmetric 4096x14336 76.3 against 85.5 us,
+// 14336x4096 107.5 against 110.5 us; symmetric group 128 4096x14336 66.8-67.1
+// against 67.4-67.8 us (M = 128: 28.5-29.6 against 30.1-30.3 us); symmetric
+// group 256 and per channel 0.5-1.5 % slower, so they keep per-lane loads.
+template <int TM, int TN, int WM, int WN, int WK, bool ASYM = false, bool SPLIT = false,
+          int PART = 0>
+hipError_t launch_mfma_t(const uint16_t* X, int64_t M, const uint32_t* packed,
+                         const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y,
+                         hipStream_t stream, int gshift, const int16_t* zeros = nullptr,
+                         const TiledSplit* split = nullptr, int scan_bn = 0) {
+    if constexpr (16 * TM * WM >= 64 && (16 * TN * WN) % kWave == 0) {
+        if ((ASYM ? gshift >= 2 : gshift == 2) && M > 64)
+            return launch_mfma_sst<TM, TN, WM, WN, WK, ASYM, SPLIT, PART, true>(
+                X, M, packed, scales, N, K, Y, stream, gshift, zeros, split, scan_bn);
+    }
+    return launch_mfma_sst<TM, TN, WM, WN, WK, ASYM, SPLIT, PART, false>(
+        X, M, packed, scales, N, K, Y, stream, gshift, zeros, split, scan_bn);
 }
 
 // Tile shapes by M for the tiled kernel (the symmetric path sends M <= 64
