@@ -23,7 +23,9 @@
 // per-thread 32-bit offset from the block's first row, fixed for the whole
 // K loop (rows past M or N clamped to the last row), so the loop has no
 // masking; X is double-buffered in LDS (one barrier per K step) and the B
-// registers of two steps alternate.
+// registers of two steps alternate.  The prefill tiles (SST) stage each
+// step's scales (and zero points) through LDS beside its X tile: one 2-byte
+// load per column for the whole block instead of one per lane and wave.
 // Precision: fp16(s*q) has relative error <= 2^-11, so |y - y_exact| <=
 // 2^-11 sum |x w| plus fp32 accumulation error, inside the 1e-3 sum |x w|
 // allowance for every K.  The block scans its scales once: a group with
