@@ -875,13 +875,13 @@ def test_linear_asym_batched_wave_grids(w4, orc, M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(512, 8192, 1024), (300, 11000, 640), (250, 7200, 384),
-                                   (200, 3000, 512)])
+                                   (200, 3000, 512), (512, 4096, 3072)])
 def test_linear_asym_prefill_fp16_weights(w4, orc, M, N, K):
     """Prefill-sized asymmetric products whose blocks all take the fp16
     weight copy (skewed layer-like weights: scales below 64, zero points in
     [0, 15]) on each prefill block tile (128 x 128 blocks when they fill the
-    compute units, 128 x 64 and 64 x 64 blocks with two waves over K), M and
-    N ragged."""
+    compute units, 64 x 128 blocks of 32-column wave tiles and 64 x 64 blocks
+    with two waves over K), M and N ragged."""
     check_linear_asym(w4, orc, M, N, K, 128, [51, M, N, K], plant=False)
 
 
@@ -892,7 +892,7 @@ def test_linear_asym_wide_prefill_common_and_slow_launches(w4, orc, M, N, K):
     several column blocks, on each asymmetric prefill tiling: where 128 x
     256 blocks fill the compute units the common-copy launch leaves the
     blocks with such groups to the slow-copy launch, which decides over the
-    same 256 columns; with fewer blocks (128 x 128 and 128 x 64 block tiles)
+    same 256 columns; with fewer blocks (128 x 128 and 64 x 128 block tiles)
     each block picks its copy.  Every output is computed exactly once and
     meets the bound."""
     W = asym_weight(N, K, [52, N, K])
@@ -909,12 +909,14 @@ def test_linear_asym_wide_prefill_common_and_slow_launches(w4, orc, M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(65, 300, 1024), (65, 300, 512), (512, 8192, 1024),
-                                   (520, 11620, 512)])
+                                   (520, 11620, 512), (512, 4096, 1024), (450, 3584, 2048)])
 def test_linear_asym_large_scales(w4, orc, M, N, K):
     """Asymmetric weights with scales of 64 and more (the tiled kernel's
     slow copy: fp16 weights s * (n - zc) clamped to +-65504), including
     groups that hold +-65504, against the oracle (rows of eight scales:
-    the 16-byte scale scan; of four: the 2-byte one; both block shapes)."""
+    the 16-byte scale scan; of four: the 2-byte one; every block shape:
+    64 x 64, 128 x 128, the two-launch 128 x 256, 64 x 128 with 32-column
+    wave tiles)."""
     rng = np.random.default_rng([49, M, N, K])
     W = (rng.standard_normal((N, K)) * 3000.0).astype(np.float16)
     W[::5, 7] = np.float16(65504.0)

@@ -780,7 +780,12 @@ hipError_t launch_tiled(const uint16_t* X, int64_t M, const uint32_t* packed,
         // blocks decide over the 256 columns of the first launch's block, so
         // every block is computed once; elsewhere they return before loading
         // anything).  Otherwise 16-column wave tiles with both copies: 128 x
-        // 128 blocks, 128 x 64 and 64 x 64 blocks with two waves over K.
+        // 128 blocks, 128 x 64 and 64 x 64 blocks with two waves over K; with
+        // one scale per step or fewer (staged through LDS) 64 x 128 blocks of
+        // 64 x 32 wave tiles, two waves over K, before 128 x 64 (M = 512:
+        // 14336x4096 91.2 against 107.0 us, 18944x3584 125.3 against 143.5,
+        // 4096x4096 28.8 against 33.1; at group 32 they were slower, 122
+        // against 113 us).
         if (fills(128, 256)) {
             const hipError_t e = launch_mfma_t<8, 2, 1, 8, 1, true, false, 1>(
                 X, M, packed, scales, N, K, Y, stream, gshift, zeros);
@@ -789,6 +794,7 @@ hipError_t launch_tiled(const uint16_t* X, int64_t M, const uint32_t* packed,
                 X, M, packed, scales, N, K, Y, stream, gshift, zeros, nullptr, 256);
         }
         if (fills(128, 128)) return W4A16_TILED(8, 1, 1, 8, 1);
+        if (gshift >= 2 && fills(64, 128)) return W4A16_TILED(4, 2, 1, 4, 2);
         if (fills(128, 64)) return W4A16_TILED(8, 1, 1, 4, 2);
         return W4A16_TILED(4, 1, 1, 4, 2);
     } else {
