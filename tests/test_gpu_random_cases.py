@@ -3,7 +3,8 @@
 kernel family (automatic, VALU, matrix cores), M from one token to a
 512-token prompt, ragged N, K from 128 to 6144 — each against the oracle:
 the GPU quantizer's bits where it takes the combination, and every output of
-w4a16_linear within |y - y_ref| <= oracle.tolerance."""
+w4a16_linear within |y - y_ref| <= oracle.tolerance; and seeded long-K
+shapes through w4a16_gemm_ws (K split over blocks where the planner splits)."""
 import numpy as np
 import pytest
 
@@ -13,7 +14,7 @@ from weight_only_int4_gemv_amd import inputs
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 
-N_CASES = 48
+N_CASES = 144
 MS = [1, 2, 3, 4, 5, 8, 13, 16, 17, 31, 32, 33, 64, 65, 100, 130, 257, 512]
 GROUPS = [32, 64, 128, 256, -1]          # -1: one scale per row
 ALGOS = [None, "valu", "mfma"]
@@ -109,5 +110,51 @@ def test_random_case(w4, orc, case):
         Yref, Yabs = orc.matmul(Xp, packed, scales, group=og)
     err = np.abs(Yg - Yref)
     bad = np.argwhere(~(err <= oracle.tolerance(Yref, Yabs)))
+    assert bad.size == 0, "%d outputs out of tolerance, first %s: got %r want %r" % (
+        len(bad), bad[0], Yg[tuple(bad[0])], Yref[tuple(bad[0])])
+
+
+# K split over blocks through a workspace (w4a16_gemm_ws, group 128): long
+# rows and few columns, where the planner splits K for batched decode (M <= 32)
+# or for prefill (M > 64); shapes it does not split run as w4a16_gemm.
+WS_MS = [5, 8, 13, 16, 24, 32, 65, 100, 200, 300, 512]
+
+
+def draw_ws(i):
+    rng = np.random.default_rng([20261204, i])
+    K = 128 * int(rng.integers(16, 129))                 # 2048 .. 16384
+    N = int(rng.integers(16, 4097))
+    M = WS_MS[int(rng.integers(len(WS_MS)))]
+    while M * N * K > 2e8 and N > 16:
+        N //= 2
+    return {"M": M, "N": N, "K": K, "seed": [20261204, i]}
+
+
+WS_CASES = [draw_ws(i) for i in range(24)]
+
+
+def test_ws_cases_reach_both_splits(w4):
+    """The long-K draw includes shapes the planner splits for batched decode
+    (M <= 32) and for prefill (M > 64), and shapes it leaves unsplit."""
+    split = [(c["M"], w4.gemm_workspace(c["M"], c["N"], c["K"]).numel() > 1) for c in WS_CASES]
+    assert any(s for m, s in split if m <= 32) and any(s for m, s in split if m > 64)
+    assert not all(s for _, s in split)
+
+
+@pytest.mark.parametrize("case", WS_CASES,
+                         ids=["%d-M%d-N%d-K%d" % (i, c["M"], c["N"], c["K"])
+                              for i, c in enumerate(WS_CASES)])
+def test_random_ws_case(w4, orc, case):
+    M, N, K = case["M"], case["N"], case["K"]
+    print("[ws case] M=%d N=%d K=%d" % (M, N, K), flush=True)
+    W = inputs.weight(N, K, seed=case["seed"])
+    X = inputs.activation(M, K, seed=[1000] + case["seed"])
+    packed, scales = orc.quantize(W)
+    ws = w4.gemm_workspace(M, N, K)
+    Yd = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    w4.gemm_ws(dev(X), dev(packed.view(np.int32)), dev(scales.view(np.float16)), ws, Yd)
+    Yg = Yd.cpu().numpy().astype(np.float64)
+    Yref, Yabs = orc.matmul(X, packed, scales)
+    bad = np.argwhere(~(np.abs(Yg - Yref) <= oracle.tolerance(Yref, Yabs)))
     assert bad.size == 0, "%d outputs out of tolerance, first %s: got %r want %r" % (
         len(bad), bad[0], Yg[tuple(bad[0])], Yref[tuple(bad[0])])
