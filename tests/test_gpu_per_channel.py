@@ -44,8 +44,11 @@ def planted(N, K, seed):
 
 
 @pytest.mark.parametrize("N,K", [(3, 128), (7, 256), (37, 768), (129, 1536), (1000, 4096),
-                                 (300, 14336), (64, 18944)])
+                                 (300, 14336), (64, 18944), (9, 20480), (5, 32768), (5, 33024)])
 def test_quantize_per_channel_bit_exact(w4, orc, N, K):
+    """One pass per row (the row held in registers: up to 1024, 2048 or 4096
+    chunks of 8 a row) and, past 32768 columns, the row reduction followed by
+    the codes: scales and packed words bit-exact with the oracle at G = K."""
     say("quantize per channel N=%d K=%d" % (N, K))
     W = planted(N, K, [61, N, K])
     pg, sg = w4.quantize(dev(W), group=w4.PER_CHANNEL)
@@ -61,7 +64,7 @@ def test_quantize_per_channel_bit_exact(w4, orc, N, K):
 
 
 @pytest.mark.parametrize("perm_kind", [None, "reverse", "random"])
-@pytest.mark.parametrize("N,K", [(37, 768), (300, 4096)])
+@pytest.mark.parametrize("N,K", [(37, 768), (300, 4096), (20, 14336), (9, 33024)])
 def test_quantize_per_channel_asym_bit_exact(w4, orc, perm_kind, N, K):
     say("quantize asym per channel N=%d K=%d perm=%s" % (N, K, perm_kind))
     W = inputs.weight_skewed(N, K, seed=[62, N, K])

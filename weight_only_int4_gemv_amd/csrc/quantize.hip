@@ -495,10 +495,92 @@ __global__ __launch_bounds__(256) void row_codes_kernel(const uint16_t* __restri
     }
 }
 
+// One pass for rows of up to 256 * CPT chunks: every thread keeps its
+// chunks of the row (c = thread + 256 i) in registers, the block reduces them
+// to the row's scale (and zero point), and each thread then forms the codes
+// of the chunks it holds, so W is read once where the two kernels above read
+// it twice.  The reduction, the scale and the codes are those functions'
+// own, so the bits are the same.
+template <bool ASYM, int CPT>
+__global__ __launch_bounds__(256) void row_quantize_kernel(const uint16_t* __restrict__ W,
+                                                           int64_t N, int K,
+                                                           uint32_t* __restrict__ packed,
+                                                           uint16_t* __restrict__ scales,
+                                                           int16_t* __restrict__ zeros,
+                                                           const int* __restrict__ perm) {
+    __shared__ uint32_t red[2][4];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int chunks = K >> 3;
+    for (int64_t n = blockIdx.x; n < N; n += gridDim.x) {
+        const uint16_t* row = W + n * (int64_t)K;
+        uint4 v[CPT];
+        uint32_t a = 0, b = 0;           // absmax; or max key, max complemented key
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int c = (int)threadIdx.x + i * 256;
+            v[i] = make_uint4(0, 0, 0, 0);
+            if (c < chunks) {
+                v[i] = row_load8(row, c * 8, K, perm);
+                if constexpr (ASYM) {
+                    uint32_t ka, kb;
+                    minmax_keys8(v[i], ka, kb);
+                    a = max(a, ka);
+                    b = max(b, kb);
+                } else {
+                    a = max(a, absmax8(v[i]));
+                }
+            }
+        }
+        a = wave_max64(a);
+        if constexpr (ASYM) b = wave_max64(b);
+        if (lane == 0) {
+            red[0][wave] = a;
+            red[1][wave] = b;
+        }
+        __syncthreads();
+        a = max(max(red[0][0], red[0][1]), max(red[0][2], red[0][3]));
+        if constexpr (ASYM) b = max(max(red[1][0], red[1][1]), max(red[1][2], red[1][3]));
+        __syncthreads();                 // red is reused by the next row
+        uint32_t* const prow = packed + n * (int64_t)chunks;
+        if constexpr (ASYM) {
+            const AsymCode p = asym_params(a, b);
+            if (threadIdx.x == 0) {
+                scales[n] = p.s_bits;
+                zeros[n] = p.zero;
+            }
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) {
+                const int c = (int)threadIdx.x + i * 256;
+                if (c < chunks) prow[c] = codes8_asym(v[i], p);
+            }
+        } else {
+            const uint16_t sb = scale_of_absmax(a);
+            if (threadIdx.x == 0) scales[n] = sb;
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) {
+                const int c = (int)threadIdx.x + i * 256;
+                if (c < chunks) prow[c] = codes8(v[i], sb);
+            }
+        }
+    }
+}
+
 template <bool ASYM>
 hipError_t launch_quantize_rows(const uint16_t* W, int64_t N, int64_t K, uint32_t* packed,
                                 uint16_t* scales, int16_t* zeros, const int* perm,
                                 hipStream_t stream) {
+    // one block per row (the grid walks the rest past 2^20 rows)
+    const int64_t chunks = K / 8;
+    const unsigned rblocks = (unsigned)(N < ((int64_t)1 << 20) ? N : ((int64_t)1 << 20));
+#define W4A16_ROWS(CPT)                                                                     \
+    hipLaunchKernelGGL((row_quantize_kernel<ASYM, CPT>), dim3(rblocks), dim3(256), 0, stream, \
+                       W, N, (int)K, packed, scales, zeros, perm);                          \
+    return hipGetLastError()
+    if (chunks <= 256 * 4) { W4A16_ROWS(4); }
+    if (chunks <= 256 * 8) { W4A16_ROWS(8); }
+    if (chunks <= 256 * 16) { W4A16_ROWS(16); }
+#undef W4A16_ROWS
+    // longer rows: the row reduction, then the codes
     const int64_t sblocks = N < 4096 ? N : 4096;
     hipLaunchKernelGGL((row_scale_kernel<ASYM>), dim3((unsigned)sblocks), dim3(256), 0, stream,
                        W, N, (int)K, scales, zeros, perm);
@@ -600,6 +682,68 @@ hipError_t launch_quantize_t(const uint16_t* W, int64_t groups, int64_t K, const
     return hipGetLastError();
 }
 
+// Weights in their own column order, on a flat grid: a slot is EPL
+// consecutive elements (EPL / 8 chunks of 8) of one group; block b takes the
+// slots [b 256 CPT, (b + 1) 256 CPT) (thread t the slots t + 256 i), issues
+// all their loads first and then quantizes them, LG lanes a group with the
+// per-lane arithmetic of quantize_kernel (a group never straddles a block:
+// 256 is a multiple of LG, and groups never straddle rows).  Measured against
+// the persistent quantize_kernel (bit-identical): symmetric (CPT 2)
+// 28672x8192 106-109 against 112-116 us, 14336x4096 27.0-27.5 against
+// 30.2-31.7 us at every group size; asymmetric (CPT 1, 16 elements a lane
+// from group 64 up) 14336x4096 31.0-32.3 against 37.6-38.7 us from group 64
+// up, 40.5-40.9 against 47.0 us at group 32, 28672x8192 115-118 against
+// 131-137 us.
+template <int LG, int CPT, bool ASYM, int EPL>
+__global__ __launch_bounds__(256) void quantize_flat_kernel(const uint4* __restrict__ W,
+                                                            int64_t slots,
+                                                            uint32_t* __restrict__ packed,
+                                                            uint16_t* __restrict__ scales,
+                                                            int16_t* __restrict__ zeros) {
+    static_assert(EPL == 8 || (EPL == 16 && ASYM), "elements per lane");
+    constexpr int V = EPL / 8;
+    const int64_t base = (int64_t)blockIdx.x * (256 * CPT) + threadIdx.x;
+    uint4 v[CPT][V];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+        const int64_t e = base + (int64_t)i * 256;
+#pragma unroll
+        for (int k = 0; k < V; ++k)
+            v[i][k] = e < slots ? W[e * V + k] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+        const int64_t e = base + (int64_t)i * 256;
+        // every lane takes part in the group reductions
+        uint32_t words[V];
+        uint16_t sb;
+        int16_t z = 0;
+        if constexpr (ASYM)
+            quantize_asym<LG, EPL>(v[i], words, sb, z);
+        else
+            words[0] = quantize8<LG>(v[i][0], sb);
+        if (e < slots) {
+#pragma unroll
+            for (int k = 0; k < V; ++k) packed[e * V + k] = words[k];
+            if ((threadIdx.x & (LG - 1)) == 0) {
+                scales[e / LG] = sb;
+                if constexpr (ASYM) zeros[e / LG] = z;
+            }
+        }
+    }
+}
+
+template <int LG, int CPT, bool ASYM, int EPL>
+hipError_t launch_quantize_flat(const uint16_t* W, int64_t N, int64_t K, uint32_t* packed,
+                                uint16_t* scales, int16_t* zeros, hipStream_t stream) {
+    const int64_t slots = N * (K / EPL);
+    const int64_t blocks = (slots + 256 * CPT - 1) / (256 * CPT);
+    hipLaunchKernelGGL((quantize_flat_kernel<LG, CPT, ASYM, EPL>), dim3((unsigned)blocks),
+                       dim3(256), 0, stream, reinterpret_cast<const uint4*>(W), slots, packed,
+                       scales, zeros);
+    return hipGetLastError();
+}
+
 hipError_t launch_quantize(const uint16_t* W, int64_t N, int64_t K, int64_t group,
                            uint32_t* packed, uint16_t* scales, hipStream_t stream, int num_cu,
                            const int* perm, int16_t* zeros) {
@@ -610,24 +754,37 @@ hipError_t launch_quantize(const uint16_t* W, int64_t N, int64_t K, int64_t grou
                    : launch_quantize_rows<false>(W, N, K, packed, scales, nullptr, perm, stream);
     const int64_t groups = N * (K / group);
     if (groups == 0) return hipSuccess;
-    // the same 16 bytes per lane and U groups' loads a step for every G;
-    // the asymmetric quantizer without perm takes 32 bytes per lane from
-    // group 64 up
-    constexpr int U = kQuantizeGroupsPerStep;
-    if (zeros != nullptr && perm == nullptr) {
+    // In their own column order: the flat grid (16 bytes a lane for
+    // symmetric weights, 32 for asymmetric ones from group 64 up).
+    if (zeros == nullptr && perm == nullptr) {
         switch (group) {
-            case 64:
-                return launch_quantize_t<4, U, 16>(W, groups, K, perm, packed, scales, zeros,
-                                                   stream, num_cu);
-            case 128:
-                return launch_quantize_t<8, U, 16>(W, groups, K, perm, packed, scales, zeros,
-                                                   stream, num_cu);
-            case 256:
-                return launch_quantize_t<16, U, 16>(W, groups, K, perm, packed, scales, zeros,
-                                                    stream, num_cu);
+            case 32: return launch_quantize_flat<4, 2, false, 8>(W, N, K, packed, scales, zeros,
+                                                                 stream);
+            case 64: return launch_quantize_flat<8, 2, false, 8>(W, N, K, packed, scales, zeros,
+                                                                 stream);
+            case 128: return launch_quantize_flat<16, 2, false, 8>(W, N, K, packed, scales, zeros,
+                                                                   stream);
+            case 256: return launch_quantize_flat<32, 2, false, 8>(W, N, K, packed, scales, zeros,
+                                                                   stream);
             default: break;
         }
     }
+    if (zeros != nullptr && perm == nullptr) {
+        switch (group) {
+            case 32: return launch_quantize_flat<4, 1, true, 8>(W, N, K, packed, scales, zeros,
+                                                                stream);
+            case 64: return launch_quantize_flat<4, 1, true, 16>(W, N, K, packed, scales, zeros,
+                                                                 stream);
+            case 128: return launch_quantize_flat<8, 1, true, 16>(W, N, K, packed, scales, zeros,
+                                                                  stream);
+            case 256: return launch_quantize_flat<16, 1, true, 16>(W, N, K, packed, scales, zeros,
+                                                                   stream);
+            default: break;
+        }
+    }
+    // Through act order (columns gathered through perm): the persistent
+    // kernel, 16 bytes a lane and U groups' loads a step for every G.
+    constexpr int U = kQuantizeGroupsPerStep;
     switch (group) {
         case 32:
             return launch_quantize_t<4, U>(W, groups, K, perm, packed, scales, zeros, stream, num_cu);
