@@ -755,8 +755,11 @@ hipError_t launch_quantize(const uint16_t* W, int64_t N, int64_t K, int64_t grou
     const int64_t groups = N * (K / group);
     if (groups == 0) return hipSuccess;
     // In their own column order: the flat grid (16 bytes a lane for
-    // symmetric weights, 32 for asymmetric ones from group 64 up).
-    if (zeros == nullptr && perm == nullptr) {
+    // symmetric weights, 32 for asymmetric ones from group 64 up), up to 2^34
+    // weights, where its work-items still fit the 32-bit grid size; larger
+    // matrices take the persistent kernel below.
+    const bool flat = perm == nullptr && N * K <= ((int64_t)1 << 34);
+    if (zeros == nullptr && flat) {
         switch (group) {
             case 32: return launch_quantize_flat<4, 2, false, 8>(W, N, K, packed, scales, zeros,
                                                                  stream);
@@ -769,7 +772,7 @@ hipError_t launch_quantize(const uint16_t* W, int64_t N, int64_t K, int64_t grou
             default: break;
         }
     }
-    if (zeros != nullptr && perm == nullptr) {
+    if (zeros != nullptr && flat) {
         switch (group) {
             case 32: return launch_quantize_flat<4, 1, true, 8>(W, N, K, packed, scales, zeros,
                                                                 stream);
@@ -782,8 +785,9 @@ hipError_t launch_quantize(const uint16_t* W, int64_t N, int64_t K, int64_t grou
             default: break;
         }
     }
-    // Through act order (columns gathered through perm): the persistent
-    // kernel, 16 bytes a lane and U groups' loads a step for every G.
+    // Through act order (columns gathered through perm), or past 2^34
+    // weights: the persistent kernel, 16 bytes a lane and U groups' loads a
+    // step for every G.
     constexpr int U = kQuantizeGroupsPerStep;
     switch (group) {
         case 32:
