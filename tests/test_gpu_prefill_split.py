@@ -52,8 +52,9 @@ def check(Y, Yref, Yabs, rows=None):
 @pytest.mark.parametrize("M,N,K", [(65, 300, 2048), (130, 1000, 4096), (200, 3000, 14336),
                                    (300, 257, 2304)])
 def test_prefill_split_parity(w4, orc, M, N, K):
-    """Ragged M and N, slices of 8 groups and more, every slice's partial
-    summed by the last block of its tile."""
+    """Ragged M and N (outputs past M or N in the tiles' last rows and
+    columns), 2 to 10 K slices of 8 groups and more, summed by the second
+    kernel."""
     say("prefill split M=%d N=%d K=%d" % (M, N, K))
     assert splits(w4, M, N, K)
     W = inputs.weight(N, K, seed=[91, N, K])
@@ -68,8 +69,8 @@ def test_prefill_split_parity(w4, orc, M, N, K):
 
 @pytest.mark.parametrize("M,K,N", [(512, 14336, 4096), (256, 14336, 4096), (128, 18944, 3584)])
 def test_prefill_split_layer_shapes_sampled(w4, orc, M, K, N):
-    """The FFN down projections of LLaMA-3-8B and Qwen-2.5-7B (24 sampled
-    rows, the first and last included)."""
+    """The FFN down projections of LLaMA-3-8B and Qwen-2.5-7B, 4 / 7 / 15 K
+    slices (24 sampled rows, the first and last included)."""
     say("prefill split layer M=%d K=%d N=%d" % (M, K, N))
     assert splits(w4, M, N, K)
     W = inputs.weight(N, K, seed=[92, K, N])
@@ -85,9 +86,9 @@ def test_prefill_split_layer_shapes_sampled(w4, orc, M, K, N):
 
 
 def test_prefill_split_workspace_reuse_and_determinism(w4, orc):
-    """One workspace serves two shapes in a row (the second smaller); every
-    call leaves its counters zero; repeated calls give the same bits (fixed
-    slice order); the unsplit w4a16_gemm meets the same bound."""
+    """One workspace serves two shapes in a row (the second smaller);
+    repeated calls give the same bits (fixed slice order); the unsplit
+    w4a16_gemm meets the same bound."""
     shapes = [(300, 1000, 8192), (130, 600, 4096)]
     ws = w4.gemm_workspace(*shapes[0], device="cuda")
     for M, N, K in shapes:
@@ -103,7 +104,6 @@ def test_prefill_split_workspace_reuse_and_determinism(w4, orc):
         c = w4.gemm_ws(Xd, pd, sd, ws)
         torch.cuda.synchronize()
         assert torch.equal(b, c)
-        assert int(ws[:4096].view(torch.int32).abs().sum().item()) == 0
         ref = orc.matmul(X, packed, scales)
         check(b.cpu().numpy(), *ref)
         check(a.cpu().numpy(), *ref)
@@ -138,4 +138,3 @@ def test_prefill_split_graph_replays(w4, orc):
         assert torch.equal(out, eager), "replay %d differs from eager" % i
         check(out2.cpu().numpy(), Yref, Yabs)
         del junk
-    assert int(ws[:4096].view(torch.int32).abs().sum().item()) == 0

@@ -66,24 +66,20 @@ hipError_t launch_gemm_mfma_asym(const uint16_t* X, int64_t M, const uint32_t* p
 // Prefill with K split over blocks (gemm_mfma.hip, symmetric weights): when
 // the output has too few 128 x 256 block tiles to give most compute units a
 // block (long-K shapes such as the FFN down projection), block (tile, z)
-// takes the groups [z * groups_per_slice, ...) of K, stores its fp32 partial
-// tile to a workspace (counters, then partials) and the last slice of each
-// tile adds them in slice order.
-constexpr int64_t kTiledSplitCounters = 1024;     // tile counters at the workspace start
+// takes the groups [z * groups_per_slice, ...) of K and stores its fp32
+// partial tile to a workspace; a second kernel adds the slices of each tile
+// in slice order and writes Y.
 struct TiledSplit {
     int ksplit;              // K slices (1: no split)
     int groups_per_slice;
     int tiles;               // output tiles of 128 x 256
-    size_t counter_bytes;    // kTiledSplitCounters uint32
-    size_t workspace_bytes;  // counters + tiles * ksplit * 128 KB of partials
-    uint32_t* counters;      // filled in by the launcher
-    void* partials;
+    size_t workspace_bytes;  // tiles * ksplit * 128 KB of partials
+    void* partials;          // filled in by the launcher
 };
 // The split used for (M, N, K) on num_cu compute units (ksplit == 1 when the
 // shape is not split); ksplit > 0 forces a slice count, for measurements.
 TiledSplit plan_tiled_split(int64_t M, int64_t N, int64_t K, int num_cu, int ksplit = 0);
-// Requires plan.ksplit > 1 and a workspace of plan.workspace_bytes whose
-// counters are zero (every call leaves them zero).
+// Requires plan.ksplit > 1 and a workspace of plan.workspace_bytes.
 hipError_t launch_gemm_tiled_split(const uint16_t* X, int64_t M, const uint32_t* packed,
                                    const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y,
                                    hipStream_t stream, int gshift, const TiledSplit& plan,
