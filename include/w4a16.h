@@ -138,9 +138,11 @@ int w4a16_gemm_ex(const uint16_t* X, int64_t M, const uint32_t* packed, const ui
  * rows and one slice of K each, store fp32 partial tiles in the workspace,
  * and the last slice of each row block to finish adds them in slice order
  * (deterministic) and writes Y.  Prefill ([BENCH] §一/§二, 512-token prompt)
- * on long-K shapes (more than 64 rows, K > N, too few 128 x 256 output tiles
- * for the compute units) splits K over blocks too, with 128 x 256 partial
- * tiles, which a second kernel on the same stream adds in slice order
+ * with more than 64 rows and too few 128 x 256 output tiles for the compute
+ * units (K > N; with K <= N where slices of at least 10 groups of K still
+ * give 3/4 of the compute units a block) splits K over blocks too, with
+ * 128 x 256 partial tiles, which a second kernel on the same stream adds in
+ * slice order
  * (w4a16_gemm keeps these shapes unsplit, so that it never needs memory of
  * its own).  Other shapes run exactly as w4a16_gemm and
  * ignore the workspace.  Same accuracy

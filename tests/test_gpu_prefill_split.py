@@ -1,6 +1,7 @@
 """Prefill with K split over blocks through a caller workspace
-(w4a16_gemm_ws on long-K shapes: more than 64 rows, K > N, too few 128 x 256
-output tiles for the compute units), against the oracle.  Bar as in
+(w4a16_gemm_ws with more than 64 rows and too few 128 x 256 output tiles for
+the compute units: K > N, or K <= N with slices of at least 10 groups that
+still fill the compute units), against the oracle.  Bar as in
 test_gpu_parity: |y - y_ref| <= oracle.tolerance per element.
 """
 import numpy as np
@@ -83,6 +84,33 @@ def test_prefill_split_layer_shapes_sampled(w4, orc, M, K, N):
     rows = np.random.default_rng([92, M]).choice(M, 24, replace=False)
     rows[:2] = (0, M - 1)
     check(Y, *orc.matmul(np.ascontiguousarray(X[rows]), packed, scales), rows=rows)
+
+
+@pytest.mark.parametrize("M,K,N", [(128, 3584, 18944), (384, 4096, 14336), (128, 8192, 8192),
+                                   (200, 8192, 8192)])
+def test_prefill_split_wide_shapes_sampled(w4, orc, M, K, N):
+    """K <= N shapes that the planner splits (slices of at least 10 groups
+    that still fill the compute units): 3, 2, 7 and 4 K slices (24 sampled
+    rows, the first and last included)."""
+    say("prefill split wide M=%d K=%d N=%d" % (M, K, N))
+    assert splits(w4, M, N, K)
+    W = inputs.weight(N, K, seed=[95, K, N])
+    packed, scales = orc.quantize(W)
+    X = inputs.activation(M, K, seed=[95, M, K])
+    ws = w4.gemm_workspace(M, N, K, device="cuda")
+    Y = w4.gemm_ws(dev(X), dev(packed.view(np.int32)), dev(scales.view(np.float16)),
+                   ws).cpu().numpy()
+    torch.cuda.synchronize()
+    rows = np.random.default_rng([95, M]).choice(M, 24, replace=False)
+    rows[:2] = (0, M - 1)
+    check(Y, *orc.matmul(np.ascontiguousarray(X[rows]), packed, scales), rows=rows)
+
+
+def test_prefill_split_skips_short_slices(w4):
+    """K <= N shapes whose split would give slices under 10 groups, or too
+    few blocks, run unsplit (no workspace)."""
+    for M, K, N in [(128, 4096, 14336), (128, 4096, 4096), (256, 4096, 4096), (512, 4096, 4096)]:
+        assert not splits(w4, M, N, K), (M, K, N)
 
 
 def test_prefill_split_workspace_reuse_and_determinism(w4, orc):

@@ -116,12 +116,24 @@ int64_t groups_per_row(int64_t K, int64_t group) {
 int status_of(hipError_t e) { return e == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH; }
 
 // The K split over blocks of the prefill kernel (w4a16_gemm_ws): symmetric
-// weights, more than 64 rows, K > N (long rows, few output tiles).
+// weights, more than 64 rows, too few 128 x 256 output tiles for the compute
+// units.  With K > N (long rows, few tiles) whenever the planner splits;
+// with K <= N only where each slice holds at least 10 groups and the split
+// grid still gives 3/4 of the compute units a block: there the unsplit
+// kernel's smaller tiles do about as well (M = 128 / 256 / 512, us, unsplit
+// against split: 4096x14336 M = 128 28.4 against 30.1 with 8 groups a slice,
+// 4096x4096 21-28 against 25-31 on 64-128 blocks; split where taken:
+// 3584x18944 M = 128 49.5 against 37.2, 8192x28672 M = 128 86.5 against
+// 77.7-80.2, 4096x14336 M = 256 45.0 against 43.2-43.8).
 w4a16::TiledSplit tiled_plan(int64_t M, int64_t N, int64_t K, int num_cu, bool asym) {
     w4a16::TiledSplit none{};
     none.ksplit = 1;
-    if (asym || K <= N) return none;
-    return w4a16::plan_tiled_split(M, N, K, num_cu);
+    if (asym) return none;
+    const w4a16::TiledSplit p = w4a16::plan_tiled_split(M, N, K, num_cu);
+    if (K > N || p.ksplit < 2) return p;
+    const bool long_slices = p.groups_per_slice >= 10;
+    const bool fills = (int64_t)p.tiles * p.ksplit * 4 >= (int64_t)num_cu * 3;
+    return long_slices && fills ? p : none;
 }
 
 bool stream_capturing(hipStream_t s) {
