@@ -251,6 +251,33 @@ int w4a16_gemm_asym(const uint16_t* X, int64_t M, const int32_t* perm, const uin
                     const uint16_t* scales, const int16_t* zeros, int64_t N, int64_t K,
                     int64_t group, uint16_t* Y, void* stream);
 
+/* Asymmetric prefill with K split over blocks ([BENCH] §一/§二, 512-token
+ * prompt; [QUANT] sub-section 2, asymmetric INT4): w4a16_gemm_asym without
+ * perm, with a caller workspace, for the shapes that
+ * w4a16_gemm_asym_workspace_bytes reports a non-zero size for (group 128,
+ * more than 64 rows, K > N, too few 64 x 256 output tiles for the compute
+ * units, at least three K slices).  Block (tile, z) takes one slice of K
+ * and stores its fp32 partial tile in the workspace; a second kernel on the
+ * same stream adds the slices in slice order (deterministic) and writes Y.
+ * Other shapes run exactly as w4a16_gemm_asym and ignore the workspace.
+ * Same accuracy bound as w4a16_gemm_asym; the sum order of split shapes
+ * differs, so their results are not bit-identical to the unsplit kernel's.
+ *   workspace  DEVICE, 256-byte aligned, at least
+ *              w4a16_gemm_asym_workspace_bytes(M, N, K, group) bytes, owned by
+ *              the caller, in use until the call's work on the stream has
+ *              finished (stream-ordered calls and graph replays may share
+ *              it; no initial contents needed); it must not overlap X, Y or
+ *              the weights.
+ * w4a16_gemm_asym_workspace_bytes returns 0 for shapes that do not split,
+ * for invalid sizes and when the current device is not gfx950.  Errors as
+ * for w4a16_gemm_asym; a workspace smaller than required is
+ * W4A16_ERR_INVALID_ARG. */
+size_t w4a16_gemm_asym_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group);
+int w4a16_gemm_asym_ws(const uint16_t* X, int64_t M, const uint32_t* packed,
+                       const uint16_t* scales, const int16_t* zeros, int64_t N, int64_t K,
+                       int64_t group, uint16_t* Y, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
 /* ---- Q4_0 block layout ([QUANT] GGUF section: the type table's Q4_0
  * entry, 32 elements in 18 bytes, symmetric with one scale per block; the
  * section's Q4_0 dequantizer for the byte order; its llama.cpp part credits

@@ -39,7 +39,8 @@ def test_header_declares_the_boundary():
                "w4a16_gemm_asym", "w4a16_q4_0_bytes", "w4a16_quantize_q4_0",
                "w4a16_gemv_q4_0", "w4a16_gemm_q4_0", "w4a16_gemv_chain",
                "w4a16_gemv_chain_noalloc", "w4a16_gemm_ws", "w4a16_gemm_workspace_bytes",
-               "w4a16_linear", "w4a16_linear_workspace_bytes"]:
+               "w4a16_linear", "w4a16_linear_workspace_bytes", "w4a16_gemm_asym_ws",
+               "w4a16_gemm_asym_workspace_bytes"]:
         assert fn in names
 
 
@@ -342,6 +343,26 @@ def test_gemm_ws_validation(lib):
     assert f(A, 0, B, C, 16, 128, D, S, 4096, None) == OK      # empty: nothing enqueued
     assert f(None, 4, B, C, 16, 128, D, S, 4096, None) == INVALID
     assert f(A, 4, B, C, 16, 128, D, S, 4096, None) in (DEVICE, OK)
+
+
+def test_gemm_asym_ws_validation(lib):
+    """The asymmetric K split: sizes and the group are checked before the
+    device; without a gfx950 device the workspace size is 0 and valid calls
+    report the device error."""
+    A, B, C, Z, D, S = FAKE, FAKE * 4, FAKE * 8, FAKE * 10, FAKE * 12, FAKE * 16
+    f = lib.w4a16_gemm_asym_ws
+    n = lib.w4a16_gemm_asym_workspace_bytes(128, 4096, 14336, 128)
+    assert n == 0 or n > 4096          # 0 without a gfx950 device
+    assert lib.w4a16_gemm_asym_workspace_bytes(-1, 4096, 14336, 128) == 0
+    assert lib.w4a16_gemm_asym_workspace_bytes(128, 4096, 100, 128) == 0
+    assert lib.w4a16_gemm_asym_workspace_bytes(128, 4096, 14336, 64) == 0   # group 128 only
+    assert lib.w4a16_gemm_asym_workspace_bytes(128, 4096, 14336, 48) == 0   # no such group
+    assert f(A, -1, B, C, Z, 16, 128, 128, D, S, 4096, None) == INVALID
+    assert f(A, 4, B, C, Z, 16, 100, 128, D, S, 4096, None) == SHAPE        # K not a multiple of 128
+    assert f(A, 4, B, C, Z, 16, 128, 48, D, S, 4096, None) == INVALID       # unknown group
+    assert f(A, 0, B, C, Z, 16, 128, 128, D, S, 4096, None) == OK           # empty: nothing enqueued
+    assert f(A, 4, B, C, None, 16, 128, 128, D, S, 4096, None) == INVALID   # zeros required
+    assert f(A, 4, B, C, Z, 16, 128, 128, D, S, 4096, None) in (DEVICE, OK)
 
 
 def test_linear_general_validation(lib):

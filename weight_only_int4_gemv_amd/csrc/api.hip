@@ -136,6 +136,20 @@ w4a16::TiledSplit tiled_plan(int64_t M, int64_t N, int64_t K, int num_cu, bool a
     return long_slices && fills ? p : none;
 }
 
+// The K split of asymmetric prefill (w4a16_gemm_asym_ws): group 128, more
+// than 64 rows, K > N, 64 x 256 tiles in at least three slices.  With two
+// slices (M = 512 on the FFN down projections) the split was as often slower
+// as faster (18944x3584 138.6 against 126.6 us, 14336x4096 88.2 against
+// 91.9); with three or more it gains (14336x4096 M = 128 / 256: 37.0 / 51.5
+// against 72.3 / 70.8 us, 18944x3584 M = 128 70.7 against 99.6).
+w4a16::TiledSplit asym_plan(int64_t M, int64_t N, int64_t K, int64_t group, int num_cu) {
+    w4a16::TiledSplit none{};
+    none.ksplit = 1;
+    if (group != 128 || K <= N) return none;
+    const w4a16::TiledSplit p = w4a16::plan_tiled_split(M, N, K, num_cu, 0, 64);
+    return p.ksplit >= 3 ? p : none;
+}
+
 bool stream_capturing(hipStream_t s) {
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     return hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone;
@@ -446,6 +460,50 @@ int w4a16_gemm_ws(const uint16_t* X, int64_t M, const uint32_t* packed, const ui
     return status_of(w4a16::launch_gemm_batched_split(X, M, packed, scales, N, K, Y,
                                                       static_cast<hipStream_t>(stream), plan,
                                                       workspace));
+}
+
+size_t w4a16_gemm_asym_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group) {
+    if (check_sizes(M, N, K) != W4A16_OK || check_group(group, K) != W4A16_OK) return 0;
+    int num_cu = 0;
+    if (current_device(&num_cu) != W4A16_OK) return 0;
+    const w4a16::TiledSplit p = asym_plan(M, N, K, group, num_cu);
+    return p.ksplit > 1 ? p.workspace_bytes : 0;
+}
+
+int w4a16_gemm_asym_ws(const uint16_t* X, int64_t M, const uint32_t* packed,
+                       const uint16_t* scales, const int16_t* zeros, int64_t N, int64_t K,
+                       int64_t group, uint16_t* Y, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+    int st = check_sizes(M, N, K);
+    if (st != W4A16_OK) return st;
+    st = check_group(group, K);
+    if (st != W4A16_OK) return st;
+    if (M == 0 || N == 0) return W4A16_OK;
+    if (K > 0 && (!X || !packed || !scales || !zeros || !Y)) return W4A16_ERR_INVALID_ARG;
+    int num_cu = 0;
+    st = current_device(&num_cu);
+    if (st != W4A16_OK) return st;
+    const w4a16::TiledSplit plan = asym_plan(M, N, K, group, num_cu);
+    // shapes the planner does not split run as w4a16_gemm_asym (workspace unused)
+    if (plan.ksplit < 2)
+        return w4a16_gemm_asym(X, M, nullptr, packed, scales, zeros, N, K, group, Y, stream);
+    if (!workspace || workspace_bytes < plan.workspace_bytes) return W4A16_ERR_INVALID_ARG;
+    if (!aligned(X, 16) || !aligned(packed, 16) || !aligned(scales, 2) || !aligned(zeros, 2) ||
+        !aligned(Y, 2) || !aligned(workspace, 256))
+        return W4A16_ERR_MISALIGNED;
+    const size_t y_bytes = (size_t)M * N * 2, x_bytes = (size_t)M * K * 2;
+    const size_t p_bytes = (size_t)N * K / 2, s_bytes = (size_t)N * (K / group) * 2;
+    const size_t w_bytes = plan.workspace_bytes;
+    if (overlap(Y, y_bytes, X, x_bytes) || overlap(Y, y_bytes, packed, p_bytes) ||
+        overlap(Y, y_bytes, scales, s_bytes) || overlap(Y, y_bytes, zeros, s_bytes) ||
+        overlap(workspace, w_bytes, X, x_bytes) || overlap(workspace, w_bytes, Y, y_bytes) ||
+        overlap(workspace, w_bytes, packed, p_bytes) ||
+        overlap(workspace, w_bytes, scales, s_bytes) ||
+        overlap(workspace, w_bytes, zeros, s_bytes))
+        return W4A16_ERR_INVALID_ARG;
+    return status_of(w4a16::launch_gemm_tiled_split_asym(X, M, packed, scales, zeros, N, K, Y,
+                                                         static_cast<hipStream_t>(stream), plan,
+                                                         workspace));
 }
 
 int w4a16_quantize_perm(const uint16_t* W, const int32_t* perm, int64_t N, int64_t K,

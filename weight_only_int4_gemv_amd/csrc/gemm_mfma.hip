@@ -788,12 +788,13 @@ hipError_t launch_tiled(const uint16_t* X, int64_t M, const uint32_t* packed,
 
 }  // namespace
 
-TiledSplit plan_tiled_split(int64_t M, int64_t N, int64_t K, int num_cu, int ksplit) {
+TiledSplit plan_tiled_split(int64_t M, int64_t N, int64_t K, int num_cu, int ksplit, int bm) {
     TiledSplit p{};
     p.ksplit = 1;
     const int64_t ngroups = K / kGroup;
-    if (M <= 64 || N < 1 || ngroups < 2 || K > kTiledMaxK || num_cu < 1) return p;
-    const int64_t tiles = ((M + 127) / 128) * ((N + 255) / 256);
+    if (M <= 64 || N < 1 || ngroups < 2 || K > kTiledMaxK || num_cu < 1 || (bm != 64 && bm != 128))
+        return p;
+    const int64_t tiles = ((M + bm - 1) / bm) * ((N + 255) / 256);
     int64_t s = ksplit;
     if (s <= 0) {
         if (tiles * 8 >= (int64_t)num_cu * 7) return p;          // the tiles fill the CUs
@@ -808,11 +809,11 @@ TiledSplit plan_tiled_split(int64_t M, int64_t N, int64_t K, int num_cu, int ksp
     const int64_t gps = (ngroups + s - 1) / s;
     s = (ngroups + gps - 1) / gps;                               // every slice holds a group
     if (s < 2) return p;
-    constexpr int64_t kPartialBytes = (int64_t)8 * 8 * 2 * kWave * 16;   // 128 x 256 fp32 tile
+    const int64_t partial_bytes = (int64_t)bm * 256 * 4;         // bm x 256 fp32 tile
     p.ksplit = (int)s;
     p.groups_per_slice = (int)gps;
     p.tiles = (int)tiles;
-    p.workspace_bytes = (size_t)tiles * s * kPartialBytes;
+    p.workspace_bytes = (size_t)tiles * s * partial_bytes;
     return p;
 }
 
@@ -893,6 +894,26 @@ hipError_t launch_gemm_mfma(const uint16_t* X, int64_t M, const uint32_t* packed
             return launch_gemm_skinny(X, M, packed, scales, N, K, Y, stream, num_cu);
     }
     return launch_tiled<false>(X, M, packed, scales, nullptr, N, K, Y, stream, num_cu, gshift);
+}
+
+hipError_t launch_gemm_tiled_split_asym(const uint16_t* X, int64_t M, const uint32_t* packed,
+                                        const uint16_t* scales, const int16_t* zeros, int64_t N,
+                                        int64_t K, uint16_t* Y, hipStream_t stream,
+                                        const TiledSplit& plan, void* workspace) {
+    // 64 x 256 blocks of 64 x 32 wave tiles: both copies of the asymmetric
+    // loop fit two waves per SIMD (the 128 x 256 block's wave tile does not).
+    if (plan.ksplit < 2 || workspace == nullptr) return hipErrorInvalidValue;
+    TiledSplit p = plan;
+    p.partials = workspace;
+    hipError_t e = launch_mfma_t<4, 2, 1, 8, 1, true, true>(X, M, packed, scales, N, K, Y, stream,
+                                                            2, zeros, &p);
+    if (e != hipSuccess) return e;
+    constexpr int PT = 4 * 2 * 1 * 8 * kWave;
+    const int ntn = (int)((N + 255) / 256);
+    hipLaunchKernelGGL((split_sum_kernel<4, 2, 1, 8>), dim3((unsigned)(p.tiles * (PT / 256))),
+                       dim3(256), 0, stream, static_cast<const float4_t*>(p.partials), p.ksplit,
+                       ntn, Y, (int)M, (int)N);
+    return hipGetLastError();
 }
 
 hipError_t launch_gemm_mfma_asym(const uint16_t* X, int64_t M, const uint32_t* packed,

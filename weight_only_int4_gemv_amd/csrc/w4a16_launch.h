@@ -72,18 +72,26 @@ hipError_t launch_gemm_mfma_asym(const uint16_t* X, int64_t M, const uint32_t* p
 struct TiledSplit {
     int ksplit;              // K slices (1: no split)
     int groups_per_slice;
-    int tiles;               // output tiles of 128 x 256
-    size_t workspace_bytes;  // tiles * ksplit * 128 KB of partials
+    int tiles;               // output tiles of bm x 256
+    size_t workspace_bytes;  // tiles * ksplit * bm x 256 fp32 partials
     void* partials;          // filled in by the launcher
 };
-// The split used for (M, N, K) on num_cu compute units (ksplit == 1 when the
-// shape is not split); ksplit > 0 forces a slice count, for measurements.
-TiledSplit plan_tiled_split(int64_t M, int64_t N, int64_t K, int num_cu, int ksplit = 0);
-// Requires plan.ksplit > 1 and a workspace of plan.workspace_bytes.
+// The split used for (M, N, K) on num_cu compute units with bm x 256 tiles
+// (128 symmetric, 64 asymmetric; ksplit == 1 when the shape is not split);
+// ksplit > 0 forces a slice count, for measurements.
+TiledSplit plan_tiled_split(int64_t M, int64_t N, int64_t K, int num_cu, int ksplit = 0,
+                            int bm = 128);
+// Requires plan.ksplit > 1 (a plan for bm = 128) and a workspace of
+// plan.workspace_bytes.
 hipError_t launch_gemm_tiled_split(const uint16_t* X, int64_t M, const uint32_t* packed,
                                    const uint16_t* scales, int64_t N, int64_t K, uint16_t* Y,
                                    hipStream_t stream, int gshift, const TiledSplit& plan,
                                    void* workspace);
+// Asymmetric weights at group 128: a plan for bm = 64, 64 x 256 blocks.
+hipError_t launch_gemm_tiled_split_asym(const uint16_t* X, int64_t M, const uint32_t* packed,
+                                        const uint16_t* scales, const int16_t* zeros, int64_t N,
+                                        int64_t K, uint16_t* Y, hipStream_t stream,
+                                        const TiledSplit& plan, void* workspace);
 
 // Activations in the act-order column order (gather_x.hip): Xp[m, j] =
 // X[m, perm[j]], 0 for an index outside [0, K).  X, Xp fp16 [M, K] (16-byte

@@ -67,6 +67,11 @@ def library() -> ctypes.CDLL:
         lib.w4a16_gemm_workspace_bytes.restype = ctypes.c_size_t
         lib.w4a16_gemm_ws.argtypes = [_p, _i64, _p, _p, _i64, _i64, _p, _p, ctypes.c_size_t, _p]
         lib.w4a16_gemm_ws.restype = ctypes.c_int
+        lib.w4a16_gemm_asym_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64]
+        lib.w4a16_gemm_asym_workspace_bytes.restype = ctypes.c_size_t
+        lib.w4a16_gemm_asym_ws.argtypes = [_p, _i64, _p, _p, _p, _i64, _i64, _i64, _p, _p,
+                                           ctypes.c_size_t, _p]
+        lib.w4a16_gemm_asym_ws.restype = ctypes.c_int
         lib.w4a16_scales_bytes_g.argtypes = [_i64, _i64, _i64]
         lib.w4a16_scales_bytes_g.restype = ctypes.c_size_t
         lib.w4a16_quantize_g.argtypes = [_p, _i64, _i64, _i64, _p, _p, _p]
@@ -438,6 +443,31 @@ def gemm_asym(X: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,
                              packed.data_ptr(), scales.data_ptr(), zeros.data_ptr(), N, K, group,
                              Y.data_ptr(), _stream())
     _check("w4a16_gemm_asym", st)
+    return Y
+
+
+def gemm_asym_workspace(M: int, N: int, K: int, group: int = W4A16_GROUP,
+                        device="cuda") -> torch.Tensor:
+    """A workspace for gemm_asym_ws (uint8, at least 1 byte)."""
+    n = library().w4a16_gemm_asym_workspace_bytes(M, N, K, group)
+    return torch.empty(max(1, n), dtype=torch.uint8, device=device)
+
+
+def gemm_asym_ws(X: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,
+                 zeros: torch.Tensor, workspace: torch.Tensor,
+                 Y: torch.Tensor = None) -> torch.Tensor:
+    """w4a16_gemm_asym_ws: gemm_asym (no perm) with K split over blocks
+    through `workspace` (from gemm_asym_workspace) where the library splits
+    the shape."""
+    lib = library()
+    N, K, group = _weights(packed, scales)
+    _zeros(zeros, scales)
+    X, Y, M = _rows(X, K, N, Y)
+    _need(workspace, "workspace", torch.uint8, 1)
+    _check("w4a16_gemm_asym_ws",
+           lib.w4a16_gemm_asym_ws(X.data_ptr(), M, packed.data_ptr(), scales.data_ptr(),
+                                  zeros.data_ptr(), N, K, group, Y.data_ptr(),
+                                  workspace.data_ptr(), workspace.numel(), _stream()))
     return Y
 
 
