@@ -381,6 +381,18 @@ def secondary(torch, w4a16, inputs, dev, stream, main_workload="llama3-8b-sweep"
                 row["M=%d_us" % M] = round(a_us, 2)
                 row["M=%d_symmetric_us" % M] = round(s_us, 2)
                 row["M=%d_TFLOP/s" % M] = round(2 * M * N * K / (a_us * 1e-6) / 1e12, 1)
+            # a 128-token prompt, with K split over blocks where the library
+            # splits the shape (w4a16_gemm_asym_ws; it runs as gemm_asym elsewhere)
+            M = 128
+            X = torch.from_numpy(inputs.activation(M, K, seed=[10, M, K])).to(dev)
+            Y = torch.empty((M, N), dtype=torch.float16, device=dev)
+            ws = w4a16.gemm_asym_workspace(M, N, K, device=dev)
+            few = copies
+            w_us = timed(lambda: [w4a16.gemm_asym_ws(X, p, s_, z, ws, Y=Y) for p, s_, z in few]) \
+                / len(few)
+            row["M=128_ws_us"] = round(w_us, 2)
+            row["M=128_ws_split"] = ws.numel() > 1
+            row["M=128_ws_TFLOP/s"] = round(2 * M * N * K / (w_us * 1e-6) / 1e12, 1)
             asym["%dx%d" % (K, N)] = row
             del copies, sym, Wd
         out["asymmetric"] = asym
